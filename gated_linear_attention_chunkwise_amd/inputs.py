@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for the Lizard hybrid attention layer.
+
+This module draws random tensors and nothing else: it holds none of the
+layer's arithmetic, so both the HIP path and the CPU oracle can take their
+inputs from it without sharing any of the method's code.
+
+Workloads (all synthetic; the explainer pages measure speed on no named
+workload and print no shapes):
+
+* ``tiny_fp32``   B=1  H=2  L=256   d=64  W=64  M=4, everything fp32
+* ``fwd_4k``      B=1  H=32 L=4096  d=128 W=128 M=4, bf16 activations
+* ``train_8k``    B=4  H=32 L=8192  d=128 W=128 M=4, bf16, with dO ~ N(0,1)
+* ``prefill_64k`` B=1  H=32 L=65536 d=128 W=128 M=4, bf16, gate input x ~ N(2,1)
+* ``decode_b64``  B=64 H=32 d=128 W=128 M=4, a 4096-token prefill followed by
+  1024 single-token decode steps, drawn up front as one 5120-token sequence
+
+Recipe (numpy ``default_rng(seed)``, draw order q, k, v, x, meta_k, dO):
+
+* q, k, v ~ N(0, 1) / 8
+* x ~ N(mu, 1) with mu = 0 (mu = 2 for ``prefill_64k``); the log-gate is
+  g = logsigmoid(x) / 16, evaluated in fp64 and stored as fp32, per key dim
+* meta_k ~ N(0, 1) / 8, shape [H, M, d_k]; meta values are absent (zero)
+* dO ~ N(0, 1)
+
+For bf16 workloads q, k, v, meta_k and dO are rounded to bf16 (round to
+nearest even) and handed out as float32 arrays that hold exactly those bf16
+values, so the oracle sees the very numbers the GPU sees; g stays fp32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    L: int
+    D: int
+    W: int
+    M: int
+    chunk: int
+    dtype: str          # "fp32" or "bf16": dtype of q, k, v, o, meta, dO and grads
+    x_mean: float
+    seed: int
+    prefill: int = 0    # decode workloads: tokens consumed by the prefill
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 2, 256, 64, 64, 4, 64, "fp32", 0.0, 1000),
+    "fwd_4k": Workload("fwd_4k", 1, 32, 4096, 128, 128, 4, 64, "bf16", 0.0, 1001),
+    "train_8k": Workload("train_8k", 4, 32, 8192, 128, 128, 4, 64, "bf16", 0.0, 1002),
+    "prefill_64k": Workload("prefill_64k", 1, 32, 65536, 128, 128, 4, 64, "bf16", 2.0, 1003),
+    "decode_b64": Workload("decode_b64", 64, 32, 5120, 128, 128, 4, 64, "bf16", 0.0, 1004,
+                           prefill=4096),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def _logsigmoid(x: np.ndarray) -> np.ndarray:
+    # log(1 / (1 + e^-x)), evaluated without overflow for either sign of x
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def make_inputs(w: Workload, *, with_grad: bool = False, L: int | None = None) -> dict:
+    """Draw the seeded inputs of workload ``w`` (optionally a shorter ``L``).
+
+    Returns a dict of float32 numpy arrays: q, k, v [B,H,L,D], g [B,H,L,D],
+    meta_k [H,M,D] and, with ``with_grad``, dO [B,H,L,D].
+    """
+    L = w.L if L is None else L
+    rng = np.random.default_rng(w.seed)
+    shp = (w.B, w.H, L, w.D)
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name] = (rng.standard_normal(shp, dtype=np.float64) / 8.0).astype(np.float32)
+    x = rng.standard_normal(shp, dtype=np.float64) + w.x_mean
+    out["g"] = (_logsigmoid(x) / 16.0).astype(np.float32)
+    del x
+    out["meta_k"] = (rng.standard_normal((w.H, w.M, w.D), dtype=np.float64) / 8.0).astype(np.float32)
+    if with_grad:
+        out["dO"] = rng.standard_normal(shp, dtype=np.float64).astype(np.float32)
+    if w.dtype == "bf16":
+        for name in ("q", "k", "v", "meta_k", "dO"):
+            if name in out:
+                out[name] = round_to_bf16(out[name])
+    return out
+
+
+def make_small(B: int, H: int, L: int, D: int, M: int, *, seed: int, bf16: bool,
+               x_mean: float = 0.0, gate_div: float = 16.0, with_grad: bool = True,
+               Dv: int | None = None, with_meta_v: bool = False) -> dict:
+    """Same recipe at arbitrary small sizes (parity and edge-case tests)."""
+    Dv = D if Dv is None else Dv
+    rng = np.random.default_rng(seed)
+    out = {
+        "q": (rng.standard_normal((B, H, L, D)) / 8.0).astype(np.float32),
+        "k": (rng.standard_normal((B, H, L, D)) / 8.0).astype(np.float32),
+        "v": (rng.standard_normal((B, H, L, Dv)) / 8.0).astype(np.float32),
+    }
+    x = rng.standard_normal((B, H, L, D)) + x_mean
+    out["g"] = (_logsigmoid(x) / gate_div).astype(np.float32)
+    out["meta_k"] = (rng.standard_normal((H, M, D)) / 8.0).astype(np.float32)
+    if with_grad:
+        out["dO"] = rng.standard_normal((B, H, L, Dv)).astype(np.float32)
+    if with_meta_v:
+        out["meta_v"] = (rng.standard_normal((H, M, Dv)) / 8.0).astype(np.float32)
+    if bf16:
+        for name in ("q", "k", "v", "meta_k", "meta_v", "dO"):
+            if name in out:
+                out[name] = round_to_bf16(out[name])
+    return out

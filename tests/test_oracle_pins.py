@@ -1,0 +1,293 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against a textbook special case, a closed form,
+a library routine (torch CPU attention / autograd), a hand-worked example,
+finite differences, or an invariant of the definition on the explainer pages
+("Lizard: An Efficient Linearization Framework for Large Language Models",
+English page §2.A hybrid attention, §2.C log-space gate handling).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lizard_oracle as orc
+from gated_linear_attention_chunkwise_amd.inputs import make_small
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(x, y):
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    return float(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300))
+
+
+def small(seed=0, B=2, H=2, L=37, D=8, M=3, **kw):
+    return {k: v.astype(np.float64) for k, v in
+            make_small(B, H, L, D, M, seed=seed, bf16=False, **kw).items()}
+
+
+# ---------------------------------------------------------------- GLA forward
+
+def quadratic_gla(q, k, v, g):
+    """Materialised parallel form: o_t = sum_{s<=t} sum_i q_t[i] e^{b_t[i]-b_s[i]} k_s[i] v_s."""
+    b = np.cumsum(g, axis=2)
+    L = q.shape[2]
+    o = np.zeros(q.shape[:3] + (v.shape[-1],))
+    for t in range(L):
+        for s in range(t + 1):
+            w = (q[:, :, t] * np.exp(b[:, :, t] - b[:, :, s]) * k[:, :, s]).sum(-1)
+            o[:, :, t] += w[..., None] * v[:, :, s]
+    return o
+
+
+def test_recurrent_equals_quadratic_gated_form():
+    x = small(seed=1, gate_div=2.0)
+    o, _ = orc.gla_forward(x["q"], x["k"], x["v"], x["g"])
+    assert rel(o, quadratic_gla(x["q"], x["k"], x["v"], x["g"])) < 1e-12
+
+
+def test_zero_log_gate_is_causal_linear_attention():
+    x = small(seed=2)
+    g = np.zeros_like(x["g"])
+    o, _ = orc.gla_forward(x["q"], x["k"], x["v"], g)
+    A = np.tril(x["q"] @ np.swapaxes(x["k"], -1, -2))
+    assert rel(o, A @ x["v"]) < 1e-12
+
+
+def test_scalar_gate_is_decay_mask_closed_form():
+    x = small(seed=3)
+    B, H, L, D = x["q"].shape
+    gamma = np.array([0.9, 0.5])                      # one constant gate per head
+    g = np.broadcast_to(np.log(gamma)[None, :, None, None], (B, H, L, D)).copy()
+    o, _ = orc.gla_forward(x["q"], x["k"], x["v"], g)
+    t = np.arange(L)
+    expo = (t[:, None] - t[None, :]).astype(float)
+    for h in range(H):
+        Dm = np.where(expo >= 0, gamma[h] ** np.maximum(expo, 0), 0.0)
+        ref = (Dm * (x["q"][:, h] @ np.swapaxes(x["k"][:, h], -1, -2))) @ x["v"][:, h]
+        assert rel(o[:, h], ref) < 1e-12
+
+
+def test_closed_gate_keeps_only_current_token():
+    x = small(seed=4)
+    g = np.full_like(x["g"], -np.inf)                # a_t = 0
+    o, S = orc.gla_forward(x["q"], x["k"], x["v"], g)
+    ref = (x["q"] * x["k"]).sum(-1, keepdims=True) * x["v"]
+    assert rel(o, ref) < 1e-14
+    assert rel(S, x["k"][:, :, -1, :, None] * x["v"][:, :, -1, None, :]) < 1e-14
+
+
+def test_gla_hand_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "hand_worked.json")))["gla"]
+    q, k, v = (np.array(ex[n], float)[None, None] for n in ("q", "k", "v"))
+    g = np.log(np.array(ex["a"], float))[None, None]
+    o, S = orc.gla_forward(q, k, v, g)
+    np.testing.assert_allclose(o[0, 0], ex["o"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S[0, 0], ex["final_state"], rtol=0, atol=1e-14)
+
+
+def test_initial_state_continuation():
+    x = small(seed=5, L=40)
+    o_full, S_full = orc.gla_forward(x["q"], x["k"], x["v"], x["g"])
+    sl = lambda a, lo, hi: a[:, :, lo:hi]
+    o1, S1 = orc.gla_forward(*(sl(x[n], 0, 17) for n in "qkvg"))
+    o2, S2 = orc.gla_forward(*(sl(x[n], 17, 40) for n in "qkvg"), initial_state=S1)
+    assert rel(np.concatenate([o1, o2], 2), o_full) < 1e-13
+    assert rel(S2, S_full) < 1e-13
+
+
+# ------------------------------------------------------------- window forward
+
+def sdpa_reference(q, k, v, mk, mv, W, scale):
+    """torch CPU scaled_dot_product_attention on keys [meta; k] with a band mask."""
+    B, H, L, D = q.shape
+    M = mk.shape[1]
+    Kt = torch.cat([torch.from_numpy(mk)[None].expand(B, H, M, D), torch.from_numpy(k)], 2)
+    mvv = np.zeros((H, M, v.shape[-1])) if mv is None else mv
+    Vt = torch.cat([torch.from_numpy(mvv)[None].expand(B, H, M, v.shape[-1]),
+                    torch.from_numpy(v)], 2)
+    t = torch.arange(L)[:, None]
+    s = torch.arange(L)[None, :]
+    band = (s <= t) & (s > t - W)
+    mask = torch.cat([torch.ones(L, M, dtype=torch.bool), band], 1)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), Kt, Vt, attn_mask=mask, scale=scale)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("W", [1, 5, 16, 37, 100])
+@pytest.mark.parametrize("with_mv", [False, True])
+def test_window_matches_torch_sdpa(W, with_mv):
+    x = small(seed=6, with_meta_v=with_mv)
+    mv = x.get("meta_v")
+    scale = 1 / math.sqrt(8)
+    o, _ = orc.window_forward(x["q"], x["k"], x["v"], x["meta_k"], mv, W, scale)
+    assert rel(o, sdpa_reference(x["q"], x["k"], x["v"], x["meta_k"], mv, W, scale)) < 1e-12
+
+
+def test_window_one_without_meta_returns_value():
+    x = small(seed=7, M=0)
+    o, lse = orc.window_forward(x["q"], x["k"], x["v"], x["meta_k"], None, 1, 0.3)
+    assert rel(o, x["v"]) < 1e-15
+    np.testing.assert_allclose(lse, 0.3 * (x["q"] * x["k"]).sum(-1), rtol=1e-13)
+
+
+def test_zero_meta_keys_are_pure_denominator_sinks():
+    x = small(seed=8, L=20)
+    M, W, sc = 3, 6, 0.5
+    mk = np.zeros((2, M, 8))
+    o, _ = orc.window_forward(x["q"], x["k"], x["v"], mk, None, W, sc)
+    L = 20
+    for t in range(L):
+        lo = max(0, t - W + 1)
+        e = np.exp(sc * np.einsum("bhd,bhnd->bhn", x["q"][:, :, t], x["k"][:, :, lo:t + 1]))
+        ref = np.einsum("bhn,bhnd->bhd", e, x["v"][:, :, lo:t + 1]) / (M + e.sum(-1))[..., None]
+        assert rel(o[:, :, t], ref) < 1e-13
+
+
+def test_window_hand_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "hand_worked.json")))["window"]
+    q = np.array(ex["q"])[None, None]
+    k = np.log(np.array(ex["k_log"]))[None, None, :, None]
+    v = np.array(ex["v"])[None, None]
+    mk = np.array(ex["meta_k"])[None]
+    o, _ = orc.window_forward(q, k, v, mk, None, ex["W"], 1.0)
+    np.testing.assert_allclose(o[0, 0], ex["o_swa"], rtol=1e-14)
+
+
+# ------------------------------------------------------------- hybrid forward
+
+def test_hybrid_is_linear_in_v_and_mix_scales_window_only():
+    x = small(seed=9)
+    kw = dict(window=7, scale=0.35)
+    r1 = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], **kw, mix=1.0)
+    r2 = orc.hybrid_forward(x["q"], x["k"], 3.0 * x["v"], x["g"], x["meta_k"], **kw, mix=1.0)
+    assert rel(r2["o"], 3.0 * r1["o"]) < 1e-13
+    r3 = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], **kw, mix=0.25)
+    assert rel(r3["o"], r1["o_gla"] + 0.25 * r1["o_swa"]) < 1e-13
+    r0 = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], **kw, mix=0.0)
+    assert rel(r0["o"], r1["o_gla"]) < 1e-15
+
+
+def test_wide_window_closed_gate_reduces_to_qk_v_plus_causal_softmax():
+    """W >= L with every gate closed (a=0): o = (q_t.k_t) v_t + causal softmax with sinks."""
+    x = small(seed=10, L=24)
+    g = np.full_like(x["g"], -np.inf)
+    sc = 1 / math.sqrt(8)
+    r = orc.hybrid_forward(x["q"], x["k"], x["v"], g, x["meta_k"], window=24, scale=sc)
+    ref = (x["q"] * x["k"]).sum(-1, keepdims=True) * x["v"] + \
+        sdpa_reference(x["q"], x["k"], x["v"], x["meta_k"], None, 10 ** 6, sc)
+    assert rel(r["o"], ref) < 1e-12
+
+
+# ------------------------------------------------------------------- backward
+
+def torch_hybrid(q, k, v, g, mk, mv, W, scale, mix):
+    """Independent torch formulation (materialised gated form + masked softmax)."""
+    B, H, L, D = q.shape
+    b = torch.cumsum(g, 2)
+    t = torch.arange(L)[:, None]
+    s = torch.arange(L)[None, :]
+    causal = (s <= t)
+    diff = b[:, :, :, None, :] - b[:, :, None, :, :]                  # [B,H,t,s,i]
+    diff = torch.where(causal[None, None, :, :, None], diff, torch.full_like(diff, -torch.inf))
+    A = torch.einsum("bhti,bhtsi,bhsi->bhts", q, torch.exp(diff), k)
+    o_gla = A @ v
+    M = mk.shape[1]
+    logits = scale * torch.cat([torch.einsum("bhtd,hmd->bhtm", q, mk), q @ k.transpose(-1, -2)], -1)
+    band = causal & (s > t - W)
+    mask = torch.cat([torch.ones(L, M, dtype=torch.bool), band], 1)
+    logits = logits.masked_fill(~mask, -torch.inf)
+    p = torch.softmax(logits, -1)
+    vals = torch.cat([(mv if mv is not None else torch.zeros(H, M, v.shape[-1], dtype=v.dtype))[None]
+                      .expand(B, H, M, v.shape[-1]), v], 2)
+    return o_gla + mix * (p @ vals)
+
+
+@pytest.mark.parametrize("with_mv", [False, True])
+def test_backward_matches_torch_autograd(with_mv):
+    x = small(seed=11, L=19, D=6, M=2, gate_div=3.0, with_meta_v=with_mv)
+    W, sc, mix = 5, 0.4, 0.7
+    names = ["q", "k", "v", "g", "meta_k"] + (["meta_v"] if with_mv else [])
+    T = {n: torch.tensor(x[n], requires_grad=True) for n in names}
+    out = torch_hybrid(T["q"], T["k"], T["v"], T["g"], T["meta_k"], T.get("meta_v"), W, sc, mix)
+    (out * torch.from_numpy(x["dO"])).sum().backward()
+    ref = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], x.get("meta_v"),
+                             window=W, scale=sc, mix=mix)
+    assert rel(ref["o"], out.detach().numpy()) < 1e-12
+    gr = orc.hybrid_backward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], x.get("meta_v"),
+                             x["dO"], window=W, scale=sc, mix=mix)
+    for n, on in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("meta_k", "dmeta_k")] + \
+            ([("meta_v", "dmeta_v")] if with_mv else []):
+        assert rel(gr[on], T[n].grad.numpy()) < 1e-11, on
+    if not with_mv:
+        assert gr["dmeta_v"] is None
+
+
+def test_backward_matches_central_differences():
+    x = small(seed=12, B=1, H=1, L=7, D=3, M=2, gate_div=2.0, with_meta_v=True)
+    W, sc, mix = 3, 0.8, 1.3
+    names = ["q", "k", "v", "g", "meta_k", "meta_v"]
+
+    def loss(d):
+        r = orc.hybrid_forward(d["q"], d["k"], d["v"], d["g"], d["meta_k"], d["meta_v"],
+                               window=W, scale=sc, mix=mix)
+        return float((r["o"] * x["dO"]).sum())
+
+    gr = orc.hybrid_backward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], x["meta_v"], x["dO"],
+                             window=W, scale=sc, mix=mix)
+    key = dict(q="dq", k="dk", v="dv", g="dg", meta_k="dmeta_k", meta_v="dmeta_v")
+    h = 1e-6
+    for n in names:
+        num = np.zeros_like(x[n])
+        for idx in np.ndindex(x[n].shape):
+            d = {m: x[m].copy() for m in names}
+            d[n][idx] += h
+            fp = loss(d)
+            d[n][idx] -= 2 * h
+            fm = loss(d)
+            num[idx] = (fp - fm) / (2 * h)
+        assert rel(gr[key[n]], num) < 1e-7, n
+
+
+def test_gate_gradient_invariants():
+    x = small(seed=13, L=23, D=5, gate_div=2.0)
+    B, H, L, D = x["q"].shape
+    dq, dk, dv, dg = orc.gla_backward(x["q"], x["k"], x["v"], x["g"], x["dO"][..., :D])
+    # the first gate multiplies the zero initial state: no gradient
+    assert np.abs(dg[:, :, 0]).max() < 1e-13 * np.abs(dg).max()
+    # rowsum form dg_t = a_t * rowsum(S_{t-1} * dS_t) from stored states
+    _, _, states = orc.gla_forward(x["q"], x["k"], x["v"], x["g"], return_states=True)
+    a = np.exp(x["g"])
+    dS = np.zeros((B, H, D, D))
+    dO = x["dO"][..., :D]
+    for t in range(L - 1, -1, -1):
+        dS = x["q"][:, :, t, :, None] * dO[:, :, t, None, :] + \
+            (a[:, :, t + 1, :, None] * dS if t + 1 < L else 0.0)
+        prev = states[t - 1] if t > 0 else np.zeros((B, H, D, D))
+        form = a[:, :, t] * (prev * dS).sum(-1)
+        np.testing.assert_allclose(dg[:, :, t], form, rtol=1e-10, atol=1e-13)
+
+
+# --------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("L0,steps,W", [(30, 25, 8), (3, 12, 8), (0, 9, 4), (10, 6, 1), (5, 5, 64)])
+@pytest.mark.parametrize("with_mv", [False, True])
+def test_decode_after_prefill_equals_full_sequence(L0, steps, W, with_mv):
+    x = small(seed=14, L=L0 + steps, with_meta_v=with_mv)
+    mv = x.get("meta_v")
+    sc = 0.33
+    full = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], mv, window=W, scale=sc)
+    pre = orc.hybrid_forward(*(x[n][:, :, :L0] for n in "qkvg"), x["meta_k"], mv, window=W, scale=sc)
+    st = orc.DecodeState.from_prefix(x["k"][:, :, :L0], x["v"][:, :, :L0], pre["state"], W)
+    outs = []
+    for t in range(L0, L0 + steps):
+        outs.append(orc.decode_step(st, *(x[n][:, :, t] for n in "qkvg"), x["meta_k"], mv, scale=sc))
+    assert rel(np.stack(outs, 2), full["o"][:, :, L0:]) < 1e-12
+    assert rel(st.S, full["state"]) < 1e-12
+    assert (st.pos == L0 + steps).all()
