@@ -1,0 +1,10 @@
+"""MI355X (gfx950) hybrid attention layer of Lizard: GLA with log-space
+per-key-dimension gates plus an anchor window with meta-memory sinks.
+
+The compute path is the HIP library liblizard_attn.so (built in-tree by
+``gated_linear_attention_chunkwise_amd.build``); this package only binds it.
+"""
+from ._lib import (  # noqa: F401
+    LizardError, Shape, SYMBOLS, lizard_attn_bwd, lizard_attn_decode_step, lizard_attn_fwd,
+    load, make_shape, workspace_bytes, fwd, bwd, decode_step, OP_FWD, OP_BWD, OP_DECODE,
+)

@@ -1,0 +1,204 @@
+"""ctypes binding of liblizard_attn.so (argument marshalling only).
+
+Every function here allocates its outputs with torch on the inputs' device,
+passes raw device pointers and the current torch stream to the C ABI and
+raises if the library reports an error.  All arithmetic runs in the HIP
+kernels; there is no fallback of any kind: without the built library on a
+ROCm device these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblizard_attn.so")
+
+LIZARD_FP32, LIZARD_BF16 = 0, 1
+OP_FWD, OP_BWD, OP_DECODE = 0, 1, 2
+SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
+           "lizard_attn_workspace_bytes", "lizard_attn_status_string")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("M", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("mix", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LizardError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"lizard_attn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library (once); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m "
+                           "gated_linear_attention_chunkwise_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    SP = ctypes.POINTER(Shape)
+    lib.lizard_attn_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_fwd.restype = I32
+    lib.lizard_attn_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_bwd.restype = I32
+    lib.lizard_attn_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.lizard_attn_decode_step.restype = I32
+    lib.lizard_attn_workspace_bytes.argtypes = [SP, ctypes.c_int]
+    lib.lizard_attn_workspace_bytes.restype = SZ
+    lib.lizard_attn_status_string.argtypes = [I32]
+    lib.lizard_attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(code: int):
+    if code != 0:
+        raise LizardError(code, load().lizard_attn_status_string(code).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return LIZARD_BF16
+    if dt == torch.float32:
+        return LIZARD_FP32
+    raise TypeError(f"unsupported dtype {dt}: use torch.bfloat16 or torch.float32")
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _opt(t, name, dtype, device):
+    if t is not None:
+        _need(t, name, dtype, device)
+
+
+def make_shape(B, H, L, d, W, M, scale, mix, dtype, chunk=64) -> Shape:
+    return Shape(B, H, L, d, d, W, M, chunk, float(scale), float(mix), _dtype_code(dtype))
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: float | None = None,
+                    mix: float = 1.0, chunk: int = 64, want_lse: bool = False,
+                    want_o_swa: bool = False, want_chunk_states: bool = False,
+                    want_state: bool = False) -> dict:
+    """Forward pass; q, k, v [B,H,L,d] (bf16 or fp32), g [B,H,L,d] fp32, meta_k [H,M,d]."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, n, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, L, d = q.shape
+    M = 0 if meta_k is None else meta_k.shape[1]
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, v, g must share one [B,H,L,d] shape")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk)
+    NC = (L + 63) // 64
+    out = {"o": torch.empty_like(q)}
+    out["lse"] = torch.empty(B, H, L, device=dev, dtype=torch.float32) if want_lse else None
+    out["o_swa"] = torch.empty_like(q) if want_o_swa else None
+    out["chunk_states"] = (torch.empty(B, H, NC, d, d, device=dev, dtype=dt)
+                           if want_chunk_states else None)
+    out["state"] = torch.empty(B, H, d, d, device=dev, dtype=torch.float32) if want_state else None
+    _check(lib.lizard_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(meta_k),
+                               _ptr(meta_v), _ptr(out["o"]), _ptr(out["lse"]), _ptr(out["o_swa"]),
+                               _ptr(out["chunk_states"]), _ptr(out["state"]), None, 0, _stream(dev)))
+    return out
+
+
+def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *, window: int,
+                    scale: float | None = None, mix: float = 1.0, chunk: int = 64) -> dict:
+    """Backward pass from the saved forward tensors; returns dq, dk, dv, dg, dmeta_k, dmeta_v."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO), ("o_swa", o_swa),
+                 ("chunk_states", chunk_states)):
+        _need(t, n, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, L, d = q.shape
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk)
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD)
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dg": torch.empty_like(g)}
+    out["dmeta_k"] = torch.empty(H, M, d, device=dev, dtype=torch.float32) if M > 0 else None
+    out["dmeta_v"] = (torch.empty(H, M, d, device=dev, dtype=torch.float32)
+                      if (meta_v is not None and M > 0) else None)
+    if M == 0:
+        meta_v = None
+    _check(lib.lizard_attn_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(meta_k),
+                               _ptr(meta_v), _ptr(dO), _ptr(lse), _ptr(o_swa), _ptr(chunk_states),
+                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                               _ptr(out["dmeta_k"]), _ptr(out["dmeta_v"]), _ptr(ws), ws_bytes,
+                               _stream(dev)))
+    return out
+
+
+def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
+                            window: int, scale: float | None = None, mix: float = 1.0, out=None):
+    """One decode step, in place on (state, ring_k, ring_v, pos); returns o [B,H,d]."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v)):
+        _need(t, n, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    _need(pos, "pos", torch.int32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, d = q.shape
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, 0, d, window, M, scale, mix, dt)
+    o = torch.empty_like(q) if out is None else out
+    _check(lib.lizard_attn_decode_step(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(meta_k), _ptr(meta_v), _ptr(state), _ptr(ring_k),
+                                       _ptr(ring_v), _ptr(pos), _ptr(o), _stream(dev)))
+    return o
+
+
+def workspace_bytes(shape: Shape, op: int) -> int:
+    return int(load().lizard_attn_workspace_bytes(ctypes.byref(shape), op))
+
+
+# short aliases
+fwd = lizard_attn_fwd
+bwd = lizard_attn_bwd
+decode_step = lizard_attn_decode_step

@@ -1,0 +1,156 @@
+// lz_api.cpp -- C ABI of the hybrid attention library: validation and launch.
+//
+// Host code only.  Every entry point validates its arguments completely
+// before the first HIP call, so an invalid call launches nothing and writes
+// nothing; kernels are then enqueued on the caller's stream without any
+// synchronisation or allocation.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/lizard_attn.h"
+#include "lz_kernels.hpp"
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kMaxMeta = 16;
+constexpr int kMaxDecodeWindow = 8192;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks common to all ops.  `need_L` is false for decode.
+lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
+  if (s == nullptr) return LIZARD_EINVAL;
+  if (s->B < 1 || s->H < 1 || s->d_k < 1 || s->d_v < 1 || s->W < 1 || s->M < 0) return LIZARD_EINVAL;
+  if (op != LIZARD_OP_DECODE && s->L < 0) return LIZARD_EINVAL;
+  if (!isfinite(s->scale) || !isfinite(s->mix)) return LIZARD_EINVAL;
+  if (s->dtype != LIZARD_FP32 && s->dtype != LIZARD_BF16) return LIZARD_EUNSUPPORTED;
+  if (s->d_k != s->d_v) return LIZARD_EUNSUPPORTED;
+  const int d = s->d_k;
+  if (d != 64 && d != 128) return LIZARD_EUNSUPPORTED;
+  if (s->M > kMaxMeta) return LIZARD_EUNSUPPORTED;
+  if (op == LIZARD_OP_DECODE) {
+    if (s->W > kMaxDecodeWindow) return LIZARD_EUNSUPPORTED;
+  } else {
+    if (s->chunk != 0 && s->chunk != kChunk) return LIZARD_EUNSUPPORTED;
+    if (s->W > 2 * kChunk + 1) return LIZARD_EUNSUPPORTED;     // window spans at most 3 chunks
+    if (s->dtype == LIZARD_FP32 && d != 64) return LIZARD_EUNSUPPORTED;
+  }
+  // every tensor of the call must be addressable with 64-bit offsets and
+  // the grid must fit one launch
+  const double elems = (double)s->B * s->H * (op == LIZARD_OP_DECODE ? s->W : (s->L > 0 ? s->L : 1)) * d;
+  if (elems > 9.0e15) return LIZARD_EUNSUPPORTED;
+  if ((double)s->B * s->H * (d / 16) > 2.0e9) return LIZARD_EUNSUPPORTED;
+  return LIZARD_OK;
+}
+
+lizard_status_t check_ptrs(std::initializer_list<const void*> required,
+                           std::initializer_list<const void*> optional) {
+  for (const void* p : required)
+    if (p == nullptr) return LIZARD_EINVAL;
+  for (const void* p : required)
+    if (!aligned16(p)) return LIZARD_EALIGN;
+  for (const void* p : optional)
+    if (p != nullptr && !aligned16(p)) return LIZARD_EALIGN;
+  return LIZARD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lizard_attn_status_string(lizard_status_t st) {
+  switch (st) {
+    case LIZARD_OK: return "ok";
+    case LIZARD_EINVAL: return "invalid argument (null pointer, bad size or inconsistent optional pair)";
+    case LIZARD_EUNSUPPORTED: return "unsupported size, dtype or parameter";
+    case LIZARD_EALIGN: return "pointer not 16-byte aligned";
+    case LIZARD_EWORKSPACE: return "workspace missing or too small";
+    case LIZARD_EHIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
+  if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE) return 0;
+  if (check_shape(s, op) != LIZARD_OK) return 0;
+  if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k);
+  return 0;
+}
+
+lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const void* meta_k, const void* meta_v,
+                                void* o, float* lse, void* o_swa, void* chunk_states,
+                                float* state_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  // L = 0: the sequence tensors are empty (possibly NULL); only state_out is written (zero)
+  if (s->L > 0)
+    st = check_ptrs({q, k, v, g, o}, {meta_k, meta_v, lse, o_swa, chunk_states, state_out});
+  else
+    st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out});
+  if (st != LIZARD_OK) return st;
+  if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
+  lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
+                s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
+  return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const void* meta_k, const void* meta_v, const void* dO,
+                                const float* lse, const void* o_swa, const void* chunk_states,
+                                void* dq, void* dk, void* dv, float* dg,
+                                float* dmeta_k, float* dmeta_v,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_BWD);
+  if (st != LIZARD_OK) return st;
+  if ((meta_v == nullptr) != (dmeta_v == nullptr)) return LIZARD_EINVAL;
+  if (s->M > 0 && (meta_k == nullptr || dmeta_k == nullptr)) return LIZARD_EINVAL;
+  if (s->L > 0)
+    st = check_ptrs({q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg},
+                    {meta_k, meta_v, dmeta_k, dmeta_v, workspace});
+  else   // L = 0: only the meta gradients (zero) are written
+    st = check_ptrs({}, {q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg,
+                         meta_k, meta_v, dmeta_k, dmeta_v, workspace});
+  if (st != LIZARD_OK) return st;
+  const size_t need = lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
+  lz::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g;
+  a.meta_k = meta_k; a.meta_v = s->M > 0 ? meta_v : nullptr; a.dO = dO;
+  a.lse = lse; a.o_swa = o_swa; a.chunk_states = chunk_states;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
+  a.dmeta_k = s->M > 0 ? dmeta_k : nullptr;
+  a.dmeta_v = s->M > 0 ? dmeta_v : nullptr;
+  a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
+  a.scale = s->scale; a.mix = s->mix;
+  if (need > 0) {
+    const size_t nd = (size_t)s->B * s->H * s->L;
+    a.ws_delta = static_cast<float*>(workspace);
+    a.ws_dmeta = static_cast<float*>(workspace) + ((nd + 63) / 64) * 64;
+  }
+  return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
+                                        const void* q, const void* k, const void* v,
+                                        const float* g, const void* meta_k, const void* meta_v,
+                                        float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                        void* o, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v});
+  if (st != LIZARD_OK) return st;
+  lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
+                   s->B, s->H, s->W, s->M, s->scale, s->mix};
+  return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+}  // extern "C"

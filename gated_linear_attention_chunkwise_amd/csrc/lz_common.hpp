@@ -1,0 +1,129 @@
+// lz_common.hpp -- device helpers shared by the gfx950 kernels.
+//
+// Matrix-core convention used everywhere: one 16x16 output block per
+// v_mfma_f32_16x16x32_bf16 (bf16 operands) or per eight v_mfma_f32_16x16x4_f32
+// (fp32 operands), reduced over a K block of 32.  For both operand types a
+// lane l of the 64-wide wave supplies, for row (A) or column (B) r = l & 15,
+// the eight K values of "slot group" kg = l >> 4; the accumulator lane l
+// holds C[4*kg + i][l & 15], i = 0..3.
+//
+// The K order inside a block is free as long as A and B agree, which lets an
+// accumulator be fed back as an operand: a score tile computed transposed
+// (keys as rows) leaves lane l with scores of query l & 15 against keys
+// 16*kb + 4*kg + i; two such key blocks (kb0, kb1) form one K=32 operand
+// whose slot s maps to key 16*kb_{s/4} + 4*kg + (s % 4).  The matching
+// operand on the other side is then read with ld_frag_perm().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lz {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+struct bf16_t { uint16_t bits; };   // storage tag for bf16 tensors in global memory
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;                 // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// ---------------------------------------------------------------- type traits
+template <typename T> struct Tr;
+
+template <> struct Tr<float> {
+  using frag = f32x8;
+  static constexpr int PAD = 4;      // row padding in LDS (elements): 16 bytes
+  static constexpr int VEC = 4;      // elements per 16-byte vector
+  __device__ static float to_f(float x) { return x; }
+  __device__ static float from_f(float x) { return x; }
+};
+
+template <> struct Tr<bf16_t> {
+  using frag = bf16x8;
+  static constexpr int PAD = 8;
+  static constexpr int VEC = 8;
+  __device__ static float to_f(bf16_t x) { return bf2f(x.bits); }
+  __device__ static bf16_t from_f(float x) { return bf16_t{f2bf(x)}; }
+};
+
+// ------------------------------------------------------------------ MFMA core
+__device__ __forceinline__ void mma32(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x4& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+// Eight consecutive K values of row `row` of an LDS tile stored [row][k].
+__device__ __forceinline__ bf16x8 ld_frag(const bf16_t* base, int ld, int row, int k) {
+  return *reinterpret_cast<const bf16x8*>(base + row * ld + k);
+}
+__device__ __forceinline__ f32x8 ld_frag(const float* base, int ld, int row, int k) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(base + row * ld + k);
+  f32x4 a = p[0], b = p[1];
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Operand matching an accumulator-fed operand over key blocks (kb0, kb1):
+// slots 0..3 <- base[row][16*kb0 + 4*kg .. +4], slots 4..7 <- base[row][16*kb1 + 4*kg .. +4].
+__device__ __forceinline__ bf16x8 ld_frag_perm(const bf16_t* base, int ld, int row, int kb0, int kb1, int kg) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(base + row * ld + 16 * kb0 + 4 * kg);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(base + row * ld + 16 * kb1 + 4 * kg);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x8 ld_frag_perm(const float* base, int ld, int row, int kb0, int kb1, int kg) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(base + row * ld + 16 * kb0 + 4 * kg);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(base + row * ld + 16 * kb1 + 4 * kg);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Accumulators of key blocks kb0, kb1 as an operand (slot order as above).
+__device__ __forceinline__ void pack_acc(bf16x8& out, const f32x4& a, const f32x4& b) {
+  out = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+               (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+}
+__device__ __forceinline__ void pack_acc(f32x8& out, const f32x4& a, const f32x4& b) {
+  out = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Four consecutive values from an accumulator to an LDS row (8 or 16 bytes).
+__device__ __forceinline__ void st4(bf16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// ------------------------------------------------------- 16-byte global I/O
+struct alignas(16) V16 { uint32_t w[4]; };
+
+template <typename T>
+__device__ __forceinline__ V16 ldg16(const T* p) { return *reinterpret_cast<const V16*>(p); }
+template <typename T>
+__device__ __forceinline__ void stg16(T* p, const V16& v) { *reinterpret_cast<V16*>(p) = v; }
+__device__ __forceinline__ V16 zero16() { return V16{{0u, 0u, 0u, 0u}}; }
+
+// Element e of a 16-byte vector of T, as float.
+__device__ __forceinline__ float v16_get(const V16& v, int e, float*) { return __uint_as_float(v.w[e]); }
+__device__ __forceinline__ float v16_get(const V16& v, int e, bf16_t*) {
+  return bf2f(uint16_t((v.w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+}
+
+// ------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, WAVE)); }
+__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, WAVE); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+}  // namespace lz

@@ -127,3 +127,31 @@ def make_small(B: int, H: int, L: int, D: int, M: int, *, seed: int, bf16: bool,
             if name in out:
                 out[name] = round_to_bf16(out[name])
     return out
+
+
+def make_inputs_device(w: Workload, device, *, with_grad: bool = False, L: int | None = None,
+                       B: int | None = None) -> dict:
+    """Same recipe drawn on the device with a seeded torch generator (for the
+    full-size workloads, whose host-side generation would take minutes).
+
+    Returns torch tensors on ``device``: q, k, v (and dO) in the workload's
+    dtype, g fp32 (logsigmoid evaluated in fp64), meta_k [H,M,D].
+    """
+    import torch
+    L = w.L if L is None else L
+    B = w.B if B is None else B
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shp = (B, w.H, L, w.D)
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name] = (torch.randn(shp, generator=gen, device=device, dtype=torch.float32) / 8.0).to(dt)
+    x = torch.randn(shp, generator=gen, device=device, dtype=torch.float64) + w.x_mean
+    out["g"] = (torch.nn.functional.logsigmoid(x) / 16.0).to(torch.float32)
+    del x
+    out["meta_k"] = (torch.randn((w.H, w.M, w.D), generator=gen, device=device,
+                                 dtype=torch.float32) / 8.0).to(dt)
+    if with_grad:
+        out["dO"] = torch.randn(shp, generator=gen, device=device, dtype=torch.float32).to(dt)
+    return out

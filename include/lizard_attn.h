@@ -1,0 +1,143 @@
+/*
+ * lizard_attn.h -- C ABI of the MI355X (gfx950) hybrid attention library.
+ *
+ * The layer is the hybrid attention of "Lizard: An Efficient Linearization
+ * Framework for Large Language Models" as described on the gist.science
+ * explainer pages (English page, section 2.A "Hybrid Attention Architecture"
+ * and section 2.C "Hardware-Aware Algorithm"):
+ *
+ *   GLA branch     S_t = diag(exp g_t) S_{t-1} + k_t^T v_t,  o^gla_t = q_t S_t
+ *                  (gate Gamma_t = diag(exp g_t), given in log space, one
+ *                  value per key dimension; zero initial state)
+ *   anchor window  o^swa_t = softmax over { scale*q_t.mk_m : m < M } and
+ *                  { scale*q_t.k_s : t-W < s <= t } applied to [mv ; v]
+ *                  (meta keys are sinks; meta values are zero when meta_v is
+ *                  NULL, the pages' reading that meta tokens add no value)
+ *   output         o_t = o^gla_t + mix * o^swa_t    (section 2.A, "Final Output")
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *   library never allocates or frees device memory, never synchronises the
+ *   stream and keeps no global mutable state: calls are re-entrant and
+ *   thread-safe; calls that overlap on the same output buffers race.
+ * - All tensors are dense row-major ("contiguous") in the shapes given:
+ *     q, k, o, dq, dk, dO : [B,H,L,d_k]      v, dv : [B,H,L,d_v]
+ *     g, dg               : [B,H,L,d_k] fp32 (log-gates, g <= 0)
+ *     meta_k              : [H,M,d_k]        meta_v: [H,M,d_v] or NULL
+ *     lse                 : [B,H,L] fp32     o_swa : [B,H,L,d_v]
+ *     chunk_states        : [B,H,ceil(L/chunk),d_k,d_v]  (state entering each chunk)
+ *     state, state_out    : [B,H,d_k,d_v] fp32
+ *     ring_k, ring_v      : [B,H,W,d_k] / [B,H,W,d_v]    pos : [B] int32
+ *   "dtype" tensors (q, k, v, o, meta_k, meta_v, dO, dq, dk, dv, o_swa,
+ *   chunk_states, ring_k, ring_v) are fp32 or bf16 as lizard_attn_shape_t
+ *   says; gates, lse, dg, dmeta_* and the decode state are always fp32.
+ * - Every pointer must be 16-byte aligned.
+ * - Validation runs on the host before any launch.  On any error nothing is
+ *   launched and no output is written; the return value says why.  A launch
+ *   failure returns LIZARD_EHIP.  Faults inside kernels surface, as usual
+ *   for HIP, at the caller's next synchronisation.
+ * - Supported: d_k = d_v in {64, 128}; chunk in {64} (0 selects 64);
+ *   W >= 1; 0 <= M <= 16; B, H >= 1; L >= 0 (L = 0 is a no-op).
+ *   Numerical domain: within one chunk the cumulative log-gate of every key
+ *   dimension must stay above -80 (the gate factors are exponentiated in
+ *   fp32 relative to the chunk's midpoint); typical gates are far inside.
+ */
+#ifndef LIZARD_ATTN_H
+#define LIZARD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIZARD_OK = 0,
+  LIZARD_EINVAL = 1,        /* null pointer, negative size, meta_v/dmeta_v mismatch */
+  LIZARD_EUNSUPPORTED = 2,  /* a size or dtype outside the supported set above */
+  LIZARD_EALIGN = 3,        /* a pointer not 16-byte aligned */
+  LIZARD_EWORKSPACE = 4,    /* workspace missing or smaller than required */
+  LIZARD_EHIP = 5           /* a HIP launch or runtime call failed */
+} lizard_status_t;
+
+typedef enum { LIZARD_FP32 = 0, LIZARD_BF16 = 1 } lizard_dtype_t;
+
+typedef struct {
+  int32_t B, H, L;          /* batch, heads, sequence length (L unused by decode) */
+  int32_t d_k, d_v;         /* head dims; must be equal */
+  int32_t W;                /* window length, counting the current token */
+  int32_t M;                /* meta-memory tokens */
+  int32_t chunk;            /* chunk length of the chunkwise form; 0 -> 64 */
+  float scale;              /* softmax logit scale, normally 1/sqrt(d_k) */
+  float mix;                /* alpha in o = o_gla + alpha * o_swa */
+  int32_t dtype;            /* lizard_dtype_t */
+} lizard_attn_shape_t;
+
+enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2 };
+
+/* Bytes of device workspace that `op` needs for shape `s` (0 when none, or
+ * when `s` is invalid).  Pass at least this many bytes to the call. */
+size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op);
+
+/* Forward pass (training or prefill): GLA branch in the chunkwise form with
+ * log-space gate handling (English page §2.C: the cumulative gate is folded
+ * into q and k so the core is a plain matrix product) plus the anchor window
+ * (English page §2.A).
+ *   o                 [B,H,L,d_v] output (written)
+ *   lse          opt  [B,H,L] fp32, log-sum-exp of each window softmax row
+ *   o_swa        opt  [B,H,L,d_v] window branch before mixing
+ *   chunk_states opt  state entering every chunk (needed by lizard_attn_bwd)
+ *   state_out    opt  [B,H,d_k,d_v] fp32 state after the last token (decode hand-off)
+ * NULL optional outputs are not written.  No workspace is needed today
+ * (workspace may be NULL with workspace_bytes 0). */
+lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const void* meta_k, const void* meta_v,
+                                void* o, float* lse, void* o_swa, void* chunk_states,
+                                float* state_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward pass: exact gradients of sum(dO * o) (the pages give no backward;
+ * the formulas are the derivative of the forward above).
+ *   lse, o_swa, chunk_states   required, as written by lizard_attn_fwd on the
+ *                              same inputs
+ *   dq, dk, dv                 written (dtype)
+ *   dg                         written, fp32 [B,H,L,d_k]
+ *   dmeta_k                    written, fp32 [H,M,d_k] (summed over batch)
+ *   dmeta_v                    fp32 [H,M,d_v]; must be NULL iff meta_v is NULL
+ *   workspace                  lizard_attn_workspace_bytes(s, LIZARD_OP_BWD) bytes */
+lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const void* meta_k, const void* meta_v, const void* dO,
+                                const float* lse, const void* o_swa, const void* chunk_states,
+                                void* dq, void* dk, void* dv, float* dg,
+                                float* dmeta_k, float* dmeta_v,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One constant-memory decode step for every sequence (English page §4,
+ * "Efficiency": constant memory at any length; French page §2.A: O(1)
+ * inference by updating an incremental hidden state).
+ *   q, k [B,H,d_k], v [B,H,d_v] (dtype), g [B,H,d_k] fp32: the new token
+ *   state  in/out: S <- diag(exp g) S + k^T v (fp32)
+ *   ring_k, ring_v in/out: the new key/value is stored in slot pos[b] mod W
+ *   pos    in/out, device int32 [B]: tokens already consumed; incremented
+ *   o      [B,H,d_v] written: q S + mix * softmax over M meta keys and the
+ *          min(pos+1, W) filled ring slots.
+ * Uses s->B, H, d_k, d_v, W, M, scale, mix, dtype; s->L and s->chunk are ignored. */
+lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
+                                        const void* q, const void* k, const void* v,
+                                        const float* g, const void* meta_k, const void* meta_v,
+                                        float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                        void* o, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* lizard_attn_status_string(lizard_status_t st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIZARD_ATTN_H */

@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid calls on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_attention_chunkwise_amd as pkg
+from gated_linear_attention_chunkwise_amd._lib import Shape, load
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lizard_attn.h")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = range(6)
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_attn_[a-z_]+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkg._lib.LIB_PATH):
+        pytest.skip("library not built")
+    return load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
+                          "lizard_attn_workspace_bytes", "lizard_attn_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(pkg.SYMBOLS) == set(names)
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.lizard_attn_status_string(code)
+    assert b"unknown" in lib.lizard_attn_status_string(99)
+
+
+def shape(**kw):
+    base = dict(B=1, H=2, L=128, d_k=128, d_v=128, W=128, M=4, chunk=64, scale=0.088, mix=1.0,
+                dtype=1)
+    base.update(kw)
+    return Shape(*(base[f] for f, _ in Shape._fields_))
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)          # aligned, never dereferenced (validation fails first)
+BAD = P(0x10008)           # 8-byte aligned only
+
+
+def fwd(lib, s, q=GOOD, meta_k=GOOD, meta_v=None, o=GOOD, lse=None):
+    return lib.lizard_attn_fwd(ctypes.byref(s), q, GOOD, GOOD, GOOD, meta_k, meta_v, o, lse, None,
+                               None, None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_k=96, d_v=96), EUNSUPPORTED), (dict(d_k=64, d_v=128), EUNSUPPORTED),
+    (dict(dtype=7), EUNSUPPORTED), (dict(dtype=0, d_k=128, d_v=128), EUNSUPPORTED),
+    (dict(M=17), EUNSUPPORTED), (dict(W=130), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED),
+    (dict(B=0), EINVAL), (dict(L=-1), EINVAL), (dict(W=0), EINVAL), (dict(M=-1), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+])
+def test_fwd_rejects_bad_shapes(lib, kw, code):
+    assert fwd(lib, shape(**kw)) == code
+
+
+def test_fwd_rejects_bad_pointers(lib):
+    assert lib.lizard_attn_fwd(None, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None, None, None,
+                               None, None, 0, None) == EINVAL
+    assert fwd(lib, shape(), q=None) == EINVAL
+    assert fwd(lib, shape(), o=None) == EINVAL
+    assert fwd(lib, shape(), meta_k=None) == EINVAL          # M > 0 needs meta keys
+    assert fwd(lib, shape(), q=BAD) == EALIGN
+    assert fwd(lib, shape(), lse=BAD) == EALIGN
+
+
+def test_bwd_validation(lib):
+    s = shape()
+    def call(meta_v=None, dmeta_v=None, ws=GOOD, ws_bytes=1 << 40, dq=GOOD, dmeta_k=GOOD):
+        return lib.lizard_attn_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, meta_v, GOOD,
+                                   GOOD, GOOD, GOOD, dq, GOOD, GOOD, GOOD, dmeta_k, dmeta_v, ws,
+                                   ws_bytes, None)
+    assert call(meta_v=GOOD, dmeta_v=None) == EINVAL
+    assert call(meta_v=None, dmeta_v=GOOD) == EINVAL
+    assert call(dq=None) == EINVAL
+    assert call(dmeta_k=None) == EINVAL
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 1)
+    if need > 0:
+        assert call(ws=None) == EWORKSPACE
+        assert call(ws_bytes=need - 1) == EWORKSPACE
+
+
+def test_decode_validation(lib):
+    s = shape(L=0)
+    def call(state=GOOD, pos=GOOD, s_=s):
+        return lib.lizard_attn_decode_step(ctypes.byref(s_), GOOD, GOOD, GOOD, GOOD, GOOD, None,
+                                           state, GOOD, GOOD, pos, GOOD, None)
+    assert call(state=None) == EINVAL
+    assert call(pos=None) == EINVAL
+    assert call(pos=BAD) == EALIGN
+    assert call(s_=shape(W=9000)) == EUNSUPPORTED
+
+
+def test_workspace_query(lib):
+    assert lib.lizard_attn_workspace_bytes(None, 1) == 0
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(d_k=96, d_v=96)), 1) == 0
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 0) == 0
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 2) == 0
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 5) == 0

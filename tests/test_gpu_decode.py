@@ -1,0 +1,90 @@
+"""GPU parity of lizard_attn_decode_step: prefill (GPU forward) then decode
+steps, checked against the oracle's full-sequence forward at the same
+positions (decode after prefill must equal the full-sequence output)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lizard_oracle as orc
+from gated_linear_attention_chunkwise_amd import lizard_attn_decode_step, lizard_attn_fwd
+from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device, make_small
+from helpers import TOL, dev, host, rel_l2, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def prefill_handoff(q, k, v, g, mk, mv, W, scale, mix):
+    """GPU forward over the prefix, then the decode state: final GLA state,
+    ring slots t mod W for the last min(L, W) tokens, pos = L."""
+    B, H, L, D = q.shape
+    ring_k = torch.zeros(B, H, W, D, device=q.device, dtype=q.dtype)
+    ring_v = torch.zeros_like(ring_k)
+    if L > 0:
+        out = lizard_attn_fwd(q, k, v, g, mk, mv, window=W, scale=scale, mix=mix, want_state=True)
+        state = out["state"]
+        ts = torch.arange(max(0, L - W), L, device=q.device)
+        ring_k[:, :, ts % W] = k[:, :, ts]
+        ring_v[:, :, ts % W] = v[:, :, ts]
+    else:
+        state = torch.zeros(B, H, D, D, device=q.device, dtype=torch.float32)
+    pos = torch.full((B,), L, device=q.device, dtype=torch.int32)
+    return state, ring_k, ring_v, pos
+
+
+@pytest.mark.parametrize("dtname,D", [("fp32", 64), ("bf16", 64), ("bf16", 128), ("fp32", 128)])
+@pytest.mark.parametrize("L0,steps,W,M,with_mv", [(20, 12, 8, 2, False), (3, 10, 8, 4, True),
+                                                  (0, 9, 4, 0, False), (70, 20, 128, 4, False),
+                                                  (130, 5, 129, 16, True)])
+def test_decode_after_prefill(dtname, D, L0, steps, W, M, with_mv):
+    x = make_small(3, 2, L0 + steps, D, M, seed=L0 + 31 * steps + W, bf16=(dtname == "bf16"),
+                   with_grad=False, with_meta_v=with_mv)
+    dt = tdtype(dtname)
+    scale, mix = 1.0 / math.sqrt(D), 0.75
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk = dev(x["meta_k"], dt) if M > 0 else None
+    mv = dev(x["meta_v"], dt) if with_mv else None
+    pre = L0 if not (dtname == "fp32" and D == 128) else 0   # fp32 forward supports d=64 only
+    state, rk, rv, pos = prefill_handoff(*(T[n][:, :, :pre].contiguous() for n in "qkvg"),
+                                         mk, mv, W, scale, mix)
+    outs = []
+    for t in range(pre, L0 + steps):
+        o = lizard_attn_decode_step(*(T[n][:, :, t].contiguous() for n in "qkvg"), mk, mv,
+                                    state, rk, rv, pos, window=W, scale=scale, mix=mix)
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = torch.stack(outs, 2)
+    ref = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], x.get("meta_v"),
+                             window=W, scale=scale, mix=mix)
+    e_o = rel_l2(host(got), ref["o"][:, :, pre:])
+    e_s = rel_l2(host(state), ref["state"])
+    print(dtname, D, L0, steps, W, M, f"o {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= TOL[dtname] and e_s <= TOL[dtname]
+    assert (pos.cpu().numpy() == L0 + steps).all()
+
+
+def test_decode_b64_full_size_sampled():
+    """4096-token prefill + 1024 decode steps at B=64, H=32, d=128, W=128, M=4."""
+    w = WORKLOADS["decode_b64"]
+    x = make_inputs_device(w, "cuda")
+    P, L = w.prefill, w.L
+    state, rk, rv, pos = prefill_handoff(*(x[n][:, :, :P].contiguous() for n in "qkvg"),
+                                         x["meta_k"], None, w.W, w.scale, 1.0)
+    outs = torch.empty(L - P, w.B, w.H, w.D, device="cuda", dtype=torch.bfloat16)
+    for t in range(P, L):
+        lizard_attn_decode_step(*(x[n][:, :, t].contiguous() for n in "qkvg"), x["meta_k"], None,
+                                state, rk, rv, pos, window=w.W, scale=w.scale, mix=1.0,
+                                out=outs[t - P])
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (63, 31), (17, 5)]:
+        sl = lambda n: x[n][b:b + 1, h:h + 1].float().cpu().numpy()
+        ref = orc.hybrid_forward(sl("q"), sl("k"), sl("v"), sl("g"),
+                                 x["meta_k"][h:h + 1].float().cpu().numpy(), None,
+                                 window=w.W, scale=w.scale)
+        e_o = rel_l2(host(outs[:, b, h]), ref["o"][0, 0, P:])
+        e_s = rel_l2(host(state[b:b + 1, h:h + 1]), ref["state"])
+        print("decode_b64", (b, h), f"o {e_o:.2e} state {e_s:.2e}", flush=True)
+        assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+    assert (pos.cpu().numpy() == L).all()
