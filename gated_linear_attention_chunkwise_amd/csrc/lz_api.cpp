@@ -74,7 +74,7 @@ const char* lizard_attn_status_string(lizard_status_t st) {
 size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
   if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE) return 0;
   if (check_shape(s, op) != LIZARD_OK) return 0;
-  if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k);
+  if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   return 0;
 }
 
@@ -119,7 +119,7 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
     st = check_ptrs({}, {q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg,
                          meta_k, meta_v, dmeta_k, dmeta_v, workspace});
   if (st != LIZARD_OK) return st;
-  const size_t need = lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k);
+  const size_t need = lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   lz::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g;
@@ -130,11 +130,7 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
   a.dmeta_v = s->M > 0 ? dmeta_v : nullptr;
   a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
   a.scale = s->scale; a.mix = s->mix;
-  if (need > 0) {
-    const size_t nd = (size_t)s->B * s->H * s->L;
-    a.ws_delta = static_cast<float*>(workspace);
-    a.ws_dmeta = static_cast<float*>(workspace) + ((nd + 63) / 64) * 64;
-  }
+  a.workspace = workspace;
   return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 

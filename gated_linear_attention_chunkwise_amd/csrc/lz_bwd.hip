@@ -1,17 +1,834 @@
-// lz_bwd.hip -- backward pass (placeholder until the kernels land).
+// lz_bwd.hip -- backward pass of the Lizard hybrid attention layer on gfx950.
+//
+// The explainer pages ("Lizard: An Efficient Linearization Framework for
+// Large Language Models", gist.science) give no backward; these kernels
+// compute the exact gradient of the forward in lz_fwd.hip.  With the gate
+// folded into q and k inside each chunk (b = chunk-local inclusive cumsum of
+// g, q~ = q e^b, k^ = k e^-b, Gamma = b at the chunk end) the chunk maps
+//   O   = (q~ k^T  masked s<=t) V + q~ S_prev,      S = e^Gamma (S_prev + k^T V)
+// and, writing dS for dL/dS (from later chunks) and dS' = e^Gamma * dS (rows),
+//   dq~ = (dO V^T masked) k^ + dO S_prev^T          dq = dq~ e^b
+//   dk^ = (dO V^T masked)^T q~ + V dS'^T            dk = dk^ e^-b
+//   dv  = (q~ k^T masked)^T dO + k^ dS'
+//   dS_prev = dS' + q~^T dO
+//   dg_r = rowsum(S * dS) + sum_{u >= r in chunk} (q~ dq~ - k^ dk^)_u
+// Only chunk-local gate sums are exponentiated; the chunk-boundary term of
+// dg is the direct rowsum, so no long telescoping sum (which cancels
+// catastrophically in low precision) is ever formed.
+//
+// Kernels, in launch order:
+//   delta_kernel   D_t = mix * dO_t . o_swa_t                       (row dots)
+//   dstate_kernel  reverse sweep over chunks per (b, h, 64-wide d_v tile):
+//                  carries dS in fp32 registers, stores dS' (operand dtype,
+//                  transposed) and the fp32 boundary rowsums per chunk
+//   chunk_kernel   one workgroup per (b, h, chunk): every GLA gradient plus
+//                  the anchor-window gradients (query side for dq, key side
+//                  for dk and dv) and per-chunk meta-key partial sums
+//   dmeta_kernel   deterministic sum of the meta partials over batch and chunks
+#include <type_traits>
+
 #include "lz_common.hpp"
 #include "lz_kernels.hpp"
 
 namespace lz {
+namespace {
 
-size_t bwd_workspace_bytes(int B, int H, int L, int M, int D) {
-  (void)B; (void)H; (void)L; (void)M; (void)D;
-  return 0;
+constexpr int C = 64;
+constexpr int NTHR = 256;
+constexpr int DVTA = 64;   // d_v tile of the state-gradient sweep
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t delta, dS, bnd, dmeta, total;
+};
+
+WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
+  const size_t NC = (size_t)(L + C - 1) / C;
+  const size_t NJ = (size_t)(D + DVTA - 1) / DVTA;
+  const size_t esz = dtype == 1 ? 2 : 4;
+  WsLayout w{};
+  w.delta = 0;
+  size_t off = round_up(sizeof(float) * (size_t)B * H * L, 256);
+  w.dS = off;
+  off += round_up(esz * (size_t)B * H * NC * D * D, 256);
+  w.bnd = off;
+  off += round_up(sizeof(float) * (size_t)B * H * NC * NJ * D, 256);
+  w.dmeta = off;
+  off += round_up(sizeof(float) * (size_t)B * NC * H * M * 2 * D, 256);
+  w.total = off;
+  return w;
+}
+
+// ------------------------------------------------------------------ delta
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void delta_kernel(const T* __restrict__ dO, const T* __restrict__ o_swa,
+                                                      float* __restrict__ delta, size_t rows, float mix) {
+  constexpr int VEC = Tr<T>::VEC, VPR = D / VEC, RPW = 64 / VPR;
+  const int lane = threadIdx.x & 63;
+  const size_t row = ((size_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6)) * RPW + lane / VPR;
+  const int cv = lane % VPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const V16 a = ldg16(dO + row * D + cv * VEC);
+    const V16 b = ldg16(o_swa + row * D + cv * VEC);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc += v16_get(a, e, (T*)nullptr) * v16_get(b, e, (T*)nullptr);
+  }
+#pragma unroll
+  for (int m = 1; m < VPR; m <<= 1) acc = xor_sum(acc, m);
+  if (row < rows && cv == 0) delta[row] = mix * acc;
+}
+
+// ------------------------------------------------------- shared gate prefix
+// Thread map of a 64 x D chunk tile: column group cg (VEC dims), tokens
+// tg*TPT .. +TPT.  Computes the chunk-local inclusive prefix b of the
+// log-gates held in rg (overwritten with b) and the chunk total Gamma.
+template <int D, int VEC>
+struct ScanMap {
+  static constexpr int VPR = D / VEC;
+  static constexpr int NTG = NTHR / VPR;
+  static constexpr int TPT = C / NTG;
+  static constexpr int GV = VEC / 4;
+};
+
+template <int D, int VEC, int TPT_, int GV_>
+__device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot)[GV_], float* sScan, int cg,
+                                             int tg) {
+  using SM = ScanMap<D, VEC>;
+  static_assert(SM::TPT == TPT_ && SM::GV == GV_, "scan map");
+#pragma unroll
+  for (int u = 1; u < SM::TPT; ++u)
+#pragma unroll
+    for (int e = 0; e < SM::GV; ++e) rg[u][e] += rg[u - 1][e];
+#pragma unroll
+  for (int e = 0; e < SM::GV; ++e)
+    *reinterpret_cast<f32x4*>(sScan + tg * D + cg * VEC + 4 * e) = rg[SM::TPT - 1][e];
+  __syncthreads();
+  f32x4 excl[SM::GV];
+#pragma unroll
+  for (int e = 0; e < SM::GV; ++e) { excl[e] = f32x4{0, 0, 0, 0}; tot[e] = f32x4{0, 0, 0, 0}; }
+  for (int p = 0; p < SM::NTG; ++p) {
+#pragma unroll
+    for (int e = 0; e < SM::GV; ++e) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sScan + p * D + cg * VEC + 4 * e);
+      tot[e] += x;
+      if (p < tg) excl[e] += x;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < SM::TPT; ++u)
+#pragma unroll
+    for (int e = 0; e < SM::GV; ++e) rg[u][e] += excl[e];
+}
+
+// ------------------------------------------------------------ dstate sweep
+template <typename T, int D>
+struct DsLayout {
+  static constexpr int PAD = Tr<T>::PAD;
+  static constexpr int LDC = C + PAD;
+  static constexpr size_t oQtT = 0;                                     // [D][C]   q~^T
+  static constexpr size_t odOT = oQtT + sizeof(T) * D * LDC;            // [DVTA][C] dO^T slice
+  static constexpr size_t oScan = odOT + sizeof(T) * DVTA * LDC;
+  static constexpr size_t oDec = oScan + sizeof(float) * (NTHR / (D / Tr<T>::VEC)) * D;
+  static constexpr size_t bytes = oDec + sizeof(float) * D;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restrict__ wsdS, float* __restrict__ wsbnd) {
+  using LY = DsLayout<T, D>;
+  using SM = ScanMap<D, Tr<T>::VEC>;
+  using frag = typename Tr<T>::frag;
+  constexpr int VEC = Tr<T>::VEC, TPT = SM::TPT, GV = SM::GV;
+  constexpr int NJ = D / DVTA;
+  constexpr int IB = D / 64, JB = DVTA / 16;
+  constexpr int VVR = DVTA / VEC, NVV = (C * VVR + NTHR - 1) / NTHR;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sQtT = reinterpret_cast<T*>(smem + LY::oQtT);
+  T* sdOT = reinterpret_cast<T*>(smem + LY::odOT);
+  float* sScan = reinterpret_cast<float*>(smem + LY::oScan);
+  float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+  const int BH = a.B * a.H;
+  int bh, jt;
+  {
+    const int bid = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int grp = bid / (8 * NJ), x = bid % (8 * NJ);
+      bh = grp * 8 + (x & 7);
+      jt = x >> 3;
+    } else {
+      bh = bid / NJ;
+      jt = bid % NJ;
+    }
+  }
+  const int j0 = jt * DVTA;
+  const int L = a.L, NC = (L + C - 1) / C;
+  const size_t hoff = (size_t)bh * L * D;
+  const T* q = reinterpret_cast<const T*>(a.q) + hoff;
+  const T* dO = reinterpret_cast<const T*>(a.dO) + hoff;
+  const float* g = a.g + hoff;
+  const T* cstates = reinterpret_cast<const T*>(a.chunk_states) + (size_t)bh * NC * D * D;
+  const int cg = tid % SM::VPR, tg = tid / SM::VPR;
+
+  V16 rq[TPT], rd[NVV];
+  f32x4 rg[TPT][GV];
+  auto prefetch = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = c * C + tg * TPT + u;
+      const bool ok = t < L;
+      rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
+#pragma unroll
+      for (int e = 0; e < GV; ++e)
+        rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+      const int idx = tid + u * NTHR;
+      rd[u] = zero16();
+      if (idx < C * VVR) {
+        const int s = idx / VVR, vc = idx % VVR;
+        const int t = c * C + s;
+        if (t < L) rd[u] = ldg16(dO + (size_t)t * D + j0 + vc * VEC);
+      }
+    }
+  };
+
+  f32x4 acc[IB][JB];
+#pragma unroll
+  for (int i = 0; i < IB; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  if (NC > 0) prefetch(NC - 1);
+  for (int c = NC - 1; c >= 0; --c) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+      const int idx = tid + u * NTHR;
+      if (idx < C * VVR) {
+        const int s = idx / VVR, vc = idx % VVR;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) put_bits(sdOT + (vc * VEC + e) * LY::LDC + s, rd[u], e);
+      }
+    }
+    f32x4 tot[GV];
+    chunk_prefix<D, VEC, TPT, GV>(rg, tot, sScan, cg, tg);
+    if (tg == 0)
+#pragma unroll
+      for (int e = 0; e < GV; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sDec[cg * VEC + 4 * e + i] = __expf(tot[e][i]);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float qt = v16_get(rq[u], e, (T*)nullptr) * __expf(rg[u][e >> 2][e & 3]);
+        put_elem(sQtT + (cg * VEC + e) * LY::LDC + tg * TPT + u, qt);
+      }
+    if (c > 0) prefetch(c - 1);
+    __syncthreads();
+
+    // acc holds dS_c (gradient w.r.t. the state after chunk c, from later chunks)
+    T* dst = wsdS + ((size_t)bh * NC + c) * D * D;
+    float* bnd = wsbnd + (((size_t)bh * NC + c) * NJ + jt) * D;
+    const T* Sc = cstates + (size_t)(c + 1) * D * D;     // state after chunk c (valid for c < NC-1)
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {
+      const int i0 = 16 * (w * IB + ib);
+      float dec[4], rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dec[i] = sDec[i0 + 4 * kg + i];
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const int j = j0 + 16 * jb + r;
+        if (c + 1 < NC) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rs[i] += Tr<T>::to_f(Sc[(size_t)(i0 + 4 * kg + i) * D + j]) * acc[ib][jb][i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ib][jb][i] *= dec[i];
+        st4(dst + (size_t)j * D + i0 + 4 * kg, acc[ib][jb][0], acc[ib][jb][1], acc[ib][jb][2], acc[ib][jb][3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) rs[i] = xor_sum(rs[i], m);
+      if (r == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bnd[i0 + 4 * kg + i] = rs[i];
+    }
+    // dS_{c-1} = dS' + q~^T dO
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {
+      const int i0 = 16 * (w * IB + ib);
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks)
+          mma32(acc[ib][jb], ld_frag(sQtT, LY::LDC, i0 + r, 32 * ks + 8 * kg),
+                ld_frag(sdOT, LY::LDC, 16 * jb + r, 32 * ks + 8 * kg));
+    }
+  }
+}
+
+// ------------------------------------------------------------ chunk kernel
+template <typename T, int D>
+struct CkLayout {
+  static constexpr int PAD = Tr<T>::PAD;
+  static constexpr int LDQ = D + PAD;    // [C][D] rows and [D][D] rows
+  static constexpr int LDC = C + PAD;    // [D][C] transposed tiles
+  static constexpr int LDM = 16 + PAD;   // [D][16] meta keys transposed
+  static constexpr size_t oQt = 0;                                   // q~   [C][D]
+  static constexpr size_t oKh = oQt + sizeof(T) * C * LDQ;           // k^   [C][D]
+  static constexpr size_t oEb = oKh + sizeof(T) * C * LDQ;           // e^b  [C][D]
+  static constexpr size_t oQtT = oEb + sizeof(T) * C * LDQ;          // q~^T [D][C]  (later raw q^T)
+  static constexpr size_t oKhT = oQtT + sizeof(T) * D * LDC;         // k^^T [D][C]  (later dO^T of another chunk)
+  static constexpr size_t odOT = oKhT + sizeof(T) * D * LDC;         // dO^T [D][C]
+  static constexpr size_t oBig = odOT + sizeof(T) * D * LDC;         // dS' [D][D] | scan | db | K^T
+  static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * D ? sizeof(T) * D * LDQ
+                                                                                 : sizeof(float) * C * D;
+  static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
+  static constexpr size_t oDLm = oMkT + sizeof(T) * D * LDM;         // dl_meta^T [16][C]
+  static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // p_meta^T  [16][C]
+  static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 chunks (log2 units)
+  static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 chunks
+  static constexpr size_t oCar = oDel + sizeof(float) * 3 * C;       // scan carry [D]
+  static constexpr size_t bytes = oCar + sizeof(float) * D;
+  static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
+                                                         const float* __restrict__ wsbnd) {
+  using LY = CkLayout<T, D>;
+  using SM = ScanMap<D, Tr<T>::VEC>;
+  using frag = typename Tr<T>::frag;
+  constexpr int VEC = Tr<T>::VEC, TPT = SM::TPT, GV = SM::GV;
+  constexpr int NB = D / 16;     // 16-wide blocks over the head dim
+  constexpr int KS = D / 32;     // K steps over the head dim
+  constexpr int NJ = D / DVTA;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
+  T* sKh = reinterpret_cast<T*>(smem + LY::oKh);
+  T* sEb = reinterpret_cast<T*>(smem + LY::oEb);
+  T* sQtT = reinterpret_cast<T*>(smem + LY::oQtT);
+  T* sKhT = reinterpret_cast<T*>(smem + LY::oKhT);
+  T* sdOT = reinterpret_cast<T*>(smem + LY::odOT);
+  T* sdSp = reinterpret_cast<T*>(smem + LY::oBig);
+  float* sScan = reinterpret_cast<float*>(smem + LY::oBig);
+  float* sDb = reinterpret_cast<float*>(smem + LY::oBig);
+  T* sKT = reinterpret_cast<T*>(smem + LY::oBig);
+  T* sMkT = reinterpret_cast<T*>(smem + LY::oMkT);
+  T* sDLm = reinterpret_cast<T*>(smem + LY::oDLm);
+  T* sPm = reinterpret_cast<T*>(smem + LY::oPm);
+  float* sLse = reinterpret_cast<float*>(smem + LY::oLse);
+  float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
+  float* sCar = reinterpret_cast<float*>(smem + LY::oCar);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+  const int L = a.L, NC = (L + C - 1) / C, W = a.W, M = a.M;
+  // workgroup -> (chunk, head); consecutive chunks of one head share an XCD
+  const int BH = a.B * a.H;
+  int bh, c;
+  {
+    const int bid = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int x = bid % 8, y = bid / 8;           // y runs over (head group, chunk)
+      c = y % NC;
+      bh = (y / NC) * 8 + x;
+    } else {
+      bh = bid / NC;
+      c = bid % NC;
+    }
+  }
+  const int b = bh / a.H, h = bh % a.H;
+  const size_t hoff = (size_t)bh * L * D;
+  const T* q = reinterpret_cast<const T*>(a.q) + hoff;
+  const T* k = reinterpret_cast<const T*>(a.k) + hoff;
+  const T* v = reinterpret_cast<const T*>(a.v) + hoff;
+  const T* dO = reinterpret_cast<const T*>(a.dO) + hoff;
+  const float* g = a.g + hoff;
+  const T* Sprev = reinterpret_cast<const T*>(a.chunk_states) + ((size_t)bh * NC + c) * D * D;
+  const T* dSpT = wsdS + ((size_t)bh * NC + c) * D * D;     // dS' transposed [j][i]
+  const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
+  const T* mv = a.meta_v ? reinterpret_cast<const T*>(a.meta_v) + (size_t)h * M * D : nullptr;
+  const float sl2 = a.scale * LOG2E;
+  const float mix = a.mix, scale = a.scale;
+  const int t0 = c * C;
+
+  // ---------------------------------------------------------------- staging
+  const int cg = tid % SM::VPR, tg = tid / SM::VPR;
+  {
+    V16 rq[TPT], rk[TPT], rd[TPT];
+    f32x4 rg[TPT][GV];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = t0 + tg * TPT + u;
+      const bool ok = t < L;
+      rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
+      rk[u] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
+      rd[u] = ok ? ldg16(dO + (size_t)t * D + cg * VEC) : zero16();
+#pragma unroll
+      for (int e = 0; e < GV; ++e)
+        rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
+    }
+    // meta keys transposed, lse / delta of this chunk and the next two
+    for (int e = tid; e < D * 16; e += NTHR) {
+      const int d = e / 16, m = e % 16;
+      put_elem(sMkT + d * LY::LDM + m, m < M ? Tr<T>::to_f(mk[(size_t)m * D + d]) : 0.f);
+    }
+    for (int e = tid; e < 3 * C; e += NTHR) {
+      const int t = t0 + e;
+      sLse[e] = t < L ? a.lse[(size_t)bh * L + t] * LOG2E : 0.f;
+      sDel[e] = t < L ? a.ws_delta[(size_t)bh * L + t] : 0.f;
+    }
+    f32x4 tot[GV];
+    chunk_prefix<D, VEC, TPT, GV>(rg, tot, sScan, cg, tg);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = tg * TPT + u;
+      float qt[VEC], kh[VEC], eb[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float bb = rg[u][e >> 2][e & 3];
+        eb[e] = __expf(bb);
+        qt[e] = v16_get(rq[u], e, (T*)nullptr) * eb[e];
+        kh[e] = v16_get(rk[u], e, (T*)nullptr) * __expf(-bb);
+        put_elem(sQtT + (cg * VEC + e) * LY::LDC + t, qt[e]);
+        put_elem(sKhT + (cg * VEC + e) * LY::LDC + t, kh[e]);
+        put_bits(sdOT + (cg * VEC + e) * LY::LDC + t, rd[u], e);
+      }
+      st_vec(sQt + t * LY::LDQ + cg * VEC, qt);
+      st_vec(sKh + t * LY::LDQ + cg * VEC, kh);
+      st_vec(sEb + t * LY::LDQ + cg * VEC, eb);
+    }
+    __syncthreads();   // scan scratch is dead: stage dS' (row-major) into the same region
+    for (int e = tid; e < D * (D / VEC); e += NTHR) {
+      const int j = e / (D / VEC), cv = e % (D / VEC);
+      const V16 x = ldg16(dSpT + (size_t)j * D + cv * VEC);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) put_bits(sdSp + (cv * VEC + i) * LY::LDQ + j, x, i);
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------ GLA gradients
+  // wave w owns chunk tokens u in [16w, 16w+16): as query rows (accQ) and as key rows (accK, accV)
+  f32x4 accQ[NB], accK[NB], accV[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) { accQ[i] = f32x4{0, 0, 0, 0}; accK[i] = accQ[i]; accV[i] = accQ[i]; }
+  const int urow = t0 + 16 * w + r;     // this lane's token as an operand row
+  {
+    // dq~ intra: dA^T blocks (keys sb <= w, queries of block w), then times k^
+    f32x4 blk[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      blk[sb] = f32x4{0, 0, 0, 0};
+      if (sb <= w) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          mma32(blk[sb], ldg_row_frag<T>(v, D, t0 + 16 * sb + r, 32 * ks + 8 * kg, L),
+                ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L));
+        if (sb == w)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * kg + i > r) blk[sb][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      if (2 * p <= w) {
+        frag op;
+        pack_acc(op, blk[2 * p], blk[2 * p + 1]);
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) mma32(accQ[ib], op, ld_frag_perm(sKhT, LY::LDC, 16 * ib + r, 2 * p, 2 * p + 1, kg));
+      }
+    // dq~ inter: dO S_prev^T
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const frag fo = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib)
+        mma32(accQ[ib], fo, ldg_frag<T>(Sprev + (size_t)(16 * ib + r) * D + 32 * ks + 8 * kg));
+    }
+    // dv intra: A blocks (queries tb >= w, keys of block w), A^T dO
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      blk[tb] = f32x4{0, 0, 0, 0};
+      if (tb >= w) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          mma32(blk[tb], ld_frag(sQt, LY::LDQ, 16 * tb + r, 32 * ks + 8 * kg),
+                ld_frag(sKh, LY::LDQ, 16 * w + r, 32 * ks + 8 * kg));
+        if (tb == w)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * kg + i < r) blk[tb][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      if (2 * p + 1 >= w) {
+        frag op;
+        pack_acc(op, blk[2 * p], blk[2 * p + 1]);
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) mma32(accV[jb], op, ld_frag_perm(sdOT, LY::LDC, 16 * jb + r, 2 * p, 2 * p + 1, kg));
+      }
+    // dk^ intra: dA blocks (queries tb >= w, keys of block w), dA^T q~
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      blk[tb] = f32x4{0, 0, 0, 0};
+      if (tb >= w) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          mma32(blk[tb], ldg_row_frag<T>(dO, D, t0 + 16 * tb + r, 32 * ks + 8 * kg, L),
+                ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L));
+        if (tb == w)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * kg + i < r) blk[tb][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      if (2 * p + 1 >= w) {
+        frag op;
+        pack_acc(op, blk[2 * p], blk[2 * p + 1]);
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) mma32(accK[ib], op, ld_frag_perm(sQtT, LY::LDC, 16 * ib + r, 2 * p, 2 * p + 1, kg));
+      }
+    // inter-chunk: dk^ += V dS'^T ; dv += k^ dS'
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const frag fv = ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L);
+      const frag fk = ld_frag(sKh, LY::LDQ, 16 * w + r, 32 * ks + 8 * kg);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        mma32(accK[nb], fv, ld_frag(sdSp, LY::LDQ, 16 * nb + r, 32 * ks + 8 * kg));
+        mma32(accV[nb], fk, ldg_frag<T>(dSpT + (size_t)(16 * nb + r) * D + 32 * ks + 8 * kg));
+      }
+    }
+  }
+  __syncthreads();   // every wave is done with sdSp: its region now holds the per-token gate gradient
+
+  // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int i = 16 * nb + r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int u = 16 * w + 4 * kg + e;
+      const float qt = Tr<T>::to_f(sQt[u * LY::LDQ + i]);
+      const float kh = Tr<T>::to_f(sKh[u * LY::LDQ + i]);
+      const float eb = Tr<T>::to_f(sEb[u * LY::LDQ + i]);
+      sDb[u * D + i] = qt * accQ[nb][e] - kh * accK[nb][e];
+      accQ[nb][e] *= eb;
+      accK[nb][e] *= 1.f / eb;
+    }
+  }
+  __syncthreads();
+  // reverse cumulative sum over the chunk plus the boundary rowsum -> dg
+  {
+    constexpr int PARTS = NTHR / D;              // threads per column
+    constexpr int SEG = C / PARTS;
+    const int i = tid % D, part = tid / D;
+    float run = 0.f;
+    for (int u = SEG * (part + 1) - 1; u >= SEG * part; --u) {
+      run += sDb[u * D + i];
+      sDb[u * D + i] = run;
+    }
+    __syncthreads();
+    float carry = 0.f;
+    for (int p2 = part + 1; p2 < PARTS; ++p2) carry += sDb[(SEG * p2) * D + i];
+    if (c + 1 < NC)
+      for (int j = 0; j < NJ; ++j) carry += wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + i];
+    for (int u = SEG * part; u < SEG * (part + 1); ++u) {
+      const int t = t0 + u;
+      if (t < L) a.dg[hoff + (size_t)t * D + i] = sDb[u * D + i] + carry;
+    }
+  }
+  __syncthreads();   // sDb dead: the region is reused for key tiles
+
+  // ------------------------------------------- anchor window, query side (dq)
+  frag qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = ldg_row_frag<T>(q, D, urow, 32 * ks + 8 * kg, L);
+    of[ks] = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
+  }
+  const int tq = t0 + 16 * w + r;                  // this lane's query
+  const float lse2 = sLse[16 * w + r], delq = sDel[16 * w + r];
+  const bool qvalid = tq < L;
+  if (M > 0) {
+    f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      mma32(x, ldg_row_frag<T>(mk, D, r, 32 * ks + 8 * kg, M), qf[ks]);
+      if (mv) mma32(dp, ldg_row_frag<T>(mv, D, r, 32 * ks + 8 * kg, M), of[ks]);
+    }
+    f32x4 dl, pm;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * kg + i;
+      const float p = (m < M && qvalid) ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
+      pm[i] = p;
+      dl[i] = p * (mix * dp[i] - delq) * scale;
+      put_elem(sDLm + m * LY::LDC + 16 * w + r, dl[i]);
+      put_elem(sPm + m * LY::LDC + 16 * w + r, p * mix);
+    }
+    frag op;
+    pack_acc(op, dl, f32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int db = 0; db < NB; ++db) mma32(accQ[db], op, ld_frag_perm(sMkT, LY::LDM, 16 * db + r, 0, 0, kg));
+  }
+  const int kt_lo = max(0, t0 - W + 1) / C;
+  const int qlo = t0 + 16 * w;
+  for (int kt = c; kt >= kt_lo; --kt) {
+    const int kbase = kt * C;
+    // K^T tile of chunk kt
+    for (int e = tid; e < C * (D / VEC); e += NTHR) {
+      const int s = e / (D / VEC), cv = e % (D / VEC);
+      const V16 x = (kbase + s < L) ? ldg16(k + (size_t)(kbase + s) * D + cv * VEC) : zero16();
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) put_bits(sKT + (cv * VEC + i) * LY::LDC + s, x, i);
+    }
+    __syncthreads();
+    f32x4 dl[4];
+    bool vis[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int s0 = kbase + 16 * kb;
+      vis[kb] = (s0 <= qlo + 15) && (s0 + 15 >= qlo - W + 1);
+      f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+      if (vis[kb]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          mma32(x, ldg_row_frag<T>(k, D, s0 + r, 32 * ks + 8 * kg, L), qf[ks]);
+          mma32(dp, ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L), of[ks]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + 4 * kg + i;
+        const bool ok = vis[kb] && qvalid && s <= tq && s > tq - W;
+        const float p = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
+        dl[kb][i] = p * (mix * dp[i] - delq) * scale;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      if (vis[2 * p] || vis[2 * p + 1]) {
+        frag op;
+        pack_acc(op, dl[2 * p], dl[2 * p + 1]);
+#pragma unroll
+        for (int db = 0; db < NB; ++db) mma32(accQ[db], op, ld_frag_perm(sKT, LY::LDC, 16 * db + r, 2 * p, 2 * p + 1, kg));
+      }
+    __syncthreads();
+  }
+
+  // ----------------------------------------- anchor window, key side (dk, dv)
+  const int srow = t0 + 16 * w + r;                // this lane's key
+  frag kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = ldg_row_frag<T>(k, D, srow, 32 * ks + 8 * kg, L);
+    vf[ks] = ldg_row_frag<T>(v, D, srow, 32 * ks + 8 * kg, L);
+  }
+  const int qc_hi = min(NC - 1, (t0 + C - 1 + W - 1) / C);
+  T* sQT = sQtT;                                    // raw q^T of the query chunk
+  for (int qc = c; qc <= qc_hi; ++qc) {
+    const int qbase = qc * C;
+    T* dOT = (qc == c) ? sdOT : sKhT;
+    for (int e = tid; e < C * (D / VEC); e += NTHR) {
+      const int t = e / (D / VEC), cv = e % (D / VEC);
+      const bool ok = qbase + t < L;
+      const V16 x = ok ? ldg16(q + (size_t)(qbase + t) * D + cv * VEC) : zero16();
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) put_bits(sQT + (cv * VEC + i) * LY::LDC + t, x, i);
+      if (qc != c) {
+        const V16 y = ok ? ldg16(dO + (size_t)(qbase + t) * D + cv * VEC) : zero16();
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) put_bits(dOT + (cv * VEC + i) * LY::LDC + t, y, i);
+      }
+    }
+    __syncthreads();
+    const int slo = t0 + 16 * w;                   // first key of this wave
+    f32x4 dl[4], pp[4];
+    bool vis[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int q0 = qbase + 16 * tb;
+      vis[tb] = (q0 + 15 >= slo) && (q0 <= slo + 15 + W - 1);
+      f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+      if (vis[tb]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          mma32(x, ldg_row_frag<T>(q, D, q0 + r, 32 * ks + 8 * kg, L), kf[ks]);
+          mma32(dp, ldg_row_frag<T>(dO, D, q0 + r, 32 * ks + 8 * kg, L), vf[ks]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tl = 16 * tb + 4 * kg + i;        // query within chunk qc
+        const int t = qbase + tl;
+        const int li = (qc - c) * C + tl;
+        const bool ok = vis[tb] && t < L && srow <= t && srow > t - W;
+        const float p = ok ? fast_exp2(x[i] * sl2 - sLse[li]) : 0.f;
+        pp[tb][i] = p * mix;
+        dl[tb][i] = p * (mix * dp[i] - sDel[li]) * scale;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      if (vis[2 * p] || vis[2 * p + 1]) {
+        frag opl, opp;
+        pack_acc(opl, dl[2 * p], dl[2 * p + 1]);
+        pack_acc(opp, pp[2 * p], pp[2 * p + 1]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          mma32(accK[nb], opl, ld_frag_perm(sQT, LY::LDC, 16 * nb + r, 2 * p, 2 * p + 1, kg));
+          mma32(accV[nb], opp, ld_frag_perm(dOT, LY::LDC, 16 * nb + r, 2 * p, 2 * p + 1, kg));
+        }
+      }
+    // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
+    if (qc == c && M > 0) {
+      float* dst = a.ws_dmeta + (((size_t)b * NC + c) * a.H + h) * M * 2 * D;
+#pragma unroll
+      for (int blk = 0; blk < NB / 4; ++blk) {
+        const int d0 = 16 * (w * (NB / 4) + blk);
+        f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks) {
+          mma32(xk, ld_frag(sQT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
+          if (mv) mma32(xv, ld_frag(sdOT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
+        }
+        if (r < M)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[(size_t)r * 2 * D + d0 + 4 * kg + i] = xk[i];
+            dst[(size_t)r * 2 * D + D + d0 + 4 * kg + i] = xv[i];
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------------ store
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + 16 * w + 4 * kg + e;
+      if (t < L) {
+        const size_t o = hoff + (size_t)t * D + 16 * nb + r;
+        put_elem(reinterpret_cast<T*>(a.dq) + o, accQ[nb][e]);
+        put_elem(reinterpret_cast<T*>(a.dk) + o, accK[nb][e]);
+        put_elem(reinterpret_cast<T*>(a.dv) + o, accV[nb][e]);
+      }
+    }
+}
+
+// ------------------------------------------------------------ meta reduce
+__global__ __launch_bounds__(NTHR) void dmeta_kernel(const float* __restrict__ part, float* __restrict__ dmk,
+                                                      float* __restrict__ dmv, int slots, int H, int M, int D) {
+  const int e = blockIdx.x * NTHR + threadIdx.x;      // over H*M*2D
+  const int n = H * M * 2 * D;
+  if (e >= n) return;
+  float acc = 0.f;
+  for (int s = 0; s < slots; ++s) acc += part[(size_t)s * n + e];
+  const int hm = e / (2 * D), col = e % (2 * D);
+  if (col < D) dmk[(size_t)hm * D + col] = acc;
+  else if (dmv != nullptr) dmv[(size_t)hm * D + col - D] = acc;
+}
+
+__global__ void fill_zero_kernel(float* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+template <typename K>
+hipError_t set_lds(K kern, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
+  BwdArgs a = args;
+  const int BH = a.B * a.H;
+  const int NC = (a.L + C - 1) / C;
+  const WsLayout wl = ws_layout(a.B, a.H, a.L, a.M, D, std::is_same<T, bf16_t>::value ? 1 : 0);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
+  a.ws_delta = reinterpret_cast<float*>(ws + wl.delta);
+  a.ws_dmeta = reinterpret_cast<float*>(ws + wl.dmeta);
+  T* wsdS = reinterpret_cast<T*>(ws + wl.dS);
+  float* wsbnd = reinterpret_cast<float*>(ws + wl.bnd);
+  hipError_t e;
+  if (a.L == 0) {
+    if (a.M > 0) {
+      const size_t n = (size_t)a.H * a.M * D;
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.dmeta_k, n);
+      if (a.dmeta_v) hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.dmeta_v, n);
+    }
+    return hipGetLastError();
+  }
+  {
+    constexpr int RPB = (NTHR / 64) * (64 / (D / Tr<T>::VEC));
+    const size_t rows = (size_t)BH * a.L;
+    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(NTHR), 0, st,
+                       reinterpret_cast<const T*>(a.dO), reinterpret_cast<const T*>(a.o_swa), a.ws_delta, rows,
+                       a.mix);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    using LY = DsLayout<T, D>;
+    static bool attr = false;
+    if (!attr) {
+      if ((e = set_lds(dstate_kernel<T, D>, LY::bytes)) != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL((dstate_kernel<T, D>), dim3(BH * (D / DVTA)), dim3(NTHR), LY::bytes, st, a, wsdS, wsbnd);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    using LY = CkLayout<T, D>;
+    static bool attr = false;
+    if (!attr) {
+      if ((e = set_lds(chunk_kernel<T, D>, LY::bytes)) != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL((chunk_kernel<T, D>), dim3(BH * NC), dim3(NTHR), LY::bytes, st, a,
+                       (const T*)wsdS, (const float*)wsbnd);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.M > 0) {
+    const int n = a.H * a.M * 2 * D;
+    hipLaunchKernelGGL(dmeta_kernel, dim3((n + NTHR - 1) / NTHR), dim3(NTHR), 0, st,
+                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, a.B * NC, a.H, a.M, D);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype) {
+  return ws_layout(B, H, L, M, D, dtype).total;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st) {
-  (void)a; (void)dtype; (void)D; (void)st;
-  return hipErrorNotSupported;
+  if (dtype == 1) {
+    if (D == 128) return launch_bwd_t<bf16_t, 128>(a, st);
+    if (D == 64) return launch_bwd_t<bf16_t, 64>(a, st);
+  } else if (dtype == 0) {
+    if (D == 64) return launch_bwd_t<float, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lz

@@ -66,50 +66,6 @@ struct FwdLayout {
   static_assert(D % 64 == 0 && DVT % 16 == 0 && DVT <= D, "tile shape");
 };
 
-template <typename T>
-__device__ __forceinline__ typename Tr<T>::frag ldg_frag(const T* p);
-template <>
-__device__ __forceinline__ bf16x8 ldg_frag<bf16_t>(const bf16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-template <>
-__device__ __forceinline__ f32x8 ldg_frag<float>(const float* p) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-template <typename T>
-__device__ __forceinline__ typename Tr<T>::frag zero_frag() {
-  typename Tr<T>::frag f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = 0;
-  return f;
-}
-
-__device__ __forceinline__ void put_elem(float* p, float x) { *p = x; }
-__device__ __forceinline__ void put_elem(bf16_t* p, float x) { p->bits = f2bf(x); }
-__device__ __forceinline__ void put_bits(float* p, const V16& v, int e) { *p = __uint_as_float(v.w[e]); }
-__device__ __forceinline__ void put_bits(bf16_t* p, const V16& v, int e) {
-  p->bits = uint16_t((v.w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-}
-
-// Four consecutive floats to global memory in T.
-__device__ __forceinline__ void stg4(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
-}
-__device__ __forceinline__ void stg4(bf16_t* p, float a, float b, float c, float d) {
-  *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
-}
-
-// VEC consecutive elements (one 16-byte vector) built from floats.
-__device__ __forceinline__ void st_vec(float* p, const float* x) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
-}
-__device__ __forceinline__ void st_vec(bf16_t* p, const float* x) {
-  *reinterpret_cast<bf16x8*>(p) = bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
-                                         (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
-}
-
 // Online-softmax update of one query row (this lane's query) with NB key
 // blocks of logits x (log2 units, -inf where masked); x is overwritten with
 // the unnormalised probabilities.

@@ -20,8 +20,9 @@ struct BwdArgs {
   const void* meta_k; const void* meta_v; const void* dO;
   const float* lse; const void* o_swa; const void* chunk_states;
   void* dq; void* dk; void* dv; float* dg; float* dmeta_k; float* dmeta_v;
-  float* ws_delta;      // [B,H,L] fp32: D_t = mix * dO_t . o_swa_t
-  float* ws_dmeta;      // [B*NC, H, M, 2*d] fp32 partial meta grads, one slot per (b, chunk)
+  void* workspace;      // bwd_workspace_bytes() bytes, carved up by launch_bwd
+  float* ws_delta;      // set by launch_bwd: [B,H,L] fp32, D_t = mix * dO_t . o_swa_t
+  float* ws_dmeta;      // set by launch_bwd: [B*NC, H, M, 2*d] fp32 meta partials per (b, chunk)
   int B, H, L, W, M;
   float scale, mix;
 };
@@ -40,6 +41,6 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
 
 // Workspace bytes needed by launch_bwd.
-size_t bwd_workspace_bytes(int B, int H, int L, int M, int D);
+size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
 
 }  // namespace lz

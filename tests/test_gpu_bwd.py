@@ -1,0 +1,113 @@
+"""GPU parity of lizard_attn_bwd (after lizard_attn_fwd) against the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lizard_oracle as orc
+from gated_linear_attention_chunkwise_amd import lizard_attn_bwd, lizard_attn_fwd
+from gated_linear_attention_chunkwise_amd.inputs import (WORKLOADS, make_inputs, make_inputs_device,
+                                                          make_small)
+from helpers import TOL, dev, host, rel_l2, tdtype
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dg", "dmeta_k", "dmeta_v")
+
+
+def run_both(x, dtname, W, mix=1.0, scale=None):
+    dt = tdtype(dtname)
+    D = x["q"].shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    M = x["meta_k"].shape[1]
+    mv = x.get("meta_v")
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v", "dO")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk = dev(x["meta_k"], dt) if M > 0 else None
+    mvt = dev(mv, dt) if (mv is not None and M > 0) else None
+    f = lizard_attn_fwd(T["q"], T["k"], T["v"], T["g"], mk, mvt, window=W, scale=scale, mix=mix,
+                        want_lse=True, want_o_swa=True, want_chunk_states=True)
+    b = lizard_attn_bwd(T["q"], T["k"], T["v"], T["g"], mk, mvt, T["dO"], f["lse"], f["o_swa"],
+                        f["chunk_states"], window=W, scale=scale, mix=mix)
+    torch.cuda.synchronize()
+    ref = orc.hybrid_backward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], mv, x["dO"], window=W,
+                              scale=scale, mix=mix)
+    return b, ref
+
+
+def check(b, ref, dtname):
+    errs = {}
+    for n in GRADS:
+        if ref.get(n) is None or b.get(n) is None:
+            continue
+        if np.linalg.norm(ref[n]) == 0:
+            assert np.abs(host(b[n])).max() == 0.0, n
+            continue
+        errs[n] = rel_l2(host(b[n]), ref[n])
+    print("rel_l2", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[dtname], (n, e)
+
+
+def test_tiny_fp32_workload():
+    w = WORKLOADS["tiny_fp32"]
+    x = make_inputs(w, with_grad=True)
+    b, ref = run_both(x, "fp32", w.W)
+    check(b, ref, "fp32")
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 200])
+def test_bf16_d128_ragged(L):
+    x = make_small(2, 3, L, 128, 4, seed=200 + L, bf16=True)
+    b, ref = run_both(x, "bf16", 128)
+    check(b, ref, "bf16")
+
+
+@pytest.mark.parametrize("W,M,with_mv,mix", [(1, 0, False, 1.0), (5, 1, False, 0.5), (64, 16, True, 1.0),
+                                             (65, 4, True, 2.0), (129, 3, False, 1.0), (100, 0, False, 1.0)])
+@pytest.mark.parametrize("dtname", ["fp32", "bf16"])
+def test_window_and_meta_edge_cases(W, M, with_mv, mix, dtname):
+    x = make_small(2, 2, 190, 64, M, seed=11 * W + M, bf16=(dtname == "bf16"), with_meta_v=with_mv)
+    b, ref = run_both(x, dtname, W, mix=mix)
+    check(b, ref, dtname)
+
+
+def test_strong_gates_fp32():
+    x = make_small(1, 2, 256, 64, 4, seed=9, bf16=False, gate_div=2.0)
+    b, ref = run_both(x, "fp32", 64)
+    check(b, ref, "fp32")
+
+
+def test_slow_gates_long_bf16():
+    # x ~ N(2,1): slow decay, long memory across many chunks
+    x = make_small(1, 2, 1000, 128, 4, seed=10, bf16=True, x_mean=2.0)
+    b, ref = run_both(x, "bf16", 128)
+    check(b, ref, "bf16")
+
+
+def test_empty_sequence_zero_meta_grads():
+    x = make_small(1, 2, 0, 64, 4, seed=1, bf16=False)
+    b, _ = run_both(x, "fp32", 64)
+    assert float(b["dmeta_k"].abs().max()) == 0.0
+
+
+def test_train_8k_full_size_sampled():
+    """B=4, H=32, L=8192, d=128 forward + backward; oracle on sampled heads."""
+    w = WORKLOADS["train_8k"]
+    x = make_inputs_device(w, "cuda", with_grad=True)
+    f = lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=w.W, scale=w.scale,
+                        want_lse=True, want_o_swa=True, want_chunk_states=True)
+    b = lizard_attn_bwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, x["dO"], f["lse"],
+                        f["o_swa"], f["chunk_states"], window=w.W, scale=w.scale)
+    torch.cuda.synchronize()
+    for h in (0, 31):
+        hs = {n: x[n][:, h:h + 1].float().cpu().numpy() for n in ("q", "k", "v", "g", "dO")}
+        mk = x["meta_k"][h:h + 1].float().cpu().numpy()
+        ref = orc.hybrid_backward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, hs["dO"],
+                                  window=w.W, scale=w.scale)
+        errs = {n: rel_l2(host(b[n][:, h:h + 1]), ref[n]) for n in ("dq", "dk", "dv", "dg")}
+        errs["dmeta_k"] = rel_l2(host(b["dmeta_k"][h:h + 1]), ref["dmeta_k"])
+        print("train_8k head", h, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], (h, n, e)
