@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid attention hot path on one MI355X.
+
+A step is one forward + backward pass of the layer (GLA branch + anchor
+window, every row of the hot path except decode) over one batch of the
+training workload B=4, H=32, L=8192, d=128, W=128, M=4, chunk 64, bf16
+activations with fp32 gates; inputs are seeded synthetic tensors already in
+HBM.  The constant-memory decode step is measured in the same run on its own
+workload (B=64 sequences after a 4096-token prefill) and reported under
+"decode".  Prints one JSON line.
+
+Per-kernel times come from HIP events recorded on the stream the kernels
+run on; the backward records them between its kernels through the
+library's stage-event hook.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attn fwd+bwd tokens/s (8B-shaped layer) + % MFMA/HBM roofline"
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 matrix peak, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def flops_per_head_token(L, d, C, W, M):
+    """Fixed-work FLOP convention: intra-chunk blocks counted full C x C,
+    window keys counted exactly (sum_t min(t+1, W) / L on average)."""
+    wk = sum(min(t + 1, W) for t in range(min(L, W))) + max(0, L - W) * W
+    wavg = wk / L
+    fwd = 4 * C * d + 4 * d * d + 2 * (wavg + M) * d + 2 * wavg * d
+    bwd = 10 * C * d + 10 * d * d + 6 * (wavg + M) * d + 4 * wavg * d
+    return fwd, bwd
+
+
+# compulsory HBM bytes per head-token (bf16 q,k,v,o,dO,dq,dk,dv; fp32 g, dg)
+FWD_BYTES = 3 * 2 * 128 + 4 * 128 + 2 * 128          # 1536
+BWD_BYTES = 4 * 2 * 128 + 4 * 128 + 3 * 2 * 128 + 4 * 128   # 2816
+
+
+class Hip:
+    """Minimal HIP event API through ctypes (events on torch's stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        P = ctypes.c_void_p
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        self.lib.hipEventRecord.argtypes = [P, P]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current sources of that kernel; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel)
+    if not ent or ent.get("source_sha") != source_sha(ent.get("sources", [])):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(x, w, heads):
+    """Time the fp64 oracle (as it stands) on a bounded sample: all batches of
+    `heads` heads at full length, forward + backward, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import lizard_oracle as orc
+    hs = {n: x[n][:, :heads].float().cpu().numpy() for n in ("q", "k", "v", "g", "dO")}
+    mk = x["meta_k"][:heads].float().cpu().numpy()
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        orc.hybrid_forward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, window=w.W, scale=w.scale)
+        orc.hybrid_backward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, hs["dO"], window=w.W,
+                            scale=w.scale)
+        dt = time.perf_counter() - t0
+    tokens = w.B * w.L * heads / w.H          # a token is one position through all H heads
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward+backward of {w.B * heads} of {w.B * w.H} "
+                      f"(batch, head) pairs at full L={w.L} ({heads}/{w.H} of the step's work, "
+                      f"{dt:.1f} s), tokens scaled by {heads}/{w.H}"}
+
+
+def bench_train(args, hip, torch, lib):
+    from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device
+    w = WORKLOADS["train_8k"]
+    x = make_inputs_device(w, "cuda", with_grad=True)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(ev=None):
+        if ev:
+            hip.record(ev[0], stream)
+        f = lib.lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=w.W,
+                                scale=w.scale, want_lse=True, want_o_swa=True,
+                                want_chunk_states=True)
+        b = lib.lizard_attn_bwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, x["dO"], f["lse"],
+                                f["o_swa"], f["chunk_states"], window=w.W, scale=w.scale,
+                                stage_events=None if ev is None else [e.value for e in ev[1:]])
+        return f, b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["fwd_kernel", "delta_kernel", "dstate_kernel", "chunk_kernel", "dmeta_kernel"]
+    per = {n: [] for n in names}
+    for ev in evs:
+        for i, n in enumerate(names):
+            per[n].append(hip.ms(ev[i], ev[i + 1]))
+    avg = {n: sum(v) / len(v) for n, v in per.items()}
+    ms_step = wall * 1e3 / args.steps
+
+    ht = w.B * w.H * w.L
+    f_fwd, f_bwd = flops_per_head_token(w.L, w.D, w.chunk, w.W, w.M)
+    flops_step = (f_fwd + f_bwd) * ht
+    bytes_step = (FWD_BYTES + BWD_BYTES) * ht
+    # dominant kernel and its algorithmic I/O: the forward kernel moves the
+    # forward's compulsory bytes, the chunk kernel the backward's
+    dom = max(("fwd_kernel", "chunk_kernel"), key=lambda n: avg[n])
+    dom_bytes = (FWD_BYTES if dom == "fwd_kernel" else BWD_BYTES) * ht
+    achieved = dom_bytes / (avg[dom] * 1e-3) / 1e9
+    traffic = load_traffic(dom)
+    return w, {
+        "ms_per_step": ms_step,
+        "value": w.B * w.L / (ms_step * 1e-3),
+        "kernels_ms": {n: round(v, 4) for n, v in avg.items()},
+        "dominant": dom,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes},
+        "step_roofline": {
+            "flop": flops_step, "bytes": bytes_step,
+            "mfma_frac": round(flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+            "hbm_frac": round(bytes_step / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+            "ideal_ms": round(max(flops_step / (PEAK_BF16_TFLOPS * 1e12), bytes_step / (PEAK_HBM_GBS * 1e9)) * 1e3, 4),
+        },
+    }, x
+
+
+def bench_decode(args, hip, torch, lib):
+    from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device
+    w = WORKLOADS["decode_b64"]
+    x = make_inputs_device(w, "cuda")
+    P, L = w.prefill, w.L
+    pre = {n: x[n][:, :, :P].contiguous() for n in ("q", "k", "v", "g")}
+    f = lib.lizard_attn_fwd(pre["q"], pre["k"], pre["v"], pre["g"], x["meta_k"], None, window=w.W,
+                            scale=w.scale, want_state=True)
+    state = f["state"]
+    ring_k = torch.zeros(w.B, w.H, w.W, w.D, device="cuda", dtype=torch.bfloat16)
+    ring_v = torch.zeros_like(ring_k)
+    ts = torch.arange(P - w.W, P, device="cuda")
+    ring_k[:, :, ts % w.W] = pre["k"][:, :, ts]
+    ring_v[:, :, ts % w.W] = pre["v"][:, :, ts]
+    pos = torch.full((w.B,), P, device="cuda", dtype=torch.int32)
+    steps = L - P
+    tok = {n: x[n][:, :, P:].permute(2, 0, 1, 3).contiguous() for n in ("q", "k", "v", "g")}
+    mk = x["meta_k"]
+    out = torch.empty(steps, w.B, w.H, w.D, device="cuda", dtype=torch.bfloat16)
+    del x, pre, f
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for t in range(steps):
+        lib.lizard_attn_decode_step(tok["q"][t], tok["k"][t], tok["v"][t], tok["g"][t], mk,
+                                    None, state, ring_k, ring_v, pos, window=w.W, scale=w.scale, out=out[t])
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    us = hip.ms(e0, e1) * 1e3 / steps
+    d = w.D
+    bytes_step = (2 * w.B * w.H * d * d * 4 + 2 * w.B * w.H * w.W * d * 2
+                  + 4 * w.B * w.H * d * 2 + w.B * w.H * d * 4 + 2 * w.B * w.H * d * 2)
+    gbs = bytes_step / (us * 1e-6) / 1e9
+    return {"workload": f"decode_b64: B={w.B} H={w.H} d={d} fp32 state, W={w.W} bf16 ring, M={w.M}; "
+                        f"{steps} steps after a {P}-token prefill",
+            "tokens_per_s": round(w.B / (us * 1e-6), 1), "us_per_step": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode_kernel"),
+                         "kernel": "decode_kernel (+ pos_advance_kernel)",
+                         "algorithmic_bytes_per_step": bytes_step}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards over batch and heads with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_linear_attention_chunkwise_amd as lib
+    lib.load()
+    hip = Hip()
+    w, tr, x = bench_train(args, hip, torch, lib)
+    rec = {
+        "metric": METRIC, "value": round(tr["value"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tr["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"train_8k: B={w.B} H={w.H} L={w.L} d={w.D} W={w.W} M={w.M} chunk={w.chunk}, "
+                               "forward+backward, bf16 activations, fp32 gates",
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
+        "roofline": tr["roofline"],
+        "kernels_ms": tr["kernels_ms"],
+        "step_roofline": tr["step_roofline"],
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads)
+    del x
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        rec["decode"] = bench_decode(args, hip, torch, lib)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,7 +52,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     SP = ctypes.POINTER(Shape)
     lib.lizard_attn_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.lizard_attn_fwd.restype = I32
-    lib.lizard_attn_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]
     lib.lizard_attn_bwd.restype = I32
     lib.lizard_attn_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.lizard_attn_decode_step.restype = I32
@@ -103,6 +103,15 @@ def make_shape(B, H, L, d, W, M, scale, mix, dtype, chunk=64) -> Shape:
     return Shape(B, H, L, d, d, W, M, chunk, float(scale), float(mix), _dtype_code(dtype))
 
 
+def _events(evs, n):
+    if evs is None:
+        return None
+    if len(evs) != n:
+        raise ValueError(f"need {n} events, got {len(evs)}")
+    arr = (ctypes.c_void_p * n)(*[int(e) for e in evs])
+    return ctypes.cast(arr, ctypes.c_void_p)
+
+
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -138,9 +147,16 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
     return out
 
 
+BWD_STAGES = 4
+
+
 def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *, window: int,
-                    scale: float | None = None, mix: float = 1.0, chunk: int = 64) -> dict:
-    """Backward pass from the saved forward tensors; returns dq, dk, dv, dg, dmeta_k, dmeta_v."""
+                    scale: float | None = None, mix: float = 1.0, chunk: int = 64,
+                    stage_events=None) -> dict:
+    """Backward pass from the saved forward tensors; returns dq, dk, dv, dg, dmeta_k, dmeta_v.
+
+    ``stage_events``: optional sequence of BWD_STAGES + 1 raw hipEvent_t handles
+    (ints) recorded around the backward's kernels (profiling hook)."""
     lib = load()
     dt, dev = q.dtype, q.device
     for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO), ("o_swa", o_swa),
@@ -167,7 +183,7 @@ def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *,
                                _ptr(meta_v), _ptr(dO), _ptr(lse), _ptr(o_swa), _ptr(chunk_states),
                                _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                                _ptr(out["dmeta_k"]), _ptr(out["dmeta_v"]), _ptr(ws), ws_bytes,
-                               _stream(dev)))
+                               _stream(dev), _events(stage_events, BWD_STAGES + 1)))
     return out
 
 

@@ -107,7 +107,8 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 const float* lse, const void* o_swa, const void* chunk_states,
                                 void* dq, void* dk, void* dv, float* dg,
                                 float* dmeta_k, float* dmeta_v,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* stage_events) {
   lizard_status_t st = check_shape(s, LIZARD_OP_BWD);
   if (st != LIZARD_OK) return st;
   if ((meta_v == nullptr) != (dmeta_v == nullptr)) return LIZARD_EINVAL;
@@ -131,6 +132,7 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
   a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
   a.scale = s->scale; a.mix = s->mix;
   a.workspace = workspace;
+  a.stage_events = stage_events;
   return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 

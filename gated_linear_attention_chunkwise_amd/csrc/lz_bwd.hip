@@ -777,6 +777,10 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     }
     return hipGetLastError();
   }
+  auto mark = [&](int i) {
+    if (a.stage_events != nullptr) (void)hipEventRecord(a.stage_events[i], st);
+  };
+  mark(0);
   {
     constexpr int RPB = (NTHR / 64) * (64 / (D / Tr<T>::VEC));
     const size_t rows = (size_t)BH * a.L;
@@ -785,6 +789,7 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
                        a.mix);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  mark(1);
   {
     using LY = DsLayout<T, D>;
     static bool attr = false;
@@ -795,6 +800,7 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     hipLaunchKernelGGL((dstate_kernel<T, D>), dim3(BH * (D / DVTA)), dim3(NTHR), LY::bytes, st, a, wsdS, wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  mark(2);
   {
     using LY = CkLayout<T, D>;
     static bool attr = false;
@@ -806,12 +812,14 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
                        (const T*)wsdS, (const float*)wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  mark(3);
   if (a.M > 0) {
     const int n = a.H * a.M * 2 * D;
     hipLaunchKernelGGL(dmeta_kernel, dim3((n + NTHR - 1) / NTHR), dim3(NTHR), 0, st,
                        (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, a.B * NC, a.H, a.M, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  mark(4);
   return hipSuccess;
 }
 

@@ -23,6 +23,7 @@ struct BwdArgs {
   void* workspace;      // bwd_workspace_bytes() bytes, carved up by launch_bwd
   float* ws_delta;      // set by launch_bwd: [B,H,L] fp32, D_t = mix * dO_t . o_swa_t
   float* ws_dmeta;      // set by launch_bwd: [B*NC, H, M, 2*d] fp32 meta partials per (b, chunk)
+  hipEvent_t* stage_events;   // optional: 5 events recorded around the 4 kernels
   int B, H, L, W, M;
   float scale, mix;
 };

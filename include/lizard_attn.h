@@ -37,11 +37,17 @@
  *   launched and no output is written; the return value says why.  A launch
  *   failure returns LIZARD_EHIP.  Faults inside kernels surface, as usual
  *   for HIP, at the caller's next synchronisation.
- * - Supported: d_k = d_v in {64, 128}; chunk in {64} (0 selects 64);
- *   W >= 1; 0 <= M <= 16; B, H >= 1; L >= 0 (L = 0 is a no-op).
- *   Numerical domain: within one chunk the cumulative log-gate of every key
- *   dimension must stay above -80 (the gate factors are exponentiated in
- *   fp32 relative to the chunk's midpoint); typical gates are far inside.
+ * - Supported: d_k = d_v; bf16: d in {64, 128}; fp32: d = 64 for the forward
+ *   and backward, d in {64, 128} for decode.  chunk in {64} (0 selects 64).
+ *   Forward/backward: 1 <= W <= 2*chunk + 1 = 129 (a query's window spans
+ *   at most three chunks); decode: 1 <= W <= 8192.  0 <= M <= 16; B, H >= 1;
+ *   L >= 0 (L = 0 writes only the zero state / zero meta gradients).
+ *   Anything else returns LIZARD_EUNSUPPORTED.
+ * - Numerical domain: within one chunk the cumulative log-gate of every key
+ *   dimension must stay above -80, so that the factor exp(-b) of the
+ *   chunk-local prefix b stays finite in fp32; the library does not scan the
+ *   gates (that would need a synchronisation).  Gates of the form
+ *   logsigmoid(x)/16 stay above -5 per chunk.
  */
 #ifndef LIZARD_ATTN_H
 #define LIZARD_ATTN_H
@@ -108,14 +114,25 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
  *   dg                         written, fp32 [B,H,L,d_k]
  *   dmeta_k                    written, fp32 [H,M,d_k] (summed over batch)
  *   dmeta_v                    fp32 [H,M,d_v]; must be NULL iff meta_v is NULL
- *   workspace                  lizard_attn_workspace_bytes(s, LIZARD_OP_BWD) bytes */
+ *   workspace                  lizard_attn_workspace_bytes(s, LIZARD_OP_BWD) bytes,
+ *                              caller-owned device memory, clobbered by the call
+ *   stage_events          opt  profiling hook: NULL, or LIZARD_BWD_STAGES + 1
+ *                              caller-created events that are recorded on
+ *                              `stream` before the first, between consecutive
+ *                              and after the last of the backward's kernels
+ *                              (row dots, state-gradient sweep, chunk
+ *                              gradients, meta reduction; a stage with nothing
+ *                              to do still gets its event).  For L = 0 they are
+ *                              not recorded. */
+#define LIZARD_BWD_STAGES 4
 lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 const void* q, const void* k, const void* v, const float* g,
                                 const void* meta_k, const void* meta_v, const void* dO,
                                 const float* lse, const void* o_swa, const void* chunk_states,
                                 void* dq, void* dk, void* dv, float* dg,
                                 float* dmeta_k, float* dmeta_v,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* stage_events);
 
 /* One constant-memory decode step for every sequence (English page §4,
  * "Efficiency": constant memory at any length; French page §2.A: O(1)

@@ -85,7 +85,7 @@ def test_bwd_validation(lib):
     def call(meta_v=None, dmeta_v=None, ws=GOOD, ws_bytes=1 << 40, dq=GOOD, dmeta_k=GOOD):
         return lib.lizard_attn_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, meta_v, GOOD,
                                    GOOD, GOOD, GOOD, dq, GOOD, GOOD, GOOD, dmeta_k, dmeta_v, ws,
-                                   ws_bytes, None)
+                                   ws_bytes, None, None)
     assert call(meta_v=GOOD, dmeta_v=None) == EINVAL
     assert call(meta_v=None, dmeta_v=GOOD) == EINVAL
     assert call(dq=None) == EINVAL
