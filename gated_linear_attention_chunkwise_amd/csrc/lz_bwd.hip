@@ -36,6 +36,7 @@ namespace {
 constexpr int C = 64;
 constexpr int NTHR = 256;
 constexpr int DVTA = 64;   // d_v tile of the state-gradient sweep
+constexpr int NTHR_CK = 512;   // chunk kernel: 8 waves, two per token block
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -84,18 +85,18 @@ __global__ __launch_bounds__(NTHR) void delta_kernel(const T* __restrict__ dO, c
 // Thread map of a 64 x D chunk tile: column group cg (VEC dims), tokens
 // tg*TPT .. +TPT.  Computes the chunk-local inclusive prefix b of the
 // log-gates held in rg (overwritten with b) and the chunk total Gamma.
-template <int D, int VEC>
+template <int D, int VEC, int NT = NTHR>
 struct ScanMap {
   static constexpr int VPR = D / VEC;
-  static constexpr int NTG = NTHR / VPR;
+  static constexpr int NTG = NT / VPR;
   static constexpr int TPT = C / NTG;
   static constexpr int GV = VEC / 4;
 };
 
-template <int D, int VEC, int TPT_, int GV_>
+template <int D, int VEC, int NT, int TPT_, int GV_>
 __device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot)[GV_], float* sScan, int cg,
                                              int tg) {
-  using SM = ScanMap<D, VEC>;
+  using SM = ScanMap<D, VEC, NT>;
   static_assert(SM::TPT == TPT_ && SM::GV == GV_, "scan map");
 #pragma unroll
   for (int u = 1; u < SM::TPT; ++u)
@@ -205,6 +206,18 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
 
   if (NC > 0) prefetch(NC - 1);
   for (int c = NC - 1; c >= 0; --c) {
+    // state after chunk c (valid for c < NC-1) at this lane's accumulator positions;
+    // issued before the next prefetch so that waiting for it never waits for that
+    const T* Sc = cstates + (size_t)(c + 1) * D * D;
+    float scv[IB][JB][4];
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          scv[ib][jb][i] = (c + 1 < NC)
+              ? Tr<T>::to_f(Sc[(size_t)(16 * (w * IB + ib) + 4 * kg + i) * D + j0 + 16 * jb + r]) : 0.f;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NVV; ++u) {
@@ -216,7 +229,7 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
       }
     }
     f32x4 tot[GV];
-    chunk_prefix<D, VEC, TPT, GV>(rg, tot, sScan, cg, tg);
+    chunk_prefix<D, VEC, NTHR, TPT, GV>(rg, tot, sScan, cg, tg);
     if (tg == 0)
 #pragma unroll
       for (int e = 0; e < GV; ++e)
@@ -235,7 +248,6 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
     // acc holds dS_c (gradient w.r.t. the state after chunk c, from later chunks)
     T* dst = wsdS + ((size_t)bh * NC + c) * D * D;
     float* bnd = wsbnd + (((size_t)bh * NC + c) * NJ + jt) * D;
-    const T* Sc = cstates + (size_t)(c + 1) * D * D;     // state after chunk c (valid for c < NC-1)
 #pragma unroll
     for (int ib = 0; ib < IB; ++ib) {
       const int i0 = 16 * (w * IB + ib);
@@ -245,10 +257,8 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
         const int j = j0 + 16 * jb + r;
-        if (c + 1 < NC) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rs[i] += Tr<T>::to_f(Sc[(size_t)(i0 + 4 * kg + i) * D + j]) * acc[ib][jb][i];
-        }
+        for (int i = 0; i < 4; ++i) rs[i] += scv[ib][jb][i] * acc[ib][jb][i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[ib][jb][i] *= dec[i];
         st4(dst + (size_t)j * D + i0 + 4 * kg, acc[ib][jb][0], acc[ib][jb][1], acc[ib][jb][2], acc[ib][jb][3]);
@@ -296,22 +306,23 @@ struct CkLayout {
   static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // p_meta^T  [16][C]
   static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 chunks (log2 units)
   static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 chunks
-  static constexpr size_t oCar = oDel + sizeof(float) * 3 * C;       // scan carry [D]
-  static constexpr size_t bytes = oCar + sizeof(float) * D;
+  static constexpr size_t bytes = oDel + sizeof(float) * 3 * C;
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
-                                                         const float* __restrict__ wsbnd) {
+__global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
+                                                            const float* __restrict__ wsbnd) {
   using LY = CkLayout<T, D>;
-  using SM = ScanMap<D, Tr<T>::VEC>;
+  using SM = ScanMap<D, Tr<T>::VEC, NTHR_CK>;
   using frag = typename Tr<T>::frag;
   constexpr int VEC = Tr<T>::VEC, TPT = SM::TPT, GV = SM::GV;
   constexpr int NB = D / 16;     // 16-wide blocks over the head dim
+  constexpr int NBH = NB / 2;    // blocks per wave (the two waves of a token block split them)
   constexpr int KS = D / 32;     // K steps over the head dim
   constexpr int NJ = D / DVTA;
 
+  static_assert(sizeof(float) * SM::NTG * D <= LY::bigBytes, "scan scratch fits in the shared region");
   extern __shared__ __align__(16) unsigned char smem[];
   T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
   T* sKh = reinterpret_cast<T*>(smem + LY::oKh);
@@ -328,9 +339,10 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
   T* sPm = reinterpret_cast<T*>(smem + LY::oPm);
   float* sLse = reinterpret_cast<float*>(smem + LY::oLse);
   float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
-  float* sCar = reinterpret_cast<float*>(smem + LY::oCar);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+  const int wb = w & 3;          // token block of this wave (rows 16*wb .. +16 of the chunk)
+  const int nb0 = (w >> 2) * NBH;  // first of this wave's output column blocks
   const int L = a.L, NC = (L + C - 1) / C, W = a.W, M = a.M;
   // workgroup -> (chunk, head); consecutive chunks of one head share an XCD
   const int BH = a.B * a.H;
@@ -378,17 +390,17 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
         rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
     }
     // meta keys transposed, lse / delta of this chunk and the next two
-    for (int e = tid; e < D * 16; e += NTHR) {
+    for (int e = tid; e < D * 16; e += NTHR_CK) {
       const int d = e / 16, m = e % 16;
       put_elem(sMkT + d * LY::LDM + m, m < M ? Tr<T>::to_f(mk[(size_t)m * D + d]) : 0.f);
     }
-    for (int e = tid; e < 3 * C; e += NTHR) {
+    for (int e = tid; e < 3 * C; e += NTHR_CK) {
       const int t = t0 + e;
       sLse[e] = t < L ? a.lse[(size_t)bh * L + t] * LOG2E : 0.f;
       sDel[e] = t < L ? a.ws_delta[(size_t)bh * L + t] : 0.f;
     }
     f32x4 tot[GV];
-    chunk_prefix<D, VEC, TPT, GV>(rg, tot, sScan, cg, tg);
+    chunk_prefix<D, VEC, NTHR_CK, TPT, GV>(rg, tot, sScan, cg, tg);
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int t = tg * TPT + u;
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
       st_vec(sEb + t * LY::LDQ + cg * VEC, eb);
     }
     __syncthreads();   // scan scratch is dead: stage dS' (row-major) into the same region
-    for (int e = tid; e < D * (D / VEC); e += NTHR) {
+    for (int e = tid; e < D * (D / VEC); e += NTHR_CK) {
       const int j = e / (D / VEC), cv = e % (D / VEC);
       const V16 x = ldg16(dSpT + (size_t)j * D + cv * VEC);
 #pragma unroll
@@ -418,23 +430,32 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
   }
 
   // ------------------------------------------------------ GLA gradients
-  // wave w owns chunk tokens u in [16w, 16w+16): as query rows (accQ) and as key rows (accK, accV)
-  f32x4 accQ[NB], accK[NB], accV[NB];
+  // wave w owns chunk tokens u in [16wb, 16wb+16) (as query rows for accQ, as
+  // key rows for accK / accV) and output column blocks nb0 .. nb0+NBH
+  f32x4 accQ[NBH], accK[NBH], accV[NBH];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) { accQ[i] = f32x4{0, 0, 0, 0}; accK[i] = accQ[i]; accV[i] = accQ[i]; }
-  const int urow = t0 + 16 * w + r;     // this lane's token as an operand row
+  for (int i = 0; i < NBH; ++i) { accQ[i] = f32x4{0, 0, 0, 0}; accK[i] = accQ[i]; accV[i] = accQ[i]; }
+  const int urow = t0 + 16 * wb + r;     // this lane's token as an operand row
   {
-    // dq~ intra: dA^T blocks (keys sb <= w, queries of block w), then times k^
+    frag fo[KS], fvu[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fo[ks] = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
+      fvu[ks] = ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L);
+    }
+    // dq~ intra: dA^T blocks (keys sb <= wb, queries of block wb), then times k^
     f32x4 blk[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       blk[sb] = f32x4{0, 0, 0, 0};
-      if (sb <= w) {
+      if (sb <= wb) {
+        frag fv[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          mma32(blk[sb], ldg_row_frag<T>(v, D, t0 + 16 * sb + r, 32 * ks + 8 * kg, L),
-                ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L));
-        if (sb == w)
+        for (int ks = 0; ks < KS; ++ks) fv[ks] = ldg_row_frag<T>(v, D, t0 + 16 * sb + r, 32 * ks + 8 * kg, L);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma32(blk[sb], fv[ks], fo[ks]);
+        mfma_drain();
+        if (sb == wb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (4 * kg + i > r) blk[sb][i] = 0.f;
@@ -442,30 +463,33 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-      if (2 * p <= w) {
+      if (2 * p <= wb) {
         frag op;
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
-        for (int ib = 0; ib < NB; ++ib) mma32(accQ[ib], op, ld_frag_perm(sKhT, LY::LDC, 16 * ib + r, 2 * p, 2 * p + 1, kg));
+        for (int x = 0; x < NBH; ++x)
+          mma32(accQ[x], op, ld_frag_perm(sKhT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
       }
     // dq~ inter: dO S_prev^T
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const frag fo = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
+      frag fs[NBH];
 #pragma unroll
-      for (int ib = 0; ib < NB; ++ib)
-        mma32(accQ[ib], fo, ldg_frag<T>(Sprev + (size_t)(16 * ib + r) * D + 32 * ks + 8 * kg));
+      for (int x = 0; x < NBH; ++x) fs[x] = ldg_frag<T>(Sprev + (size_t)(16 * (nb0 + x) + r) * D + 32 * ks + 8 * kg);
+#pragma unroll
+      for (int x = 0; x < NBH; ++x) mma32(accQ[x], fo[ks], fs[x]);
     }
-    // dv intra: A blocks (queries tb >= w, keys of block w), A^T dO
+    // dv intra: A blocks (queries tb >= wb, keys of block wb), A^T dO
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       blk[tb] = f32x4{0, 0, 0, 0};
-      if (tb >= w) {
+      if (tb >= wb) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           mma32(blk[tb], ld_frag(sQt, LY::LDQ, 16 * tb + r, 32 * ks + 8 * kg),
-                ld_frag(sKh, LY::LDQ, 16 * w + r, 32 * ks + 8 * kg));
-        if (tb == w)
+                ld_frag(sKh, LY::LDQ, 16 * wb + r, 32 * ks + 8 * kg));
+        mfma_drain();
+        if (tb == wb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (4 * kg + i < r) blk[tb][i] = 0.f;
@@ -473,22 +497,25 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-      if (2 * p + 1 >= w) {
+      if (2 * p + 1 >= wb) {
         frag op;
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) mma32(accV[jb], op, ld_frag_perm(sdOT, LY::LDC, 16 * jb + r, 2 * p, 2 * p + 1, kg));
+        for (int x = 0; x < NBH; ++x)
+          mma32(accV[x], op, ld_frag_perm(sdOT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
       }
-    // dk^ intra: dA blocks (queries tb >= w, keys of block w), dA^T q~
+    // dk^ intra: dA blocks (queries tb >= wb, keys of block wb), dA^T q~
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       blk[tb] = f32x4{0, 0, 0, 0};
-      if (tb >= w) {
+      if (tb >= wb) {
+        frag fd[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          mma32(blk[tb], ldg_row_frag<T>(dO, D, t0 + 16 * tb + r, 32 * ks + 8 * kg, L),
-                ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L));
-        if (tb == w)
+        for (int ks = 0; ks < KS; ++ks) fd[ks] = ldg_row_frag<T>(dO, D, t0 + 16 * tb + r, 32 * ks + 8 * kg, L);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], fd[ks], fvu[ks]);
+        mfma_drain();
+        if (tb == wb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (4 * kg + i < r) blk[tb][i] = 0.f;
@@ -496,45 +523,49 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-      if (2 * p + 1 >= w) {
+      if (2 * p + 1 >= wb) {
         frag op;
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
-        for (int ib = 0; ib < NB; ++ib) mma32(accK[ib], op, ld_frag_perm(sQtT, LY::LDC, 16 * ib + r, 2 * p, 2 * p + 1, kg));
+        for (int x = 0; x < NBH; ++x)
+          mma32(accK[x], op, ld_frag_perm(sQtT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
       }
     // inter-chunk: dk^ += V dS'^T ; dv += k^ dS'
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const frag fv = ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L);
-      const frag fk = ld_frag(sKh, LY::LDQ, 16 * w + r, 32 * ks + 8 * kg);
+      frag fd[NBH];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        mma32(accK[nb], fv, ld_frag(sdSp, LY::LDQ, 16 * nb + r, 32 * ks + 8 * kg));
-        mma32(accV[nb], fk, ldg_frag<T>(dSpT + (size_t)(16 * nb + r) * D + 32 * ks + 8 * kg));
+      for (int x = 0; x < NBH; ++x) fd[x] = ldg_frag<T>(dSpT + (size_t)(16 * (nb0 + x) + r) * D + 32 * ks + 8 * kg);
+      const frag fk = ld_frag(sKh, LY::LDQ, 16 * wb + r, 32 * ks + 8 * kg);
+#pragma unroll
+      for (int x = 0; x < NBH; ++x) {
+        mma32(accK[x], fvu[ks], ld_frag(sdSp, LY::LDQ, 16 * (nb0 + x) + r, 32 * ks + 8 * kg));
+        mma32(accV[x], fk, fd[x]);
       }
     }
   }
+  mfma_drain();
   __syncthreads();   // every wave is done with sdSp: its region now holds the per-token gate gradient
 
   // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int i = 16 * nb + r;
+  for (int x = 0; x < NBH; ++x) {
+    const int i = 16 * (nb0 + x) + r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int u = 16 * w + 4 * kg + e;
+      const int u = 16 * wb + 4 * kg + e;
       const float qt = Tr<T>::to_f(sQt[u * LY::LDQ + i]);
       const float kh = Tr<T>::to_f(sKh[u * LY::LDQ + i]);
       const float eb = Tr<T>::to_f(sEb[u * LY::LDQ + i]);
-      sDb[u * D + i] = qt * accQ[nb][e] - kh * accK[nb][e];
-      accQ[nb][e] *= eb;
-      accK[nb][e] *= 1.f / eb;
+      sDb[u * D + i] = qt * accQ[x][e] - kh * accK[x][e];
+      accQ[x][e] *= eb;
+      accK[x][e] *= 1.f / eb;
     }
   }
   __syncthreads();
   // reverse cumulative sum over the chunk plus the boundary rowsum -> dg
   {
-    constexpr int PARTS = NTHR / D;              // threads per column
+    constexpr int PARTS = NTHR_CK / D;           // threads per column
     constexpr int SEG = C / PARTS;
     const int i = tid % D, part = tid / D;
     float run = 0.f;
@@ -561,16 +592,20 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
     qf[ks] = ldg_row_frag<T>(q, D, urow, 32 * ks + 8 * kg, L);
     of[ks] = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
   }
-  const int tq = t0 + 16 * w + r;                  // this lane's query
-  const float lse2 = sLse[16 * w + r], delq = sDel[16 * w + r];
+  const int tq = urow;                             // this lane's query
+  const float lse2 = sLse[16 * wb + r], delq = sDel[16 * wb + r];
   const bool qvalid = tq < L;
   if (M > 0) {
+    // meta values: absent ones read as zero rows (no branch around the product)
+    const T* mvp = mv ? mv : mk;
+    const int mvrows = mv ? M : 0;
     f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       mma32(x, ldg_row_frag<T>(mk, D, r, 32 * ks + 8 * kg, M), qf[ks]);
-      if (mv) mma32(dp, ldg_row_frag<T>(mv, D, r, 32 * ks + 8 * kg, M), of[ks]);
+      mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), of[ks]);
     }
+    mfma_drain();
     f32x4 dl, pm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -578,26 +613,28 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
       const float p = (m < M && qvalid) ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
       pm[i] = p;
       dl[i] = p * (mix * dp[i] - delq) * scale;
-      put_elem(sDLm + m * LY::LDC + 16 * w + r, dl[i]);
-      put_elem(sPm + m * LY::LDC + 16 * w + r, p * mix);
+      if (nb0 == 0) {
+        put_elem(sDLm + m * LY::LDC + 16 * wb + r, dl[i]);
+        put_elem(sPm + m * LY::LDC + 16 * wb + r, p * mix);
+      }
     }
     frag op;
     pack_acc(op, dl, f32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int db = 0; db < NB; ++db) mma32(accQ[db], op, ld_frag_perm(sMkT, LY::LDM, 16 * db + r, 0, 0, kg));
+    for (int x2 = 0; x2 < NBH; ++x2)
+      mma32(accQ[x2], op, ld_frag_perm(sMkT, LY::LDM, 16 * (nb0 + x2) + r, 0, 0, kg));
   }
   const int kt_lo = max(0, t0 - W + 1) / C;
-  const int qlo = t0 + 16 * w;
+  const int qlo = t0 + 16 * wb;
   for (int kt = c; kt >= kt_lo; --kt) {
     const int kbase = kt * C;
     // K^T tile of chunk kt
-    for (int e = tid; e < C * (D / VEC); e += NTHR) {
+    for (int e = tid; e < C * (D / VEC); e += NTHR_CK) {
       const int s = e / (D / VEC), cv = e % (D / VEC);
       const V16 x = (kbase + s < L) ? ldg16(k + (size_t)(kbase + s) * D + cv * VEC) : zero16();
 #pragma unroll
       for (int i = 0; i < VEC; ++i) put_bits(sKT + (cv * VEC + i) * LY::LDC + s, x, i);
     }
-    __syncthreads();
     f32x4 dl[4];
     bool vis[4];
 #pragma unroll
@@ -606,11 +643,18 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
       vis[kb] = (s0 <= qlo + 15) && (s0 + 15 >= qlo - W + 1);
       f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
       if (vis[kb]) {
+        frag fk[KS], fv[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          mma32(x, ldg_row_frag<T>(k, D, s0 + r, 32 * ks + 8 * kg, L), qf[ks]);
-          mma32(dp, ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L), of[ks]);
+          fk[ks] = ldg_row_frag<T>(k, D, s0 + r, 32 * ks + 8 * kg, L);
+          fv[ks] = ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L);
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          mma32(x, fk[ks], qf[ks]);
+          mma32(dp, fv[ks], of[ks]);
+        }
+        mfma_drain();
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -620,19 +664,21 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
         dl[kb][i] = p * (mix * dp[i] - delq) * scale;
       }
     }
+    __syncthreads();   // K^T tile staged
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       if (vis[2 * p] || vis[2 * p + 1]) {
         frag op;
         pack_acc(op, dl[2 * p], dl[2 * p + 1]);
 #pragma unroll
-        for (int db = 0; db < NB; ++db) mma32(accQ[db], op, ld_frag_perm(sKT, LY::LDC, 16 * db + r, 2 * p, 2 * p + 1, kg));
+        for (int x = 0; x < NBH; ++x)
+          mma32(accQ[x], op, ld_frag_perm(sKT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
       }
     __syncthreads();
   }
 
   // ----------------------------------------- anchor window, key side (dk, dv)
-  const int srow = t0 + 16 * w + r;                // this lane's key
+  const int srow = urow;                           // this lane's key
   frag kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -644,7 +690,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
   for (int qc = c; qc <= qc_hi; ++qc) {
     const int qbase = qc * C;
     T* dOT = (qc == c) ? sdOT : sKhT;
-    for (int e = tid; e < C * (D / VEC); e += NTHR) {
+    for (int e = tid; e < C * (D / VEC); e += NTHR_CK) {
       const int t = e / (D / VEC), cv = e % (D / VEC);
       const bool ok = qbase + t < L;
       const V16 x = ok ? ldg16(q + (size_t)(qbase + t) * D + cv * VEC) : zero16();
@@ -656,8 +702,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
         for (int i = 0; i < VEC; ++i) put_bits(dOT + (cv * VEC + i) * LY::LDC + t, y, i);
       }
     }
-    __syncthreads();
-    const int slo = t0 + 16 * w;                   // first key of this wave
+    const int slo = t0 + 16 * wb;                  // first key of this wave
     f32x4 dl[4], pp[4];
     bool vis[4];
 #pragma unroll
@@ -666,11 +711,18 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
       vis[tb] = (q0 + 15 >= slo) && (q0 <= slo + 15 + W - 1);
       f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
       if (vis[tb]) {
+        frag fq[KS], fd[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          mma32(x, ldg_row_frag<T>(q, D, q0 + r, 32 * ks + 8 * kg, L), kf[ks]);
-          mma32(dp, ldg_row_frag<T>(dO, D, q0 + r, 32 * ks + 8 * kg, L), vf[ks]);
+          fq[ks] = ldg_row_frag<T>(q, D, q0 + r, 32 * ks + 8 * kg, L);
+          fd[ks] = ldg_row_frag<T>(dO, D, q0 + r, 32 * ks + 8 * kg, L);
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          mma32(x, fq[ks], kf[ks]);
+          mma32(dp, fd[ks], vf[ks]);
+        }
+        mfma_drain();
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -683,6 +735,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
         dl[tb][i] = p * (mix * dp[i] - sDel[li]) * scale;
       }
     }
+    __syncthreads();   // q^T / dO^T of chunk qc staged
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       if (vis[2 * p] || vis[2 * p + 1]) {
@@ -690,57 +743,67 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(BwdArgs a, const T* __re
         pack_acc(opl, dl[2 * p], dl[2 * p + 1]);
         pack_acc(opp, pp[2 * p], pp[2 * p + 1]);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          mma32(accK[nb], opl, ld_frag_perm(sQT, LY::LDC, 16 * nb + r, 2 * p, 2 * p + 1, kg));
-          mma32(accV[nb], opp, ld_frag_perm(dOT, LY::LDC, 16 * nb + r, 2 * p, 2 * p + 1, kg));
+        for (int x = 0; x < NBH; ++x) {
+          mma32(accK[x], opl, ld_frag_perm(sQT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
+          mma32(accV[x], opp, ld_frag_perm(dOT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
         }
       }
     // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
-    if (qc == c && M > 0) {
+    if (qc == c && M > 0 && w < NB) {
       float* dst = a.ws_dmeta + (((size_t)b * NC + c) * a.H + h) * M * 2 * D;
+      const int d0 = 16 * w;
+      f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int blk = 0; blk < NB / 4; ++blk) {
-        const int d0 = 16 * (w * (NB / 4) + blk);
-        f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < C / 32; ++ks) {
-          mma32(xk, ld_frag(sQT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
-          if (mv) mma32(xv, ld_frag(sdOT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
-        }
-        if (r < M)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dst[(size_t)r * 2 * D + d0 + 4 * kg + i] = xk[i];
-            dst[(size_t)r * 2 * D + D + d0 + 4 * kg + i] = xv[i];
-          }
+      for (int ks = 0; ks < C / 32; ++ks) {
+        mma32(xk, ld_frag(sQT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
+        mma32(xv, ld_frag(sdOT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
       }
+      mfma_drain();
+      if (r < M)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[(size_t)r * 2 * D + d0 + 4 * kg + i] = xk[i];
+          dst[(size_t)r * 2 * D + D + d0 + 4 * kg + i] = xv[i];
+        }
     }
     __syncthreads();
   }
 
   // ------------------------------------------------------------------ store
+  mfma_drain();
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int x = 0; x < NBH; ++x)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = t0 + 16 * w + 4 * kg + e;
+      const int t = t0 + 16 * wb + 4 * kg + e;
       if (t < L) {
-        const size_t o = hoff + (size_t)t * D + 16 * nb + r;
-        put_elem(reinterpret_cast<T*>(a.dq) + o, accQ[nb][e]);
-        put_elem(reinterpret_cast<T*>(a.dk) + o, accK[nb][e]);
-        put_elem(reinterpret_cast<T*>(a.dv) + o, accV[nb][e]);
+        const size_t o = hoff + (size_t)t * D + 16 * (nb0 + x) + r;
+        put_elem(reinterpret_cast<T*>(a.dq) + o, accQ[x][e]);
+        put_elem(reinterpret_cast<T*>(a.dk) + o, accK[x][e]);
+        put_elem(reinterpret_cast<T*>(a.dv) + o, accV[x][e]);
       }
     }
 }
 
 // ------------------------------------------------------------ meta reduce
+// Two-level deterministic sum of the per-(batch, chunk) meta partials
+// part[slot][H*M*2D]: level 1 folds each run of `per` slots into its first
+// slot (in place), level 2 sums the run heads in order.
+__global__ __launch_bounds__(NTHR) void dmeta_fold_kernel(float* __restrict__ part, int slots, int n, int per) {
+  const int e = blockIdx.x * NTHR + threadIdx.x;
+  if (e >= n) return;
+  const int s0 = blockIdx.y * per, s1 = min(slots, s0 + per);
+  float acc = 0.f;
+  for (int s = s0; s < s1; ++s) acc += part[(size_t)s * n + e];
+  if (s0 < slots) part[(size_t)s0 * n + e] = acc;
+}
+
 __global__ __launch_bounds__(NTHR) void dmeta_kernel(const float* __restrict__ part, float* __restrict__ dmk,
-                                                      float* __restrict__ dmv, int slots, int H, int M, int D) {
-  const int e = blockIdx.x * NTHR + threadIdx.x;      // over H*M*2D
-  const int n = H * M * 2 * D;
+                                                      float* __restrict__ dmv, int slots, int per, int n, int D) {
+  const int e = blockIdx.x * NTHR + threadIdx.x;   // over H*M*2D
   if (e >= n) return;
   float acc = 0.f;
-  for (int s = 0; s < slots; ++s) acc += part[(size_t)s * n + e];
+  for (int s = 0; s < slots; s += per) acc += part[(size_t)s * n + e];
   const int hm = e / (2 * D), col = e % (2 * D);
   if (col < D) dmk[(size_t)hm * D + col] = acc;
   else if (dmv != nullptr) dmv[(size_t)hm * D + col - D] = acc;
@@ -808,15 +871,21 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
       if ((e = set_lds(chunk_kernel<T, D>, LY::bytes)) != hipSuccess) return e;
       attr = true;
     }
-    hipLaunchKernelGGL((chunk_kernel<T, D>), dim3(BH * NC), dim3(NTHR), LY::bytes, st, a,
+    hipLaunchKernelGGL((chunk_kernel<T, D>), dim3(BH * NC), dim3(NTHR_CK), LY::bytes, st, a,
                        (const T*)wsdS, (const float*)wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(3);
   if (a.M > 0) {
     const int n = a.H * a.M * 2 * D;
+    const int slots = a.B * NC;
+    const int runs = slots < 32 ? slots : 32;
+    const int per = (slots + runs - 1) / runs;
+    hipLaunchKernelGGL(dmeta_fold_kernel, dim3((n + NTHR - 1) / NTHR, runs), dim3(NTHR), 0, st,
+                       a.ws_dmeta, slots, n, per);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(dmeta_kernel, dim3((n + NTHR - 1) / NTHR), dim3(NTHR), 0, st,
-                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, a.B * NC, a.H, a.M, D);
+                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, slots, per, n, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(4);

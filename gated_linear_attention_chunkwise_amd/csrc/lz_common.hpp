@@ -126,6 +126,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Matrix-core results must not be read until the instruction has drained
+// (several wait states).  The compiler inserts those wait states within a
+// basic block, but a read reached through a branch taken right after a
+// matrix instruction has been seen to go unprotected, so every block of
+// matrix instructions that ends in control flow finishes with this drain.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------------ operand / store helpers
 // Eight consecutive K values straight from global memory (row-major tensor).
 template <typename T>

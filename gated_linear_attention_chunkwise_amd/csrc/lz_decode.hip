@@ -8,13 +8,18 @@
 //   ring  [B,H,W,d]            last W keys / values, token n in slot n mod W
 //   pos   [B] int32            tokens consumed so far
 //
-// One workgroup per (b, h, d_v slice of 64): it streams its fp32 state slice
-// from HBM, applies S <- diag(exp g) S + k^T v, reduces o_gla = q S over d_k
-// across the workgroup, attends over the M meta keys plus the filled ring
-// slots (the slot of the new token is read from the inputs, so no workgroup
-// ever reads a ring entry that another one writes), and stores its slice of
-// the new key/value.  pos is advanced by a second one-wave kernel so that
-// every workgroup of a sequence reads the same pos.
+// One workgroup per (b, h).  It issues every load of the step up front (the
+// fp32 state, one 128-key block of the key and value rings, the new token),
+// so the whole 128 KB working set of the head is in flight at once; then
+//   S <- diag(exp g) S + k^T v,  o_gla = q S           (rows reduced across waves)
+//   o_swa = softmax(meta keys, filled ring slots) . values
+// The ring slot of the new token is read from the inputs, never from the
+// ring, so no workgroup reads an entry that is being written.
+//
+// pos is shared by the H heads of a sequence: every workgroup reads it first;
+// when done, it adds 1 << 24 to it, and the workgroup that brings that
+// arrival count to H stores pos + 1 (clearing the count).  Between calls the
+// top byte of pos is zero; pos must stay below 2^24 and H below 256.
 #include "lz_common.hpp"
 #include "lz_kernels.hpp"
 
@@ -22,37 +27,54 @@ namespace lz {
 namespace {
 
 constexpr int NTHR = 256;
+constexpr int KB = 128;          // ring keys per register block
 
-template <typename T, int D, int DVT>
+template <typename T, int D>
 __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
-  constexpr int NJ = D / DVT;
   constexpr int VEC = Tr<T>::VEC;
-  constexpr int F4R = DVT / 4;                // float4 per state-slice row
-  constexpr int NS = D * F4R / NTHR;          // float4 per thread
-  static_assert(D * F4R % NTHR == 0, "state slice map");
-  constexpr int NG = NTHR / DVT;              // key groups for the value reduction
+  constexpr int F4R = D / 4;                  // float4 per state row
+  constexpr int NS = D * F4R / NTHR;          // state float4 per thread
+  constexpr int VPR = D / VEC;                // 16-byte vectors per ring row
+  constexpr int RPP = NTHR / VPR;             // ring rows per pass
+  constexpr int NR = KB / RPP;                // ring vectors per thread per block
+  static_assert(NTHR % F4R == 0 && NTHR % VPR == 0 && KB % RPP == 0, "thread maps");
 
-  extern __shared__ __align__(16) float dsm[];
-  __shared__ float sq[D], sk[D], sa[D], sv[D];
-  __shared__ float sred[NTHR / 64][DVT];
-  __shared__ float sw[NG][DVT];
+  extern __shared__ __align__(16) float slog[];   // [M + W] logits, then probabilities
+  __shared__ float sq[D], sk[D], sv[D], sa[D];
+  __shared__ float sred[NTHR / 64][D];
   __shared__ float sstat[2][NTHR / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bid = blockIdx.x;
-  const int jt = bid % NJ;
-  const int bh = bid / NJ;
+  const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh % a.H;
-  const int j0 = jt * DVT;
   const int W = a.W, M = a.M;
-  const int pos = a.pos[b];
+  unsigned int* posu = reinterpret_cast<unsigned int*>(a.pos);
+  const int pos = (int)(*reinterpret_cast<volatile unsigned int*>(posu + b) & 0x00FFFFFFu);
   const int slot = pos % W;
   const int n = min(pos + 1, W);
   const size_t vo = (size_t)bh * D;
-
   const T* qg = reinterpret_cast<const T*>(a.q) + vo;
   const T* kg = reinterpret_cast<const T*>(a.k) + vo;
   const T* vg = reinterpret_cast<const T*>(a.v) + vo;
+  float* S = a.state + (size_t)bh * D * D;
+  const T* rk = reinterpret_cast<const T*>(a.ring_k) + (size_t)bh * W * D;
+  const T* rv = reinterpret_cast<const T*>(a.ring_v) + (size_t)bh * W * D;
+
+  // ---- issue every load of the step
+  const int c4 = tid % F4R, r0 = tid / F4R;
+  f32x4 st[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+    st[u] = *reinterpret_cast<const f32x4*>(S + (size_t)(r0 + u * (NTHR / F4R)) * D + 4 * c4);
+  const int cv = tid % VPR, s0 = tid / VPR;
+  V16 kr[NR], vr[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int s = s0 + u * RPP;
+    const bool ok = s < n && s != slot;
+    kr[u] = ok ? ldg16(rk + (size_t)s * D + cv * VEC) : zero16();
+    vr[u] = ok ? ldg16(rv + (size_t)s * D + cv * VEC) : zero16();
+  }
   for (int i = tid; i < D; i += NTHR) {
     sq[i] = Tr<T>::to_f(qg[i]);
     sk[i] = Tr<T>::to_f(kg[i]);
@@ -61,29 +83,20 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- GLA: state slice update and partial q.S over this thread's rows
-  float* S = a.state + (size_t)bh * D * D + j0;
+  // ---- GLA: state update, partial q.S over this thread's rows
   f32x4 part = f32x4{0, 0, 0, 0};
-  const int c4 = tid % F4R;
   {
-    f32x4 st[NS];
+    f32x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = sv[4 * c4 + e];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const int i = (tid + u * NTHR) / F4R;
-      st[u] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + 4 * c4);
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int i = (tid + u * NTHR) / F4R;
-      const float ai = sa[i], ki = sk[i], qi = sq[i];
-      f32x4 x = st[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = ai * x[e] + ki * sv[j0 + 4 * c4 + e];
+      const int i = r0 + u * (NTHR / F4R);
+      const f32x4 x = sa[i] * st[u] + sk[i] * vv;
       *reinterpret_cast<f32x4*>(S + (size_t)i * D + 4 * c4) = x;
-      part += qi * x;
+      part += sq[i] * x;
     }
   }
-  // threads sharing c4 within a wave differ in bits above log2(F4R)
 #pragma unroll
   for (int m = F4R; m < 64; m <<= 1)
 #pragma unroll
@@ -92,37 +105,53 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) sred[wv][4 * lane + e] = part[e];
 
-  // ---- window logits over meta keys and the filled ring slots
-  float* slog = dsm;                          // [M + W]
-  const T* rk = reinterpret_cast<const T*>(a.ring_k) + (size_t)bh * W * D;
-  const T* rv = reinterpret_cast<const T*>(a.ring_v) + (size_t)bh * W * D;
-  const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
+  // ---- window logits (log2 units): meta keys, then ring slots (new token from the inputs)
   const float sl2 = a.scale * LOG2E;
   float lmax = -INFINITY;
-  for (int e = tid; e < M + n; e += NTHR) {
-    float acc = 0.f;
-    if (e < M || e - M == slot) {
-      if (e < M) {
-        const T* kr = mk + (size_t)e * D;
-        for (int d = 0; d < D; d += VEC) {
-          const V16 x = ldg16(kr + d);
+  {
+    const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
+    for (int m0 = 0; m0 < M; m0 += RPP) {   // uniform trip count across the workgroup
+      const int m = m0 + s0;
+      float acc = 0.f;
+      if (m < M) {
+        const V16 x = ldg16(mk + (size_t)m * D + cv * VEC);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc += sq[d + i] * v16_get(x, i, (T*)nullptr);
-        }
-      } else {
-        for (int d = 0; d < D; ++d) acc += sq[d] * sk[d];
+        for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(x, e, (T*)nullptr);
       }
-    } else {
-      const T* kr = rk + (size_t)(e - M) * D;
-      for (int d = 0; d < D; d += VEC) {
-        const V16 x = ldg16(kr + d);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc += sq[d + i] * v16_get(x, i, (T*)nullptr);
+      for (int o = 1; o < VPR; o <<= 1) acc = xor_sum(acc, o);
+      if (m < M) {
+        if (cv == 0) slog[m] = acc * sl2;
+        lmax = fmaxf(lmax, acc * sl2);
       }
     }
-    acc *= sl2;
-    slog[e] = acc;
-    lmax = fmaxf(lmax, acc);
+  }
+  for (int blk = 0; blk < n; blk += KB) {
+    if (blk > 0) {   // windows longer than one register block: load the next block
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int s = blk + s0 + u * RPP;
+        kr[u] = (s < n && s != slot) ? ldg16(rk + (size_t)s * D + cv * VEC) : zero16();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int s = blk + s0 + u * RPP;
+      float acc = 0.f;
+      if (s == slot) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * sk[cv * VEC + e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(kr[u], e, (T*)nullptr);
+      }
+#pragma unroll
+      for (int o = 1; o < VPR; o <<= 1) acc = xor_sum(acc, o);
+      if (s < n) {
+        if (cv == 0) slog[M + s] = acc * sl2;
+        lmax = fmaxf(lmax, acc * sl2);
+      }
+    }
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lmax = xor_max(lmax, m);
@@ -145,53 +174,82 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NTHR / 64; ++i) l += sstat[1][i];
 
-  // ---- o_swa slice: sum_p p * value, keys split over NG groups
-  {
-    const int jj = tid % DVT, grp = tid / DVT;
-    float acc = 0.f;
-    for (int s = grp; s < n; s += NG) {
-      const float vs = (s == slot) ? sv[j0 + jj] : Tr<T>::to_f(rv[(size_t)s * D + j0 + jj]);
-      acc += slog[M + s] * vs;
+  // ---- o_swa: thread sums p_s v_s over its ring rows for its VEC columns
+  float ow[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) ow[e] = 0.f;
+  for (int blk = 0; blk < n; blk += KB) {
+    if (blk > 0) {
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int s = blk + s0 + u * RPP;
+        vr[u] = (s < n && s != slot) ? ldg16(rv + (size_t)s * D + cv * VEC) : zero16();
+      }
     }
-    if (a.meta_v != nullptr && grp == 0) {
-      const T* mv = reinterpret_cast<const T*>(a.meta_v) + (size_t)h * M * D;
-      for (int m = 0; m < M; ++m) acc += slog[m] * Tr<T>::to_f(mv[(size_t)m * D + j0 + jj]);
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int s = blk + s0 + u * RPP;
+      if (s < n) {
+        const float p = slog[M + s];
+        if (s == slot) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ow[e] += p * sv[cv * VEC + e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ow[e] += p * v16_get(vr[u], e, (T*)nullptr);
+        }
+      }
     }
-    sw[grp][jj] = acc;
   }
+  if (a.meta_v != nullptr) {
+    for (int m = s0; m < M; m += RPP) {
+      const V16 x = ldg16(reinterpret_cast<const T*>(a.meta_v) + ((size_t)h * M + m) * D + cv * VEC);
+      const float p = slog[m];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ow[e] += p * v16_get(x, e, (T*)nullptr);
+    }
+  }
+  // threads sharing cv differ in the lane bits above log2(VPR), then across waves
+#pragma unroll
+  for (int m = VPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ow[e] = xor_sum(ow[e], m);
+  __syncthreads();   // sred holds the GLA partials; reuse a second copy for the window
+  __shared__ float swin[NTHR / 64][D];
+  if (lane < VPR)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) swin[wv][lane * VEC + e] = ow[e];
   __syncthreads();
-  if (tid < DVT) {
-    float osw = 0.f, og = 0.f;
+  for (int j = tid; j < D; j += NTHR) {
+    float og = 0.f, osw = 0.f;
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) osw += sw[g2][tid];
-#pragma unroll
-    for (int w2 = 0; w2 < NTHR / 64; ++w2) og += sred[w2][tid];
-    T* o = reinterpret_cast<T*>(a.o) + vo + j0 + tid;
-    *o = Tr<T>::from_f(og + a.mix * osw / l);
+    for (int w2 = 0; w2 < NTHR / 64; ++w2) {
+      og += sred[w2][j];
+      osw += swin[w2][j];
+    }
+    reinterpret_cast<T*>(a.o)[vo + j] = Tr<T>::from_f(og + a.mix * osw / l);
   }
-  // ---- ring: this workgroup's slice of the new key and value
+  // ---- ring: the new key and value into slot pos mod W
   {
     T* rkw = reinterpret_cast<T*>(a.ring_k) + ((size_t)bh * W + slot) * D;
     T* rvw = reinterpret_cast<T*>(a.ring_v) + ((size_t)bh * W + slot) * D;
-    for (int d = jt * (D / NJ) + tid; d < (jt + 1) * (D / NJ); d += NTHR) rkw[d] = kg[d];
-    for (int d = j0 + tid; d < j0 + DVT; d += NTHR) rvw[d] = vg[d];
+    for (int d = tid; d < D; d += NTHR) {
+      rkw[d] = kg[d];
+      rvw[d] = vg[d];
+    }
   }
-}
-
-__global__ void pos_advance_kernel(int32_t* pos, int B) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B) pos[i] += 1;
+  // ---- pos: the last of the H workgroups of sequence b advances it
+  if (tid == 0) {
+    __threadfence();
+    const unsigned int old = atomicAdd(posu + b, 1u << 24);
+    if ((old >> 24) == (unsigned int)(a.H - 1)) atomicExch(posu + b, (old & 0x00FFFFFFu) + 1u);
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-  constexpr int DVT = 64;
-  const int grid = a.B * a.H * (D / DVT);
   const size_t lds = sizeof(float) * (size_t)(a.M + a.W);
-  hipLaunchKernelGGL((decode_kernel<T, D, DVT>), dim3(grid), dim3(NTHR), lds, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pos_advance_kernel, dim3((a.B + 255) / 256), dim3(256), 0, st, a.pos, a.B);
+  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(a.B * a.H), dim3(NTHR), lds, st, a);
   return hipGetLastError();
 }
 

@@ -14,9 +14,11 @@
 //   (which underflows fp32 at long L) ever appears.
 //
 //   Anchor window (English page §2.A): online softmax of q_t against the M
-//   meta keys and keys s in (t-W, t], meta values optional; query/key
-//   operands come straight from global memory (L1/L2 hits), the transposed
-//   value tiles of the last three chunks live in an LDS ring.
+//   meta keys and keys s in (t-W, t], meta values optional.  The raw keys
+//   and the transposed values of the last three chunks live in LDS rings, so
+//   the window reads no global memory; the query operands are issued before
+//   the next chunk's prefetch (vector-memory counters retire in order, so a
+//   wait on them never waits for the prefetch).
 //
 //   Output (English page §2.A, final output): o = O_gla + mix * O_swa.
 //
@@ -24,6 +26,8 @@
 // holds one query's scores: row max / row sum need two cross-lane steps, and
 // the probabilities feed the next matrix product straight from registers.
 // The outputs are accumulated transposed as well (d_v x queries).
+#include <type_traits>
+
 #include "lz_common.hpp"
 #include "lz_kernels.hpp"
 
@@ -56,11 +60,13 @@ struct FwdLayout {
   static constexpr size_t oKbT = oKh + sizeof(T) * C * LDQ;
   static constexpr size_t oSt = oKbT + sizeof(T) * D * LDKT;
   static constexpr size_t oRing = oSt + sizeof(T) * DVT * LDST;
-  static constexpr size_t oMk = oRing + sizeof(T) * 3 * DVT * LDV;
+  static constexpr size_t oKring = oRing + sizeof(T) * 3 * DVT * LDV;   // raw keys of the last 3 chunks [3][C][D]
+  static constexpr size_t oMk = oKring + sizeof(T) * 3 * C * LDQ;
   static constexpr size_t oMvt = oMk + sizeof(T) * 16 * LDQ;
-  static constexpr size_t oScan = oMvt + sizeof(T) * DVT * LDMV;
-  static constexpr size_t oDec = oScan + sizeof(float) * NTG * D;
+  static constexpr size_t oScan = oKbT;                                 // gate-scan scratch aliases k^T
+  static constexpr size_t oDec = oMvt + sizeof(T) * DVT * LDMV;
   static constexpr size_t bytes = oDec + sizeof(float) * D;
+  static_assert(sizeof(float) * NTG * D <= sizeof(T) * D * LDKT, "scan scratch fits in the k^T tile");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert(NTG * TPT == C && TPT >= 1, "gate scan thread map");
   static_assert(D % 64 == 0 && DVT % 16 == 0 && DVT <= D, "tile shape");
@@ -107,6 +113,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
   T* sKbT = reinterpret_cast<T*>(smem + LY::oKbT);
   T* sSt = reinterpret_cast<T*>(smem + LY::oSt);
   T* sRing = reinterpret_cast<T*>(smem + LY::oRing);
+  T* sKring = reinterpret_cast<T*>(smem + LY::oKring);
   T* sMk = reinterpret_cast<T*>(smem + LY::oMk);
   T* sMvt = reinterpret_cast<T*>(smem + LY::oMvt);
   float* sScan = reinterpret_cast<float*>(smem + LY::oScan);
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
   const float* g = a.g + hoff;
   const float sl2 = a.scale * LOG2E;
   const int M = a.M;
-  const bool has_mv = a.meta_v != nullptr;
+  const bool has_mv = a.meta_v != nullptr;   // absent meta values are staged as zeros
 
   // ---- one-time staging: meta keys / values, zero state
   for (int e = tid; e < 16 * (D / VEC); e += NTHR) {
@@ -207,6 +214,17 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
         for (int e = 0; e < VEC; ++e) put_bits(vt_cur + (vc * VEC + e) * LY::LDV + s, rv[u], e);
       }
     }
+    {
+      T* kr = sKring + slot * C * LY::LDQ;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) *reinterpret_cast<V16*>(kr + (tg * TPT + u) * LY::LDQ + cg * VEC) = rk[u];
+    }
+    // this wave's query operands for the window, issued ahead of the next prefetch
+    const int tq = c * C + 16 * w + r;
+    frag qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = (tq < L) ? ldg_frag<T>(q + (size_t)tq * D + 32 * ks + 8 * kg) : zero_frag<T>();
 #pragma unroll
     for (int u = 1; u < TPT; ++u)
 #pragma unroll
@@ -229,6 +247,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
           if (p < tg) excl[e] += x;
         }
       }
+      __syncthreads();   // (5) scan scratch read; its region (the k^T tile) is written below
       if (tg == 0) {
 #pragma unroll
         for (int e = 0; e < GV; ++e)
@@ -261,7 +280,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
     }
 
     const int qlo = c * C + 16 * w;       // first query of this wave
-    const int tq = qlo + r;               // this lane's query
     // (7) GLA: O^T = V^T (q~ k^T masked)^T + S^T q~^T
     f32x4 OG[JB];
 #pragma unroll
@@ -276,6 +294,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
           for (int ks = 0; ks < KS; ++ks)
             mma32(sc[kb], ld_frag(sKh, LY::LDQ, 16 * kb + r, 32 * ks + 8 * kg),
                   ld_frag(sQt, LY::LDQ, 16 * w + r, 32 * ks + 8 * kg));
+          mfma_drain();
           if (kb == w) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -305,11 +324,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < JB; ++j) OW[j] = f32x4{0, 0, 0, 0};
     float mrun = -INFINITY, lpart = 0.f;
-    frag qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = (tq < L) ? ldg_frag<T>(q + (size_t)tq * D + 32 * ks + 8 * kg) : zero_frag<T>();
-
     if (M > 0) {
       f32x4 xm[1];
       xm[0] = f32x4{0, 0, 0, 0};
@@ -318,19 +332,22 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
         mma32(xm[0], ld_frag(sMk, LY::LDQ, r, 32 * ks + 8 * kg), qf[ks]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xm[0][i] = (4 * kg + i < M) ? xm[0][i] * sl2 : -INFINITY;
+      mfma_drain();
       absorb<1, JB>(xm, mrun, lpart, OW);
-      if (has_mv) {
+      {   // meta values (zero-filled in LDS when absent: no branch around the product)
         frag bop;
         pack_acc(bop, xm[0], f32x4{0, 0, 0, 0});
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) mma32(OW[jb], ld_frag_perm(sMvt, LY::LDMV, 16 * jb + r, 0, 0, kg), bop);
       }
+      mfma_drain();
     }
 
     const int kt_lo = max(0, c * C - a.W + 1) / C;   // oldest key tile any query of the chunk sees
     for (int kt = c; kt >= kt_lo; --kt) {
       const int kbase = kt * C;
       const T* vt = sRing + (kt % 3) * DVT * LY::LDV;
+      const T* kt_rows = sKring + (kt % 3) * C * LY::LDQ;
       f32x4 x[4];
       bool vis[4];
 #pragma unroll
@@ -339,12 +356,10 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
         vis[kb] = (s0 <= qlo + 15) && (s0 + 15 >= qlo - a.W + 1);
         x[kb] = f32x4{0, 0, 0, 0};
         if (vis[kb]) {
-          const int srow = s0 + r;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const frag kf = (srow < L) ? ldg_frag<T>(k + (size_t)srow * D + 32 * ks + 8 * kg) : zero_frag<T>();
-            mma32(x[kb], kf, qf[ks]);
-          }
+          for (int ks = 0; ks < KS; ++ks)
+            mma32(x[kb], ld_frag(kt_rows, LY::LDQ, 16 * kb + r, 32 * ks + 8 * kg), qf[ks]);
+          mfma_drain();
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -366,6 +381,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
     }
 
     // (9) epilogue: o = O_gla + mix * O_swa / l, optional lse and o_swa
+    mfma_drain();
     {
       float l = xor_sum(xor_sum(lpart, 16), 32);
       const float inv = 1.f / l;
@@ -451,9 +467,11 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 
 template <typename T, int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t st) {
-  // smallest d_v tile that still gives >= 256 workgroups (256 CUs), at most 64 wide
+  // widest d_v tile (64 for bf16, 32 for fp32: LDS) that still gives >= 240 workgroups
   const long bh = (long)a.B * a.H;
-  if (bh * (D / 64) >= 240) return launch_fwd_t<T, D, 64>(a, st);
+  if constexpr (!std::is_same<T, float>::value) {
+    if (bh * (D / 64) >= 240) return launch_fwd_t<T, D, 64>(a, st);
+  }
   if (bh * (D / 32) >= 240) return launch_fwd_t<T, D, 32>(a, st);
   return launch_fwd_t<T, D, 16>(a, st);
 }

@@ -140,7 +140,9 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
  *   q, k [B,H,d_k], v [B,H,d_v] (dtype), g [B,H,d_k] fp32: the new token
  *   state  in/out: S <- diag(exp g) S + k^T v (fp32)
  *   ring_k, ring_v in/out: the new key/value is stored in slot pos[b] mod W
- *   pos    in/out, device int32 [B]: tokens already consumed; incremented
+ *   pos    in/out, device int32 [B]: tokens already consumed, < 2^24; its top
+ *          byte is used as an arrival count during the call (zero before and
+ *          after; H <= 255); incremented
  *   o      [B,H,d_v] written: q S + mix * softmax over M meta keys and the
  *          min(pos+1, W) filled ring slots.
  * Uses s->B, H, d_k, d_v, W, M, scale, mix, dtype; s->L and s->chunk are ignored. */

@@ -111,3 +111,26 @@ def test_train_8k_full_size_sampled():
         print("train_8k head", h, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
         for n, e in errs.items():
             assert e <= TOL["bf16"], (h, n, e)
+
+
+@pytest.mark.parametrize("dtname,D,with_mv", [("fp32", 64, False), ("fp32", 64, True), ("bf16", 128, False)])
+def test_forward_backward_bit_reproducible(dtname, D, with_mv):
+    """Same inputs, same launches -> bit-identical outputs and gradients (no
+    atomics or races anywhere in the path)."""
+    x = make_small(2, 2, 300, D, 4, seed=21, bf16=(dtname == "bf16"), with_meta_v=with_mv)
+    dt = tdtype(dtname)
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v", "dO", "meta_k")}
+    T["g"] = dev(x["g"], torch.float32)
+    mv = dev(x["meta_v"], dt) if with_mv else None
+    outs = []
+    for _ in range(3):
+        f = lizard_attn_fwd(T["q"], T["k"], T["v"], T["g"], T["meta_k"], mv, window=128,
+                            want_lse=True, want_o_swa=True, want_chunk_states=True, want_state=True)
+        b = lizard_attn_bwd(T["q"], T["k"], T["v"], T["g"], T["meta_k"], mv, T["dO"], f["lse"],
+                            f["o_swa"], f["chunk_states"], window=128)
+        torch.cuda.synchronize()
+        outs.append({**{n: f[n].clone() for n in ("o", "lse", "o_swa", "chunk_states", "state")},
+                     **{n: t.clone() for n, t in b.items() if t is not None}})
+    for n in outs[0]:
+        for o in outs[1:]:
+            assert torch.equal(outs[0][n], o[n]), n
