@@ -127,10 +127,11 @@ __device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot
 template <typename T, int D>
 struct DsLayout {
   static constexpr int PAD = Tr<T>::PAD;
-  static constexpr int LDC = C + PAD;
-  static constexpr size_t oQtT = 0;                                     // [D][C]   q~^T
-  static constexpr size_t odOT = oQtT + sizeof(T) * D * LDC;            // [DVTA][C] dO^T slice
-  static constexpr size_t oScan = odOT + sizeof(T) * DVTA * LDC;
+  static constexpr int LDQ = D + PAD;
+  static constexpr int LDO = DVTA + PAD;
+  static constexpr size_t oQt = 0;                                      // [C][D]    q~ (row-major)
+  static constexpr size_t odO = oQt + sizeof(T) * C * LDQ;             // [C][DVTA] dO slice (row-major)
+  static constexpr size_t oScan = odO + sizeof(T) * C * LDO;
   static constexpr size_t oDec = oScan + sizeof(float) * (NTHR / (D / Tr<T>::VEC)) * D;
   static constexpr size_t bytes = oDec + sizeof(float) * D;
 };
@@ -146,8 +147,8 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
   constexpr int VVR = DVTA / VEC, NVV = (C * VVR + NTHR - 1) / NTHR;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  T* sQtT = reinterpret_cast<T*>(smem + LY::oQtT);
-  T* sdOT = reinterpret_cast<T*>(smem + LY::odOT);
+  T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
+  T* sdO = reinterpret_cast<T*>(smem + LY::odO);
   float* sScan = reinterpret_cast<float*>(smem + LY::oScan);
   float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
 
@@ -224,8 +225,7 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
       const int idx = tid + u * NTHR;
       if (idx < C * VVR) {
         const int s = idx / VVR, vc = idx % VVR;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) put_bits(sdOT + (vc * VEC + e) * LY::LDC + s, rd[u], e);
+        *reinterpret_cast<V16*>(sdO + s * LY::LDO + vc * VEC) = rd[u];
       }
     }
     f32x4 tot[GV];
@@ -236,12 +236,12 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
 #pragma unroll
         for (int i = 0; i < 4; ++i) sDec[cg * VEC + 4 * e + i] = __expf(tot[e][i]);
 #pragma unroll
-    for (int u = 0; u < TPT; ++u)
+    for (int u = 0; u < TPT; ++u) {
+      float qt[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float qt = v16_get(rq[u], e, (T*)nullptr) * __expf(rg[u][e >> 2][e & 3]);
-        put_elem(sQtT + (cg * VEC + e) * LY::LDC + tg * TPT + u, qt);
-      }
+      for (int e = 0; e < VEC; ++e) qt[e] = v16_get(rq[u], e, (T*)nullptr) * __expf(rg[u][e >> 2][e & 3]);
+      st_vec(sQt + (tg * TPT + u) * LY::LDQ + cg * VEC, qt);
+    }
     if (c > 0) prefetch(c - 1);
     __syncthreads();
 
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int ks = 0; ks < C / 32; ++ks)
-          mma32(acc[ib][jb], ld_frag(sQtT, LY::LDC, i0 + r, 32 * ks + 8 * kg),
-                ld_frag(sdOT, LY::LDC, 16 * jb + r, 32 * ks + 8 * kg));
+          mma32(acc[ib][jb], ld_frag_tr(sQt, LY::LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, i0, lane),
+                ld_frag_tr(sdO, LY::LDO, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane));
     }
   }
 }
@@ -289,16 +289,14 @@ __global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restric
 template <typename T, int D>
 struct CkLayout {
   static constexpr int PAD = Tr<T>::PAD;
-  static constexpr int LDQ = D + PAD;    // [C][D] rows and [D][D] rows
-  static constexpr int LDC = C + PAD;    // [D][C] transposed tiles
+  static constexpr int LDQ = D + PAD;    // row-major [C][D] and [D][D] tiles
+  static constexpr int LDC = C + PAD;    // [16][C] meta tiles
   static constexpr int LDM = 16 + PAD;   // [D][16] meta keys transposed
-  static constexpr size_t oQt = 0;                                   // q~   [C][D]
-  static constexpr size_t oKh = oQt + sizeof(T) * C * LDQ;           // k^   [C][D]
+  static constexpr size_t oQt = 0;                                   // q~   [C][D]  (later raw q of a chunk)
+  static constexpr size_t oKh = oQt + sizeof(T) * C * LDQ;           // k^   [C][D]  (later dO of another chunk)
   static constexpr size_t oEb = oKh + sizeof(T) * C * LDQ;           // e^b  [C][D]
-  static constexpr size_t oQtT = oEb + sizeof(T) * C * LDQ;          // q~^T [D][C]  (later raw q^T)
-  static constexpr size_t oKhT = oQtT + sizeof(T) * D * LDC;         // k^^T [D][C]  (later dO^T of another chunk)
-  static constexpr size_t odOT = oKhT + sizeof(T) * D * LDC;         // dO^T [D][C]
-  static constexpr size_t oBig = odOT + sizeof(T) * D * LDC;         // dS' [D][D] | scan | db | K^T
+  static constexpr size_t odO = oEb + sizeof(T) * C * LDQ;           // dO   [C][D]
+  static constexpr size_t oBig = odO + sizeof(T) * C * LDQ;          // dS'^T [D][D] | scan | db | key tile
   static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * D ? sizeof(T) * D * LDQ
                                                                                  : sizeof(float) * C * D;
   static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
@@ -321,19 +319,18 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   constexpr int NBH = NB / 2;    // blocks per wave (the two waves of a token block split them)
   constexpr int KS = D / 32;     // K steps over the head dim
   constexpr int NJ = D / DVTA;
-
+  constexpr int LDQ = LY::LDQ;
   static_assert(sizeof(float) * SM::NTG * D <= LY::bigBytes, "scan scratch fits in the shared region");
+
   extern __shared__ __align__(16) unsigned char smem[];
   T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
   T* sKh = reinterpret_cast<T*>(smem + LY::oKh);
   T* sEb = reinterpret_cast<T*>(smem + LY::oEb);
-  T* sQtT = reinterpret_cast<T*>(smem + LY::oQtT);
-  T* sKhT = reinterpret_cast<T*>(smem + LY::oKhT);
-  T* sdOT = reinterpret_cast<T*>(smem + LY::odOT);
-  T* sdSp = reinterpret_cast<T*>(smem + LY::oBig);
+  T* sdO = reinterpret_cast<T*>(smem + LY::odO);
+  T* sdSt = reinterpret_cast<T*>(smem + LY::oBig);          // dS' transposed [j][i], row-major
   float* sScan = reinterpret_cast<float*>(smem + LY::oBig);
   float* sDb = reinterpret_cast<float*>(smem + LY::oBig);
-  T* sKT = reinterpret_cast<T*>(smem + LY::oBig);
+  T* sKt = reinterpret_cast<T*>(smem + LY::oBig);           // raw keys of a window chunk [C][D]
   T* sMkT = reinterpret_cast<T*>(smem + LY::oMkT);
   T* sDLm = reinterpret_cast<T*>(smem + LY::oDLm);
   T* sPm = reinterpret_cast<T*>(smem + LY::oPm);
@@ -341,7 +338,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
-  const int wb = w & 3;          // token block of this wave (rows 16*wb .. +16 of the chunk)
+  const int wb = w & 3;            // token block of this wave (rows 16*wb .. +16 of the chunk)
   const int nb0 = (w >> 2) * NBH;  // first of this wave's output column blocks
   const int L = a.L, NC = (L + C - 1) / C, W = a.W, M = a.M;
   // workgroup -> (chunk, head); consecutive chunks of one head share an XCD
@@ -373,10 +370,19 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const float mix = a.mix, scale = a.scale;
   const int t0 = c * C;
 
+  // Copy a [C][D] row-major chunk tile (rows past L are zero) into LDS.
+  auto stage_rows = [&](T* dst, const T* src, int row0) {
+    for (int e = tid; e < C * (D / VEC); e += NTHR_CK) {
+      const int t = e / (D / VEC), cv = e % (D / VEC);
+      *reinterpret_cast<V16*>(dst + t * LDQ + cv * VEC) =
+          (row0 + t < L) ? ldg16(src + (size_t)(row0 + t) * D + cv * VEC) : zero16();
+    }
+  };
+
   // ---------------------------------------------------------------- staging
   const int cg = tid % SM::VPR, tg = tid / SM::VPR;
   {
-    V16 rq[TPT], rk[TPT], rd[TPT];
+    V16 rq[TPT], rk[TPT];
     f32x4 rg[TPT][GV];
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
@@ -384,11 +390,11 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       const bool ok = t < L;
       rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
       rk[u] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
-      rd[u] = ok ? ldg16(dO + (size_t)t * D + cg * VEC) : zero16();
 #pragma unroll
       for (int e = 0; e < GV; ++e)
         rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
     }
+    stage_rows(sdO, dO, t0);
     // meta keys transposed, lse / delta of this chunk and the next two
     for (int e = tid; e < D * 16; e += NTHR_CK) {
       const int d = e / 16, m = e % 16;
@@ -411,20 +417,15 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         eb[e] = __expf(bb);
         qt[e] = v16_get(rq[u], e, (T*)nullptr) * eb[e];
         kh[e] = v16_get(rk[u], e, (T*)nullptr) * __expf(-bb);
-        put_elem(sQtT + (cg * VEC + e) * LY::LDC + t, qt[e]);
-        put_elem(sKhT + (cg * VEC + e) * LY::LDC + t, kh[e]);
-        put_bits(sdOT + (cg * VEC + e) * LY::LDC + t, rd[u], e);
       }
-      st_vec(sQt + t * LY::LDQ + cg * VEC, qt);
-      st_vec(sKh + t * LY::LDQ + cg * VEC, kh);
-      st_vec(sEb + t * LY::LDQ + cg * VEC, eb);
+      st_vec(sQt + t * LDQ + cg * VEC, qt);
+      st_vec(sKh + t * LDQ + cg * VEC, kh);
+      st_vec(sEb + t * LDQ + cg * VEC, eb);
     }
-    __syncthreads();   // scan scratch is dead: stage dS' (row-major) into the same region
+    __syncthreads();   // scan scratch is dead: stage dS' (transposed, as stored) into the same region
     for (int e = tid; e < D * (D / VEC); e += NTHR_CK) {
       const int j = e / (D / VEC), cv = e % (D / VEC);
-      const V16 x = ldg16(dSpT + (size_t)j * D + cv * VEC);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) put_bits(sdSp + (cv * VEC + i) * LY::LDQ + j, x, i);
+      *reinterpret_cast<V16*>(sdSt + j * LDQ + cv * VEC) = ldg16(dSpT + (size_t)j * D + cv * VEC);
     }
     __syncthreads();
   }
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     frag fo[KS], fvu[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      fo[ks] = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
+      fo[ks] = ld_frag(sdO, LDQ, 16 * wb + r, 32 * ks + 8 * kg);
       fvu[ks] = ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L);
     }
     // dq~ intra: dA^T blocks (keys sb <= wb, queries of block wb), then times k^
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
         for (int x = 0; x < NBH; ++x)
-          mma32(accQ[x], op, ld_frag_perm(sKhT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
+          mma32(accQ[x], op, ld_frag_tr(sKh, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
       }
     // dq~ inter: dO S_prev^T
 #pragma unroll
@@ -486,8 +487,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       if (tb >= wb) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          mma32(blk[tb], ld_frag(sQt, LY::LDQ, 16 * tb + r, 32 * ks + 8 * kg),
-                ld_frag(sKh, LY::LDQ, 16 * wb + r, 32 * ks + 8 * kg));
+          mma32(blk[tb], ld_frag(sQt, LDQ, 16 * tb + r, 32 * ks + 8 * kg),
+                ld_frag(sKh, LDQ, 16 * wb + r, 32 * ks + 8 * kg));
         mfma_drain();
         if (tb == wb)
 #pragma unroll
@@ -502,18 +503,15 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
         for (int x = 0; x < NBH; ++x)
-          mma32(accV[x], op, ld_frag_perm(sdOT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
+          mma32(accV[x], op, ld_frag_tr(sdO, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
       }
     // dk^ intra: dA blocks (queries tb >= wb, keys of block wb), dA^T q~
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       blk[tb] = f32x4{0, 0, 0, 0};
       if (tb >= wb) {
-        frag fd[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) fd[ks] = ldg_row_frag<T>(dO, D, t0 + 16 * tb + r, 32 * ks + 8 * kg, L);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], fd[ks], fvu[ks]);
+        for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sdO, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fvu[ks]);
         mfma_drain();
         if (tb == wb)
 #pragma unroll
@@ -528,24 +526,21 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
         for (int x = 0; x < NBH; ++x)
-          mma32(accK[x], op, ld_frag_perm(sQtT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
+          mma32(accK[x], op, ld_frag_tr(sQt, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
       }
-    // inter-chunk: dk^ += V dS'^T ; dv += k^ dS'
+    // inter-chunk: dk^ += V dS'^T (dS' read down the columns of its transpose) ; dv += k^ dS'
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      frag fd[NBH];
-#pragma unroll
-      for (int x = 0; x < NBH; ++x) fd[x] = ldg_frag<T>(dSpT + (size_t)(16 * (nb0 + x) + r) * D + 32 * ks + 8 * kg);
-      const frag fk = ld_frag(sKh, LY::LDQ, 16 * wb + r, 32 * ks + 8 * kg);
+      const frag fk = ld_frag(sKh, LDQ, 16 * wb + r, 32 * ks + 8 * kg);
 #pragma unroll
       for (int x = 0; x < NBH; ++x) {
-        mma32(accK[x], fvu[ks], ld_frag(sdSp, LY::LDQ, 16 * (nb0 + x) + r, 32 * ks + 8 * kg));
-        mma32(accV[x], fk, fd[x]);
+        mma32(accK[x], fvu[ks], ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * (nb0 + x), lane));
+        mma32(accV[x], fk, ld_frag(sdSt, LDQ, 16 * (nb0 + x) + r, 32 * ks + 8 * kg));
       }
     }
   }
   mfma_drain();
-  __syncthreads();   // every wave is done with sdSp: its region now holds the per-token gate gradient
+  __syncthreads();   // every wave is done with dS': its region now holds the per-token gate gradient
 
   // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b
 #pragma unroll
@@ -554,9 +549,9 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int u = 16 * wb + 4 * kg + e;
-      const float qt = Tr<T>::to_f(sQt[u * LY::LDQ + i]);
-      const float kh = Tr<T>::to_f(sKh[u * LY::LDQ + i]);
-      const float eb = Tr<T>::to_f(sEb[u * LY::LDQ + i]);
+      const float qt = Tr<T>::to_f(sQt[u * LDQ + i]);
+      const float kh = Tr<T>::to_f(sKh[u * LDQ + i]);
+      const float eb = Tr<T>::to_f(sEb[u * LDQ + i]);
       sDb[u * D + i] = qt * accQ[x][e] - kh * accK[x][e];
       accQ[x][e] *= eb;
       accK[x][e] *= 1.f / eb;
@@ -583,14 +578,14 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       if (t < L) a.dg[hoff + (size_t)t * D + i] = sDb[u * D + i] + carry;
     }
   }
-  __syncthreads();   // sDb dead: the region is reused for key tiles
+  __syncthreads();   // sDb, q~, k^ dead: their regions now hold window tiles
 
   // ------------------------------------------- anchor window, query side (dq)
   frag qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qf[ks] = ldg_row_frag<T>(q, D, urow, 32 * ks + 8 * kg, L);
-    of[ks] = ldg_row_frag<T>(dO, D, urow, 32 * ks + 8 * kg, L);
+    of[ks] = ld_frag(sdO, LDQ, 16 * wb + r, 32 * ks + 8 * kg);
   }
   const int tq = urow;                             // this lane's query
   const float lse2 = sLse[16 * wb + r], delq = sDel[16 * wb + r];
@@ -606,12 +601,11 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), of[ks]);
     }
     mfma_drain();
-    f32x4 dl, pm;
+    f32x4 dl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * kg + i;
       const float p = (m < M && qvalid) ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
-      pm[i] = p;
       dl[i] = p * (mix * dp[i] - delq) * scale;
       if (nb0 == 0) {
         put_elem(sDLm + m * LY::LDC + 16 * wb + r, dl[i]);
@@ -628,13 +622,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const int qlo = t0 + 16 * wb;
   for (int kt = c; kt >= kt_lo; --kt) {
     const int kbase = kt * C;
-    // K^T tile of chunk kt
-    for (int e = tid; e < C * (D / VEC); e += NTHR_CK) {
-      const int s = e / (D / VEC), cv = e % (D / VEC);
-      const V16 x = (kbase + s < L) ? ldg16(k + (size_t)(kbase + s) * D + cv * VEC) : zero16();
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) put_bits(sKT + (cv * VEC + i) * LY::LDC + s, x, i);
-    }
+    stage_rows(sKt, k, kbase);
+    __syncthreads();   // key tile of chunk kt staged
     f32x4 dl[4];
     bool vis[4];
 #pragma unroll
@@ -643,15 +632,12 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       vis[kb] = (s0 <= qlo + 15) && (s0 + 15 >= qlo - W + 1);
       f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
       if (vis[kb]) {
-        frag fk[KS], fv[KS];
+        frag fv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) fv[ks] = ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          fk[ks] = ldg_row_frag<T>(k, D, s0 + r, 32 * ks + 8 * kg, L);
-          fv[ks] = ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          mma32(x, fk[ks], qf[ks]);
+          mma32(x, ld_frag(sKt, LDQ, 16 * kb + r, 32 * ks + 8 * kg), qf[ks]);
           mma32(dp, fv[ks], of[ks]);
         }
         mfma_drain();
@@ -664,7 +650,6 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         dl[kb][i] = p * (mix * dp[i] - delq) * scale;
       }
     }
-    __syncthreads();   // K^T tile staged
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       if (vis[2 * p] || vis[2 * p + 1]) {
@@ -672,7 +657,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         pack_acc(op, dl[2 * p], dl[2 * p + 1]);
 #pragma unroll
         for (int x = 0; x < NBH; ++x)
-          mma32(accQ[x], op, ld_frag_perm(sKT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
+          mma32(accQ[x], op, ld_frag_tr(sKt, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
       }
     __syncthreads();
   }
@@ -686,22 +671,13 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     vf[ks] = ldg_row_frag<T>(v, D, srow, 32 * ks + 8 * kg, L);
   }
   const int qc_hi = min(NC - 1, (t0 + C - 1 + W - 1) / C);
-  T* sQT = sQtT;                                    // raw q^T of the query chunk
+  T* sQr = sQt;                                    // raw q of the query chunk (row-major)
   for (int qc = c; qc <= qc_hi; ++qc) {
     const int qbase = qc * C;
-    T* dOT = (qc == c) ? sdOT : sKhT;
-    for (int e = tid; e < C * (D / VEC); e += NTHR_CK) {
-      const int t = e / (D / VEC), cv = e % (D / VEC);
-      const bool ok = qbase + t < L;
-      const V16 x = ok ? ldg16(q + (size_t)(qbase + t) * D + cv * VEC) : zero16();
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) put_bits(sQT + (cv * VEC + i) * LY::LDC + t, x, i);
-      if (qc != c) {
-        const V16 y = ok ? ldg16(dO + (size_t)(qbase + t) * D + cv * VEC) : zero16();
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) put_bits(dOT + (cv * VEC + i) * LY::LDC + t, y, i);
-      }
-    }
+    T* dOr = (qc == c) ? sdO : sKh;                // dO of the query chunk (row-major)
+    stage_rows(sQr, q, qbase);
+    if (qc != c) stage_rows(dOr, dO, qbase);
+    __syncthreads();   // q / dO of chunk qc staged
     const int slo = t0 + 16 * wb;                  // first key of this wave
     f32x4 dl[4], pp[4];
     bool vis[4];
@@ -711,16 +687,10 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       vis[tb] = (q0 + 15 >= slo) && (q0 <= slo + 15 + W - 1);
       f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
       if (vis[tb]) {
-        frag fq[KS], fd[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          fq[ks] = ldg_row_frag<T>(q, D, q0 + r, 32 * ks + 8 * kg, L);
-          fd[ks] = ldg_row_frag<T>(dO, D, q0 + r, 32 * ks + 8 * kg, L);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          mma32(x, fq[ks], kf[ks]);
-          mma32(dp, fd[ks], vf[ks]);
+          mma32(x, ld_frag(sQr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), kf[ks]);
+          mma32(dp, ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), vf[ks]);
         }
         mfma_drain();
       }
@@ -735,7 +705,6 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         dl[tb][i] = p * (mix * dp[i] - sDel[li]) * scale;
       }
     }
-    __syncthreads();   // q^T / dO^T of chunk qc staged
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       if (vis[2 * p] || vis[2 * p + 1]) {
@@ -744,8 +713,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         pack_acc(opp, pp[2 * p], pp[2 * p + 1]);
 #pragma unroll
         for (int x = 0; x < NBH; ++x) {
-          mma32(accK[x], opl, ld_frag_perm(sQT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
-          mma32(accV[x], opp, ld_frag_perm(dOT, LY::LDC, 16 * (nb0 + x) + r, 2 * p, 2 * p + 1, kg));
+          mma32(accK[x], opl, ld_frag_tr(sQr, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
+          mma32(accV[x], opp, ld_frag_tr(dOr, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
         }
       }
     // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
@@ -755,8 +724,10 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
-        mma32(xk, ld_frag(sQT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
-        mma32(xv, ld_frag(sdOT, LY::LDC, d0 + r, 32 * ks + 8 * kg), ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
+        mma32(xk, ld_frag_tr(sQr, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
+              ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
+        mma32(xv, ld_frag_tr(sdO, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
+              ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
       }
       mfma_drain();
       if (r < M)

@@ -86,6 +86,38 @@ __device__ __forceinline__ f32x8 ld_frag_perm(const float* base, int ld, int row
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Operand whose row/column index runs along the COLUMNS of a row-major LDS
+// tile and whose K index runs down its ROWS (a transposed read).  Lane l
+// gets tile[ra + e][c0 + (l & 15)] in slots e = 0..3 and
+// tile[rb + e][c0 + (l & 15)] in slots 4..7, where ra / rb are chosen per
+// 16-lane group by the caller (ra = k0 + 8*kg, rb = ra + 4 for the plain K
+// order; ra = 16*kb0 + 4*kg, rb = 16*kb1 + 4*kg for the accumulator-fed
+// order).  bf16 uses the gfx950 LDS transpose read: within a 16-lane group,
+// lane k addresses row r + k/4, columns c0 + 4*(k%4) .. +4, and lane j
+// receives the four values of column c0 + j from rows r .. r+3 (layout
+// established with an in-bounds probe).  fp32 reads the four values directly.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ bf16x4 tr4(const bf16_t* tile, int ld, int r, int c0, int lane) {
+  const int k = lane & 15;
+  const bf16_t* p = tile + (r + (k >> 2)) * ld + c0 + 4 * (k & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 ld_frag_tr(const bf16_t* tile, int ld, int ra, int rb, int c0, int lane) {
+  const bf16x4 a = tr4(tile, ld, ra, c0, lane);
+  const bf16x4 b = tr4(tile, ld, rb, c0, lane);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x8 ld_frag_tr(const float* tile, int ld, int ra, int rb, int c0, int lane) {
+  const int c = c0 + (lane & 15);
+  f32x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = tile[(ra + e) * ld + c];
+    f[4 + e] = tile[(rb + e) * ld + c];
+  }
+  return f;
+}
+
 // Accumulators of key blocks kb0, kb1 as an operand (slot order as above).
 __device__ __forceinline__ void pack_acc(bf16x8& out, const f32x4& a, const f32x4& b) {
   out = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],

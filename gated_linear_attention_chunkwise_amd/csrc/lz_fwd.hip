@@ -42,9 +42,8 @@ struct FwdLayout {
   static constexpr int PAD = Tr<T>::PAD;
   static constexpr int VEC = Tr<T>::VEC;
   static constexpr int LDQ = D + PAD;     // sQt, sKh, sMk rows
-  static constexpr int LDKT = C + PAD;    // sKbT: [D][C]
   static constexpr int LDST = D + PAD;    // sSt : [DVT][D]  (transposed state, operand type)
-  static constexpr int LDV = C + PAD;     // ring: [3][DVT][C] (transposed value tiles)
+  static constexpr int LDVR = DVT + PAD;  // ring: [3][C][DVT] value tiles, row-major
   static constexpr int LDMV = 16 + PAD;   // sMvt: [DVT][16]
   static constexpr int VPR = D / VEC;     // 16-byte vectors per q/k row
   static constexpr int NTG = NTHR / VPR;  // token groups of the gate scan
@@ -57,16 +56,14 @@ struct FwdLayout {
   static constexpr int KS = D / 32;       // K steps over the head dim
   static constexpr size_t oQt = 0;
   static constexpr size_t oKh = oQt + sizeof(T) * C * LDQ;
-  static constexpr size_t oKbT = oKh + sizeof(T) * C * LDQ;
-  static constexpr size_t oSt = oKbT + sizeof(T) * D * LDKT;
+  static constexpr size_t oSt = oKh + sizeof(T) * C * LDQ;
   static constexpr size_t oRing = oSt + sizeof(T) * DVT * LDST;
-  static constexpr size_t oKring = oRing + sizeof(T) * 3 * DVT * LDV;   // raw keys of the last 3 chunks [3][C][D]
+  static constexpr size_t oKring = oRing + sizeof(T) * 3 * C * LDVR;   // raw keys of the last 3 chunks [3][C][D]
   static constexpr size_t oMk = oKring + sizeof(T) * 3 * C * LDQ;
   static constexpr size_t oMvt = oMk + sizeof(T) * 16 * LDQ;
-  static constexpr size_t oScan = oKbT;                                 // gate-scan scratch aliases k^T
-  static constexpr size_t oDec = oMvt + sizeof(T) * DVT * LDMV;
+  static constexpr size_t oScan = oMvt + sizeof(T) * DVT * LDMV;
+  static constexpr size_t oDec = oScan + sizeof(float) * NTG * D;
   static constexpr size_t bytes = oDec + sizeof(float) * D;
-  static_assert(sizeof(float) * NTG * D <= sizeof(T) * D * LDKT, "scan scratch fits in the k^T tile");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert(NTG * TPT == C && TPT >= 1, "gate scan thread map");
   static_assert(D % 64 == 0 && DVT % 16 == 0 && DVT <= D, "tile shape");
@@ -110,7 +107,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
   T* sKh = reinterpret_cast<T*>(smem + LY::oKh);
-  T* sKbT = reinterpret_cast<T*>(smem + LY::oKbT);
   T* sSt = reinterpret_cast<T*>(smem + LY::oSt);
   T* sRing = reinterpret_cast<T*>(smem + LY::oRing);
   T* sKring = reinterpret_cast<T*>(smem + LY::oKring);
@@ -201,17 +197,16 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
 
   for (int c = 0; c < NC; ++c) {
     const int slot = c % 3;
-    T* vt_cur = sRing + slot * DVT * LY::LDV;
+    T* vt_cur = sRing + slot * C * LY::LDVR;
     __syncthreads();   // (1) previous chunk's readers of every staged tile are done
 
-    // (2) value tile -> ring (transposed); local gate prefix -> scan scratch
+    // (2) value tile and raw keys -> rings (row-major); local gate prefix -> scan scratch
 #pragma unroll
     for (int u = 0; u < LY::NVV; ++u) {
       const int idx = tid + u * NTHR;
       if (idx < C * LY::VVR) {
         const int s = idx / LY::VVR, vc = idx % LY::VVR;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) put_bits(vt_cur + (vc * VEC + e) * LY::LDV + s, rv[u], e);
+        *reinterpret_cast<V16*>(vt_cur + s * LY::LDVR + vc * VEC) = rv[u];
       }
     }
     {
@@ -247,7 +242,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
           if (p < tg) excl[e] += x;
         }
       }
-      __syncthreads();   // (5) scan scratch read; its region (the k^T tile) is written below
       if (tg == 0) {
 #pragma unroll
         for (int e = 0; e < GV; ++e)
@@ -266,8 +260,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
         const int t = tg * TPT + u;
         st_vec(sQt + t * LY::LDQ + cg * VEC, qt);
         st_vec(sKh + t * LY::LDQ + cg * VEC, kh);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) put_elem(sKbT + (cg * VEC + e) * LY::LDKT + t, kh[e]);
       }
     }
     if (c + 1 < NC) prefetch(c + 1);
@@ -309,7 +301,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
           if (2 * p <= w) {
             frag bop;
             pack_acc(bop, sc[2 * p], sc[2 * p + 1]);
-            mma32(OG[jb], ld_frag_perm(vt_cur, LY::LDV, 16 * jb + r, 2 * p, 2 * p + 1, kg), bop);
+            mma32(OG[jb], ld_frag_tr(vt_cur, LY::LDVR, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane), bop);
           }
         }
 #pragma unroll
@@ -346,7 +338,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
     const int kt_lo = max(0, c * C - a.W + 1) / C;   // oldest key tile any query of the chunk sees
     for (int kt = c; kt >= kt_lo; --kt) {
       const int kbase = kt * C;
-      const T* vt = sRing + (kt % 3) * DVT * LY::LDV;
+      const T* vt = sRing + (kt % 3) * C * LY::LDVR;
       const T* kt_rows = sKring + (kt % 3) * C * LY::LDQ;
       f32x4 x[4];
       bool vis[4];
@@ -376,7 +368,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
           if (vis[2 * p] || vis[2 * p + 1]) {
             frag bop;
             pack_acc(bop, x[2 * p], x[2 * p + 1]);
-            mma32(OW[jb], ld_frag_perm(vt, LY::LDV, 16 * jb + r, 2 * p, 2 * p + 1, kg), bop);
+            mma32(OW[jb], ld_frag_tr(vt, LY::LDVR, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane), bop);
           }
     }
 
@@ -419,8 +411,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdArgs a) {
         for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
           for (int ks = 0; ks < C / 32; ++ks)
-            mma32(accS[ib][jb], ld_frag(sKbT, LY::LDKT, i0 + r, 32 * ks + 8 * kg),
-                  ld_frag(vt_cur, LY::LDV, 16 * jb + r, 32 * ks + 8 * kg));
+            mma32(accS[ib][jb], ld_frag_tr(sKh, LY::LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, i0, lane),
+                  ld_frag_tr(vt_cur, LY::LDVR, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane));
 #pragma unroll
           for (int i = 0; i < 4; ++i) accS[ib][jb][i] *= dec[i];
           st4(sSt + (16 * jb + r) * LY::LDST + i0 + 4 * kg, accS[ib][jb][0], accS[ib][jb][1],
