@@ -199,8 +199,8 @@ def bench_decode(args, hip, torch, lib):
     ring_k[:, :, ts % w.W] = pre["k"][:, :, ts]
     ring_v[:, :, ts % w.W] = pre["v"][:, :, ts]
     pos = torch.full((w.B,), P, device="cuda", dtype=torch.int32)
-    steps = L - P
-    tok = {n: x[n][:, :, P:].permute(2, 0, 1, 3).contiguous() for n in ("q", "k", "v", "g")}
+    steps = L - P if args.decode_steps is None else min(args.decode_steps, L - P)
+    tok = {n: x[n][:, :, P:P + steps].permute(2, 0, 1, 3).contiguous() for n in ("q", "k", "v", "g")}
     mk = x["meta_k"]
     out = torch.empty(steps, w.B, w.H, w.D, device="cuda", dtype=torch.bfloat16)
     del x, pre, f
@@ -223,7 +223,7 @@ def bench_decode(args, hip, torch, lib):
             "tokens_per_s": round(w.B / (us * 1e-6), 1), "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode_kernel"),
-                         "kernel": "decode_kernel (+ pos_advance_kernel)",
+                         "kernel": "decode_kernel",
                          "algorithmic_bytes_per_step": bytes_step}}
 
 
@@ -235,6 +235,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
+    ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -259,6 +262,12 @@ def main():
         "kernels_ms": tr["kernels_ms"],
         "step_roofline": tr["step_roofline"],
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, device="cuda", dtype=torch.bfloat16).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads)
     del x
