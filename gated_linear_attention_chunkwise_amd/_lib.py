@@ -141,9 +141,14 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
     out["chunk_states"] = (torch.empty(B, H, NC, d, d, device=dev, dtype=dt)
                            if want_chunk_states else None)
     out["state"] = torch.empty(B, H, d, d, device=dev, dtype=torch.float32) if want_state else None
+    ws, ws_bytes = None, 0
+    if not want_chunk_states and L > 0:
+        ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD)
+        ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     _check(lib.lizard_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(meta_k),
                                _ptr(meta_v), _ptr(out["o"]), _ptr(out["lse"]), _ptr(out["o_swa"]),
-                               _ptr(out["chunk_states"]), _ptr(out["state"]), None, 0, _stream(dev)))
+                               _ptr(out["chunk_states"]), _ptr(out["state"]), _ptr(ws), ws_bytes,
+                               _stream(dev)))
     return out
 
 

@@ -19,7 +19,8 @@ ARCH = "gfx950"
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-    # packed fp32 instructions stay off (see the build notes in the design doc)
+    # packed fp32 arithmetic instructions stay off: the compiler would otherwise
+    # form them from plain float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]

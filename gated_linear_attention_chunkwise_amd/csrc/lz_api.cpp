@@ -42,6 +42,8 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
   const double elems = (double)s->B * s->H * (op == LIZARD_OP_DECODE ? s->W : (s->L > 0 ? s->L : 1)) * d;
   if (elems > 9.0e15) return LIZARD_EUNSUPPORTED;
   if ((double)s->B * s->H * (d / 16) > 2.0e9) return LIZARD_EUNSUPPORTED;
+  if (op != LIZARD_OP_DECODE && (double)s->B * s->H * ((s->L + kChunk - 1) / kChunk) > 2.0e9)
+    return LIZARD_EUNSUPPORTED;   // one workgroup per (batch, head, chunk)
   return LIZARD_OK;
 }
 
@@ -76,6 +78,7 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
   if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE) return 0;
   if (check_shape(s, op) != LIZARD_OK) return 0;
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
+  if (op == LIZARD_OP_FWD) return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
   return 0;
 }
 
@@ -85,20 +88,22 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
                                 void* o, float* lse, void* o_swa, void* chunk_states,
                                 float* state_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
   if (st != LIZARD_OK) return st;
   if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
   // L = 0: the sequence tensors are empty (possibly NULL); only state_out is written (zero)
   if (s->L > 0)
-    st = check_ptrs({q, k, v, g, o}, {meta_k, meta_v, lse, o_swa, chunk_states, state_out});
+    st = check_ptrs({q, k, v, g, o}, {meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace});
   else
-    st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out});
+    st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace});
   if (st != LIZARD_OK) return st;
+  // the chunk states go to chunk_states when given, else to the workspace
+  if (s->L > 0 && chunk_states == nullptr &&
+      (workspace == nullptr || workspace_bytes < lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype)))
+    return LIZARD_EWORKSPACE;
   if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
-                s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
+                workspace, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
   return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 

@@ -18,9 +18,9 @@
 //
 // Kernels, in launch order:
 //   delta_kernel   D_t = mix * dO_t . o_swa_t                       (row dots)
-//   dstate_kernel  reverse sweep over chunks per (b, h, 64-wide d_v tile):
-//                  carries dS in fp32 registers, stores dS' (operand dtype,
-//                  transposed) and the fp32 boundary rowsums per chunk
+//   sweep_kernel   (lz_sweep.hip) reverse sweep over chunks per (b, h, 64 x 64
+//                  tile of dS): carries dS in fp32 registers, stores dS'
+//                  (operand dtype, transposed) and the fp32 boundary rowsums
 //   chunk_kernel   one workgroup per (b, h, chunk): every GLA gradient plus
 //                  the anchor-window gradients (query side for dq, key side
 //                  for dk and dv) and per-chunk meta-key partial sums
@@ -79,210 +79,6 @@ __global__ __launch_bounds__(NTHR) void delta_kernel(const T* __restrict__ dO, c
 #pragma unroll
   for (int m = 1; m < VPR; m <<= 1) acc = xor_sum(acc, m);
   if (row < rows && cv == 0) delta[row] = mix * acc;
-}
-
-// ------------------------------------------------------- shared gate prefix
-// Thread map of a 64 x D chunk tile: column group cg (VEC dims), tokens
-// tg*TPT .. +TPT.  Computes the chunk-local inclusive prefix b of the
-// log-gates held in rg (overwritten with b) and the chunk total Gamma.
-template <int D, int VEC, int NT = NTHR>
-struct ScanMap {
-  static constexpr int VPR = D / VEC;
-  static constexpr int NTG = NT / VPR;
-  static constexpr int TPT = C / NTG;
-  static constexpr int GV = VEC / 4;
-};
-
-template <int D, int VEC, int NT, int TPT_, int GV_>
-__device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot)[GV_], float* sScan, int cg,
-                                             int tg) {
-  using SM = ScanMap<D, VEC, NT>;
-  static_assert(SM::TPT == TPT_ && SM::GV == GV_, "scan map");
-#pragma unroll
-  for (int u = 1; u < SM::TPT; ++u)
-#pragma unroll
-    for (int e = 0; e < SM::GV; ++e) rg[u][e] += rg[u - 1][e];
-#pragma unroll
-  for (int e = 0; e < SM::GV; ++e)
-    *reinterpret_cast<f32x4*>(sScan + tg * D + cg * VEC + 4 * e) = rg[SM::TPT - 1][e];
-  __syncthreads();
-  f32x4 excl[SM::GV];
-#pragma unroll
-  for (int e = 0; e < SM::GV; ++e) { excl[e] = f32x4{0, 0, 0, 0}; tot[e] = f32x4{0, 0, 0, 0}; }
-  for (int p = 0; p < SM::NTG; ++p) {
-#pragma unroll
-    for (int e = 0; e < SM::GV; ++e) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(sScan + p * D + cg * VEC + 4 * e);
-      tot[e] += x;
-      if (p < tg) excl[e] += x;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < SM::TPT; ++u)
-#pragma unroll
-    for (int e = 0; e < SM::GV; ++e) rg[u][e] += excl[e];
-}
-
-// ------------------------------------------------------------ dstate sweep
-template <typename T, int D>
-struct DsLayout {
-  static constexpr int PAD = Tr<T>::PAD;
-  static constexpr int LDQ = D + PAD;
-  static constexpr int LDO = DVTA + PAD;
-  static constexpr size_t oQt = 0;                                      // [C][D]    q~ (row-major)
-  static constexpr size_t odO = oQt + sizeof(T) * C * LDQ;             // [C][DVTA] dO slice (row-major)
-  static constexpr size_t oScan = odO + sizeof(T) * C * LDO;
-  static constexpr size_t oDec = oScan + sizeof(float) * (NTHR / (D / Tr<T>::VEC)) * D;
-  static constexpr size_t bytes = oDec + sizeof(float) * D;
-};
-
-template <typename T, int D>
-__global__ __launch_bounds__(NTHR, 1) void dstate_kernel(BwdArgs a, T* __restrict__ wsdS, float* __restrict__ wsbnd) {
-  using LY = DsLayout<T, D>;
-  using SM = ScanMap<D, Tr<T>::VEC>;
-  using frag = typename Tr<T>::frag;
-  constexpr int VEC = Tr<T>::VEC, TPT = SM::TPT, GV = SM::GV;
-  constexpr int NJ = D / DVTA;
-  constexpr int IB = D / 64, JB = DVTA / 16;
-  constexpr int VVR = DVTA / VEC, NVV = (C * VVR + NTHR - 1) / NTHR;
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
-  T* sdO = reinterpret_cast<T*>(smem + LY::odO);
-  float* sScan = reinterpret_cast<float*>(smem + LY::oScan);
-  float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
-  const int BH = a.B * a.H;
-  int bh, jt;
-  {
-    const int bid = blockIdx.x;
-    if ((BH & 7) == 0) {
-      const int grp = bid / (8 * NJ), x = bid % (8 * NJ);
-      bh = grp * 8 + (x & 7);
-      jt = x >> 3;
-    } else {
-      bh = bid / NJ;
-      jt = bid % NJ;
-    }
-  }
-  const int j0 = jt * DVTA;
-  const int L = a.L, NC = (L + C - 1) / C;
-  const size_t hoff = (size_t)bh * L * D;
-  const T* q = reinterpret_cast<const T*>(a.q) + hoff;
-  const T* dO = reinterpret_cast<const T*>(a.dO) + hoff;
-  const float* g = a.g + hoff;
-  const T* cstates = reinterpret_cast<const T*>(a.chunk_states) + (size_t)bh * NC * D * D;
-  const int cg = tid % SM::VPR, tg = tid / SM::VPR;
-
-  V16 rq[TPT], rd[NVV];
-  f32x4 rg[TPT][GV];
-  auto prefetch = [&](int c) {
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int t = c * C + tg * TPT + u;
-      const bool ok = t < L;
-      rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
-#pragma unroll
-      for (int e = 0; e < GV; ++e)
-        rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < NVV; ++u) {
-      const int idx = tid + u * NTHR;
-      rd[u] = zero16();
-      if (idx < C * VVR) {
-        const int s = idx / VVR, vc = idx % VVR;
-        const int t = c * C + s;
-        if (t < L) rd[u] = ldg16(dO + (size_t)t * D + j0 + vc * VEC);
-      }
-    }
-  };
-
-  f32x4 acc[IB][JB];
-#pragma unroll
-  for (int i = 0; i < IB; ++i)
-#pragma unroll
-    for (int j = 0; j < JB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-
-  if (NC > 0) prefetch(NC - 1);
-  for (int c = NC - 1; c >= 0; --c) {
-    // state after chunk c (valid for c < NC-1) at this lane's accumulator positions;
-    // issued before the next prefetch so that waiting for it never waits for that
-    const T* Sc = cstates + (size_t)(c + 1) * D * D;
-    float scv[IB][JB][4];
-#pragma unroll
-    for (int ib = 0; ib < IB; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          scv[ib][jb][i] = (c + 1 < NC)
-              ? Tr<T>::to_f(Sc[(size_t)(16 * (w * IB + ib) + 4 * kg + i) * D + j0 + 16 * jb + r]) : 0.f;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NVV; ++u) {
-      const int idx = tid + u * NTHR;
-      if (idx < C * VVR) {
-        const int s = idx / VVR, vc = idx % VVR;
-        *reinterpret_cast<V16*>(sdO + s * LY::LDO + vc * VEC) = rd[u];
-      }
-    }
-    f32x4 tot[GV];
-    chunk_prefix<D, VEC, NTHR, TPT, GV>(rg, tot, sScan, cg, tg);
-    if (tg == 0)
-#pragma unroll
-      for (int e = 0; e < GV; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sDec[cg * VEC + 4 * e + i] = __expf(tot[e][i]);
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      float qt[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) qt[e] = v16_get(rq[u], e, (T*)nullptr) * __expf(rg[u][e >> 2][e & 3]);
-      st_vec(sQt + (tg * TPT + u) * LY::LDQ + cg * VEC, qt);
-    }
-    if (c > 0) prefetch(c - 1);
-    __syncthreads();
-
-    // acc holds dS_c (gradient w.r.t. the state after chunk c, from later chunks)
-    T* dst = wsdS + ((size_t)bh * NC + c) * D * D;
-    float* bnd = wsbnd + (((size_t)bh * NC + c) * NJ + jt) * D;
-#pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-      const int i0 = 16 * (w * IB + ib);
-      float dec[4], rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dec[i] = sDec[i0 + 4 * kg + i];
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb) {
-        const int j = j0 + 16 * jb + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rs[i] += scv[ib][jb][i] * acc[ib][jb][i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[ib][jb][i] *= dec[i];
-        st4(dst + (size_t)j * D + i0 + 4 * kg, acc[ib][jb][0], acc[ib][jb][1], acc[ib][jb][2], acc[ib][jb][3]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) rs[i] = xor_sum(rs[i], m);
-      if (r == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bnd[i0 + 4 * kg + i] = rs[i];
-    }
-    // dS_{c-1} = dS' + q~^T dO
-#pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-      const int i0 = 16 * (w * IB + ib);
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int ks = 0; ks < C / 32; ++ks)
-          mma32(acc[ib][jb], ld_frag_tr(sQt, LY::LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, i0, lane),
-                ld_frag_tr(sdO, LY::LDO, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane));
-    }
-  }
 }
 
 // ------------------------------------------------------------ chunk kernel
@@ -825,14 +621,8 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   }
   mark(1);
   {
-    using LY = DsLayout<T, D>;
-    static bool attr = false;
-    if (!attr) {
-      if ((e = set_lds(dstate_kernel<T, D>, LY::bytes)) != hipSuccess) return e;
-      attr = true;
-    }
-    hipLaunchKernelGGL((dstate_kernel<T, D>), dim3(BH * (D / DVTA)), dim3(NTHR), LY::bytes, st, a, wsdS, wsbnd);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const SweepArgs sw{a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, a.B, a.H, a.L};
+    if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, true, st)) != hipSuccess) return e;
   }
   mark(2);
   {

@@ -26,6 +26,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
+constexpr int CHUNK = 64;   // tokens per chunk of the chunkwise form
 
 struct bf16_t { uint16_t bits; };   // storage tag for bf16 tensors in global memory
 
@@ -156,6 +157,30 @@ __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Cross-lane moves inside rows of 16 lanes through DPP (no LDS traffic).
+// CTRL 0x110 + n: shift right by n within the row (zero fill);
+// CTRL 0x120 + n: rotate right by n within the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// Inclusive prefix sum over the 16 lanes of each row.
+__device__ __forceinline__ float row_scan16(float x) {
+  x += dpp_row<0x111>(x);
+  x += dpp_row<0x112>(x);
+  x += dpp_row<0x114>(x);
+  x += dpp_row<0x118>(x);
+  return x;
+}
+// Sum over the 16 lanes of each row, returned in every lane of the row.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_row<0x128>(x);
+  x += dpp_row<0x124>(x);
+  x += dpp_row<0x122>(x);
+  x += dpp_row<0x121>(x);
+  return x;
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Matrix-core results must not be read until the instruction has drained
@@ -219,6 +244,48 @@ __device__ __forceinline__ void st_vec(bf16_t* p, const float* x) {
 template <typename T>
 __device__ __forceinline__ typename Tr<T>::frag ldg_row_frag(const T* base, int ld, int row, int col, int nrows) {
   return row < nrows ? ldg_frag<T>(base + (size_t)row * ld + col) : zero_frag<T>();
+}
+
+// ------------------------------------------------------- chunk-local gate prefix
+// Thread map of a CHUNK x D tile: column group cg (VEC dims), tokens
+// tg*TPT .. +TPT.  Computes the chunk-local inclusive prefix b of the
+// log-gates held in rg (overwritten with b) and the chunk total Gamma.
+template <int D, int VEC, int NT>
+struct ScanMap {
+  static constexpr int VPR = D / VEC;
+  static constexpr int NTG = NT / VPR;
+  static constexpr int TPT = CHUNK / NTG;
+  static constexpr int GV = VEC / 4;
+};
+
+template <int D, int VEC, int NT, int TPT_, int GV_>
+__device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot)[GV_], float* sScan, int cg,
+                                             int tg) {
+  using SM = ScanMap<D, VEC, NT>;
+  static_assert(SM::TPT == TPT_ && SM::GV == GV_, "scan map");
+#pragma unroll
+  for (int u = 1; u < SM::TPT; ++u)
+#pragma unroll
+    for (int e = 0; e < SM::GV; ++e) rg[u][e] += rg[u - 1][e];
+#pragma unroll
+  for (int e = 0; e < SM::GV; ++e)
+    *reinterpret_cast<f32x4*>(sScan + tg * D + cg * VEC + 4 * e) = rg[SM::TPT - 1][e];
+  __syncthreads();
+  f32x4 excl[SM::GV];
+#pragma unroll
+  for (int e = 0; e < SM::GV; ++e) { excl[e] = f32x4{0, 0, 0, 0}; tot[e] = f32x4{0, 0, 0, 0}; }
+  for (int p = 0; p < SM::NTG; ++p) {
+#pragma unroll
+    for (int e = 0; e < SM::GV; ++e) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sScan + p * D + cg * VEC + 4 * e);
+      tot[e] += x;
+      if (p < tg) excl[e] += x;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < SM::TPT; ++u)
+#pragma unroll
+    for (int e = 0; e < SM::GV; ++e) rg[u][e] += excl[e];
 }
 
 }  // namespace lz

@@ -11,6 +11,7 @@ struct FwdArgs {
   const void* q; const void* k; const void* v; const float* g;
   const void* meta_k; const void* meta_v;
   void* o; float* lse; void* o_swa; void* chunk_states; float* state_out;
+  void* workspace;      // chunk-state buffer (fwd_workspace_bytes) used when chunk_states is NULL
   int B, H, L, W, M;
   float scale, mix;
 };
@@ -28,6 +29,17 @@ struct BwdArgs {
   float scale, mix;
 };
 
+// One sequential sweep over chunks (lz_sweep.hip).  Forward: a_src = k,
+// b_src = v, out = chunk states [B,H,NC,d,d] (state entering each chunk),
+// state_out = final state (fp32, optional).  Backward: a_src = q, b_src = dO,
+// states = the forward's chunk states, out = dS' transposed [B,H,NC,d,d],
+// bnd = boundary rowsums [B,H,NC,d/64,d].
+struct SweepArgs {
+  const void* a_src; const void* b_src; const float* g;
+  const void* states; void* out; float* bnd; float* state_out;
+  int B, H, L;
+};
+
 struct DecodeArgs {
   const void* q; const void* k; const void* v; const float* g;
   const void* meta_k; const void* meta_v;
@@ -40,7 +52,10 @@ struct DecodeArgs {
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
+hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st);
 
+// Workspace bytes needed by launch_fwd when no chunk-state output is given.
+size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype);
 // Workspace bytes needed by launch_bwd.
 size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
 

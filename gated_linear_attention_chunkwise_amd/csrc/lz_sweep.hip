@@ -1,0 +1,288 @@
+// lz_sweep.hip -- the sequential chunk sweeps of the GLA branch on gfx950.
+//
+// The GLA state (gist.science explainer of "Lizard: An Efficient
+// Linearization Framework for Large Language Models", English page §2.A,
+// state update with a per-key-dimension gate) and its gradient both follow,
+// chunk by chunk, with b the chunk-local inclusive prefix of the log-gates
+// and Gamma its value at the chunk end (English page §2.C: gates handled in
+// log space, only chunk-local sums exponentiated):
+//
+//   forward,  chunks ascending:   S_{c+1} = diag(e^Gamma) S_c + (k e^{Gamma-b})^T v
+//             stores S_c (the state entering chunk c) in the operand dtype,
+//             row-major [d_k][d_v], and the final state in fp32;
+//   backward, chunks descending:  dS_{c-1} = diag(e^Gamma) dS_c + (q e^b)^T dO
+//             where dS_c is the gradient w.r.t. the state after chunk c;
+//             stores dS'_c = diag(e^Gamma) dS_c transposed ([d_v][d_k]) and the
+//             boundary term of the gate gradient, rowsum(S_{c+1} (.) dS_c),
+//             per 64-wide d_v tile.
+//
+// Element (i, j) of the carried matrix evolves independently of every other,
+// so the sweep is tiled 64 x 64 over (d_k, d_v): one workgroup of four waves
+// per (b, h, i tile, j tile) carries its tile in fp32 registers through all
+// chunks, with the inputs of the next two chunks in flight while one is
+// processed (none of them depends on the carried matrix).  The gate prefix
+// runs inside rows of 16 lanes (DPP), with no LDS round trip or barrier.
+#include <type_traits>
+
+#include "lz_common.hpp"
+#include "lz_kernels.hpp"
+
+namespace lz {
+namespace {
+
+constexpr int TT = 64;          // tile edge over d_k and d_v
+constexpr int NTHR_SW = 256;
+
+template <typename T>
+struct SwLayout {
+  static constexpr int LDT = TT + Tr<T>::PAD;
+  static constexpr size_t oA = 0;                                   // [C][TT]  gate-folded q or k
+  static constexpr size_t oB = oA + sizeof(T) * CHUNK * LDT;        // [C][TT]  v or dO
+  static constexpr size_t oS = oB + sizeof(T) * CHUNK * LDT;        // [TT][TT] state tile (backward)
+  static constexpr size_t oDec = oS + sizeof(T) * TT * LDT;
+  static constexpr size_t bytes = oDec + sizeof(float) * TT;
+};
+
+// Four consecutive elements of T (8 or 16 bytes) as floats.
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4f(const bf16_t* p) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// Four values of column c0 + (lane & 15), rows r0 .. r0+3, of a row-major LDS tile.
+__device__ __forceinline__ f32x4 col4(const bf16_t* tile, int ld, int r0, int c0, int lane) {
+  const bf16x4 x = tr4(tile, ld, r0, c0, lane);
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ f32x4 col4(const float* tile, int ld, int r0, int c0, int lane) {
+  const int c = c0 + (lane & 15);
+  return f32x4{tile[r0 * ld + c], tile[(r0 + 1) * ld + c], tile[(r0 + 2) * ld + c], tile[(r0 + 3) * ld + c]};
+}
+
+// Inputs of one chunk held in registers while the previous chunk is processed.
+template <int NV>
+struct SwStage {
+  f32x4 ra[4];   // q or k: tokens 4*tg+u, four columns
+  f32x4 rg[4];   // log-gates, same positions
+  V16 rb[NV];    // v or dO tile, 16-byte vectors
+  V16 rs[NV];    // state tile (backward)
+};
+
+template <typename T, int D, bool REV>
+__global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
+  using LY = SwLayout<T>;
+  constexpr int NTI = D / TT;                      // tiles per edge
+  constexpr int VEC = Tr<T>::VEC;
+  constexpr int NV = CHUNK * (TT / VEC) / NTHR_SW; // 16-byte vectors per thread of a [64][64] tile
+  constexpr int LDT = LY::LDT;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sA = reinterpret_cast<T*>(smem + LY::oA);
+  T* sB = reinterpret_cast<T*>(smem + LY::oB);
+  T* sS = reinterpret_cast<T*>(smem + LY::oS);
+  float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+  // workgroup -> (b*h, i tile, j tile); the tiles of one head share an XCD
+  const int BH = a.B * a.H;
+  int bh, tile;
+  {
+    const int bid = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int x = bid % 8, y = bid / 8;
+      bh = (y / (NTI * NTI)) * 8 + x;
+      tile = y % (NTI * NTI);
+    } else {
+      bh = bid / (NTI * NTI);
+      tile = bid % (NTI * NTI);
+    }
+  }
+  const int it = tile / NTI, jt = tile % NTI;
+  const int i0 = it * TT, j0 = jt * TT;
+  const int L = a.L, NC = (L + CHUNK - 1) / CHUNK;
+  const size_t hoff = (size_t)bh * L * D;
+  const T* asrc = reinterpret_cast<const T*>(a.a_src) + hoff;
+  const T* bsrc = reinterpret_cast<const T*>(a.b_src) + hoff;
+  const float* g = a.g + hoff;
+  const T* states = reinterpret_cast<const T*>(a.states) + (size_t)bh * NC * D * D;
+  T* out = reinterpret_cast<T*>(a.out) + (size_t)bh * NC * D * D;
+
+  // gate scan map: wave w owns columns 16w .. 16w+15 of the tile; a row of 16
+  // lanes (column group cg = kg) holds tokens 4*tg .. 4*tg+3, tg = lane & 15,
+  // so the prefix over tokens is an in-row scan
+  const int tg = r, cg = kg;
+  const int acol = i0 + 16 * w + 4 * cg;
+  auto load = [&](SwStage<NV>& s, int c) {
+    const int t0 = c * CHUNK;
+    if (t0 + CHUNK <= L) {   // full chunk: no bounds checks
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t o = (size_t)(t0 + 4 * tg + u) * D + acol;
+        s.ra[u] = ld4f(asrc + o);
+        s.rg[u] = ld4f(g + o);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
+        s.rb[u] = ldg16(bsrc + (size_t)(t0 + row) * D + j0 + cv * VEC);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + 4 * tg + u;
+        const size_t o = (size_t)t * D + acol;
+        s.ra[u] = t < L ? ld4f(asrc + o) : f32x4{0, 0, 0, 0};
+        s.rg[u] = t < L ? ld4f(g + o) : f32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
+        s.rb[u] = t0 + row < L ? ldg16(bsrc + (size_t)(t0 + row) * D + j0 + cv * VEC) : zero16();
+      }
+    }
+    if constexpr (REV) {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
+        s.rs[u] = (c + 1 < NC) ? ldg16(states + ((size_t)(c + 1) * D + i0 + row) * D + j0 + cv * VEC) : zero16();
+      }
+    }
+  };
+
+  // carried tile: forward acc[ib][e] = S[i0+16ib+r][j0+16w+4kg+e];
+  //               backward acc[jb][e] = dS[i0+16w+4kg+e][j0+16jb+r]
+  f32x4 acc[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc[x] = f32x4{0, 0, 0, 0};
+
+  auto chunk_of = [&](int n) { return REV ? NC - 1 - n : n; };
+  auto process = [&](SwStage<NV>& s, int n) {
+    const int c = chunk_of(n);
+    if constexpr (!REV) {
+      // state entering chunk c
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+        stg4(out + ((size_t)c * D + i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1],
+             acc[ib][2], acc[ib][3]);
+    }
+    __syncthreads();   // the previous chunk's operand reads are done
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
+      *reinterpret_cast<V16*>(sB + row * LDT + cv * VEC) = s.rb[u];
+      if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDT + cv * VEC) = s.rs[u];
+    }
+    // chunk-local inclusive prefix b of the gates and the chunk total Gamma
+#pragma unroll
+    for (int u = 1; u < 4; ++u) s.rg[u] += s.rg[u - 1];
+    f32x4 excl, tot;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float own = s.rg[3][e];
+      excl[e] = row_scan16(own) - own;
+      tot[e] = row_sum16(own);
+    }
+    if (tg == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sDec[16 * w + 4 * cg + e] = __expf(tot[e]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b = s.rg[u][e] + excl[e];
+        x[e] = s.ra[u][e] * __expf(REV ? b : tot[e] - b);
+      }
+      st4(sA + (4 * tg + u) * LDT + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
+    }
+    if (n + 2 < NC) load(s, chunk_of(n + 2));
+    __syncthreads();
+
+    if constexpr (REV) {
+      // boundary rowsum over this j tile, decay, store dS' transposed
+      f32x4 rsum = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) rsum += col4(sS, LDT, 16 * w + 4 * kg, 16 * jb, lane) * acc[jb];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rsum[e] = row_sum16(rsum[e]);
+      if (r == 0)
+        stg4(a.bnd + (((size_t)bh * NC + c) * NTI + jt) * D + i0 + 16 * w + 4 * kg, rsum[0], rsum[1], rsum[2],
+             rsum[3]);
+      f32x4 dec;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dec[e] = sDec[16 * w + 4 * kg + e];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        acc[jb] *= dec;
+        stg4(out + ((size_t)c * D + j0 + 16 * jb + r) * D + i0 + 16 * w + 4 * kg, acc[jb][0], acc[jb][1],
+             acc[jb][2], acc[jb][3]);
+      }
+      // + (q e^b)^T dO
+#pragma unroll
+      for (int ks = 0; ks < CHUNK / 32; ++ks) {
+        const auto fa = ld_frag_tr(sA, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * w, lane);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+          mma32(acc[jb], fa, ld_frag_tr(sB, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane));
+      }
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) acc[ib] *= sDec[16 * ib + r];
+      // + (k e^{Gamma-b})^T v, computed transposed so each lane holds four consecutive d_v entries
+#pragma unroll
+      for (int ks = 0; ks < CHUNK / 32; ++ks) {
+        const auto fb = ld_frag_tr(sB, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * w, lane);
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+          mma32(acc[ib], fb, ld_frag_tr(sA, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * ib, lane));
+      }
+    }
+  };
+
+  // two chunks of inputs in flight: stage 0 serves even steps, stage 1 odd steps
+  SwStage<NV> s0, s1;
+  if (NC > 0) load(s0, chunk_of(0));
+  if (NC > 1) load(s1, chunk_of(1));
+  for (int n = 0; n < NC; n += 2) {
+    process(s0, n);
+    if (n + 1 < NC) process(s1, n + 1);
+  }
+  mfma_drain();
+  if constexpr (!REV) {
+    if (a.state_out != nullptr) {
+      float* so = a.state_out + (size_t)bh * D * D;
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+        stg4(so + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1], acc[ib][2],
+             acc[ib][3]);
+    }
+  }
+}
+
+template <typename T, int D, bool REV>
+hipError_t launch_sweep_t(const SweepArgs& a, hipStream_t st) {
+  using LY = SwLayout<T>;
+  const int grid = a.B * a.H * (D / TT) * (D / TT);
+  hipLaunchKernelGGL((sweep_kernel<T, D, REV>), dim3(grid), dim3(NTHR_SW), LY::bytes, st, a);
+  return hipGetLastError();
+}
+
+template <bool REV>
+hipError_t launch_sweep_dir(const SweepArgs& a, int dtype, int D, hipStream_t st) {
+  if (dtype == 1) {
+    if (D == 128) return launch_sweep_t<bf16_t, 128, REV>(a, st);
+    if (D == 64) return launch_sweep_t<bf16_t, 64, REV>(a, st);
+  } else if (dtype == 0) {
+    if (D == 64) return launch_sweep_t<float, 64, REV>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st) {
+  return reverse ? launch_sweep_dir<true>(a, dtype, D, st) : launch_sweep_dir<false>(a, dtype, D, st);
+}
+
+}  // namespace lz

@@ -97,8 +97,12 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op);
  *   o_swa        opt  [B,H,L,d_v] window branch before mixing
  *   chunk_states opt  state entering every chunk (needed by lizard_attn_bwd)
  *   state_out    opt  [B,H,d_k,d_v] fp32 state after the last token (decode hand-off)
- * NULL optional outputs are not written.  No workspace is needed today
- * (workspace may be NULL with workspace_bytes 0). */
+ *   workspace         when chunk_states is NULL: at least
+ *                     lizard_attn_workspace_bytes(s, LIZARD_OP_FWD) bytes of
+ *                     caller-owned device memory (clobbered) that receive the
+ *                     chunk states instead; otherwise unused (may be NULL)
+ * NULL optional outputs are not written.  Two launches on `stream`: the state
+ * sweep over chunks, then one workgroup per (batch, head, chunk). */
 lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
                                 const void* q, const void* k, const void* v, const float* g,
                                 const void* meta_k, const void* meta_v,

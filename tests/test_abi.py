@@ -107,9 +107,21 @@ def test_decode_validation(lib):
     assert call(s_=shape(W=9000)) == EUNSUPPORTED
 
 
+def test_fwd_needs_workspace_without_chunk_states(lib):
+    s = shape()
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)
+    assert need == 1 * 2 * 2 * 128 * 128 * 2          # B*H*chunks*d*d bf16 chunk states
+    def call(ws, ws_bytes):
+        return lib.lizard_attn_fwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None,
+                                   None, None, None, ws, ws_bytes, None)
+    assert call(None, 0) == EWORKSPACE
+    assert call(GOOD, need - 1) == EWORKSPACE
+    assert call(BAD, need) == EALIGN
+
+
 def test_workspace_query(lib):
     assert lib.lizard_attn_workspace_bytes(None, 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(d_k=96, d_v=96)), 1) == 0
-    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 0) == 0
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 0) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 2) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 5) == 0
