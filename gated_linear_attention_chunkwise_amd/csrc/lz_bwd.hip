@@ -86,24 +86,39 @@ template <typename T, int D>
 struct CkLayout {
   static constexpr int PAD = Tr<T>::PAD;
   static constexpr int LDQ = D + PAD;    // row-major [C][D] and [D][D] tiles
+  static constexpr int LDB = D + 4;      // fp32 gate-gradient rows
   static constexpr int LDC = C + PAD;    // [16][C] meta tiles
   static constexpr int LDM = 16 + PAD;   // [D][16] meta keys transposed
-  static constexpr size_t oQt = 0;                                   // q~   [C][D]  (later raw q of a chunk)
-  static constexpr size_t oKh = oQt + sizeof(T) * C * LDQ;           // k^   [C][D]  (later dO of another chunk)
-  static constexpr size_t oEb = oKh + sizeof(T) * C * LDQ;           // e^b  [C][D]
-  static constexpr size_t odO = oEb + sizeof(T) * C * LDQ;           // dO   [C][D]
-  static constexpr size_t oBig = odO + sizeof(T) * C * LDQ;          // dS'^T [D][D] | scan | db | key tile
-  static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * D ? sizeof(T) * D * LDQ
-                                                                                 : sizeof(float) * C * D;
+  static constexpr size_t tile = sizeof(T) * C * LDQ;
+  static constexpr size_t oQt = 0;            // q~ ; window: key tile of an earlier chunk
+  static constexpr size_t oKh = tile;         // k^ ; window: query tile of a later chunk
+  static constexpr size_t oEb = 2 * tile;     // e^b; window: dO tile of a later chunk
+  static constexpr size_t odO = 3 * tile;     // dO of this chunk
+  static constexpr size_t oBig = 4 * tile;    // dS'^T [D][D] | gate-scan scratch | d b [C][LDB] fp32
+  static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * LDB ? sizeof(T) * D * LDQ
+                                                                                   : sizeof(float) * C * LDB;
   static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
   static constexpr size_t oDLm = oMkT + sizeof(T) * D * LDM;         // dl_meta^T [16][C]
-  static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // p_meta^T  [16][C]
+  static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // mix * p_meta^T [16][C]
   static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 chunks (log2 units)
   static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 chunks
   static constexpr size_t bytes = oDel + sizeof(float) * 3 * C;
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
+// Four consecutive LDS elements as floats.
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 lds4(const bf16_t* p) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// One workgroup per (b, h, chunk), eight waves in two roles over the four
+// 16-token blocks of the chunk: waves 0..3 accumulate dq (GLA and the window
+// seen from the query side), waves 4..7 accumulate dk and dv (GLA and the
+// window seen from the key side), so every score tile is formed once.
+// Accumulators are kept transposed: acc[x][e] belongs to token 16*wb + r of
+// the chunk and column 16*x + 4*kg + e.
 template <typename T, int D>
 __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
                                                             const float* __restrict__ wsbnd) {
@@ -112,10 +127,9 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   using frag = typename Tr<T>::frag;
   constexpr int VEC = Tr<T>::VEC, TPT = SM::TPT, GV = SM::GV;
   constexpr int NB = D / 16;     // 16-wide blocks over the head dim
-  constexpr int NBH = NB / 2;    // blocks per wave (the two waves of a token block split them)
   constexpr int KS = D / 32;     // K steps over the head dim
   constexpr int NJ = D / DVTA;
-  constexpr int LDQ = LY::LDQ;
+  constexpr int LDQ = LY::LDQ, LDB = LY::LDB;
   static_assert(sizeof(float) * SM::NTG * D <= LY::bigBytes, "scan scratch fits in the shared region");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -126,7 +140,9 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   T* sdSt = reinterpret_cast<T*>(smem + LY::oBig);          // dS' transposed [j][i], row-major
   float* sScan = reinterpret_cast<float*>(smem + LY::oBig);
   float* sDb = reinterpret_cast<float*>(smem + LY::oBig);
-  T* sKt = reinterpret_cast<T*>(smem + LY::oBig);           // raw keys of a window chunk [C][D]
+  T* sKw = sQt;    // window: raw keys of chunk kt (query side)
+  T* sQw = sKh;    // window: raw queries of chunk qc (key side)
+  T* sDw = sEb;    // window: dO of chunk qc > c (key side)
   T* sMkT = reinterpret_cast<T*>(smem + LY::oMkT);
   T* sDLm = reinterpret_cast<T*>(smem + LY::oDLm);
   T* sPm = reinterpret_cast<T*>(smem + LY::oPm);
@@ -134,8 +150,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+  const bool qrole = w < 4;        // waves 0..3: dq; waves 4..7: dk, dv
   const int wb = w & 3;            // token block of this wave (rows 16*wb .. +16 of the chunk)
-  const int nb0 = (w >> 2) * NBH;  // first of this wave's output column blocks
   const int L = a.L, NC = (L + C - 1) / C, W = a.W, M = a.M;
   // workgroup -> (chunk, head); consecutive chunks of one head share an XCD
   const int BH = a.B * a.H;
@@ -165,6 +181,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const float sl2 = a.scale * LOG2E;
   const float mix = a.mix, scale = a.scale;
   const int t0 = c * C;
+  const int u = 16 * wb + r;        // this lane's token within the chunk
+  const int tok = t0 + u;
 
   // Copy a [C][D] row-major chunk tile (rows past L are zero) into LDS.
   auto stage_rows = [&](T* dst, const T* src, int row0) {
@@ -181,14 +199,14 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     V16 rq[TPT], rk[TPT];
     f32x4 rg[TPT][GV];
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int t = t0 + tg * TPT + u;
+    for (int uu = 0; uu < TPT; ++uu) {
+      const int t = t0 + tg * TPT + uu;
       const bool ok = t < L;
-      rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
-      rk[u] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
+      rq[uu] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
+      rk[uu] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
 #pragma unroll
       for (int e = 0; e < GV; ++e)
-        rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
+        rg[uu][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
     }
     stage_rows(sdO, dO, t0);
     // meta keys transposed, lse / delta of this chunk and the next two
@@ -204,15 +222,15 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     f32x4 tot[GV];
     chunk_prefix<D, VEC, NTHR_CK, TPT, GV>(rg, tot, sScan, cg, tg);
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int t = tg * TPT + u;
+    for (int uu = 0; uu < TPT; ++uu) {
+      const int t = tg * TPT + uu;
       float qt[VEC], kh[VEC], eb[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float bb = rg[u][e >> 2][e & 3];
+        const float bb = rg[uu][e >> 2][e & 3];
         eb[e] = __expf(bb);
-        qt[e] = v16_get(rq[u], e, (T*)nullptr) * eb[e];
-        kh[e] = v16_get(rk[u], e, (T*)nullptr) * __expf(-bb);
+        qt[e] = v16_get(rq[uu], e, (T*)nullptr) * eb[e];
+        kh[e] = v16_get(rk[uu], e, (T*)nullptr) * __expf(-bb);
       }
       st_vec(sQt + t * LDQ + cg * VEC, qt);
       st_vec(sKh + t * LDQ + cg * VEC, kh);
@@ -227,20 +245,15 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   }
 
   // ------------------------------------------------------ GLA gradients
-  // wave w owns chunk tokens u in [16wb, 16wb+16) (as query rows for accQ, as
-  // key rows for accK / accV) and output column blocks nb0 .. nb0+NBH
-  f32x4 accQ[NBH], accK[NBH], accV[NBH];
+  // Q role: acc0 = dq~.  K role: acc0 = dk^, acc1 = dv.
+  f32x4 acc0[NB], acc1[NB];
 #pragma unroll
-  for (int i = 0; i < NBH; ++i) { accQ[i] = f32x4{0, 0, 0, 0}; accK[i] = accQ[i]; accV[i] = accQ[i]; }
-  const int urow = t0 + 16 * wb + r;     // this lane's token as an operand row
-  {
-    frag fo[KS], fvu[KS];
+  for (int x = 0; x < NB; ++x) { acc0[x] = f32x4{0, 0, 0, 0}; acc1[x] = acc0[x]; }
+  if (qrole) {
+    frag fo[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      fo[ks] = ld_frag(sdO, LDQ, 16 * wb + r, 32 * ks + 8 * kg);
-      fvu[ks] = ldg_row_frag<T>(v, D, urow, 32 * ks + 8 * kg, L);
-    }
-    // dq~ intra: dA^T blocks (keys sb <= wb, queries of block wb), then times k^
+    for (int ks = 0; ks < KS; ++ks) fo[ks] = ld_frag(sdO, LDQ, u, 32 * ks + 8 * kg);
+    // dA^T blocks (keys of block sb <= wb, queries of block wb), then dq~ += dA k^
     f32x4 blk[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
@@ -264,27 +277,31 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         frag op;
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
-        for (int x = 0; x < NBH; ++x)
-          mma32(accQ[x], op, ld_frag_tr(sKh, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
+        for (int x = 0; x < NB; ++x)
+          mma32(acc0[x], ld_frag_tr(sKh, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
       }
-    // dq~ inter: dO S_prev^T
+    // dq~ += dO S_prev^T
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      frag fs[NBH];
 #pragma unroll
-      for (int x = 0; x < NBH; ++x) fs[x] = ldg_frag<T>(Sprev + (size_t)(16 * (nb0 + x) + r) * D + 32 * ks + 8 * kg);
-#pragma unroll
-      for (int x = 0; x < NBH; ++x) mma32(accQ[x], fo[ks], fs[x]);
+      for (int x = 0; x < NB; ++x)
+        mma32(acc0[x], ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 32 * ks + 8 * kg), fo[ks]);
     }
-    // dv intra: A blocks (queries tb >= wb, keys of block wb), A^T dO
+  } else {
+    frag fvu[KS], fkh[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fvu[ks] = ldg_row_frag<T>(v, D, tok, 32 * ks + 8 * kg, L);
+      fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
+    }
+    // A blocks (queries of block tb >= wb, keys of block wb): dv += A^T dO
+    f32x4 blk[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       blk[tb] = f32x4{0, 0, 0, 0};
       if (tb >= wb) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          mma32(blk[tb], ld_frag(sQt, LDQ, 16 * tb + r, 32 * ks + 8 * kg),
-                ld_frag(sKh, LDQ, 16 * wb + r, 32 * ks + 8 * kg));
+        for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sQt, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fkh[ks]);
         mfma_drain();
         if (tb == wb)
 #pragma unroll
@@ -298,10 +315,10 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         frag op;
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
-        for (int x = 0; x < NBH; ++x)
-          mma32(accV[x], op, ld_frag_tr(sdO, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
+        for (int x = 0; x < NB; ++x)
+          mma32(acc1[x], ld_frag_tr(sdO, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
       }
-    // dk^ intra: dA blocks (queries tb >= wb, keys of block wb), dA^T q~
+    // dA blocks (queries tb >= wb, keys of block wb): dk^ += dA^T q~
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       blk[tb] = f32x4{0, 0, 0, 0};
@@ -321,17 +338,16 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         frag op;
         pack_acc(op, blk[2 * p], blk[2 * p + 1]);
 #pragma unroll
-        for (int x = 0; x < NBH; ++x)
-          mma32(accK[x], op, ld_frag_tr(sQt, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
+        for (int x = 0; x < NB; ++x)
+          mma32(acc0[x], ld_frag_tr(sQt, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
       }
     // inter-chunk: dk^ += V dS'^T (dS' read down the columns of its transpose) ; dv += k^ dS'
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const frag fk = ld_frag(sKh, LDQ, 16 * wb + r, 32 * ks + 8 * kg);
 #pragma unroll
-      for (int x = 0; x < NBH; ++x) {
-        mma32(accK[x], fvu[ks], ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * (nb0 + x), lane));
-        mma32(accV[x], fk, ld_frag(sdSt, LDQ, 16 * (nb0 + x) + r, 32 * ks + 8 * kg));
+      for (int x = 0; x < NB; ++x) {
+        mma32(acc0[x], ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * x, lane), fvu[ks]);
+        mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fkh[ks]);
       }
     }
   }
@@ -339,18 +355,24 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   __syncthreads();   // every wave is done with dS': its region now holds the per-token gate gradient
 
   // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b
+  if (qrole) {
 #pragma unroll
-  for (int x = 0; x < NBH; ++x) {
-    const int i = 16 * (nb0 + x) + r;
+    for (int x = 0; x < NB; ++x) {
+      const int i = 16 * x + 4 * kg;
+      *reinterpret_cast<f32x4*>(sDb + u * LDB + i) = lds4(sQt + u * LDQ + i) * acc0[x];
+      acc0[x] *= lds4(sEb + u * LDQ + i);
+    }
+  }
+  __syncthreads();
+  if (!qrole) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int u = 16 * wb + 4 * kg + e;
-      const float qt = Tr<T>::to_f(sQt[u * LDQ + i]);
-      const float kh = Tr<T>::to_f(sKh[u * LDQ + i]);
-      const float eb = Tr<T>::to_f(sEb[u * LDQ + i]);
-      sDb[u * D + i] = qt * accQ[x][e] - kh * accK[x][e];
-      accQ[x][e] *= eb;
-      accK[x][e] *= 1.f / eb;
+    for (int x = 0; x < NB; ++x) {
+      const int i = 16 * x + 4 * kg;
+      f32x4* p = reinterpret_cast<f32x4*>(sDb + u * LDB + i);
+      *p = *p - lds4(sKh + u * LDQ + i) * acc0[x];
+      const f32x4 eb = lds4(sEb + u * LDQ + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc0[x][e] *= __builtin_amdgcn_rcpf(eb[e]);
     }
   }
   __syncthreads();
@@ -360,196 +382,195 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     constexpr int SEG = C / PARTS;
     const int i = tid % D, part = tid / D;
     float run = 0.f;
-    for (int u = SEG * (part + 1) - 1; u >= SEG * part; --u) {
-      run += sDb[u * D + i];
-      sDb[u * D + i] = run;
+    for (int uu = SEG * (part + 1) - 1; uu >= SEG * part; --uu) {
+      run += sDb[uu * LDB + i];
+      sDb[uu * LDB + i] = run;
     }
     __syncthreads();
     float carry = 0.f;
-    for (int p2 = part + 1; p2 < PARTS; ++p2) carry += sDb[(SEG * p2) * D + i];
+    for (int p2 = part + 1; p2 < PARTS; ++p2) carry += sDb[(SEG * p2) * LDB + i];
     if (c + 1 < NC)
       for (int j = 0; j < NJ; ++j) carry += wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + i];
-    for (int u = SEG * part; u < SEG * (part + 1); ++u) {
-      const int t = t0 + u;
-      if (t < L) a.dg[hoff + (size_t)t * D + i] = sDb[u * D + i] + carry;
+    for (int uu = SEG * part; uu < SEG * (part + 1); ++uu) {
+      const int t = t0 + uu;
+      if (t < L) a.dg[hoff + (size_t)t * D + i] = sDb[uu * LDB + i] + carry;
     }
   }
-  __syncthreads();   // sDb, q~, k^ dead: their regions now hold window tiles
+  // (the first window iteration begins with a barrier: d b, q~, k^, e^b are then dead)
 
-  // ------------------------------------------- anchor window, query side (dq)
-  frag qf[KS], of[KS];
+  // ----------------------------------------------------------- anchor window
+  const bool tvalid = tok < L;
+  frag fa[KS], fb[KS];   // Q role: raw q, dO of this lane's query; K role: raw k, v of this lane's key
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = ldg_row_frag<T>(q, D, urow, 32 * ks + 8 * kg, L);
-    of[ks] = ld_frag(sdO, LDQ, 16 * wb + r, 32 * ks + 8 * kg);
+    fa[ks] = ldg_row_frag<T>(qrole ? q : k, D, tok, 32 * ks + 8 * kg, L);
+    fb[ks] = qrole ? ld_frag(sdO, LDQ, u, 32 * ks + 8 * kg) : ldg_row_frag<T>(v, D, tok, 32 * ks + 8 * kg, L);
   }
-  const int tq = urow;                             // this lane's query
-  const float lse2 = sLse[16 * wb + r], delq = sDel[16 * wb + r];
-  const bool qvalid = tq < L;
-  if (M > 0) {
-    // meta values: absent ones read as zero rows (no branch around the product)
+  const float lse2 = sLse[u], delq = sDel[u];
+  if (qrole && M > 0) {
+    // meta keys (always visible); absent meta values read as zero rows (no branch around the product)
     const T* mvp = mv ? mv : mk;
     const int mvrows = mv ? M : 0;
     f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      mma32(x, ldg_row_frag<T>(mk, D, r, 32 * ks + 8 * kg, M), qf[ks]);
-      mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), of[ks]);
+      mma32(x, ldg_row_frag<T>(mk, D, r, 32 * ks + 8 * kg, M), fa[ks]);
+      mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), fb[ks]);
     }
     mfma_drain();
     f32x4 dl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * kg + i;
-      const float p = (m < M && qvalid) ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
+      const float p = (m < M && tvalid) ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
       dl[i] = p * (mix * dp[i] - delq) * scale;
-      if (nb0 == 0) {
-        put_elem(sDLm + m * LY::LDC + 16 * wb + r, dl[i]);
-        put_elem(sPm + m * LY::LDC + 16 * wb + r, p * mix);
-      }
+      put_elem(sDLm + m * LY::LDC + u, dl[i]);
+      put_elem(sPm + m * LY::LDC + u, p * mix);
     }
     frag op;
     pack_acc(op, dl, f32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int x2 = 0; x2 < NBH; ++x2)
-      mma32(accQ[x2], op, ld_frag_perm(sMkT, LY::LDM, 16 * (nb0 + x2) + r, 0, 0, kg));
+    for (int x2 = 0; x2 < NB; ++x2) mma32(acc0[x2], ld_frag_perm(sMkT, LY::LDM, 16 * x2 + r, 0, 0, kg), op);
   }
   const int kt_lo = max(0, t0 - W + 1) / C;
-  const int qlo = t0 + 16 * wb;
-  for (int kt = c; kt >= kt_lo; --kt) {
-    const int kbase = kt * C;
-    stage_rows(sKt, k, kbase);
-    __syncthreads();   // key tile of chunk kt staged
-    f32x4 dl[4];
-    bool vis[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int s0 = kbase + 16 * kb;
-      vis[kb] = (s0 <= qlo + 15) && (s0 + 15 >= qlo - W + 1);
-      f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
-      if (vis[kb]) {
-        frag fv[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) fv[ks] = ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          mma32(x, ld_frag(sKt, LDQ, 16 * kb + r, 32 * ks + 8 * kg), qf[ks]);
-          mma32(dp, fv[ks], of[ks]);
-        }
-        mfma_drain();
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + 4 * kg + i;
-        const bool ok = vis[kb] && qvalid && s <= tq && s > tq - W;
-        const float p = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
-        dl[kb][i] = p * (mix * dp[i] - delq) * scale;
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      if (vis[2 * p] || vis[2 * p + 1]) {
-        frag op;
-        pack_acc(op, dl[2 * p], dl[2 * p + 1]);
-#pragma unroll
-        for (int x = 0; x < NBH; ++x)
-          mma32(accQ[x], op, ld_frag_tr(sKt, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
-      }
-    __syncthreads();
-  }
-
-  // ----------------------------------------- anchor window, key side (dk, dv)
-  const int srow = urow;                           // this lane's key
-  frag kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = ldg_row_frag<T>(k, D, srow, 32 * ks + 8 * kg, L);
-    vf[ks] = ldg_row_frag<T>(v, D, srow, 32 * ks + 8 * kg, L);
-  }
   const int qc_hi = min(NC - 1, (t0 + C - 1 + W - 1) / C);
-  T* sQr = sQt;                                    // raw q of the query chunk (row-major)
-  for (int qc = c; qc <= qc_hi; ++qc) {
-    const int qbase = qc * C;
-    T* dOr = (qc == c) ? sdO : sKh;                // dO of the query chunk (row-major)
-    stage_rows(sQr, q, qbase);
-    if (qc != c) stage_rows(dOr, dO, qbase);
-    __syncthreads();   // q / dO of chunk qc staged
-    const int slo = t0 + 16 * wb;                  // first key of this wave
-    f32x4 dl[4], pp[4];
-    bool vis[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int q0 = qbase + 16 * tb;
-      vis[tb] = (q0 + 15 >= slo) && (q0 <= slo + 15 + W - 1);
-      f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
-      if (vis[tb]) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          mma32(x, ld_frag(sQr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), kf[ks]);
-          mma32(dp, ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), vf[ks]);
-        }
-        mfma_drain();
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tl = 16 * tb + 4 * kg + i;        // query within chunk qc
-        const int t = qbase + tl;
-        const int li = (qc - c) * C + tl;
-        const bool ok = vis[tb] && t < L && srow <= t && srow > t - W;
-        const float p = ok ? fast_exp2(x[i] * sl2 - sLse[li]) : 0.f;
-        pp[tb][i] = p * mix;
-        dl[tb][i] = p * (mix * dp[i] - sDel[li]) * scale;
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      if (vis[2 * p] || vis[2 * p + 1]) {
-        frag opl, opp;
-        pack_acc(opl, dl[2 * p], dl[2 * p + 1]);
-        pack_acc(opp, pp[2 * p], pp[2 * p + 1]);
-#pragma unroll
-        for (int x = 0; x < NBH; ++x) {
-          mma32(accK[x], opl, ld_frag_tr(sQr, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
-          mma32(accV[x], opp, ld_frag_tr(dOr, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * (nb0 + x), lane));
-        }
-      }
-    // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
-    if (qc == c && M > 0 && w < NB) {
-      float* dst = a.ws_dmeta + (((size_t)b * NC + c) * a.H + h) * M * 2 * D;
-      const int d0 = 16 * w;
-      f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks) {
-        mma32(xk, ld_frag_tr(sQr, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
-              ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
-        mma32(xv, ld_frag_tr(sdO, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
-              ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
-      }
-      mfma_drain();
-      if (r < M)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[(size_t)r * 2 * D + d0 + 4 * kg + i] = xk[i];
-          dst[(size_t)r * 2 * D + D + d0 + 4 * kg + i] = xv[i];
-        }
+  const int n_q = c - kt_lo + 1, n_k = qc_hi - c + 1;
+  const int n_it = max(n_q, n_k);
+  const int lo = t0 + 16 * wb;                     // first query (Q role) or key (K role) of this wave
+  for (int it = 0; it < n_it; ++it) {
+    __syncthreads();   // the previous tiles' readers are done
+    if (it < n_q) stage_rows(sKw, k, (c - it) * C);
+    if (it < n_k) {
+      stage_rows(sQw, q, (c + it) * C);
+      if (it > 0) stage_rows(sDw, dO, (c + it) * C);
     }
     __syncthreads();
+    if (qrole) {
+      if (it < n_q) {
+        // query side: keys of chunk kt, dq += dl K
+        const int kbase = (c - it) * C;
+        f32x4 dl[4];
+        bool vis[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int s0 = kbase + 16 * kb;
+          vis[kb] = (s0 <= lo + 15) && (s0 + 15 >= lo - W + 1);
+          f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+          if (vis[kb]) {
+            frag fv[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) fv[ks] = ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              mma32(x, ld_frag(sKw, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fa[ks]);
+              mma32(dp, fv[ks], fb[ks]);
+            }
+            mfma_drain();
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = s0 + 4 * kg + i;
+            const bool ok = vis[kb] && tvalid && s <= tok && s > tok - W;
+            const float p = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
+            dl[kb][i] = p * (mix * dp[i] - delq) * scale;
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (vis[2 * p] || vis[2 * p + 1]) {
+            frag op;
+            pack_acc(op, dl[2 * p], dl[2 * p + 1]);
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+              mma32(acc0[x], ld_frag_tr(sKw, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
+          }
+      }
+    } else {
+      if (it < n_k) {
+        // key side: queries of chunk qc, dk += dl^T Q, dv += (mix P)^T dO
+        const int qc = c + it, qbase = qc * C;
+        const T* dOr = it == 0 ? sdO : sDw;
+        f32x4 dl[4], pp[4];
+        bool vis[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int q0 = qbase + 16 * tb;
+          vis[tb] = (q0 + 15 >= lo) && (q0 <= lo + 15 + W - 1);
+          f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+          if (vis[tb]) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              mma32(x, ld_frag(sQw, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fa[ks]);
+              mma32(dp, ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fb[ks]);
+            }
+            mfma_drain();
+          }
+          const f32x4 lse4 = lds4(sLse + it * C + 16 * tb + 4 * kg);
+          const f32x4 del4 = lds4(sDel + it * C + 16 * tb + 4 * kg);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = q0 + 4 * kg + i;
+            const bool ok = vis[tb] && t < L && tok <= t && tok > t - W;
+            const float p = ok ? fast_exp2(x[i] * sl2 - lse4[i]) : 0.f;
+            pp[tb][i] = p * mix;
+            dl[tb][i] = p * (mix * dp[i] - del4[i]) * scale;
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (vis[2 * p] || vis[2 * p + 1]) {
+            frag opl, opp;
+            pack_acc(opl, dl[2 * p], dl[2 * p + 1]);
+            pack_acc(opp, pp[2 * p], pp[2 * p + 1]);
+#pragma unroll
+            for (int x = 0; x < NB; ++x) {
+              mma32(acc0[x], ld_frag_tr(sQw, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), opl);
+              mma32(acc1[x], ld_frag_tr(dOr, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), opp);
+            }
+          }
+      }
+      // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
+      if (it == 0 && M > 0) {
+        float* dst = a.ws_dmeta + (((size_t)b * NC + c) * a.H + h) * M * 2 * D;
+#pragma unroll
+        for (int xb = 0; xb < NB / 4; ++xb) {
+          const int d0 = 16 * (wb * (NB / 4) + xb);
+          f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < C / 32; ++ks) {
+            mma32(xk, ld_frag_tr(sQw, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
+                  ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
+            mma32(xv, ld_frag_tr(sdO, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
+                  ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
+          }
+          mfma_drain();
+          if (r < M)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              dst[(size_t)r * 2 * D + d0 + 4 * kg + i] = xk[i];
+              dst[(size_t)r * 2 * D + D + d0 + 4 * kg + i] = xv[i];
+            }
+        }
+      }
+    }
   }
 
   // ------------------------------------------------------------------ store
   mfma_drain();
+  if (tvalid) {
+    const size_t o = hoff + (size_t)tok * D;
+    if (qrole) {
 #pragma unroll
-  for (int x = 0; x < NBH; ++x)
+      for (int x = 0; x < NB; ++x)
+        stg4(reinterpret_cast<T*>(a.dq) + o + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = t0 + 16 * wb + 4 * kg + e;
-      if (t < L) {
-        const size_t o = hoff + (size_t)t * D + 16 * (nb0 + x) + r;
-        put_elem(reinterpret_cast<T*>(a.dq) + o, accQ[x][e]);
-        put_elem(reinterpret_cast<T*>(a.dk) + o, accK[x][e]);
-        put_elem(reinterpret_cast<T*>(a.dv) + o, accV[x][e]);
+      for (int x = 0; x < NB; ++x) {
+        stg4(reinterpret_cast<T*>(a.dk) + o + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
+        stg4(reinterpret_cast<T*>(a.dv) + o + 16 * x + 4 * kg, acc1[x][0], acc1[x][1], acc1[x][2], acc1[x][3]);
       }
     }
+  }
 }
 
 // ------------------------------------------------------------ meta reduce
