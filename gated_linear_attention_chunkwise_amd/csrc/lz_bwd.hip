@@ -94,7 +94,8 @@ struct CkLayout {
   static constexpr size_t oKh = tile;         // k^ ; window: query tile of a later chunk
   static constexpr size_t oEb = 2 * tile;     // e^b; window: dO tile of a later chunk
   static constexpr size_t odO = 3 * tile;     // dO of this chunk
-  static constexpr size_t oBig = 4 * tile;    // dS'^T [D][D] | gate-scan scratch | d b [C][LDB] fp32
+  static constexpr size_t oV = 4 * tile;      // v of this chunk; window: value tile of an earlier chunk
+  static constexpr size_t oBig = 5 * tile;    // dS'^T [D][D] | gate-scan scratch | d b [C][LDB] fp32
   static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * LDB ? sizeof(T) * D * LDQ
                                                                                    : sizeof(float) * C * LDB;
   static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   T* sdSt = reinterpret_cast<T*>(smem + LY::oBig);          // dS' transposed [j][i], row-major
   float* sScan = reinterpret_cast<float*>(smem + LY::oBig);
   float* sDb = reinterpret_cast<float*>(smem + LY::oBig);
+  T* sV = reinterpret_cast<T*>(smem + LY::oV);
   T* sKw = sQt;    // window: raw keys of chunk kt (query side)
   T* sQw = sKh;    // window: raw queries of chunk qc (key side)
   T* sDw = sEb;    // window: dO of chunk qc > c (key side)
@@ -193,11 +195,35 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     }
   };
 
+  // Register image of a [C][D] chunk tile: NVT 16-byte vectors per thread.
+  constexpr int NVT = C * (D / VEC) / NTHR_CK;
+  auto fetch_rows = [&](V16 (&dst)[NVT], const T* src, int row0) {
+#pragma unroll
+    for (int e = 0; e < NVT; ++e) {
+      const int idx = tid + e * NTHR_CK, t = idx / (D / VEC), cv = idx % (D / VEC);
+      dst[e] = (row0 + t < L) ? ldg16(src + (size_t)(row0 + t) * D + cv * VEC) : zero16();
+    }
+  };
+  auto put_rows = [&](T* dst, const V16 (&src)[NVT]) {
+#pragma unroll
+    for (int e = 0; e < NVT; ++e) {
+      const int idx = tid + e * NTHR_CK, t = idx / (D / VEC), cv = idx % (D / VEC);
+      *reinterpret_cast<V16*>(dst + t * LDQ + cv * VEC) = src[e];
+    }
+  };
+
   // ---------------------------------------------------------------- staging
   const int cg = tid % SM::VPR, tg = tid / SM::VPR;
   {
     V16 rq[TPT], rk[TPT];
     f32x4 rg[TPT][GV];
+    constexpr int NVS = D * (D / VEC) / NTHR_CK;   // dS' vectors per thread
+    V16 rds[NVS];
+#pragma unroll
+    for (int e = 0; e < NVS; ++e) {
+      const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
+      rds[e] = ldg16(dSpT + (size_t)j * D + cv * VEC);
+    }
 #pragma unroll
     for (int uu = 0; uu < TPT; ++uu) {
       const int t = t0 + tg * TPT + uu;
@@ -209,6 +235,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         rg[uu][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
     }
     stage_rows(sdO, dO, t0);
+    stage_rows(sV, v, t0);
     // meta keys transposed, lse / delta of this chunk and the next two
     for (int e = tid; e < D * 16; e += NTHR_CK) {
       const int d = e / 16, m = e % 16;
@@ -236,10 +263,11 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       st_vec(sKh + t * LDQ + cg * VEC, kh);
       st_vec(sEb + t * LDQ + cg * VEC, eb);
     }
-    __syncthreads();   // scan scratch is dead: stage dS' (transposed, as stored) into the same region
-    for (int e = tid; e < D * (D / VEC); e += NTHR_CK) {
-      const int j = e / (D / VEC), cv = e % (D / VEC);
-      *reinterpret_cast<V16*>(sdSt + j * LDQ + cv * VEC) = ldg16(dSpT + (size_t)j * D + cv * VEC);
+    __syncthreads();   // scan scratch is dead: dS' (transposed, as stored) goes into the same region
+#pragma unroll
+    for (int e = 0; e < NVS; ++e) {
+      const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
+      *reinterpret_cast<V16*>(sdSt + j * LDQ + cv * VEC) = rds[e];
     }
     __syncthreads();
   }
@@ -259,11 +287,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     for (int sb = 0; sb < 4; ++sb) {
       blk[sb] = f32x4{0, 0, 0, 0};
       if (sb <= wb) {
-        frag fv[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) fv[ks] = ldg_row_frag<T>(v, D, t0 + 16 * sb + r, 32 * ks + 8 * kg, L);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma32(blk[sb], fv[ks], fo[ks]);
+        for (int ks = 0; ks < KS; ++ks) mma32(blk[sb], ld_frag(sV, LDQ, 16 * sb + r, 32 * ks + 8 * kg), fo[ks]);
         mfma_drain();
         if (sb == wb)
 #pragma unroll
@@ -291,7 +316,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     frag fvu[KS], fkh[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      fvu[ks] = ldg_row_frag<T>(v, D, tok, 32 * ks + 8 * kg, L);
+      fvu[ks] = ld_frag(sV, LDQ, u, 32 * ks + 8 * kg);
       fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
     }
     // A blocks (queries of block tb >= wb, keys of block wb): dv += A^T dO
@@ -352,6 +377,10 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     }
   }
   mfma_drain();
+  // window tiles of the first iteration (raw keys and queries of this chunk; its values and dO are staged)
+  V16 pk[NVT], pv[NVT], pq[NVT], pd[NVT];
+  fetch_rows(pk, k, t0);
+  fetch_rows(pq, q, t0);
   __syncthreads();   // every wave is done with dS': its region now holds the per-token gate gradient
 
   // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b
@@ -439,95 +468,106 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const int lo = t0 + 16 * wb;                     // first query (Q role) or key (K role) of this wave
   for (int it = 0; it < n_it; ++it) {
     __syncthreads();   // the previous tiles' readers are done
-    if (it < n_q) stage_rows(sKw, k, (c - it) * C);
+    if (it < n_q) {
+      put_rows(sKw, pk);
+      if (it > 0) put_rows(sV, pv);
+    }
     if (it < n_k) {
-      stage_rows(sQw, q, (c + it) * C);
-      if (it > 0) stage_rows(sDw, dO, (c + it) * C);
+      put_rows(sQw, pq);
+      if (it > 0) put_rows(sDw, pd);
+    }
+    // next iteration's tiles load while this one is processed
+    if (it + 1 < n_q) {
+      fetch_rows(pk, k, (c - it - 1) * C);
+      fetch_rows(pv, v, (c - it - 1) * C);
+    }
+    if (it + 1 < n_k) {
+      fetch_rows(pq, q, (c + it + 1) * C);
+      fetch_rows(pd, dO, (c + it + 1) * C);
     }
     __syncthreads();
     if (qrole) {
       if (it < n_q) {
-        // query side: keys of chunk kt, dq += dl K
+        // query side: keys of chunk kt, dq += dl K, two 16-key blocks at a time
         const int kbase = (c - it) * C;
-        f32x4 dl[4];
-        bool vis[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int s0 = kbase + 16 * kb;
-          vis[kb] = (s0 <= lo + 15) && (s0 + 15 >= lo - W + 1);
-          f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
-          if (vis[kb]) {
-            frag fv[KS];
+        for (int p = 0; p < 2; ++p) {
+          f32x4 dl[2];
+          bool vis[2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) fv[ks] = ldg_row_frag<T>(v, D, s0 + r, 32 * ks + 8 * kg, L);
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int kb = 2 * p + h2, s0 = kbase + 16 * kb;
+            vis[h2] = (s0 <= lo + 15) && (s0 + 15 >= lo - W + 1);
+            f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+            if (vis[h2]) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              mma32(x, ld_frag(sKw, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fa[ks]);
-              mma32(dp, fv[ks], fb[ks]);
+              for (int ks = 0; ks < KS; ++ks) {
+                mma32(x, ld_frag(sKw, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fa[ks]);
+                mma32(dp, ld_frag(sV, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fb[ks]);
+              }
+              mfma_drain();
             }
-            mfma_drain();
-          }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int s = s0 + 4 * kg + i;
-            const bool ok = vis[kb] && tvalid && s <= tok && s > tok - W;
-            const float p = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
-            dl[kb][i] = p * (mix * dp[i] - delq) * scale;
+            for (int i = 0; i < 4; ++i) {
+              const int s2 = s0 + 4 * kg + i;
+              const bool ok = vis[h2] && tvalid && s2 <= tok && s2 > tok - W;
+              const float pr = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
+              dl[h2][i] = pr * (mix * dp[i] - delq) * scale;
+            }
           }
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          if (vis[2 * p] || vis[2 * p + 1]) {
+          if (vis[0] || vis[1]) {
             frag op;
-            pack_acc(op, dl[2 * p], dl[2 * p + 1]);
+            pack_acc(op, dl[0], dl[1]);
 #pragma unroll
             for (int x = 0; x < NB; ++x)
               mma32(acc0[x], ld_frag_tr(sKw, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
           }
+        }
       }
     } else {
       if (it < n_k) {
-        // key side: queries of chunk qc, dk += dl^T Q, dv += (mix P)^T dO
+        // key side: queries of chunk qc, dk += dl^T Q, dv += (mix P)^T dO, two 16-query blocks at a time
         const int qc = c + it, qbase = qc * C;
         const T* dOr = it == 0 ? sdO : sDw;
-        f32x4 dl[4], pp[4];
-        bool vis[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int q0 = qbase + 16 * tb;
-          vis[tb] = (q0 + 15 >= lo) && (q0 <= lo + 15 + W - 1);
-          f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
-          if (vis[tb]) {
+        for (int p = 0; p < 2; ++p) {
+          f32x4 dl[2], pp[2];
+          bool vis[2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              mma32(x, ld_frag(sQw, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fa[ks]);
-              mma32(dp, ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fb[ks]);
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int tb = 2 * p + h2, q0 = qbase + 16 * tb;
+            vis[h2] = (q0 + 15 >= lo) && (q0 <= lo + 15 + W - 1);
+            f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+            if (vis[h2]) {
+#pragma unroll
+              for (int ks = 0; ks < KS; ++ks) {
+                mma32(x, ld_frag(sQw, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fa[ks]);
+                mma32(dp, ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fb[ks]);
+              }
+              mfma_drain();
             }
-            mfma_drain();
-          }
-          const f32x4 lse4 = lds4(sLse + it * C + 16 * tb + 4 * kg);
-          const f32x4 del4 = lds4(sDel + it * C + 16 * tb + 4 * kg);
+            const f32x4 lse4 = lds4(sLse + it * C + 16 * tb + 4 * kg);
+            const f32x4 del4 = lds4(sDel + it * C + 16 * tb + 4 * kg);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = q0 + 4 * kg + i;
-            const bool ok = vis[tb] && t < L && tok <= t && tok > t - W;
-            const float p = ok ? fast_exp2(x[i] * sl2 - lse4[i]) : 0.f;
-            pp[tb][i] = p * mix;
-            dl[tb][i] = p * (mix * dp[i] - del4[i]) * scale;
+            for (int i = 0; i < 4; ++i) {
+              const int t = q0 + 4 * kg + i;
+              const bool ok = vis[h2] && t < L && tok <= t && tok > t - W;
+              const float pr = ok ? fast_exp2(x[i] * sl2 - lse4[i]) : 0.f;
+              pp[h2][i] = pr * mix;
+              dl[h2][i] = pr * (mix * dp[i] - del4[i]) * scale;
+            }
           }
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          if (vis[2 * p] || vis[2 * p + 1]) {
+          if (vis[0] || vis[1]) {
             frag opl, opp;
-            pack_acc(opl, dl[2 * p], dl[2 * p + 1]);
-            pack_acc(opp, pp[2 * p], pp[2 * p + 1]);
+            pack_acc(opl, dl[0], dl[1]);
+            pack_acc(opp, pp[0], pp[1]);
 #pragma unroll
             for (int x = 0; x < NB; ++x) {
               mma32(acc0[x], ld_frag_tr(sQw, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), opl);
               mma32(acc1[x], ld_frag_tr(dOr, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), opp);
             }
           }
+        }
       }
       // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
       if (it == 0 && M > 0) {
