@@ -212,6 +212,12 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     }
   };
 
+  // boundary term of dg for this thread's column (consumed after the GLA phase)
+  float bnd = 0.f;
+  if (c + 1 < NC)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bnd += wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + tid % D];
+
   // ---------------------------------------------------------------- staging
   const int cg = tid % SM::VPR, tg = tid / SM::VPR;
   {
@@ -377,6 +383,13 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     }
   }
   mfma_drain();
+  // this lane's window operands: Q role raw q and dO of its query, K role raw k and v of its key
+  frag fa[KS], fb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    fa[ks] = ldg_row_frag<T>(qrole ? q : k, D, tok, 32 * ks + 8 * kg, L);
+    fb[ks] = ld_frag(qrole ? sdO : sV, LDQ, u, 32 * ks + 8 * kg);
+  }
   // window tiles of the first iteration (raw keys and queries of this chunk; its values and dO are staged)
   V16 pk[NVT], pv[NVT], pq[NVT], pd[NVT];
   fetch_rows(pk, k, t0);
@@ -416,10 +429,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       sDb[uu * LDB + i] = run;
     }
     __syncthreads();
-    float carry = 0.f;
+    float carry = bnd;
     for (int p2 = part + 1; p2 < PARTS; ++p2) carry += sDb[(SEG * p2) * LDB + i];
-    if (c + 1 < NC)
-      for (int j = 0; j < NJ; ++j) carry += wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + i];
     for (int uu = SEG * part; uu < SEG * (part + 1); ++uu) {
       const int t = t0 + uu;
       if (t < L) a.dg[hoff + (size_t)t * D + i] = sDb[uu * LDB + i] + carry;
@@ -429,12 +440,6 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 
   // ----------------------------------------------------------- anchor window
   const bool tvalid = tok < L;
-  frag fa[KS], fb[KS];   // Q role: raw q, dO of this lane's query; K role: raw k, v of this lane's key
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    fa[ks] = ldg_row_frag<T>(qrole ? q : k, D, tok, 32 * ks + 8 * kg, L);
-    fb[ks] = qrole ? ld_frag(sdO, LDQ, u, 32 * ks + 8 * kg) : ldg_row_frag<T>(v, D, tok, 32 * ks + 8 * kg, L);
-  }
   const float lse2 = sLse[u], delq = sDel[u];
   if (qrole && M > 0) {
     // meta keys (always visible); absent meta values read as zero rows (no branch around the product)
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      mma32(x, ldg_row_frag<T>(mk, D, r, 32 * ks + 8 * kg, M), fa[ks]);
+      mma32(x, ld_frag_tr(sMkT, LY::LDM, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 0, lane), fa[ks]);
       mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), fb[ks]);
     }
     mfma_drain();
