@@ -240,17 +240,32 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       for (int e = 0; e < GV; ++e)
         rg[uu][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
     }
-    stage_rows(sdO, dO, t0);
-    stage_rows(sV, v, t0);
-    // meta keys transposed, lse / delta of this chunk and the next two
-    for (int e = tid; e < D * 16; e += NTHR_CK) {
-      const int d = e / 16, m = e % 16;
-      put_elem(sMkT + d * LY::LDM + m, m < M ? Tr<T>::to_f(mk[(size_t)m * D + d]) : 0.f);
+    // every other load of the staging phase is issued before anything waits on one
+    V16 rdo[NVT], rv[NVT];
+    fetch_rows(rdo, dO, t0);
+    fetch_rows(rv, v, t0);
+    constexpr int NMK = D * 16 / NTHR_CK;          // meta-key elements per thread
+    float rmk[NMK];
+#pragma unroll
+    for (int e = 0; e < NMK; ++e) {
+      const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
+      rmk[e] = m < M ? Tr<T>::to_f(mk[(size_t)m * D + d]) : 0.f;
     }
-    for (int e = tid; e < 3 * C; e += NTHR_CK) {
-      const int t = t0 + e;
-      sLse[e] = t < L ? a.lse[(size_t)bh * L + t] * LOG2E : 0.f;
-      sDel[e] = t < L ? a.ws_delta[(size_t)bh * L + t] : 0.f;
+    float rls = 0.f, rdl = 0.f;                    // lse / delta of this chunk and the next two
+    if (tid < 3 * C && t0 + tid < L) {
+      rls = a.lse[(size_t)bh * L + t0 + tid] * LOG2E;
+      rdl = a.ws_delta[(size_t)bh * L + t0 + tid];
+    }
+    put_rows(sdO, rdo);
+    put_rows(sV, rv);
+#pragma unroll
+    for (int e = 0; e < NMK; ++e) {
+      const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
+      put_elem(sMkT + d * LY::LDM + m, rmk[e]);
+    }
+    if (tid < 3 * C) {
+      sLse[tid] = rls;
+      sDel[tid] = rdl;
     }
     f32x4 tot[GV];
     chunk_prefix<D, VEC, NTHR_CK, TPT, GV>(rg, tot, sScan, cg, tg);
