@@ -95,7 +95,7 @@ struct CkLayout {
   static constexpr size_t oEb = 2 * tile;     // e^b; window: dO tile of a later chunk
   static constexpr size_t odO = 3 * tile;     // dO of this chunk
   static constexpr size_t oV = 4 * tile;      // v of this chunk; window: value tile of an earlier chunk
-  static constexpr size_t oBig = 5 * tile;    // dS'^T [D][D] | gate-scan scratch | d b [C][LDB] fp32
+  static constexpr size_t oBig = 5 * tile;    // dS'^T [D][D] | d b [C][LDB] fp32
   static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * LDB ? sizeof(T) * D * LDQ
                                                                                    : sizeof(float) * C * LDB;
   static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
@@ -124,14 +124,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
                                                             const float* __restrict__ wsbnd) {
   using LY = CkLayout<T, D>;
-  using SM = ScanMap<D, Tr<T>::VEC, NTHR_CK>;
   using frag = typename Tr<T>::frag;
-  constexpr int VEC = Tr<T>::VEC, TPT = SM::TPT, GV = SM::GV;
+  constexpr int VEC = Tr<T>::VEC;
   constexpr int NB = D / 16;     // 16-wide blocks over the head dim
   constexpr int KS = D / 32;     // K steps over the head dim
   constexpr int NJ = D / DVTA;
   constexpr int LDQ = LY::LDQ, LDB = LY::LDB;
-  static_assert(sizeof(float) * SM::NTG * D <= LY::bigBytes, "scan scratch fits in the shared region");
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
@@ -139,7 +137,6 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   T* sEb = reinterpret_cast<T*>(smem + LY::oEb);
   T* sdO = reinterpret_cast<T*>(smem + LY::odO);
   T* sdSt = reinterpret_cast<T*>(smem + LY::oBig);          // dS' transposed [j][i], row-major
-  float* sScan = reinterpret_cast<float*>(smem + LY::oBig);
   float* sDb = reinterpret_cast<float*>(smem + LY::oBig);
   T* sV = reinterpret_cast<T*>(smem + LY::oV);
   T* sKw = sQt;    // window: raw keys of chunk kt (query side)
@@ -186,14 +183,6 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const int u = 16 * wb + r;        // this lane's token within the chunk
   const int tok = t0 + u;
 
-  // Copy a [C][D] row-major chunk tile (rows past L are zero) into LDS.
-  auto stage_rows = [&](T* dst, const T* src, int row0) {
-    for (int e = tid; e < C * (D / VEC); e += NTHR_CK) {
-      const int t = e / (D / VEC), cv = e % (D / VEC);
-      *reinterpret_cast<V16*>(dst + t * LDQ + cv * VEC) =
-          (row0 + t < L) ? ldg16(src + (size_t)(row0 + t) * D + cv * VEC) : zero16();
-    }
-  };
 
   // Register image of a [C][D] chunk tile: NVT 16-byte vectors per thread.
   constexpr int NVT = C * (D / VEC) / NTHR_CK;
@@ -219,10 +208,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     for (int j = 0; j < NJ; ++j) bnd += wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + tid % D];
 
   // ---------------------------------------------------------------- staging
-  const int cg = tid % SM::VPR, tg = tid / SM::VPR;
+  // every load of the staging phase is issued before anything waits on one
   {
-    V16 rq[TPT], rk[TPT];
-    f32x4 rg[TPT][GV];
     constexpr int NVS = D * (D / VEC) / NTHR_CK;   // dS' vectors per thread
     V16 rds[NVS];
 #pragma unroll
@@ -230,17 +217,9 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
       rds[e] = ldg16(dSpT + (size_t)j * D + cv * VEC);
     }
-#pragma unroll
-    for (int uu = 0; uu < TPT; ++uu) {
-      const int t = t0 + tg * TPT + uu;
-      const bool ok = t < L;
-      rq[uu] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
-      rk[uu] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
-#pragma unroll
-      for (int e = 0; e < GV; ++e)
-        rg[uu][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
-    }
-    // every other load of the staging phase is issued before anything waits on one
+    const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
+    GateStrip<T> gs;
+    if (has_strip) gs.load(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
     V16 rdo[NVT], rv[NVT];
     fetch_rows(rdo, dO, t0);
     fetch_rows(rv, v, t0);
@@ -267,24 +246,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       sLse[tid] = rls;
       sDel[tid] = rdl;
     }
-    f32x4 tot[GV];
-    chunk_prefix<D, VEC, NTHR_CK, TPT, GV>(rg, tot, sScan, cg, tg);
-#pragma unroll
-    for (int uu = 0; uu < TPT; ++uu) {
-      const int t = tg * TPT + uu;
-      float qt[VEC], kh[VEC], eb[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float bb = rg[uu][e >> 2][e & 3];
-        eb[e] = __expf(bb);
-        qt[e] = v16_get(rq[uu], e, (T*)nullptr) * eb[e];
-        kh[e] = v16_get(rk[uu], e, (T*)nullptr) * __expf(-bb);
-      }
-      st_vec(sQt + t * LDQ + cg * VEC, qt);
-      st_vec(sKh + t * LDQ + cg * VEC, kh);
-      st_vec(sEb + t * LDQ + cg * VEC, eb);
-    }
-    __syncthreads();   // scan scratch is dead: dS' (transposed, as stored) goes into the same region
+    // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b
+    if (has_strip) gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
 #pragma unroll
     for (int e = 0; e < NVS; ++e) {
       const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);

@@ -288,4 +288,66 @@ __device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot
     for (int e = 0; e < SM::GV; ++e) rg[u][e] += excl[e];
 }
 
+// ------------------------------------------------- gate prefix in column strips
+// One wave handles a strip of 16 columns of a chunk: lane (tg = lane & 15,
+// cg = lane >> 4) holds tokens 4*tg .. 4*tg+3 of columns col .. col+3 with
+// col = 16*strip + 4*cg, so the chunk-local prefix over tokens is an
+// in-thread sum plus a scan inside the 16-lane row (DPP): no LDS round trip,
+// no barrier.
+__device__ __forceinline__ bf16x4 ld4raw(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ f32x4 ld4raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+template <typename T>
+struct GateStrip {
+  using R4 = decltype(ld4raw(static_cast<const T*>(nullptr)));
+  R4 q[4], k[4];   // raw q and k
+  f32x4 g[4];      // log-gates, then the inclusive prefix b
+
+  __device__ __forceinline__ void load(const T* qp, const T* kp, const float* gp, int D, int t0, int L, int col,
+                                       int tg) {
+    if (t0 + CHUNK <= L) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t o = (size_t)(t0 + 4 * tg + u) * D + col;
+        q[u] = ld4raw(qp + o);
+        k[u] = ld4raw(kp + o);
+        g[u] = ld4raw(gp + o);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + 4 * tg + u;
+        const size_t o = (size_t)t * D + col;
+        q[u] = t < L ? ld4raw(qp + o) : R4{};
+        k[u] = t < L ? ld4raw(kp + o) : R4{};
+        g[u] = t < L ? ld4raw(gp + o) : f32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  // q e^b, k e^-b and (if sEb) e^b into rows 4*tg+u, columns lcol .. lcol+3 of LDS tiles
+  __device__ __forceinline__ void fold(T* sQt, T* sKh, T* sEb, int ldq, int lcol, int tg) {
+#pragma unroll
+    for (int u = 1; u < 4; ++u) g[u] += g[u - 1];
+    f32x4 excl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) excl[e] = row_scan16(g[3][e]) - g[3][e];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 eb, qt, kh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b = g[u][e] + excl[e];
+        eb[e] = __expf(b);
+        qt[e] = (float)q[u][e] * eb[e];
+        kh[e] = (float)k[u][e] * __expf(-b);
+      }
+      const int row = (4 * tg + u) * ldq + lcol;
+      st4(sQt + row, qt[0], qt[1], qt[2], qt[3]);
+      st4(sKh + row, kh[0], kh[1], kh[2], kh[3]);
+      if (sEb != nullptr) st4(sEb + row, eb[0], eb[1], eb[2], eb[3]);
+    }
+  }
+};
+
 }  // namespace lz
