@@ -180,6 +180,20 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_row<0x121>(x);
   return x;
 }
+// Sum over aligned groups of N consecutive lanes, returned in every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float x);
+template <>
+__device__ __forceinline__ float group_sum<8>(float x) {
+  x += dpp_row<0x141>(x);   // half-row mirror: lane i of 8 pairs with lane 7-i
+  x += dpp_row<0xB1>(x);    // quad permute [1,0,3,2]
+  x += dpp_row<0x4E>(x);    // quad permute [2,3,0,1]
+  return x;
+}
+template <>
+__device__ __forceinline__ float group_sum<16>(float x) { return row_sum16(x); }
+template <>
+__device__ __forceinline__ float group_sum<32>(float x) { return xor_sum(row_sum16(x), 16); }
 
 constexpr float LOG2E = 1.4426950408889634f;
 

@@ -75,6 +75,15 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
     kr[u] = ok ? ldg16(rk + (size_t)s * D + cv * VEC) : zero16();
     vr[u] = ok ? ldg16(rv + (size_t)s * D + cv * VEC) : zero16();
   }
+  // meta keys: rows m = s0 + p * RPP of the ring thread map (M <= 16)
+  constexpr int NMP = (16 + RPP - 1) / RPP;
+  const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
+  V16 mkr[NMP];
+#pragma unroll
+  for (int p = 0; p < NMP; ++p) {
+    const int m = s0 + p * RPP;
+    mkr[p] = m < M ? ldg16(mk + (size_t)m * D + cv * VEC) : zero16();
+  }
   for (int i = tid; i < D; i += NTHR) {
     sq[i] = Tr<T>::to_f(qg[i]);
     sk[i] = Tr<T>::to_f(kg[i]);
@@ -108,22 +117,16 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
   // ---- window logits (log2 units): meta keys, then ring slots (new token from the inputs)
   const float sl2 = a.scale * LOG2E;
   float lmax = -INFINITY;
-  {
-    const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
-    for (int m0 = 0; m0 < M; m0 += RPP) {   // uniform trip count across the workgroup
-      const int m = m0 + s0;
-      float acc = 0.f;
-      if (m < M) {
-        const V16 x = ldg16(mk + (size_t)m * D + cv * VEC);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(x, e, (T*)nullptr);
-      }
+  for (int p = 0; p < NMP; ++p) {
+    const int m = s0 + p * RPP;
+    float acc = 0.f;
 #pragma unroll
-      for (int o = 1; o < VPR; o <<= 1) acc = xor_sum(acc, o);
-      if (m < M) {
-        if (cv == 0) slog[m] = acc * sl2;
-        lmax = fmaxf(lmax, acc * sl2);
-      }
+    for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(mkr[p], e, (T*)nullptr);
+    acc = group_sum<VPR>(acc);
+    if (m < M) {
+      if (cv == 0) slog[m] = acc * sl2;
+      lmax = fmaxf(lmax, acc * sl2);
     }
   }
   for (int blk = 0; blk < n; blk += KB) {
@@ -145,8 +148,7 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(kr[u], e, (T*)nullptr);
       }
-#pragma unroll
-      for (int o = 1; o < VPR; o <<= 1) acc = xor_sum(acc, o);
+      acc = group_sum<VPR>(acc);
       if (s < n) {
         if (cv == 0) slog[M + s] = acc * sl2;
         lmax = fmaxf(lmax, acc * sl2);
@@ -233,14 +235,15 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
   {
     T* rkw = reinterpret_cast<T*>(a.ring_k) + ((size_t)bh * W + slot) * D;
     T* rvw = reinterpret_cast<T*>(a.ring_v) + ((size_t)bh * W + slot) * D;
-    for (int d = tid; d < D; d += NTHR) {
-      rkw[d] = kg[d];
-      rvw[d] = vg[d];
+    for (int d = tid; d < D; d += NTHR) {   // exact: the LDS copies came from these values
+      put_elem(rkw + d, sk[d]);
+      put_elem(rvw + d, sv[d]);
     }
   }
   // ---- pos: the last of the H workgroups of sequence b advances it
+  // (no fence: nothing this step writes is read by another workgroup of the step;
+  // the next step is a later launch)
   if (tid == 0) {
-    __threadfence();
     const unsigned int old = atomicAdd(posu + b, 1u << 24);
     if ((old >> 24) == (unsigned int)(a.H - 1)) atomicExch(posu + b, (old & 0x00FFFFFFu) + 1u);
   }
