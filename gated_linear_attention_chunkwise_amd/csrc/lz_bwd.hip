@@ -103,7 +103,9 @@ struct CkLayout {
   static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // mix * p_meta^T [16][C]
   static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 chunks (log2 units)
   static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 chunks
-  static constexpr size_t bytes = oDel + sizeof(float) * 3 * C;
+  static constexpr size_t oBnd = oDel + sizeof(float) * 3 * C;       // boundary term of dg [D]
+  static constexpr size_t oTot = oBnd + sizeof(float) * D;           // per-block column totals of d b [4][D]
+  static constexpr size_t bytes = oTot + sizeof(float) * 4 * D;
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -147,6 +149,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   T* sPm = reinterpret_cast<T*>(smem + LY::oPm);
   float* sLse = reinterpret_cast<float*>(smem + LY::oLse);
   float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
+  float* sBnd = reinterpret_cast<float*>(smem + LY::oBnd);
+  float* sTot = reinterpret_cast<float*>(smem + LY::oTot);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
   const bool qrole = w < 4;        // waves 0..3: dq; waves 4..7: dk, dv
@@ -246,6 +250,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       sLse[tid] = rls;
       sDel[tid] = rdl;
     }
+    if (tid < D) sBnd[tid] = bnd;
     // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b
     if (has_strip) gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
 #pragma unroll
@@ -262,6 +267,10 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
   for (int x = 0; x < NB; ++x) { acc0[x] = f32x4{0, 0, 0, 0}; acc1[x] = acc0[x]; }
   if (qrole) {
+    // S_prev rows for the first K step of the inter-chunk product: issued before the intra-chunk work
+    frag fs[NB];
+#pragma unroll
+    for (int x = 0; x < NB; ++x) fs[x] = ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 8 * kg);
     frag fo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) fo[ks] = ld_frag(sdO, LDQ, u, 32 * ks + 8 * kg);
@@ -289,12 +298,18 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         for (int x = 0; x < NB; ++x)
           mma32(acc0[x], ld_frag_tr(sKh, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
       }
-    // dq~ += dO S_prev^T
+    // dq~ += dO S_prev^T, the next K step's rows loading while one is used
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      frag fn[NB];
+      if (ks + 1 < KS)
 #pragma unroll
-      for (int x = 0; x < NB; ++x)
-        mma32(acc0[x], ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 32 * ks + 8 * kg), fo[ks]);
+        for (int x = 0; x < NB; ++x) fn[x] = ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 32 * (ks + 1) + 8 * kg);
+#pragma unroll
+      for (int x = 0; x < NB; ++x) mma32(acc0[x], fs[x], fo[ks]);
+      if (ks + 1 < KS)
+#pragma unroll
+        for (int x = 0; x < NB; ++x) fs[x] = fn[x];
     }
   } else {
     frag fvu[KS], fkh[KS];
@@ -374,7 +389,10 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   fetch_rows(pq, q, t0);
   __syncthreads();   // every wave is done with dS': its region now holds the per-token gate gradient
 
-  // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b
+  // gate gradient terms d b_u = q~ dq~ - k^ dk^, then dq = dq~ e^b, dk = dk^ e^-b.  The dq waves
+  // hand q~ dq~ over through LDS; the dk/dv waves (same token rows, same lane layout) form d b,
+  // take its suffix sums over their 16 tokens in registers and over later blocks through the
+  // block totals, add the boundary term and store dg.
   if (qrole) {
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
@@ -384,34 +402,29 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     }
   }
   __syncthreads();
+  f32x4 db[NB];
   if (!qrole) {
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
       const int i = 16 * x + 4 * kg;
-      f32x4* p = reinterpret_cast<f32x4*>(sDb + u * LDB + i);
-      *p = *p - lds4(sKh + u * LDQ + i) * acc0[x];
+      db[x] = *reinterpret_cast<const f32x4*>(sDb + u * LDB + i) - lds4(sKh + u * LDQ + i) * acc0[x];
       const f32x4 eb = lds4(sEb + u * LDQ + i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc0[x][e] *= __builtin_amdgcn_rcpf(eb[e]);
+      for (int e = 0; e < 4; ++e) {
+        acc0[x][e] *= __builtin_amdgcn_rcpf(eb[e]);
+        db[x][e] = row_suffix16(db[x][e]);
+      }
+      if (r == 0) *reinterpret_cast<f32x4*>(sTot + wb * D + i) = db[x];
     }
   }
   __syncthreads();
-  // reverse cumulative sum over the chunk plus the boundary rowsum -> dg
-  {
-    constexpr int PARTS = NTHR_CK / D;           // threads per column
-    constexpr int SEG = C / PARTS;
-    const int i = tid % D, part = tid / D;
-    float run = 0.f;
-    for (int uu = SEG * (part + 1) - 1; uu >= SEG * part; --uu) {
-      run += sDb[uu * LDB + i];
-      sDb[uu * LDB + i] = run;
-    }
-    __syncthreads();
-    float carry = bnd;
-    for (int p2 = part + 1; p2 < PARTS; ++p2) carry += sDb[(SEG * p2) * LDB + i];
-    for (int uu = SEG * part; uu < SEG * (part + 1); ++uu) {
-      const int t = t0 + uu;
-      if (t < L) a.dg[hoff + (size_t)t * D + i] = sDb[uu * LDB + i] + carry;
+  if (!qrole) {
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+      const int i = 16 * x + 4 * kg;
+      f32x4 carry = *reinterpret_cast<const f32x4*>(sBnd + i);
+      for (int b2 = wb + 1; b2 < 4; ++b2) carry += *reinterpret_cast<const f32x4*>(sTot + b2 * D + i);
+      if (tok < L) *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = db[x] + carry;
     }
   }
   // (the first window iteration begins with a barrier: d b, q~, k^, e^b are then dead)

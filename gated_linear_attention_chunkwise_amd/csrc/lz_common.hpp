@@ -172,6 +172,14 @@ __device__ __forceinline__ float row_scan16(float x) {
   x += dpp_row<0x118>(x);
   return x;
 }
+// Suffix sum over the 16 lanes of each row: lane r gets the sum of lanes r .. 15.
+__device__ __forceinline__ float row_suffix16(float x) {
+  x += dpp_row<0x101>(x);
+  x += dpp_row<0x102>(x);
+  x += dpp_row<0x104>(x);
+  x += dpp_row<0x108>(x);
+  return x;
+}
 // Sum over the 16 lanes of each row, returned in every lane of the row.
 __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_row<0x128>(x);
