@@ -503,12 +503,20 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
               }
               mfma_drain();
             }
+            // blocks wholly inside the band (every key at or before every query, within the
+            // window, queries inside the sequence) need no per-element mask
+            const bool full = vis[h2] && s0 + 15 <= lo && lo + 15 - s0 < W && lo + 15 < L;
+            if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int s2 = s0 + 4 * kg + i;
-              const bool ok = vis[h2] && tvalid && s2 <= tok && s2 > tok - W;
-              const float pr = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
-              dl[h2][i] = pr * (mix * dp[i] - delq) * scale;
+              for (int i = 0; i < 4; ++i) dl[h2][i] = fast_exp2(x[i] * sl2 - lse2) * (mix * dp[i] - delq) * scale;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int s2 = s0 + 4 * kg + i;
+                const bool ok = vis[h2] && tvalid && s2 <= tok && s2 > tok - W;
+                const float pr = ok ? fast_exp2(x[i] * sl2 - lse2) : 0.f;
+                dl[h2][i] = pr * (mix * dp[i] - delq) * scale;
+              }
             }
           }
           if (vis[0] || vis[1]) {
@@ -544,13 +552,25 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
             }
             const f32x4 lse4 = lds4(sLse + it * C + 16 * tb + 4 * kg);
             const f32x4 del4 = lds4(sDel + it * C + 16 * tb + 4 * kg);
+            // every query of the block at or after every key of this wave, within the window,
+            // inside the sequence: no per-element mask
+            const bool full = vis[h2] && q0 >= lo + 15 && q0 + 15 - lo < W && q0 + 15 < L;
+            if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = q0 + 4 * kg + i;
-              const bool ok = vis[h2] && t < L && tok <= t && tok > t - W;
-              const float pr = ok ? fast_exp2(x[i] * sl2 - lse4[i]) : 0.f;
-              pp[h2][i] = pr * mix;
-              dl[h2][i] = pr * (mix * dp[i] - del4[i]) * scale;
+              for (int i = 0; i < 4; ++i) {
+                const float pr = fast_exp2(x[i] * sl2 - lse4[i]);
+                pp[h2][i] = pr * mix;
+                dl[h2][i] = pr * (mix * dp[i] - del4[i]) * scale;
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int t = q0 + 4 * kg + i;
+                const bool ok = vis[h2] && t < L && tok <= t && tok > t - W;
+                const float pr = ok ? fast_exp2(x[i] * sl2 - lse4[i]) : 0.f;
+                pp[h2][i] = pr * mix;
+                dl[h2][i] = pr * (mix * dp[i] - del4[i]) * scale;
+              }
             }
           }
           if (vis[0] || vis[1]) {
