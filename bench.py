@@ -204,6 +204,7 @@ def bench_decode(args, hip, torch, lib):
     tok = {n: x[n][:, :, P:P + steps].permute(2, 0, 1, 3).contiguous() for n in ("q", "k", "v", "g")}
     mk = x["meta_k"]
     out = torch.empty(steps, w.B, w.H, w.D, device="cuda", dtype=torch.bfloat16)
+    ws = lib.decode_workspace(w.B, w.H, w.D, "cuda")
     del x, pre, f
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
@@ -211,7 +212,8 @@ def bench_decode(args, hip, torch, lib):
     hip.record(e0, stream)
     for t in range(steps):
         lib.lizard_attn_decode_step(tok["q"][t], tok["k"][t], tok["v"][t], tok["g"][t], mk,
-                                    None, state, ring_k, ring_v, pos, window=w.W, scale=w.scale, out=out[t])
+                                    None, state, ring_k, ring_v, pos, window=w.W, scale=w.scale, out=out[t],
+                                    workspace=ws)
     hip.record(e1, stream)
     torch.cuda.synchronize()
     us = hip.ms(e0, e1) * 1e3 / steps
@@ -223,8 +225,8 @@ def bench_decode(args, hip, torch, lib):
                         f"{steps} steps after a {P}-token prefill",
             "tokens_per_s": round(w.B / (us * 1e-6), 1), "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode_kernel"),
-                         "kernel": "decode_kernel",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode"),
+                         "kernel": "decode_state_kernel + decode_window_kernel",
                          "algorithmic_bytes_per_step": bytes_step}}
 
 

@@ -54,7 +54,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd.restype = I32
     lib.lizard_attn_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]
     lib.lizard_attn_bwd.restype = I32
-    lib.lizard_attn_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.lizard_attn_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.lizard_attn_decode_step.restype = I32
     lib.lizard_attn_workspace_bytes.argtypes = [SP, ctypes.c_int]
     lib.lizard_attn_workspace_bytes.restype = SZ
@@ -192,9 +192,19 @@ def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *,
     return out
 
 
+def decode_workspace(B: int, H: int, d: int, device) -> torch.Tensor:
+    """Workspace for lizard_attn_decode_step at this shape (reusable across steps)."""
+    s = make_shape(B, H, 0, d, 1, 0, 1.0, 1.0, torch.bfloat16)
+    n = int(load().lizard_attn_workspace_bytes(ctypes.byref(s), OP_DECODE))
+    return torch.empty(max(n, 1), device=device, dtype=torch.uint8)
+
+
 def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
-                            window: int, scale: float | None = None, mix: float = 1.0, out=None):
-    """One decode step, in place on (state, ring_k, ring_v, pos); returns o [B,H,d]."""
+                            window: int, scale: float | None = None, mix: float = 1.0, out=None,
+                            workspace=None):
+    """One decode step, in place on (state, ring_k, ring_v, pos); returns o [B,H,d].
+    ``workspace``: optional uint8 device tensor from decode_workspace() (allocated per call
+    when omitted)."""
     lib = load()
     dt, dev = q.dtype, q.device
     for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v)):
@@ -209,9 +219,16 @@ def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, p
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     s = make_shape(B, H, 0, d, window, M, scale, mix, dt)
     o = torch.empty_like(q) if out is None else out
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_DECODE)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if workspace.numel() < ws_bytes:
+        raise ValueError(f"decode workspace needs {ws_bytes} bytes, got {workspace.numel()}")
     _check(lib.lizard_attn_decode_step(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                        _ptr(meta_k), _ptr(meta_v), _ptr(state), _ptr(ring_k),
-                                       _ptr(ring_v), _ptr(pos), _ptr(o), _stream(dev)))
+                                       _ptr(ring_v), _ptr(pos), _ptr(o), _ptr(workspace),
+                                       ws_bytes, _stream(dev)))
     return o
 
 

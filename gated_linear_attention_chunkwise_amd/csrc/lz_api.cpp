@@ -79,7 +79,7 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
   if (check_shape(s, op) != LIZARD_OK) return 0;
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (op == LIZARD_OP_FWD) return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
-  return 0;
+  return lz::decode_workspace_bytes(s->B, s->H, s->d_k);
 }
 
 lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
@@ -146,14 +146,17 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         const void* q, const void* k, const void* v,
                                         const float* g, const void* meta_k, const void* meta_v,
                                         float* state, void* ring_k, void* ring_v, int32_t* pos,
-                                        void* o, hipStream_t stream) {
+                                        void* o, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
   lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
   if (st != LIZARD_OK) return st;
   if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
-  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v});
+  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace});
   if (st != LIZARD_OK) return st;
+  if (workspace == nullptr || workspace_bytes < lz::decode_workspace_bytes(s->B, s->H, s->d_k))
+    return LIZARD_EWORKSPACE;
   lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
-                   s->B, s->H, s->W, s->M, s->scale, s->mix};
+                   reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix};
   return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 

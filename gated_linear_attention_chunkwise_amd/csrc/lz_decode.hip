@@ -8,16 +8,21 @@
 //   ring  [B,H,W,d]            last W keys / values, token n in slot n mod W
 //   pos   [B] int32            tokens consumed so far
 //
-// One workgroup per (b, h).  It issues every load of the step up front (the
-// fp32 state, one 128-key block of the key and value rings, the new token),
-// so the whole 128 KB working set of the head is in flight at once; then
-//   S <- diag(exp g) S + k^T v,  o_gla = q S           (rows reduced across waves)
-//   o_swa = softmax(meta keys, filled ring slots) . values
-// The ring slot of the new token is read from the inputs, never from the
-// ring, so no workgroup reads an entry that is being written.
+// Two launches per step:
+//   decode_state_kernel   one workgroup per (b, h, 32 state rows): streams the
+//                         fp32 state, S <- diag(exp g) S + k^T v, and writes the
+//                         rows' partial q . S to the workspace;
+//   decode_window_kernel  one workgroup per (b, h): softmax over the meta keys
+//                         and the filled ring slots (the new token's slot taken
+//                         from the inputs, never from the ring), values, sum of
+//                         the partials, o = o_gla + mix * o_swa, the ring write
+//                         and the advance of pos.  Every load it needs is issued
+//                         up front (one 128-key block of the key and value rings).
+// Splitting keeps the state stream (two thirds of the step's bytes) in small,
+// register-light workgroups that fill the chip.
 //
-// pos is shared by the H heads of a sequence: every workgroup reads it first;
-// when done, it adds 1 << 24 to it, and the workgroup that brings that
+// pos is shared by the H heads of a sequence: every window workgroup reads it
+// first; when done, it adds 1 << 24 to it, and the workgroup that brings that
 // arrival count to H stores pos + 1 (clearing the count).  Between calls the
 // top byte of pos is zero; pos must stay below 2^24 and H below 256.
 #include "lz_common.hpp"
@@ -29,19 +34,70 @@ namespace {
 constexpr int NTHR = 256;
 constexpr int KB = 128;          // ring keys per register block
 
+constexpr int RB = 32;           // state rows per workgroup of the state kernel
+
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
-  constexpr int VEC = Tr<T>::VEC;
+__global__ __launch_bounds__(NTHR) void decode_state_kernel(DecodeArgs a) {
   constexpr int F4R = D / 4;                  // float4 per state row
-  constexpr int NS = D * F4R / NTHR;          // state float4 per thread
+  constexpr int RPT = RB * F4R / NTHR;        // rows per thread
+  constexpr int RS = NTHR / F4R;              // row stride between a thread's rows
+  static_assert(NTHR % F4R == 0 && RPT * RS == RB, "state thread map");
+  __shared__ float sred[NTHR / 64][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bh = blockIdx.x / (D / RB), rb = blockIdx.x % (D / RB);
+  const int c4 = tid % F4R, r0 = tid / F4R;
+  const size_t vo = (size_t)bh * D;
+  float* S = a.state + ((size_t)bh * D + rb * RB) * D;
+  f32x4 st[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) st[u] = *reinterpret_cast<const f32x4*>(S + (size_t)(r0 + u * RS) * D + 4 * c4);
+  const T* vg = reinterpret_cast<const T*>(a.v) + vo;
+  f32x4 vv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = Tr<T>::to_f(vg[4 * c4 + e]);
+  float qi[RPT], ki[RPT], ai[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int i = rb * RB + r0 + u * RS;
+    qi[u] = Tr<T>::to_f(reinterpret_cast<const T*>(a.q)[vo + i]);
+    ki[u] = Tr<T>::to_f(reinterpret_cast<const T*>(a.k)[vo + i]);
+    ai[u] = __expf(a.g[vo + i]);
+  }
+  f32x4 part = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const f32x4 x = ai[u] * st[u] + ki[u] * vv;
+    *reinterpret_cast<f32x4*>(S + (size_t)(r0 + u * RS) * D + 4 * c4) = x;
+    part += qi[u] * x;
+  }
+  // threads sharing c4 differ in the lane bits above log2(F4R), then across waves
+#pragma unroll
+  for (int m = F4R; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[e] = xor_sum(part[e], m);
+  if (lane < F4R)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sred[wv][4 * lane + e] = part[e];
+  __syncthreads();
+  for (int j = tid; j < D; j += NTHR) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NTHR / 64; ++w2) acc += sred[w2][j];
+    a.o_part[((size_t)bh * (D / RB) + rb) * D + j] = acc;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
+  constexpr int VEC = Tr<T>::VEC;
   constexpr int VPR = D / VEC;                // 16-byte vectors per ring row
   constexpr int RPP = NTHR / VPR;             // ring rows per pass
   constexpr int NR = KB / RPP;                // ring vectors per thread per block
-  static_assert(NTHR % F4R == 0 && NTHR % VPR == 0 && KB % RPP == 0, "thread maps");
+  static_assert(NTHR % VPR == 0 && KB % RPP == 0, "thread maps");
 
   extern __shared__ __align__(16) float slog[];   // [M + W] logits, then probabilities
-  __shared__ float sq[D], sk[D], sv[D], sa[D];
-  __shared__ float sred[NTHR / 64][D];
+  __shared__ float sq[D], sk[D], sv[D], sgla[D];
   __shared__ float sstat[2][NTHR / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -56,16 +112,10 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
   const T* qg = reinterpret_cast<const T*>(a.q) + vo;
   const T* kg = reinterpret_cast<const T*>(a.k) + vo;
   const T* vg = reinterpret_cast<const T*>(a.v) + vo;
-  float* S = a.state + (size_t)bh * D * D;
   const T* rk = reinterpret_cast<const T*>(a.ring_k) + (size_t)bh * W * D;
   const T* rv = reinterpret_cast<const T*>(a.ring_v) + (size_t)bh * W * D;
 
   // ---- issue every load of the step
-  const int c4 = tid % F4R, r0 = tid / F4R;
-  f32x4 st[NS];
-#pragma unroll
-  for (int u = 0; u < NS; ++u)
-    st[u] = *reinterpret_cast<const f32x4*>(S + (size_t)(r0 + u * (NTHR / F4R)) * D + 4 * c4);
   const int cv = tid % VPR, s0 = tid / VPR;
   V16 kr[NR], vr[NR];
 #pragma unroll
@@ -88,31 +138,12 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
     sq[i] = Tr<T>::to_f(qg[i]);
     sk[i] = Tr<T>::to_f(kg[i]);
     sv[i] = Tr<T>::to_f(vg[i]);
-    sa[i] = __expf(a.g[vo + i]);
+    float og = 0.f;
+#pragma unroll
+    for (int p = 0; p < D / RB; ++p) og += a.o_part[((size_t)bh * (D / RB) + p) * D + i];
+    sgla[i] = og;
   }
   __syncthreads();
-
-  // ---- GLA: state update, partial q.S over this thread's rows
-  f32x4 part = f32x4{0, 0, 0, 0};
-  {
-    f32x4 vv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = sv[4 * c4 + e];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int i = r0 + u * (NTHR / F4R);
-      const f32x4 x = sa[i] * st[u] + sk[i] * vv;
-      *reinterpret_cast<f32x4*>(S + (size_t)i * D + 4 * c4) = x;
-      part += sq[i] * x;
-    }
-  }
-#pragma unroll
-  for (int m = F4R; m < 64; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) part[e] = xor_sum(part[e], m);
-  if (lane < F4R)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sred[wv][4 * lane + e] = part[e];
 
   // ---- window logits (log2 units): meta keys, then ring slots (new token from the inputs)
   const float sl2 = a.scale * LOG2E;
@@ -216,20 +247,16 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
   for (int m = VPR; m < 64; m <<= 1)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) ow[e] = xor_sum(ow[e], m);
-  __syncthreads();   // sred holds the GLA partials; reuse a second copy for the window
   __shared__ float swin[NTHR / 64][D];
   if (lane < VPR)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) swin[wv][lane * VEC + e] = ow[e];
   __syncthreads();
   for (int j = tid; j < D; j += NTHR) {
-    float og = 0.f, osw = 0.f;
+    float osw = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < NTHR / 64; ++w2) {
-      og += sred[w2][j];
-      osw += swin[w2][j];
-    }
-    reinterpret_cast<T*>(a.o)[vo + j] = Tr<T>::from_f(og + a.mix * osw / l);
+    for (int w2 = 0; w2 < NTHR / 64; ++w2) osw += swin[w2][j];
+    reinterpret_cast<T*>(a.o)[vo + j] = Tr<T>::from_f(sgla[j] + a.mix * osw / l);
   }
   // ---- ring: the new key and value into slot pos mod W
   {
@@ -251,12 +278,17 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_state_kernel<T, D>), dim3(a.B * a.H * (D / RB)), dim3(NTHR), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const size_t lds = sizeof(float) * (size_t)(a.M + a.W);
-  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(a.B * a.H), dim3(NTHR), lds, st, a);
+  hipLaunchKernelGGL((decode_window_kernel<T, D>), dim3(a.B * a.H), dim3(NTHR), lds, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t decode_workspace_bytes(int B, int H, int D) { return sizeof(float) * (size_t)B * H * (D / RB) * D; }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st) {
   if (dtype == 1) {

@@ -44,6 +44,7 @@ struct DecodeArgs {
   const void* q; const void* k; const void* v; const float* g;
   const void* meta_k; const void* meta_v;
   float* state; void* ring_k; void* ring_v; int32_t* pos; void* o;
+  float* o_part;        // workspace: [B,H,d/32,d] fp32 partial q.S per block of 32 state rows
   int B, H, W, M;
   float scale, mix;
 };
@@ -56,6 +57,8 @@ hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipS
 
 // Workspace bytes needed by launch_fwd when no chunk-state output is given.
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype);
+// Workspace bytes needed by launch_decode.
+size_t decode_workspace_bytes(int B, int H, int D);
 // Workspace bytes needed by launch_bwd.
 size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
 

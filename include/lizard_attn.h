@@ -149,12 +149,17 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
  *          after; H <= 255); incremented
  *   o      [B,H,d_v] written: q S + mix * softmax over M meta keys and the
  *          min(pos+1, W) filled ring slots.
+ *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_DECODE) bytes of
+ *          caller-owned device memory (clobbered): the partial q S of each
+ *          block of 32 state rows, passed between the step's two launches
  * Uses s->B, H, d_k, d_v, W, M, scale, mix, dtype; s->L and s->chunk are ignored. */
 lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         const void* q, const void* k, const void* v,
                                         const float* g, const void* meta_k, const void* meta_v,
                                         float* state, void* ring_k, void* ring_v, int32_t* pos,
-                                        void* o, hipStream_t stream);
+                                        void* o,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
 
 /* Static description of a status code. */
 const char* lizard_attn_status_string(lizard_status_t st);

@@ -98,13 +98,18 @@ def test_bwd_validation(lib):
 
 def test_decode_validation(lib):
     s = shape(L=0)
-    def call(state=GOOD, pos=GOOD, s_=s):
+    def call(state=GOOD, pos=GOOD, s_=s, ws=GOOD, ws_bytes=1 << 40):
         return lib.lizard_attn_decode_step(ctypes.byref(s_), GOOD, GOOD, GOOD, GOOD, GOOD, None,
-                                           state, GOOD, GOOD, pos, GOOD, None)
+                                           state, GOOD, GOOD, pos, GOOD, ws, ws_bytes, None)
     assert call(state=None) == EINVAL
     assert call(pos=None) == EINVAL
     assert call(pos=BAD) == EALIGN
     assert call(s_=shape(W=9000)) == EUNSUPPORTED
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 2)
+    assert need == 1 * 2 * (128 // 32) * 128 * 4       # B*H partial q.S rows per 32 state rows, fp32
+    assert call(ws=None) == EWORKSPACE
+    assert call(ws_bytes=need - 1) == EWORKSPACE
+    assert call(ws=BAD, ws_bytes=need) == EALIGN
 
 
 def test_fwd_needs_workspace_without_chunk_states(lib):
@@ -123,5 +128,4 @@ def test_workspace_query(lib):
     assert lib.lizard_attn_workspace_bytes(None, 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(d_k=96, d_v=96)), 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 0) == 0
-    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 2) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 5) == 0
