@@ -88,3 +88,24 @@ def test_decode_b64_full_size_sampled():
         print("decode_b64", (b, h), f"o {e_o:.2e} state {e_s:.2e}", flush=True)
         assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
     assert (pos.cpu().numpy() == L).all()
+
+
+def test_decode_caller_workspace_matches_default():
+    """A caller-owned workspace reused across steps gives bit-identical results to the
+    per-call one (the workspace carries only values recomputed every step)."""
+    from gated_linear_attention_chunkwise_amd import decode_workspace
+    x = make_small(3, 4, 40, 128, 4, seed=77, bf16=True)
+    T = {n: dev(x[n], torch.bfloat16) for n in ("q", "k", "v")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk = dev(x["meta_k"], torch.bfloat16)
+    runs = []
+    for use_ws in (False, True):
+        state, rk, rv, pos = prefill_handoff(*(T[n][:, :, :30].contiguous() for n in ("q", "k", "v", "g")),
+                                             mk, None, 16, 1 / math.sqrt(128), 1.0)
+        ws = decode_workspace(3, 4, 128, "cuda") if use_ws else None
+        outs = [lizard_attn_decode_step(*(T[n][:, :, t].contiguous() for n in ("q", "k", "v", "g")), mk, None,
+                                        state, rk, rv, pos, window=16, workspace=ws) for t in range(30, 40)]
+        torch.cuda.synchronize()
+        runs.append((torch.stack(outs), state.clone(), rk.clone(), rv.clone(), pos.clone()))
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
