@@ -7,7 +7,8 @@ training workload B=4, H=32, L=8192, d=128, W=128, M=4, chunk 64, bf16
 activations with fp32 gates; inputs are seeded synthetic tensors already in
 HBM.  The constant-memory decode step is measured in the same run on its own
 workload (B=64 sequences after a 4096-token prefill) and reported under
-"decode".  Prints one JSON line.
+"decode"; the 65 536-token prefill, one shot and as continued segments, under
+"prefill".  Prints one JSON line.
 
 Per-kernel times come from HIP events recorded on the stream the kernels
 run on; the backward records them between its kernels through the
@@ -230,12 +231,66 @@ def bench_decode(args, hip, torch, lib):
                          "algorithmic_bytes_per_step": bytes_step}}
 
 
+def bench_prefill(args, hip, torch, lib):
+    """Forward of the 65 536-token prefill, one shot and as continued 8192-token segments
+    (chunked prefill carrying state, key/value ring and position between calls)."""
+    from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device
+    w = WORKLOADS["prefill_64k"]
+    x = make_inputs_device(w, "cuda")
+    S = 8192
+    segs = [{n: x[n][:, :, a:a + S].contiguous() for n in ("q", "k", "v", "g")} for a in range(0, w.L, S)]
+    mk = x["meta_k"]
+    state = torch.zeros(w.B, w.H, w.D, w.D, device="cuda", dtype=torch.float32)
+    ring_k = torch.zeros(w.B, w.H, w.W, w.D, device="cuda", dtype=torch.bfloat16)
+    ring_v = torch.zeros_like(ring_k)
+    pos = torch.zeros(w.B, device="cuda", dtype=torch.int32)
+    ws = lib.continue_workspace(w.B, w.H, S, w.D, torch.bfloat16, "cuda")
+    outs = [torch.empty_like(sg["q"]) for sg in segs]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one_shot():
+        lib.lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], mk, None, window=w.W, scale=w.scale)
+
+    def chunked():
+        state.zero_()
+        pos.zero_()
+        for sg, o in zip(segs, outs):
+            lib.lizard_attn_fwd_continue(sg["q"], sg["k"], sg["v"], sg["g"], mk, None, state, ring_k, ring_v,
+                                         pos, window=w.W, scale=w.scale, out=o, workspace=ws)
+
+    res = {}
+    reps = 5
+    for name, fn in (("one_shot", one_shot), ("chunked", chunked)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(reps):
+            fn()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        res[name] = hip.ms(e0, e1) / reps
+    tokens = w.B * w.L
+    alg = FWD_BYTES * w.B * w.H * w.L
+    gbs = alg / (res["chunked"] * 1e-3) / 1e9
+    return {"workload": f"prefill_64k: B={w.B} H={w.H} L={w.L} d={w.D} W={w.W} M={w.M}, gate input N(2,1); "
+                        f"chunked = {w.L // S} continued segments of {S} tokens",
+            "one_shot": {"ms": round(res["one_shot"], 4), "tokens_per_s": round(tokens / res["one_shot"] * 1e3, 1)},
+            "chunked": {"ms": round(res["chunked"], 4), "tokens_per_s": round(tokens / res["chunked"] * 1e3, 1)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "chunked prefill (sweep + out kernel + ring update per segment)",
+                         "algorithmic_bytes": alg}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
@@ -277,6 +332,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode:
         rec["decode"] = bench_decode(args, hip, torch, lib)
+        torch.cuda.empty_cache()
+    if not args.no_prefill:
+        rec["prefill"] = bench_prefill(args, hip, torch, lib)
     print(json.dumps(rec), flush=True)
 
 

@@ -18,8 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblizard_attn.so")
 
 LIZARD_FP32, LIZARD_BF16 = 0, 1
-OP_FWD, OP_BWD, OP_DECODE = 0, 1, 2
-SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
+OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE = 0, 1, 2, 3
+SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
            "lizard_attn_workspace_bytes", "lizard_attn_status_string")
 
 
@@ -56,6 +56,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_bwd.restype = I32
     lib.lizard_attn_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.lizard_attn_decode_step.restype = I32
+    lib.lizard_attn_fwd_continue.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_fwd_continue.restype = I32
     lib.lizard_attn_workspace_bytes.argtypes = [SP, ctypes.c_int]
     lib.lizard_attn_workspace_bytes.restype = SZ
     lib.lizard_attn_status_string.argtypes = [I32]
@@ -232,6 +234,52 @@ def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, p
     return o
 
 
+def continue_workspace(B: int, H: int, L: int, d: int, dtype, device) -> torch.Tensor:
+    """Workspace for lizard_attn_fwd_continue at this shape (reusable across segments of length <= L)."""
+    s = make_shape(B, H, L, d, 1, 0, 1.0, 1.0, dtype)
+    n = int(load().lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD_CONTINUE))
+    return torch.empty(max(n, 1), device=device, dtype=torch.uint8)
+
+
+def lizard_attn_fwd_continue(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
+                             window: int, scale: float | None = None, mix: float = 1.0,
+                             out=None, workspace=None):
+    """Forward of the next L tokens of every sequence, resuming from the carry
+    (state [B,H,d,d] fp32, ring_k / ring_v [B,H,W,d], pos [B] int32), all updated in
+    place for the next segment or decode step; returns o [B,H,L,d].  ``workspace``:
+    optional uint8 device tensor from continue_workspace() (allocated per call when omitted)."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v)):
+        _need(t, n, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    _need(pos, "pos", torch.int32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, L, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, v, g must share one [B,H,L,d] shape")
+    if state.shape != (B, H, d, d) or ring_k.shape != (B, H, window, d) or ring_v.shape != ring_k.shape \
+            or pos.shape != (B,):
+        raise ValueError("carry shapes must be state [B,H,d,d], ring [B,H,W,d], pos [B]")
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt)
+    o = torch.empty_like(q) if out is None else out
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD_CONTINUE)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if workspace.numel() < ws_bytes:
+        raise ValueError(f"continuation workspace needs {ws_bytes} bytes, got {workspace.numel()}")
+    _check(lib.lizard_attn_fwd_continue(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                        _ptr(meta_k), _ptr(meta_v), _ptr(state), _ptr(ring_k),
+                                        _ptr(ring_v), _ptr(pos), _ptr(o), _ptr(workspace),
+                                        workspace.numel(), _stream(dev)))
+    return o
+
+
 def workspace_bytes(shape: Shape, op: int) -> int:
     return int(load().lizard_attn_workspace_bytes(ctypes.byref(shape), op))
 
@@ -240,3 +288,4 @@ def workspace_bytes(shape: Shape, op: int) -> int:
 fwd = lizard_attn_fwd
 bwd = lizard_attn_bwd
 decode_step = lizard_attn_decode_step
+fwd_continue = lizard_attn_fwd_continue

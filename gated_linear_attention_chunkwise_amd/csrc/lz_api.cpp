@@ -75,10 +75,12 @@ const char* lizard_attn_status_string(lizard_status_t st) {
 }
 
 size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
-  if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE) return 0;
+  if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE && op != LIZARD_OP_FWD_CONTINUE)
+    return 0;
   if (check_shape(s, op) != LIZARD_OK) return 0;
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
-  if (op == LIZARD_OP_FWD) return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
+  if (op == LIZARD_OP_FWD || op == LIZARD_OP_FWD_CONTINUE)
+    return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
   return lz::decode_workspace_bytes(s->B, s->H, s->d_k);
 }
 
@@ -103,8 +105,30 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
     return LIZARD_EWORKSPACE;
   if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
-                workspace, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
+                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
   return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
+                                         const void* q, const void* k, const void* v, const float* g,
+                                         const void* meta_k, const void* meta_v,
+                                         float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                         void* o, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD_CONTINUE);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  if (s->L > 0)
+    st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace});
+  else   // L = 0: nothing to do; the carry is left as it is
+    st = check_ptrs({}, {q, k, v, g, state, ring_k, ring_v, pos, o, meta_k, meta_v, workspace});
+  if (st != LIZARD_OK) return st;
+  if (s->L == 0) return LIZARD_OK;
+  if (workspace == nullptr || workspace_bytes < lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype))
+    return LIZARD_EWORKSPACE;
+  lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, nullptr, nullptr, nullptr, state,
+                workspace, state, pos, ring_k, ring_v, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
+  return lz::launch_fwd_continue(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
 lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,

@@ -86,7 +86,8 @@ struct OutLayout {
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
 };
 
-template <typename T, int D>
+// CONT: the segment continues a sequence (key history in the ring, position offset pos[b]).
+template <typename T, int D, bool CONT>
 __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __restrict__ cstates) {
   using LY = OutLayout<T, D>;
   using SM = ScanMap<D, Tr<T>::VEC, NTHR>;
@@ -149,17 +150,31 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
     for (int e = 0; e < GV; ++e)
       rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
   }
+  // Continuation: the P tokens before this segment are key positions -P .. -1; the last
+  // min(P, W) of them sit in the ring, position s in slot (P + s) mod W.
+  const int P = CONT ? a.pos[bh / a.H] : 0;
+  const int smin = -min(P, W);                  // oldest key position held
+  const T* ringk = reinterpret_cast<const T*>(a.ring_k) + (size_t)bh * W * D;
+  const T* ringv = reinterpret_cast<const T*>(a.ring_v) + (size_t)bh * W * D;
   V16 wk[NVT], wv[NVT];
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int u = 0; u < NVT; ++u) {
       const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
       const int t = kt * C + row;
-      wk[u] = t < L ? ldg16(k + (size_t)t * D + cv * VEC) : zero16();
-      wv[u] = t < L ? ldg16(v + (size_t)t * D + cv * VEC) : zero16();
+      if (!CONT || t >= 0) {
+        wk[u] = t < L ? ldg16(k + (size_t)t * D + cv * VEC) : zero16();
+        wv[u] = t < L ? ldg16(v + (size_t)t * D + cv * VEC) : zero16();
+      } else {
+        const size_t o = (size_t)((P + t) % W) * D + cv * VEC;
+        wk[u] = t >= smin ? ldg16(ringk + o) : zero16();
+        wv[u] = t >= smin ? ldg16(ringv + o) : zero16();
+      }
     }
   };
-  const int kt_lo = max(0, t0 - W + 1) / C;     // oldest key chunk any query of this chunk sees
+  // oldest key chunk any query of this chunk sees (negative: ring history)
+  const int s_lo = CONT ? max(t0 - W + 1, smin) : max(t0 - W + 1, 0);
+  const int kt_lo = s_lo >= 0 ? s_lo / C : -((C - 1 - s_lo) / C);
   load_tile(kt_lo);
   frag qf[KS];
 #pragma unroll
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = s0 + 4 * kg + i;
-        const bool ok = vis[kb] && s <= tq && s > tq - W;
+        const bool ok = vis[kb] && s <= tq && s > tq - W && (!CONT || s >= smin);
         x[kb][i] = ok ? x[kb][i] * sl2 : -INFINITY;
       }
     }
@@ -380,22 +395,70 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   void* states = a.chunk_states != nullptr ? a.chunk_states : a.workspace;
-  const SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.B, a.H, a.L};
+  const SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in, a.B, a.H, a.L};
   if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, false, st)) != hipSuccess) return e;
-  auto kern = out_kernel<T, D>;
-  static bool attr_set = false;   // idempotent; a race only repeats the same call
-  if (!attr_set) {
+  const bool cont = a.pos != nullptr;
+  auto kern = cont ? out_kernel<T, D, true> : out_kernel<T, D, false>;
+  static bool attr_set[2] = {false, false};   // idempotent; a race only repeats the same call
+  if (!attr_set[cont]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[cont] = true;
   }
   const int NC = (a.L + C - 1) / C;
   hipLaunchKernelGGL(kern, dim3(a.B * a.H * NC), dim3(NTHR), LY::bytes, st, a, (const T*)states);
   return hipGetLastError();
 }
 
+// After a continued segment: its last min(L, W) keys / values go to ring slots (P + t) mod W.
+// Runs after the out kernel has read the old ring (stream order).
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void ring_advance_kernel(FwdArgs a) {
+  constexpr int VEC = Tr<T>::VEC;
+  const int bh = blockIdx.x, L = a.L, W = a.W;
+  const int P = a.pos[bh / a.H];
+  const int nw = min(L, W);
+  const size_t hoff = (size_t)bh * L * D;
+  const T* k = reinterpret_cast<const T*>(a.k) + hoff;
+  const T* v = reinterpret_cast<const T*>(a.v) + hoff;
+  T* rk = reinterpret_cast<T*>(a.ring_k) + (size_t)bh * W * D;
+  T* rv = reinterpret_cast<T*>(a.ring_v) + (size_t)bh * W * D;
+  for (int e = threadIdx.x; e < nw * (D / VEC); e += NTHR) {
+    const int j = e / (D / VEC), cv = e % (D / VEC);
+    const int t = L - nw + j;
+    const size_t slot = (size_t)((P + t) % W);
+    stg16(rk + slot * D + cv * VEC, ldg16(k + (size_t)t * D + cv * VEC));
+    stg16(rv + slot * D + cv * VEC, ldg16(v + (size_t)t * D + cv * VEC));
+  }
+}
+
+__global__ void pos_advance_kernel(int32_t* pos, int B, int L) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < B) pos[i] += L;
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_continue_t(const FwdArgs& a, hipStream_t st) {
+  if (a.L == 0) return hipSuccess;   // no tokens: state, ring and pos stay as they are
+  hipError_t e = launch_fwd_t<T, D>(a, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((ring_advance_kernel<T, D>), dim3(a.B * a.H), dim3(NTHR), 0, st, a);
+  hipLaunchKernelGGL(pos_advance_kernel, dim3((a.B + 255) / 256), dim3(256), 0, st, a.pos, a.B, a.L);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t st) {
+  if (dtype == 1) {
+    if (D == 128) return launch_fwd_continue_t<bf16_t, 128>(a, st);
+    if (D == 64) return launch_fwd_continue_t<bf16_t, 64>(a, st);
+  } else {
+    if (D == 64) return launch_fwd_continue_t<float, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
 
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype) {
   return (size_t)B * H * ((L + C - 1) / C) * D * D * (dtype == 1 ? 2 : 4);

@@ -12,6 +12,10 @@ struct FwdArgs {
   const void* meta_k; const void* meta_v;
   void* o; float* lse; void* o_swa; void* chunk_states; float* state_out;
   void* workspace;      // chunk-state buffer (fwd_workspace_bytes) used when chunk_states is NULL
+  // continuation from a carried state (all NULL for a forward from the start of the sequences):
+  // state_in [B,H,d,d] fp32 enters the first chunk; pos [B] counts the tokens before the segment;
+  // ring_k / ring_v [B,H,W,d] hold the keys / values of the last min(pos, W) of them in slots t mod W
+  const float* state_in; int32_t* pos; void* ring_k; void* ring_v;
   int B, H, L, W, M;
   float scale, mix;
 };
@@ -31,12 +35,13 @@ struct BwdArgs {
 
 // One sequential sweep over chunks (lz_sweep.hip).  Forward: a_src = k,
 // b_src = v, out = chunk states [B,H,NC,d,d] (state entering each chunk),
-// state_out = final state (fp32, optional).  Backward: a_src = q, b_src = dO,
+// state_out = final state (fp32, optional), state_in = state entering the
+// first chunk (fp32, optional; may alias state_out).  Backward: a_src = q, b_src = dO,
 // states = the forward's chunk states, out = dS' transposed [B,H,NC,d,d],
 // bnd = boundary rowsums [B,H,NC,d/64,d].
 struct SweepArgs {
   const void* a_src; const void* b_src; const float* g;
-  const void* states; void* out; float* bnd; float* state_out;
+  const void* states; void* out; float* bnd; float* state_out; const float* state_in;
   int B, H, L;
 };
 
@@ -53,6 +58,8 @@ struct DecodeArgs {
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
+// Segment forward resuming from (state_in, ring, pos): launch_fwd, then the ring and pos advance.
+hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st);
 
 // Workspace bytes needed by launch_fwd when no chunk-state output is given.

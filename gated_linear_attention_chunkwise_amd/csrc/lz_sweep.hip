@@ -155,6 +155,14 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   f32x4 acc[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) acc[x] = f32x4{0, 0, 0, 0};
+  if constexpr (!REV) {
+    if (a.state_in != nullptr) {   // continuation: the carried state enters the first chunk
+      const float* si = a.state_in + (size_t)bh * D * D;
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+        acc[ib] = *reinterpret_cast<const f32x4*>(si + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg);
+    }
+  }
 
   auto chunk_of = [&](int n) { return REV ? NC - 1 - n : n; };
   auto process = [&](SwStage<NV>& s, int n) {

@@ -82,7 +82,7 @@ typedef struct {
   int32_t dtype;            /* lizard_dtype_t */
 } lizard_attn_shape_t;
 
-enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2 };
+enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2, LIZARD_OP_FWD_CONTINUE = 3 };
 
 /* Bytes of device workspace that `op` needs for shape `s` (0 when none, or
  * when `s` is invalid).  Pass at least this many bytes to the call. */
@@ -137,6 +137,37 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 float* dmeta_k, float* dmeta_v,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* stage_events);
+
+/* Chunked prefill: the forward of the next L tokens of every sequence, resuming
+ * from the carry that earlier segments or decode steps left.  The state update
+ * of the GLA branch (English page section 2.A, "Gated Linear Attention (GLA)
+ * with Learnable Gating") is continued from the carried state instead of zero,
+ * and the anchor window of
+ * the segment's first tokens reaches back into the carried ring; the result is
+ * the forward of the whole sequence restricted to the new tokens (French page
+ * section 2.A: inference in O(1) memory through an incremental state; English
+ * page section 4, "Efficiency": constant memory at any length).  A segment with
+ * pos = 0 and a zero state is the plain prefill that also writes the hand-off.
+ *   q, k [B,H,L,d_k], v [B,H,L,d_v] (dtype), g [B,H,L,d_k] fp32: the segment
+ *   state   in/out [B,H,d_k,d_v] fp32: state after the pos[b] earlier tokens;
+ *           on return the state after the segment
+ *   ring_k, ring_v in/out [B,H,W,d] (dtype): keys / values of the last
+ *           min(pos[b], W) earlier tokens, token t in slot t mod W (the decode
+ *           layout); on return the segment's last tokens are stored likewise
+ *   pos     in/out, device int32 [B]: tokens before the segment, per sequence
+ *           (sequences of one batch may differ); pos[b] + L < 2^31 (and < 2^24
+ *           with a zero top byte if decode steps follow); incremented by L
+ *   o       [B,H,L,d_v] written
+ *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_FWD_CONTINUE) bytes of
+ *           caller-owned device memory (clobbered): the chunk states
+ * Same size limits as lizard_attn_fwd.  L = 0 launches nothing.  Four launches
+ * on `stream`: state sweep, output kernel, ring update, pos update. */
+lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
+                                         const void* q, const void* k, const void* v, const float* g,
+                                         const void* meta_k, const void* meta_v,
+                                         float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                         void* o, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
 
 /* One constant-memory decode step for every sequence (English page §4,
  * "Efficiency": constant memory at any length; French page §2.A: O(1)

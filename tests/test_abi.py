@@ -30,7 +30,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
-                          "lizard_attn_workspace_bytes", "lizard_attn_status_string"}
+                          "lizard_attn_fwd_continue", "lizard_attn_workspace_bytes",
+                          "lizard_attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(pkg.SYMBOLS) == set(names)
@@ -122,6 +123,29 @@ def test_fwd_needs_workspace_without_chunk_states(lib):
     assert call(None, 0) == EWORKSPACE
     assert call(GOOD, need - 1) == EWORKSPACE
     assert call(BAD, need) == EALIGN
+
+
+def test_fwd_continue_validation(lib):
+    s = shape()
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 3)
+    assert need == lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)   # the chunk states
+    def call(s_=s, state=GOOD, ring_k=GOOD, pos=GOOD, meta_k=GOOD, ws=GOOD, ws_bytes=1 << 40, q=GOOD):
+        return lib.lizard_attn_fwd_continue(ctypes.byref(s_), q, GOOD, GOOD, GOOD, meta_k, None,
+                                            state, ring_k, GOOD, pos, GOOD, ws, ws_bytes, None)
+    assert call(state=None) == EINVAL
+    assert call(ring_k=None) == EINVAL
+    assert call(pos=None) == EINVAL
+    assert call(meta_k=None) == EINVAL
+    assert call(pos=BAD) == EALIGN
+    assert call(s_=shape(W=130)) == EUNSUPPORTED
+    assert call(s_=shape(dtype=0)) == EUNSUPPORTED          # fp32 runs d = 64 only
+    assert call(ws=None) == EWORKSPACE
+    assert call(ws_bytes=need - 1) == EWORKSPACE
+    assert call(ws=BAD, ws_bytes=need) == EALIGN
+    # no new tokens: nothing is touched, NULL tensors allowed
+    z = shape(L=0)
+    assert lib.lizard_attn_fwd_continue(ctypes.byref(z), None, None, None, None, GOOD, None, None, None,
+                                        None, None, None, None, 0, None) == OK
 
 
 def test_workspace_query(lib):
