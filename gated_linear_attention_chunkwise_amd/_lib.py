@@ -144,9 +144,13 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
                            if want_chunk_states else None)
     out["state"] = torch.empty(B, H, d, d, device=dev, dtype=torch.float32) if want_state else None
     ws, ws_bytes = None, 0
-    if not want_chunk_states and L > 0:
+    if L > 0:
+        # segment buffers of the state sweep, plus the chunk states unless they are an output
         ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD)
-        ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+        if want_chunk_states:
+            ws_bytes -= out["chunk_states"].numel() * out["chunk_states"].element_size()
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
     _check(lib.lizard_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(meta_k),
                                _ptr(meta_v), _ptr(out["o"]), _ptr(out["lse"]), _ptr(out["o_swa"]),
                                _ptr(out["chunk_states"]), _ptr(out["state"]), _ptr(ws), ws_bytes,

@@ -99,10 +99,11 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
   else
     st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace});
   if (st != LIZARD_OK) return st;
-  // the chunk states go to chunk_states when given, else to the workspace
-  if (s->L > 0 && chunk_states == nullptr &&
-      (workspace == nullptr || workspace_bytes < lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype)))
-    return LIZARD_EWORKSPACE;
+  // the workspace holds the sweep's segment buffers, and the chunk states unless chunk_states is given
+  const size_t need = s->L == 0 ? 0
+                      : chunk_states != nullptr ? lz::fwd_segment_bytes(s->B, s->H, s->L, s->d_k)
+                                                : lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
                 workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};

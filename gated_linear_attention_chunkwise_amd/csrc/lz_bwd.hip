@@ -698,7 +698,8 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   }
   mark(1);
   {
-    const SweepArgs sw{a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr, a.B, a.H, a.L};
+    const SweepArgs sw{a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr, a.B, a.H, a.L, 1, NC,
+                       nullptr, nullptr, nullptr};
     if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, true, st)) != hipSuccess) return e;
   }
   mark(2);

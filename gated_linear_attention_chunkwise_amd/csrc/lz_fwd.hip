@@ -394,8 +394,20 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  void* states = a.chunk_states != nullptr ? a.chunk_states : a.workspace;
-  const SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in, a.B, a.H, a.L};
+  // workspace: segment buffers of the sweep (when it runs in segments), then the chunk states
+  const int NC = (a.L + C - 1) / C;
+  const int NS = sweep_segments(a.B, a.H, a.L, D);
+  const size_t segb = fwd_segment_bytes(a.B, a.H, a.L, D);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
+  void* states = a.chunk_states != nullptr ? a.chunk_states : ws + segb;
+  SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in, a.B, a.H, a.L,
+               NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr};
+  if (NS > 1) {
+    const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
+    sw.seg_in = reinterpret_cast<float*>(ws);
+    sw.seg_fin = reinterpret_cast<float*>(ws + mat);
+    sw.seg_gtot = reinterpret_cast<float*>(ws + 2 * mat);
+  }
   if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, false, st)) != hipSuccess) return e;
   const bool cont = a.pos != nullptr;
   auto kern = cont ? out_kernel<T, D, true> : out_kernel<T, D, false>;
@@ -406,7 +418,6 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set[cont] = true;
   }
-  const int NC = (a.L + C - 1) / C;
   hipLaunchKernelGGL(kern, dim3(a.B * a.H * NC), dim3(NTHR), LY::bytes, st, a, (const T*)states);
   return hipGetLastError();
 }
@@ -460,8 +471,16 @@ hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+size_t fwd_segment_bytes(int B, int H, int L, int D) {
+  const int NS = sweep_segments(B, H, L, D);
+  if (NS <= 1) return 0;
+  const size_t mat = (size_t)B * H * NS * D * D * sizeof(float);
+  const size_t vec = (size_t)B * H * NS * D * sizeof(float);
+  return 2 * mat + (vec + 255) / 256 * 256;
+}
+
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype) {
-  return (size_t)B * H * ((L + C - 1) / C) * D * D * (dtype == 1 ? 2 : 4);
+  return fwd_segment_bytes(B, H, L, D) + (size_t)B * H * ((L + C - 1) / C) * D * D * (dtype == 1 ? 2 : 4);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st) {

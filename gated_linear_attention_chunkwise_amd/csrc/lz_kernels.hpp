@@ -39,10 +39,20 @@ struct BwdArgs {
 // first chunk (fp32, optional; may alias state_out).  Backward: a_src = q, b_src = dO,
 // states = the forward's chunk states, out = dS' transposed [B,H,NC,d,d],
 // bnd = boundary rowsums [B,H,NC,d/64,d].
+//
+// Sequence segments (forward only): with NS > 1 the chunks are cut into NS
+// segments of SC chunks that sweep in parallel.  A reduce pass carries every
+// segment but the last from a zero state and writes its final state to
+// seg_fin [B*H][NS][d][d] and its gate total to seg_gtot [B*H][NS][d]; a scan
+// over segments writes the state entering each segment to seg_in [B*H][NS][d][d]
+// (the first one is state_in, or zero); the sweep pass then starts segment s
+// from seg_in[s].  NS = 1: one segment, the fields below it are unused.
 struct SweepArgs {
   const void* a_src; const void* b_src; const float* g;
   const void* states; void* out; float* bnd; float* state_out; const float* state_in;
   int B, H, L;
+  int NS, SC;
+  float* seg_in; float* seg_fin; float* seg_gtot;
 };
 
 struct DecodeArgs {
@@ -62,7 +72,11 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st);
 
-// Workspace bytes needed by launch_fwd when no chunk-state output is given.
+// Segments of the forward sweep for this shape (sequence parallelism when B*H is small).
+int sweep_segments(int B, int H, int L, int D);
+// Workspace bytes of the forward: the segment buffers (first), then the chunk states
+// (used when no chunk-state output is given).
+size_t fwd_segment_bytes(int B, int H, int L, int D);
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype);
 // Workspace bytes needed by launch_decode.
 size_t decode_workspace_bytes(int B, int H, int D);

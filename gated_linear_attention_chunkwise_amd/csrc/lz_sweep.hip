@@ -22,6 +22,7 @@
 // chunks, with the inputs of the next two chunks in flight while one is
 // processed (none of them depends on the carried matrix).  The gate prefix
 // runs inside rows of 16 lanes (DPP), with no LDS round trip or barrier.
+#include <algorithm>
 #include <type_traits>
 
 #include "lz_common.hpp"
@@ -69,7 +70,9 @@ struct SwStage {
   V16 rs[NV];    // state tile (backward)
 };
 
-template <typename T, int D, bool REV>
+// REDUCE (forward only): carry a segment from a zero state and keep only its final
+// state and gate total (no chunk states).
+template <typename T, int D, bool REV, bool REDUCE>
 __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   using LY = SwLayout<T>;
   constexpr int NTI = D / TT;                      // tiles per edge
@@ -84,23 +87,29 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
-  // workgroup -> (b*h, i tile, j tile); the tiles of one head share an XCD
+  // workgroup -> (b*h, segment, i tile, j tile); the tiles and segments of one head share an XCD
   const int BH = a.B * a.H;
-  int bh, tile;
+  const int NSL = REDUCE ? a.NS - 1 : a.NS;        // segments launched (the reduce skips the last)
+  const int PER = NTI * NTI * NSL;
+  int bh, tile, seg;
   {
     const int bid = blockIdx.x;
+    int y2;
     if ((BH & 7) == 0) {
       const int x = bid % 8, y = bid / 8;
-      bh = (y / (NTI * NTI)) * 8 + x;
-      tile = y % (NTI * NTI);
+      bh = (y / PER) * 8 + x;
+      y2 = y % PER;
     } else {
-      bh = bid / (NTI * NTI);
-      tile = bid % (NTI * NTI);
+      bh = bid / PER;
+      y2 = bid % PER;
     }
+    seg = y2 / (NTI * NTI);
+    tile = y2 % (NTI * NTI);
   }
   const int it = tile / NTI, jt = tile % NTI;
   const int i0 = it * TT, j0 = jt * TT;
   const int L = a.L, NC = (L + CHUNK - 1) / CHUNK;
+  const int c_begin = seg * a.SC, c_end = min(NC, c_begin + a.SC), NCs = c_end - c_begin;
   const size_t hoff = (size_t)bh * L * D;
   const T* asrc = reinterpret_cast<const T*>(a.a_src) + hoff;
   const T* bsrc = reinterpret_cast<const T*>(a.b_src) + hoff;
@@ -155,19 +164,22 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   f32x4 acc[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) acc[x] = f32x4{0, 0, 0, 0};
-  if constexpr (!REV) {
-    if (a.state_in != nullptr) {   // continuation: the carried state enters the first chunk
-      const float* si = a.state_in + (size_t)bh * D * D;
+  if constexpr (!REV && !REDUCE) {
+    // the state entering this segment: from the segment scan, or the carried state of a
+    // continuation for a single segment
+    const float* si = a.NS > 1 ? a.seg_in + ((size_t)bh * a.NS + seg) * D * D
+                               : (a.state_in != nullptr ? a.state_in + (size_t)bh * D * D : nullptr);
+    if (si != nullptr)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
         acc[ib] = *reinterpret_cast<const f32x4*>(si + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg);
-    }
   }
+  f32x4 gsum = f32x4{0, 0, 0, 0};   // reduce: gate total of this lane's four key columns
 
-  auto chunk_of = [&](int n) { return REV ? NC - 1 - n : n; };
+  auto chunk_of = [&](int n) { return REV ? c_end - 1 - n : c_begin + n; };
   auto process = [&](SwStage<NV>& s, int n) {
     const int c = chunk_of(n);
-    if constexpr (!REV) {
+    if constexpr (!REV && !REDUCE) {
       // state entering chunk c
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
@@ -194,6 +206,7 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
     if (tg == 0)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sDec[16 * w + 4 * cg + e] = __expf(tot[e]);
+    if constexpr (REDUCE) gsum += tot;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       f32x4 x;
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       }
       st4(sA + (4 * tg + u) * LDT + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
     }
-    if (n + 2 < NC) load(s, chunk_of(n + 2));
+    if (n + 2 < NCs) load(s, chunk_of(n + 2));
     __syncthreads();
 
     if constexpr (REV) {
@@ -250,15 +263,24 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
 
   // two chunks of inputs in flight: stage 0 serves even steps, stage 1 odd steps
   SwStage<NV> s0, s1;
-  if (NC > 0) load(s0, chunk_of(0));
-  if (NC > 1) load(s1, chunk_of(1));
-  for (int n = 0; n < NC; n += 2) {
+  if (NCs > 0) load(s0, chunk_of(0));
+  if (NCs > 1) load(s1, chunk_of(1));
+  for (int n = 0; n < NCs; n += 2) {
     process(s0, n);
-    if (n + 1 < NC) process(s1, n + 1);
+    if (n + 1 < NCs) process(s1, n + 1);
   }
   mfma_drain();
-  if constexpr (!REV) {
-    if (a.state_out != nullptr) {
+  if constexpr (REDUCE) {
+    const size_t sb = (size_t)bh * a.NS + seg;
+    float* sf = a.seg_fin + sb * D * D;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+      stg4(sf + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1], acc[ib][2],
+           acc[ib][3]);
+    if (jt == 0 && tg == 0)
+      *reinterpret_cast<f32x4*>(a.seg_gtot + sb * D + acol) = gsum;
+  } else if constexpr (!REV) {
+    if (a.state_out != nullptr && seg == a.NS - 1) {
       float* so = a.state_out + (size_t)bh * D * D;
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
@@ -268,11 +290,32 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   }
 }
 
+// The state entering each segment: seg_in[0] = state_in (or zero),
+// seg_in[s+1] = diag(e^{gtot[s]}) seg_in[s] + seg_fin[s].  One thread per (b*h, i, j).
+__global__ __launch_bounds__(256) void seg_scan_kernel(SweepArgs a, int D) {
+  const int per = D * D / 256;
+  const int bh = blockIdx.x / per, e = (blockIdx.x % per) * 256 + threadIdx.x, i = e / D;
+  const int NS = a.NS;
+  const size_t base = (size_t)bh * NS;
+  float S = a.state_in != nullptr ? a.state_in[(size_t)bh * D * D + e] : 0.f;
+  a.seg_in[base * D * D + e] = S;
+  for (int s = 0; s + 1 < NS; ++s) {
+    S = __expf(a.seg_gtot[(base + s) * D + i]) * S + a.seg_fin[(base + s) * D * D + e];
+    a.seg_in[(base + s + 1) * D * D + e] = S;
+  }
+}
+
 template <typename T, int D, bool REV>
 hipError_t launch_sweep_t(const SweepArgs& a, hipStream_t st) {
   using LY = SwLayout<T>;
-  const int grid = a.B * a.H * (D / TT) * (D / TT);
-  hipLaunchKernelGGL((sweep_kernel<T, D, REV>), dim3(grid), dim3(NTHR_SW), LY::bytes, st, a);
+  const int tiles = (D / TT) * (D / TT);
+  if (!REV && a.NS > 1) {
+    hipLaunchKernelGGL((sweep_kernel<T, D, false, true>), dim3(a.B * a.H * tiles * (a.NS - 1)), dim3(NTHR_SW),
+                       LY::bytes, st, a);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(a.B * a.H * (D * D / 256)), dim3(256), 0, st, a, D);
+  }
+  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false>), dim3(a.B * a.H * tiles * a.NS), dim3(NTHR_SW), LY::bytes,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -288,6 +331,17 @@ hipError_t launch_sweep_dir(const SweepArgs& a, int dtype, int D, hipStream_t st
 }
 
 }  // namespace
+
+int sweep_segments(int B, int H, int L, int D) {
+  const int NC = (L + CHUNK - 1) / CHUNK;
+  const double base = (double)B * H * (D / TT) * (D / TT);   // workgroups of one segment
+  if (base >= 512) return 1;
+  int ns = (int)((2048 + base - 1) / base);                 // aim at ~2048 workgroups
+  ns = std::min(ns, NC / 16);                                // segments of at least 16 chunks
+  if (ns <= 1) return 1;
+  const int sc = (NC + ns - 1) / ns;
+  return (NC + sc - 1) / sc;                                 // no empty segment
+}
 
 hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st) {
   return reverse ? launch_sweep_dir<true>(a, dtype, D, st) : launch_sweep_dir<false>(a, dtype, D, st);

@@ -97,12 +97,18 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op);
  *   o_swa        opt  [B,H,L,d_v] window branch before mixing
  *   chunk_states opt  state entering every chunk (needed by lizard_attn_bwd)
  *   state_out    opt  [B,H,d_k,d_v] fp32 state after the last token (decode hand-off)
- *   workspace         when chunk_states is NULL: at least
- *                     lizard_attn_workspace_bytes(s, LIZARD_OP_FWD) bytes of
- *                     caller-owned device memory (clobbered) that receive the
- *                     chunk states instead; otherwise unused (may be NULL)
- * NULL optional outputs are not written.  Two launches on `stream`: the state
- * sweep over chunks, then one workgroup per (batch, head, chunk). */
+ *   workspace         caller-owned device memory, clobbered: when chunk_states
+ *                     is NULL at least lizard_attn_workspace_bytes(s, LIZARD_OP_FWD)
+ *                     bytes (the chunk states go there); when chunk_states is
+ *                     given, that figure less B*H*ceil(L/chunk)*d_k*d_v*esz
+ *                     bytes (esz = 2 for bf16, 4 for fp32), which is zero unless
+ *                     B*H is small enough for the state sweep to run in
+ *                     sequence segments; NULL when zero bytes are needed
+ * NULL optional outputs are not written.  Launches on `stream`: the state
+ * sweep over chunks (when B*H*(d/64)^2 < 512 and L spans at least 32
+ * chunks, in segments of the sequence: a reduce pass per segment, a scan
+ * over segments, then the sweep of every segment from its entering state),
+ * then one workgroup per (batch, head, chunk). */
 lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
                                 const void* q, const void* k, const void* v, const float* g,
                                 const void* meta_k, const void* meta_v,

@@ -44,6 +44,8 @@ CASES = [
     ("bf16", 128, (130, 3, 64), 1, 129, 16, True, 33),
     ("bf16", 64, (17, 0, 300), 130, 1, 0, False, 100),
     ("fp32", 64, (64, 128, 2), 200, 129, 2, True, 64),
+    # a segment long enough for the state sweep to run in sequence segments from the carried state
+    ("bf16", 64, (100, 0, 3000), 2100, 64, 4, False, 1024),
 ]
 
 
@@ -144,8 +146,9 @@ def test_continue_zero_length_is_noop():
 
 def test_prefill_64k_in_segments_equals_one_shot():
     """The 65 536-token prefill (B=1, H=32, d=128, W=128, M=4) as eight continued
-    8192-token segments: bit-identical outputs and final state to the one-shot forward,
-    which the forward tests pin to the oracle on sampled rows."""
+    8192-token segments against the one-shot forward (which the forward tests pin to the
+    oracle on sampled heads): the same outputs and final state up to the rounding order
+    of the state sums (both sweep the sequence in segments, cut differently)."""
     w = WORKLOADS["prefill_64k"]
     x = make_inputs_device(w, "cuda", with_grad=False)
     ref = lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=w.W, scale=w.scale,
@@ -159,6 +162,8 @@ def test_prefill_64k_in_segments_equals_one_shot():
         o[:, :, a:a + S] = lizard_attn_fwd_continue(seg["q"], seg["k"], seg["v"], seg["g"], x["meta_k"], None,
                                                     *carry, window=w.W, scale=w.scale, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(o, ref["o"])
-    assert torch.equal(carry[0], ref["state"])
+    e_o = rel_l2(host(o), host(ref["o"]))
+    e_s = rel_l2(host(carry[0]), host(ref["state"]))
+    print(f"chunked vs one-shot: o {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= 1e-3 and e_s <= 1e-5
     assert carry[3].cpu().tolist() == [w.L]

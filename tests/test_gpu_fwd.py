@@ -85,6 +85,21 @@ def test_empty_sequence_is_noop():
     assert float(out["state"].abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("dtname,D,L", [("fp32", 64, 2085), ("bf16", 64, 4101), ("bf16", 128, 2048)])
+def test_segmented_state_sweep(dtname, D, L):
+    """Few heads and a long sequence: the state sweep runs in sequence segments (a
+    reduce pass per segment, a scan over segments, then the sweep of every segment from
+    its entering state).  Outputs, the final state and every chunk state match the oracle."""
+    x = make_small(1, 2, L, D, 4, seed=L + D, bf16=(dtname == "bf16"), with_grad=False)
+    out, ref = run_fwd(x, dtname, 128 if D == 128 else 64)
+    check(out, ref, dtname)
+    _, _, states = orc.gla_forward(x["q"], x["k"], x["v"], x["g"], return_states=True)
+    cs = host(out["chunk_states"])
+    assert np.abs(cs[:, :, 0]).max() == 0.0
+    for c in range(1, cs.shape[2]):
+        assert rel_l2(cs[:, :, c], states[64 * c - 1]) <= TOL[dtname], c
+
+
 def _sampled(name, heads):
     w = WORKLOADS[name]
     x = make_inputs(w)
