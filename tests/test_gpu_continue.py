@@ -167,3 +167,37 @@ def test_prefill_64k_in_segments_equals_one_shot():
     print(f"chunked vs one-shot: o {e_o:.2e} state {e_s:.2e}", flush=True)
     assert e_o <= 1e-3 and e_s <= 1e-5
     assert carry[3].cpu().tolist() == [w.L]
+
+
+@pytest.mark.parametrize("dtname,D,W", [("bf16", 128, 128), ("fp32", 64, 16)])
+def test_variable_length_batched_decode(dtname, D, W):
+    """Sequences of one batch at different positions (prefixes of 0, 5, 130 and 64
+    tokens) decode together: each step's output per sequence is the oracle's output of
+    that sequence at its own position."""
+    prefix, steps, M = (0, 5, 130, 64), 12, 4
+    B, H = len(prefix), 2
+    N = max(prefix) + steps
+    x = make_small(B, H, N, D, M, seed=11 * D + W, bf16=(dtname == "bf16"), with_grad=False, with_meta_v=True)
+    dt = tdtype(dtname)
+    scale, mix = 1.0 / math.sqrt(D), 0.5
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk, mv = dev(x["meta_k"], dt), dev(x["meta_v"], dt)
+    parts = [carry_after(T, b, prefix[b], mk, mv, W, scale, mix, 64) for b in range(B)]
+    state, rk, rv, pos = (torch.cat([p[i] for p in parts]).contiguous() for i in range(4))
+    outs = []
+    for j in range(steps):
+        tok = {n: torch.stack([T[n][b, :, prefix[b] + j] for b in range(B)]).contiguous() for n in "qkvg"}
+        outs.append(lizard_attn_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], mk, mv, state, rk, rv, pos,
+                                            window=W, scale=scale, mix=mix))
+    torch.cuda.synchronize()
+    got = torch.stack(outs, 2)
+    for b in range(B):
+        n = prefix[b] + steps
+        ref = orc.hybrid_forward(*(x[k][b:b + 1, :, :n] for k in ("q", "k", "v", "g")), x["meta_k"], x["meta_v"],
+                                 window=W, scale=scale, mix=mix)
+        e_o = rel_l2(host(got[b:b + 1]), ref["o"][:, :, prefix[b]:])
+        e_s = rel_l2(host(state[b:b + 1]), ref["state"])
+        print(dtname, D, W, prefix[b], f"o {e_o:.2e} state {e_s:.2e}", flush=True)
+        assert e_o <= TOL[dtname] and e_s <= TOL[dtname]
+    assert pos.cpu().tolist() == [p + steps for p in prefix]
