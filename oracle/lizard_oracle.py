@@ -16,6 +16,11 @@ Language Models" (gist.science, English / French / Spanish / Chinese):
   Algorithm": the gate is handled in log space), one value per key dimension,
   so Gamma_i = diag(exp g_i).  q and k arrive after any feature map phi.  The
   output reads the updated state: o_t = q_t S_t.
+* Scalar gate -- the Chinese page's ablation (section on ablation experiments)
+  finds a lightweight scalar gate works better than richer gate structures:
+  one log-gate per head and token, g [B,H,L], Gamma_t = exp(g_t) I.  Every
+  function below accepts it wherever it accepts a per-dimension gate; its
+  gradient is the derivative with respect to that one value.
 * Anchor-window branch -- English page §2.A: a local sliding window plus
   learnable meta-memory tokens that act as sinks in the softmax denominator
   without contributing directly to the output value (French page §2.A: the
@@ -48,6 +53,13 @@ def _as(x, dtype):
     return None if x is None else np.asarray(x, dtype=dtype)
 
 
+def _decay(g, ndim_tok):
+    """exp(g) shaped to scale state rows: a per-dimension gate [..., dk] keeps its
+    last axis; a scalar gate (one fewer axis than q) gains a unit axis."""
+    a = np.exp(g)
+    return a if g.ndim == ndim_tok else a[..., None]
+
+
 # --------------------------------------------------------------------------
 # Forward
 # --------------------------------------------------------------------------
@@ -58,14 +70,15 @@ def gla_forward(q, k, v, g, *, dtype=np.float64, initial_state=None, return_stat
     S_{-1} = initial_state (zero by default);
     S_t = diag(exp g_t) S_{t-1} + k_t^T v_t ;  o_t = q_t S_t.
 
-    q, k, g: [B,H,L,dk]; v: [B,H,L,dv].  Returns (o [B,H,L,dv], S_final
-    [B,H,dk,dv]) and, with ``return_states``, the list of every S_t.
+    q, k: [B,H,L,dk]; v: [B,H,L,dv]; g: [B,H,L,dk] or scalar per head [B,H,L].
+    Returns (o [B,H,L,dv], S_final [B,H,dk,dv]) and, with ``return_states``,
+    the list of every S_t.
     """
     q, k, v, g = (_as(a, dtype) for a in (q, k, v, g))
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     S = np.zeros((B, H, dk, dv), dtype) if initial_state is None else np.array(initial_state, dtype)
-    a = np.exp(g)
+    a = _decay(g, q.ndim)
     o = np.empty((B, H, L, dv), dtype)
     states = []
     for t in range(L):
@@ -141,11 +154,13 @@ def gla_backward(q, k, v, g, dO, *, dtype=np.float64):
     Gates: with b_t = sum_{r<=t} g_r, o depends on g only through
     exp(b_t - b_s); dL/db_u = q_u*dq_u - k_u*dk_u, hence
     dg_r = sum_{u>=r} (q_u*dq_u - k_u*dk_u)  (a reverse cumulative sum).
+    A scalar gate [B,H,L] scales every key dimension by the same b_t, so its
+    dL/db_u is the sum of those terms over the key dimensions.
     """
     q, k, v, g, dO = (_as(a, dtype) for a in (q, k, v, g, dO))
     B, H, L, dk_ = q.shape
     dv_ = v.shape[-1]
-    a = np.exp(g)
+    a = _decay(g, q.ndim)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
@@ -160,6 +175,8 @@ def gla_backward(q, k, v, g, dO, *, dtype=np.float64):
         dv[:, :, t, :] = np.matmul(k[:, :, t, None, :], dS)[:, :, 0, :]
         carry = a[:, :, t, :, None] * dS
     contrib = q * dq - k * dk
+    if g.ndim != q.ndim:
+        contrib = contrib.sum(-1)
     dg = np.flip(np.cumsum(np.flip(contrib, axis=2), axis=2), axis=2)
     return dq, dk, dv, dg
 
@@ -251,7 +268,8 @@ class DecodeState:
 
 
 def decode_step(st: DecodeState, q, k, v, g, meta_k, meta_v, *, scale, mix=1.0):
-    """One token for every sequence (q, k, v, g: [B,H,d]); returns o [B,H,dv].
+    """One token for every sequence (q, k, v: [B,H,d]; g: [B,H,d] or scalar [B,H]);
+    returns o [B,H,dv].
 
     S <- diag(exp g) S + k^T v; o_gla = q S; the new key/value goes to slot
     pos mod W; o_swa = softmax attention of q over the M meta keys and the
@@ -262,7 +280,7 @@ def decode_step(st: DecodeState, q, k, v, g, meta_k, meta_v, *, scale, mix=1.0):
     B, H, dk = q.shape
     M = meta_k.shape[1]
     W = st.window
-    st.S = np.exp(g)[..., None] * st.S + k[..., :, None] * v[..., None, :]
+    st.S = _decay(g, q.ndim)[..., None] * st.S + k[..., :, None] * v[..., None, :]
     o_gla = np.matmul(q[:, :, None, :], st.S)[:, :, 0, :]
     o_swa = np.empty_like(o_gla)
     for b in range(B):

@@ -73,6 +73,23 @@ def test_scalar_gate_is_decay_mask_closed_form():
         assert rel(o[:, h], ref) < 1e-12
 
 
+def test_time_varying_scalar_gate_is_decay_mask_closed_form():
+    """One log-gate per head and token (the scalar gate): o = (D * (Q K^T)) V with the
+    decay mask D[t, s] = exp(G_t - G_s) for s <= t, G the running sum of the gates."""
+    x = small(seed=21, L=29)
+    B, H, L, D = x["q"].shape
+    g = np.log(np.random.default_rng(21).uniform(0.3, 1.0, (B, H, L)))
+    o, S = orc.gla_forward(x["q"], x["k"], x["v"], g)
+    G = np.cumsum(g, axis=2)
+    mask = np.tril(np.ones((L, L), bool))
+    Dm = np.where(mask, np.exp(np.where(mask, G[..., :, None] - G[..., None, :], 0.0)), 0.0)
+    ref = (Dm * (x["q"] @ np.swapaxes(x["k"], -1, -2))) @ x["v"]
+    assert rel(o, ref) < 1e-12
+    # final state: sum_s exp(G_{L-1} - G_s) k_s^T v_s
+    w = np.exp(G[..., -1:] - G)
+    assert rel(S, np.einsum("bhs,bhsi,bhsj->bhij", w, x["k"], x["v"])) < 1e-12
+
+
 def test_closed_gate_keeps_only_current_token():
     x = small(seed=4)
     g = np.full_like(x["g"], -np.inf)                # a_t = 0
@@ -255,6 +272,31 @@ def test_backward_matches_central_differences():
         assert rel(gr[key[n]], num) < 1e-7, n
 
 
+def test_scalar_gate_backward_matches_central_differences():
+    x = small(seed=22, B=1, H=2, L=9, D=3, M=2, gate_div=2.0)
+    g = x["g"][..., 0].copy()                          # one gate per head and token
+    W, sc, mix = 4, 0.7, 0.9
+    names = ["q", "k", "v", "g"]
+    base = dict(q=x["q"], k=x["k"], v=x["v"], g=g)
+
+    def loss(d):
+        r = orc.hybrid_forward(d["q"], d["k"], d["v"], d["g"], x["meta_k"], None, window=W, scale=sc, mix=mix)
+        return float((r["o"] * x["dO"]).sum())
+
+    gr = orc.hybrid_backward(x["q"], x["k"], x["v"], g, x["meta_k"], None, x["dO"], window=W, scale=sc, mix=mix)
+    assert gr["dg"].shape == g.shape
+    h = 1e-6
+    for n in names:
+        num = np.zeros_like(base[n])
+        for idx in np.ndindex(base[n].shape):
+            d = {m: base[m].copy() for m in names}
+            d[n][idx] += h
+            fp = loss(d)
+            d[n][idx] -= 2 * h
+            num[idx] = (fp - loss(d)) / (2 * h)
+        assert rel(gr["d" + n], num) < 1e-7, n
+
+
 def test_gate_gradient_invariants():
     x = small(seed=13, L=23, D=5, gate_div=2.0)
     B, H, L, D = x["q"].shape
@@ -291,3 +333,17 @@ def test_decode_after_prefill_equals_full_sequence(L0, steps, W, with_mv):
     assert rel(np.stack(outs, 2), full["o"][:, :, L0:]) < 1e-12
     assert rel(st.S, full["state"]) < 1e-12
     assert (st.pos == L0 + steps).all()
+
+
+def test_scalar_gate_decode_after_prefill_equals_full_sequence():
+    x = small(seed=23, L=30)
+    g = x["g"][..., 0].copy()
+    W, sc, L0 = 6, 0.4, 17
+    full = orc.hybrid_forward(x["q"], x["k"], x["v"], g, x["meta_k"], None, window=W, scale=sc)
+    pre = orc.hybrid_forward(x["q"][:, :, :L0], x["k"][:, :, :L0], x["v"][:, :, :L0], g[:, :, :L0],
+                             x["meta_k"], None, window=W, scale=sc)
+    st = orc.DecodeState.from_prefix(x["k"][:, :, :L0], x["v"][:, :, :L0], pre["state"], W)
+    outs = [orc.decode_step(st, x["q"][:, :, t], x["k"][:, :, t], x["v"][:, :, t], g[:, :, t], x["meta_k"],
+                            None, scale=sc) for t in range(L0, 30)]
+    assert rel(np.stack(outs, 2), full["o"][:, :, L0:]) < 1e-12
+    assert rel(st.S, full["state"]) < 1e-12
