@@ -8,7 +8,8 @@ activations with fp32 gates; inputs are seeded synthetic tensors already in
 HBM.  The constant-memory decode step is measured in the same run on its own
 workload (B=64 sequences after a 4096-token prefill) and reported under
 "decode"; the 65 536-token prefill, one shot and as continued segments, under
-"prefill".  Prints one JSON line.
+"prefill"; the training step with one gate per head and token under
+"scalar_gate".  Prints one JSON line.
 
 Per-kernel times come from HIP events recorded on the stream the kernels
 run on; the backward records them between its kernels through the
@@ -186,6 +187,49 @@ def bench_train(args, hip, torch, lib):
     }, x
 
 
+# compulsory bytes per head-token with one gate per head and token (4 B of gate, 4 B of dg)
+FWD_BYTES_SCALAR = 3 * 2 * 128 + 4 + 2 * 128                  # 1028
+BWD_BYTES_SCALAR = 4 * 2 * 128 + 4 + 3 * 2 * 128 + 4           # 1800
+
+
+def bench_scalar_gate(args, hip, torch, lib, x, w):
+    """The same training step with one log-gate per head and token (g, dg [B,H,L])."""
+    g = x["g"][..., 0].contiguous()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(ev=None):
+        f = lib.lizard_attn_fwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, window=w.W, scale=w.scale,
+                                want_lse=True, want_o_swa=True, want_chunk_states=True)
+        lib.lizard_attn_bwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, x["dO"], f["lse"], f["o_swa"],
+                            f["chunk_states"], window=w.W, scale=w.scale,
+                            stage_events=None if ev is None else [e.value for e in ev])
+
+    for _ in range(3):
+        step()
+    steps = max(1, min(args.steps, 10))
+    evs = [[hip.event() for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for k in range(steps):
+        step(evs[k])
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    chunk_ms = sum(hip.ms(ev[2], ev[3]) for ev in evs) / steps
+    ht = w.B * w.H * w.L
+    step_bytes = (FWD_BYTES_SCALAR + BWD_BYTES_SCALAR) * ht
+    ck = BWD_BYTES_SCALAR * ht / (chunk_ms * 1e-3) / 1e9
+    return {"workload": f"train_8k with one log-gate per head and token: B={w.B} H={w.H} L={w.L} d={w.D} "
+                        f"W={w.W} M={w.M}, forward+backward",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+            "chunk_kernel_ms": round(chunk_ms, 4),
+            "step_hbm_frac": round(step_bytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+            "roofline": {"bound": "hbm", "achieved": round(ck, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ck / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "chunk_kernel",
+                         "algorithmic_bytes_per_launch": BWD_BYTES_SCALAR * ht}}
+
+
 def bench_decode(args, hip, torch, lib):
     from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device
     w = WORKLOADS["decode_b64"]
@@ -291,6 +335,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-scalar-gate", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
@@ -328,6 +373,8 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads)
+    if not args.no_scalar_gate:
+        rec["scalar_gate"] = bench_scalar_gate(args, hip, torch, lib, x, w)
     del x
     torch.cuda.empty_cache()
     if not args.no_decode:

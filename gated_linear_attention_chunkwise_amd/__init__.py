@@ -7,5 +7,6 @@ The compute path is the HIP library liblizard_attn.so (built in-tree by
 from ._lib import (  # noqa: F401
     LizardError, Shape, SYMBOLS, lizard_attn_bwd, lizard_attn_decode_step, lizard_attn_fwd,
     lizard_attn_fwd_continue, load, make_shape, workspace_bytes, decode_workspace, continue_workspace,
-    fwd, bwd, decode_step, fwd_continue, OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE,
+    fwd, bwd, decode_step, fwd_continue, OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE, GATE_PER_DIM,
+    GATE_SCALAR,
 )

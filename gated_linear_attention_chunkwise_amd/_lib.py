@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "liblizard_attn.so")
 
 LIZARD_FP32, LIZARD_BF16 = 0, 1
 OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE = 0, 1, 2, 3
+GATE_PER_DIM, GATE_SCALAR = 0, 1
 SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
            "lizard_attn_workspace_bytes", "lizard_attn_status_string")
 
@@ -27,7 +28,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("W", ctypes.c_int32), ("M", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("mix", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("mix", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32)]
 
 
 class LizardError(RuntimeError):
@@ -101,8 +103,19 @@ def _opt(t, name, dtype, device):
         _need(t, name, dtype, device)
 
 
-def make_shape(B, H, L, d, W, M, scale, mix, dtype, chunk=64) -> Shape:
-    return Shape(B, H, L, d, d, W, M, chunk, float(scale), float(mix), _dtype_code(dtype))
+def make_shape(B, H, L, d, W, M, scale, mix, dtype, chunk=64, gate=GATE_PER_DIM) -> Shape:
+    return Shape(B, H, L, d, d, W, M, chunk, float(scale), float(mix), _dtype_code(dtype), gate)
+
+
+def _gate_mode(g, q) -> int:
+    """Per key dimension when g has q's shape; scalar per head and token when g drops
+    q's last axis."""
+    if tuple(g.shape) == tuple(q.shape):
+        return GATE_PER_DIM
+    if tuple(g.shape) == tuple(q.shape[:-1]):
+        return GATE_SCALAR
+    raise ValueError(f"g must have shape {tuple(q.shape)} (per key dimension) or {tuple(q.shape[:-1])} "
+                     f"(one per head and token), got {tuple(g.shape)}")
 
 
 def _events(evs, n):
@@ -132,10 +145,11 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
     _opt(meta_v, "meta_v", dt, dev)
     B, H, L, d = q.shape
     M = 0 if meta_k is None else meta_k.shape[1]
-    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
-        raise ValueError("q, k, v, g must share one [B,H,L,d] shape")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B,H,L,d] shape")
+    gate = _gate_mode(g, q)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk)
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, gate)
     NC = (L + 63) // 64
     out = {"o": torch.empty_like(q)}
     out["lse"] = torch.empty(B, H, L, device=dev, dtype=torch.float32) if want_lse else None
@@ -180,7 +194,7 @@ def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *,
     B, H, L, d = q.shape
     M = 0 if meta_k is None else meta_k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk)
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, _gate_mode(g, q))
     ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD)
     ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
@@ -223,7 +237,7 @@ def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, p
     B, H, d = q.shape
     M = 0 if meta_k is None else meta_k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    s = make_shape(B, H, 0, d, window, M, scale, mix, dt)
+    s = make_shape(B, H, 0, d, window, M, scale, mix, dt, gate=_gate_mode(g, q))
     o = torch.empty_like(q) if out is None else out
     ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_DECODE)
     if workspace is None:
@@ -262,14 +276,15 @@ def lizard_attn_fwd_continue(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, 
     _opt(meta_k, "meta_k", dt, dev)
     _opt(meta_v, "meta_v", dt, dev)
     B, H, L, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
-        raise ValueError("q, k, v, g must share one [B,H,L,d] shape")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B,H,L,d] shape")
+    gate = _gate_mode(g, q)
     if state.shape != (B, H, d, d) or ring_k.shape != (B, H, window, d) or ring_v.shape != ring_k.shape \
             or pos.shape != (B,):
         raise ValueError("carry shapes must be state [B,H,d,d], ring [B,H,W,d], pos [B]")
     M = 0 if meta_k is None else meta_k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    s = make_shape(B, H, L, d, window, M, scale, mix, dt)
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, gate=gate)
     o = torch.empty_like(q) if out is None else out
     ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD_CONTINUE)
     if workspace is None:

@@ -25,6 +25,7 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
   if (op != LIZARD_OP_DECODE && s->L < 0) return LIZARD_EINVAL;
   if (!isfinite(s->scale) || !isfinite(s->mix)) return LIZARD_EINVAL;
   if (s->dtype != LIZARD_FP32 && s->dtype != LIZARD_BF16) return LIZARD_EUNSUPPORTED;
+  if (s->gate != LIZARD_GATE_PER_DIM && s->gate != LIZARD_GATE_SCALAR) return LIZARD_EUNSUPPORTED;
   if (s->d_k != s->d_v) return LIZARD_EUNSUPPORTED;
   const int d = s->d_k;
   if (d != 64 && d != 128) return LIZARD_EUNSUPPORTED;
@@ -106,7 +107,8 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
-                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
+                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix,
+                s->gate};
   return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
@@ -128,7 +130,7 @@ lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
   if (workspace == nullptr || workspace_bytes < lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype))
     return LIZARD_EWORKSPACE;
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, nullptr, nullptr, nullptr, state,
-                workspace, state, pos, ring_k, ring_v, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix};
+                workspace, state, pos, ring_k, ring_v, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix, s->gate};
   return lz::launch_fwd_continue(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
@@ -161,7 +163,7 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
   a.dmeta_k = s->M > 0 ? dmeta_k : nullptr;
   a.dmeta_v = s->M > 0 ? dmeta_v : nullptr;
   a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
-  a.scale = s->scale; a.mix = s->mix;
+  a.scale = s->scale; a.mix = s->mix; a.gate = s->gate;
   a.workspace = workspace;
   a.stage_events = stage_events;
   return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
@@ -181,7 +183,7 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
   if (workspace == nullptr || workspace_bytes < lz::decode_workspace_bytes(s->B, s->H, s->d_k))
     return LIZARD_EWORKSPACE;
   lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
-                   reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix};
+                   reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate};
   return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 

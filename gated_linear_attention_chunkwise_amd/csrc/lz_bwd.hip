@@ -122,7 +122,8 @@ __device__ __forceinline__ f32x4 lds4(const bf16_t* p) {
 // window seen from the key side), so every score tile is formed once.
 // Accumulators are kept transposed: acc[x][e] belongs to token 16*wb + r of
 // the chunk and column 16*x + 4*kg + e.
-template <typename T, int D>
+// SG: one log-gate per head and token (g, dg [B,H,L]).
+template <typename T, int D, bool SG>
 __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
                                                             const float* __restrict__ wsbnd) {
   using LY = CkLayout<T, D>;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const T* k = reinterpret_cast<const T*>(a.k) + hoff;
   const T* v = reinterpret_cast<const T*>(a.v) + hoff;
   const T* dO = reinterpret_cast<const T*>(a.dO) + hoff;
-  const float* g = a.g + hoff;
+  const float* g = a.g + (SG ? (size_t)bh * L : hoff);
   const T* Sprev = reinterpret_cast<const T*>(a.chunk_states) + ((size_t)bh * NC + c) * D * D;
   const T* dSpT = wsdS + ((size_t)bh * NC + c) * D * D;     // dS' transposed [j][i]
   const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     }
     const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
     GateStrip<T> gs;
-    if (has_strip) gs.load(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
+    if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
     V16 rdo[NVT], rv[NVT];
     fetch_rows(rdo, dO, t0);
     fetch_rows(rv, v, t0);
@@ -419,12 +420,21 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   }
   __syncthreads();
   if (!qrole) {
+    float dsum = 0.f;   // scalar gate: the token's gradient is the sum over the key dimensions
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
       const int i = 16 * x + 4 * kg;
       f32x4 carry = *reinterpret_cast<const f32x4*>(sBnd + i);
       for (int b2 = wb + 1; b2 < 4; ++b2) carry += *reinterpret_cast<const f32x4*>(sTot + b2 * D + i);
-      if (tok < L) *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = db[x] + carry;
+      const f32x4 dgv = db[x] + carry;
+      if constexpr (SG)
+        dsum += (dgv[0] + dgv[1]) + (dgv[2] + dgv[3]);
+      else if (tok < L)
+        *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = dgv;
+    }
+    if constexpr (SG) {
+      dsum = xor_sum(xor_sum(dsum, 16), 32);   // the four column groups of the token
+      if (kg == 0 && tok < L) a.dg[(size_t)bh * L + tok] = dsum;
     }
   }
   // (the first window iteration begins with a barrier: d b, q~, k^, e^b are then dead)
@@ -699,19 +709,19 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   mark(1);
   {
     const SweepArgs sw{a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr, a.B, a.H, a.L, 1, NC,
-                       nullptr, nullptr, nullptr};
+                       nullptr, nullptr, nullptr, a.gate};
     if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, true, st)) != hipSuccess) return e;
   }
   mark(2);
   {
     using LY = CkLayout<T, D>;
-    static bool attr = false;
-    if (!attr) {
-      if ((e = set_lds(chunk_kernel<T, D>, LY::bytes)) != hipSuccess) return e;
-      attr = true;
+    static bool attr[2] = {false, false};   // idempotent; a race only repeats the same call
+    auto kern = a.gate ? chunk_kernel<T, D, true> : chunk_kernel<T, D, false>;
+    if (!attr[a.gate ? 1 : 0]) {
+      if ((e = set_lds(kern, LY::bytes)) != hipSuccess) return e;
+      attr[a.gate ? 1 : 0] = true;
     }
-    hipLaunchKernelGGL((chunk_kernel<T, D>), dim3(BH * NC), dim3(NTHR_CK), LY::bytes, st, a,
-                       (const T*)wsdS, (const float*)wsbnd);
+    hipLaunchKernelGGL(kern, dim3(BH * NC), dim3(NTHR_CK), LY::bytes, st, a, (const T*)wsdS, (const float*)wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(3);

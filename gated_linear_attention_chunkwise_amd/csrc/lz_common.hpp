@@ -325,15 +325,26 @@ struct GateStrip {
   R4 q[4], k[4];   // raw q and k
   f32x4 g[4];      // log-gates, then the inclusive prefix b
 
+  // SG: gp holds one gate per token (broadcast over the columns); else one per (token, column)
+  template <bool SG>
   __device__ __forceinline__ void load(const T* qp, const T* kp, const float* gp, int D, int t0, int L, int col,
                                        int tg) {
+    auto gate4 = [&](int t, size_t o) {
+      if constexpr (SG) {
+        const float x = gp[t];
+        return f32x4{x, x, x, x};
+      } else {
+        return ld4raw(gp + o);
+      }
+    };
     if (t0 + CHUNK <= L) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const size_t o = (size_t)(t0 + 4 * tg + u) * D + col;
+        const int t = t0 + 4 * tg + u;
+        const size_t o = (size_t)t * D + col;
         q[u] = ld4raw(qp + o);
         k[u] = ld4raw(kp + o);
-        g[u] = ld4raw(gp + o);
+        g[u] = gate4(t, o);
       }
     } else {
 #pragma unroll
@@ -342,7 +353,7 @@ struct GateStrip {
         const size_t o = (size_t)t * D + col;
         q[u] = t < L ? ld4raw(qp + o) : R4{};
         k[u] = t < L ? ld4raw(kp + o) : R4{};
-        g[u] = t < L ? ld4raw(gp + o) : f32x4{0, 0, 0, 0};
+        g[u] = t < L ? gate4(t, o) : f32x4{0, 0, 0, 0};
       }
     }
   }

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(NTHR) void decode_state_kernel(DecodeArgs a) {
     const int i = rb * RB + r0 + u * RS;
     qi[u] = Tr<T>::to_f(reinterpret_cast<const T*>(a.q)[vo + i]);
     ki[u] = Tr<T>::to_f(reinterpret_cast<const T*>(a.k)[vo + i]);
-    ai[u] = __expf(a.g[vo + i]);
+    ai[u] = __expf(a.gate ? a.g[bh] : a.g[vo + i]);   // scalar gate: one per head
   }
   f32x4 part = f32x4{0, 0, 0, 0};
 #pragma unroll

@@ -87,7 +87,8 @@ struct OutLayout {
 };
 
 // CONT: the segment continues a sequence (key history in the ring, position offset pos[b]).
-template <typename T, int D, bool CONT>
+// SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
+template <typename T, int D, bool CONT, bool SG>
 __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __restrict__ cstates) {
   using LY = OutLayout<T, D>;
   using SM = ScanMap<D, Tr<T>::VEC, NTHR>;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   const T* q = reinterpret_cast<const T*>(a.q) + hoff;
   const T* k = reinterpret_cast<const T*>(a.k) + hoff;
   const T* v = reinterpret_cast<const T*>(a.v) + hoff;
-  const float* g = a.g + hoff;
+  const float* g = a.g + (SG ? (size_t)bh * L : hoff);
   const T* Sc = cstates + ((size_t)bh * NC + c) * D * D;
   const float sl2 = a.scale * LOG2E;
   const int t0 = c * C;
@@ -148,7 +149,12 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
     rk[u] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
 #pragma unroll
     for (int e = 0; e < GV; ++e)
-      rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
+      if constexpr (SG) {
+        const float x = ok ? g[t] : 0.f;
+        rg[u][e] = f32x4{x, x, x, x};
+      } else {
+        rg[u][e] = ok ? *reinterpret_cast<const f32x4*>(g + (size_t)t * D + cg * VEC + 4 * e) : f32x4{0, 0, 0, 0};
+      }
   }
   // Continuation: the P tokens before this segment are key positions -P .. -1; the last
   // min(P, W) of them sit in the ring, position s in slot (P + s) mod W.
@@ -401,7 +407,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
   void* states = a.chunk_states != nullptr ? a.chunk_states : ws + segb;
   SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in, a.B, a.H, a.L,
-               NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr};
+               NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate};
   if (NS > 1) {
     const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
     sw.seg_in = reinterpret_cast<float*>(ws);
@@ -409,14 +415,16 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     sw.seg_gtot = reinterpret_cast<float*>(ws + 2 * mat);
   }
   if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, false, st)) != hipSuccess) return e;
-  const bool cont = a.pos != nullptr;
-  auto kern = cont ? out_kernel<T, D, true> : out_kernel<T, D, false>;
-  static bool attr_set[2] = {false, false};   // idempotent; a race only repeats the same call
-  if (!attr_set[cont]) {
+  const int variant = (a.pos != nullptr ? 1 : 0) + (a.gate ? 2 : 0);
+  decltype(&out_kernel<T, D, false, false>) kern =
+      variant == 0 ? out_kernel<T, D, false, false> : variant == 1 ? out_kernel<T, D, true, false>
+      : variant == 2 ? out_kernel<T, D, false, true> : out_kernel<T, D, true, true>;
+  static bool attr_set[4] = {false, false, false, false};   // idempotent; a race only repeats the same call
+  if (!attr_set[variant]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::bytes);
     if (e != hipSuccess) return e;
-    attr_set[cont] = true;
+    attr_set[variant] = true;
   }
   hipLaunchKernelGGL(kern, dim3(a.B * a.H * NC), dim3(NTHR), LY::bytes, st, a, (const T*)states);
   return hipGetLastError();

@@ -18,6 +18,7 @@ struct FwdArgs {
   const float* state_in; int32_t* pos; void* ring_k; void* ring_v;
   int B, H, L, W, M;
   float scale, mix;
+  int gate;             // 0: g [B,H,L,d] per key dimension; 1: g [B,H,L] one per head and token
 };
 
 struct BwdArgs {
@@ -31,6 +32,7 @@ struct BwdArgs {
   hipEvent_t* stage_events;   // optional: 5 events recorded around the 4 kernels
   int B, H, L, W, M;
   float scale, mix;
+  int gate;             // as in FwdArgs; dg has the shape of g
 };
 
 // One sequential sweep over chunks (lz_sweep.hip).  Forward: a_src = k,
@@ -53,6 +55,7 @@ struct SweepArgs {
   int B, H, L;
   int NS, SC;
   float* seg_in; float* seg_fin; float* seg_gtot;
+  int gate;             // as in FwdArgs
 };
 
 struct DecodeArgs {
@@ -62,6 +65,7 @@ struct DecodeArgs {
   float* o_part;        // workspace: [B,H,d/32,d] fp32 partial q.S per block of 32 state rows
   int B, H, W, M;
   float scale, mix;
+  int gate;             // 0: g [B,H,d]; 1: g [B,H]
 };
 
 // Each returns hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.

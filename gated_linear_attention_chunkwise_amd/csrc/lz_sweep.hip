@@ -72,7 +72,8 @@ struct SwStage {
 
 // REDUCE (forward only): carry a segment from a zero state and keep only its final
 // state and gate total (no chunk states).
-template <typename T, int D, bool REV, bool REDUCE>
+// SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
+template <typename T, int D, bool REV, bool REDUCE, bool SG>
 __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   using LY = SwLayout<T>;
   constexpr int NTI = D / TT;                      // tiles per edge
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   const size_t hoff = (size_t)bh * L * D;
   const T* asrc = reinterpret_cast<const T*>(a.a_src) + hoff;
   const T* bsrc = reinterpret_cast<const T*>(a.b_src) + hoff;
-  const float* g = a.g + hoff;
+  const float* g = a.g + (SG ? (size_t)bh * L : hoff);
   const T* states = reinterpret_cast<const T*>(a.states) + (size_t)bh * NC * D * D;
   T* out = reinterpret_cast<T*>(a.out) + (size_t)bh * NC * D * D;
 
@@ -129,7 +130,12 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       for (int u = 0; u < 4; ++u) {
         const size_t o = (size_t)(t0 + 4 * tg + u) * D + acol;
         s.ra[u] = ld4f(asrc + o);
-        s.rg[u] = ld4f(g + o);
+        if constexpr (SG) {
+          const float x = g[t0 + 4 * tg + u];
+          s.rg[u] = f32x4{x, x, x, x};
+        } else {
+          s.rg[u] = ld4f(g + o);
+        }
       }
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
@@ -142,7 +148,12 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
         const int t = t0 + 4 * tg + u;
         const size_t o = (size_t)t * D + acol;
         s.ra[u] = t < L ? ld4f(asrc + o) : f32x4{0, 0, 0, 0};
-        s.rg[u] = t < L ? ld4f(g + o) : f32x4{0, 0, 0, 0};
+        if constexpr (SG) {
+          const float x = t < L ? g[t] : 0.f;
+          s.rg[u] = f32x4{x, x, x, x};
+        } else {
+          s.rg[u] = t < L ? ld4f(g + o) : f32x4{0, 0, 0, 0};
+        }
       }
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
@@ -305,18 +316,23 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(SweepArgs a, int D) {
   }
 }
 
-template <typename T, int D, bool REV>
-hipError_t launch_sweep_t(const SweepArgs& a, hipStream_t st) {
+template <typename T, int D, bool REV, bool SG>
+hipError_t launch_sweep_g(const SweepArgs& a, hipStream_t st) {
   using LY = SwLayout<T>;
   const int tiles = (D / TT) * (D / TT);
   if (!REV && a.NS > 1) {
-    hipLaunchKernelGGL((sweep_kernel<T, D, false, true>), dim3(a.B * a.H * tiles * (a.NS - 1)), dim3(NTHR_SW),
-                       LY::bytes, st, a);
+    hipLaunchKernelGGL((sweep_kernel<T, D, false, true, SG>), dim3(a.B * a.H * tiles * (a.NS - 1)),
+                       dim3(NTHR_SW), LY::bytes, st, a);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(a.B * a.H * (D * D / 256)), dim3(256), 0, st, a, D);
   }
-  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false>), dim3(a.B * a.H * tiles * a.NS), dim3(NTHR_SW), LY::bytes,
-                     st, a);
+  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false, SG>), dim3(a.B * a.H * tiles * a.NS), dim3(NTHR_SW),
+                     LY::bytes, st, a);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool REV>
+hipError_t launch_sweep_t(const SweepArgs& a, hipStream_t st) {
+  return a.gate ? launch_sweep_g<T, D, REV, true>(a, st) : launch_sweep_g<T, D, REV, false>(a, st);
 }
 
 template <bool REV>

@@ -71,6 +71,13 @@ typedef enum {
 
 typedef enum { LIZARD_FP32 = 0, LIZARD_BF16 = 1 } lizard_dtype_t;
 
+/* Gate granularity.  PER_DIM: one log-gate per key dimension, g and dg
+ * [B,H,L,d_k] (decode g [B,H,d_k]).  SCALAR: one log-gate per head and token,
+ * g and dg [B,H,L] (decode g [B,H]): Gamma_t = exp(g_t) I, the lightweight
+ * gate the Chinese page's ablation section prefers over richer gate
+ * structures; it cuts the gate traffic from 4*d_k to 4 bytes per head-token. */
+typedef enum { LIZARD_GATE_PER_DIM = 0, LIZARD_GATE_SCALAR = 1 } lizard_gate_t;
+
 typedef struct {
   int32_t B, H, L;          /* batch, heads, sequence length (L unused by decode) */
   int32_t d_k, d_v;         /* head dims; must be equal */
@@ -80,6 +87,7 @@ typedef struct {
   float scale;              /* softmax logit scale, normally 1/sqrt(d_k) */
   float mix;                /* alpha in o = o_gla + alpha * o_swa */
   int32_t dtype;            /* lizard_dtype_t */
+  int32_t gate;             /* lizard_gate_t (0, the zero-initialised default, is per key dimension) */
 } lizard_attn_shape_t;
 
 enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2, LIZARD_OP_FWD_CONTINUE = 3 };

@@ -45,7 +45,7 @@ def test_status_strings(lib):
 
 def shape(**kw):
     base = dict(B=1, H=2, L=128, d_k=128, d_v=128, W=128, M=4, chunk=64, scale=0.088, mix=1.0,
-                dtype=1)
+                dtype=1, gate=0)
     base.update(kw)
     return Shape(*(base[f] for f, _ in Shape._fields_))
 
@@ -62,7 +62,7 @@ def fwd(lib, s, q=GOOD, meta_k=GOOD, meta_v=None, o=GOOD, lse=None):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d_k=96, d_v=96), EUNSUPPORTED), (dict(d_k=64, d_v=128), EUNSUPPORTED),
-    (dict(dtype=7), EUNSUPPORTED), (dict(dtype=0, d_k=128, d_v=128), EUNSUPPORTED),
+    (dict(dtype=7), EUNSUPPORTED), (dict(dtype=0, d_k=128, d_v=128), EUNSUPPORTED), (dict(gate=2), EUNSUPPORTED),
     (dict(M=17), EUNSUPPORTED), (dict(W=130), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED),
     (dict(B=0), EINVAL), (dict(L=-1), EINVAL), (dict(W=0), EINVAL), (dict(M=-1), EINVAL),
     (dict(scale=float("nan")), EINVAL),

@@ -1,0 +1,118 @@
+"""GPU parity of the scalar-gate variant (one log-gate per head and token, g and dg
+[B,H,L]) against the CPU oracle: forward, backward, the segmented state sweep,
+chunked prefill and decode."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lizard_oracle as orc
+from gated_linear_attention_chunkwise_amd import (lizard_attn_bwd, lizard_attn_decode_step, lizard_attn_fwd,
+                                                  lizard_attn_fwd_continue)
+from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device, make_small
+from helpers import TOL, dev, host, rel_l2, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def scalar_inputs(B, H, L, D, M, seed, dtname, with_mv=False, x_mean=0.0):
+    """The per-dimension recipe with the gate of key column 0 as the head's gate."""
+    x = make_small(B, H, L, D, M, seed=seed, bf16=(dtname == "bf16"), with_meta_v=with_mv, x_mean=x_mean)
+    x["g"] = np.ascontiguousarray(x["g"][..., 0])
+    return x
+
+
+def upload(x, dtname):
+    dt = tdtype(dtname)
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v", "dO")}
+    T["g"] = dev(x["g"], torch.float32)
+    M = x["meta_k"].shape[1]
+    T["mk"] = dev(x["meta_k"], dt) if M > 0 else None
+    T["mv"] = dev(x["meta_v"], dt) if (x.get("meta_v") is not None and M > 0) else None
+    return T
+
+
+CASES = [("fp32", 64, 190, 64, 4, True), ("bf16", 128, 200, 128, 4, False), ("bf16", 64, 65, 1, 0, False),
+         ("bf16", 128, 1, 129, 16, True), ("bf16", 64, 2085, 100, 2, False)]
+
+
+@pytest.mark.parametrize("dtname,D,L,W,M,with_mv", CASES)
+def test_scalar_gate_forward_backward(dtname, D, L, W, M, with_mv):
+    x = scalar_inputs(2, 2, L, D, M, seed=L + W + D, dtname=dtname, with_mv=with_mv)
+    T = upload(x, dtname)
+    scale, mix = 1.0 / math.sqrt(D), 0.8
+    f = lizard_attn_fwd(T["q"], T["k"], T["v"], T["g"], T["mk"], T["mv"], window=W, scale=scale, mix=mix,
+                        want_lse=True, want_o_swa=True, want_chunk_states=True, want_state=True)
+    b = lizard_attn_bwd(T["q"], T["k"], T["v"], T["g"], T["mk"], T["mv"], T["dO"], f["lse"], f["o_swa"],
+                        f["chunk_states"], window=W, scale=scale, mix=mix)
+    torch.cuda.synchronize()
+    mv = x.get("meta_v") if M > 0 else None
+    ref = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], mv, window=W, scale=scale, mix=mix)
+    gref = orc.hybrid_backward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], mv, x["dO"], window=W, scale=scale,
+                               mix=mix)
+    assert b["dg"].shape == (2, 2, L)
+    errs = {n: rel_l2(host(f[n]), ref[n]) for n in ("o", "o_swa", "lse", "state")}
+    errs.update({n: rel_l2(host(b[n]), gref[n]) for n in ("dq", "dk", "dv", "dg")})
+    if M > 0:
+        errs["dmeta_k"] = rel_l2(host(b["dmeta_k"]), gref["dmeta_k"])
+    if mv is not None:
+        errs["dmeta_v"] = rel_l2(host(b["dmeta_v"]), gref["dmeta_v"])
+    print(dtname, D, L, W, M, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[dtname], (n, e)
+    # the states entering each chunk
+    _, _, states = orc.gla_forward(x["q"], x["k"], x["v"], x["g"], return_states=True)
+    cs = host(f["chunk_states"])
+    for c in range(1, cs.shape[2]):
+        assert rel_l2(cs[:, :, c], states[64 * c - 1]) <= TOL[dtname], c
+
+
+def test_scalar_gate_chunked_prefill_then_decode():
+    D, W, M, B, H, N = 128, 128, 4, 2, 2, 300
+    x = scalar_inputs(B, H, N, D, M, seed=77, dtname="bf16")
+    T = upload(x, "bf16")
+    carry = (torch.zeros(B, H, D, D, device="cuda"), torch.zeros(B, H, W, D, device="cuda", dtype=torch.bfloat16),
+             torch.zeros(B, H, W, D, device="cuda", dtype=torch.bfloat16),
+             torch.zeros(B, device="cuda", dtype=torch.int32))
+    outs = []
+    for a, e in ((0, 150), (150, 270)):
+        outs.append(lizard_attn_fwd_continue(T["q"][:, :, a:e].contiguous(), T["k"][:, :, a:e].contiguous(),
+                                             T["v"][:, :, a:e].contiguous(), T["g"][:, :, a:e].contiguous(),
+                                             T["mk"], None, *carry, window=W))
+    for t in range(270, N):
+        outs.append(lizard_attn_decode_step(T["q"][:, :, t].contiguous(), T["k"][:, :, t].contiguous(),
+                                            T["v"][:, :, t].contiguous(), T["g"][:, :, t].contiguous(),
+                                            T["mk"], None, *carry, window=W).unsqueeze(2))
+    torch.cuda.synchronize()
+    ref = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=W,
+                             scale=1.0 / math.sqrt(D))
+    e_o = rel_l2(host(torch.cat(outs, 2)), ref["o"])
+    e_s = rel_l2(host(carry[0]), ref["state"])
+    print(f"o {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+
+
+def test_scalar_gate_train_8k_full_size_sampled():
+    """B=4, H=32, L=8192, d=128 with one gate per head and token; oracle on a sampled head."""
+    w = WORKLOADS["train_8k"]
+    x = make_inputs_device(w, "cuda", with_grad=True)
+    g = x["g"][..., 0].contiguous()
+    f = lizard_attn_fwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, window=w.W, scale=w.scale,
+                        want_lse=True, want_o_swa=True, want_chunk_states=True, want_state=True)
+    b = lizard_attn_bwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, x["dO"], f["lse"], f["o_swa"],
+                        f["chunk_states"], window=w.W, scale=w.scale)
+    torch.cuda.synchronize()
+    h = 17
+    hs = {n: x[n][:, h:h + 1].float().cpu().numpy() for n in ("q", "k", "v", "dO")}
+    gh = g[:, h:h + 1].cpu().numpy()
+    mk = x["meta_k"][h:h + 1].float().cpu().numpy()
+    ref = orc.hybrid_forward(hs["q"], hs["k"], hs["v"], gh, mk, None, window=w.W, scale=w.scale)
+    gref = orc.hybrid_backward(hs["q"], hs["k"], hs["v"], gh, mk, None, hs["dO"], window=w.W, scale=w.scale)
+    errs = {"o": rel_l2(host(f["o"][:, h:h + 1]), ref["o"]), "state": rel_l2(host(f["state"][:, h:h + 1]),
+                                                                            ref["state"])}
+    errs.update({n: rel_l2(host(b[n][:, h:h + 1]), gref[n]) for n in ("dq", "dk", "dv", "dg")})
+    errs["dmeta_k"] = rel_l2(host(b["dmeta_k"][h:h + 1]), gref["dmeta_k"])
+    print("train_8k scalar gate head", h, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)
