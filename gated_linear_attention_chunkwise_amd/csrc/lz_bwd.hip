@@ -189,32 +189,55 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   const int tok = t0 + u;
 
 
-  // Register image of a [C][D] chunk tile: NVT 16-byte vectors per thread.
+  // Register image of a [C][D] chunk tile: NVT 16-byte vectors per thread.  Rows past the
+  // sequence end are loaded clamped (no branch around the load) and zeroed when stored.
   constexpr int NVT = C * (D / VEC) / NTHR_CK;
   auto fetch_rows = [&](V16 (&dst)[NVT], const T* src, int row0) {
 #pragma unroll
     for (int e = 0; e < NVT; ++e) {
       const int idx = tid + e * NTHR_CK, t = idx / (D / VEC), cv = idx % (D / VEC);
-      dst[e] = (row0 + t < L) ? ldg16(src + (size_t)(row0 + t) * D + cv * VEC) : zero16();
+      dst[e] = ldg16(src + (size_t)min(row0 + t, L - 1) * D + cv * VEC);
     }
   };
-  auto put_rows = [&](T* dst, const V16 (&src)[NVT]) {
+  auto put_rows = [&](T* dst, const V16 (&src)[NVT], int row0) {
 #pragma unroll
     for (int e = 0; e < NVT; ++e) {
       const int idx = tid + e * NTHR_CK, t = idx / (D / VEC), cv = idx % (D / VEC);
-      *reinterpret_cast<V16*>(dst + t * LDQ + cv * VEC) = src[e];
+      *reinterpret_cast<V16*>(dst + t * LDQ + cv * VEC) = row0 + t < L ? src[e] : zero16();
     }
   };
 
-  // boundary term of dg for this thread's column (consumed after the GLA phase)
-  float bnd = 0.f;
-  if (c + 1 < NC)
+  // S_prev rows of the dq waves' inter-chunk product, two K steps ahead: the first two go out
+  // last among the staging loads (so nothing in the staging phase waits for them) and arrive
+  // during it; each step of the product then issues the rows of the step two ahead.
+  auto load_s = [&](frag (&dst)[NB], int ks) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bnd += wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + tid % D];
+    for (int x = 0; x < NB; ++x) dst[x] = ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 32 * ks + 8 * kg);
+  };
+  frag fs0[NB], fs1[NB];
 
   // ---------------------------------------------------------------- staging
-  // every load of the staging phase is issued before anything waits on one
+  // Every load of the staging phase is issued before anything waits on one: no load sits
+  // in a branch with its use, so the compiler places no wait between them (each such wait
+  // would cost a full memory round trip before the next loads go out).
   {
+    // lse / delta of this chunk and the next two (rows clamped into the sequence)
+    const int lrow = min(t0 + min(tid, 3 * C - 1), L - 1);
+    const float rls = a.lse[(size_t)bh * L + lrow], rdl = a.ws_delta[(size_t)bh * L + lrow];
+    // boundary term of dg for this thread's column, per d_v tile (the sweep writes zero for
+    // the last chunk); summed when stored
+    float bndp[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bndp[j] = wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + tid % D];
+    // meta keys, raw, rows clamped (any valid address when there are none)
+    constexpr int NMK = D * 16 / NTHR_CK;          // meta-key elements per thread
+    const T* mkp = M > 0 ? mk : q;
+    T rmk[NMK];
+#pragma unroll
+    for (int e = 0; e < NMK; ++e) {
+      const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
+      rmk[e] = mkp[(size_t)min(m, max(M - 1, 0)) * D + d];
+    }
     constexpr int NVS = D * (D / VEC) / NTHR_CK;   // dS' vectors per thread
     V16 rds[NVS];
 #pragma unroll
@@ -222,36 +245,34 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
       rds[e] = ldg16(dSpT + (size_t)j * D + cv * VEC);
     }
-    const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
-    GateStrip<T> gs;
-    if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
     V16 rdo[NVT], rv[NVT];
     fetch_rows(rdo, dO, t0);
     fetch_rows(rv, v, t0);
-    constexpr int NMK = D * 16 / NTHR_CK;          // meta-key elements per thread
-    float rmk[NMK];
+    const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
+    GateStrip<T> gs;
+    if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
+    if (qrole) {
+      load_s(fs0, 0);
+      if (KS > 1) load_s(fs1, 1);
+    }
+    put_rows(sdO, rdo, t0);
+    put_rows(sV, rv, t0);
 #pragma unroll
     for (int e = 0; e < NMK; ++e) {
       const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
-      rmk[e] = m < M ? Tr<T>::to_f(mk[(size_t)m * D + d]) : 0.f;
-    }
-    float rls = 0.f, rdl = 0.f;                    // lse / delta of this chunk and the next two
-    if (tid < 3 * C && t0 + tid < L) {
-      rls = a.lse[(size_t)bh * L + t0 + tid] * LOG2E;
-      rdl = a.ws_delta[(size_t)bh * L + t0 + tid];
-    }
-    put_rows(sdO, rdo);
-    put_rows(sV, rv);
-#pragma unroll
-    for (int e = 0; e < NMK; ++e) {
-      const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
-      put_elem(sMkT + d * LY::LDM + m, rmk[e]);
+      put_elem(sMkT + d * LY::LDM + m, m < M ? Tr<T>::to_f(rmk[e]) : 0.f);
     }
     if (tid < 3 * C) {
-      sLse[tid] = rls;
-      sDel[tid] = rdl;
+      const bool ok = t0 + tid < L;
+      sLse[tid] = ok ? rls * LOG2E : 0.f;
+      sDel[tid] = ok ? rdl : 0.f;
     }
-    if (tid < D) sBnd[tid] = bnd;
+    if (tid < D) {
+      float bnd = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bnd += bndp[j];
+      sBnd[tid] = bnd;
+    }
     // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b
     if (has_strip) gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
 #pragma unroll
@@ -268,10 +289,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
   for (int x = 0; x < NB; ++x) { acc0[x] = f32x4{0, 0, 0, 0}; acc1[x] = acc0[x]; }
   if (qrole) {
-    // S_prev rows for the first K step of the inter-chunk product: issued before the intra-chunk work
-    frag fs[NB];
-#pragma unroll
-    for (int x = 0; x < NB; ++x) fs[x] = ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 8 * kg);
+    // (the S_prev rows of the first two K steps were issued with the staging loads)
     frag fo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) fo[ks] = ld_frag(sdO, LDQ, u, 32 * ks + 8 * kg);
@@ -299,18 +317,13 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
         for (int x = 0; x < NB; ++x)
           mma32(acc0[x], ld_frag_tr(sKh, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
       }
-    // dq~ += dO S_prev^T, the next K step's rows loading while one is used
+    // dq~ += dO S_prev^T
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      frag fn[NB];
-      if (ks + 1 < KS)
+      frag (&cur)[NB] = (ks & 1) ? fs1 : fs0;
 #pragma unroll
-        for (int x = 0; x < NB; ++x) fn[x] = ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 32 * (ks + 1) + 8 * kg);
-#pragma unroll
-      for (int x = 0; x < NB; ++x) mma32(acc0[x], fs[x], fo[ks]);
-      if (ks + 1 < KS)
-#pragma unroll
-        for (int x = 0; x < NB; ++x) fs[x] = fn[x];
+      for (int x = 0; x < NB; ++x) mma32(acc0[x], cur[x], fo[ks]);
+      if (ks + 2 < KS) load_s(cur, ks + 2);
     }
   } else {
     frag fvu[KS], fkh[KS];
@@ -475,12 +488,12 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   for (int it = 0; it < n_it; ++it) {
     __syncthreads();   // the previous tiles' readers are done
     if (it < n_q) {
-      put_rows(sKw, pk);
-      if (it > 0) put_rows(sV, pv);
+      put_rows(sKw, pk, (c - it) * C);
+      if (it > 0) put_rows(sV, pv, (c - it) * C);
     }
     if (it < n_k) {
-      put_rows(sQw, pq);
-      if (it > 0) put_rows(sDw, pd);
+      put_rows(sQw, pq, (c + it) * C);
+      if (it > 0) put_rows(sDw, pd, (c + it) * C);
     }
     // next iteration's tiles load while this one is processed
     if (it + 1 < n_q) {
