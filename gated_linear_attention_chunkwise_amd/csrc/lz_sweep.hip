@@ -34,13 +34,14 @@ namespace {
 constexpr int TT = 64;          // tile edge over d_k and d_v
 constexpr int NTHR_SW = 256;
 
-template <typename T>
+template <typename T, int D>
 struct SwLayout {
-  static constexpr int LDT = TT + Tr<T>::PAD;
-  static constexpr size_t oA = 0;                                   // [C][TT]  gate-folded q or k
-  static constexpr size_t oB = oA + sizeof(T) * CHUNK * LDT;        // [C][TT]  v or dO
-  static constexpr size_t oS = oB + sizeof(T) * CHUNK * LDT;        // [TT][TT] state tile (backward)
-  static constexpr size_t oDec = oS + sizeof(T) * TT * LDT;
+  static constexpr int LDA = TT + Tr<T>::PAD;
+  static constexpr int LDB = D + Tr<T>::PAD;
+  static constexpr size_t oA = 0;                                   // [C][TT]  gate-folded q or k (i tile)
+  static constexpr size_t oB = oA + sizeof(T) * CHUNK * LDA;        // [C][D]   v or dO (every j)
+  static constexpr size_t oS = oB + sizeof(T) * CHUNK * LDB;        // [TT][D]  state rows (backward)
+  static constexpr size_t oDec = oS + sizeof(T) * TT * LDB;
   static constexpr size_t bytes = oDec + sizeof(float) * TT;
 };
 
@@ -74,12 +75,13 @@ struct SwStage {
 // state and gate total (no chunk states).
 // SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
 template <typename T, int D, bool REV, bool REDUCE, bool SG>
-__global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
-  using LY = SwLayout<T>;
+__global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) {
+  using LY = SwLayout<T, D>;
   constexpr int NTI = D / TT;                      // tiles per edge
+  constexpr int NTHR = NTHR_SW * NTI;              // four waves per 64 x 64 tile of the row block
   constexpr int VEC = Tr<T>::VEC;
-  constexpr int NV = CHUNK * (TT / VEC) / NTHR_SW; // 16-byte vectors per thread of a [64][64] tile
-  constexpr int LDT = LY::LDT;
+  constexpr int NV = CHUNK * (D / VEC) / NTHR;     // 16-byte vectors per thread of a [64][D] tile
+  constexpr int LDA = LY::LDA, LDB = LY::LDB;
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* sA = reinterpret_cast<T*>(smem + LY::oA);
@@ -87,12 +89,16 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
   T* sS = reinterpret_cast<T*>(smem + LY::oS);
   float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
-  // workgroup -> (b*h, segment, i tile, j tile); the tiles and segments of one head share an XCD
+  // One workgroup carries a block of 64 rows (i) of the state over every column (j): four waves
+  // per 64 x 64 tile (wave w of tile jt), so the i tile's gate-folded q or k is formed once and
+  // the v or dO rows are loaded once for all tiles of the row block.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kg = lane >> 4;
+  const int jt = wave >> 2, w = wave & 3;
+  // workgroup -> (b*h, segment, i tile); the row blocks and segments of one head share an XCD
   const int BH = a.B * a.H;
   const int NSL = REDUCE ? a.NS - 1 : a.NS;        // segments launched (the reduce skips the last)
-  const int PER = NTI * NTI * NSL;
-  int bh, tile, seg;
+  const int PER = NTI * NSL;
+  int bh, it, seg;
   {
     const int bid = blockIdx.x;
     int y2;
@@ -104,10 +110,9 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       bh = bid / PER;
       y2 = bid % PER;
     }
-    seg = y2 / (NTI * NTI);
-    tile = y2 % (NTI * NTI);
+    seg = y2 / NTI;
+    it = y2 % NTI;
   }
-  const int it = tile / NTI, jt = tile % NTI;
   const int i0 = it * TT, j0 = jt * TT;
   const int L = a.L, NC = (L + CHUNK - 1) / CHUNK;
   const int c_begin = seg * a.SC, c_end = min(NC, c_begin + a.SC), NCs = c_end - c_begin;
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
     const int t0 = c * CHUNK;
     if (t0 + CHUNK <= L) {   // full chunk: no bounds checks
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4 && jt == 0; ++u) {
         const size_t o = (size_t)(t0 + 4 * tg + u) * D + acol;
         s.ra[u] = ld4f(asrc + o);
         if constexpr (SG) {
@@ -139,12 +144,12 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
-        s.rb[u] = ldg16(bsrc + (size_t)(t0 + row) * D + j0 + cv * VEC);
+        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        s.rb[u] = ldg16(bsrc + (size_t)(t0 + row) * D + cv * VEC);
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4 && jt == 0; ++u) {
         const int t = t0 + 4 * tg + u;
         const size_t o = (size_t)t * D + acol;
         s.ra[u] = t < L ? ld4f(asrc + o) : f32x4{0, 0, 0, 0};
@@ -157,15 +162,15 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
-        s.rb[u] = t0 + row < L ? ldg16(bsrc + (size_t)(t0 + row) * D + j0 + cv * VEC) : zero16();
+        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        s.rb[u] = t0 + row < L ? ldg16(bsrc + (size_t)(t0 + row) * D + cv * VEC) : zero16();
       }
     }
     if constexpr (REV) {
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
-        s.rs[u] = (c + 1 < NC) ? ldg16(states + ((size_t)(c + 1) * D + i0 + row) * D + j0 + cv * VEC) : zero16();
+        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        s.rs[u] = (c + 1 < NC) ? ldg16(states + ((size_t)(c + 1) * D + i0 + row) * D + cv * VEC) : zero16();
       }
     }
   };
@@ -200,33 +205,35 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
     __syncthreads();   // the previous chunk's operand reads are done
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int idx = tid + u * NTHR_SW, row = idx / (TT / VEC), cv = idx % (TT / VEC);
-      *reinterpret_cast<V16*>(sB + row * LDT + cv * VEC) = s.rb[u];
-      if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDT + cv * VEC) = s.rs[u];
+      const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+      *reinterpret_cast<V16*>(sB + row * LDB + cv * VEC) = s.rb[u];
+      if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDB + cv * VEC) = s.rs[u];
     }
-    // chunk-local inclusive prefix b of the gates and the chunk total Gamma
+    if (jt == 0) {
+      // chunk-local inclusive prefix b of the gates and the chunk total Gamma
 #pragma unroll
-    for (int u = 1; u < 4; ++u) s.rg[u] += s.rg[u - 1];
-    f32x4 excl, tot;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float own = s.rg[3][e];
-      excl[e] = row_scan16(own) - own;
-      tot[e] = row_sum16(own);
-    }
-    if (tg == 0)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sDec[16 * w + 4 * cg + e] = __expf(tot[e]);
-    if constexpr (REDUCE) gsum += tot;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f32x4 x;
+      for (int u = 1; u < 4; ++u) s.rg[u] += s.rg[u - 1];
+      f32x4 excl, tot;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float b = s.rg[u][e] + excl[e];
-        x[e] = s.ra[u][e] * __expf(REV ? b : tot[e] - b);
+        const float own = s.rg[3][e];
+        excl[e] = row_scan16(own) - own;
+        tot[e] = row_sum16(own);
       }
-      st4(sA + (4 * tg + u) * LDT + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
+      if (tg == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDec[16 * w + 4 * cg + e] = __expf(tot[e]);
+      if constexpr (REDUCE) gsum += tot;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float b = s.rg[u][e] + excl[e];
+          x[e] = s.ra[u][e] * __expf(REV ? b : tot[e] - b);
+        }
+        st4(sA + (4 * tg + u) * LDA + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
+      }
     }
     if (n + 2 < NCs) load(s, chunk_of(n + 2));
     __syncthreads();
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       // boundary rowsum over this j tile, decay, store dS' transposed
       f32x4 rsum = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) rsum += col4(sS, LDT, 16 * w + 4 * kg, 16 * jb, lane) * acc[jb];
+      for (int jb = 0; jb < 4; ++jb) rsum += col4(sS, LDB, 16 * w + 4 * kg, j0 + 16 * jb, lane) * acc[jb];
 #pragma unroll
       for (int e = 0; e < 4; ++e) rsum[e] = row_sum16(rsum[e]);
       if (r == 0)
@@ -253,10 +260,10 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       // + (q e^b)^T dO
 #pragma unroll
       for (int ks = 0; ks < CHUNK / 32; ++ks) {
-        const auto fa = ld_frag_tr(sA, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * w, lane);
+        const auto fa = ld_frag_tr(sA, LDA, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * w, lane);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
-          mma32(acc[jb], fa, ld_frag_tr(sB, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane));
+          mma32(acc[jb], fa, ld_frag_tr(sB, LDB, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, j0 + 16 * jb, lane));
       }
     } else {
 #pragma unroll
@@ -264,10 +271,10 @@ __global__ __launch_bounds__(NTHR_SW) void sweep_kernel(SweepArgs a) {
       // + (k e^{Gamma-b})^T v, computed transposed so each lane holds four consecutive d_v entries
 #pragma unroll
       for (int ks = 0; ks < CHUNK / 32; ++ks) {
-        const auto fb = ld_frag_tr(sB, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * w, lane);
+        const auto fb = ld_frag_tr(sB, LDB, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, j0 + 16 * w, lane);
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
-          mma32(acc[ib], fb, ld_frag_tr(sA, LDT, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * ib, lane));
+          mma32(acc[ib], fb, ld_frag_tr(sA, LDA, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * ib, lane));
       }
     }
   };
@@ -318,14 +325,15 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(SweepArgs a, int D) {
 
 template <typename T, int D, bool REV, bool SG>
 hipError_t launch_sweep_g(const SweepArgs& a, hipStream_t st) {
-  using LY = SwLayout<T>;
-  const int tiles = (D / TT) * (D / TT);
+  using LY = SwLayout<T, D>;
+  const int blocks = D / TT;                    // 64-row blocks of the state
+  const int nthr = NTHR_SW * (D / TT);
   if (!REV && a.NS > 1) {
-    hipLaunchKernelGGL((sweep_kernel<T, D, false, true, SG>), dim3(a.B * a.H * tiles * (a.NS - 1)),
-                       dim3(NTHR_SW), LY::bytes, st, a);
+    hipLaunchKernelGGL((sweep_kernel<T, D, false, true, SG>), dim3(a.B * a.H * blocks * (a.NS - 1)),
+                       dim3(nthr), LY::bytes, st, a);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(a.B * a.H * (D * D / 256)), dim3(256), 0, st, a, D);
   }
-  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false, SG>), dim3(a.B * a.H * tiles * a.NS), dim3(NTHR_SW),
+  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false, SG>), dim3(a.B * a.H * blocks * a.NS), dim3(nthr),
                      LY::bytes, st, a);
   return hipGetLastError();
 }
@@ -350,9 +358,9 @@ hipError_t launch_sweep_dir(const SweepArgs& a, int dtype, int D, hipStream_t st
 
 int sweep_segments(int B, int H, int L, int D) {
   const int NC = (L + CHUNK - 1) / CHUNK;
-  const double base = (double)B * H * (D / TT) * (D / TT);   // workgroups of one segment
-  if (base >= 512) return 1;
-  int ns = (int)((2048 + base - 1) / base);                 // aim at ~2048 workgroups
+  const double base = (double)B * H * (D / TT);             // workgroups of one segment
+  if (base >= 256) return 1;                                 // one per CU or more already
+  int ns = (int)((1024 + base - 1) / base);                 // aim at ~1024 workgroups
   ns = std::min(ns, NC / 16);                                // segments of at least 16 chunks
   if (ns <= 1) return 1;
   const int sc = (NC + ns - 1) / ns;
