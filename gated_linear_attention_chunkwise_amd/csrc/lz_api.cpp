@@ -32,7 +32,6 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
   if (s->M > kMaxMeta) return LIZARD_EUNSUPPORTED;
   if (op == LIZARD_OP_DECODE) {
     if (s->W > kMaxDecodeWindow) return LIZARD_EUNSUPPORTED;
-    if (s->H > 255) return LIZARD_EUNSUPPORTED;          // pos carries an 8-bit arrival count
   } else {
     if (s->chunk != 0 && s->chunk != kChunk) return LIZARD_EUNSUPPORTED;
     if (s->W > 2 * kChunk + 1) return LIZARD_EUNSUPPORTED;     // window spans at most 3 chunks

@@ -8,23 +8,21 @@
 //   ring  [B,H,W,d]            last W keys / values, token n in slot n mod W
 //   pos   [B] int32            tokens consumed so far
 //
-// Two launches per step:
-//   decode_state_kernel   one workgroup per (b, h, 32 state rows): streams the
-//                         fp32 state, S <- diag(exp g) S + k^T v, and writes the
-//                         rows' partial q . S to the workspace;
-//   decode_window_kernel  one workgroup per (b, h): softmax over the meta keys
-//                         and the filled ring slots (the new token's slot taken
-//                         from the inputs, never from the ring), values, sum of
-//                         the partials, o = o_gla + mix * o_swa, the ring write
-//                         and the advance of pos.  Every load it needs is issued
-//                         up front (one 128-key block of the key and value rings).
-// Splitting keeps the state stream (two thirds of the step's bytes) in small,
-// register-light workgroups that fill the chip.
-//
-// pos is shared by the H heads of a sequence: every window workgroup reads it
-// first; when done, it adds 1 << 24 to it, and the workgroup that brings that
-// arrival count to H stores pos + 1 (clearing the count).  Between calls the
-// top byte of pos is zero; pos must stay below 2^24 and H below 256.
+// One launch per step, NP = d/32 workgroups per (b, h).  Part j of a head
+//   - streams state rows 32j .. 32j+31: S <- diag(exp g) S + k^T v, and forms
+//     the rows' partial q . S;
+//   - covers ring slots [j*WS, (j+1)*WS) (WS = ceil(W / NP); part 0 also the M
+//     meta keys): partial softmax statistics of its logits (max m_j and sum
+//     l_j, log2 units) and the unnormalised partial sum o_j of its values; the
+//     new token's slot is taken from the inputs, never from the ring, and the
+//     part owning it writes the new key and value there;
+//   - writes both partials to the workspace.
+// Every workgroup moves the same share of the step's bytes (state rows and ring
+// slots alike), so the state stream and the window read fill the chip together.
+// A second, small launch (one workgroup per (b, h)) combines the partials,
+//   o = sum_j gla_j + mix * sum_j e^{m_j - m} o_j / sum_j e^{m_j - m} l_j  (m = max_j m_j),
+// and advances pos: the kernel boundary orders the partials' writes and reads, and
+// orders every read of pos (first launch) before its update (second launch).
 #include "lz_common.hpp"
 #include "lz_kernels.hpp"
 
@@ -32,26 +30,76 @@ namespace lz {
 namespace {
 
 constexpr int NTHR = 256;
-constexpr int KB = 128;          // ring keys per register block
+constexpr int RB = 32;           // state rows (and the share of ring slots) per workgroup
+constexpr int KBP = 32;          // ring slots per register block
 
-constexpr int RB = 32;           // state rows per workgroup of the state kernel
+// workspace: per (b, h, part) [D] partial q.S, [D] unnormalised window sum, (max, sum)
+template <int D>
+struct DecWs {
+  static constexpr int NP = D / RB;
+  static constexpr int PS = 2 * D + 4;       // floats per part (16-byte aligned)
+  static size_t bytes(int B, int H) { return (size_t)B * H * NP * PS * sizeof(float); }
+};
 
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void decode_state_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
+  using WS_ = DecWs<D>;
+  constexpr int NP = WS_::NP, PS = WS_::PS;
   constexpr int F4R = D / 4;                  // float4 per state row
-  constexpr int RPT = RB * F4R / NTHR;        // rows per thread
+  constexpr int RPT = RB * F4R / NTHR;        // state rows per thread
   constexpr int RS = NTHR / F4R;              // row stride between a thread's rows
-  static_assert(NTHR % F4R == 0 && RPT * RS == RB, "state thread map");
+  constexpr int VEC = Tr<T>::VEC;
+  constexpr int VPR = D / VEC;                // 16-byte vectors per ring row
+  constexpr int RPP = NTHR / VPR;             // ring rows per pass
+  constexpr int NR = (KBP + RPP - 1) / RPP;   // ring vectors per thread per block
+  constexpr int NMP = (16 + RPP - 1) / RPP;   // meta-key passes (M <= 16)
+  static_assert(NTHR % F4R == 0 && RPT * RS == RB && NTHR % VPR == 0, "thread maps");
+
+  extern __shared__ __align__(16) float slog[];   // [WS + 16] logits of the part, then probabilities
   __shared__ float sred[NTHR / 64][D];
+  __shared__ float sq[D], sk[D], sv[D];
+  __shared__ float sstat[2][NTHR / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bh = blockIdx.x / (D / RB), rb = blockIdx.x % (D / RB);
-  const int c4 = tid % F4R, r0 = tid / F4R;
+  const int bh = blockIdx.x / NP, part = blockIdx.x % NP;
+  const int b = bh / a.H, h = bh % a.H;
+  const int W = a.W, M = a.M;
+  const int WSL = (W + NP - 1) / NP;          // ring slots per part
+  const int lo = part * WSL, hi = min(W, lo + WSL);
   const size_t vo = (size_t)bh * D;
-  float* S = a.state + ((size_t)bh * D + rb * RB) * D;
+  float* wsp = a.o_part + ((size_t)bh * NP) * PS;
+  const unsigned int* posu = reinterpret_cast<const unsigned int*>(a.pos);
+  const T* rk = reinterpret_cast<const T*>(a.ring_k) + (size_t)bh * W * D;
+  const T* rv = reinterpret_cast<const T*>(a.ring_v) + (size_t)bh * W * D;
+
+  // ---- issue the step's loads: state rows, the first ring block (slots clamped, masked when
+  // used: no load waits for pos), pos, meta keys, inputs
+  const int c4 = tid % F4R, r0 = tid / F4R;
+  float* S = a.state + ((size_t)bh * D + part * RB) * D;
   f32x4 st[RPT];
 #pragma unroll
   for (int u = 0; u < RPT; ++u) st[u] = *reinterpret_cast<const f32x4*>(S + (size_t)(r0 + u * RS) * D + 4 * c4);
+  const int cv = tid % VPR, s0 = tid / VPR;
+  V16 kr[NR], vr[NR];
+  auto load_block = [&](int blk) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int sl = min(blk + s0 + u * RPP, hi - 1);
+      kr[u] = ldg16(rk + (size_t)sl * D + cv * VEC);
+      vr[u] = ldg16(rv + (size_t)sl * D + cv * VEC);
+    }
+  };
+  load_block(lo);
+  const int pos = (int)posu[b];
+  const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
+  V16 mkr[NMP];
+#pragma unroll
+  for (int p = 0; p < NMP; ++p) {
+    const int m = s0 + p * RPP;
+    mkr[p] = (part == 0 && m < M) ? ldg16(mk + (size_t)m * D + cv * VEC) : zero16();
+  }
+  const T* qg = reinterpret_cast<const T*>(a.q) + vo;
+  const T* kg = reinterpret_cast<const T*>(a.k) + vo;
   const T* vg = reinterpret_cast<const T*>(a.v) + vo;
   f32x4 vv;
 #pragma unroll
@@ -59,120 +107,56 @@ __global__ __launch_bounds__(NTHR) void decode_state_kernel(DecodeArgs a) {
   float qi[RPT], ki[RPT], ai[RPT];
 #pragma unroll
   for (int u = 0; u < RPT; ++u) {
-    const int i = rb * RB + r0 + u * RS;
-    qi[u] = Tr<T>::to_f(reinterpret_cast<const T*>(a.q)[vo + i]);
-    ki[u] = Tr<T>::to_f(reinterpret_cast<const T*>(a.k)[vo + i]);
+    const int i = part * RB + r0 + u * RS;
+    qi[u] = Tr<T>::to_f(qg[i]);
+    ki[u] = Tr<T>::to_f(kg[i]);
     ai[u] = __expf(a.gate ? a.g[bh] : a.g[vo + i]);   // scalar gate: one per head
-  }
-  f32x4 part = f32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const f32x4 x = ai[u] * st[u] + ki[u] * vv;
-    *reinterpret_cast<f32x4*>(S + (size_t)(r0 + u * RS) * D + 4 * c4) = x;
-    part += qi[u] * x;
-  }
-  // threads sharing c4 differ in the lane bits above log2(F4R), then across waves
-#pragma unroll
-  for (int m = F4R; m < 64; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) part[e] = xor_sum(part[e], m);
-  if (lane < F4R)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sred[wv][4 * lane + e] = part[e];
-  __syncthreads();
-  for (int j = tid; j < D; j += NTHR) {
-    float acc = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < NTHR / 64; ++w2) acc += sred[w2][j];
-    a.o_part[((size_t)bh * (D / RB) + rb) * D + j] = acc;
-  }
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
-  constexpr int VEC = Tr<T>::VEC;
-  constexpr int VPR = D / VEC;                // 16-byte vectors per ring row
-  constexpr int RPP = NTHR / VPR;             // ring rows per pass
-  constexpr int NR = KB / RPP;                // ring vectors per thread per block
-  static_assert(NTHR % VPR == 0 && KB % RPP == 0, "thread maps");
-
-  extern __shared__ __align__(16) float slog[];   // [M + W] logits, then probabilities
-  __shared__ float sq[D], sk[D], sv[D], sgla[D];
-  __shared__ float sstat[2][NTHR / 64];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bh = blockIdx.x;
-  const int b = bh / a.H, h = bh % a.H;
-  const int W = a.W, M = a.M;
-  unsigned int* posu = reinterpret_cast<unsigned int*>(a.pos);
-  const int pos = (int)(*reinterpret_cast<volatile unsigned int*>(posu + b) & 0x00FFFFFFu);
-  const int slot = pos % W;
-  const int n = min(pos + 1, W);
-  const size_t vo = (size_t)bh * D;
-  const T* qg = reinterpret_cast<const T*>(a.q) + vo;
-  const T* kg = reinterpret_cast<const T*>(a.k) + vo;
-  const T* vg = reinterpret_cast<const T*>(a.v) + vo;
-  const T* rk = reinterpret_cast<const T*>(a.ring_k) + (size_t)bh * W * D;
-  const T* rv = reinterpret_cast<const T*>(a.ring_v) + (size_t)bh * W * D;
-
-  // ---- issue every load of the step
-  const int cv = tid % VPR, s0 = tid / VPR;
-  V16 kr[NR], vr[NR];
-#pragma unroll
-  for (int u = 0; u < NR; ++u) {
-    const int s = s0 + u * RPP;
-    const bool ok = s < n && s != slot;
-    kr[u] = ok ? ldg16(rk + (size_t)s * D + cv * VEC) : zero16();
-    vr[u] = ok ? ldg16(rv + (size_t)s * D + cv * VEC) : zero16();
-  }
-  // meta keys: rows m = s0 + p * RPP of the ring thread map (M <= 16)
-  constexpr int NMP = (16 + RPP - 1) / RPP;
-  const T* mk = reinterpret_cast<const T*>(a.meta_k) + (size_t)h * M * D;
-  V16 mkr[NMP];
-#pragma unroll
-  for (int p = 0; p < NMP; ++p) {
-    const int m = s0 + p * RPP;
-    mkr[p] = m < M ? ldg16(mk + (size_t)m * D + cv * VEC) : zero16();
   }
   for (int i = tid; i < D; i += NTHR) {
     sq[i] = Tr<T>::to_f(qg[i]);
     sk[i] = Tr<T>::to_f(kg[i]);
     sv[i] = Tr<T>::to_f(vg[i]);
-    float og = 0.f;
+  }
+
+  // ---- state rows: decay + rank-1 update, partial q . S of the rows
+  {
+    f32x4 pq = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int p = 0; p < D / RB; ++p) og += a.o_part[((size_t)bh * (D / RB) + p) * D + i];
-    sgla[i] = og;
+    for (int u = 0; u < RPT; ++u) {
+      const f32x4 x = ai[u] * st[u] + ki[u] * vv;
+      *reinterpret_cast<f32x4*>(S + (size_t)(r0 + u * RS) * D + 4 * c4) = x;
+      pq += qi[u] * x;
+    }
+    // threads sharing c4 differ in the lane bits above log2(F4R), then across waves
+#pragma unroll
+    for (int m = F4R; m < 64; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pq[e] = xor_sum(pq[e], m);
+    if (lane < F4R)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sred[wv][4 * lane + e] = pq[e];
   }
   __syncthreads();
-
-  // ---- window logits (log2 units): meta keys, then ring slots (new token from the inputs)
-  const float sl2 = a.scale * LOG2E;
-  float lmax = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < NMP; ++p) {
-    const int m = s0 + p * RPP;
+  for (int j = tid; j < D; j += NTHR) {
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(mkr[p], e, (T*)nullptr);
-    acc = group_sum<VPR>(acc);
-    if (m < M) {
-      if (cv == 0) slog[m] = acc * sl2;
-      lmax = fmaxf(lmax, acc * sl2);
-    }
+    for (int w2 = 0; w2 < NTHR / 64; ++w2) acc += sred[w2][j];
+    wsp[part * PS + j] = acc;
   }
-  for (int blk = 0; blk < n; blk += KB) {
-    if (blk > 0) {   // windows longer than one register block: load the next block
-#pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int s = blk + s0 + u * RPP;
-        kr[u] = (s < n && s != slot) ? ldg16(rk + (size_t)s * D + cv * VEC) : zero16();
-      }
-    }
+
+  // ---- window logits (log2 units) of this part's slots that hold a token, then its meta keys
+  const int slot = pos % W;
+  const int n = min(pos + 1, W);              // filled slots, the new token's included
+  const float sl2 = a.scale * LOG2E;
+  const int nhold = max(0, min(hi, n) - lo);  // this part's filled slots: lo .. lo+nhold-1
+  float lmax = -INFINITY;
+  for (int blk = lo; blk < lo + nhold; blk += KBP) {
+    if (blk > lo) load_block(blk);
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
-      const int s = blk + s0 + u * RPP;
+      const int sl = blk + s0 + u * RPP;
       float acc = 0.f;
-      if (s == slot) {
+      if (sl == slot) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * sk[cv * VEC + e];
       } else {
@@ -180,8 +164,22 @@ __global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
         for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(kr[u], e, (T*)nullptr);
       }
       acc = group_sum<VPR>(acc);
-      if (s < n) {
-        if (cv == 0) slog[M + s] = acc * sl2;
+      if (sl < lo + nhold && u * RPP < KBP) {
+        if (cv == 0) slog[sl - lo] = acc * sl2;
+        lmax = fmaxf(lmax, acc * sl2);
+      }
+    }
+  }
+  if (part == 0) {
+#pragma unroll
+    for (int p = 0; p < NMP; ++p) {
+      const int m = s0 + p * RPP;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += sq[cv * VEC + e] * v16_get(mkr[p], e, (T*)nullptr);
+      acc = group_sum<VPR>(acc);
+      if (m < M) {
+        if (cv == 0) slog[WSL + m] = acc * sl2;
         lmax = fmaxf(lmax, acc * sl2);
       }
     }
@@ -190,41 +188,40 @@ __global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
   for (int m = 1; m < 64; m <<= 1) lmax = xor_max(lmax, m);
   if (lane == 0) sstat[0][wv] = lmax;
   __syncthreads();
-  float gmax = sstat[0][0];
+  float pmax = sstat[0][0];
 #pragma unroll
-  for (int i = 1; i < NTHR / 64; ++i) gmax = fmaxf(gmax, sstat[0][i]);
+  for (int i = 1; i < NTHR / 64; ++i) pmax = fmaxf(pmax, sstat[0][i]);
+  const int nmeta = part == 0 ? M : 0;
   float lsum = 0.f;
-  for (int e = tid; e < M + n; e += NTHR) {
-    const float p = fast_exp2(slog[e] - gmax);
-    slog[e] = p;
-    lsum += p;
+  if (pmax > -INFINITY) {
+    for (int e = tid; e < nhold; e += NTHR) {
+      const float p = fast_exp2(slog[e] - pmax);
+      slog[e] = p;
+      lsum += p;
+    }
+    for (int e = tid; e < nmeta; e += NTHR) {
+      const float p = fast_exp2(slog[WSL + e] - pmax);
+      slog[WSL + e] = p;
+      lsum += p;
+    }
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lsum = xor_sum(lsum, m);
+  __syncthreads();   // probabilities visible; sstat[0] read by every thread
   if (lane == 0) sstat[1][wv] = lsum;
-  __syncthreads();
-  float l = 0.f;
-#pragma unroll
-  for (int i = 0; i < NTHR / 64; ++i) l += sstat[1][i];
 
-  // ---- o_swa: thread sums p_s v_s over its ring rows for its VEC columns
+  // ---- unnormalised value sum of the part
   float ow[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) ow[e] = 0.f;
-  for (int blk = 0; blk < n; blk += KB) {
-    if (blk > 0) {
-#pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int s = blk + s0 + u * RPP;
-        vr[u] = (s < n && s != slot) ? ldg16(rv + (size_t)s * D + cv * VEC) : zero16();
-      }
-    }
+  for (int blk = lo; blk < lo + nhold; blk += KBP) {
+    if (blk > lo || nhold > KBP) load_block(blk);   // the first block is still held unless reloaded
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
-      const int s = blk + s0 + u * RPP;
-      if (s < n) {
-        const float p = slog[M + s];
-        if (s == slot) {
+      const int sl = blk + s0 + u * RPP;
+      if (sl < lo + nhold && u * RPP < KBP) {
+        const float p = slog[sl - lo];
+        if (sl == slot) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) ow[e] += p * sv[cv * VEC + e];
         } else {
@@ -235,9 +232,9 @@ __global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
     }
   }
   if (a.meta_v != nullptr) {
-    for (int m = s0; m < M; m += RPP) {
+    for (int m = s0; m < nmeta; m += RPP) {
       const V16 x = ldg16(reinterpret_cast<const T*>(a.meta_v) + ((size_t)h * M + m) * D + cv * VEC);
-      const float p = slog[m];
+      const float p = slog[WSL + m];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) ow[e] += p * v16_get(x, e, (T*)nullptr);
     }
@@ -247,19 +244,25 @@ __global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
   for (int m = VPR; m < 64; m <<= 1)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) ow[e] = xor_sum(ow[e], m);
-  __shared__ float swin[NTHR / 64][D];
   if (lane < VPR)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) swin[wv][lane * VEC + e] = ow[e];
+    for (int e = 0; e < VEC; ++e) sred[wv][lane * VEC + e] = ow[e];
   __syncthreads();
   for (int j = tid; j < D; j += NTHR) {
     float osw = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < NTHR / 64; ++w2) osw += swin[w2][j];
-    reinterpret_cast<T*>(a.o)[vo + j] = Tr<T>::from_f(sgla[j] + a.mix * osw / l);
+    for (int w2 = 0; w2 < NTHR / 64; ++w2) osw += sred[w2][j];
+    wsp[part * PS + D + j] = osw;
   }
-  // ---- ring: the new key and value into slot pos mod W
-  {
+  if (tid == 0) {
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < NTHR / 64; ++i) l += sstat[1][i];
+    wsp[part * PS + 2 * D] = pmax;
+    wsp[part * PS + 2 * D + 1] = l;
+  }
+  // ---- ring: the new key and value into slot pos mod W, by the part that owns it
+  if (slot >= lo && slot < hi) {
     T* rkw = reinterpret_cast<T*>(a.ring_k) + ((size_t)bh * W + slot) * D;
     T* rvw = reinterpret_cast<T*>(a.ring_v) + ((size_t)bh * W + slot) * D;
     for (int d = tid; d < D; d += NTHR) {   // exact: the LDS copies came from these values
@@ -267,28 +270,52 @@ __global__ __launch_bounds__(NTHR) void decode_window_kernel(DecodeArgs a) {
       put_elem(rvw + d, sv[d]);
     }
   }
-  // ---- pos: the last of the H workgroups of sequence b advances it
-  // (no fence: nothing this step writes is read by another workgroup of the step;
-  // the next step is a later launch)
-  if (tid == 0) {
-    const unsigned int old = atomicAdd(posu + b, 1u << 24);
-    if ((old >> 24) == (unsigned int)(a.H - 1)) atomicExch(posu + b, (old & 0x00FFFFFFu) + 1u);
+
+}
+
+// One workgroup per (b, h), one thread per output column: combine the NP partials of the
+// head, store o, and advance pos (the last of the H heads of a sequence).
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  using WS_ = DecWs<D>;
+  constexpr int NP = WS_::NP, PS = WS_::PS;
+  const int bh = blockIdx.x, d = threadIdx.x, b = bh / a.H;
+  const float* wsp = a.o_part + ((size_t)bh * NP) * PS;
+  float mj[NP], gmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    mj[j] = wsp[j * PS + 2 * D];
+    gmax = fmaxf(gmax, mj[j]);
   }
+  float og = 0.f, osw = 0.f, l = 0.f;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const float wj = mj[j] > -INFINITY ? fast_exp2(mj[j] - gmax) : 0.f;
+    l += wj * wsp[j * PS + 2 * D + 1];
+    og += wsp[j * PS + d];
+    osw += wj * wsp[j * PS + D + d];
+  }
+  reinterpret_cast<T*>(a.o)[(size_t)bh * D + d] = Tr<T>::from_f(og + a.mix * osw / l);
+  // pos: nothing in this launch reads it, so head 0's workgroup advances it alone
+  if (d == 0 && bh % a.H == 0) a.pos[b] = a.pos[b] + 1;
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_state_kernel<T, D>), dim3(a.B * a.H * (D / RB)), dim3(NTHR), 0, st, a);
+  constexpr int NP = D / RB;
+  const size_t lds = sizeof(float) * (size_t)((a.W + NP - 1) / NP + 16);
+  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(a.B * a.H * NP), dim3(NTHR), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(float) * (size_t)(a.M + a.W);
-  hipLaunchKernelGGL((decode_window_kernel<T, D>), dim3(a.B * a.H), dim3(NTHR), lds, st, a);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.H), dim3(D), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int H, int D) { return sizeof(float) * (size_t)B * H * (D / RB) * D; }
+size_t decode_workspace_bytes(int B, int H, int D) {
+  return D == 128 ? DecWs<128>::bytes(B, H) : DecWs<64>::bytes(B, H);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st) {
   if (dtype == 1) {

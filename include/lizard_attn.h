@@ -169,8 +169,7 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
  *           min(pos[b], W) earlier tokens, token t in slot t mod W (the decode
  *           layout); on return the segment's last tokens are stored likewise
  *   pos     in/out, device int32 [B]: tokens before the segment, per sequence
- *           (sequences of one batch may differ); pos[b] + L < 2^31 (and < 2^24
- *           with a zero top byte if decode steps follow); incremented by L
+ *           (sequences of one batch may differ); pos[b] + L < 2^31; incremented by L
  *   o       [B,H,L,d_v] written
  *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_FWD_CONTINUE) bytes of
  *           caller-owned device memory (clobbered): the chunk states
@@ -189,14 +188,14 @@ lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
  *   q, k [B,H,d_k], v [B,H,d_v] (dtype), g [B,H,d_k] fp32: the new token
  *   state  in/out: S <- diag(exp g) S + k^T v (fp32)
  *   ring_k, ring_v in/out: the new key/value is stored in slot pos[b] mod W
- *   pos    in/out, device int32 [B]: tokens already consumed, < 2^24; its top
- *          byte is used as an arrival count during the call (zero before and
- *          after; H <= 255); incremented
+ *   pos    in/out, device int32 [B]: tokens already consumed (>= 0); incremented
  *   o      [B,H,d_v] written: q S + mix * softmax over M meta keys and the
  *          min(pos+1, W) filled ring slots.
  *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_DECODE) bytes of
- *          caller-owned device memory (clobbered): the partial q S of each
- *          block of 32 state rows, passed between the step's two launches
+ *          caller-owned device memory (clobbered): the partials of the d/32
+ *          workgroups of each head (q S of 32 state rows; softmax statistics
+ *          and value sum of a share of the ring slots), passed from the step's
+ *          first launch to its second
  * Uses s->B, H, d_k, d_v, W, M, scale, mix, dtype; s->L and s->chunk are ignored. */
 lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         const void* q, const void* k, const void* v,

@@ -107,7 +107,7 @@ def test_decode_validation(lib):
     assert call(pos=BAD) == EALIGN
     assert call(s_=shape(W=9000)) == EUNSUPPORTED
     need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 2)
-    assert need == 1 * 2 * (128 // 32) * 128 * 4       # B*H partial q.S rows per 32 state rows, fp32
+    assert need == 1 * 2 * (128 // 32) * (2 * 128 + 4) * 4   # per (b, h, part): q.S, window sum, statistics
     assert call(ws=None) == EWORKSPACE
     assert call(ws_bytes=need - 1) == EWORKSPACE
     assert call(ws=BAD, ws_bytes=need) == EALIGN
