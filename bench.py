@@ -271,7 +271,7 @@ def bench_decode(args, hip, torch, lib):
             "tokens_per_s": round(w.B / (us * 1e-6), 1), "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode"),
-                         "kernel": "decode_state_kernel + decode_window_kernel",
+                         "kernel": "decode_kernel + decode_combine_kernel",
                          "algorithmic_bytes_per_step": bytes_step}}
 
 
