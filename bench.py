@@ -143,7 +143,7 @@ def bench_train(args, hip, torch, lib):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
+    evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -151,8 +151,8 @@ def bench_train(args, hip, torch, lib):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # forward = state sweep + output kernel; then the backward's four stages
-    names = ["forward", "delta_kernel", "sweep_kernel_bwd", "chunk_kernel", "dmeta_kernels"]
+    # forward = state sweep + output kernel; then the backward's three stages
+    names = ["forward", "sweep_kernel_bwd", "chunk_kernel", "dmeta_kernels"]
     per = {n: [] for n in names}
     for ev in evs:
         for i, n in enumerate(names):
@@ -207,7 +207,7 @@ def bench_scalar_gate(args, hip, torch, lib, x, w):
     for _ in range(3):
         step()
     steps = max(1, min(args.steps, 10))
-    evs = [[hip.event() for _ in range(5)] for _ in range(steps)]
+    evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
@@ -216,7 +216,7 @@ def bench_scalar_gate(args, hip, torch, lib, x, w):
     hip.record(e1, stream)
     torch.cuda.synchronize()
     ms = hip.ms(e0, e1) / steps
-    chunk_ms = sum(hip.ms(ev[2], ev[3]) for ev in evs) / steps
+    chunk_ms = sum(hip.ms(ev[1], ev[2]) for ev in evs) / steps
     ht = w.B * w.H * w.L
     step_bytes = (FWD_BYTES_SCALAR + BWD_BYTES_SCALAR) * ht
     ck = BWD_BYTES_SCALAR * ht / (chunk_ms * 1e-3) / 1e9

@@ -172,7 +172,7 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
     return out
 
 
-BWD_STAGES = 4
+BWD_STAGES = 3
 
 
 def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *, window: int,

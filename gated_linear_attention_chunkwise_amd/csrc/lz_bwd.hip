@@ -17,10 +17,11 @@
 // catastrophically in low precision) is ever formed.
 //
 // Kernels, in launch order:
-//   delta_kernel   D_t = mix * dO_t . o_swa_t                       (row dots)
-//   sweep_kernel   (lz_sweep.hip) reverse sweep over chunks per (b, h, 64 x 64
-//                  tile of dS): carries dS in fp32 registers, stores dS'
-//                  (operand dtype, transposed) and the fp32 boundary rowsums
+//   sweep_kernel   (lz_sweep.hip) reverse sweep over chunks per (b, h, 64-row
+//                  block of dS): carries dS in fp32 registers, stores dS'
+//                  (operand dtype, transposed) and the fp32 boundary rowsums;
+//                  the block of rows 0..63 also forms the window row dots
+//                  D_t = mix * dO_t . o_swa_t from the dO rows it streams
 //   chunk_kernel   one workgroup per (b, h, chunk): every GLA gradient plus
 //                  the anchor-window gradients (query side for dq, key side
 //                  for dk and dv) and per-chunk meta-key partial sums
@@ -59,26 +60,6 @@ WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
   off += round_up(sizeof(float) * (size_t)B * NC * H * M * 2 * D, 256);
   w.total = off;
   return w;
-}
-
-// ------------------------------------------------------------------ delta
-template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void delta_kernel(const T* __restrict__ dO, const T* __restrict__ o_swa,
-                                                      float* __restrict__ delta, size_t rows, float mix) {
-  constexpr int VEC = Tr<T>::VEC, VPR = D / VEC, RPW = 64 / VPR;
-  const int lane = threadIdx.x & 63;
-  const size_t row = ((size_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6)) * RPW + lane / VPR;
-  const int cv = lane % VPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const V16 a = ldg16(dO + row * D + cv * VEC);
-    const V16 b = ldg16(o_swa + row * D + cv * VEC);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc += v16_get(a, e, (T*)nullptr) * v16_get(b, e, (T*)nullptr);
-  }
-#pragma unroll
-  for (int m = 1; m < VPR; m <<= 1) acc = xor_sum(acc, m);
-  if (row < rows && cv == 0) delta[row] = mix * acc;
 }
 
 // ------------------------------------------------------------ chunk kernel
@@ -711,21 +692,13 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     if (a.stage_events != nullptr) (void)hipEventRecord(a.stage_events[i], st);
   };
   mark(0);
-  {
-    constexpr int RPB = (NTHR / 64) * (64 / (D / Tr<T>::VEC));
-    const size_t rows = (size_t)BH * a.L;
-    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(NTHR), 0, st,
-                       reinterpret_cast<const T*>(a.dO), reinterpret_cast<const T*>(a.o_swa), a.ws_delta, rows,
-                       a.mix);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  mark(1);
+  // the state-gradient sweep also forms the window row dots delta_t from the dO rows it streams
   {
     const SweepArgs sw{a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr, a.B, a.H, a.L, 1, NC,
-                       nullptr, nullptr, nullptr, a.gate};
+                       nullptr, nullptr, nullptr, a.gate, a.o_swa, a.ws_delta, a.mix};
     if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, true, st)) != hipSuccess) return e;
   }
-  mark(2);
+  mark(1);
   {
     using LY = CkLayout<T, D>;
     static bool attr[2] = {false, false};   // idempotent; a race only repeats the same call
@@ -737,7 +710,7 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3(BH * NC), dim3(NTHR_CK), LY::bytes, st, a, (const T*)wsdS, (const float*)wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  mark(3);
+  mark(2);
   if (a.M > 0) {
     const int n = a.H * a.M * 2 * D;
     const int slots = a.B * NC;
@@ -750,7 +723,7 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
                        (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, slots, per, n, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  mark(4);
+  mark(3);
   return hipSuccess;
 }
 

@@ -407,7 +407,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
   void* states = a.chunk_states != nullptr ? a.chunk_states : ws + segb;
   SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in, a.B, a.H, a.L,
-               NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate};
+               NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate, nullptr, nullptr, 0.f};
   if (NS > 1) {
     const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
     sw.seg_in = reinterpret_cast<float*>(ws);

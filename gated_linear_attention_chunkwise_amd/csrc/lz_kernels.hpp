@@ -56,6 +56,9 @@ struct SweepArgs {
   int NS, SC;
   float* seg_in; float* seg_fin; float* seg_gtot;
   int gate;             // as in FwdArgs
+  // backward: with delta set, the workgroups of state rows 0..63 also form the window
+  // row dots delta_t = mix * dO_t . o_swa_t [B,H,L] fp32 from the dO rows they stream
+  const void* o_swa; float* delta; float mix;
 };
 
 struct DecodeArgs {

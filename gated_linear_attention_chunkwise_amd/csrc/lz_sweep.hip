@@ -69,6 +69,7 @@ struct SwStage {
   f32x4 rg[4];   // log-gates, same positions
   V16 rb[NV];    // v or dO tile, 16-byte vectors
   V16 rs[NV];    // state tile (backward)
+  V16 ro[NV];    // o_swa rows (backward row dots)
 };
 
 // REDUCE (forward only): carry a segment from a zero state and keep only its final
@@ -119,6 +120,10 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   const size_t hoff = (size_t)bh * L * D;
   const T* asrc = reinterpret_cast<const T*>(a.a_src) + hoff;
   const T* bsrc = reinterpret_cast<const T*>(a.b_src) + hoff;
+  // backward: the row blocks of a head also form the window row dots of each chunk, the block of
+  // state rows i0.. taking the token rows of its own register slots u with u % NTI == it
+  const bool dots = REV && a.delta != nullptr;
+  const T* osrc = dots ? reinterpret_cast<const T*>(a.o_swa) + hoff : nullptr;
   const float* g = a.g + (SG ? (size_t)bh * L : hoff);
   const T* states = reinterpret_cast<const T*>(a.states) + (size_t)bh * NC * D * D;
   T* out = reinterpret_cast<T*>(a.out) + (size_t)bh * NC * D * D;
@@ -172,6 +177,12 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
         const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
         s.rs[u] = (c + 1 < NC) ? ldg16(states + ((size_t)(c + 1) * D + i0 + row) * D + cv * VEC) : zero16();
       }
+      if (dots)
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+          if (u % NTI == it) s.ro[u] = ldg16(osrc + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
+        }
     }
   };
 
@@ -208,6 +219,21 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
       const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
       *reinterpret_cast<V16*>(sB + row * LDB + cv * VEC) = s.rb[u];
       if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDB + cv * VEC) = s.rs[u];
+    }
+    if (REV && dots) {
+      // delta_t = mix * dO_t . o_swa_t, formed before this stage's registers take chunk n + 2;
+      // a row's D/VEC vectors sit in consecutive lanes
+      const int t0 = c * CHUNK;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        if (u % NTI != it) continue;
+        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dot += v16_get(s.rb[u], e, (T*)nullptr) * v16_get(s.ro[u], e, (T*)nullptr);
+        dot = group_sum<D / VEC>(dot);
+        if (cv == 0 && t0 + row < L) a.delta[(size_t)bh * L + t0 + row] = a.mix * dot;
+      }
     }
     if (jt == 0) {
       // chunk-local inclusive prefix b of the gates and the chunk total Gamma

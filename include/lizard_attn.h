@@ -138,11 +138,11 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
  *                              caller-created events that are recorded on
  *                              `stream` before the first, between consecutive
  *                              and after the last of the backward's kernels
- *                              (row dots, state-gradient sweep, chunk
- *                              gradients, meta reduction; a stage with nothing
- *                              to do still gets its event).  For L = 0 they are
- *                              not recorded. */
-#define LIZARD_BWD_STAGES 4
+ *                              (state-gradient sweep with the window row
+ *                              dots, chunk gradients, meta reduction; a stage
+ *                              with nothing to do still gets its event).  For
+ *                              L = 0 they are not recorded. */
+#define LIZARD_BWD_STAGES 3
 lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 const void* q, const void* k, const void* v, const float* g,
                                 const void* meta_k, const void* meta_v, const void* dO,
