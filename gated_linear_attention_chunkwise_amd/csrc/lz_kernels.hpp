@@ -29,7 +29,7 @@ struct BwdArgs {
   void* workspace;      // bwd_workspace_bytes() bytes, carved up by launch_bwd
   float* ws_delta;      // set by launch_bwd: [B,H,L] fp32, D_t = mix * dO_t . o_swa_t
   float* ws_dmeta;      // set by launch_bwd: [B*NC, H, M, 2*d] fp32 meta partials per (b, chunk)
-  hipEvent_t* stage_events;   // optional: 5 events recorded around the 4 kernels
+  hipEvent_t* stage_events;   // optional: 4 events recorded around the 3 stages
   int B, H, L, W, M;
   float scale, mix;
   int gate;             // as in FwdArgs; dg has the shape of g
@@ -56,8 +56,9 @@ struct SweepArgs {
   int NS, SC;
   float* seg_in; float* seg_fin; float* seg_gtot;
   int gate;             // as in FwdArgs
-  // backward: with delta set, the workgroups of state rows 0..63 also form the window
-  // row dots delta_t = mix * dO_t . o_swa_t [B,H,L] fp32 from the dO rows they stream
+  // backward: with delta set, the row blocks of each head also form the window row dots
+  // delta_t = mix * dO_t . o_swa_t [B,H,L] fp32 from the dO rows they stream (each block a
+  // share of the token rows)
   const void* o_swa; float* delta; float mix;
 };
 
