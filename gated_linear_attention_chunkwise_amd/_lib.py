@@ -21,7 +21,8 @@ LIZARD_FP32, LIZARD_BF16 = 0, 1
 OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE = 0, 1, 2, 3
 GATE_PER_DIM, GATE_SCALAR = 0, 1
 SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
-           "lizard_attn_workspace_bytes", "lizard_attn_status_string")
+           "lizard_attn_workspace_bytes", "lizard_attn_status_string", "lizard_gate_proj_fwd",
+           "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes")
 
 
 class Shape(ctypes.Structure):
@@ -62,6 +63,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_continue.restype = I32
     lib.lizard_attn_workspace_bytes.argtypes = [SP, ctypes.c_int]
     lib.lizard_attn_workspace_bytes.restype = SZ
+    lib.lizard_gate_proj_fwd.argtypes = [SP, I32, F, P, P, P, P]
+    lib.lizard_gate_proj_fwd.restype = I32
+    lib.lizard_gate_proj_bwd.argtypes = [SP, I32, F, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_gate_proj_bwd.restype = I32
+    lib.lizard_gate_proj_workspace_bytes.argtypes = [SP, I32]
+    lib.lizard_gate_proj_workspace_bytes.restype = SZ
     lib.lizard_attn_status_string.argtypes = [I32]
     lib.lizard_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -299,6 +306,62 @@ def lizard_attn_fwd_continue(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, 
     return o
 
 
+def _gate_shape(x, w, heads, d_k, scalar):
+    B, L, Dm = x.shape
+    ng = heads if scalar else heads * d_k
+    if tuple(w.shape) != (ng, Dm):
+        raise ValueError(f"w must have shape ({ng}, {Dm}), got {tuple(w.shape)}")
+    return make_shape(B, heads, L, d_k, 1, 0, 1.0, 1.0, x.dtype,
+                      gate=GATE_SCALAR if scalar else GATE_PER_DIM), Dm
+
+
+def lizard_gate_proj_fwd(x, w, *, heads: int, d_k: int, tau: float = 1.0, scalar: bool = False):
+    """g = log sigmoid(x w^T) / tau in the layer's gate layout: x [B,L,d_model], w [Ng,d_model]
+    (Ng = heads*d_k, or heads for the scalar gate), both bf16 or fp32; returns g fp32
+    [B,heads,L,d_k] or [B,heads,L]."""
+    lib = load()
+    dt, dev = x.dtype, x.device
+    _need(x, "x", dt, dev)
+    _need(w, "w", dt, dev)
+    s, Dm = _gate_shape(x, w, heads, d_k, scalar)
+    B, L = x.shape[0], x.shape[1]
+    g = torch.empty((B, heads, L) if scalar else (B, heads, L, d_k), device=dev, dtype=torch.float32)
+    _check(lib.lizard_gate_proj_fwd(ctypes.byref(s), Dm, float(tau), _ptr(x), _ptr(w), _ptr(g), _stream(dev)))
+    return g
+
+
+def lizard_gate_proj_bwd(x, w, g, dg, *, heads: int, d_k: int, tau: float = 1.0, scalar: bool = False,
+                         workspace=None):
+    """Gradients (dx [B,L,d_model] in x's dtype, dw [Ng,d_model] fp32) of sum(dg * g) for
+    g = lizard_gate_proj_fwd(x, w, ...); g is that forward's output."""
+    lib = load()
+    dt, dev = x.dtype, x.device
+    _need(x, "x", dt, dev)
+    _need(w, "w", dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(dg, "dg", torch.float32, dev)
+    s, Dm = _gate_shape(x, w, heads, d_k, scalar)
+    if tuple(g.shape) != tuple(dg.shape):
+        raise ValueError("g and dg must share one shape")
+    n = int(lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), Dm))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    dx = torch.empty_like(x)
+    dw = torch.empty(w.shape, device=dev, dtype=torch.float32)
+    _check(lib.lizard_gate_proj_bwd(ctypes.byref(s), Dm, float(tau), _ptr(x), _ptr(w), _ptr(g), _ptr(dg),
+                                    _ptr(dx), _ptr(dw), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dx, dw
+
+
+def gate_proj_workspace(x_shape, heads: int, d_k: int, dtype, device, scalar: bool = False) -> torch.Tensor:
+    """Workspace for lizard_gate_proj_bwd at this shape (reusable across calls)."""
+    B, L, Dm = x_shape
+    s = make_shape(B, heads, L, d_k, 1, 0, 1.0, 1.0, dtype, gate=GATE_SCALAR if scalar else GATE_PER_DIM)
+    n = int(load().lizard_gate_proj_workspace_bytes(ctypes.byref(s), Dm))
+    return torch.empty(max(n, 1), device=device, dtype=torch.uint8)
+
+
 def workspace_bytes(shape: Shape, op: int) -> int:
     return int(load().lizard_attn_workspace_bytes(ctypes.byref(shape), op))
 
@@ -308,3 +371,5 @@ fwd = lizard_attn_fwd
 bwd = lizard_attn_bwd
 decode_step = lizard_attn_decode_step
 fwd_continue = lizard_attn_fwd_continue
+gate_proj_fwd = lizard_gate_proj_fwd
+gate_proj_bwd = lizard_gate_proj_bwd

@@ -58,6 +58,22 @@ lizard_status_t check_ptrs(std::initializer_list<const void*> required,
   return LIZARD_OK;
 }
 
+// Shape checks of the gate projection (B, H, L, d_k, dtype, gate and d_model only).
+lizard_status_t check_gate_shape(const lizard_attn_shape_t* s, int32_t d_model, float tau) {
+  if (s == nullptr) return LIZARD_EINVAL;
+  if (s->B < 1 || s->H < 1 || s->L < 0 || s->d_k < 1 || d_model < 1) return LIZARD_EINVAL;
+  if (!isfinite(tau) || !(tau > 0.f)) return LIZARD_EINVAL;
+  if (s->dtype != LIZARD_FP32 && s->dtype != LIZARD_BF16) return LIZARD_EUNSUPPORTED;
+  if (s->gate != LIZARD_GATE_PER_DIM && s->gate != LIZARD_GATE_SCALAR) return LIZARD_EUNSUPPORTED;
+  if (s->d_k != 64 && s->d_k != 128) return LIZARD_EUNSUPPORTED;
+  if (d_model % 32 != 0 || d_model > 65536) return LIZARD_EUNSUPPORTED;
+  const double ng = s->gate == LIZARD_GATE_SCALAR ? (double)s->H : (double)s->H * s->d_k;
+  const double tokens = (double)s->B * s->L;
+  if (tokens * (ng > d_model ? ng : d_model) >= 2147483648.0) return LIZARD_EUNSUPPORTED;
+  if (ng * d_model >= 2147483648.0) return LIZARD_EUNSUPPORTED;
+  return LIZARD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,6 +200,39 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
   lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
                    reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate};
   return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_gate_proj_fwd(const lizard_attn_shape_t* s, int32_t d_model, float tau,
+                                     const void* x, const void* w, float* g, hipStream_t stream) {
+  lizard_status_t st = check_gate_shape(s, d_model, tau);
+  if (st != LIZARD_OK) return st;
+  st = s->L > 0 ? check_ptrs({x, w, g}, {}) : check_ptrs({w}, {x, g});
+  if (st != LIZARD_OK) return st;
+  if (s->L == 0) return LIZARD_OK;
+  lz::GateArgs a{x, w, g, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->d_k,
+                 s->gate == LIZARD_GATE_SCALAR ? 1 : 0, d_model, tau};
+  return lz::launch_gate_fwd(a, s->dtype, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+size_t lizard_gate_proj_workspace_bytes(const lizard_attn_shape_t* s, int32_t d_model) {
+  if (check_gate_shape(s, d_model, 1.f) != LIZARD_OK || s->L == 0) return 0;
+  return lz::gate_bwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->gate == LIZARD_GATE_SCALAR ? 1 : 0, d_model,
+                                      s->dtype);
+}
+
+lizard_status_t lizard_gate_proj_bwd(const lizard_attn_shape_t* s, int32_t d_model, float tau,
+                                     const void* x, const void* w, const float* g, const float* dg,
+                                     void* dx, float* dw, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  lizard_status_t st = check_gate_shape(s, d_model, tau);
+  if (st != LIZARD_OK) return st;
+  st = s->L > 0 ? check_ptrs({x, w, g, dg, dx, dw}, {workspace}) : check_ptrs({w, dw}, {x, g, dg, dx, workspace});
+  if (st != LIZARD_OK) return st;
+  const size_t need = lizard_gate_proj_workspace_bytes(s, d_model);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
+  lz::GateArgs a{x, w, const_cast<float*>(g), dg, dx, dw, workspace, s->B, s->H, s->L, s->d_k,
+                 s->gate == LIZARD_GATE_SCALAR ? 1 : 0, d_model, tau};
+  return lz::launch_gate_bwd(a, s->dtype, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
 }  // extern "C"

@@ -72,6 +72,17 @@ struct DecodeArgs {
   int gate;             // 0: g [B,H,d]; 1: g [B,H]
 };
 
+// Gate projection (lz_gate.hip).  Forward: g (output) = log sigmoid(x W^T) / tau in the gate
+// layout.  Backward: g is the forward's output (input), dg its gradient; writes dx and dw.
+struct GateArgs {
+  const void* x; const void* w;   // x [B*L][d_model], w [Ng][d_model]; Ng = H*dk, or H when sg
+  float* g; const float* dg;
+  void* dx; float* dw;
+  void* workspace;                // backward: gate_bwd_workspace_bytes()
+  int B, H, L, dk, sg, d_model;
+  float tau;
+};
+
 // Each returns hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st);
@@ -79,6 +90,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
 // Segment forward resuming from (state_in, ring, pos): launch_fwd, then the ring and pos advance.
 hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st);
+hipError_t launch_gate_fwd(const GateArgs& a, int dtype, hipStream_t st);
+hipError_t launch_gate_bwd(const GateArgs& a, int dtype, hipStream_t st);   // L = 0: dw = 0
 
 // Segments of the forward sweep for this shape (sequence parallelism when B*H is small).
 int sweep_segments(int B, int H, int L, int D);
@@ -88,6 +101,9 @@ size_t fwd_segment_bytes(int B, int H, int L, int D);
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype);
 // Workspace bytes needed by launch_decode.
 size_t decode_workspace_bytes(int B, int H, int D);
+// Workspace bytes needed by launch_gate_bwd: dz [B*L][Ng rounded up to 16 bytes] in the operand
+// dtype, then the fp32 partial sums of dW when its contraction over tokens is split.
+size_t gate_bwd_workspace_bytes(int B, int H, int L, int dk, int sg, int d_model, int dtype);
 // Workspace bytes needed by launch_bwd.
 size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
 

@@ -25,6 +25,13 @@ Recipe (numpy ``default_rng(seed)``, draw order q, k, v, x, meta_k, dO):
 For bf16 workloads q, k, v, meta_k and dO are rounded to bf16 (round to
 nearest even) and handed out as float32 arrays that hold exactly those bf16
 values, so the oracle sees the very numbers the GPU sees; g stays fp32.
+
+Gate-projection inputs (``make_gate_small`` / ``make_gate_device``, draw order
+x, w, dg): the layer input x ~ N(0, 1) [B, L, d_model]; the gate weight
+w ~ N(0, 1) / sqrt(d_model) [Ng, d_model], so that every pre-activation is
+about N(0, 1) like the gate input of the recipe above; dg ~ N(0, 1) in the
+gate layout.  The train-shaped case is d_model = 4096 (the 8B-shaped layer
+with H = 32 heads of d = 128): Ng = 4096 per key dimension, 32 scalar.
 """
 from __future__ import annotations
 
@@ -127,6 +134,30 @@ def make_small(B: int, H: int, L: int, D: int, M: int, *, seed: int, bf16: bool,
             if name in out:
                 out[name] = round_to_bf16(out[name])
     return out
+
+
+def make_gate_small(B: int, L: int, d_model: int, ng: int, dg_shape, *, seed: int, bf16: bool) -> dict:
+    """Gate-projection inputs at small sizes (x and w bf16-rounded when bf16)."""
+    rng = np.random.default_rng(seed)
+    out = {"x": rng.standard_normal((B, L, d_model)).astype(np.float32),
+           "w": (rng.standard_normal((ng, d_model)) / np.sqrt(d_model)).astype(np.float32),
+           "dg": rng.standard_normal(tuple(dg_shape)).astype(np.float32)}
+    if bf16:
+        out["x"] = round_to_bf16(out["x"])
+        out["w"] = round_to_bf16(out["w"])
+    return out
+
+
+def make_gate_device(B: int, L: int, d_model: int, ng: int, dg_shape, *, seed: int, device, dtype) -> dict:
+    """The same recipe drawn on the device with a seeded torch generator."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn((B, L, d_model), generator=gen, device=device, dtype=torch.float32).to(dtype)
+    w = (torch.randn((ng, d_model), generator=gen, device=device, dtype=torch.float32) /
+         float(np.sqrt(d_model))).to(dtype)
+    dg = torch.randn(tuple(dg_shape), generator=gen, device=device, dtype=torch.float32)
+    return {"x": x, "w": w, "dg": dg}
 
 
 def make_inputs_device(w: Workload, device, *, with_grad: bool = False, L: int | None = None,

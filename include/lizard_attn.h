@@ -205,6 +205,49 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* Gate projection: the learnable gating module Gamma_t = sigmoid(W x_t)
+ * (English page §2.A "Adaptive Memory Control"; Chinese page §2.1), produced
+ * in log space for the layer (English page §2.C):
+ *
+ *   g = log sigmoid(x W^T) / tau
+ *
+ *   s        uses B, H, L, d_k, dtype and gate; the number of gate rows is
+ *            Ng = H*d_k (LIZARD_GATE_PER_DIM) or Ng = H (LIZARD_GATE_SCALAR)
+ *   d_model  width of x and W: a multiple of 32 in [32, 65536]
+ *   tau      temperature, finite and > 0 (1 is the pages' gate; larger values
+ *            slow the decay)
+ *   x        [B,L,d_model] dtype, the layer input
+ *   w        [Ng,d_model] dtype; row h*d_k + i gives gate dimension i of head h
+ *            (row h for the scalar gate)
+ *   g        written: fp32 in the layer's gate layout, [B,H,L,d_k] or [B,H,L]
+ * One launch: an MFMA matrix product whose epilogue applies the log-sigmoid
+ * and the temperature and writes the gate layout directly.  Sizes beyond the
+ * supported set (d_k in {64, 128}, B*L*max(Ng, d_model) below 2^31 elements)
+ * return LIZARD_EUNSUPPORTED; L = 0 writes nothing. */
+lizard_status_t lizard_gate_proj_fwd(const lizard_attn_shape_t* s, int32_t d_model, float tau,
+                                     const void* x, const void* w, float* g, hipStream_t stream);
+
+/* Device workspace bytes that lizard_gate_proj_bwd needs (0 for an invalid shape). */
+size_t lizard_gate_proj_workspace_bytes(const lizard_attn_shape_t* s, int32_t d_model);
+
+/* Backward of the gate projection (the exact derivative; the pages give none):
+ * with dz = dg * (1 - sigmoid(z)) / tau = -dg * expm1(tau*g) / tau,
+ *   dx = dz W   written, [B,L,d_model] dtype (not accumulated)
+ *   dw = dz^T x written, [Ng,d_model] fp32, summed over batch and tokens in a
+ *               fixed order (deterministic)
+ *   g           the forward's output for the same x and w; dg its gradient,
+ *               both fp32 in the gate layout
+ *   workspace   lizard_gate_proj_workspace_bytes(s, d_model) bytes of
+ *               caller-owned device memory, clobbered (dz in the operand dtype,
+ *               then partial sums of dw)
+ * Launches: the dz pass, the dx product, the dw product (split over tokens
+ * when Ng*d_model alone gives too few tiles) and, when split, the sum of the
+ * splits.  L = 0 writes dw = 0. */
+lizard_status_t lizard_gate_proj_bwd(const lizard_attn_shape_t* s, int32_t d_model, float tau,
+                                     const void* x, const void* w, const float* g, const float* dg,
+                                     void* dx, float* dw, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Static description of a status code. */
 const char* lizard_attn_status_string(lizard_status_t st);
 

@@ -17,7 +17,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = range(6)
 
 def declared_functions():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_attn_[a-z_]+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_(?:attn|gate)_[a-z_]+)\s*\(", txt, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
                           "lizard_attn_fwd_continue", "lizard_attn_workspace_bytes",
-                          "lizard_attn_status_string"}
+                          "lizard_attn_status_string", "lizard_gate_proj_fwd", "lizard_gate_proj_bwd",
+                          "lizard_gate_proj_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(pkg.SYMBOLS) == set(names)
@@ -153,3 +154,44 @@ def test_workspace_query(lib):
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(d_k=96, d_v=96)), 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 0) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 5) == 0
+
+
+def test_gate_proj_validation(lib):
+    F = ctypes.c_float
+    def fwdc(s, d_model=256, tau=1.0, x=GOOD, w=GOOD, g=GOOD):
+        return lib.lizard_gate_proj_fwd(ctypes.byref(s), d_model, F(tau), x, w, g, None)
+    def bwdc(s, d_model=256, tau=1.0, dx=GOOD, dw=GOOD, ws=GOOD, ws_bytes=1 << 40):
+        return lib.lizard_gate_proj_bwd(ctypes.byref(s), d_model, F(tau), GOOD, GOOD, GOOD, GOOD, dx, dw, ws,
+                                        ws_bytes, None)
+    s = shape()
+    assert lib.lizard_gate_proj_fwd(None, 256, F(1.0), GOOD, GOOD, GOOD, None) == EINVAL
+    assert fwdc(s, tau=0.0) == EINVAL
+    assert fwdc(s, tau=float("inf")) == EINVAL
+    assert fwdc(s, d_model=0) == EINVAL
+    assert fwdc(s, d_model=100) == EUNSUPPORTED
+    assert fwdc(s, d_model=65568) == EUNSUPPORTED
+    assert fwdc(shape(d_k=96, d_v=96)) == EUNSUPPORTED
+    assert fwdc(shape(gate=2)) == EUNSUPPORTED
+    assert fwdc(shape(dtype=5)) == EUNSUPPORTED
+    assert fwdc(shape(B=4, H=32, L=1 << 20)) == EUNSUPPORTED      # 2^22 tokens x 4096 gate rows
+    assert fwdc(s, x=None) == EINVAL
+    assert fwdc(s, g=BAD) == EALIGN
+    assert bwdc(s, dx=None) == EINVAL
+    assert bwdc(s, dw=BAD) == EALIGN
+    need = lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), 256)
+    assert need > 0
+    assert bwdc(s, ws=None) == EWORKSPACE
+    assert bwdc(s, ws_bytes=need - 1) == EWORKSPACE
+    # L = 0: the forward writes nothing and accepts absent token tensors
+    assert lib.lizard_gate_proj_fwd(ctypes.byref(shape(L=0)), 256, F(1.0), None, GOOD, None, None) == OK
+
+
+def test_gate_proj_workspace_sizes(lib):
+    # dz [tokens][Ng rounded up to 16 bytes] in the operand dtype (256-byte aligned), then fp32
+    # partials of dw when its contraction over tokens is split
+    s = shape(B=1, H=2, L=128, d_k=128, d_v=128, dtype=1, gate=0)      # Ng = 256, 4 output tiles
+    assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), 256) == 128 * 256 * 2 + 4 * 256 * 256 * 4
+    s = shape(B=1, H=2, L=128, d_k=128, d_v=128, dtype=1, gate=1)      # Ng = 2 (padded to 8), one split
+    assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), 256) == 128 * 8 * 2
+    assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(shape(L=0)), 256) == 0
+    assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), 100) == 0
