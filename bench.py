@@ -9,7 +9,9 @@ HBM.  The constant-memory decode step is measured in the same run on its own
 workload (B=64 sequences after a 4096-token prefill) and reported under
 "decode"; the 65 536-token prefill, one shot and as continued segments, under
 "prefill"; the training step with one gate per head and token under
-"scalar_gate".  Prints one JSON line.
+"scalar_gate"; the gate projection g = log sigmoid(x W^T)/tau that feeds
+the layer, per key dimension and scalar, under "gate_proj".  Prints one
+JSON line.
 
 Per-kernel times come from HIP events recorded on the stream the kernels
 run on; the backward records them between its kernels through the
@@ -328,6 +330,67 @@ def bench_prefill(args, hip, torch, lib):
                          "algorithmic_bytes": alg}}
 
 
+def bench_gate_proj(args, hip, torch, lib):
+    """The gate projection g = log sigmoid(x W^T)/16 at the train shape (d_model = 4096 for H = 32
+    heads of d = 128), forward + backward, per key dimension (Ng = 4096) and scalar (Ng = 32)."""
+    from gated_linear_attention_chunkwise_amd.inputs import make_gate_device
+    B, L, Dm, H, dk, tau = 4, 8192, 4096, 32, 128, 16.0
+    T = B * L
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"workload": f"gate projection at train_8k: x [{B},{L},{Dm}] bf16, W [Ng,{Dm}] bf16, tau {tau:g}; "
+                       "forward + backward (dz pass, dx = dz W, dW = dz^T x)"}
+    for scalar in (False, True):
+        ng = H if scalar else H * dk
+        gshape = (B, H, L) if scalar else (B, H, L, dk)
+        t = make_gate_device(B, L, Dm, ng, gshape, seed=77, device="cuda", dtype=torch.bfloat16)
+        ws = lib.gate_proj_workspace((B, L, Dm), H, dk, torch.bfloat16, "cuda", scalar=scalar)
+        g = lib.lizard_gate_proj_fwd(t["x"], t["w"], heads=H, d_k=dk, tau=tau, scalar=scalar)
+
+        def fwd():
+            return lib.lizard_gate_proj_fwd(t["x"], t["w"], heads=H, d_k=dk, tau=tau, scalar=scalar)
+
+        def bwd():
+            return lib.lizard_gate_proj_bwd(t["x"], t["w"], g, t["dg"], heads=H, d_k=dk, tau=tau,
+                                            scalar=scalar, workspace=ws)
+        for _ in range(2):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        n = max(2, min(args.steps, 10))
+        e = [hip.event() for _ in range(3)]
+        hip.record(e[0], stream)
+        for _ in range(n):
+            fwd()
+        hip.record(e[1], stream)
+        for _ in range(n):
+            bwd()
+        hip.record(e[2], stream)
+        torch.cuda.synchronize()
+        tf, tb = hip.ms(e[0], e[1]) / n, hip.ms(e[1], e[2]) / n
+        flop_f = 2.0 * T * Dm * ng
+        # compulsory bytes: forward x, W in, g out; backward x, W, g, dg in, dx, dW out
+        bytes_f = T * Dm * 2 + ng * Dm * 2 + T * ng * 4
+        bytes_b = T * Dm * 2 + ng * Dm * 2 + 2 * T * ng * 4 + T * Dm * 2 + ng * Dm * 4
+        rec = {"Ng": ng, "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+               "tokens_per_s": round(T / ((tf + tb) * 1e-3), 1)}
+        if scalar:
+            gbs = (bytes_f + bytes_b) / ((tf + tb) * 1e-3) / 1e9
+            rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                               "kernel": "gate projection forward + backward (skinny products, bound by x and dx)",
+                               "algorithmic_bytes": bytes_f + bytes_b}
+        else:
+            tfs = 3 * flop_f / ((tf + tb) * 1e-3) / 1e12
+            rec["roofline"] = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(tfs / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                               "kernel": "gate projection forward + backward (three bf16 products of 2*T*d_model*Ng)",
+                               "algorithmic_flop": 3 * flop_f}
+        out["scalar" if scalar else "per_dim"] = rec
+        del t, ws, g
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +399,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-scalar-gate", action="store_true")
+    ap.add_argument("--no-gate-proj", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
@@ -382,6 +446,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill:
         rec["prefill"] = bench_prefill(args, hip, torch, lib)
+        torch.cuda.empty_cache()
+    if not args.no_gate_proj:
+        rec["gate_proj"] = bench_gate_proj(args, hip, torch, lib)
     print(json.dumps(rec), flush=True)
 
 

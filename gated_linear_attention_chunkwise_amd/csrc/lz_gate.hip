@@ -44,9 +44,17 @@ struct GemmArgs {
   float* g; int B, H, L, dk, sg; float tau;   // EPI_GATE: rows are tokens, columns gate rows n
 };
 
+// Row padding (elements) of an LDS operand tile.  Tiles read with 16-byte rows of
+// fragments (contraction index along the row) take 16 bytes; tiles read with the
+// transpose read (four rows of 32 bytes per 16 lanes) take 32 bytes, so the four rows
+// of one read start 8 banks apart.
+template <typename T, bool KC>
+constexpr int tile_pad() { return sizeof(T) == 2 ? (KC ? 8 : 16) : 4; }
+
 // One operand tile: R rows x C contiguous columns of a row-major source, held
-// in registers as 16-byte vectors between its global load and its LDS store.
-template <typename T, int R, int C, int NT>
+// in registers as 16-byte vectors between its global load and its LDS store
+// (rows of C + PAD elements).
+template <typename T, int R, int C, int NT, int PAD>
 struct TileLd {
   static constexpr int VEC = Tr<T>::VEC;
   static constexpr int NV = R * C / VEC / NT;
@@ -69,29 +77,49 @@ struct TileLd {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int idx = tid + u * NT, r = idx / (C / VEC), c = (idx % (C / VEC)) * VEC;
-      *reinterpret_cast<V16*>(lds + r * (C + Tr<T>::PAD) + c) = ((ok >> u) & 1u) ? v[u] : zero16();
+      *reinterpret_cast<V16*>(lds + r * (C + PAD) + c) = ((ok >> u) & 1u) ? v[u] : zero16();
     }
   }
 };
 
-__device__ __forceinline__ float log_sigmoid(float z) { return fminf(z, 0.f) - log1pf(expf(-fabsf(z))); }
+// log sigmoid(z) = min(z, 0) - log1p(exp(-|z|)), short enough to unroll over a whole
+// accumulator tile: exp and log from the base-2 hardware instructions, and log1p(u) as
+// log(w) * u / (w - 1) with w = 1 + u, which cancels the rounding of w (Goldberg, "What
+// every computer scientist should know about floating-point arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float log_sigmoid(float z) {
+  const float u = __builtin_amdgcn_exp2f(-fabsf(z) * 1.44269504088896341f);   // in (0, 1]
+  const float w = 1.f + u;
+  const float l = w == 1.f ? u : __builtin_amdgcn_logf(w) * 0.693147180559945309f * (u * __builtin_amdgcn_rcpf(w - 1.f));
+  return fminf(z, 0.f) - l;
+}
 
 // C[M][N] = sum_k A[m][k] B[k][n] over this workgroup's split of k.
 // WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN) block of C in 16 x 16 MFMA tiles.
 template <typename T, bool AKC, bool BKC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
+struct GemmShape {
+  static constexpr int PA = tile_pad<T, AKC>(), PB = tile_pad<T, BKC>();
+  // LDS tiles: [rows][cols + pad] with the source's contiguous direction along the rows
+  static constexpr int AR = AKC ? BM : BK, AC = AKC ? BK : BM;
+  static constexpr int BR = BKC ? BN : BK, BC = BKC ? BK : BN;
+  static constexpr int A_ELEMS = AR * (AC + PA), B_ELEMS = BR * (BC + PB);
+  static constexpr size_t lds_bytes = 2 * sizeof(T) * (size_t)(A_ELEMS + B_ELEMS);   // two stages
+};
+
+// C[M][N] = sum_k A[m][k] B[k][n] over this workgroup's split of k.
+// WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN) block of C in 16 x 16 MFMA tiles.
+// Two LDS stages: the tiles of step k+1 are loaded to registers while step k is
+// multiplied from one stage, then stored to the other; one barrier per step.
+template <typename T, bool AKC, bool BKC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
+  using SH = GemmShape<T, AKC, BKC, EPI, BM, BN, BK, WGM, WGN>;
   constexpr int NT = 64 * WGM * WGN;
   constexpr int TM = BM / WGM, TN = BN / WGN, MB = TM / 16, NB = TN / 16;
-  constexpr int PAD = Tr<T>::PAD;
-  // LDS tiles: [rows][cols + PAD] with the source's contiguous direction along the rows
-  constexpr int AR = AKC ? BM : BK, AC = AKC ? BK : BM;
-  constexpr int BR = BKC ? BN : BK, BC = BKC ? BK : BN;
+  constexpr int AR = SH::AR, AC = SH::AC, BR = SH::BR, BC = SH::BC, PA = SH::PA, PB = SH::PB;
   static_assert(BK % 32 == 0 && TM % 16 == 0 && TN % 16 == 0, "tile shape");
   using FragT = typename Tr<T>::frag;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  T* sA = reinterpret_cast<T*>(smem);
-  T* sB = sA + AR * (AC + PAD);
+  T* const lds = reinterpret_cast<T*>(smem);   // stage s: A at s * (A + B) elements, then B
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kg = lane >> 4;
   const int wm0 = (wave / WGN) * TM, wn0 = (wave % WGN) * TN;
@@ -107,13 +135,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
 
   const T* Ag = reinterpret_cast<const T*>(a.A);
   const T* Bg = reinterpret_cast<const T*>(a.Bm);
-  TileLd<T, AR, AC, NT> ta;
-  TileLd<T, BR, BC, NT> tb;
+  TileLd<T, AR, AC, NT, PA> ta;
+  TileLd<T, BR, BC, NT, PB> tb;
   auto load = [&](int k0) {
     if (AKC) ta.load(Ag, a.lda, m0, k0, a.a_rows, a.a_cols, tid);
     else     ta.load(Ag, a.lda, k0, m0, a.a_rows, a.a_cols, tid);
     if (BKC) tb.load(Bg, a.ldb, n0, k0, a.b_rows, a.b_cols, tid);
     else     tb.load(Bg, a.ldb, k0, n0, a.b_rows, a.b_cols, tid);
+  };
+  auto store = [&](int stage) {
+    T* sa = lds + stage * (SH::A_ELEMS + SH::B_ELEMS);
+    ta.store(sa, tid);
+    tb.store(sa + SH::A_ELEMS, tid);
   };
 
   f32x4 acc[MB][NB];
@@ -124,68 +157,95 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
 
   if (kbeg < kend) {
     load(kbeg);
-    ta.store(sA, tid);
-    tb.store(sB, tid);
+    store(0);
     __syncthreads();
   }
+  int stage = 0;
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
     if (more) load(k0 + BK);   // next tiles in flight while this one is multiplied
+    const T* sA = lds + stage * (SH::A_ELEMS + SH::B_ELEMS);
+    const T* sB = sA + SH::A_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int kk = 32 * ks + 8 * kg;
       FragT fa[MB], fb[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
-        if constexpr (AKC) fa[i] = ld_frag(sA, AC + PAD, wm0 + 16 * i + r, kk);
-        else               fa[i] = ld_frag_tr(sA, AC + PAD, kk, kk + 4, wm0 + 16 * i, lane);
+        if constexpr (AKC) fa[i] = ld_frag(sA, AC + PA, wm0 + 16 * i + r, kk);
+        else               fa[i] = ld_frag_tr(sA, AC + PA, kk, kk + 4, wm0 + 16 * i, lane);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        if constexpr (BKC) fb[j] = ld_frag(sB, BC + PAD, wn0 + 16 * j + r, kk);
-        else               fb[j] = ld_frag_tr(sB, BC + PAD, kk, kk + 4, wn0 + 16 * j, lane);
+        if constexpr (BKC) fb[j] = ld_frag(sB, BC + PB, wn0 + 16 * j + r, kk);
+        else               fb[j] = ld_frag_tr(sB, BC + PB, kk, kk + 4, wn0 + 16 * j, lane);
       }
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) mma32(acc[i][j], fa[i], fb[j]);
+        for (int j = 0; j < NB; ++j) mma32(acc[i][j], fb[j], fa[i]);   // C^T blocks: lanes hold row runs of C
     }
-    if (more) {
-      __syncthreads();
-      ta.store(sA, tid);
-      tb.store(sB, tid);
-      __syncthreads();
-    }
+    if (more) store(stage ^ 1);   // that stage was last read before the previous barrier
+    __syncthreads();
+    stage ^= 1;
   }
 
-  // epilogue: lane holds C[m0 + wm0 + 16 i + 4 kg + e][n0 + wn0 + 16 j + r]
+  // epilogue: the blocks were formed transposed, so lane holds C[m][n .. n+3] with
+  // m = m0 + wm0 + 16 i + r, n = n0 + wn0 + 16 j + 4 kg (four consecutive columns)
+  if constexpr (EPI == EPI_GATE) {
+    // m = token b*L + t, n = gate row; the gate offset splits into a row part and a column
+    // part: per key dimension ((b*H*L + t) * dk) + (h*L*dk + i) with n = h*dk + i (the four
+    // columns are four consecutive i of one head), scalar (b*H*L + t) + n*L
+    const float inv_tau = 1.f / a.tau;
+    size_t colp[NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + wn0 + 16 * j + 4 * kg;
+      const int h = a.sg ? n : n / a.dk;
+      colp[j] = a.sg ? (size_t)n * a.L : (size_t)h * a.L * a.dk + (n - h * a.dk);
+    }
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm0 + 16 * i + r;
+      if (m >= a.M) continue;
+      const int b = m / a.L, t = m - b * a.L;
+      const size_t rowp = ((size_t)b * a.H * a.L + t) * (a.sg ? 1 : a.dk);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm0 + 16 * i + 4 * kg + e, n = n0 + wn0 + 16 * j + r;
-        if (m >= a.M || n >= a.N) continue;
-        const float z = acc[i][j][e];
-        if constexpr (EPI == EPI_GATE) {
-          // m = token b*L + t, n = gate row (h*dk + i, or h)
-          const int b = m / a.L, t = m - b * a.L;
-          size_t off;
-          if (a.sg) {
-            off = ((size_t)b * a.H + n) * a.L + t;
-          } else {
-            const int h = n / a.dk, ii = n - h * a.dk;
-            off = (((size_t)b * a.H + h) * a.L + t) * a.dk + ii;
-          }
-          a.g[off] = log_sigmoid(z) / a.tau;
-        } else if constexpr (EPI == EPI_STORE) {
-          reinterpret_cast<T*>(a.C)[(size_t)m * a.ldc + n] = Tr<T>::from_f(z);
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + wn0 + 16 * j + 4 * kg;
+        const f32x4 v = acc[i][j];
+        if (!a.sg) {
+          if (n < a.N)   // N = H*dk is a multiple of 4
+            *reinterpret_cast<f32x4*>(a.g + rowp + colp[j]) =
+                f32x4{log_sigmoid(v[0]) * inv_tau, log_sigmoid(v[1]) * inv_tau, log_sigmoid(v[2]) * inv_tau,
+                      log_sigmoid(v[3]) * inv_tau};
         } else {
-          float* out = reinterpret_cast<float*>(a.C) + (a.ksplit > 1 ? (size_t)split * a.M * a.ldc : 0);
-          out[(size_t)m * a.ldc + n] = z;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.N) a.g[rowp + colp[j] + (size_t)e * a.L] = log_sigmoid(v[e]) * inv_tau;
         }
       }
+    }
+  } else {
+    // N is d_model, a multiple of 32: the four columns are all in range together
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm0 + 16 * i + r;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + wn0 + 16 * j + 4 * kg;
+        if (n >= a.N) continue;
+        const f32x4 v = acc[i][j];
+        if constexpr (EPI == EPI_STORE) {
+          st4(reinterpret_cast<T*>(a.C) + (size_t)m * a.ldc + n, v[0], v[1], v[2], v[3]);
+        } else {
+          float* out = reinterpret_cast<float*>(a.C) + (a.ksplit > 1 ? (size_t)split * a.M * a.ldc : 0);
+          *reinterpret_cast<f32x4*>(out + (size_t)m * a.ldc + n) = v;
+        }
+      }
+    }
+  }
 }
 
 // dz[t][n] = -dg * expm1(tau * g) / tau, token-major with leading dimension ldz (Ng rounded
@@ -249,10 +309,8 @@ __global__ __launch_bounds__(256) void zero4_kernel(float* __restrict__ out, siz
 
 template <typename T, bool AKC, bool BKC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
 hipError_t run_gemm(const GemmArgs& a, hipStream_t st) {
-  constexpr int PAD = Tr<T>::PAD;
-  constexpr int AR = AKC ? BM : BK, AC = AKC ? BK : BM;
-  constexpr int BR = BKC ? BN : BK, BC = BKC ? BK : BN;
-  constexpr size_t lds = sizeof(T) * ((size_t)AR * (AC + PAD) + (size_t)BR * (BC + PAD));
+  constexpr size_t lds = GemmShape<T, AKC, BKC, EPI, BM, BN, BK, WGM, WGN>::lds_bytes;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = gemm_kernel<T, AKC, BKC, EPI, BM, BN, BK, WGM, WGN>;
   static bool attr = false;   // idempotent; a race only repeats the same call
   if (!attr) {
@@ -284,14 +342,22 @@ int dz_ld(int Ng, int dtype) {
 
 // Tile shapes.  Gate rows Ng = H*d_k (per key dimension: a square, MFMA-bound problem at
 // d_model ~ Ng) or H (scalar: a skinny product bound by streaming x or dx).
-constexpr int DW_BK_SCALAR = 128;
+// contraction depth of the skinny (scalar-gate) products: deep steps keep enough bytes in flight
+constexpr int fwd_bk_scalar(int dtype) { return dtype == 1 ? 256 : 128; }
+constexpr int dw_bk_scalar(int dtype) { return dtype == 1 ? 128 : 64; }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-size_t dw_part_bytes(int T_, int Ng, int Dm, bool sg) {
+// output tiles of the per-key-dimension dW product (256 x 256 for bf16, 128 x 128 for fp32)
+int dw_tiles(int Ng, int Dm, int dtype) {
+  const int t = dtype == 1 ? 256 : 128;
+  return ((Ng + t - 1) / t) * ((Dm + t - 1) / t);
+}
+
+size_t dw_part_bytes(int T_, int Ng, int Dm, bool sg, int dtype) {
   int ksplit, kper;
-  if (sg) split_k(T_, ((Ng + 31) / 32) * ((Dm + 127) / 128), DW_BK_SCALAR, ksplit, kper);
-  else    split_k(T_, ((Ng + 127) / 128) * ((Dm + 127) / 128), 32, ksplit, kper);
+  if (sg) split_k(T_, ((Ng + 31) / 32) * ((Dm + 127) / 128), dw_bk_scalar(dtype), ksplit, kper);
+  else    split_k(T_, dw_tiles(Ng, Dm, dtype), 32, ksplit, kper);
   return ksplit > 1 ? (size_t)ksplit * Ng * Dm * sizeof(float) : 0;
 }
 
@@ -303,7 +369,9 @@ hipError_t gate_fwd_t(const GateArgs& p, hipStream_t st) {
   a.Bm = p.w; a.ldb = p.d_model; a.b_rows = Ng; a.b_cols = p.d_model;
   a.M = T_; a.N = Ng; a.ksplit = 1; a.k_total = p.d_model; a.kper = p.d_model;
   a.g = p.g; a.B = p.B; a.H = p.H; a.L = p.L; a.dk = p.dk; a.sg = p.sg; a.tau = p.tau;
-  if (p.sg) return run_gemm<T, true, true, EPI_GATE, 64, 32, 256, 4, 1>(a, st);
+  constexpr int DT = sizeof(T) == 2 ? 1 : 0;
+  if (p.sg) return run_gemm<T, true, true, EPI_GATE, 64, 32, fwd_bk_scalar(DT), 4, 1>(a, st);
+  if constexpr (DT == 1) return run_gemm<T, true, true, EPI_GATE, 256, 256, 64, 4, 2>(a, st);
   return run_gemm<T, true, true, EPI_GATE, 128, 128, 32, 2, 2>(a, st);
 }
 
@@ -328,7 +396,12 @@ hipError_t gate_bwd_t(const GateArgs& p, hipStream_t st) {
     a.Bm = p.w; a.ldb = p.d_model; a.b_rows = Ng; a.b_cols = p.d_model;
     a.M = T_; a.N = p.d_model; a.ksplit = 1; a.k_total = Ng; a.kper = Ng;
     a.C = p.dx; a.ldc = p.d_model;
-    e = run_gemm<T, true, false, EPI_STORE, 128, 128, 32, 2, 2>(a, st);
+    // scalar gate: one 32-deep step per tile, bound by writing dx
+    bool big = false;
+    if constexpr (sizeof(T) == 2) {
+      if (!p.sg) { e = run_gemm<T, true, false, EPI_STORE, 256, 256, 64, 4, 2>(a, st); big = true; }
+    }
+    if (!big) e = run_gemm<T, true, false, EPI_STORE, 128, 128, 32, 2, 2>(a, st);
     if (e != hipSuccess) return e;
   }
   {
@@ -338,12 +411,14 @@ hipError_t gate_bwd_t(const GateArgs& p, hipStream_t st) {
     a.Bm = p.x; a.ldb = p.d_model; a.b_rows = T_; a.b_cols = p.d_model;
     a.M = Ng; a.N = p.d_model; a.k_total = T_; a.ldc = p.d_model;
     int ksplit, kper;
-    if (p.sg) split_k(T_, ((Ng + 31) / 32) * ((p.d_model + 127) / 128), DW_BK_SCALAR, ksplit, kper);
-    else      split_k(T_, ((Ng + 127) / 128) * ((p.d_model + 127) / 128), 32, ksplit, kper);
+    constexpr int DT = sizeof(T) == 2 ? 1 : 0;
+    if (p.sg) split_k(T_, ((Ng + 31) / 32) * ((p.d_model + 127) / 128), dw_bk_scalar(DT), ksplit, kper);
+    else      split_k(T_, dw_tiles(Ng, p.d_model, DT), 32, ksplit, kper);
     a.ksplit = ksplit; a.kper = kper;
     a.C = ksplit > 1 ? (void*)part : (void*)p.dw;
-    if (p.sg) e = run_gemm<T, false, false, EPI_F32, 32, 128, DW_BK_SCALAR, 1, 4>(a, st);
-    else      e = run_gemm<T, false, false, EPI_F32, 128, 128, 32, 2, 2>(a, st);
+    if (p.sg) e = run_gemm<T, false, false, EPI_F32, 32, 128, dw_bk_scalar(DT), 1, 4>(a, st);
+    else if constexpr (DT == 1) e = run_gemm<T, false, false, EPI_F32, 256, 256, 32, 4, 2>(a, st);
+    else                        e = run_gemm<T, false, false, EPI_F32, 128, 128, 32, 2, 2>(a, st);
     if (e != hipSuccess) return e;
     if (ksplit > 1) {
       const size_t n4 = (size_t)Ng * p.d_model / 4;
@@ -360,7 +435,7 @@ hipError_t gate_bwd_t(const GateArgs& p, hipStream_t st) {
 size_t gate_bwd_workspace_bytes(int B, int H, int L, int dk, int sg, int d_model, int dtype) {
   const int T_ = B * L, Ng = sg ? H : H * dk;
   const size_t esz = dtype == 1 ? 2 : 4;
-  return align256((size_t)T_ * dz_ld(Ng, dtype) * esz) + dw_part_bytes(T_, Ng, d_model, sg != 0);
+  return align256((size_t)T_ * dz_ld(Ng, dtype) * esz) + dw_part_bytes(T_, Ng, d_model, sg != 0, dtype);
 }
 
 hipError_t launch_gate_fwd(const GateArgs& a, int dtype, hipStream_t st) {
