@@ -18,11 +18,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblizard_attn.so")
 
 LIZARD_FP32, LIZARD_BF16 = 0, 1
-OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE = 0, 1, 2, 3
+OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE, OP_DISTILL = 0, 1, 2, 3, 4
 GATE_PER_DIM, GATE_SCALAR = 0, 1
 SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
            "lizard_attn_workspace_bytes", "lizard_attn_status_string", "lizard_gate_proj_fwd",
-           "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes")
+           "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes", "lizard_distill_mse")
 
 
 class Shape(ctypes.Structure):
@@ -63,6 +63,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_continue.restype = I32
     lib.lizard_attn_workspace_bytes.argtypes = [SP, ctypes.c_int]
     lib.lizard_attn_workspace_bytes.restype = SZ
+    lib.lizard_distill_mse.argtypes = [SP, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_distill_mse.restype = I32
     lib.lizard_gate_proj_fwd.argtypes = [SP, I32, F, P, P, P, P]
     lib.lizard_gate_proj_fwd.restype = I32
     lib.lizard_gate_proj_bwd.argtypes = [SP, I32, F, P, P, P, P, P, P, P, SZ, P]
@@ -306,6 +308,30 @@ def lizard_attn_fwd_continue(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, 
     return o
 
 
+def lizard_distill_mse(q_t, k_t, v_t, o_s, *, scale: float | None = None, out=None, workspace=None) -> dict:
+    """Stage-1 loss: the teacher's causal softmax attention of (q_t, k_t, v_t) against the layer
+    output o_s; returns {"loss": fp32 device scalar (mean squared error over every element),
+    "dO": 2 (o_s - o_T) / N in o_s's dtype, the gradient for lizard_attn_bwd}."""
+    lib = load()
+    dt, dev = q_t.dtype, q_t.device
+    for n, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("o_s", o_s)):
+        _need(t, n, dt, dev)
+    if not (q_t.shape == k_t.shape == v_t.shape == o_s.shape):
+        raise ValueError("q_t, k_t, v_t and o_s must share one [B,H,L,d] shape")
+    B, H, L, d = q_t.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, 1, 0, scale, 1.0, dt)
+    n = int(lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_DISTILL))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    dO = torch.empty_like(o_s) if out is None else out
+    loss = torch.empty((), device=dev, dtype=torch.float32)
+    _check(lib.lizard_distill_mse(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(o_s), _ptr(dO),
+                                  _ptr(loss), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return {"loss": loss, "dO": dO}
+
+
 def _gate_shape(x, w, heads, d_k, scalar):
     B, L, Dm = x.shape
     ng = heads if scalar else heads * d_k
@@ -371,5 +397,6 @@ fwd = lizard_attn_fwd
 bwd = lizard_attn_bwd
 decode_step = lizard_attn_decode_step
 fwd_continue = lizard_attn_fwd_continue
+distill_mse = lizard_distill_mse
 gate_proj_fwd = lizard_gate_proj_fwd
 gate_proj_bwd = lizard_gate_proj_bwd

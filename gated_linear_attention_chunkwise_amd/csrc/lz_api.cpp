@@ -91,9 +91,11 @@ const char* lizard_attn_status_string(lizard_status_t st) {
 }
 
 size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
-  if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE && op != LIZARD_OP_FWD_CONTINUE)
+  if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE && op != LIZARD_OP_FWD_CONTINUE &&
+      op != LIZARD_OP_DISTILL)
     return 0;
-  if (check_shape(s, op) != LIZARD_OK) return 0;
+  if (check_shape(s, op == LIZARD_OP_DISTILL ? LIZARD_OP_FWD : op) != LIZARD_OK) return 0;
+  if (op == LIZARD_OP_DISTILL) return lz::distill_workspace_bytes(s->B, s->H, s->L);
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (op == LIZARD_OP_FWD || op == LIZARD_OP_FWD_CONTINUE)
     return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
@@ -200,6 +202,21 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
   lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
                    reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate};
   return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_distill_mse(const lizard_attn_shape_t* s, const void* q_t, const void* k_t,
+                                   const void* v_t, const void* o_s, void* dO, float* loss, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
+  if (st != LIZARD_OK) return st;
+  st = s->L > 0 ? check_ptrs({q_t, k_t, v_t, o_s, dO, loss, workspace}, {})
+                : check_ptrs({loss}, {q_t, k_t, v_t, o_s, dO, workspace});
+  if (st != LIZARD_OK) return st;
+  if (s->L > 0 && workspace_bytes < lz::distill_workspace_bytes(s->B, s->H, s->L)) return LIZARD_EWORKSPACE;
+  const double n = (double)s->B * s->H * s->L * s->d_v;
+  lz::DistillArgs a{q_t, k_t, v_t, o_s, dO, loss, reinterpret_cast<float*>(workspace), s->B, s->H, s->L, s->scale,
+                    n > 0 ? (float)(1.0 / n) : 0.f};
+  return lz::launch_distill(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
 lizard_status_t lizard_gate_proj_fwd(const lizard_attn_shape_t* s, int32_t d_model, float tau,

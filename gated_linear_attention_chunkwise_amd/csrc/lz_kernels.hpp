@@ -83,6 +83,15 @@ struct GateArgs {
   float tau;
 };
 
+// Stage-1 distillation loss (lz_distill.hip): teacher causal attention of (q, k, v), MSE against
+// the student output o_s, dO = 2 (o_s - o_T) / N; partial: distill_workspace_bytes() bytes.
+struct DistillArgs {
+  const void* q; const void* k; const void* v; const void* o_s;
+  void* dO; float* loss; float* partial;
+  int B, H, L;
+  float scale, inv_n;
+};
+
 // Each returns hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st);
@@ -90,6 +99,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
 // Segment forward resuming from (state_in, ring, pos): launch_fwd, then the ring and pos advance.
 hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st);
+hipError_t launch_distill(const DistillArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_gate_fwd(const GateArgs& a, int dtype, hipStream_t st);
 hipError_t launch_gate_bwd(const GateArgs& a, int dtype, hipStream_t st);   // L = 0: dw = 0
 
@@ -104,6 +114,8 @@ size_t decode_workspace_bytes(int B, int H, int D);
 // Workspace bytes needed by launch_gate_bwd: dz [B*L][Ng rounded up to 16 bytes] in the operand
 // dtype, then the fp32 partial sums of dW when its contraction over tokens is split.
 size_t gate_bwd_workspace_bytes(int B, int H, int L, int dk, int sg, int d_model, int dtype);
+// Workspace bytes needed by launch_distill: one fp32 partial per workgroup.
+size_t distill_workspace_bytes(int B, int H, int L);
 // Workspace bytes needed by launch_bwd.
 size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
 

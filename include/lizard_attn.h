@@ -90,7 +90,8 @@ typedef struct {
   int32_t gate;             /* lizard_gate_t (0, the zero-initialised default, is per key dimension) */
 } lizard_attn_shape_t;
 
-enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2, LIZARD_OP_FWD_CONTINUE = 3 };
+enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2, LIZARD_OP_FWD_CONTINUE = 3,
+       LIZARD_OP_DISTILL = 4 };
 
 /* Bytes of device workspace that `op` needs for shape `s` (0 when none, or
  * when `s` is invalid).  Pass at least this many bytes to the call. */
@@ -204,6 +205,31 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         void* o,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
+
+/* Stage-1 attention-approximation loss (English page §2, "Stage 1: Attention
+ * Approximation"; French page "Étape 1"): the layer is trained to reproduce
+ * the teacher's softmax attention output under a mean squared error.
+ *
+ *   o_T  = causal softmax attention: o_T[t] = sum_{s<=t} softmax_s(scale q_t.k_s) v_s
+ *   loss = sum over every element of (o_S - o_T)^2 / N,  N = B*H*L*d_v
+ *   dO   = 2 (o_S - o_T) / N
+ *
+ *   s        validated as for lizard_attn_fwd (bf16 d in {64, 128}, fp32 d = 64);
+ *            B, H, L, d_k, d_v, scale and dtype define the call, W, M, chunk,
+ *            mix and gate do not affect it
+ *   q_t, k_t, v_t  the teacher's queries, keys and values, [B,H,L,d] dtype
+ *            (they may alias the layer's q, k, v)
+ *   o_s      the layer's output for the same tokens, [B,H,L,d_v] dtype
+ *   dO       written, [B,H,L,d_v] dtype: the gradient to pass to lizard_attn_bwd
+ *   loss     written, device fp32 scalar (0 when L = 0)
+ *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_DISTILL) bytes of
+ *            caller-owned device memory (one partial sum per workgroup)
+ * o_T is never written: the loss is applied in the attention kernel's
+ * epilogue, and the partial sums are added in a fixed order (deterministic).
+ * A stage-1 step is lizard_attn_fwd -> lizard_distill_mse -> lizard_attn_bwd. */
+lizard_status_t lizard_distill_mse(const lizard_attn_shape_t* s, const void* q_t, const void* k_t,
+                                   const void* v_t, const void* o_s, void* dO, float* loss, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Gate projection: the learnable gating module Gamma_t = sigmoid(W x_t)
  * (English page §2.A "Adaptive Memory Control"; Chinese page §2.1), produced

@@ -30,7 +30,7 @@ import numpy as np
 
 from . import lizard_oracle as orc
 
-__all__ = ["teacher_attention", "mse_and_grad", "stage1_step"]
+__all__ = ["teacher_attention", "teacher_attention_rows", "mse_and_grad", "stage1_step"]
 
 
 def teacher_attention(q, k, v, *, scale):
@@ -40,6 +40,18 @@ def teacher_attention(q, k, v, *, scale):
     no_meta = np.zeros((H, 0, D))
     o, _ = orc.window_forward(q, k, v, no_meta, None, max(L, 1), scale)
     return o
+
+
+def teacher_attention_rows(q, k, v, rows, *, scale):
+    """Rows ``rows`` of teacher_attention for one (b, h): q, k, v [L, d]; returns [len(rows), d].
+    The same definition evaluated only where asked (for sampled checks at long L)."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    out = np.empty((len(rows), v.shape[-1]))
+    for n, t in enumerate(rows):
+        logits = scale * (k[:t + 1] @ q[t])
+        p = np.exp(logits - logits.max())
+        out[n] = (p / p.sum()) @ v[:t + 1]
+    return out
 
 
 def mse_and_grad(o_student, o_teacher):

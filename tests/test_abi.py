@@ -17,7 +17,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = range(6)
 
 def declared_functions():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_(?:attn|gate)_[a-z_]+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_(?:attn|gate|distill)_[a-z_]+)\s*\(", txt, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
                           "lizard_attn_fwd_continue", "lizard_attn_workspace_bytes",
                           "lizard_attn_status_string", "lizard_gate_proj_fwd", "lizard_gate_proj_bwd",
-                          "lizard_gate_proj_workspace_bytes"}
+                          "lizard_gate_proj_workspace_bytes", "lizard_distill_mse"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(pkg.SYMBOLS) == set(names)
@@ -195,3 +195,19 @@ def test_gate_proj_workspace_sizes(lib):
     assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), 256) == 128 * 8 * 2
     assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(shape(L=0)), 256) == 0
     assert lib.lizard_gate_proj_workspace_bytes(ctypes.byref(s), 100) == 0
+
+
+def test_distill_validation(lib):
+    s = shape()
+    def call(s=s, q=GOOD, dO=GOOD, loss=GOOD, ws=GOOD, ws_bytes=1 << 30):
+        return lib.lizard_distill_mse(ctypes.byref(s), q, GOOD, GOOD, GOOD, dO, loss, ws, ws_bytes, None)
+    assert lib.lizard_distill_mse(None, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 30, None) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(loss=None) == EINVAL
+    assert call(dO=BAD) == EALIGN
+    assert call(s=shape(d_k=96, d_v=96)) == EUNSUPPORTED
+    assert call(s=shape(dtype=0)) == EUNSUPPORTED           # fp32 only at d = 64
+    # one fp32 partial per (batch, head, block of 128 queries)
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(B=2, H=3, L=300)), 4) == 2 * 3 * 3 * 4
+    assert call(ws_bytes=4 * 2 - 1) == EWORKSPACE             # B=1 H=2 L=128: two partials
+    assert call(ws=None) == EINVAL

@@ -26,6 +26,15 @@ def test_teacher_is_causal_sdpa(L):
     assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)
 
 
+def test_teacher_rows_match_full():
+    rng = np.random.default_rng(9)
+    q, k, v = (rnd(rng, 1, 1, 30, 6) for _ in range(3))
+    full = dst.teacher_attention(q, k, v, scale=0.3)
+    rows = [0, 7, 29]
+    assert np.allclose(dst.teacher_attention_rows(q[0, 0], k[0, 0], v[0, 0], rows, scale=0.3), full[0, 0, rows],
+                       rtol=1e-13, atol=1e-14)
+
+
 def test_teacher_closed_forms():
     rng = np.random.default_rng(1)
     L = 9

@@ -1,0 +1,101 @@
+"""GPU parity of the stage-1 attention-approximation loss (teacher causal
+attention + MSE, fused) and of the whole step forward -> loss -> backward
+against the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import distill as dst
+from oracle import lizard_oracle as orc
+from gated_linear_attention_chunkwise_amd import lizard_attn_bwd, lizard_attn_fwd, lizard_distill_mse
+from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device, make_small
+from helpers import TOL, dev, host, rel_l2, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def step_case(dtname, B, H, L, D, W, M, seed, separate_teacher):
+    x = make_small(B, H, L, D, M, seed=seed, bf16=(dtname == "bf16"))
+    t = make_small(B, H, L, D, 0, seed=seed + 1, bf16=(dtname == "bf16"), with_grad=False)
+    dt = tdtype(dtname)
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v", "meta_k")}
+    T["g"] = dev(x["g"], torch.float32)
+    teacher = (t["q"], t["k"], t["v"]) if separate_teacher else (x["q"], x["k"], x["v"])
+    TT = [dev(a, dt) for a in teacher]
+    scale = 1.0 / math.sqrt(D)
+    f = lizard_attn_fwd(T["q"], T["k"], T["v"], T["g"], T["meta_k"], None, window=W, scale=scale, want_lse=True,
+                        want_o_swa=True, want_chunk_states=True)
+    ls = lizard_distill_mse(*TT, f["o"], scale=scale)
+    b = lizard_attn_bwd(T["q"], T["k"], T["v"], T["g"], T["meta_k"], None, ls["dO"], f["lse"], f["o_swa"],
+                        f["chunk_states"], window=W, scale=scale)
+    torch.cuda.synchronize()
+    ref = dst.stage1_step(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=W, scale=scale,
+                          teacher=teacher)
+    # The loss and every gradient are driven by o_S - o_T, formed from o_S as the layer returns it
+    # (rounded to the operand dtype).  That rounding, relative size TOL at most, is amplified by
+    # |o_S| / |o_S - o_T| when the student is close to the teacher (one token, a one-token window),
+    # so the bound scales with that factor, taken from the oracle.
+    amp = max(1.0, float(np.linalg.norm(ref["o"]) / np.linalg.norm(ref["o"] - ref["o_teacher"])))
+    errs = {"loss": abs(float(ls["loss"]) - ref["loss"]) / ref["loss"], "dO": rel_l2(host(ls["dO"]), ref["dO"])}
+    errs.update({n: rel_l2(host(b[n]), ref[n]) for n in ("dq", "dk", "dv")})
+    if L > 1:
+        errs["dg"] = rel_l2(host(b["dg"]), ref["dg"])
+    else:   # the first token's gate multiplies the zero initial state: dg = 0 exactly
+        assert float(b["dg"].abs().max()) == 0.0
+    if M > 0:
+        errs["dmeta_k"] = rel_l2(host(b["dmeta_k"]), ref["dmeta_k"])
+    print(dtname, B, H, L, D, W, M, f"amp {amp:.1f}", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[dtname] * amp, (n, e, amp)
+
+
+# (dtype, B, H, L, d, W, M): several query blocks and key tiles, ragged tails, L = 1
+CASES = [("fp32", 1, 2, 256, 64, 64, 4), ("fp32", 2, 1, 77, 64, 5, 0), ("bf16", 2, 2, 300, 128, 128, 4),
+         ("bf16", 1, 2, 129, 64, 100, 2), ("bf16", 1, 1, 1, 128, 1, 0), ("bf16", 1, 3, 640, 128, 64, 16)]
+
+
+@pytest.mark.parametrize("dtname,B,H,L,D,W,M", CASES)
+@pytest.mark.parametrize("separate_teacher", [False, True])
+def test_stage1_step_parity(dtname, B, H, L, D, W, M, separate_teacher):
+    step_case(dtname, B, H, L, D, W, M, seed=L + D + W + M, separate_teacher=separate_teacher)
+
+
+def test_distill_loss_is_deterministic_and_empty_is_zero():
+    x = make_small(2, 2, 500, 128, 0, seed=4, bf16=True, with_grad=False)
+    T = [dev(x[n], torch.bfloat16) for n in ("q", "k", "v")]
+    o = dev(make_small(2, 2, 500, 128, 0, seed=5, bf16=True, with_grad=False)["q"], torch.bfloat16)
+    a = lizard_distill_mse(*T, o)
+    b = lizard_distill_mse(*T, o)
+    torch.cuda.synchronize()
+    assert float(a["loss"]) == float(b["loss"]) and torch.equal(a["dO"], b["dO"])
+    e = torch.zeros(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    z = lizard_distill_mse(e, e, e, e)
+    torch.cuda.synchronize()
+    assert float(z["loss"]) == 0.0
+
+
+def test_stage1_train_shape_sampled():
+    """B=4, H=32, L=8192, d=128: dO on sampled rows of a sampled head against the oracle's
+    student forward and teacher rows; the loss against the property loss = N/4 * sum(dO^2)."""
+    w = WORKLOADS["train_8k"]
+    x = make_inputs_device(w, "cuda", with_grad=False)
+    f = lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=w.W, scale=w.scale)
+    ls = lizard_distill_mse(x["q"], x["k"], x["v"], f["o"], scale=w.scale)
+    torch.cuda.synchronize()
+    N = w.B * w.H * w.L * w.D
+    dO = ls["dO"].double()
+    loss_prop = float((dO * dO).sum()) * N / 4.0
+    e_loss = abs(float(ls["loss"]) - loss_prop) / loss_prop
+    b, h = 2, 11
+    hs = {n: x[n][b:b + 1, h:h + 1].float().cpu().numpy() for n in ("q", "k", "v", "g")}
+    mk = x["meta_k"][h:h + 1].float().cpu().numpy()
+    o_s = orc.hybrid_forward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, window=w.W, scale=w.scale)["o"][0, 0]
+    rng = np.random.default_rng(3)
+    rows = sorted(set(rng.integers(0, w.L, 24).tolist()) | {0, w.L - 1})
+    o_t = dst.teacher_attention_rows(hs["q"][0, 0], hs["k"][0, 0], hs["v"][0, 0], rows, scale=w.scale)
+    ref = 2.0 * (o_s[rows] - o_t) / N
+    e_dO = rel_l2(host(ls["dO"][b, h])[rows], ref)
+    print(f"train shape: loss vs property {e_loss:.2e}, dO rows {e_dO:.2e}", flush=True)
+    assert e_loss <= TOL["bf16"] and e_dO <= TOL["bf16"]
