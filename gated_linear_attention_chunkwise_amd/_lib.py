@@ -18,11 +18,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblizard_attn.so")
 
 LIZARD_FP32, LIZARD_BF16 = 0, 1
-OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE, OP_DISTILL = 0, 1, 2, 3, 4
+OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE, OP_DISTILL, OP_FEATURE_BWD = 0, 1, 2, 3, 4, 5
 GATE_PER_DIM, GATE_SCALAR = 0, 1
 SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
            "lizard_attn_workspace_bytes", "lizard_attn_status_string", "lizard_gate_proj_fwd",
-           "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes", "lizard_distill_mse")
+           "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes", "lizard_distill_mse",
+           "lizard_attn_fwd_feat", "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd")
 
 
 class Shape(ctypes.Structure):
@@ -63,6 +64,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_continue.restype = I32
     lib.lizard_attn_workspace_bytes.argtypes = [SP, ctypes.c_int]
     lib.lizard_attn_workspace_bytes.restype = SZ
+    lib.lizard_attn_fwd_feat.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_fwd_feat.restype = I32
+    lib.lizard_attn_bwd_feat.argtypes = [SP] + [P] * 21 + [SZ, P, P]
+    lib.lizard_attn_bwd_feat.restype = I32
+    lib.lizard_hedgehog_fwd.argtypes = [SP, P, P, P, P]
+    lib.lizard_hedgehog_fwd.restype = I32
+    lib.lizard_hedgehog_bwd.argtypes = [SP, P, P, P, P, P, P, SZ, P]
+    lib.lizard_hedgehog_bwd.restype = I32
     lib.lizard_distill_mse.argtypes = [SP, P, P, P, P, P, P, P, SZ, P]
     lib.lizard_distill_mse.restype = I32
     lib.lizard_gate_proj_fwd.argtypes = [SP, I32, F, P, P, P, P]
@@ -308,6 +317,119 @@ def lizard_attn_fwd_continue(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, 
     return o
 
 
+def lizard_attn_fwd_feat(q, k, v, lq, lk, g, meta_k, meta_v=None, *, window: int, scale: float | None = None,
+                         mix: float = 1.0, chunk: int = 64, want_lse: bool = False, want_o_swa: bool = False,
+                         want_chunk_states: bool = False, want_state: bool = False) -> dict:
+    """Forward with GLA log features: the GLA branch runs on exp(lq), exp(lk) (fp32 [B,H,L,d],
+    gate absorbed in log space), the window on q, k; otherwise as lizard_attn_fwd."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, n, dt, dev)
+    for n, t in (("lq", lq), ("lk", lk), ("g", g)):
+        _need(t, n, torch.float32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, L, d = q.shape
+    if not (k.shape == v.shape == lq.shape == lk.shape == g.shape == q.shape):
+        raise ValueError("q, k, v, lq, lk and g must share one [B,H,L,d] shape")
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, GATE_PER_DIM)
+    NC = (L + 63) // 64
+    out = {"o": torch.empty_like(q)}
+    out["lse"] = torch.empty(B, H, L, device=dev, dtype=torch.float32) if want_lse else None
+    out["o_swa"] = torch.empty_like(q) if want_o_swa else None
+    out["chunk_states"] = (torch.empty(B, H, NC, d, d, device=dev, dtype=dt) if want_chunk_states else None)
+    out["state"] = torch.empty(B, H, d, d, device=dev, dtype=torch.float32) if want_state else None
+    ws, ws_bytes = None, 0
+    if L > 0:
+        ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD)
+        if want_chunk_states:
+            ws_bytes -= out["chunk_states"].numel() * out["chunk_states"].element_size()
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+    _check(lib.lizard_attn_fwd_feat(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(lq), _ptr(lk), _ptr(g),
+                                    _ptr(meta_k), _ptr(meta_v), _ptr(out["o"]), _ptr(out["lse"]),
+                                    _ptr(out["o_swa"]), _ptr(out["chunk_states"]), _ptr(out["state"]), _ptr(ws),
+                                    ws_bytes, _stream(dev)))
+    return out
+
+
+def lizard_attn_bwd_feat(q, k, v, lq, lk, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *, window: int,
+                         scale: float | None = None, mix: float = 1.0, chunk: int = 64,
+                         stage_events=None) -> dict:
+    """Backward of lizard_attn_fwd_feat: dq, dk (window branch), dv, dlq, dlk (GLA log features),
+    dg, dmeta_k, dmeta_v."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO), ("o_swa", o_swa), ("chunk_states", chunk_states)):
+        _need(t, n, dt, dev)
+    for n, t in (("lq", lq), ("lk", lk), ("g", g), ("lse", lse)):
+        _need(t, n, torch.float32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, L, d = q.shape
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, GATE_PER_DIM)
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD)
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dlq": torch.empty_like(lq), "dlk": torch.empty_like(lk), "dg": torch.empty_like(g)}
+    out["dmeta_k"] = torch.empty(H, M, d, device=dev, dtype=torch.float32) if M > 0 else None
+    out["dmeta_v"] = (torch.empty(H, M, d, device=dev, dtype=torch.float32)
+                      if (meta_v is not None and M > 0) else None)
+    if M == 0:
+        meta_v = None
+    _check(lib.lizard_attn_bwd_feat(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(lq), _ptr(lk), _ptr(g),
+                                    _ptr(meta_k), _ptr(meta_v), _ptr(dO), _ptr(lse), _ptr(o_swa),
+                                    _ptr(chunk_states), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                    _ptr(out["dlq"]), _ptr(out["dlk"]), _ptr(out["dg"]), _ptr(out["dmeta_k"]),
+                                    _ptr(out["dmeta_v"]), _ptr(ws), ws_bytes, _stream(dev),
+                                    _events(stage_events, BWD_STAGES + 1)))
+    return out
+
+
+def _feat_shape(x, w):
+    B, H, L, d = x.shape
+    if tuple(w.shape) != (H, d, d // 2):
+        raise ValueError(f"w must have shape ({H}, {d}, {d // 2}), got {tuple(w.shape)}")
+    return make_shape(B, H, L, d, 1, 0, 1.0, 1.0, x.dtype)
+
+
+def lizard_hedgehog_fwd(x, w):
+    """log phi(x) = [z - lse(z), -z - lse(-z)], z = x w_h: x [B,H,L,d] (bf16 or fp32), w [H,d,d/2]
+    in x's dtype; returns fp32 [B,H,L,d]."""
+    lib = load()
+    dt, dev = x.dtype, x.device
+    _need(x, "x", dt, dev)
+    _need(w, "w", dt, dev)
+    s = _feat_shape(x, w)
+    out = torch.empty(x.shape, device=dev, dtype=torch.float32)
+    _check(lib.lizard_hedgehog_fwd(ctypes.byref(s), _ptr(x), _ptr(w), _ptr(out), _stream(dev)))
+    return out
+
+
+def lizard_hedgehog_bwd(x, w, dl, workspace=None):
+    """Gradients (dx in x's dtype, dw fp32 [H,d,d/2]) of sum(dl * log phi(x))."""
+    lib = load()
+    dt, dev = x.dtype, x.device
+    _need(x, "x", dt, dev)
+    _need(w, "w", dt, dev)
+    _need(dl, "dl", torch.float32, dev)
+    s = _feat_shape(x, w)
+    n = int(lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FEATURE_BWD))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    dx = torch.empty_like(x)
+    dw = torch.empty(w.shape, device=dev, dtype=torch.float32)
+    _check(lib.lizard_hedgehog_bwd(ctypes.byref(s), _ptr(x), _ptr(w), _ptr(dl), _ptr(dx), _ptr(dw),
+                                   _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dx, dw
+
+
 def lizard_distill_mse(q_t, k_t, v_t, o_s, *, scale: float | None = None, out=None, workspace=None) -> dict:
     """Stage-1 loss: the teacher's causal softmax attention of (q_t, k_t, v_t) against the layer
     output o_s; returns {"loss": fp32 device scalar (mean squared error over every element),
@@ -398,5 +520,9 @@ bwd = lizard_attn_bwd
 decode_step = lizard_attn_decode_step
 fwd_continue = lizard_attn_fwd_continue
 distill_mse = lizard_distill_mse
+fwd_feat = lizard_attn_fwd_feat
+hedgehog_fwd = lizard_hedgehog_fwd
+hedgehog_bwd = lizard_hedgehog_bwd
+bwd_feat = lizard_attn_bwd_feat
 gate_proj_fwd = lizard_gate_proj_fwd
 gate_proj_bwd = lizard_gate_proj_bwd

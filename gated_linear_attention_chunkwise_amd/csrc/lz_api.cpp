@@ -74,6 +74,68 @@ lizard_status_t check_gate_shape(const lizard_attn_shape_t* s, int32_t d_model, 
   return LIZARD_OK;
 }
 
+lizard_status_t fwd_impl(const lizard_attn_shape_t* s,
+                         const void* q, const void* k, const void* v, const float* lq, const float* lk,
+                         const float* g, const void* meta_k, const void* meta_v,
+                         void* o, float* lse, void* o_swa, void* chunk_states, float* state_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  // L = 0: the sequence tensors are empty (possibly NULL); only state_out is written (zero)
+  if (s->L > 0)
+    st = check_ptrs({q, k, v, g, o}, {meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace, lq, lk});
+  else
+    st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace, lq, lk});
+  if (st != LIZARD_OK) return st;
+  // the workspace holds the sweep's segment buffers, and the chunk states unless chunk_states is given
+  const size_t need = s->L == 0 ? 0
+                      : chunk_states != nullptr ? lz::fwd_segment_bytes(s->B, s->H, s->L, s->d_k)
+                                                : lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
+  if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
+  lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
+                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix,
+                s->gate, s->L > 0 ? lq : nullptr, s->L > 0 ? lk : nullptr};
+  return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
+                         const void* q, const void* k, const void* v, const float* lq, const float* lk,
+                         const float* g, const void* meta_k, const void* meta_v, const void* dO,
+                         const float* lse, const void* o_swa, const void* chunk_states,
+                         void* dq, void* dk, void* dv, float* dlq, float* dlk, float* dg,
+                         float* dmeta_k, float* dmeta_v,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         hipEvent_t* stage_events) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_BWD);
+  if (st != LIZARD_OK) return st;
+  if ((meta_v == nullptr) != (dmeta_v == nullptr)) return LIZARD_EINVAL;
+  if (s->M > 0 && (meta_k == nullptr || dmeta_k == nullptr)) return LIZARD_EINVAL;
+  if (s->L > 0)
+    st = check_ptrs({q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg},
+                    {meta_k, meta_v, dmeta_k, dmeta_v, workspace, lq, lk, dlq, dlk});
+  else   // L = 0: only the meta gradients (zero) are written
+    st = check_ptrs({}, {q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg,
+                         meta_k, meta_v, dmeta_k, dmeta_v, workspace, lq, lk, dlq, dlk});
+  if (st != LIZARD_OK) return st;
+  const size_t need = lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
+  lz::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g;
+  a.meta_k = meta_k; a.meta_v = s->M > 0 ? meta_v : nullptr; a.dO = dO;
+  a.lse = lse; a.o_swa = o_swa; a.chunk_states = chunk_states;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
+  a.dmeta_k = s->M > 0 ? dmeta_k : nullptr;
+  a.dmeta_v = s->M > 0 ? dmeta_v : nullptr;
+  a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
+  a.scale = s->scale; a.mix = s->mix; a.gate = s->gate;
+  a.workspace = workspace;
+  a.stage_events = stage_events;
+  if (s->L > 0 && lq != nullptr) { a.lq = lq; a.lk = lk; a.dlq = dlq; a.dlk = dlk; }
+  return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,10 +154,12 @@ const char* lizard_attn_status_string(lizard_status_t st) {
 
 size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
   if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE && op != LIZARD_OP_FWD_CONTINUE &&
-      op != LIZARD_OP_DISTILL)
+      op != LIZARD_OP_DISTILL && op != LIZARD_OP_FEATURE_BWD)
     return 0;
-  if (check_shape(s, op == LIZARD_OP_DISTILL ? LIZARD_OP_FWD : op) != LIZARD_OK) return 0;
+  const bool seq_op = op == LIZARD_OP_DISTILL || op == LIZARD_OP_FEATURE_BWD;
+  if (check_shape(s, seq_op ? LIZARD_OP_FWD : op) != LIZARD_OK) return 0;
   if (op == LIZARD_OP_DISTILL) return lz::distill_workspace_bytes(s->B, s->H, s->L);
+  if (op == LIZARD_OP_FEATURE_BWD) return s->L > 0 ? lz::feature_workspace_bytes(s->B, s->H, s->L, s->d_k) : 0;
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (op == LIZARD_OP_FWD || op == LIZARD_OP_FWD_CONTINUE)
     return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
@@ -108,25 +172,21 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
                                 void* o, float* lse, void* o_swa, void* chunk_states,
                                 float* state_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
-  if (st != LIZARD_OK) return st;
-  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
-  // L = 0: the sequence tensors are empty (possibly NULL); only state_out is written (zero)
-  if (s->L > 0)
-    st = check_ptrs({q, k, v, g, o}, {meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace});
-  else
-    st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace});
-  if (st != LIZARD_OK) return st;
-  // the workspace holds the sweep's segment buffers, and the chunk states unless chunk_states is given
-  const size_t need = s->L == 0 ? 0
-                      : chunk_states != nullptr ? lz::fwd_segment_bytes(s->B, s->H, s->L, s->d_k)
-                                                : lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
-  if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
-  lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
-                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix,
-                s->gate};
-  return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  return fwd_impl(s, q, k, v, nullptr, nullptr, g, meta_k, meta_v, o, lse, o_swa, chunk_states, state_out,
+                  workspace, workspace_bytes, stream);
+}
+
+lizard_status_t lizard_attn_fwd_feat(const lizard_attn_shape_t* s,
+                                     const void* q, const void* k, const void* v,
+                                     const float* lq, const float* lk, const float* g,
+                                     const void* meta_k, const void* meta_v,
+                                     void* o, float* lse, void* o_swa, void* chunk_states,
+                                     float* state_out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (s != nullptr && s->gate != LIZARD_GATE_PER_DIM) return LIZARD_EUNSUPPORTED;
+  if (s != nullptr && s->L > 0 && (lq == nullptr || lk == nullptr)) return LIZARD_EINVAL;
+  return fwd_impl(s, q, k, v, lq, lk, g, meta_k, meta_v, o, lse, o_swa, chunk_states, state_out, workspace,
+                  workspace_bytes, stream);
 }
 
 lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
@@ -159,31 +219,24 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 float* dmeta_k, float* dmeta_v,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* stage_events) {
-  lizard_status_t st = check_shape(s, LIZARD_OP_BWD);
-  if (st != LIZARD_OK) return st;
-  if ((meta_v == nullptr) != (dmeta_v == nullptr)) return LIZARD_EINVAL;
-  if (s->M > 0 && (meta_k == nullptr || dmeta_k == nullptr)) return LIZARD_EINVAL;
-  if (s->L > 0)
-    st = check_ptrs({q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg},
-                    {meta_k, meta_v, dmeta_k, dmeta_v, workspace});
-  else   // L = 0: only the meta gradients (zero) are written
-    st = check_ptrs({}, {q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg,
-                         meta_k, meta_v, dmeta_k, dmeta_v, workspace});
-  if (st != LIZARD_OK) return st;
-  const size_t need = lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
-  lz::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.g = g;
-  a.meta_k = meta_k; a.meta_v = s->M > 0 ? meta_v : nullptr; a.dO = dO;
-  a.lse = lse; a.o_swa = o_swa; a.chunk_states = chunk_states;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
-  a.dmeta_k = s->M > 0 ? dmeta_k : nullptr;
-  a.dmeta_v = s->M > 0 ? dmeta_v : nullptr;
-  a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
-  a.scale = s->scale; a.mix = s->mix; a.gate = s->gate;
-  a.workspace = workspace;
-  a.stage_events = stage_events;
-  return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  return bwd_impl(s, q, k, v, nullptr, nullptr, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, dq, dk, dv,
+                  nullptr, nullptr, dg, dmeta_k, dmeta_v, workspace, workspace_bytes, stream, stage_events);
+}
+
+lizard_status_t lizard_attn_bwd_feat(const lizard_attn_shape_t* s,
+                                     const void* q, const void* k, const void* v,
+                                     const float* lq, const float* lk, const float* g,
+                                     const void* meta_k, const void* meta_v, const void* dO,
+                                     const float* lse, const void* o_swa, const void* chunk_states,
+                                     void* dq, void* dk, void* dv, float* dlq, float* dlk, float* dg,
+                                     float* dmeta_k, float* dmeta_v,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     hipEvent_t* stage_events) {
+  if (s != nullptr && s->gate != LIZARD_GATE_PER_DIM) return LIZARD_EUNSUPPORTED;
+  if (s != nullptr && s->L > 0 && (lq == nullptr || lk == nullptr || dlq == nullptr || dlk == nullptr))
+    return LIZARD_EINVAL;
+  return bwd_impl(s, q, k, v, lq, lk, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, dq, dk, dv, dlq, dlk, dg,
+                  dmeta_k, dmeta_v, workspace, workspace_bytes, stream, stage_events);
 }
 
 lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
@@ -202,6 +255,29 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
   lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
                    reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate};
   return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_hedgehog_fwd(const lizard_attn_shape_t* s, const void* x, const void* w, float* lphi,
+                                    hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
+  if (st != LIZARD_OK) return st;
+  st = s->L > 0 ? check_ptrs({x, w, lphi}, {}) : check_ptrs({}, {x, w, lphi});
+  if (st != LIZARD_OK) return st;
+  if (s->L == 0) return LIZARD_OK;
+  lz::FeatArgs a{x, w, lphi, nullptr, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, 0};
+  return lz::launch_feature_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+lizard_status_t lizard_hedgehog_bwd(const lizard_attn_shape_t* s, const void* x, const void* w, const float* dl,
+                                    void* dx, float* dw, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
+  if (st != LIZARD_OK) return st;
+  st = s->L > 0 ? check_ptrs({x, w, dl, dx, dw, workspace}, {}) : check_ptrs({w, dw}, {x, dl, dx, workspace});
+  if (st != LIZARD_OK) return st;
+  if (s->L > 0 && workspace_bytes < lz::feature_workspace_bytes(s->B, s->H, s->L, s->d_k)) return LIZARD_EWORKSPACE;
+  lz::FeatArgs a{x, w, nullptr, dl, dx, dw, workspace, nullptr, s->B, s->H, s->L, 0};
+  return lz::launch_feature_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
 lizard_status_t lizard_distill_mse(const lizard_attn_shape_t* s, const void* q_t, const void* k_t,

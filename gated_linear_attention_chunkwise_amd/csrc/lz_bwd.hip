@@ -104,7 +104,9 @@ __device__ __forceinline__ f32x4 lds4(const bf16_t* p) {
 // Accumulators are kept transposed: acc[x][e] belongs to token 16*wb + r of
 // the chunk and column 16*x + 4*kg + e.
 // SG: one log-gate per head and token (g, dg [B,H,L]).
-template <typename T, int D, bool SG>
+// FEAT: the GLA branch reads fp32 log features lq, lk (q~ = exp(lq + b), k^ = exp(lk - b)) and
+// its q / k gradients leave as dlq = q~ dq~, dlk = k^ dk^; dq, dk keep the window part only.
+template <typename T, int D, bool SG, bool FEAT>
 __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
                                                             const float* __restrict__ wsbnd) {
   using LY = CkLayout<T, D>;
@@ -230,8 +232,12 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
     fetch_rows(rdo, dO, t0);
     fetch_rows(rv, v, t0);
     const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
-    GateStrip<T> gs;
-    if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
+    std::conditional_t<FEAT, GateStripLog<T>, GateStrip<T>> gs;
+    if constexpr (FEAT) {
+      if (has_strip) gs.template load<SG>(a.lq + hoff, a.lk + hoff, g, D, t0, L, 16 * w + 4 * kg, r);
+    } else {
+      if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
+    }
     if (qrole) {
       load_s(fs0, 0);
       if (KS > 1) load_s(fs1, 1);
@@ -392,8 +398,14 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
       const int i = 16 * x + 4 * kg;
-      *reinterpret_cast<f32x4*>(sDb + u * LDB + i) = lds4(sQt + u * LDQ + i) * acc0[x];
-      acc0[x] *= lds4(sEb + u * LDQ + i);
+      const f32x4 qd = lds4(sQt + u * LDQ + i) * acc0[x];
+      *reinterpret_cast<f32x4*>(sDb + u * LDB + i) = qd;
+      if constexpr (FEAT) {   // dlq = q~ dq~; the window part of dq starts from zero
+        if (tok < L) *reinterpret_cast<f32x4*>(a.dlq + hoff + (size_t)tok * D + i) = qd;
+        acc0[x] = f32x4{0, 0, 0, 0};
+      } else {
+        acc0[x] *= lds4(sEb + u * LDQ + i);
+      }
     }
   }
   __syncthreads();
@@ -402,12 +414,20 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
       const int i = 16 * x + 4 * kg;
-      db[x] = *reinterpret_cast<const f32x4*>(sDb + u * LDB + i) - lds4(sKh + u * LDQ + i) * acc0[x];
-      const f32x4 eb = lds4(sEb + u * LDQ + i);
+      const f32x4 kd = lds4(sKh + u * LDQ + i) * acc0[x];
+      db[x] = *reinterpret_cast<const f32x4*>(sDb + u * LDB + i) - kd;
+      if constexpr (FEAT) {   // dlk = k^ dk^; the window part of dk starts from zero
+        if (tok < L) *reinterpret_cast<f32x4*>(a.dlk + hoff + (size_t)tok * D + i) = kd;
+        acc0[x] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc0[x][e] *= __builtin_amdgcn_rcpf(eb[e]);
-        db[x][e] = row_suffix16(db[x][e]);
+        for (int e = 0; e < 4; ++e) db[x][e] = row_suffix16(db[x][e]);
+      } else {
+        const f32x4 eb = lds4(sEb + u * LDQ + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc0[x][e] *= __builtin_amdgcn_rcpf(eb[e]);
+          db[x][e] = row_suffix16(db[x][e]);
+        }
       }
       if (r == 0) *reinterpret_cast<f32x4*>(sTot + wb * D + i) = db[x];
     }
@@ -694,18 +714,22 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   mark(0);
   // the state-gradient sweep also forms the window row dots delta_t from the dO rows it streams
   {
-    const SweepArgs sw{a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr, a.B, a.H, a.L, 1, NC,
-                       nullptr, nullptr, nullptr, a.gate, a.o_swa, a.ws_delta, a.mix};
+    const bool feat = a.lq != nullptr;
+    const SweepArgs sw{feat ? (const void*)a.lq : a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr,
+                       a.B, a.H, a.L, 1, NC, nullptr, nullptr, nullptr, a.gate, feat ? 1 : 0, a.o_swa,
+                       a.ws_delta, a.mix};
     if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, true, st)) != hipSuccess) return e;
   }
   mark(1);
   {
     using LY = CkLayout<T, D>;
-    static bool attr[2] = {false, false};   // idempotent; a race only repeats the same call
-    auto kern = a.gate ? chunk_kernel<T, D, true> : chunk_kernel<T, D, false>;
-    if (!attr[a.gate ? 1 : 0]) {
+    static bool attr[3] = {false, false, false};   // idempotent; a race only repeats the same call
+    const int variant = a.lq != nullptr ? 2 : a.gate ? 1 : 0;   // log features: per-dimension gates only
+    auto kern = variant == 2 ? chunk_kernel<T, D, false, true>
+              : variant == 1 ? chunk_kernel<T, D, true, false> : chunk_kernel<T, D, false, false>;
+    if (!attr[variant]) {
       if ((e = set_lds(kern, LY::bytes)) != hipSuccess) return e;
-      attr[a.gate ? 1 : 0] = true;
+      attr[variant] = true;
     }
     hipLaunchKernelGGL(kern, dim3(BH * NC), dim3(NTHR_CK), LY::bytes, st, a, (const T*)wsdS, (const float*)wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;

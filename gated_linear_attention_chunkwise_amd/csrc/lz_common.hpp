@@ -383,4 +383,55 @@ struct GateStrip {
   }
 };
 
+// The same strip for log features lq, lk (fp32) of the GLA branch: the gate is absorbed in log
+// space, q~ = exp(lq + b), k^ = exp(lk - b).  Rows past the sequence end are loaded clamped and
+// given l = -inf at the fold, so their q~, k^ are exactly zero as in the raw form.
+template <typename T>
+struct GateStripLog {
+  f32x4 q[4], k[4];   // log features
+  f32x4 g[4];         // log-gates, then the inclusive prefix b
+  int nvalid;         // rows of this strip inside the sequence
+
+  template <bool SG>
+  __device__ __forceinline__ void load(const float* qp, const float* kp, const float* gp, int D, int t0, int L,
+                                       int col, int tg) {
+    static_assert(!SG, "log features are taken with per-dimension gates");
+    nvalid = L - t0 - 4 * tg;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t o = (size_t)min(t0 + 4 * tg + u, L - 1) * D + col;
+      q[u] = ld4raw(qp + o);
+      k[u] = ld4raw(kp + o);
+      g[u] = ld4raw(gp + o);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u >= nvalid) g[u] = f32x4{0, 0, 0, 0};   // no decay past the end (b stays finite)
+  }
+
+  __device__ __forceinline__ void fold(T* sQt, T* sKh, T* sEb, int ldq, int lcol, int tg) {
+#pragma unroll
+    for (int u = 1; u < 4; ++u) g[u] += g[u - 1];
+    f32x4 excl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) excl[e] = row_scan16(g[3][e]) - g[3][e];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = u < nvalid;
+      f32x4 eb, qt, kh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b = g[u][e] + excl[e];
+        eb[e] = __expf(b);
+        qt[e] = __expf((ok ? q[u][e] : -INFINITY) + b);
+        kh[e] = __expf((ok ? k[u][e] : -INFINITY) - b);
+      }
+      const int row = (4 * tg + u) * ldq + lcol;
+      st4(sQt + row, qt[0], qt[1], qt[2], qt[3]);
+      st4(sKh + row, kh[0], kh[1], kh[2], kh[3]);
+      if (sEb != nullptr) st4(sEb + row, eb[0], eb[1], eb[2], eb[3]);
+    }
+  }
+};
+
 }  // namespace lz

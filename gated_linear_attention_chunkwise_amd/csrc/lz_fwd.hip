@@ -88,7 +88,9 @@ struct OutLayout {
 
 // CONT: the segment continues a sequence (key history in the ring, position offset pos[b]).
 // SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
-template <typename T, int D, bool CONT, bool SG>
+// FEAT: the GLA branch reads the fp32 log features lq, lk of phi(q), phi(k) and absorbs the
+// gate in log space (q~ = exp(lq + b), k^ = exp(lk - b)); the window keeps the raw q, k.
+template <typename T, int D, bool CONT, bool SG, bool FEAT>
 __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __restrict__ cstates) {
   using LY = OutLayout<T, D>;
   using SM = ScanMap<D, Tr<T>::VEC, NTHR>;
@@ -140,13 +142,16 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   // ---- loads: this chunk's q, k, g (gate scan map), the first window tile, query operands
   const int cg = tid % SM::VPR, tg = tid / SM::VPR;
   V16 rq[TPT], rk[TPT];
+  f32x4 lqv[TPT][VEC / 4], lkv[TPT][VEC / 4];   // FEAT: log features of the GLA branch
   f32x4 rg[TPT][GV];
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
     const int t = t0 + tg * TPT + u;
     const bool ok = t < L;
-    rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
-    rk[u] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
+    if constexpr (!FEAT) {   // (log features are loaded just before the GLA fold)
+      rq[u] = ok ? ldg16(q + (size_t)t * D + cg * VEC) : zero16();
+      rk[u] = ok ? ldg16(k + (size_t)t * D + cg * VEC) : zero16();
+    }
 #pragma unroll
     for (int e = 0; e < GV; ++e)
       if constexpr (SG) {
@@ -304,6 +309,16 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   // ---- GLA branch
   __syncthreads();   // every wave is done with the last key tile
   {
+    if constexpr (FEAT) {
+#pragma unroll
+      for (int u = 0; u < TPT; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC / 4; ++e) {
+          const size_t o = hoff + (size_t)min(t0 + tg * TPT + u, L - 1) * D + cg * VEC + 4 * e;
+          lqv[u][e] = *reinterpret_cast<const f32x4*>(a.lq + o);
+          lkv[u][e] = *reinterpret_cast<const f32x4*>(a.lk + o);
+        }
+    }
     f32x4 tot[GV];
     chunk_prefix<D, VEC, NTHR, TPT, GV>(rg, tot, sScan, cg, tg);
 #pragma unroll
@@ -312,8 +327,14 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float bb = rg[u][e >> 2][e & 3];
-        qt[e] = v16_get(rq[u], e, (T*)nullptr) * __expf(bb);
-        kh[e] = v16_get(rk[u], e, (T*)nullptr) * __expf(-bb);
+        if constexpr (FEAT) {   // rows past the end: -inf, a zero operand as in the raw form
+          const bool in = t0 + tg * TPT + u < L;
+          qt[e] = __expf((in ? lqv[u][e >> 2][e & 3] : -INFINITY) + bb);
+          kh[e] = __expf((in ? lkv[u][e >> 2][e & 3] : -INFINITY) - bb);
+        } else {
+          qt[e] = v16_get(rq[u], e, (T*)nullptr) * __expf(bb);
+          kh[e] = v16_get(rk[u], e, (T*)nullptr) * __expf(-bb);
+        }
       }
       const int t = tg * TPT + u;
       st_vec(sK + t * LDQ + cg * VEC, qt);
@@ -406,8 +427,10 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const size_t segb = fwd_segment_bytes(a.B, a.H, a.L, D);
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
   void* states = a.chunk_states != nullptr ? a.chunk_states : ws + segb;
-  SweepArgs sw{a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in, a.B, a.H, a.L,
-               NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate, nullptr, nullptr, 0.f};
+  const bool feat = a.lk != nullptr;
+  SweepArgs sw{feat ? (const void*)a.lk : a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in,
+               a.B, a.H, a.L, NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate, feat ? 1 : 0,
+               nullptr, nullptr, 0.f};
   if (NS > 1) {
     const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
     sw.seg_in = reinterpret_cast<float*>(ws);
@@ -415,11 +438,14 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     sw.seg_gtot = reinterpret_cast<float*>(ws + 2 * mat);
   }
   if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, false, st)) != hipSuccess) return e;
-  const int variant = (a.pos != nullptr ? 1 : 0) + (a.gate ? 2 : 0);
-  decltype(&out_kernel<T, D, false, false>) kern =
-      variant == 0 ? out_kernel<T, D, false, false> : variant == 1 ? out_kernel<T, D, true, false>
-      : variant == 2 ? out_kernel<T, D, false, true> : out_kernel<T, D, true, true>;
-  static bool attr_set[4] = {false, false, false, false};   // idempotent; a race only repeats the same call
+  // variants: continuation, scalar gate, log features (these two only on a fresh sequence
+  // with per-dimension gates)
+  const int variant = feat ? 4 : (a.pos != nullptr ? 1 : 0) + (a.gate ? 2 : 0);
+  decltype(&out_kernel<T, D, false, false, false>) kern =
+      variant == 0 ? out_kernel<T, D, false, false, false> : variant == 1 ? out_kernel<T, D, true, false, false>
+      : variant == 2 ? out_kernel<T, D, false, true, false> : variant == 3 ? out_kernel<T, D, true, true, false>
+      : out_kernel<T, D, false, false, true>;
+  static bool attr_set[5] = {false, false, false, false, false};   // idempotent; a race only repeats the same call
   if (!attr_set[variant]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::bytes);

@@ -19,6 +19,9 @@ struct FwdArgs {
   int B, H, L, W, M;
   float scale, mix;
   int gate;             // 0: g [B,H,L,d] per key dimension; 1: g [B,H,L] one per head and token
+  // optional fp32 log features [B,H,L,d] of phi(q), phi(k) for the GLA branch (both or neither;
+  // per-dimension gates, no continuation); the window branch reads q and k
+  const float* lq; const float* lk;
 };
 
 struct BwdArgs {
@@ -33,6 +36,9 @@ struct BwdArgs {
   int B, H, L, W, M;
   float scale, mix;
   int gate;             // as in FwdArgs; dg has the shape of g
+  // optional log features as in FwdArgs, with their gradients dlq, dlk [B,H,L,d] fp32 written;
+  // dq, dk then hold the window branch's part only
+  const float* lq; const float* lk; float* dlq; float* dlk;
 };
 
 // One sequential sweep over chunks (lz_sweep.hip).  Forward: a_src = k,
@@ -56,6 +62,7 @@ struct SweepArgs {
   int NS, SC;
   float* seg_in; float* seg_fin; float* seg_gtot;
   int gate;             // as in FwdArgs
+  int feat;             // a_src is fp32 log features (per-dimension gates only)
   // backward: with delta set, the row blocks of each head also form the window row dots
   // delta_t = mix * dO_t . o_swa_t [B,H,L] fp32 from the dO rows they stream (each block a
   // share of the token rows)
@@ -92,6 +99,18 @@ struct DistillArgs {
   float scale, inv_n;
 };
 
+// Hedgehog feature map in log space (lz_feature.hip).  Forward: lphi [B,H,L,d] fp32 from
+// x [B,H,L,d] and w [H,d,d/2].  Backward: dx [B,H,L,d] (dtype) and dw [H,d,d/2] fp32 from dl.
+struct FeatArgs {
+  const void* x; const void* w;
+  float* lphi; const float* dl;
+  void* dx; float* dw;
+  void* workspace;      // backward: feature_workspace_bytes() bytes
+  float* dw_part;       // set by the launcher
+  int B, H, L;
+  int cpg;              // set by the launcher: (batch, chunk) slots per backward workgroup
+};
+
 // Each returns hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st);
@@ -100,6 +119,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_fwd_continue(const FwdArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_sweep(const SweepArgs& a, int dtype, int D, bool reverse, hipStream_t st);
 hipError_t launch_distill(const DistillArgs& a, int dtype, int D, hipStream_t st);
+hipError_t launch_feature_fwd(const FeatArgs& a, int dtype, int D, hipStream_t st);
+hipError_t launch_feature_bwd(const FeatArgs& a, int dtype, int D, hipStream_t st);   // L = 0: dw = 0
 hipError_t launch_gate_fwd(const GateArgs& a, int dtype, hipStream_t st);
 hipError_t launch_gate_bwd(const GateArgs& a, int dtype, hipStream_t st);   // L = 0: dw = 0
 
@@ -114,6 +135,8 @@ size_t decode_workspace_bytes(int B, int H, int D);
 // Workspace bytes needed by launch_gate_bwd: dz [B*L][Ng rounded up to 16 bytes] in the operand
 // dtype, then the fp32 partial sums of dW when its contraction over tokens is split.
 size_t gate_bwd_workspace_bytes(int B, int H, int L, int dk, int sg, int d_model, int dtype);
+// Workspace bytes needed by launch_feature_bwd: per-group partial sums of dw.
+size_t feature_workspace_bytes(int B, int H, int L, int D);
 // Workspace bytes needed by launch_distill: one fp32 partial per workgroup.
 size_t distill_workspace_bytes(int B, int H, int L);
 // Workspace bytes needed by launch_bwd.

@@ -75,7 +75,9 @@ struct SwStage {
 // REDUCE (forward only): carry a segment from a zero state and keep only its final
 // state and gate total (no chunk states).
 // SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
-template <typename T, int D, bool REV, bool REDUCE, bool SG>
+// FEAT: a_src holds fp32 log features l (of phi(k) forward, phi(q) backward); the gate is
+// absorbed in log space, exp(l + c), instead of scaling a raw operand by exp(c).
+template <typename T, int D, bool REV, bool REDUCE, bool SG, bool FEAT>
 __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) {
   using LY = SwLayout<T, D>;
   constexpr int NTI = D / TT;                      // tiles per edge
@@ -118,7 +120,8 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   const int L = a.L, NC = (L + CHUNK - 1) / CHUNK;
   const int c_begin = seg * a.SC, c_end = min(NC, c_begin + a.SC), NCs = c_end - c_begin;
   const size_t hoff = (size_t)bh * L * D;
-  const T* asrc = reinterpret_cast<const T*>(a.a_src) + hoff;
+  using AT = std::conditional_t<FEAT, float, T>;
+  const AT* asrc = reinterpret_cast<const AT*>(a.a_src) + hoff;
   const T* bsrc = reinterpret_cast<const T*>(a.b_src) + hoff;
   // backward: the row blocks of a head also form the window row dots of each chunk, the block of
   // state rows i0.. taking the token rows of its own register slots u with u % NTI == it
@@ -157,7 +160,9 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
       for (int u = 0; u < 4 && jt == 0; ++u) {
         const int t = t0 + 4 * tg + u;
         const size_t o = (size_t)t * D + acol;
-        s.ra[u] = t < L ? ld4f(asrc + o) : f32x4{0, 0, 0, 0};
+        // past the end: a zero operand (log features: -inf, whose exponential is zero)
+        const float fill = FEAT ? -INFINITY : 0.f;
+        s.ra[u] = t < L ? ld4f(asrc + o) : f32x4{fill, fill, fill, fill};
         if constexpr (SG) {
           const float x = t < L ? g[t] : 0.f;
           s.rg[u] = f32x4{x, x, x, x};
@@ -256,7 +261,8 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float b = s.rg[u][e] + excl[e];
-          x[e] = s.ra[u][e] * __expf(REV ? b : tot[e] - b);
+          const float c = REV ? b : tot[e] - b;
+          x[e] = FEAT ? __expf(s.ra[u][e] + c) : s.ra[u][e] * __expf(c);
         }
         st4(sA + (4 * tg + u) * LDA + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
       }
@@ -349,24 +355,26 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(SweepArgs a, int D) {
   }
 }
 
-template <typename T, int D, bool REV, bool SG>
+template <typename T, int D, bool REV, bool SG, bool FEAT>
 hipError_t launch_sweep_g(const SweepArgs& a, hipStream_t st) {
   using LY = SwLayout<T, D>;
   const int blocks = D / TT;                    // 64-row blocks of the state
   const int nthr = NTHR_SW * (D / TT);
   if (!REV && a.NS > 1) {
-    hipLaunchKernelGGL((sweep_kernel<T, D, false, true, SG>), dim3(a.B * a.H * blocks * (a.NS - 1)),
+    hipLaunchKernelGGL((sweep_kernel<T, D, false, true, SG, FEAT>), dim3(a.B * a.H * blocks * (a.NS - 1)),
                        dim3(nthr), LY::bytes, st, a);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(a.B * a.H * (D * D / 256)), dim3(256), 0, st, a, D);
   }
-  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false, SG>), dim3(a.B * a.H * blocks * a.NS), dim3(nthr),
+  hipLaunchKernelGGL((sweep_kernel<T, D, REV, false, SG, FEAT>), dim3(a.B * a.H * blocks * a.NS), dim3(nthr),
                      LY::bytes, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool REV>
 hipError_t launch_sweep_t(const SweepArgs& a, hipStream_t st) {
-  return a.gate ? launch_sweep_g<T, D, REV, true>(a, st) : launch_sweep_g<T, D, REV, false>(a, st);
+  // log features are taken with per-dimension gates only
+  if (a.feat) return a.gate ? hipErrorInvalidValue : launch_sweep_g<T, D, REV, false, true>(a, st);
+  return a.gate ? launch_sweep_g<T, D, REV, true, false>(a, st) : launch_sweep_g<T, D, REV, false, false>(a, st);
 }
 
 template <bool REV>

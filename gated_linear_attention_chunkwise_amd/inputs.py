@@ -32,6 +32,9 @@ w ~ N(0, 1) / sqrt(d_model) [Ng, d_model], so that every pre-activation is
 about N(0, 1) like the gate input of the recipe above; dg ~ N(0, 1) in the
 gate layout.  The train-shaped case is d_model = 4096 (the 8B-shaped layer
 with H = 32 heads of d = 128): Ng = 4096 per key dimension, 32 scalar.
+
+Log features for the GLA branch (``make_log_features``): lq, lk ~
+N(-log(d/2), 0.5^2) fp32, the spread of a softmax over d/2 features.
 """
 from __future__ import annotations
 
@@ -158,6 +161,25 @@ def make_gate_device(B: int, L: int, d_model: int, ng: int, dg_shape, *, seed: i
          float(np.sqrt(d_model))).to(dtype)
     dg = torch.randn(tuple(dg_shape), generator=gen, device=device, dtype=torch.float32)
     return {"x": x, "w": w, "dg": dg}
+
+
+def make_log_features(shape, *, seed: int) -> dict:
+    """Log features lq, lk for the GLA branch's feature-map inputs: ~ N(-log(d/2), 0.5^2) each
+    (the spread of a softmax over d/2 features), fp32."""
+    rng = np.random.default_rng(seed)
+    mu = -np.log(shape[-1] / 2.0)
+    return {"lq": (rng.standard_normal(shape) * 0.5 + mu).astype(np.float32),
+            "lk": (rng.standard_normal(shape) * 0.5 + mu).astype(np.float32)}
+
+
+def make_log_features_device(shape, *, seed: int, device) -> dict:
+    """The same law drawn on the device with a seeded torch generator."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    mu = -float(np.log(shape[-1] / 2.0))
+    return {n: torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32) * 0.5 + mu
+            for n in ("lq", "lk")}
 
 
 def make_inputs_device(w: Workload, device, *, with_grad: bool = False, L: int | None = None,

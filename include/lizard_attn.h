@@ -91,7 +91,7 @@ typedef struct {
 } lizard_attn_shape_t;
 
 enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2, LIZARD_OP_FWD_CONTINUE = 3,
-       LIZARD_OP_DISTILL = 4 };
+       LIZARD_OP_DISTILL = 4, LIZARD_OP_FEATURE_BWD = 5 };
 
 /* Bytes of device workspace that `op` needs for shape `s` (0 when none, or
  * when `s` is invalid).  Pass at least this many bytes to the call. */
@@ -152,6 +152,60 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 float* dmeta_k, float* dmeta_v,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* stage_events);
+
+/* Forward and backward with a feature map on the GLA branch.  The branch keeps
+ * its state from feature-mapped keys, S_t = Gamma_t S_{t-1} + phi(k_t) v_t^T,
+ * read by phi(q_t) (English page §2.A, state update), and the pages absorb the
+ * cumulative gate into the query and key projections in log space, which the
+ * feature map's non-negativity allows (Chinese page §2.3; English page §2.C).
+ * These calls take the logarithms of the features and form
+ *   q~ = exp(lq + b),  k^ = exp(lk - b)   (b: chunk-local gate prefix)
+ * directly, so no feature, however small, is rounded before the gate meets it.
+ * The anchor window keeps the raw q and k; v is shared.
+ *   lq, lk   [B,H,L,d_k] fp32: log phi(q), log phi(k) (e.g. from a Hedgehog map)
+ *   dlq, dlk [B,H,L,d_k] fp32, written: gradients of lq and lk
+ *   dq, dk   written: the window branch's gradients of q and k only
+ * Everything else is as for lizard_attn_fwd / lizard_attn_bwd; per-dimension
+ * gates only (LIZARD_GATE_SCALAR returns LIZARD_EUNSUPPORTED). */
+lizard_status_t lizard_attn_fwd_feat(const lizard_attn_shape_t* s,
+                                     const void* q, const void* k, const void* v,
+                                     const float* lq, const float* lk, const float* g,
+                                     const void* meta_k, const void* meta_v,
+                                     void* o, float* lse, void* o_swa, void* chunk_states,
+                                     float* state_out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+lizard_status_t lizard_attn_bwd_feat(const lizard_attn_shape_t* s,
+                                     const void* q, const void* k, const void* v,
+                                     const float* lq, const float* lk, const float* g,
+                                     const void* meta_k, const void* meta_v, const void* dO,
+                                     const float* lse, const void* o_swa, const void* chunk_states,
+                                     void* dq, void* dk, void* dv, float* dlq, float* dlk, float* dg,
+                                     float* dmeta_k, float* dmeta_v,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     hipEvent_t* stage_events);
+
+/* Hedgehog feature map in log space, the input of the *_feat calls above.  The
+ * pages name the GLA branch's feature map a Hedgehog map and rely on its
+ * non-negativity (Chinese page §2.3); they do not print it.  This is its
+ * two-sided softmax form, per head h:
+ *
+ *   log phi(x) = [ z - lse(z),  -z - lse(-z) ],  z = x W_h  (d/2 features each half)
+ *
+ *   s      validated as for lizard_attn_fwd; uses B, H, L, d_k and dtype
+ *   x      [B,H,L,d_k] dtype (q or k of the layer)
+ *   w      [H,d_k,d_k/2] dtype, row-major per head
+ *   lphi   written, [B,H,L,d_k] fp32
+ * Backward, from dl = dL/dlog phi ([B,H,L,d_k] fp32):
+ *   dx     written, [B,H,L,d_k] dtype (the feature map's part only)
+ *   dw     written, [H,d_k,d_k/2] fp32, summed over batch and tokens in a fixed order
+ *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_FEATURE_BWD) bytes of
+ *          caller-owned device memory (per-group partial sums of dw)
+ * L = 0: the forward writes nothing, the backward writes dw = 0. */
+lizard_status_t lizard_hedgehog_fwd(const lizard_attn_shape_t* s, const void* x, const void* w, float* lphi,
+                                    hipStream_t stream);
+lizard_status_t lizard_hedgehog_bwd(const lizard_attn_shape_t* s, const void* x, const void* w, const float* dl,
+                                    void* dx, float* dw, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* Chunked prefill: the forward of the next L tokens of every sequence, resuming
  * from the carry that earlier segments or decode steps left.  The state update

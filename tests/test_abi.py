@@ -17,7 +17,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = range(6)
 
 def declared_functions():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_(?:attn|gate|distill)_[a-z_]+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^[a-z_][a-z_0-9 ]*[\s\*]+(lizard_(?:attn|gate|distill|hedgehog)_[a-z_]+)\s*\(", txt, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step",
                           "lizard_attn_fwd_continue", "lizard_attn_workspace_bytes",
                           "lizard_attn_status_string", "lizard_gate_proj_fwd", "lizard_gate_proj_bwd",
-                          "lizard_gate_proj_workspace_bytes", "lizard_distill_mse"}
+                          "lizard_gate_proj_workspace_bytes", "lizard_distill_mse", "lizard_attn_fwd_feat",
+                          "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(pkg.SYMBOLS) == set(names)
@@ -153,7 +154,7 @@ def test_workspace_query(lib):
     assert lib.lizard_attn_workspace_bytes(None, 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(d_k=96, d_v=96)), 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 0) == 0
-    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 5) == 0
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 6) == 0       # unknown op
 
 
 def test_gate_proj_validation(lib):
@@ -211,3 +212,37 @@ def test_distill_validation(lib):
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(B=2, H=3, L=300)), 4) == 2 * 3 * 3 * 4
     assert call(ws_bytes=4 * 2 - 1) == EWORKSPACE             # B=1 H=2 L=128: two partials
     assert call(ws=None) == EINVAL
+
+
+def test_feature_entry_points_validation(lib):
+    s = shape()
+    def fwdf(s=s, lq=GOOD, lk=GOOD):
+        return lib.lizard_attn_fwd_feat(ctypes.byref(s), GOOD, GOOD, GOOD, lq, lk, GOOD, GOOD, None, GOOD, None,
+                                        None, GOOD, None, None, 0, None)
+    assert fwdf(lq=None) == EINVAL
+    assert fwdf(lk=None) == EINVAL
+    assert fwdf(lq=BAD) == EALIGN
+    assert fwdf(s=shape(gate=1)) == EUNSUPPORTED
+    assert fwdf(s=shape(d_k=96, d_v=96)) == EUNSUPPORTED
+    def bwdf(dlq=GOOD, dlk=GOOD, s=s):
+        return lib.lizard_attn_bwd_feat(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD,
+                                        GOOD, GOOD, GOOD, GOOD, GOOD, dlq, dlk, GOOD, GOOD, None, GOOD, 1 << 40,
+                                        None, None)
+    assert bwdf(dlq=None) == EINVAL
+    assert bwdf(dlk=BAD) == EALIGN
+    assert bwdf(s=shape(gate=1)) == EUNSUPPORTED
+
+
+def test_hedgehog_validation(lib):
+    s = shape()
+    assert lib.lizard_hedgehog_fwd(ctypes.byref(s), None, GOOD, GOOD, None) == EINVAL
+    assert lib.lizard_hedgehog_fwd(ctypes.byref(s), GOOD, GOOD, BAD, None) == EALIGN
+    assert lib.lizard_hedgehog_fwd(ctypes.byref(shape(d_k=96, d_v=96)), GOOD, GOOD, GOOD, None) == EUNSUPPORTED
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 5)
+    assert need > 0
+    def bw(ws=GOOD, nb=need, dx=GOOD):
+        return lib.lizard_hedgehog_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, dx, GOOD, ws, nb, None)
+    assert bw(dx=None) == EINVAL
+    assert bw(ws=None) == EINVAL
+    assert bw(nb=need - 1) == EWORKSPACE
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 5) == 0
