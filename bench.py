@@ -10,8 +10,10 @@ workload (B=64 sequences after a 4096-token prefill) and reported under
 "decode"; the 65 536-token prefill, one shot and as continued segments, under
 "prefill"; the training step with one gate per head and token under
 "scalar_gate"; the gate projection g = log sigmoid(x W^T)/tau that feeds
-the layer, per key dimension and scalar, under "gate_proj".  Prints one
-JSON line.
+the layer, per key dimension and scalar, under "gate_proj"; the stage-1
+attention-approximation step (layer forward, teacher attention + MSE, layer
+backward) under "stage1"; the layer with a Hedgehog feature map on its GLA
+branch under "features".  Prints one JSON line.
 
 Per-kernel times come from HIP events recorded on the stream the kernels
 run on; the backward records them between its kernels through the
@@ -391,6 +393,102 @@ def bench_gate_proj(args, hip, torch, lib):
     return out
 
 
+def bench_stage1(args, hip, torch, lib, x, w):
+    """The stage-1 attention-approximation step at the train shape: the layer forward, the teacher's
+    causal softmax attention with the MSE fused in (lizard_distill_mse), the layer backward from dO."""
+    stream = torch.cuda.current_stream().cuda_stream
+    ws = torch.empty(w.B * w.H * ((w.L + 127) // 128) * 4, device="cuda", dtype=torch.uint8)
+
+    def step(ev=None):
+        f = lib.lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=w.W, scale=w.scale,
+                                want_lse=True, want_o_swa=True, want_chunk_states=True)
+        if ev:
+            hip.record(ev[0], stream)
+        ls = lib.lizard_distill_mse(x["q"], x["k"], x["v"], f["o"], scale=w.scale, workspace=ws)
+        if ev:
+            hip.record(ev[1], stream)
+        lib.lizard_attn_bwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, ls["dO"], f["lse"], f["o_swa"],
+                            f["chunk_states"], window=w.W, scale=w.scale)
+
+    for _ in range(2):
+        step()
+    steps = max(2, min(args.steps, 10))
+    evs = [[hip.event() for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for k in range(steps):
+        step(evs[k])
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    t_mse = sum(hip.ms(ev[0], ev[1]) for ev in evs) / steps
+    flop = 4.0 * w.B * w.H * w.D * w.L * (w.L + 1) / 2     # teacher Q K^T and P V over the causal triangle
+    tf = flop / (t_mse * 1e-3) / 1e12
+    return {"workload": f"stage-1 step at train_8k: B={w.B} H={w.H} L={w.L} d={w.D} W={w.W} M={w.M}; teacher = "
+                        "causal softmax attention of the same q, k, v",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+            "teacher_mse_ms": round(t_mse, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "kernel": "teacher_mse_kernel (causal attention + MSE epilogue)", "algorithmic_flop": flop}}
+
+
+def bench_features(args, hip, torch, lib, x, w):
+    """The layer with a Hedgehog feature map on the GLA branch at the train shape: the map for q and
+    k (log features), the log-feature layer forward + backward, the map's backward for q and k."""
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    Wq = (torch.randn(w.H, w.D, w.D // 2, generator=gen, device="cuda") * 8.0 / math.sqrt(w.D)).to(x["q"].dtype)
+    Wk = (torch.randn(w.H, w.D, w.D // 2, generator=gen, device="cuda") * 8.0 / math.sqrt(w.D)).to(x["q"].dtype)
+    ws = torch.empty(lib.workspace_bytes(lib.make_shape(w.B, w.H, w.L, w.D, 1, 0, 1.0, 1.0, x["q"].dtype),
+                                         lib.OP_FEATURE_BWD), device="cuda", dtype=torch.uint8)
+
+    def step(ev=None):
+        if ev:
+            hip.record(ev[0], stream)
+        lq = lib.lizard_hedgehog_fwd(x["q"], Wq)
+        lk = lib.lizard_hedgehog_fwd(x["k"], Wk)
+        if ev:
+            hip.record(ev[1], stream)
+        f = lib.lizard_attn_fwd_feat(x["q"], x["k"], x["v"], lq, lk, x["g"], x["meta_k"], None, window=w.W,
+                                     scale=w.scale, want_lse=True, want_o_swa=True, want_chunk_states=True)
+        b = lib.lizard_attn_bwd_feat(x["q"], x["k"], x["v"], lq, lk, x["g"], x["meta_k"], None, x["dO"], f["lse"],
+                                     f["o_swa"], f["chunk_states"], window=w.W, scale=w.scale)
+        if ev:
+            hip.record(ev[2], stream)
+        lib.lizard_hedgehog_bwd(x["q"], Wq, b["dlq"], workspace=ws)
+        lib.lizard_hedgehog_bwd(x["k"], Wk, b["dlk"], workspace=ws)
+        if ev:
+            hip.record(ev[3], stream)
+
+    for _ in range(2):
+        step()
+    steps = max(2, min(args.steps, 10))
+    evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t = [sum(hip.ms(ev[i], ev[i + 1]) for ev in evs) / steps for i in range(3)]
+    ms = sum(t)
+    ht = w.B * w.H * w.L
+    # feature map: x bf16 in, fp32 log features out (forward); x, fp32 dl in, dx out (backward); q and k each
+    fbytes = 2 * ht * (2 * w.D + 4 * w.D)
+    bbytes = 2 * ht * (2 * w.D + 4 * w.D + 2 * w.D)
+    gbs = (fbytes + bbytes) / ((t[0] + t[2]) * 1e-3) / 1e9
+    return {"workload": f"train_8k with a Hedgehog map on the GLA branch (log features, W_q, W_k [{w.H},{w.D},"
+                        f"{w.D // 2}]); map forward for q, k + layer forward/backward + map backward for q, k",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+            "feature_map_fwd_ms": round(t[0], 4), "layer_fwd_bwd_ms": round(t[1], 4),
+            "feature_map_bwd_ms": round(t[2], 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "hedgehog_fwd_kernel + hedgehog_bwd_kernel (q and k)",
+                         "algorithmic_bytes": fbytes + bbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +498,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-scalar-gate", action="store_true")
     ap.add_argument("--no-gate-proj", action="store_true")
+    ap.add_argument("--no-stage1", action="store_true")
+    ap.add_argument("--no-features", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
@@ -439,6 +539,10 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads)
     if not args.no_scalar_gate:
         rec["scalar_gate"] = bench_scalar_gate(args, hip, torch, lib, x, w)
+    if not args.no_stage1:
+        rec["stage1"] = bench_stage1(args, hip, torch, lib, x, w)
+    if not args.no_features:
+        rec["features"] = bench_features(args, hip, torch, lib, x, w)
     del x
     torch.cuda.empty_cache()
     if not args.no_decode:
