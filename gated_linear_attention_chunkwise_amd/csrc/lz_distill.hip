@@ -147,7 +147,40 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
     const T* sK = reinterpret_cast<const T*>(smem + (2 * stage) * LY::tile);
     const T* sV = reinterpret_cast<const T*>(smem + (2 * stage + 1) * LY::tile);
     const int kbase = kt * TK;
-    if (kbase <= qw + 31) {   // some key of the tile is visible to this wave's queries
+    if (kbase + TK - 1 <= qw) {
+      // every key of the tile precedes every query of the wave: no mask, no branch, no drain
+      f32x4 x[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        x[0][kb] = f32x4{0, 0, 0, 0};
+        x[1][kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const frag kf = ld_frag(sK, LDQ, 16 * kb + r, 32 * ks + 8 * kg);
+          mma32(x[0][kb], kf, qf[0][ks]);
+          mma32(x[1][kb], kf, qf[1][ks]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) x[b][kb] *= sl2;
+        te_absorb<JB>(x[b], mrun[b], lpart[b], O[b]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        frag bop[2];
+        pack_acc(bop[0], x[0][2 * p], x[0][2 * p + 1]);
+        pack_acc(bop[1], x[1][2 * p], x[1][2 * p + 1]);
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const frag vf = ld_frag_tr(sV, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane);
+          mma32(O[0][jb], vf, bop[0]);
+          mma32(O[1][jb], vf, bop[1]);
+        }
+      }
+      mfma_drain();   // the block ends in control flow
+    } else if (kbase <= qw + 31) {   // the diagonal: some keys are visible to some queries
       bool vis[2][4];
       f32x4 x[2][4];
 #pragma unroll
