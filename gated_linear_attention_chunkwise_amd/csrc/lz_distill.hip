@@ -30,7 +30,11 @@ namespace {
 
 constexpr int TQ = 128;        // queries per workgroup
 constexpr int TK = 64;         // keys per tile
-constexpr int NTHR_TE = 256;
+// four waves of 32 queries: eight waves of 16 read the same K and V tiles for half the
+// queries each (slower), two waves of 64 do not fit their tiles and accumulators in registers
+constexpr int NW_TE = 4;                   // waves per workgroup
+constexpr int NQB_TE = TQ / (16 * NW_TE);  // 16-query blocks per wave
+constexpr int NTHR_TE = 64 * NW_TE;
 
 template <typename T, int D>
 struct TeLayout {
@@ -38,6 +42,7 @@ struct TeLayout {
   static constexpr size_t tile = sizeof(T) * TK * LDQ;
   static constexpr size_t bytes = 4 * tile;   // stage s: keys at 2s, values at 2s + 1
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+  static_assert(NQB_TE * 16 * NW_TE == TQ, "query blocks");
 };
 
 // Online-softmax update of one query row (this lane's query) with four key
@@ -78,6 +83,7 @@ __device__ __forceinline__ f32x4 ldg4f(const bf16_t* p) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) {
+  constexpr int NQ = NQB_TE, QW = 16 * NQ;        // query blocks / queries per wave
   using LY = TeLayout<T, D>;
   using frag = typename Tr<T>::frag;
   constexpr int VEC = Tr<T>::VEC, LDQ = LY::LDQ;
@@ -98,12 +104,14 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
   const T* k = reinterpret_cast<const T*>(a.k) + hoff;
   const T* v = reinterpret_cast<const T*>(a.v) + hoff;
   const float sl2 = a.scale * LOG2E;
-  const int q0 = qb * TQ, qw = q0 + 32 * w;       // first query of the block / of this wave
-  const int tq[2] = {qw + r, qw + 16 + r};        // this lane's queries
-
-  frag qf[2][KS];
+  const int q0 = qb * TQ, qw = q0 + QW * w;       // first query of the block / of this wave
+  int tq[NQ];                                     // this lane's queries
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < NQ; ++b) tq[b] = qw + 16 * b + r;
+
+  frag qf[NQ][KS];
+#pragma unroll
+  for (int b = 0; b < NQ; ++b)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[b][ks] = ldg_row_frag<T>(q, D, tq[b], 32 * ks + 8 * kg, L);
 
@@ -129,12 +137,15 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
     }
   };
 
-  f32x4 O[2][JB];
+  f32x4 O[NQ][JB];
+  float mrun[NQ], lpart[NQ];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < NQ; ++b) {
 #pragma unroll
     for (int j = 0; j < JB; ++j) O[b][j] = f32x4{0, 0, 0, 0};
-  float mrun[2] = {-INFINITY, -INFINITY}, lpart[2] = {0.f, 0.f};
+    mrun[b] = -INFINITY;
+    lpart[b] = 0.f;
+  }
 
   const int ktmax = min(L - 1, q0 + TQ - 1) / TK;   // last key tile the block sees
   load_tile(0);
@@ -149,59 +160,61 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
     const int kbase = kt * TK;
     if (kbase + TK - 1 <= qw) {
       // every key of the tile precedes every query of the wave: no mask, no branch, no drain
-      f32x4 x[2][4];
+      f32x4 x[NQ][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        x[0][kb] = f32x4{0, 0, 0, 0};
-        x[1][kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < NQ; ++b) x[b][kb] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const frag kf = ld_frag(sK, LDQ, 16 * kb + r, 32 * ks + 8 * kg);
-          mma32(x[0][kb], kf, qf[0][ks]);
-          mma32(x[1][kb], kf, qf[1][ks]);
+#pragma unroll
+          for (int b = 0; b < NQ; ++b) mma32(x[b][kb], kf, qf[b][ks]);
         }
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < NQ; ++b) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) x[b][kb] *= sl2;
         te_absorb<JB>(x[b], mrun[b], lpart[b], O[b]);
       }
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        frag bop[2];
-        pack_acc(bop[0], x[0][2 * p], x[0][2 * p + 1]);
-        pack_acc(bop[1], x[1][2 * p], x[1][2 * p + 1]);
+        frag bop[NQ];
+#pragma unroll
+        for (int b = 0; b < NQ; ++b) pack_acc(bop[b], x[b][2 * p], x[b][2 * p + 1]);
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
           const frag vf = ld_frag_tr(sV, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane);
-          mma32(O[0][jb], vf, bop[0]);
-          mma32(O[1][jb], vf, bop[1]);
+#pragma unroll
+          for (int b = 0; b < NQ; ++b) mma32(O[b][jb], vf, bop[b]);
         }
       }
       mfma_drain();   // the block ends in control flow
-    } else if (kbase <= qw + 31) {   // the diagonal: some keys are visible to some queries
-      bool vis[2][4];
-      f32x4 x[2][4];
+    } else if (kbase <= qw + QW - 1) {   // the diagonal: some keys are visible to some queries
+      bool vis[NQ][4];
+      f32x4 x[NQ][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int s0 = kbase + 16 * kb;
-        vis[0][kb] = s0 <= qw + 15;
-        vis[1][kb] = s0 <= qw + 31;
-        x[0][kb] = f32x4{0, 0, 0, 0};
-        x[1][kb] = f32x4{0, 0, 0, 0};
-        if (vis[1][kb]) {
+#pragma unroll
+        for (int b = 0; b < NQ; ++b) {
+          vis[b][kb] = s0 <= qw + 16 * b + 15;
+          x[b][kb] = f32x4{0, 0, 0, 0};
+        }
+        if (vis[NQ - 1][kb]) {   // the last block sees every key an earlier block sees
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const frag kf = ld_frag(sK, LDQ, 16 * kb + r, 32 * ks + 8 * kg);
-            mma32(x[1][kb], kf, qf[1][ks]);
-            if (vis[0][kb]) mma32(x[0][kb], kf, qf[0][ks]);
+#pragma unroll
+            for (int b = 0; b < NQ; ++b)
+              if (vis[b][kb]) mma32(x[b][kb], kf, qf[b][ks]);
           }
           mfma_drain();
         }
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < NQ; ++b) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -213,16 +226,20 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
       }
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        if (!(vis[1][2 * p] || vis[1][2 * p + 1])) continue;
-        frag bop[2];
-        pack_acc(bop[0], x[0][2 * p], x[0][2 * p + 1]);
-        pack_acc(bop[1], x[1][2 * p], x[1][2 * p + 1]);
-        const bool v0 = vis[0][2 * p] || vis[0][2 * p + 1];
+        if (!(vis[NQ - 1][2 * p] || vis[NQ - 1][2 * p + 1])) continue;
+        frag bop[NQ];
+        bool vb[NQ];
+#pragma unroll
+        for (int b = 0; b < NQ; ++b) {
+          pack_acc(bop[b], x[b][2 * p], x[b][2 * p + 1]);
+          vb[b] = vis[b][2 * p] || vis[b][2 * p + 1];
+        }
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
           const frag vf = ld_frag_tr(sV, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane);
-          mma32(O[1][jb], vf, bop[1]);
-          if (v0) mma32(O[0][jb], vf, bop[0]);
+#pragma unroll
+          for (int b = 0; b < NQ; ++b)
+            if (vb[b]) mma32(O[b][jb], vf, bop[b]);
         }
         mfma_drain();
       }
@@ -237,7 +254,7 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
   const float g2 = 2.f * a.inv_n;
   float sq = 0.f;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < NQ; ++b) {
     const float l = xor_sum(xor_sum(lpart[b], 16), 32);
     const float inv = 1.f / l;
     if (tq[b] < L) {
