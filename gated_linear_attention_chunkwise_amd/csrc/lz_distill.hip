@@ -58,12 +58,14 @@ __device__ __forceinline__ void te_absorb(f32x4 (&x)[4], float& mrun, float& lpa
   mx = xor_max(mx, 16);
   mx = xor_max(mx, 32);
   const float mnew = fmaxf(mrun, mx);
-  const float alpha = (mrun == -INFINITY) ? 0.f : fast_exp2(mrun - mnew);
+  if (__any(mnew != mrun)) {   // wave-uniform: rescale only when some query's running max moved
+    const float alpha = (mrun == -INFINITY) ? 0.f : fast_exp2(mrun - mnew);
+    lpart *= alpha;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) O[j] *= alpha;
+  }
   const float mref = (mnew == -INFINITY) ? 0.f : mnew;
   mrun = mnew;
-  lpart *= alpha;
-#pragma unroll
-  for (int j = 0; j < JB; ++j) O[j] *= alpha;
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
