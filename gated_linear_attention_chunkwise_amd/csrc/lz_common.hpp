@@ -152,8 +152,39 @@ __device__ __forceinline__ float v16_get(const V16& v, int e, bf16_t*) {
 }
 
 // ------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, WAVE)); }
-__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, WAVE); }
+// Reductions over lane pairs (l, l ^ m).  For m = 16 and m = 32 they use the gfx950 row
+// swap instead of the LDS permute path: swapping a register with a copy of itself (the odd
+// 16-lane rows, or the upper 32 lanes, of one copy trading places with the even rows, or the
+// lower 32 lanes, of the other) leaves each lane holding its own value in one copy and its
+// partner's in the other, so max and sum of the two copies are the pair's max and sum.
+__device__ __forceinline__ void swap_pair(float x, int m, float& a, float& b) {
+  const unsigned u = __float_as_uint(x);
+  if (m == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+__device__ __forceinline__ float xor_max(float x, int m) {
+  if (m == 16 || m == 32) {
+    float a, b;
+    swap_pair(x, m, a, b);
+    return fmaxf(a, b);
+  }
+  return fmaxf(x, __shfl_xor(x, m, WAVE));
+}
+__device__ __forceinline__ float xor_sum(float x, int m) {
+  if (m == 16 || m == 32) {
+    float a, b;
+    swap_pair(x, m, a, b);
+    return a + b;
+  }
+  return x + __shfl_xor(x, m, WAVE);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
