@@ -219,6 +219,17 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_row<0x121>(x);
   return x;
 }
+// Max over the 16 lanes of each row, returned in every lane of the row.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_row<0x128>(x));
+  x = fmaxf(x, dpp_row<0x124>(x));
+  x = fmaxf(x, dpp_row<0x122>(x));
+  x = fmaxf(x, dpp_row<0x121>(x));
+  return x;
+}
+// Max / sum over the whole wave, returned in every lane: rows by DPP, then the row swaps.
+__device__ __forceinline__ float wave_max(float x) { return xor_max(xor_max(row_max16(x), 16), 32); }
+__device__ __forceinline__ float wave_sum(float x) { return xor_sum(xor_sum(row_sum16(x), 16), 32); }
 // Sum over aligned groups of N consecutive lanes, returned in every lane of the group.
 template <int N>
 __device__ __forceinline__ float group_sum(float x);

@@ -184,8 +184,7 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) lmax = xor_max(lmax, m);
+  lmax = wave_max(lmax);
   if (lane == 0) sstat[0][wv] = lmax;
   __syncthreads();
   float pmax = sstat[0][0];
@@ -205,8 +204,7 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
       lsum += p;
     }
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) lsum = xor_sum(lsum, m);
+  lsum = wave_sum(lsum);
   __syncthreads();   // probabilities visible; sstat[0] read by every thread
   if (lane == 0) sstat[1][wv] = lsum;
 
