@@ -187,6 +187,9 @@ def bench_train(args, hip, torch, lib):
             "mfma_frac": round(flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
             "hbm_frac": round(bytes_step / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
             "ideal_ms": round(max(flops_step / (PEAK_BF16_TFLOPS * 1e12), bytes_step / (PEAK_HBM_GBS * 1e9)) * 1e3, 4),
+            # fraction of the attainable roofline: max(FLOP/peak, bytes/bandwidth) / measured time
+            "attainable_frac": round(max(flops_step / (PEAK_BF16_TFLOPS * 1e12),
+                                         bytes_step / (PEAK_HBM_GBS * 1e9)) / (ms_step * 1e-3), 4),
         },
     }, x
 
@@ -266,6 +269,32 @@ def bench_decode(args, hip, torch, lib):
     hip.record(e1, stream)
     torch.cuda.synchronize()
     us = hip.ms(e0, e1) * 1e3 / steps
+    # cold cache: the state and ring (268 MB) nearly fit the 256 MB last-level cache, so back-to-back
+    # steps may read part of them from it.  Each of these steps runs on its own after a
+    # synchronisation; "isolated" follows nothing else, "cold" follows a read of 1 GiB elsewhere
+    # (clean lines: nothing left to write back), so their difference is the cache's share.
+    flush = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    cold, iso = [], []
+    ncold = min(16, steps)
+
+    def one_step(t):
+        ea, eb = hip.event(), hip.event()
+        hip.record(ea, stream)
+        lib.lizard_attn_decode_step(tok["q"][t], tok["k"][t], tok["v"][t], tok["g"][t], mk,
+                                    None, state, ring_k, ring_v, pos, window=w.W, scale=w.scale, out=out[t],
+                                    workspace=ws)
+        hip.record(eb, stream)
+        torch.cuda.synchronize()
+        return hip.ms(ea, eb) * 1e3
+
+    for t in range(ncold):
+        torch.cuda.synchronize()
+        iso.append(one_step(t))
+        float(flush.max())
+        cold.append(one_step(t))
+    del flush
+    us_cold = sorted(cold)[len(cold) // 2]
+    us_iso = sorted(iso)[len(iso) // 2]
     d = w.D
     bytes_step = (2 * w.B * w.H * d * d * 4 + 2 * w.B * w.H * w.W * d * 2
                   + 4 * w.B * w.H * d * 2 + w.B * w.H * d * 4 + 2 * w.B * w.H * d * 2)
@@ -273,6 +302,11 @@ def bench_decode(args, hip, torch, lib):
     return {"workload": f"decode_b64: B={w.B} H={w.H} d={d} fp32 state, W={w.W} bf16 ring, M={w.M}; "
                         f"{steps} steps after a {P}-token prefill",
             "tokens_per_s": round(w.B / (us * 1e-6), 1), "us_per_step": round(us, 2),
+            "cold_cache": {"us_per_step_median": round(us_cold, 2), "isolated_us_per_step_median": round(us_iso, 2),
+                           "steps": ncold,
+                           "hbm_frac": round(bytes_step / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                           "method": "single steps after a synchronisation, with (cold) and without (isolated) "
+                                     "a read of 1 GiB elsewhere first"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode"),
                          "kernel": "decode_kernel + decode_combine_kernel",
