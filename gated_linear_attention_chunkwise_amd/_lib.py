@@ -23,7 +23,8 @@ GATE_PER_DIM, GATE_SCALAR = 0, 1
 SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
            "lizard_attn_workspace_bytes", "lizard_attn_status_string", "lizard_gate_proj_fwd",
            "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes", "lizard_distill_mse",
-           "lizard_attn_fwd_feat", "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd")
+           "lizard_attn_fwd_feat", "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd",
+           "lizard_attn_fwd_continue_feat", "lizard_attn_decode_step_feat")
 
 
 class Shape(ctypes.Structure):
@@ -68,6 +69,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_feat.restype = I32
     lib.lizard_attn_bwd_feat.argtypes = [SP] + [P] * 21 + [SZ, P, P]
     lib.lizard_attn_bwd_feat.restype = I32
+    lib.lizard_attn_fwd_continue_feat.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_fwd_continue_feat.restype = I32
+    lib.lizard_attn_decode_step_feat.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lizard_attn_decode_step_feat.restype = I32
     lib.lizard_hedgehog_fwd.argtypes = [SP, P, P, P, P]
     lib.lizard_hedgehog_fwd.restype = I32
     lib.lizard_hedgehog_bwd.argtypes = [SP, P, P, P, P, P, P, SZ, P]
@@ -389,6 +394,68 @@ def lizard_attn_bwd_feat(q, k, v, lq, lk, g, meta_k, meta_v, dO, lse, o_swa, chu
                                     _ptr(out["dmeta_v"]), _ptr(ws), ws_bytes, _stream(dev),
                                     _events(stage_events, BWD_STAGES + 1)))
     return out
+
+
+def lizard_attn_fwd_continue_feat(q, k, v, lq, lk, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
+                                  window: int, scale: float | None = None, mix: float = 1.0, out=None,
+                                  workspace=None):
+    """lizard_attn_fwd_continue with GLA log features lq, lk (fp32 [B,H,L,d]); returns o."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v)):
+        _need(t, n, dt, dev)
+    for n, t in (("lq", lq), ("lk", lk), ("g", g), ("state", state)):
+        _need(t, n, torch.float32, dev)
+    _need(pos, "pos", torch.int32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, L, d = q.shape
+    if not (k.shape == v.shape == lq.shape == lk.shape == g.shape == q.shape):
+        raise ValueError("q, k, v, lq, lk and g must share one [B,H,L,d] shape")
+    if state.shape != (B, H, d, d) or ring_k.shape != (B, H, window, d) or ring_v.shape != ring_k.shape \
+            or pos.shape != (B,):
+        raise ValueError("carry shapes must be state [B,H,d,d], ring [B,H,W,d], pos [B]")
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, L, d, window, M, scale, mix, dt, gate=GATE_PER_DIM)
+    o = torch.empty_like(q) if out is None else out
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_FWD_CONTINUE)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    _check(lib.lizard_attn_fwd_continue_feat(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(lq), _ptr(lk),
+                                             _ptr(g), _ptr(meta_k), _ptr(meta_v), _ptr(state), _ptr(ring_k),
+                                             _ptr(ring_v), _ptr(pos), _ptr(o), _ptr(workspace), workspace.numel(),
+                                             _stream(dev)))
+    return o
+
+
+def lizard_attn_decode_step_feat(q, k, v, lq, lk, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
+                                 window: int, scale: float | None = None, mix: float = 1.0, out=None,
+                                 workspace=None):
+    """lizard_attn_decode_step with GLA log features lq, lk (fp32 [B,H,d]); returns o [B,H,d]."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v)):
+        _need(t, n, dt, dev)
+    for n, t in (("lq", lq), ("lk", lk), ("g", g), ("state", state)):
+        _need(t, n, torch.float32, dev)
+    _need(pos, "pos", torch.int32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, d = q.shape
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, 0, d, window, M, scale, mix, dt, gate=GATE_PER_DIM)
+    o = torch.empty_like(q) if out is None else out
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_DECODE)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8, dev)
+    _check(lib.lizard_attn_decode_step_feat(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(lq), _ptr(lk), _ptr(g),
+                                            _ptr(meta_k), _ptr(meta_v), _ptr(state), _ptr(ring_k), _ptr(ring_v),
+                                            _ptr(pos), _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o
 
 
 def _feat_shape(x, w):

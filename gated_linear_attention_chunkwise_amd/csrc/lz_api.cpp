@@ -136,6 +136,44 @@ lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
   return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
+lizard_status_t continue_impl(const lizard_attn_shape_t* s, const void* q, const void* k, const void* v,
+                              const float* lq, const float* lk, const float* g, const void* meta_k,
+                              const void* meta_v, float* state, void* ring_k, void* ring_v, int32_t* pos, void* o,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_FWD_CONTINUE);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  if (s->L > 0)
+    st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace, lq, lk});
+  else   // L = 0: nothing to do; the carry is left as it is
+    st = check_ptrs({}, {q, k, v, g, state, ring_k, ring_v, pos, o, meta_k, meta_v, workspace, lq, lk});
+  if (st != LIZARD_OK) return st;
+  if (s->L == 0) return LIZARD_OK;
+  if (workspace == nullptr || workspace_bytes < lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype))
+    return LIZARD_EWORKSPACE;
+  lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, nullptr, nullptr, nullptr, state,
+                workspace, state, pos, ring_k, ring_v, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix, s->gate,
+                lq, lk};
+  return lz::launch_fwd_continue(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
+
+lizard_status_t decode_impl(const lizard_attn_shape_t* s, const void* q, const void* k, const void* v,
+                            const float* lq, const float* lk, const float* g, const void* meta_k, const void* meta_v,
+                            float* state, void* ring_k, void* ring_v, int32_t* pos, void* o, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace, lq, lk});
+  if (st != LIZARD_OK) return st;
+  if (workspace == nullptr || workspace_bytes < lz::decode_workspace_bytes(s->B, s->H, s->d_k))
+    return LIZARD_EWORKSPACE;
+  lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
+                   reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate, lq, lk};
+  return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,20 +233,21 @@ lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
                                          float* state, void* ring_k, void* ring_v, int32_t* pos,
                                          void* o, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream) {
-  lizard_status_t st = check_shape(s, LIZARD_OP_FWD_CONTINUE);
-  if (st != LIZARD_OK) return st;
-  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
-  if (s->L > 0)
-    st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace});
-  else   // L = 0: nothing to do; the carry is left as it is
-    st = check_ptrs({}, {q, k, v, g, state, ring_k, ring_v, pos, o, meta_k, meta_v, workspace});
-  if (st != LIZARD_OK) return st;
-  if (s->L == 0) return LIZARD_OK;
-  if (workspace == nullptr || workspace_bytes < lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype))
-    return LIZARD_EWORKSPACE;
-  lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, nullptr, nullptr, nullptr, state,
-                workspace, state, pos, ring_k, ring_v, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix, s->gate};
-  return lz::launch_fwd_continue(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  return continue_impl(s, q, k, v, nullptr, nullptr, g, meta_k, meta_v, state, ring_k, ring_v, pos, o, workspace,
+                       workspace_bytes, stream);
+}
+
+lizard_status_t lizard_attn_fwd_continue_feat(const lizard_attn_shape_t* s,
+                                              const void* q, const void* k, const void* v,
+                                              const float* lq, const float* lk, const float* g,
+                                              const void* meta_k, const void* meta_v,
+                                              float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                              void* o, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  if (s != nullptr && s->gate != LIZARD_GATE_PER_DIM) return LIZARD_EUNSUPPORTED;
+  if (s != nullptr && s->L > 0 && (lq == nullptr || lk == nullptr)) return LIZARD_EINVAL;
+  return continue_impl(s, q, k, v, lq, lk, g, meta_k, meta_v, state, ring_k, ring_v, pos, o, workspace,
+                       workspace_bytes, stream);
 }
 
 lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
@@ -245,16 +284,21 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         float* state, void* ring_k, void* ring_v, int32_t* pos,
                                         void* o, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
-  lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
-  if (st != LIZARD_OK) return st;
-  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
-  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace});
-  if (st != LIZARD_OK) return st;
-  if (workspace == nullptr || workspace_bytes < lz::decode_workspace_bytes(s->B, s->H, s->d_k))
-    return LIZARD_EWORKSPACE;
-  lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
-                   reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate};
-  return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  return decode_impl(s, q, k, v, nullptr, nullptr, g, meta_k, meta_v, state, ring_k, ring_v, pos, o, workspace,
+                     workspace_bytes, stream);
+}
+
+lizard_status_t lizard_attn_decode_step_feat(const lizard_attn_shape_t* s,
+                                             const void* q, const void* k, const void* v,
+                                             const float* lq, const float* lk, const float* g,
+                                             const void* meta_k, const void* meta_v,
+                                             float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                             void* o, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  if (s != nullptr && s->gate != LIZARD_GATE_PER_DIM) return LIZARD_EUNSUPPORTED;
+  if (lq == nullptr || lk == nullptr) return LIZARD_EINVAL;
+  return decode_impl(s, q, k, v, lq, lk, g, meta_k, meta_v, state, ring_k, ring_v, pos, o, workspace,
+                     workspace_bytes, stream);
 }
 
 lizard_status_t lizard_hedgehog_fwd(const lizard_attn_shape_t* s, const void* x, const void* w, float* lphi,

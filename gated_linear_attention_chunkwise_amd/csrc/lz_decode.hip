@@ -41,7 +41,9 @@ struct DecWs {
   static size_t bytes(int B, int H) { return (size_t)B * H * NP * PS * sizeof(float); }
 };
 
-template <typename T, int D>
+// FEAT: the state update and readout use phi(k), phi(q) given as fp32 log features lk, lq
+// [B,H,d] (S <- diag(exp g) S + exp(lk)^T v, o_gla = exp(lq) S); the window keeps q and k.
+template <typename T, int D, bool FEAT>
 __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
   using WS_ = DecWs<D>;
   constexpr int NP = WS_::NP, PS = WS_::PS;
@@ -108,8 +110,13 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < RPT; ++u) {
     const int i = part * RB + r0 + u * RS;
-    qi[u] = Tr<T>::to_f(qg[i]);
-    ki[u] = Tr<T>::to_f(kg[i]);
+    if constexpr (FEAT) {
+      qi[u] = __expf(a.lq[vo + i]);
+      ki[u] = __expf(a.lk[vo + i]);
+    } else {
+      qi[u] = Tr<T>::to_f(qg[i]);
+      ki[u] = Tr<T>::to_f(kg[i]);
+    }
     ai[u] = __expf(a.gate ? a.g[bh] : a.g[vo + i]);   // scalar gate: one per head
   }
   for (int i = tid; i < D; i += NTHR) {
@@ -302,7 +309,10 @@ template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   constexpr int NP = D / RB;
   const size_t lds = sizeof(float) * (size_t)((a.W + NP - 1) / NP + 16);
-  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(a.B * a.H * NP), dim3(NTHR), lds, st, a);
+  if (a.lq != nullptr)
+    hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3(a.B * a.H * NP), dim3(NTHR), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3(a.B * a.H * NP), dim3(NTHR), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.H), dim3(D), 0, st, a);

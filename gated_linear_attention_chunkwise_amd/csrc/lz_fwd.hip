@@ -438,14 +438,14 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     sw.seg_gtot = reinterpret_cast<float*>(ws + 2 * mat);
   }
   if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, false, st)) != hipSuccess) return e;
-  // variants: continuation, scalar gate, log features (these two only on a fresh sequence
-  // with per-dimension gates)
-  const int variant = feat ? 4 : (a.pos != nullptr ? 1 : 0) + (a.gate ? 2 : 0);
+  // variants: continuation (bit 0), scalar gate (bit 1), log features (bit 2; per-dimension gates)
+  const int variant = (a.pos != nullptr ? 1 : 0) + (a.gate ? 2 : 0) + (feat ? 4 : 0);
+  if (variant >= 6) return hipErrorInvalidValue;
   decltype(&out_kernel<T, D, false, false, false>) kern =
       variant == 0 ? out_kernel<T, D, false, false, false> : variant == 1 ? out_kernel<T, D, true, false, false>
       : variant == 2 ? out_kernel<T, D, false, true, false> : variant == 3 ? out_kernel<T, D, true, true, false>
-      : out_kernel<T, D, false, false, true>;
-  static bool attr_set[5] = {false, false, false, false, false};   // idempotent; a race only repeats the same call
+      : variant == 4 ? out_kernel<T, D, false, false, true> : out_kernel<T, D, true, false, true>;
+  static bool attr_set[6] = {false, false, false, false, false, false};   // idempotent; a race only repeats the same call
   if (!attr_set[variant]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::bytes);

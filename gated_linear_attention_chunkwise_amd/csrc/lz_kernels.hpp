@@ -77,6 +77,8 @@ struct DecodeArgs {
   int B, H, W, M;
   float scale, mix;
   int gate;             // 0: g [B,H,d]; 1: g [B,H]
+  // optional fp32 log features [B,H,d] of phi(q), phi(k) for the state (both or neither)
+  const float* lq; const float* lk;
 };
 
 // Gate projection (lz_gate.hip).  Forward: g (output) = log sigmoid(x W^T) / tau in the gate

@@ -166,7 +166,8 @@ lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
  *   dlq, dlk [B,H,L,d_k] fp32, written: gradients of lq and lk
  *   dq, dk   written: the window branch's gradients of q and k only
  * Everything else is as for lizard_attn_fwd / lizard_attn_bwd; per-dimension
- * gates only (LIZARD_GATE_SCALAR returns LIZARD_EUNSUPPORTED). */
+ * gates only (LIZARD_GATE_SCALAR returns LIZARD_EUNSUPPORTED); the chunked-prefill
+ * and decode forms follow below. */
 lizard_status_t lizard_attn_fwd_feat(const lizard_attn_shape_t* s,
                                      const void* q, const void* k, const void* v,
                                      const float* lq, const float* lk, const float* g,
@@ -183,6 +184,27 @@ lizard_status_t lizard_attn_bwd_feat(const lizard_attn_shape_t* s,
                                      float* dmeta_k, float* dmeta_v,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream,
                                      hipEvent_t* stage_events);
+
+/* Chunked prefill and decode with log features: as lizard_attn_fwd_continue and
+ * lizard_attn_decode_step, with the GLA state updated by exp(lk) and read by
+ * exp(lq) (lq, lk [B,H,L,d_k] or, for decode, [B,H,d_k], fp32) and the window
+ * on the raw q, k.  The carry (state, ring of raw keys and values, pos) is
+ * the same as for the plain calls, so a log-feature prefill
+ * (lizard_attn_fwd_feat with state_out) hands over to these. */
+lizard_status_t lizard_attn_fwd_continue_feat(const lizard_attn_shape_t* s,
+                                              const void* q, const void* k, const void* v,
+                                              const float* lq, const float* lk, const float* g,
+                                              const void* meta_k, const void* meta_v,
+                                              float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                              void* o, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
+lizard_status_t lizard_attn_decode_step_feat(const lizard_attn_shape_t* s,
+                                             const void* q, const void* k, const void* v,
+                                             const float* lq, const float* lk, const float* g,
+                                             const void* meta_k, const void* meta_v,
+                                             float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                             void* o, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
 
 /* Hedgehog feature map in log space, the input of the *_feat calls above.  The
  * pages name the GLA branch's feature map a Hedgehog map and rely on its

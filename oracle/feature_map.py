@@ -41,7 +41,7 @@ import numpy as np
 from . import lizard_oracle as orc
 
 __all__ = ["hedgehog_log_features", "hedgehog_log_features_backward", "hybrid_forward_features",
-           "hybrid_backward_features"]
+           "hybrid_backward_features", "decode_step_features"]
 
 
 def _lse(z):
@@ -91,3 +91,16 @@ def hybrid_backward_features(q, k, v, lq, lk, g, meta_k, meta_v, dO, *, window, 
     gq, gk, gv, dg = orc.gla_backward(fq, fk, v, g, dO)
     wq, wk, wv, dmk, dmv = orc.window_backward(q, k, v, meta_k, meta_v, dO, window, scale, mix)
     return dict(dq=wq, dk=wk, dv=gv + wv, dlq=fq * gq, dlk=fk * gk, dg=dg, dmeta_k=dmk, dmeta_v=dmv)
+
+
+def decode_step_features(st, q, k, v, lq, lk, g, meta_k, meta_v, *, scale, mix=1.0):
+    """One decode step of the layer with GLA log features: S <- diag(exp g) S + exp(lk)^T v,
+    o_gla = exp(lq) S; the anchor window on the raw q, k (ring of raw keys and values);
+    o = o_gla + mix * o_swa; pos += 1.  q, k, v, lq, lk, g: [B,H,d]."""
+    fq, fk = np.exp(np.asarray(lq, np.float64)), np.exp(np.asarray(lk, np.float64))
+    v64 = np.asarray(v, np.float64)
+    st.S = np.exp(np.asarray(g, np.float64))[..., None] * st.S + fk[..., :, None] * v64[..., None, :]
+    o_gla = np.matmul(fq[:, :, None, :], st.S)[:, :, 0, :]
+    o_swa = orc.decode_window(st, q, k, v, meta_k, meta_v, scale=scale)
+    st.pos += 1
+    return o_gla + mix * o_swa

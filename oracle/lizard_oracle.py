@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "gla_forward", "window_forward", "hybrid_forward",
     "gla_backward", "window_backward", "hybrid_backward",
-    "DecodeState", "decode_step",
+    "DecodeState", "decode_step", "decode_window",
 ]
 
 
@@ -267,22 +267,16 @@ class DecodeState:
         return st
 
 
-def decode_step(st: DecodeState, q, k, v, g, meta_k, meta_v, *, scale, mix=1.0):
-    """One token for every sequence (q, k, v: [B,H,d]; g: [B,H,d] or scalar [B,H]);
-    returns o [B,H,dv].
-
-    S <- diag(exp g) S + k^T v; o_gla = q S; the new key/value goes to slot
-    pos mod W; o_swa = softmax attention of q over the M meta keys and the
-    min(pos+1, W) filled ring slots; o = o_gla + mix*o_swa; pos += 1.
-    """
+def decode_window(st: DecodeState, q, k, v, meta_k, meta_v, *, scale):
+    """The anchor window of one decode step: the new key/value goes to slot pos mod W, then
+    softmax attention of q over the M meta keys and the min(pos+1, W) filled ring slots.
+    Returns o_swa [B,H,dv]; pos is not advanced."""
     dt = st.dtype
-    q, k, v, g, meta_k, meta_v = (_as(a, dt) for a in (q, k, v, g, meta_k, meta_v))
-    B, H, dk = q.shape
+    q, k, v, meta_k, meta_v = (_as(a, dt) for a in (q, k, v, meta_k, meta_v))
+    B = q.shape[0]
     M = meta_k.shape[1]
     W = st.window
-    st.S = _decay(g, q.ndim)[..., None] * st.S + k[..., :, None] * v[..., None, :]
-    o_gla = np.matmul(q[:, :, None, :], st.S)[:, :, 0, :]
-    o_swa = np.empty_like(o_gla)
+    o_swa = np.empty(v.shape, dt)
     for b in range(B):
         slot = int(st.pos[b] % W)
         st.ring_k[b, :, slot] = k[b]
@@ -299,5 +293,21 @@ def decode_step(st: DecodeState, q, k, v, g, meta_k, meta_v, *, scale, mix=1.0):
         if meta_v is not None and M > 0:
             ob = ob + np.einsum("hm,hmd->hd", p[:, :M], meta_v)
         o_swa[b] = ob
+    return o_swa
+
+
+def decode_step(st: DecodeState, q, k, v, g, meta_k, meta_v, *, scale, mix=1.0):
+    """One token for every sequence (q, k, v: [B,H,d]; g: [B,H,d] or scalar [B,H]);
+    returns o [B,H,dv].
+
+    S <- diag(exp g) S + k^T v; o_gla = q S; the new key/value goes to slot
+    pos mod W; o_swa = softmax attention of q over the M meta keys and the
+    min(pos+1, W) filled ring slots; o = o_gla + mix*o_swa; pos += 1.
+    """
+    dt = st.dtype
+    q, k, v, g = (_as(a, dt) for a in (q, k, v, g))
+    st.S = _decay(g, q.ndim)[..., None] * st.S + k[..., :, None] * v[..., None, :]
+    o_gla = np.matmul(q[:, :, None, :], st.S)[:, :, 0, :]
+    o_swa = decode_window(st, q, k, v, meta_k, meta_v, scale=scale)
     st.pos += 1
     return o_gla + mix * o_swa

@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "lizard_attn_fwd_continue", "lizard_attn_workspace_bytes",
                           "lizard_attn_status_string", "lizard_gate_proj_fwd", "lizard_gate_proj_bwd",
                           "lizard_gate_proj_workspace_bytes", "lizard_distill_mse", "lizard_attn_fwd_feat",
-                          "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd"}
+                          "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd",
+                          "lizard_attn_fwd_continue_feat", "lizard_attn_decode_step_feat"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(pkg.SYMBOLS) == set(names)
@@ -246,3 +247,20 @@ def test_hedgehog_validation(lib):
     assert bw(ws=None) == EINVAL
     assert bw(nb=need - 1) == EWORKSPACE
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 5) == 0
+
+
+def test_feature_carry_entry_points_validation(lib):
+    s = shape()
+    def cont(s=s, lq=GOOD):
+        return lib.lizard_attn_fwd_continue_feat(ctypes.byref(s), GOOD, GOOD, GOOD, lq, GOOD, GOOD, GOOD, None,
+                                                 GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 40, None)
+    assert cont(lq=None) == EINVAL
+    assert cont(lq=BAD) == EALIGN
+    assert cont(s=shape(gate=1)) == EUNSUPPORTED
+    d = shape(L=0)
+    def dec(s=d, lk=GOOD):
+        return lib.lizard_attn_decode_step_feat(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, lk, GOOD, GOOD, None,
+                                                GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 40, None)
+    assert dec(lk=None) == EINVAL
+    assert dec(lk=BAD) == EALIGN
+    assert dec(s=shape(L=0, gate=1)) == EUNSUPPORTED

@@ -116,3 +116,24 @@ def test_layer_with_features_finite_differences():
             am[idx] -= h
             fd = (loss(**{name: ap}) - loss(**{name: am})) / (2 * h)
             assert abs(fd - out[gname][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx)
+
+
+def test_feature_decode_continues_the_sequence():
+    """A prefill of P tokens, then decode steps with log features, equal the whole-sequence
+    log-feature forward at the decoded positions (W smaller and larger than P)."""
+    rng = np.random.default_rng(6)
+    B, H, L, d, M = 2, 2, 14, 4, 2
+    q, k, v = (rnd(rng, B, H, L, d) for _ in range(3))
+    lq, lk = rnd(rng, B, H, L, d, s=0.5) - 1.0, rnd(rng, B, H, L, d, s=0.5) - 1.0
+    g = -np.abs(rnd(rng, B, H, L, d, s=0.3))
+    mk = rnd(rng, H, M, d)
+    for W, P in ((4, 9), (20, 5)):
+        full = fm.hybrid_forward_features(q, k, v, lq, lk, g, mk, window=W, scale=0.5)
+        pre = fm.hybrid_forward_features(q[:, :, :P], k[:, :, :P], v[:, :, :P], lq[:, :, :P], lk[:, :, :P],
+                                         g[:, :, :P], mk, window=W, scale=0.5)
+        st = orc.DecodeState.from_prefix(k[:, :, :P], v[:, :, :P], pre["state"], W)
+        for t in range(P, L):
+            o = fm.decode_step_features(st, q[:, :, t], k[:, :, t], v[:, :, t], lq[:, :, t], lk[:, :, t], g[:, :, t],
+                                        mk, None, scale=0.5)
+            assert np.allclose(o, full["o"][:, :, t], rtol=1e-12, atol=1e-12), (W, P, t)
+        assert np.allclose(st.S, full["state"], rtol=1e-12, atol=1e-12)

@@ -81,3 +81,43 @@ def test_features_train_shape_sampled_head():
     print("train shape features head", h, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for n, e in errs.items():
         assert e <= TOL["bf16"], (n, e)
+
+
+def test_features_prefill_continue_decode():
+    """Log-feature prefill (state hand-off) -> two continued segments -> decode steps, against
+    the oracle's whole-sequence log-feature forward."""
+    from gated_linear_attention_chunkwise_amd import lizard_attn_decode_step_feat, lizard_attn_fwd_continue_feat
+    B, H, N, D, W, M, P = 2, 2, 300, 128, 128, 4, 100
+    x = make_small(B, H, N, D, M, seed=41, bf16=True)
+    x.update(make_log_features((B, H, N, D), seed=42))
+    bf = torch.bfloat16
+    T = {n: dev(x[n], bf) for n in ("q", "k", "v", "meta_k")}
+    for n in ("g", "lq", "lk"):
+        T[n] = dev(x[n], torch.float32)
+    scale = 1.0 / math.sqrt(D)
+    seg = lambda n, a, e: T[n][:, :, a:e].contiguous()
+    f = lizard_attn_fwd_feat(*(seg(n, 0, P) for n in ("q", "k", "v", "lq", "lk", "g")), T["meta_k"], None, window=W,
+                             scale=scale, want_state=True)
+    outs = [f["o"]]
+    state = f["state"]
+    ring_k = torch.zeros(B, H, W, D, device="cuda", dtype=bf)
+    ring_v = torch.zeros_like(ring_k)
+    ts = torch.arange(max(0, P - W), P, device="cuda")
+    ring_k[:, :, ts % W] = T["k"][:, :, ts]
+    ring_v[:, :, ts % W] = T["v"][:, :, ts]
+    pos = torch.full((B,), P, device="cuda", dtype=torch.int32)
+    for a, e in ((P, 180), (180, 250)):
+        outs.append(lizard_attn_fwd_continue_feat(*(seg(n, a, e) for n in ("q", "k", "v", "lq", "lk", "g")),
+                                                  T["meta_k"], None, state, ring_k, ring_v, pos, window=W,
+                                                  scale=scale))
+    for t in range(250, N):
+        outs.append(lizard_attn_decode_step_feat(*(T[n][:, :, t].contiguous() for n in ("q", "k", "v", "lq", "lk", "g")),
+                                                 T["meta_k"], None, state, ring_k, ring_v, pos, window=W,
+                                                 scale=scale).unsqueeze(2))
+    torch.cuda.synchronize()
+    ref = fm.hybrid_forward_features(x["q"], x["k"], x["v"], x["lq"], x["lk"], x["g"], x["meta_k"], None, window=W,
+                                     scale=scale)
+    e_o = rel_l2(host(torch.cat(outs, 2)), ref["o"])
+    e_s = rel_l2(host(state), ref["state"])
+    print(f"feature carry: o {e_o:.2e} state {e_s:.2e}; pos {pos.tolist()}", flush=True)
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"] and pos.tolist() == [N] * B
