@@ -97,10 +97,20 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
   const int L = a.L, BH = a.B * a.H, NQB = (L + TQ - 1) / TQ;
-  // workgroup -> (head, query block): the longest blocks first; with B*H a multiple of 8,
-  // workgroup bid runs on XCD bid % 8 = bh % 8, so a head's blocks share one L2
+  // workgroup -> (head, query block).  With B*H a multiple of 8, workgroup bid runs on XCD
+  // bid % 8, and each XCD takes its heads one after another, every query block of a head
+  // (longest first) before the next head: the blocks in flight on an XCD then stream the same
+  // keys and values, which stay in its L2.  Otherwise the longest blocks of all heads go first.
   const int bid = blockIdx.x;
-  const int bh = bid % BH, qb = NQB - 1 - bid / BH;
+  int bh, qb;
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, slot = bid >> 3;
+    bh = (slot / NQB) * 8 + x;
+    qb = NQB - 1 - slot % NQB;
+  } else {
+    bh = bid % BH;
+    qb = NQB - 1 - bid / BH;
+  }
   const size_t hoff = (size_t)bh * L * D;
   const T* q = reinterpret_cast<const T*>(a.q) + hoff;
   const T* k = reinterpret_cast<const T*>(a.k) + hoff;
