@@ -20,12 +20,17 @@
 //   sweep_kernel   (lz_sweep.hip) reverse sweep over chunks per (b, h, 64-row
 //                  block of dS): carries dS in fp32 registers, stores dS'
 //                  (operand dtype, transposed) and the fp32 boundary rowsums;
-//                  the block of rows 0..63 also forms the window row dots
-//                  D_t = mix * dO_t . o_swa_t from the dO rows it streams
+//                  the row blocks of each head also form the window row dots
+//                  D_t = mix * dO_t . o_swa_t from the dO rows they stream
+//                  (each block a share of the token rows)
 //   chunk_kernel   one workgroup per (b, h, chunk): every GLA gradient plus
 //                  the anchor-window gradients (query side for dq, key side
 //                  for dk and dv) and per-chunk meta-key partial sums
-//   dmeta_kernel   deterministic sum of the meta partials over batch and chunks
+//   dmeta_fold_kernel, dmeta_kernel
+//                  deterministic sum of the meta partials over batch and chunks
+// With log features (lizard_attn_bwd_feat) the GLA operands are exp(lq + b) and
+// exp(lk - b), and the GLA gradients of q and k leave as dlq = q~ dq~ and
+// dlk = k^ dk^ (the terms of the gate gradient) instead of joining dq and dk.
 #include <type_traits>
 
 #include "lz_common.hpp"

@@ -1,8 +1,8 @@
 // lz_fwd.hip -- forward pass of the Lizard hybrid attention layer on gfx950.
 //
-// Two launches:
-//   sweep_kernel (lz_sweep.hip)  the GLA state recurrence over chunks, tiled
-//                 64 x 64 over the state; writes the state entering every chunk
+// Two launches (more when the sweep runs in sequence segments):
+//   sweep_kernel (lz_sweep.hip)  the GLA state recurrence over chunks, in
+//                 64-row blocks of the state; writes the state entering every chunk
 //   out_kernel    one workgroup (4 waves, 16 queries each) per (batch, head,
 //                 chunk of C = 64 tokens), all of d_v, so every score is
 //                 computed once:
