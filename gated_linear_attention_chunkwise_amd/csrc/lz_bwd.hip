@@ -521,17 +521,28 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
           bool vis[2];
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
-            const int kb = 2 * p + h2, s0 = kbase + 16 * kb;
+            const int s0 = kbase + 16 * (2 * p + h2);
             vis[h2] = (s0 <= lo + 15) && (s0 + 15 >= lo - W + 1);
-            f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
-            if (vis[h2]) {
+          }
+          // both blocks of the pair are formed when either is visible (the mask zeroes the
+          // other), so their products interleave with one drain
+          if (!(vis[0] || vis[1])) continue;
+          f32x4 xs[2], dps[2];
 #pragma unroll
-              for (int ks = 0; ks < KS; ++ks) {
-                mma32(x, ld_frag(sKw, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fa[ks]);
-                mma32(dp, ld_frag(sV, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fb[ks]);
-              }
-              mfma_drain();
+          for (int h2 = 0; h2 < 2; ++h2) { xs[h2] = f32x4{0, 0, 0, 0}; dps[h2] = xs[h2]; }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int kb = 2 * p + h2;
+              mma32(xs[h2], ld_frag(sKw, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fa[ks]);
+              mma32(dps[h2], ld_frag(sV, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fb[ks]);
             }
+          mfma_drain();
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int kb = 2 * p + h2, s0 = kbase + 16 * kb;
+            const f32x4 x = xs[h2], dp = dps[h2];
             // blocks wholly inside the band (every key at or before every query, within the
             // window, queries inside the sequence) need no per-element mask
             const bool full = vis[h2] && s0 + 15 <= lo && lo + 15 - s0 < W && lo + 15 < L;
@@ -548,7 +559,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
               }
             }
           }
-          if (vis[0] || vis[1]) {
+          {
             frag op;
             pack_acc(op, dl[0], dl[1]);
 #pragma unroll
@@ -568,17 +579,26 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
           bool vis[2];
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
-            const int tb = 2 * p + h2, q0 = qbase + 16 * tb;
+            const int q0 = qbase + 16 * (2 * p + h2);
             vis[h2] = (q0 + 15 >= lo) && (q0 <= lo + 15 + W - 1);
-            f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
-            if (vis[h2]) {
+          }
+          if (!(vis[0] || vis[1])) continue;
+          f32x4 xs[2], dps[2];
 #pragma unroll
-              for (int ks = 0; ks < KS; ++ks) {
-                mma32(x, ld_frag(sQw, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fa[ks]);
-                mma32(dp, ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fb[ks]);
-              }
-              mfma_drain();
+          for (int h2 = 0; h2 < 2; ++h2) { xs[h2] = f32x4{0, 0, 0, 0}; dps[h2] = xs[h2]; }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int tb = 2 * p + h2;
+              mma32(xs[h2], ld_frag(sQw, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fa[ks]);
+              mma32(dps[h2], ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fb[ks]);
             }
+          mfma_drain();
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int tb = 2 * p + h2, q0 = qbase + 16 * tb;
+            const f32x4 x = xs[h2], dp = dps[h2];
             const f32x4 lse4 = lds4(sLse + it * C + 16 * tb + 4 * kg);
             const f32x4 del4 = lds4(sDel + it * C + 16 * tb + 4 * kg);
             // every query of the block at or after every key of this wave, within the window,
@@ -602,7 +622,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
               }
             }
           }
-          if (vis[0] || vis[1]) {
+          {
             frag opl, opp;
             pack_acc(opl, dl[0], dl[1]);
             pack_acc(opp, pp[0], pp[1]);
