@@ -261,8 +261,17 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
   }
 
   // epilogue: o_T = O / l; dO = 2 (o_S - o_T) / N; sum of squares for the loss
+  // Every o_S value is loaded (raw, rows clamped into the sequence) before the first dO
+  // store: the compiler cannot tell the two tensors apart, so a load after a store would
+  // wait for a full memory round trip each time.
   const T* os = reinterpret_cast<const T*>(a.o_s) + hoff;
   T* dO = reinterpret_cast<T*>(a.dO) + hoff;
+  using R4 = decltype(ld4raw(os));
+  R4 sraw[NQ][JB];
+#pragma unroll
+  for (int b = 0; b < NQ; ++b)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) sraw[b][jb] = ld4raw(os + (size_t)min(tq[b], L - 1) * D + 16 * jb + 4 * kg);
   const float g2 = 2.f * a.inv_n;
   float sq = 0.f;
 #pragma unroll
@@ -273,11 +282,10 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
         const size_t o = (size_t)tq[b] * D + 16 * jb + 4 * kg;
-        const f32x4 s = ldg4f(os + o);
         f32x4 d;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          d[e] = s[e] - inv * O[b][jb][e];
+          d[e] = (float)sraw[b][jb][e] - inv * O[b][jb][e];
           sq += d[e] * d[e];
         }
         stg4(dO + o, g2 * d[0], g2 * d[1], g2 * d[2], g2 * d[3]);

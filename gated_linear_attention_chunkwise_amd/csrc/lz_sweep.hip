@@ -63,11 +63,14 @@ __device__ __forceinline__ f32x4 col4(const float* tile, int ld, int r0, int c0,
   return f32x4{tile[r0 * ld + c], tile[(r0 + 1) * ld + c], tile[(r0 + 2) * ld + c], tile[(r0 + 3) * ld + c]};
 }
 
-// Inputs of one chunk held in registers while the previous chunk is processed.
-template <int NV>
+// Inputs of one chunk held in registers while the previous chunk is processed.  Every
+// value is kept as loaded (no conversion, no broadcast) until the chunk is processed: a
+// use right after a load in a branch makes the compiler wait for it there, and that
+// wait (vmcnt counts in issue order) also drains every chunk already in flight.
+template <int NV, typename RA>
 struct SwStage {
-  f32x4 ra[4];   // q or k: tokens 4*tg+u, four columns
-  f32x4 rg[4];   // log-gates, same positions
+  RA ra[4];      // q or k (or fp32 log features): tokens 4*tg+u, four columns, as loaded
+  f32x4 rg[4];   // log-gates, same positions (scalar gates: component 0 only)
   V16 rb[NV];    // v or dO tile, 16-byte vectors
   V16 rs[NV];    // state tile (backward)
   V16 ro[NV];    // o_swa rows (backward row dots)
@@ -81,13 +84,14 @@ struct SwStage {
 template <typename T, int D, bool REV, bool REDUCE, bool SG, bool FEAT>
 __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) {
   using LY = SwLayout<T, D>;
-  // chunks of inputs in flight: three forward (one more measured 2 % faster at the train shape;
-  // four spill), two backward (its stages also carry state rows and o_swa)
+  // chunks of inputs in flight: three forward (two measured the same at the train shape; four
+  // spill), two backward (its stages also carry state rows and o_swa)
   constexpr int DEPTH = REV ? 2 : 3;
   constexpr int NTI = D / TT;                      // tiles per edge
   constexpr int NTHR = NTHR_SW * NTI;              // four waves per 64 x 64 tile of the row block
   constexpr int VEC = Tr<T>::VEC;
   constexpr int NV = CHUNK * (D / VEC) / NTHR;     // 16-byte vectors per thread of a [64][D] tile
+  static_assert(NV % NTI == 0, "the row-dot slots split evenly over the row blocks");
   constexpr int LDA = LY::LDA, LDB = LY::LDB;
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   // backward: the row blocks of a head also form the window row dots of each chunk, the block of
   // state rows i0.. taking the token rows of its own register slots u with u % NTI == it
   const bool dots = REV && a.delta != nullptr;
-  const T* osrc = dots ? reinterpret_cast<const T*>(a.o_swa) + hoff : nullptr;
+  const T* osrc = reinterpret_cast<const T*>(dots ? a.o_swa : a.b_src) + hoff;   // (unused without dots)
   const float* g = a.g + (SG ? (size_t)bh * L : hoff);
   const T* states = reinterpret_cast<const T*>(a.states) + (size_t)bh * NC * D * D;
   T* out = reinterpret_cast<T*>(a.out) + (size_t)bh * NC * D * D;
@@ -140,58 +144,42 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   // so the prefix over tokens is an in-row scan
   const int tg = r, cg = kg;
   const int acol = i0 + 16 * w + 4 * cg;
-  auto load = [&](SwStage<NV>& s, int c) {
+  using RA = decltype(ld4raw(static_cast<const AT*>(nullptr)));
+  // No bounds branches: rows past the sequence end are loaded clamped onto its last row (and
+  // the state after the last chunk onto the last state) and masked when the chunk is processed.
+  auto load = [&](SwStage<NV, RA>& s, int c) {
     const int t0 = c * CHUNK;
-    if (t0 + CHUNK <= L) {   // full chunk: no bounds checks
+    // Only the waves of the first column tile use q or k and the gates; the others read one
+    // fixed line instead, so that every wave issues the same loads (a wave that skipped them
+    // would, by the reasoning above, make the compiler's waits shallower for all).
 #pragma unroll
-      for (int u = 0; u < 4 && jt == 0; ++u) {
-        const size_t o = (size_t)(t0 + 4 * tg + u) * D + acol;
-        s.ra[u] = ld4f(asrc + o);
-        if constexpr (SG) {
-          const float x = g[t0 + 4 * tg + u];
-          s.rg[u] = f32x4{x, x, x, x};
-        } else {
-          s.rg[u] = ld4f(g + o);
-        }
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int t = jt == 0 ? min(t0 + 4 * tg + u, L - 1) : 0;
+      const size_t o = jt == 0 ? (size_t)t * D + acol : 0;
+      s.ra[u] = ld4raw(asrc + o);
+      if constexpr (SG)
+        s.rg[u][0] = g[t];
+      else
+        s.rg[u] = ld4raw(g + o);
+    }
 #pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
-        s.rb[u] = ldg16(bsrc + (size_t)(t0 + row) * D + cv * VEC);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4 && jt == 0; ++u) {
-        const int t = t0 + 4 * tg + u;
-        const size_t o = (size_t)t * D + acol;
-        // past the end: a zero operand (log features: -inf, whose exponential is zero)
-        const float fill = FEAT ? -INFINITY : 0.f;
-        s.ra[u] = t < L ? ld4f(asrc + o) : f32x4{fill, fill, fill, fill};
-        if constexpr (SG) {
-          const float x = t < L ? g[t] : 0.f;
-          s.rg[u] = f32x4{x, x, x, x};
-        } else {
-          s.rg[u] = t < L ? ld4f(g + o) : f32x4{0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
-        s.rb[u] = t0 + row < L ? ldg16(bsrc + (size_t)(t0 + row) * D + cv * VEC) : zero16();
-      }
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+      s.rb[u] = ldg16(bsrc + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
     }
     if constexpr (REV) {
+      const int cn = min(c + 1, NC - 1);
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
         const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
-        s.rs[u] = (c + 1 < NC) ? ldg16(states + ((size_t)(c + 1) * D + i0 + row) * D + cv * VEC) : zero16();
+        s.rs[u] = ldg16(states + ((size_t)cn * D + i0 + row) * D + cv * VEC);
       }
-      if (dots)
+      // the token rows of slots u = it, it + NTI, ... (slot u / NTI holds slot u's row)
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-          const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
-          if (u % NTI == it) s.ro[u] = ldg16(osrc + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
-        }
+      for (int m = 0; m < NV / NTI; ++m) {
+        const int idx = tid + (m * NTI + it) * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        s.ro[m] = ldg16(osrc + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
+      }
     }
   };
 
@@ -209,11 +197,17 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
         acc[ib] = *reinterpret_cast<const f32x4*>(si + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg);
+    // take the wait for these loads here, before any chunk is in flight: otherwise the loop
+    // (whose first step stores the carried tile) inherits a possibly pending load into the
+    // carried registers and waits on it at every step, draining the chunks in flight
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) asm volatile("" ::"v"(acc[ib][0]), "v"(acc[ib][1]), "v"(acc[ib][2]), "v"(acc[ib][3]));
   }
   f32x4 gsum = f32x4{0, 0, 0, 0};   // reduce: gate total of this lane's four key columns
 
   auto chunk_of = [&](int n) { return REV ? c_end - 1 - n : c_begin + n; };
-  auto process = [&](SwStage<NV>& s, int n) {
+  const int nlast = max(NCs - 1, 0);
+  auto process = [&](SwStage<NV, RA>& s, int n) {
     const int c = chunk_of(n);
     if constexpr (!REV && !REDUCE) {
       // state entering chunk c
@@ -226,8 +220,8 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
-      *reinterpret_cast<V16*>(sB + row * LDB + cv * VEC) = s.rb[u];
-      if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDB + cv * VEC) = s.rs[u];
+      *reinterpret_cast<V16*>(sB + row * LDB + cv * VEC) = c * CHUNK + row < L ? s.rb[u] : zero16();
+      if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDB + cv * VEC) = c + 1 < NC ? s.rs[u] : zero16();
     }
     if (REV && dots) {
       // delta_t = mix * dO_t . o_swa_t, formed before this stage's registers take the next chunk;
@@ -239,12 +233,24 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
         const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
         float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dot += v16_get(s.rb[u], e, (T*)nullptr) * v16_get(s.ro[u], e, (T*)nullptr);
+        for (int e = 0; e < VEC; ++e)
+          dot += v16_get(s.rb[u], e, (T*)nullptr) * v16_get(s.ro[u / NTI], e, (T*)nullptr);
         dot = group_sum<D / VEC>(dot);
         if (cv == 0 && t0 + row < L) a.delta[(size_t)bh * L + t0 + row] = a.mix * dot;
       }
     }
     if (jt == 0) {
+      // rows past the end: no decay, and a zero operand (log features: -inf)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool okr = c * CHUNK + 4 * tg + u < L;
+        if constexpr (SG) {
+          const float x = okr ? s.rg[u][0] : 0.f;
+          s.rg[u] = f32x4{x, x, x, x};
+        } else if (!okr) {
+          s.rg[u] = f32x4{0, 0, 0, 0};
+        }
+      }
       // chunk-local inclusive prefix b of the gates and the chunk total Gamma
 #pragma unroll
       for (int u = 1; u < 4; ++u) s.rg[u] += s.rg[u - 1];
@@ -266,12 +272,15 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
         for (int e = 0; e < 4; ++e) {
           const float b = s.rg[u][e] + excl[e];
           const float c = REV ? b : tot[e] - b;
-          x[e] = FEAT ? __expf(s.ra[u][e] + c) : s.ra[u][e] * __expf(c);
+          const bool okr = c * CHUNK + 4 * tg + u < L;
+          const float av = okr ? (float)s.ra[u][e] : (FEAT ? -INFINITY : 0.f);
+          x[e] = FEAT ? __expf(av + c) : av * __expf(c);
         }
         st4(sA + (4 * tg + u) * LDA + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
       }
     }
-    if (n + DEPTH < NCs) load(s, chunk_of(n + DEPTH));
+    // unconditional for the same reason as the first loads (the last rounds repeat the last chunk)
+    load(s, chunk_of(min(n + DEPTH, nlast)));
     __syncthreads();
 
     if constexpr (REV) {
@@ -316,15 +325,25 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   };
 
   // DEPTH chunks of inputs in flight, stage i serving the steps n with n % DEPTH == i
-  SwStage<NV> s0, s1, s2;
-  if (NCs > 0) load(s0, chunk_of(0));
-  if (NCs > 1) load(s1, chunk_of(1));
-  if (DEPTH > 2 && NCs > 2) load(s2, chunk_of(2));
-  for (int n = 0; n < NCs; n += DEPTH) {
-    process(s0, n);
-    if (n + 1 < NCs) process(s1, n + 1);
-    if (DEPTH > 2 && n + 2 < NCs) process(s2, n + 2);
+  SwStage<NV, RA> s0, s1, s2;
+  // The first stages load unconditionally (a short segment repeats its last chunk; every row
+  // is clamped into the sequence): a stage skipped on some path would make the compiler
+  // assume, at the loop head, that its registers were loaded just before and wait for them.
+  load(s0, chunk_of(0));
+  load(s1, chunk_of(min(1, nlast)));
+  if constexpr (DEPTH > 2) load(s2, chunk_of(min(2, nlast)));
+  // Full rounds, then the tail: with the tail's conditions inside the loop, its control flow
+  // would hold a path back to the loop head after one stage only, along which the next
+  // stage's loads look recent, and the compiler would wait for them (and for every chunk
+  // in flight) at each step.
+  int n0 = 0;
+  for (; n0 + DEPTH <= NCs; n0 += DEPTH) {
+    process(s0, n0);
+    process(s1, n0 + 1);
+    if constexpr (DEPTH > 2) process(s2, n0 + 2);
   }
+  if (n0 < NCs) process(s0, n0);
+  if (DEPTH > 2 && n0 + 1 < NCs) process(s1, n0 + 1);
   mfma_drain();
   if constexpr (REDUCE) {
     const size_t sb = (size_t)bh * a.NS + seg;
