@@ -135,9 +135,10 @@ __global__ __launch_bounds__(NTHR_FM) void hedgehog_fwd_kernel(FeatArgs a) {
   }
 }
 
-// One workgroup per (head, group of `a.cpg` consecutive (batch, chunk) slots).
+// One workgroup per (head, group of `a.cpg` consecutive (batch, chunk) slots); three per CU,
+// as many as the LDS allows (the registers are held to 168).
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR_FM) void hedgehog_bwd_kernel(FeatArgs a) {
+__global__ __launch_bounds__(NTHR_FM, 3) void hedgehog_bwd_kernel(FeatArgs a) {
   using LY = FmLayout<T, D>;
   using frag = typename Tr<T>::frag;
   constexpr int F = LY::F, NB = F / 16, KS = D / 32, VEC = Tr<T>::VEC;
@@ -160,20 +161,48 @@ __global__ __launch_bounds__(NTHR_FM) void hedgehog_bwd_kernel(FeatArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) dw[i][j] = f32x4{0, 0, 0, 0};
 
-  for (int sl = s_begin; sl < s_end; ++sl) {
+  // The next chunk's x tile and dl rows are loaded (unconditionally, rows clamped into the
+  // sequence) while the current chunk is processed, and masked when they are taken.
+  constexpr int NXV = CHUNK * D / VEC / NTHR_FM;   // 16-byte vectors of the x tile per thread
+  static_assert(CHUNK * D / VEC % NTHR_FM == 0, "x tile splits evenly over the threads");
+  const int u = 16 * w + r;
+  V16 xn[NXV];
+  f32x4 gpn[NB], gmn[NB];
+  auto fetch_x = [&](int sl) {
     const int b = sl / NC, c = sl % NC, bh = b * a.H + h, t0 = c * CHUNK;
     const T* x = reinterpret_cast<const T*>(a.x) + (size_t)bh * L * D;
-    const float* dl = a.dl + (size_t)bh * L * D;
-    __syncthreads();   // the previous chunk's readers of sX / sZ are done (and W is staged)
-    // x chunk to LDS (rows past the end as zeros: they add nothing to dW)
-    for (int idx = tid; idx < CHUNK * D / VEC; idx += NTHR_FM) {
-      const int row = idx / (D / VEC), cv = idx % (D / VEC);
-      const V16 v = ldg16(x + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
-      *reinterpret_cast<V16*>(sX + row * LY::LDX + cv * VEC) = t0 + row < L ? v : zero16();
+#pragma unroll
+    for (int i = 0; i < NXV; ++i) {
+      const int idx = tid + i * NTHR_FM, row = idx / (D / VEC), cv = idx % (D / VEC);
+      xn[i] = ldg16(x + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
     }
-    __syncthreads();
-    const int u = 16 * w + r, tok = t0 + u;
+  };
+  auto fetch_dl = [&](int sl) {
+    const int b = sl / NC, c = sl % NC, bh = b * a.H + h, t0 = c * CHUNK;
+    const float* dlr = a.dl + ((size_t)bh * L + min(t0 + u, L - 1)) * D;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      gpn[j] = *reinterpret_cast<const f32x4*>(dlr + 16 * j + 4 * kg);
+      gmn[j] = *reinterpret_cast<const f32x4*>(dlr + F + 16 * j + 4 * kg);
+    }
+  };
+  if (s_begin < s_end) {
+    fetch_x(s_begin);
+    fetch_dl(s_begin);
+  }
+  for (int sl = s_begin; sl < s_end; ++sl) {
+    const int b = sl / NC, c = sl % NC, bh = b * a.H + h, t0 = c * CHUNK;
+    const int tok = t0 + u;
     const bool ok = tok < L;
+    __syncthreads();   // the previous chunk's readers of sX / sZ are done (and W is staged)
+    // x chunk to LDS (rows past the end as zeros: they add nothing to dW), then the next x
+#pragma unroll
+    for (int i = 0; i < NXV; ++i) {
+      const int idx = tid + i * NTHR_FM, row = idx / (D / VEC), cv = idx % (D / VEC);
+      *reinterpret_cast<V16*>(sX + row * LY::LDX + cv * VEC) = t0 + row < L ? xn[i] : zero16();
+    }
+    fetch_x(min(sl + 1, s_end - 1));
+    __syncthreads();
     frag xf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) xf[ks] = ld_frag(sX, LY::LDX, u, 32 * ks + 8 * kg);
@@ -181,14 +210,13 @@ __global__ __launch_bounds__(NTHR_FM) void hedgehog_bwd_kernel(FeatArgs a) {
     form_z<T, D>(z, xf, sW, lane);
     const float lp = lse_row<NB>(z, 1.f), lm = lse_row<NB>(z, -1.f);
     // dz in the same lane layout
+    // this lane's dl (a token past the end: zero), then the next chunk's
     f32x4 gp[NB], gm[NB];
     float sp = 0.f, sm = 0.f;
-    const float* dlr = dl + (size_t)min(tok, L - 1) * D;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int f = 16 * j + 4 * kg;
-      gp[j] = ok ? *reinterpret_cast<const f32x4*>(dlr + f) : f32x4{0, 0, 0, 0};
-      gm[j] = ok ? *reinterpret_cast<const f32x4*>(dlr + F + f) : f32x4{0, 0, 0, 0};
+      gp[j] = ok ? gpn[j] : f32x4{0, 0, 0, 0};
+      gm[j] = ok ? gmn[j] : f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 4; ++e) { sp += gp[j][e]; sm += gm[j][e]; }
     }
@@ -202,6 +230,7 @@ __global__ __launch_bounds__(NTHR_FM) void hedgehog_bwd_kernel(FeatArgs a) {
         const float pp = __expf(z[j][e] - lp), pm = __expf(-z[j][e] - lm);
         dz[j][e] = (gp[j][e] - pp * sp) - (gm[j][e] - pm * sm);
       }
+    fetch_dl(min(sl + 1, s_end - 1));
     // dz chunk to LDS for the dW product (token rows, feature columns)
 #pragma unroll
     for (int j = 0; j < NB; ++j) st4(sZ + u * LY::LDZ + 16 * j + 4 * kg, dz[j][0], dz[j][1], dz[j][2], dz[j][3]);
