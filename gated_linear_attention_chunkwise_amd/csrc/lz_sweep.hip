@@ -419,7 +419,10 @@ int sweep_segments(int B, int H, int L, int D) {
   const int NC = (L + CHUNK - 1) / CHUNK;
   const double base = (double)B * H * (D / TT);             // workgroups of one segment
   if (base >= 256) return 1;                                 // one per CU or more already
-  int ns = (int)((1024 + base - 1) / base);                 // aim at ~1024 workgroups
+  // aim at ~256 workgroups, one per CU: the sweep streams at the same rate with more
+  // (measured with 512 and 1024 on the 64K prefill), while every further segment adds
+  // reduce work (reads of k, v and the gates)
+  int ns = (int)((256 + base - 1) / base);
   ns = std::min(ns, NC / 16);                                // segments of at least 16 chunks
   if (ns <= 1) return 1;
   const int sc = (NC + ns - 1) / ns;
