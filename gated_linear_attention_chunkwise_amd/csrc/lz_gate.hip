@@ -103,11 +103,14 @@ struct GemmShape {
   static constexpr int BR = BKC ? BN : BK, BC = BKC ? BK : BN;
   static constexpr int A_ELEMS = AR * (AC + PA), B_ELEMS = BR * (BC + PB);
   static constexpr size_t lds_bytes = 2 * sizeof(T) * (size_t)(A_ELEMS + B_ELEMS);   // two stages
+  // the largest tiles keep two register sets of tiles in flight (smaller ones would lose
+  // occupancy to the extra registers)
+  static constexpr bool DEEP = BM * BN >= 256 * 256;
 };
 
 // C[M][N] = sum_k A[m][k] B[k][n] over this workgroup's split of k.
 // WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN) block of C in 16 x 16 MFMA tiles.
-// Two LDS stages: the tiles of step k+1 are loaded to registers while step k is
+// Two LDS stages: the tiles of a later step are loaded to registers while step k is
 // multiplied from one stage, then stored to the other; one barrier per step.
 template <typename T, bool AKC, bool BKC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
@@ -135,18 +138,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
 
   const T* Ag = reinterpret_cast<const T*>(a.A);
   const T* Bg = reinterpret_cast<const T*>(a.Bm);
-  TileLd<T, AR, AC, NT, PA> ta;
-  TileLd<T, BR, BC, NT, PB> tb;
-  auto load = [&](int k0) {
-    if (AKC) ta.load(Ag, a.lda, m0, k0, a.a_rows, a.a_cols, tid);
-    else     ta.load(Ag, a.lda, k0, m0, a.a_rows, a.a_cols, tid);
-    if (BKC) tb.load(Bg, a.ldb, n0, k0, a.b_rows, a.b_cols, tid);
-    else     tb.load(Bg, a.ldb, k0, n0, a.b_rows, a.b_cols, tid);
+  auto load = [&](auto& xa, auto& xb, int k0) {
+    if (AKC) xa.load(Ag, a.lda, m0, k0, a.a_rows, a.a_cols, tid);
+    else     xa.load(Ag, a.lda, k0, m0, a.a_rows, a.a_cols, tid);
+    if (BKC) xb.load(Bg, a.ldb, n0, k0, a.b_rows, a.b_cols, tid);
+    else     xb.load(Bg, a.ldb, k0, n0, a.b_rows, a.b_cols, tid);
   };
-  auto store = [&](int stage) {
+  auto store = [&](const auto& xa, const auto& xb, int stage) {
     T* sa = lds + stage * (SH::A_ELEMS + SH::B_ELEMS);
-    ta.store(sa, tid);
-    tb.store(sa + SH::A_ELEMS, tid);
+    xa.store(sa, tid);
+    xb.store(sa + SH::A_ELEMS, tid);
   };
 
   f32x4 acc[MB][NB];
@@ -155,15 +156,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (kbeg < kend) {
-    load(kbeg);
-    store(0);
-    __syncthreads();
-  }
-  int stage = 0;
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    const bool more = k0 + BK < kend;
-    if (more) load(k0 + BK);   // next tiles in flight while this one is multiplied
+  auto multiply = [&](int stage) {
     const T* sA = lds + stage * (SH::A_ELEMS + SH::B_ELEMS);
     const T* sB = sA + SH::A_ELEMS;
 #pragma unroll
@@ -185,9 +178,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) mma32(acc[i][j], fb[j], fa[i]);   // C^T blocks: lanes hold row runs of C
     }
-    if (more) store(stage ^ 1);   // that stage was last read before the previous barrier
-    __syncthreads();
-    stage ^= 1;
+  };
+
+  TileLd<T, AR, AC, NT, PA> ta0;
+  TileLd<T, BR, BC, NT, PB> tb0;
+  if constexpr (SH::DEEP) {
+    // Two register sets of tiles: tile t is loaded into set t % 2 two steps before it is
+    // stored, so a step's loads have two steps of products to arrive.  The loads are
+    // unconditional (the last steps repeat the last tile) and the loop runs in pairs of
+    // steps, so that no path reaches a wait with a set's loads looking recent.
+    TileLd<T, AR, AC, NT, PA> ta1;
+    TileLd<T, BR, BC, NT, PB> tb1;
+    const int nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    const int klast = kbeg + (nsteps > 0 ? nsteps - 1 : 0) * BK;
+    auto kstep = [&](int t) { return min(kbeg + t * BK, klast); };
+    if (nsteps > 0) {
+      // tile 0 to LDS stage 0, tile 1 in set 1, tile 2 in set 0
+      load(ta0, tb0, kstep(0));
+      store(ta0, tb0, 0);
+      load(ta1, tb1, kstep(1));
+      load(ta0, tb0, kstep(2));
+      __syncthreads();
+      int t = 0;
+      // step t multiplies stage t % 2, stores tile t + 1 (set (t + 1) % 2) into the other
+      // stage, then loads tile t + 3 into that set
+      for (; t + 2 <= nsteps; t += 2) {
+        multiply(0);
+        store(ta1, tb1, 1);
+        load(ta1, tb1, kstep(t + 3));
+        __syncthreads();
+        multiply(1);
+        store(ta0, tb0, 0);
+        load(ta0, tb0, kstep(t + 4));
+        __syncthreads();
+      }
+      if (t < nsteps) multiply(0);
+    }
+  } else {
+    // one register set: the tiles of step k+1 are loaded while step k is multiplied
+    if (kbeg < kend) {
+      load(ta0, tb0, kbeg);
+      store(ta0, tb0, 0);
+      __syncthreads();
+    }
+    int stage = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+      const bool more = k0 + BK < kend;
+      if (more) load(ta0, tb0, k0 + BK);   // next tiles in flight while this one is multiplied
+      multiply(stage);
+      if (more) store(ta0, tb0, stage ^ 1);   // that stage was last read before the previous barrier
+      __syncthreads();
+      stage ^= 1;
+    }
   }
 
   // epilogue: the blocks were formed transposed, so lane holds C[m][n .. n+3] with
@@ -371,7 +413,7 @@ hipError_t gate_fwd_t(const GateArgs& p, hipStream_t st) {
   a.g = p.g; a.B = p.B; a.H = p.H; a.L = p.L; a.dk = p.dk; a.sg = p.sg; a.tau = p.tau;
   constexpr int DT = sizeof(T) == 2 ? 1 : 0;
   if (p.sg) return run_gemm<T, true, true, EPI_GATE, 64, 32, fwd_bk_scalar(DT), 4, 1>(a, st);
-  if constexpr (DT == 1) return run_gemm<T, true, true, EPI_GATE, 256, 256, 64, 4, 2>(a, st);
+  if constexpr (DT == 1) return run_gemm<T, true, true, EPI_GATE, 256, 256, 32, 4, 2>(a, st);
   return run_gemm<T, true, true, EPI_GATE, 128, 128, 32, 2, 2>(a, st);
 }
 
@@ -399,7 +441,7 @@ hipError_t gate_bwd_t(const GateArgs& p, hipStream_t st) {
     // scalar gate: one 32-deep step per tile, bound by writing dx
     bool big = false;
     if constexpr (sizeof(T) == 2) {
-      if (!p.sg) { e = run_gemm<T, true, false, EPI_STORE, 256, 256, 64, 4, 2>(a, st); big = true; }
+      if (!p.sg) { e = run_gemm<T, true, false, EPI_STORE, 256, 256, 32, 4, 2>(a, st); big = true; }
     }
     if (!big) e = run_gemm<T, true, false, EPI_STORE, 128, 128, 32, 2, 2>(a, st);
     if (e != hipSuccess) return e;
