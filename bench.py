@@ -541,8 +541,8 @@ def main():
                     help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards over batch and heads with no exchange; see the design notes)",
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards over batch and heads with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
