@@ -47,7 +47,7 @@ constexpr int NTHR_CK = 512;   // chunk kernel: 8 waves, two per token block
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t delta, dS, bnd, dmeta, total;
+  size_t delta, dS, bnd, dmeta, seg, total;
 };
 
 WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
@@ -63,6 +63,8 @@ WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
   off += round_up(sizeof(float) * (size_t)B * H * NC * NJ * D, 256);
   w.dmeta = off;
   off += round_up(sizeof(float) * (size_t)B * NC * H * M * 2 * D, 256);
+  w.seg = off;   // segment buffers of the reverse sweep when it runs in segments (few heads)
+  off += round_up(fwd_segment_bytes(B, H, L, D), 256);
   w.total = off;
   return w;
 }
@@ -740,9 +742,16 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   // the state-gradient sweep also forms the window row dots delta_t from the dO rows it streams
   {
     const bool feat = a.lq != nullptr;
-    const SweepArgs sw{feat ? (const void*)a.lq : a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr,
-                       a.B, a.H, a.L, 1, NC, nullptr, nullptr, nullptr, a.gate, feat ? 1 : 0, a.o_swa,
-                       a.ws_delta, a.mix};
+    const int NS = sweep_segments(a.B, a.H, a.L, D);
+    SweepArgs sw{feat ? (const void*)a.lq : a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr,
+                 a.B, a.H, a.L, NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate, feat ? 1 : 0, a.o_swa,
+                 a.ws_delta, a.mix};
+    if (NS > 1) {
+      const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
+      sw.seg_in = reinterpret_cast<float*>(ws + wl.seg);
+      sw.seg_fin = reinterpret_cast<float*>(ws + wl.seg + mat);
+      sw.seg_gtot = reinterpret_cast<float*>(ws + wl.seg + 2 * mat);
+    }
     if ((e = launch_sweep(sw, std::is_same<T, bf16_t>::value ? 1 : 0, D, true, st)) != hipSuccess) return e;
   }
   mark(1);

@@ -48,13 +48,14 @@ struct BwdArgs {
 // states = the forward's chunk states, out = dS' transposed [B,H,NC,d,d],
 // bnd = boundary rowsums [B,H,NC,d/64,d].
 //
-// Sequence segments (forward only): with NS > 1 the chunks are cut into NS
-// segments of SC chunks that sweep in parallel.  A reduce pass carries every
-// segment but the last from a zero state and writes its final state to
-// seg_fin [B*H][NS][d][d] and its gate total to seg_gtot [B*H][NS][d]; a scan
-// over segments writes the state entering each segment to seg_in [B*H][NS][d][d]
-// (the first one is state_in, or zero); the sweep pass then starts segment s
-// from seg_in[s].  NS = 1: one segment, the fields below it are unused.
+// Sequence segments: with NS > 1 the chunks are cut into NS segments of SC chunks
+// that sweep in parallel.  A reduce pass carries every segment but the one swept
+// first (the last forward, the first backward) from zero and writes its final state
+// (state gradient) to seg_fin [B*H][NS][d][d] and its gate total to seg_gtot
+// [B*H][NS][d]; a scan over segments writes what enters each segment to seg_in
+// [B*H][NS][d][d] (forward: state_in or zero first; backward: zero last); the sweep
+// pass then starts segment s from seg_in[s].  NS = 1: one segment, the fields below
+// it are unused.
 struct SweepArgs {
   const void* a_src; const void* b_src; const float* g;
   const void* states; void* out; float* bnd; float* state_out; const float* state_in;

@@ -76,8 +76,8 @@ struct SwStage {
   V16 ro[NV];    // o_swa rows (backward row dots)
 };
 
-// REDUCE (forward only): carry a segment from a zero state and keep only its final
-// state and gate total (no chunk states).
+// REDUCE: carry a segment from a zero state (gradient) and keep only its final state
+// (gradient at the segment's first chunk boundary) and gate total; no chunk outputs.
 // SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
 // FEAT: a_src holds fp32 log features l (of phi(k) forward, phi(q) backward); the gate is
 // absorbed in log space, exp(l + c), instead of scaling a raw operand by exp(c).
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   const int jt = wave >> 2, w = wave & 3;
   // workgroup -> (b*h, segment, i tile); the row blocks and segments of one head share an XCD
   const int BH = a.B * a.H;
-  const int NSL = REDUCE ? a.NS - 1 : a.NS;        // segments launched (the reduce skips the last)
+  const int NSL = REDUCE ? a.NS - 1 : a.NS;        // segments launched (a reduce skips the one swept first)
   const int PER = NTI * NSL;
   int bh, it, seg;
   {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
       bh = bid / PER;
       y2 = bid % PER;
     }
-    seg = y2 / NTI;
+    seg = y2 / NTI + (REV && REDUCE ? 1 : 0);   // the reverse reduce skips the first segment
     it = y2 % NTI;
   }
   const int i0 = it * TT, j0 = jt * TT;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   const T* bsrc = reinterpret_cast<const T*>(a.b_src) + hoff;
   // backward: the row blocks of a head also form the window row dots of each chunk, the block of
   // state rows i0.. taking the token rows of its own register slots u with u % NTI == it
-  const bool dots = REV && a.delta != nullptr;
+  const bool dots = REV && !REDUCE && a.delta != nullptr;
   const T* osrc = reinterpret_cast<const T*>(dots ? a.o_swa : a.b_src) + hoff;   // (unused without dots)
   const float* g = a.g + (SG ? (size_t)bh * L : hoff);
   const T* states = reinterpret_cast<const T*>(a.states) + (size_t)bh * NC * D * D;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
       const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
       s.rb[u] = ldg16(bsrc + (size_t)min(t0 + row, L - 1) * D + cv * VEC);
     }
-    if constexpr (REV) {
+    if constexpr (REV && !REDUCE) {
       const int cn = min(c + 1, NC - 1);
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
@@ -188,6 +188,19 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   f32x4 acc[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) acc[x] = f32x4{0, 0, 0, 0};
+  if constexpr (REV && !REDUCE) {
+    // the gradient entering this segment from the later ones (the reverse segment scan)
+    if (a.NS > 1) {
+      const float* si = a.seg_in + ((size_t)bh * a.NS + seg) * D * D;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[jb][e] = si[(size_t)(i0 + 16 * w + 4 * kg + e) * D + j0 + 16 * jb + r];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        asm volatile("" ::"v"(acc[jb][0]), "v"(acc[jb][1]), "v"(acc[jb][2]), "v"(acc[jb][3]));
+    }
+  }
   if constexpr (!REV && !REDUCE) {
     // the state entering this segment: from the segment scan, or the carried state of a
     // continuation for a single segment
@@ -221,7 +234,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
     for (int u = 0; u < NV; ++u) {
       const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
       *reinterpret_cast<V16*>(sB + row * LDB + cv * VEC) = c * CHUNK + row < L ? s.rb[u] : zero16();
-      if constexpr (REV) *reinterpret_cast<V16*>(sS + row * LDB + cv * VEC) = c + 1 < NC ? s.rs[u] : zero16();
+      if constexpr (REV && !REDUCE) *reinterpret_cast<V16*>(sS + row * LDB + cv * VEC) = c + 1 < NC ? s.rs[u] : zero16();
     }
     if (REV && dots) {
       // delta_t = mix * dO_t . o_swa_t, formed before this stage's registers take the next chunk;
@@ -284,23 +297,26 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
     __syncthreads();
 
     if constexpr (REV) {
-      // boundary rowsum over this j tile, decay, store dS' transposed
-      f32x4 rsum = f32x4{0, 0, 0, 0};
+      // boundary rowsum over this j tile, decay, store dS' transposed (a reduce only decays)
+      if constexpr (!REDUCE) {
+        f32x4 rsum = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) rsum += col4(sS, LDB, 16 * w + 4 * kg, j0 + 16 * jb, lane) * acc[jb];
+        for (int jb = 0; jb < 4; ++jb) rsum += col4(sS, LDB, 16 * w + 4 * kg, j0 + 16 * jb, lane) * acc[jb];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rsum[e] = row_sum16(rsum[e]);
-      if (r == 0)
-        stg4(a.bnd + (((size_t)bh * NC + c) * NTI + jt) * D + i0 + 16 * w + 4 * kg, rsum[0], rsum[1], rsum[2],
-             rsum[3]);
+        for (int e = 0; e < 4; ++e) rsum[e] = row_sum16(rsum[e]);
+        if (r == 0)
+          stg4(a.bnd + (((size_t)bh * NC + c) * NTI + jt) * D + i0 + 16 * w + 4 * kg, rsum[0], rsum[1], rsum[2],
+               rsum[3]);
+      }
       f32x4 dec;
 #pragma unroll
       for (int e = 0; e < 4; ++e) dec[e] = sDec[16 * w + 4 * kg + e];
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
         acc[jb] *= dec;
-        stg4(out + ((size_t)c * D + j0 + 16 * jb + r) * D + i0 + 16 * w + 4 * kg, acc[jb][0], acc[jb][1],
-             acc[jb][2], acc[jb][3]);
+        if constexpr (!REDUCE)
+          stg4(out + ((size_t)c * D + j0 + 16 * jb + r) * D + i0 + 16 * w + 4 * kg, acc[jb][0], acc[jb][1],
+               acc[jb][2], acc[jb][3]);
       }
       // + (q e^b)^T dO
 #pragma unroll
@@ -348,10 +364,17 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   if constexpr (REDUCE) {
     const size_t sb = (size_t)bh * a.NS + seg;
     float* sf = a.seg_fin + sb * D * D;
+    if constexpr (REV) {
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-      stg4(sf + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1], acc[ib][2],
-           acc[ib][3]);
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sf[(size_t)(i0 + 16 * w + 4 * kg + e) * D + j0 + 16 * jb + r] = acc[jb][e];
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+        stg4(sf + (size_t)(i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1], acc[ib][2],
+             acc[ib][3]);
+    }
     if (jt == 0 && tg == 0)
       *reinterpret_cast<f32x4*>(a.seg_gtot + sb * D + acol) = gsum;
   } else if constexpr (!REV) {
@@ -366,12 +389,23 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
 }
 
 // The state entering each segment: seg_in[0] = state_in (or zero),
-// seg_in[s+1] = diag(e^{gtot[s]}) seg_in[s] + seg_fin[s].  One thread per (b*h, i, j).
-__global__ __launch_bounds__(256) void seg_scan_kernel(SweepArgs a, int D) {
+// seg_in[s+1] = diag(e^{gtot[s]}) seg_in[s] + seg_fin[s].  Reverse (state gradients):
+// seg_in[NS-1] = 0, seg_in[s-1] = diag(e^{gtot[s]}) seg_in[s] + seg_fin[s].  One thread
+// per (b*h, i, j).
+__global__ __launch_bounds__(256) void seg_scan_kernel(SweepArgs a, int D, int rev) {
   const int per = D * D / 256;
   const int bh = blockIdx.x / per, e = (blockIdx.x % per) * 256 + threadIdx.x, i = e / D;
   const int NS = a.NS;
   const size_t base = (size_t)bh * NS;
+  if (rev) {
+    float S = 0.f;
+    a.seg_in[(base + NS - 1) * D * D + e] = S;
+    for (int s = NS - 1; s > 0; --s) {
+      S = __expf(a.seg_gtot[(base + s) * D + i]) * S + a.seg_fin[(base + s) * D * D + e];
+      a.seg_in[(base + s - 1) * D * D + e] = S;
+    }
+    return;
+  }
   float S = a.state_in != nullptr ? a.state_in[(size_t)bh * D * D + e] : 0.f;
   a.seg_in[base * D * D + e] = S;
   for (int s = 0; s + 1 < NS; ++s) {
@@ -385,10 +419,10 @@ hipError_t launch_sweep_g(const SweepArgs& a, hipStream_t st) {
   using LY = SwLayout<T, D>;
   const int blocks = D / TT;                    // 64-row blocks of the state
   const int nthr = NTHR_SW * (D / TT);
-  if (!REV && a.NS > 1) {
-    hipLaunchKernelGGL((sweep_kernel<T, D, false, true, SG, FEAT>), dim3(a.B * a.H * blocks * (a.NS - 1)),
+  if (a.NS > 1) {   // segments: reduce (all but the first to be swept), scan, then the sweep
+    hipLaunchKernelGGL((sweep_kernel<T, D, REV, true, SG, FEAT>), dim3(a.B * a.H * blocks * (a.NS - 1)),
                        dim3(nthr), LY::bytes, st, a);
-    hipLaunchKernelGGL(seg_scan_kernel, dim3(a.B * a.H * (D * D / 256)), dim3(256), 0, st, a, D);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(a.B * a.H * (D * D / 256)), dim3(256), 0, st, a, D, REV ? 1 : 0);
   }
   hipLaunchKernelGGL((sweep_kernel<T, D, REV, false, SG, FEAT>), dim3(a.B * a.H * blocks * a.NS), dim3(nthr),
                      LY::bytes, st, a);

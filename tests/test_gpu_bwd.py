@@ -113,6 +113,17 @@ def test_train_8k_full_size_sampled():
             assert e <= TOL["bf16"], (h, n, e)
 
 
+@pytest.mark.parametrize("dtname,B,H,D,L,W,M", [("fp32", 1, 2, 64, 2085, 64, 2), ("bf16", 1, 2, 128, 4101, 128, 4),
+                                                  ("bf16", 2, 1, 128, 2113, 33, 3)])
+def test_backward_in_sequence_segments(dtname, B, H, D, L, W, M):
+    """Few heads and a long sequence: the state-gradient sweep runs in segments (a reduce of
+    every segment but the last from zero, a reverse scan, then the sweep of each segment from
+    the gradient entering it; 2, 4 and 2 segments here, the last one ragged)."""
+    x = make_small(B, H, L, D, M, seed=L + D, bf16=(dtname == "bf16"))
+    b, ref = run_both(x, dtname, W)
+    check(b, ref, dtname)
+
+
 @pytest.mark.parametrize("dtname,D,with_mv", [("fp32", 64, False), ("fp32", 64, True), ("bf16", 128, False)])
 def test_forward_backward_bit_reproducible(dtname, D, with_mv):
     """Same inputs, same launches -> bit-identical outputs and gradients (no

@@ -51,7 +51,8 @@ def run_case(dtname, B, H, L, D, W, M, with_mv, seed):
 
 CASES = [("fp32", 1, 2, 256, 64, 64, 4, True), ("fp32", 2, 1, 130, 64, 5, 0, False),
          ("bf16", 2, 2, 200, 128, 128, 4, False), ("bf16", 1, 2, 65, 64, 129, 16, True),
-         ("bf16", 1, 1, 1, 128, 1, 0, False), ("bf16", 1, 3, 1000, 128, 100, 2, False)]
+         ("bf16", 1, 1, 1, 128, 1, 0, False), ("bf16", 1, 3, 1000, 128, 100, 2, False),
+         ("bf16", 1, 1, 2100, 128, 128, 4, False)]   # long, one head: the sweeps run in segments
 
 
 @pytest.mark.parametrize("dtname,B,H,L,D,W,M,with_mv", CASES)
