@@ -18,8 +18,10 @@
 //
 // Kernels, in launch order:
 //   sweep_kernel   (lz_sweep.hip) reverse sweep over chunks per (b, h, 64-row
-//                  block of dS): carries dS in fp32 registers, stores dS'
-//                  (operand dtype, transposed) and the fp32 boundary rowsums;
+//                  block of dS; with few heads, per sequence segment after a
+//                  reduce pass and a reverse scan over the segments): carries
+//                  dS in fp32 registers, stores dS' (operand dtype, transposed)
+//                  and the fp32 boundary rowsums;
 //                  the row blocks of each head also form the window row dots
 //                  D_t = mix * dO_t . o_swa_t from the dO rows they stream
 //                  (each block a share of the token rows)

@@ -23,6 +23,10 @@
 // next chunks in flight (three forward, two backward) while one is
 // processed (none of them depends on the carried matrix).  The gate prefix
 // runs inside rows of 16 lanes (DPP), with no LDS round trip or barrier.
+// With few heads both directions also split the chunks into sequence segments
+// that sweep in parallel: a reduce pass carries every segment but the one swept
+// first from zero, a scan over the segments forms what enters each of them, and
+// the sweep proper then starts every segment from it.
 #include <algorithm>
 #include <type_traits>
 
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   for (int x = 0; x < 4; ++x) acc[x] = f32x4{0, 0, 0, 0};
   if constexpr (REV && !REDUCE) {
     // the gradient entering this segment from the later ones (the reverse segment scan)
-    if (a.NS > 1) {
+    if (a.NS > 1) {   // (its wait taken here, as for the forward's entering state below)
       const float* si = a.seg_in + ((size_t)bh * a.NS + seg) * D * D;
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
