@@ -173,6 +173,10 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
     if (kbase + TK - 1 <= qw) {
       // every key of the tile precedes every query of the wave: no mask, no branch, no drain
       f32x4 x[NQ][4];
+      // a wave issues the products of a tile at raised priority and its softmax at the
+      // normal one: of the two waves sharing a SIMD, the one with matrix work is served
+      // first, and the other's softmax fills the remaining issue slots
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -184,12 +188,14 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
           for (int b = 0; b < NQ; ++b) mma32(x[b][kb], kf, qf[b][ks]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int b = 0; b < NQ; ++b) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) x[b][kb] *= sl2;
         te_absorb<JB>(x[b], mrun[b], lpart[b], O[b]);
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         frag bop[NQ];
@@ -202,6 +208,7 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
           for (int b = 0; b < NQ; ++b) mma32(O[b][jb], vf, bop[b]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       mfma_drain();   // the block ends in control flow
     } else if (kbase <= qw + QW - 1) {   // the diagonal: some keys are visible to some queries
       bool vis[NQ][4];
