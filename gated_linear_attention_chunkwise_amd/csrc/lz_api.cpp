@@ -90,7 +90,7 @@ lizard_status_t fwd_impl(const lizard_attn_shape_t* s,
   if (st != LIZARD_OK) return st;
   // the workspace holds the sweep's segment buffers, and the chunk states unless chunk_states is given
   const size_t need = s->L == 0 ? 0
-                      : chunk_states != nullptr ? lz::fwd_segment_bytes(s->B, s->H, s->L, s->d_k)
+                      : chunk_states != nullptr ? lz::fwd_aux_bytes(s->B, s->H, s->L, s->d_k)
                                                 : lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   if (s->L == 0 && state_out == nullptr) return LIZARD_OK;

@@ -49,7 +49,7 @@ constexpr int NTHR_CK = 512;   // chunk kernel: 8 waves, two per token block
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t delta, dS, bnd, dmeta, seg, total;
+  size_t delta, dS, bnd, dmeta, seg, disp, total;
 };
 
 WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
@@ -67,12 +67,14 @@ WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
   off += round_up(sizeof(float) * (size_t)B * NC * H * M * 2 * D, 256);
   w.seg = off;   // segment buffers of the reverse sweep when it runs in segments (few heads)
   off += round_up(fwd_segment_bytes(B, H, L, D), 256);
+  w.disp = off;  // strong-gate dispatch: masks, list
+  off += dispatch_bytes(B, H, L, D);
   w.total = off;
   return w;
 }
 
 // ------------------------------------------------------------ chunk kernel
-template <typename T, int D>
+template <typename T, int D, bool STRONG = false>
 struct CkLayout {
   static constexpr int PAD = Tr<T>::PAD;
   static constexpr int LDQ = D + PAD;    // row-major [C][D] and [D][D] tiles
@@ -80,12 +82,14 @@ struct CkLayout {
   static constexpr int LDC = C + PAD;    // [16][C] meta tiles
   static constexpr int LDM = 16 + PAD;   // [D][16] meta keys transposed
   static constexpr size_t tile = sizeof(T) * C * LDQ;
-  static constexpr size_t oQt = 0;            // q~ ; window: key tile of an earlier chunk
-  static constexpr size_t oKh = tile;         // k^ ; window: query tile of a later chunk
-  static constexpr size_t oEb = 2 * tile;     // e^b; window: dO tile of a later chunk
-  static constexpr size_t odO = 3 * tile;     // dO of this chunk
-  static constexpr size_t oV = 4 * tile;      // v of this chunk; window: value tile of an earlier chunk
-  static constexpr size_t oBig = 5 * tile;    // dS'^T [D][D] | d b [C][LDB] fp32
+  static constexpr int NT = STRONG ? 4 : 5;   // [C][D] tiles (the sub-block path keeps no e^b)
+  static constexpr size_t oQt = 0;            // q~ (sub-block path: raw q); window: key tile of an earlier chunk
+  static constexpr size_t oKh = tile;         // k^ (sub-block path: keys folded to their block end);
+                                              // window: query tile of a later chunk
+  static constexpr size_t oEb = 2 * tile;     // fast path: e^b; window: dO tile of a later chunk
+  static constexpr size_t odO = (NT - 2) * tile;   // dO of this chunk
+  static constexpr size_t oV = (NT - 1) * tile;    // v of this chunk; window: value tile of an earlier chunk
+  static constexpr size_t oBig = NT * tile;   // dS'^T [D][D] | d b [C][LDB] fp32
   static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * LDB ? sizeof(T) * D * LDQ
                                                                                    : sizeof(float) * C * LDB;
   static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
@@ -95,16 +99,38 @@ struct CkLayout {
   static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 chunks
   static constexpr size_t oBnd = oDel + sizeof(float) * 3 * C;       // boundary term of dg [D]
   static constexpr size_t oTot = oBnd + sizeof(float) * D;           // per-block column totals of d b [4][D]
-  static constexpr size_t bytes = oTot + sizeof(float) * 4 * D;
+  static constexpr size_t fast_end = oTot + sizeof(float) * 4 * D;
+  // sub-block path: fp32 block-local gate prefixes [C][LDBF] (the window's dO tile of a later
+  // chunk afterwards), the 16-token block totals [4][D], the strips' largest in-block decays [D/16][4]
+  static constexpr int LDBF = D + 4;
+  static constexpr size_t oB = fast_end;
+  static constexpr size_t oBT = oB + sizeof(float) * C * LDBF;
+  static constexpr size_t oSpan = oBT + sizeof(float) * 4 * D;
+  static constexpr size_t bytes = STRONG ? oSpan + sizeof(float) * 4 * (D / 16) : fast_end;
+  static constexpr size_t oDw = STRONG ? oB : oEb;                  // window: dO tile of a later chunk
+  static_assert(sizeof(float) * C * LDBF >= tile, "dO tile fits the prefix area");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
-// Four consecutive LDS elements as floats.
-__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 lds4(const bf16_t* p) {
-  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+__device__ __forceinline__ void set_elem(bf16x8& f, int e, float x) { f[e] = (__bf16)x; }
+__device__ __forceinline__ void set_elem(f32x8& f, int e, float x) { f[e] = x; }
+// The value an operand of type T holds for x (bf16 rounding, or none).
+template <typename T>
+__device__ __forceinline__ float rnd_op(float x) {
+  if constexpr (std::is_same<T, bf16_t>::value)
+    return (float)(__bf16)x;
+  else
+    return x;
 }
+// One term q_t k_s e^(b_t - b_s) of a pairwise score (x = b_t - b_s), raw or log features.
+template <bool FEAT>
+__device__ __forceinline__ float pair_term(float qv, float kv, float x) {
+  if constexpr (FEAT)
+    return __expf(qv + kv + x);
+  else
+    return qv * kv * __expf(x);
+}
+
 
 // One workgroup per (b, h, chunk), eight waves in two roles over the four
 // 16-token blocks of the chunk: waves 0..3 accumulate dq (GLA and the window
@@ -115,18 +141,28 @@ __device__ __forceinline__ f32x4 lds4(const bf16_t* p) {
 // SG: one log-gate per head and token (g, dg [B,H,L]).
 // FEAT: the GLA branch reads fp32 log features lq, lk (q~ = exp(lq + b), k^ = exp(lk - b)) and
 // its q / k gradients leave as dlq = q~ dq~, dlk = k^ dk^; dq, dk keep the window part only.
-template <typename T, int D, bool SG, bool FEAT>
-__global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
-                                                            const float* __restrict__ wsbnd) {
-  using LY = CkLayout<T, D>;
+// STRONG: the GLA part by 16-token blocks, for chunks whose gates are too strong for the
+// chunk-start factoring (see out_chunk in lz_fwd.hip): the score of query t (block tb) against key
+// s (block sb <= tb) is formed from q e^(b_t - rho_sb) and k e^(rho_sb - b_s), rho_sb = b at the
+// last token of block sb; a diagonal block whose own decay exceeds the factoring's range is
+// formed pairwise.
+// Every pair's operand values are the same on the query side (dq, q-terms of d b) and the key
+// side (dk, dv, k-terms of d b), so the chunk-local sums of d b cancel as on the fast path.  The
+// inter-chunk terms use k e^(gamma - b) against the stored state gradient, gamma = Gamma in the
+// columns the sweep stored undecayed and 0 elsewhere.
+// Without STRONG, a chunk flagged by the sweep is appended to the dispatch list and left.
+template <typename T, int D, bool SG, bool FEAT, bool STRONG>
+__device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict__ wsdS,
+                                           const float* __restrict__ wsbnd, int bh, int c, unsigned char* smem,
+                                           int tid) {
+  using LY = CkLayout<T, D, STRONG>;
   using frag = typename Tr<T>::frag;
   constexpr int VEC = Tr<T>::VEC;
   constexpr int NB = D / 16;     // 16-wide blocks over the head dim
   constexpr int KS = D / 32;     // K steps over the head dim
   constexpr int NJ = D / DVTA;
-  constexpr int LDQ = LY::LDQ, LDB = LY::LDB;
+  constexpr int LDQ = LY::LDQ, LDB = LY::LDB, LDBF = LY::LDBF;
 
-  extern __shared__ __align__(16) unsigned char smem[];
   T* sQt = reinterpret_cast<T*>(smem + LY::oQt);
   T* sKh = reinterpret_cast<T*>(smem + LY::oKh);
   T* sEb = reinterpret_cast<T*>(smem + LY::oEb);
@@ -136,7 +172,7 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   T* sV = reinterpret_cast<T*>(smem + LY::oV);
   T* sKw = sQt;    // window: raw keys of chunk kt (query side)
   T* sQw = sKh;    // window: raw queries of chunk qc (key side)
-  T* sDw = sEb;    // window: dO of chunk qc > c (key side)
+  T* sDw = reinterpret_cast<T*>(smem + LY::oDw);    // window: dO of chunk qc > c (key side)
   T* sMkT = reinterpret_cast<T*>(smem + LY::oMkT);
   T* sDLm = reinterpret_cast<T*>(smem + LY::oDLm);
   T* sPm = reinterpret_cast<T*>(smem + LY::oPm);
@@ -144,24 +180,20 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
   float* sBnd = reinterpret_cast<float*>(smem + LY::oBnd);
   float* sTot = reinterpret_cast<float*>(smem + LY::oTot);
+  float* sB = reinterpret_cast<float*>(smem + LY::oB);         // STRONG only
+  float* sBT = reinterpret_cast<float*>(smem + LY::oBT);       // STRONG only
+  float* sSpan = reinterpret_cast<float*>(smem + LY::oSpan);   // STRONG only
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+  const int lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
   const bool qrole = w < 4;        // waves 0..3: dq; waves 4..7: dk, dv
   const int wb = w & 3;            // token block of this wave (rows 16*wb .. +16 of the chunk)
   const int L = a.L, NC = (L + C - 1) / C, W = a.W, M = a.M;
-  // workgroup -> (chunk, head); consecutive chunks of one head share an XCD
-  const int BH = a.B * a.H;
-  int bh, c;
+  // the sweep's strong-column masks of this chunk (bit i: column i was stored undecayed)
+  uint64_t sm0, sm1 = 0;
   {
-    const int bid = blockIdx.x;
-    if ((BH & 7) == 0) {
-      const int x = bid % 8, y = bid / 8;           // y runs over (head group, chunk)
-      c = y % NC;
-      bh = (y / NC) * 8 + x;
-    } else {
-      bh = bid / NC;
-      c = bid % NC;
-    }
+    const uint64_t* mp = reinterpret_cast<const uint64_t*>(a.strong + ((size_t)bh * NC + c) * (D / 16));
+    sm0 = mp[0];
+    if constexpr (D == 128) sm1 = mp[1];
   }
   const int b = bh / a.H, h = bh % a.H;
   const size_t hoff = (size_t)bh * L * D;
@@ -251,6 +283,12 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       load_s(fs0, 0);
       if (KS > 1) load_s(fs1, 1);
     }
+    if constexpr (!STRONG) {
+      if ((sm0 | sm1) != 0) {   // the sub-block launch takes this chunk
+        if (tid == 0) a.list[atomicAdd(a.list_count, 1)] = bh * NC + c;
+        return;
+      }
+    }
     put_rows(sdO, rdo, t0);
     put_rows(sV, rv, t0);
 #pragma unroll
@@ -269,8 +307,14 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
       for (int j = 0; j < NJ; ++j) bnd += bndp[j];
       sBnd[tid] = bnd;
     }
-    // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b
-    if (has_strip) gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
+    // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b (sub-block path: b, rho, raw q and
+    // keys folded to the end of their block)
+    if (has_strip) {
+      if constexpr (STRONG)
+        gs.fold_strong(sQt, sKh, LDQ, sB, LDBF, sBT, D, sSpan + 4 * w, 16 * w + 4 * kg, r, lane);
+      else
+        gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
+    }
 #pragma unroll
     for (int e = 0; e < NVS; ++e) {
       const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
@@ -284,7 +328,355 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   f32x4 acc0[NB], acc1[NB];
 #pragma unroll
   for (int x = 0; x < NB; ++x) { acc0[x] = f32x4{0, 0, 0, 0}; acc1[x] = acc0[x]; }
-  if (qrole) {
+  f32x4 dbs[NB];   // sub-block path: this lane's gate-gradient terms (q side or k side)
+  if constexpr (STRONG) {
+    // Exponents come from block-local sums only (sB: P, the inclusive prefix inside each 16-token
+    // block; sBT: the block totals T), never as differences of chunk-cumulative sums, so that
+    // each is as accurate as its own size.  Relative to the end of key block j, query t of block
+    // i > j has exponent b_t - rho_j = P_t + T_{j+1} + .. + T_{i-1}; key s of block j has
+    // rho_j - b_s = T_j - P_s.  The pairwise form sums the gates between key and query directly.
+    // Diagonal blocks formed pairwise: those whose own decay exceeds the factoring's range (bf16)
+    // or its accurate range (fp32); the same decision in every wave.
+    constexpr float kPairSpan = std::is_same<T, float>::value ? 16.f : kStrongGate;
+    int prm = 0;   // bit kb: diagonal block kb is formed pairwise
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float m = 0.f;
+      for (int w2 = 0; w2 < D / 16; ++w2) m = fmaxf(m, sSpan[4 * w2 + kb]);
+      if (m > kPairSpan) prm |= 1 << kb;
+    }
+    const bool prw = (prm >> wb) & 1;   // this wave's diagonal block
+    // raw GLA operands (log features) of chunk row `row`, columns col .. col+3; rows past the
+    // end give zero operands (log features: -inf)
+    auto qraw4 = [&](int row, int col) -> f32x4 {
+      if constexpr (FEAT) {
+        if (t0 + row >= L) return f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        return ld4f(a.lq + hoff + (size_t)(t0 + row) * D + col);
+      } else {
+        return ld4f(sQt + row * LDQ + col);   // the raw-q tile (zero rows past the end)
+      }
+    };
+    auto qraw1 = [&](int row, int col) -> float {
+      if constexpr (FEAT)
+        return t0 + row < L ? a.lq[hoff + (size_t)(t0 + row) * D + col] : -INFINITY;
+      else
+        return Tr<T>::to_f(sQt[row * LDQ + col]);
+    };
+    auto kraw4 = [&](int row, int col) -> f32x4 {
+      if constexpr (FEAT) {
+        if (t0 + row >= L) return f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        return ld4f(a.lk + hoff + (size_t)(t0 + row) * D + col);
+      } else {
+        if (t0 + row >= L) return f32x4{0, 0, 0, 0};
+        return ld4f(k + (size_t)(t0 + row) * D + col);
+      }
+    };
+    // the log-gates of chunk row `row` (zero past the end; a scalar gate broadcast)
+    auto graw4 = [&](int row, int col) -> f32x4 {
+      if (t0 + row >= L) return f32x4{0, 0, 0, 0};
+      if constexpr (SG) {
+        const float x = g[t0 + row];
+        return f32x4{x, x, x, x};
+      } else {
+        return ld4f(g + (size_t)(t0 + row) * D + col);
+      }
+    };
+    // T_{j0} + .. + T_{j1} (zero when j0 > j1), four columns or one
+    auto bsum4 = [&](int j0, int j1, int col) {
+      f32x4 z = f32x4{0, 0, 0, 0};
+      for (int m = j0; m <= j1; ++m) z += ld4f(sBT + m * D + col);
+      return z;
+    };
+    auto bsum1 = [&](int j0, int j1, int col) {
+      float z = 0.f;
+      for (int m = j0; m <= j1; ++m) z += sBT[m * D + col];
+      return z;
+    };
+#pragma unroll
+    for (int x = 0; x < NB; ++x) dbs[x] = f32x4{0, 0, 0, 0};
+    if (qrole) {
+      frag fo[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) fo[ks] = ld_frag(sdO, LDQ, u, 32 * ks + 8 * kg);
+      // inter-chunk first (the prefetched S_prev rows are then free): Y = dO S_prev^T, the
+      // gradient of q~ = q e^b, b_t = T_0 + .. + T_{wb-1} + P_t
+      f32x4 Y[NB];
+#pragma unroll
+      for (int x = 0; x < NB; ++x) Y[x] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        frag (&cur)[NB] = (ks & 1) ? fs1 : fs0;
+#pragma unroll
+        for (int x = 0; x < NB; ++x) mma32(Y[x], cur[x], fo[ks]);
+        if (ks + 2 < KS) load_s(cur, ks + 2);
+      }
+      mfma_drain();
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int col = 16 * x + 4 * kg;
+        const f32x4 bt = bsum4(0, wb - 1, col) + ld4f(sB + u * LDBF + col), qv = qraw4(u, col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dbs[x][e] += rnd_op<T>(gate_op<FEAT>(qv[e], bt[e])) * Y[x][e];
+          if constexpr (!FEAT) acc0[x][e] += __expf(bt[e]) * Y[x][e];
+        }
+      }
+      // dA^T blocks (keys of block sb <= wb, queries of block wb)
+      f32x4 blk[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        blk[sb] = f32x4{0, 0, 0, 0};
+        if (sb <= wb) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma32(blk[sb], ld_frag(sV, LDQ, 16 * sb + r, 32 * ks + 8 * kg), fo[ks]);
+          mfma_drain();
+          if (sb == wb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * kg + i > r) blk[sb][i] = 0.f;
+        }
+      }
+      // acc0: raw dq.  Per key block: X = dA k'' (k'' = k e^(rho_sb - b)), then the query factor
+      // e^(b_t - rho_sb) turns it into dq and the operand value q e^(b_t - rho_sb) into d b terms
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        if (sb > wb) continue;
+        if (sb == wb && prw) {
+          // pairwise: e^(g_{s+1} + .. + g_t), the sum formed going back from the query;
+          // dA[this query][key 16 sb + s2] sits in lane r + 16 (s2 / 4), slot s2 % 4
+#pragma unroll
+          for (int x = 0; x < NB; ++x) {
+            const int col = 16 * x + 4 * kg;
+            const f32x4 qv = qraw4(u, col);
+            f32x4 run = f32x4{0, 0, 0, 0};
+#pragma unroll 1
+            for (int s2 = 15; s2 >= 0; --s2) {
+              if (s2 < r) run += graw4(16 * sb + s2 + 1, col);   // keys after the query carry dA = 0
+              const float dAv = __shfl(blk[sb][s2 & 3], r + 16 * (s2 >> 2), WAVE);
+              const f32x4 kv = kraw4(16 * sb + s2, col);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                dbs[x][e] += dAv * pair_term<FEAT>(qv[e], kv[e], run[e]);
+                if constexpr (!FEAT) acc0[x][e] += dAv * (kv[e] * __expf(run[e]));
+              }
+            }
+          }
+        } else {
+          f32x4 X[NB];
+#pragma unroll
+          for (int x = 0; x < NB; ++x) X[x] = f32x4{0, 0, 0, 0};
+          frag op;
+          pack_acc(op, blk[sb], f32x4{0, 0, 0, 0});
+#pragma unroll
+          for (int x = 0; x < NB; ++x)
+            mma32(X[x], ld_frag_tr(sKh, LDQ, 16 * sb + 4 * kg, 16 * sb + 4 * kg, 16 * x, lane), op);
+          mfma_drain();
+#pragma unroll
+          for (int x = 0; x < NB; ++x) {
+            const int col = 16 * x + 4 * kg;
+            // b_t - rho_sb: P_t + T_{sb+1} + .. + T_{wb-1} below the diagonal, P_t - T_wb on it
+            const f32x4 pt = ld4f(sB + u * LDBF + col), qv = qraw4(u, col);
+            const f32x4 xb = sb < wb ? pt + bsum4(sb + 1, wb - 1, col) : pt - ld4f(sBT + wb * D + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dbs[x][e] += rnd_op<T>(gate_op<FEAT>(qv[e], xb[e])) * X[x][e];
+              if constexpr (!FEAT) acc0[x][e] += __expf(xb[e]) * X[x][e];
+            }
+          }
+        }
+      }
+    } else {
+      frag fvu[KS], fkh[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        fvu[ks] = ld_frag(sV, LDQ, u, 32 * ks + 8 * kg);
+        fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
+      }
+      // exponent of query row `row` (block tb >= wb) against this key block's end: b_t - rho_wb
+      auto qexp1 = [&](int row, int col) {
+        const int tb = row >> 4;
+        const float pt = sB[row * LDBF + col];
+        return tb > wb ? pt + bsum1(wb + 1, tb - 1, col) : pt - sBT[wb * D + col];
+      };
+      auto qop_row = [&](int row, int ks) {
+        frag f;
+        const int col = 32 * ks + 8 * kg, tb = row >> 4;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int c4 = col + 4 * h2;
+          const f32x4 pt = ld4f(sB + row * LDBF + c4), qv = qraw4(row, c4);
+          const f32x4 xb = tb > wb ? pt + bsum4(wb + 1, tb - 1, c4) : pt - ld4f(sBT + wb * D + c4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) set_elem(f, 4 * h2 + e, gate_op<FEAT>(qv[e], xb[e]));
+        }
+        return f;
+      };
+      // A blocks (queries of block tb >= wb, keys of block wb): dv += A^T dO
+      f32x4 blk[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        blk[tb] = f32x4{0, 0, 0, 0};
+        if (tb >= wb) {
+          if (tb == wb && prw) {
+            // pairwise: this key against queries 16 tb + 4 kg + i, every column (P_t - P_s: the
+            // same block)
+#pragma unroll 1
+            for (int f = 0; f < D; f += 4) {
+              const f32x4 bs = ld4f(sB + u * LDBF + f), kv = kraw4(u, f);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int tr = 16 * tb + 4 * kg + i;
+                const f32x4 bt = ld4f(sB + tr * LDBF + f), qv = qraw4(tr, f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) blk[tb][i] += pair_term<FEAT>(qv[e], kv[e], fminf(bt[e] - bs[e], 0.f));
+              }
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], qop_row(16 * tb + r, ks), fkh[ks]);
+            mfma_drain();
+          }
+          if (tb == wb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * kg + i < r) blk[tb][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        if (2 * p + 1 >= wb) {
+          frag op;
+          pack_acc(op, blk[2 * p], blk[2 * p + 1]);
+#pragma unroll
+          for (int x = 0; x < NB; ++x)
+            mma32(acc1[x], ld_frag_tr(sdO, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
+        }
+      // dA blocks (queries tb >= wb, keys of block wb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        blk[tb] = f32x4{0, 0, 0, 0};
+        if (tb >= wb) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sdO, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fvu[ks]);
+          mfma_drain();
+          if (tb == wb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * kg + i < r) blk[tb][i] = 0.f;
+        }
+      }
+      f32x4 dkr[NB];   // raw dk (GLA)
+#pragma unroll
+      for (int x = 0; x < NB; ++x) dkr[x] = f32x4{0, 0, 0, 0};
+      if (prw) {
+        // pairwise diagonal block: dk and the k-side terms directly, e^(g_{s+1} + .. + g_t) with
+        // the sum formed going forward from the key; dA[query 16 wb + t2][this key] sits in lane
+        // r + 16 (t2 / 4), slot t2 % 4
+        const f32x4 dAq = blk[wb];
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+          const int col = 16 * x + 4 * kg;
+          const f32x4 kv = kraw4(u, col);
+          f32x4 run = f32x4{0, 0, 0, 0};
+#pragma unroll 1
+          for (int t2 = 0; t2 < 16; ++t2) {
+            if (t2 > r) run += graw4(16 * wb + t2, col);   // queries before the key carry dA = 0
+            const float dAv = __shfl(dAq[t2 & 3], r + 16 * (t2 >> 2), WAVE);
+            const f32x4 qv = qraw4(16 * wb + t2, col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dbs[x][e] += dAv * pair_term<FEAT>(qv[e], kv[e], run[e]);
+              if constexpr (!FEAT) dkr[x][e] += dAv * (qv[e] * __expf(run[e]));
+            }
+          }
+        }
+      }
+      // dk'' += dA^T q' over the other blocks (q' of queries before this key block is zero)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        if (2 * p + 1 >= wb) {
+          f32x4 b0 = blk[2 * p], b1 = blk[2 * p + 1];
+          if (prw) {
+            if (2 * p == wb) b0 = f32x4{0, 0, 0, 0};
+            if (2 * p + 1 == wb) b1 = f32x4{0, 0, 0, 0};
+          }
+          frag op;
+          pack_acc(op, b0, b1);
+#pragma unroll
+          for (int x = 0; x < NB; ++x) {
+            const int col = 16 * x + r;
+            frag qa;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int row = 32 * p + (e < 4 ? 0 : 16) + 4 * kg + (e & 3);
+              const bool use = row >= 16 * wb && !(prw && (row >> 4) == wb);
+              set_elem(qa, e, use ? gate_op<FEAT>(qraw1(row, col), qexp1(row, col)) : 0.f);
+            }
+            mma32(acc0[x], qa, op);
+            __builtin_amdgcn_sched_barrier(0);   // one operand's loads at a time (register pressure)
+          }
+        }
+      mfma_drain();
+      // intra-chunk k side: terms of d b from k'', and dk = dk'' e^(T_wb - P_s) (at most 1)
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int col = 16 * x + 4 * kg;
+        const f32x4 kpp = ld4f(sKh + u * LDQ + col);
+        const f32x4 xs = ld4f(sBT + wb * D + col) - ld4f(sB + u * LDBF + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dbs[x][e] += kpp[e] * acc0[x][e];
+          if constexpr (!FEAT) dkr[x][e] += __expf(xs[e]) * acc0[x][e];
+        }
+      }
+      // inter-chunk with k e^(gamma - b) against the stored state gradient (gamma = Gamma in the
+      // columns stored undecayed, 0 in the others): Gamma - b_s = (T_wb - P_s) + T_{wb+1} + .. + T_3,
+      // -b_s = -(T_0 + .. + T_{wb-1} + P_s); dk part V dS^T, dv += k e^(gamma - b) dS
+      auto kexp4 = [&](int col) {
+        const f32x4 ps = ld4f(sB + u * LDBF + col);
+        const f32x4 ks = ld4f(sBT + wb * D + col) - ps + bsum4(wb + 1, 3, col);
+        const f32x4 kw = -(bsum4(0, wb - 1, col) + ps);
+        f32x4 z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cc = col + e;
+          z[e] = ((cc < 64 ? sm0 >> cc : sm1 >> (cc - 64)) & 1ull) ? ks[e] : kw[e];
+        }
+        return z;
+      };
+#pragma unroll
+      for (int x = 0; x < NB; ++x) acc0[x] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        frag fki;
+        const int col = 32 * ks + 8 * kg;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f32x4 xk = kexp4(col + 4 * h2), kv = kraw4(u, col + 4 * h2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) set_elem(fki, 4 * h2 + e, gate_op<FEAT>(kv[e], xk[e]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+          mma32(acc0[x], ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * x, lane), fvu[ks]);
+          mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fki);
+        }
+      }
+      mfma_drain();
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int col = 16 * x + 4 * kg;
+        const f32x4 xk = kexp4(col), kv = kraw4(u, col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dbs[x][e] += rnd_op<T>(gate_op<FEAT>(kv[e], xk[e])) * acc0[x][e];
+          if constexpr (!FEAT) dkr[x][e] += __expf(xk[e]) * acc0[x][e];
+        }
+        acc0[x] = dkr[x];
+      }
+    }
+  } else if (qrole) {
     // (the S_prev rows of the first two K steps were issued with the staging loads)
     frag fo[KS];
 #pragma unroll
@@ -407,13 +799,17 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
       const int i = 16 * x + 4 * kg;
-      const f32x4 qd = lds4(sQt + u * LDQ + i) * acc0[x];
+      f32x4 qd;
+      if constexpr (STRONG)
+        qd = dbs[x];   // (acc0 already holds the raw dq)
+      else
+        qd = ld4f(sQt + u * LDQ + i) * acc0[x];
       *reinterpret_cast<f32x4*>(sDb + u * LDB + i) = qd;
       if constexpr (FEAT) {   // dlq = q~ dq~; the window part of dq starts from zero
         if (tok < L) *reinterpret_cast<f32x4*>(a.dlq + hoff + (size_t)tok * D + i) = qd;
         acc0[x] = f32x4{0, 0, 0, 0};
-      } else {
-        acc0[x] *= lds4(sEb + u * LDQ + i);
+      } else if constexpr (!STRONG) {
+        acc0[x] *= ld4f(sEb + u * LDQ + i);
       }
     }
   }
@@ -423,15 +819,21 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
       const int i = 16 * x + 4 * kg;
-      const f32x4 kd = lds4(sKh + u * LDQ + i) * acc0[x];
+      f32x4 kd;
+      if constexpr (STRONG)
+        kd = dbs[x];   // (acc0 already holds the raw dk)
+      else
+        kd = ld4f(sKh + u * LDQ + i) * acc0[x];
       db[x] = *reinterpret_cast<const f32x4*>(sDb + u * LDB + i) - kd;
-      if constexpr (FEAT) {   // dlk = k^ dk^; the window part of dk starts from zero
-        if (tok < L) *reinterpret_cast<f32x4*>(a.dlk + hoff + (size_t)tok * D + i) = kd;
-        acc0[x] = f32x4{0, 0, 0, 0};
+      if constexpr (FEAT || STRONG) {   // dlk = k^ dk^; the window part of dk starts from zero
+        if constexpr (FEAT) {
+          if (tok < L) *reinterpret_cast<f32x4*>(a.dlk + hoff + (size_t)tok * D + i) = kd;
+          acc0[x] = f32x4{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) db[x][e] = row_suffix16(db[x][e]);
       } else {
-        const f32x4 eb = lds4(sEb + u * LDQ + i);
+        const f32x4 eb = ld4f(sEb + u * LDQ + i);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc0[x][e] *= __builtin_amdgcn_rcpf(eb[e]);
@@ -603,8 +1005,8 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
           for (int h2 = 0; h2 < 2; ++h2) {
             const int tb = 2 * p + h2, q0 = qbase + 16 * tb;
             const f32x4 x = xs[h2], dp = dps[h2];
-            const f32x4 lse4 = lds4(sLse + it * C + 16 * tb + 4 * kg);
-            const f32x4 del4 = lds4(sDel + it * C + 16 * tb + 4 * kg);
+            const f32x4 lse4 = ld4f(sLse + it * C + 16 * tb + 4 * kg);
+            const f32x4 del4 = ld4f(sDel + it * C + 16 * tb + 4 * kg);
             // every query of the block at or after every key of this wave, within the window,
             // inside the sequence: no per-element mask
             const bool full = vis[h2] && q0 >= lo + 15 && q0 + 15 - lo < W && q0 + 15 < L;
@@ -682,6 +1084,43 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* _
   }
 }
 
+// The fast path: one workgroup per (b, h, chunk); consecutive chunks of one head share an XCD.
+template <typename T, int D, bool SG, bool FEAT>
+__global__ __launch_bounds__(NTHR_CK, 1) void chunk_kernel(BwdArgs a, const T* __restrict__ wsdS,
+                                                            const float* __restrict__ wsbnd) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NC = (a.L + C - 1) / C, BH = a.B * a.H;
+  int bh, c;
+  const int bid = blockIdx.x;
+  if ((BH & 7) == 0) {
+    const int x = bid % 8, y = bid / 8;           // y runs over (head group, chunk)
+    c = y % NC;
+    bh = (y / NC) * 8 + x;
+  } else {
+    bh = bid / NC;
+    c = bid % NC;
+  }
+  chunk_body<T, D, SG, FEAT, false>(a, wsdS, wsbnd, bh, c, smem, threadIdx.x);
+}
+
+// The sub-block path over the dispatch list (persistent workgroups; an empty list ends at once).
+template <typename T, int D, bool SG, bool FEAT>
+__global__ __launch_bounds__(NTHR_CK, 1) void chunk_strong_kernel(BwdArgs a, const T* __restrict__ wsdS,
+                                                                   const float* __restrict__ wsbnd) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NC = (a.L + C - 1) / C;
+  const int n = *a.list_count;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int id = a.list[i];
+    __syncthreads();   // the previous chunk's LDS readers are done
+    // the thread index passes through an empty asm so that nothing derived from it is hoisted out
+    // of this loop (it would stay live, and spill, across the whole chunk)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    chunk_body<T, D, SG, FEAT, true>(a, wsdS, wsbnd, id / NC, id % NC, smem, tid);
+  }
+}
+
 // ------------------------------------------------------------ meta reduce
 // Two-level deterministic sum of the per-(batch, chunk) meta partials
 // part[slot][H*M*2D]: level 1 folds each run of `per` slots into its first
@@ -713,9 +1152,13 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
 
 template <typename K>
 hipError_t set_lds(K kern, size_t bytes) {
+  // every launch: idempotent and cheap, and no process-wide flag to race on
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)bytes);
 }
+
+// Workgroups of the sub-block launch: persistent, one per compute unit.
+constexpr int kStrongGridBwd = 256;
 
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
@@ -728,6 +1171,10 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   a.ws_dmeta = reinterpret_cast<float*>(ws + wl.dmeta);
   T* wsdS = reinterpret_cast<T*>(ws + wl.dS);
   float* wsbnd = reinterpret_cast<float*>(ws + wl.bnd);
+  const StrongDispatch sd = dispatch_layout(ws + wl.disp, a.B, a.H, a.L, D);
+  a.strong = sd.mask;
+  a.list = sd.list;
+  a.list_count = sd.count;
   hipError_t e;
   if (a.L == 0) {
     if (a.M > 0) {
@@ -747,7 +1194,7 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     const int NS = sweep_segments(a.B, a.H, a.L, D);
     SweepArgs sw{feat ? (const void*)a.lq : a.q, a.dO, a.g, a.chunk_states, wsdS, wsbnd, nullptr, nullptr,
                  a.B, a.H, a.L, NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate, feat ? 1 : 0, a.o_swa,
-                 a.ws_delta, a.mix};
+                 a.ws_delta, a.mix, sd.mask, sd.count};
     if (NS > 1) {
       const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
       sw.seg_in = reinterpret_cast<float*>(ws + wl.seg);
@@ -758,16 +1205,19 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   }
   mark(1);
   {
-    using LY = CkLayout<T, D>;
-    static bool attr[3] = {false, false, false};   // idempotent; a race only repeats the same call
+    using LY = CkLayout<T, D, false>;
+    using LS = CkLayout<T, D, true>;
     const int variant = a.lq != nullptr ? 2 : a.gate ? 1 : 0;   // log features: per-dimension gates only
     auto kern = variant == 2 ? chunk_kernel<T, D, false, true>
               : variant == 1 ? chunk_kernel<T, D, true, false> : chunk_kernel<T, D, false, false>;
-    if (!attr[variant]) {
-      if ((e = set_lds(kern, LY::bytes)) != hipSuccess) return e;
-      attr[variant] = true;
-    }
+    auto skern = variant == 2 ? chunk_strong_kernel<T, D, false, true>
+               : variant == 1 ? chunk_strong_kernel<T, D, true, false> : chunk_strong_kernel<T, D, false, false>;
+    if ((e = set_lds(kern, LY::bytes)) != hipSuccess) return e;
+    if ((e = set_lds(skern, LS::bytes)) != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(BH * NC), dim3(NTHR_CK), LY::bytes, st, a, (const T*)wsdS, (const float*)wsbnd);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(skern, dim3(min(BH * NC, kStrongGridBwd)), dim3(NTHR_CK), LS::bytes, st, a, (const T*)wsdS,
+                       (const float*)wsbnd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(2);

@@ -310,6 +310,25 @@ __device__ __forceinline__ typename Tr<T>::frag ldg_row_frag(const T* base, int 
   return row < nrows ? ldg_frag<T>(base + (size_t)row * ld + col) : zero_frag<T>();
 }
 
+// Four consecutive elements (LDS or global) as floats.
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4f(const bf16_t* p) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// ------------------------------------------------------- gate absorbed into an operand
+// The gate meets a GLA operand as src * e^x (raw q or k) or e^(src + x) (log features src); x is
+// a difference of chunk-local cumulative log-gates.  Every kernel that must reproduce another's
+// operand value bit for bit forms it through this one function.
+template <bool FEAT>
+__device__ __forceinline__ float gate_op(float src, float x) {
+  if constexpr (FEAT)
+    return __expf(src + x);
+  else
+    return src * __expf(x);
+}
+
 // ------------------------------------------------------- chunk-local gate prefix
 // Thread map of a CHUNK x D tile: column group cg (VEC dims), tokens
 // tg*TPT .. +TPT.  Computes the chunk-local inclusive prefix b of the
@@ -353,6 +372,39 @@ __device__ __forceinline__ void chunk_prefix(f32x4 (&rg)[TPT_][GV_], f32x4 (&tot
 }
 
 // ------------------------------------------------- gate prefix in column strips
+// Block-local sums of a strip (see GateStrip below) for the sub-block form.  The 16 tokens of a
+// 16-token block sit in four consecutive lanes of a row (tg & ~3 .. tg | 3, four tokens each).
+// g[u] is replaced by P, the inclusive prefix of the log-gates inside the token's block; S[u]
+// gets the exclusive suffix inside the block and T the block total.  Each is a sum of at most 16
+// gates, so its rounding error is relative to its own size: exponents formed from them stay
+// accurate however far the chunk-cumulative sum has fallen.
+__device__ __forceinline__ void block_sums(f32x4 (&g)[4], f32x4 (&S)[4], f32x4& T, int lane) {
+  f32x4 pin[4], sin[4];
+  pin[0] = g[0];
+#pragma unroll
+  for (int u = 1; u < 4; ++u) pin[u] = pin[u - 1] + g[u];
+  sin[3] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 2; u >= 0; --u) sin[u] = sin[u + 1] + g[u + 1];
+  const int q0 = lane & ~3, qi = lane & 3;
+  f32x4 ep = f32x4{0, 0, 0, 0}, es = ep, tot = ep;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __shfl(pin[3][e], q0 + j, WAVE);
+    tot += o;
+    if (j < qi) ep += o;
+    if (j > qi) es += o;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    g[u] = pin[u] + ep;
+    S[u] = sin[u] + es;
+  }
+  T = tot;
+}
+
 // One wave handles a strip of 16 columns of a chunk: lane (tg = lane & 15,
 // cg = lane >> 4) holds tokens 4*tg .. 4*tg+3 of columns col .. col+3 with
 // col = 16*strip + 4*cg, so the chunk-local prefix over tokens is an
@@ -423,6 +475,30 @@ struct GateStrip {
       if (sEb != nullptr) st4(sEb + row, eb[0], eb[1], eb[2], eb[3]);
     }
   }
+
+  // Sub-block form (gates too strong for the chunk-start factoring): the block-local prefixes P to
+  // sB, the block totals T to sBT (row kb), the keys folded to the end of their own block,
+  // k e^S (S the block-local suffix, so at most |k|), to sKh, the raw q to sQr; sSpan[kb] gets
+  // the largest decay inside block kb, -T, over the strip's 16 columns.
+  __device__ __forceinline__ void fold_strong(T* sQr, T* sKh, int ldq, float* sB, int ldb, float* sBT, int D,
+                                              float* sSpan, int lcol, int tg, int lane) {
+    f32x4 S[4], Tb;
+    block_sums(g, S, Tb, lane);
+    float m = fmaxf(fmaxf(-Tb[0], -Tb[1]), fmaxf(-Tb[2], -Tb[3]));
+    m = xor_max(xor_max(m, 16), 32);
+    if ((lane & 51) == 0) sSpan[tg >> 2] = m;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 4 * tg + u;
+      *reinterpret_cast<f32x4*>(sB + row * ldb + lcol) = g[u];
+      f32x4 kh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kh[e] = gate_op<false>((float)k[u][e], S[u][e]);
+      st4(sKh + row * ldq + lcol, kh[0], kh[1], kh[2], kh[3]);
+      st4(sQr + row * ldq + lcol, (float)q[u][0], (float)q[u][1], (float)q[u][2], (float)q[u][3]);
+    }
+    if ((tg & 3) == 0) *reinterpret_cast<f32x4*>(sBT + (tg >> 2) * D + lcol) = Tb;
+  }
 };
 
 // The same strip for log features lq, lk (fp32) of the GLA branch: the gate is absorbed in log
@@ -473,6 +549,27 @@ struct GateStripLog {
       st4(sKh + row, kh[0], kh[1], kh[2], kh[3]);
       if (sEb != nullptr) st4(sEb + row, eb[0], eb[1], eb[2], eb[3]);
     }
+  }
+
+  // Sub-block form as for GateStrip (the log-feature queries are read where they are used).
+  __device__ __forceinline__ void fold_strong(T*, T* sKh, int ldq, float* sB, int ldb, float* sBT, int D,
+                                              float* sSpan, int lcol, int tg, int lane) {
+    f32x4 S[4], Tb;
+    block_sums(g, S, Tb, lane);
+    float m = fmaxf(fmaxf(-Tb[0], -Tb[1]), fmaxf(-Tb[2], -Tb[3]));
+    m = xor_max(xor_max(m, 16), 32);
+    if ((lane & 51) == 0) sSpan[tg >> 2] = m;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 4 * tg + u;
+      const bool ok = u < nvalid;
+      *reinterpret_cast<f32x4*>(sB + row * ldb + lcol) = g[u];
+      f32x4 kh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kh[e] = gate_op<true>(ok ? k[u][e] : -INFINITY, S[u][e]);
+      st4(sKh + row * ldq + lcol, kh[0], kh[1], kh[2], kh[3]);
+    }
+    if ((tg & 3) == 0) *reinterpret_cast<f32x4*>(sBT + (tg >> 2) * D + lcol) = Tb;
   }
 };
 

@@ -77,30 +77,54 @@ struct OutLayout {
   static constexpr size_t tile = sizeof(T) * C * LDQ;
   static constexpr size_t oK = 0;          // raw keys of a window chunk, then q~
   static constexpr size_t oV = tile;       // values of a window chunk (ends with this chunk's)
-  static constexpr size_t oX = 2 * tile;   // k^
+  static constexpr size_t oX = 2 * tile;   // k^ (sub-block path: keys folded to their block end)
   static constexpr size_t oS = 3 * tile;   // 64 rows of the entering state; gate-scan scratch before
   static constexpr size_t oMk = 4 * tile;
   static constexpr size_t oMvt = oMk + sizeof(T) * 16 * LDQ;
   static constexpr size_t bytes = oMvt + sizeof(T) * D * LDMV;
   static_assert(sizeof(float) * ScanMap<D, VEC, NTHR>::NTG * D <= tile, "scan scratch fits");
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+  // sub-block path only: the fp32 block-local gate prefixes [C][D+4], the 16-token block
+  // totals [4][D] and the diagonal blocks' choice
+  static constexpr int LDBF = D + 4;
+  static constexpr size_t oB = bytes;
+  static constexpr size_t oBT = oB + sizeof(float) * C * LDBF;
+  static constexpr size_t oPair = oBT + sizeof(float) * 4 * D;
+  static constexpr size_t strong_bytes = oPair + sizeof(int) * 4;
+  static_assert(strong_bytes <= 160 * 1024, "LDS budget");
 };
 
+__device__ __forceinline__ void set_elem(bf16x8& f, int e, float x) { f[e] = (__bf16)x; }
+__device__ __forceinline__ void set_elem(f32x8& f, int e, float x) { f[e] = x; }
+
+// One chunk of the forward: 64 queries over all of d_v.
 // CONT: the segment continues a sequence (key history in the ring, position offset pos[b]).
 // SG: one log-gate per head and token (g [B,H,L]), broadcast over the key dimensions.
 // FEAT: the GLA branch reads the fp32 log features lq, lk of phi(q), phi(k) and absorbs the
 // gate in log space (q~ = exp(lq + b), k^ = exp(lk - b)); the window keeps the raw q, k.
-template <typename T, int D, bool CONT, bool SG, bool FEAT>
-__global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __restrict__ cstates) {
+// STRONG: the intra-chunk scores by 16-token blocks.  Folding the gate into q and k relative
+// to the chunk start needs e^(-b) inside the floating-point range, which fails when a column's
+// gate sums to less than -kStrongGate over the chunk.  Here the score of query t against key
+// s of key block j is sum_i q_t e^(b_t - rho_j) * k_s e^(rho_j - b_s), rho_j = b at the last
+// token of block j: both factors are at most 1 for every j below the query's block; on the
+// diagonal block the query factor stays below e^kStrongGate unless the block itself decays
+// more than that, and such a block takes the exact pairwise form sum_i q k e^(b_t - b_s).  The
+// exponents come from block-local sums (the prefix P and suffix S inside a 16-token block, the
+// block totals T), never from differences of chunk-cumulative sums, so each is as accurate as
+// its own size: b_t - rho_j = P_t + T_{j+1} + .. + T_{i-1} (t in block i), rho_j - b_s = S_s.
+// Without STRONG, a chunk flagged by the state sweep is appended to the dispatch list and left
+// to the STRONG launch.
+template <typename T, int D, bool CONT, bool SG, bool FEAT, bool STRONG>
+__device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict__ cstates, int bh, int c,
+                                          unsigned char* smem, int tid) {
   using LY = OutLayout<T, D>;
   using SM = ScanMap<D, Tr<T>::VEC, NTHR>;
   using frag = typename Tr<T>::frag;
   constexpr int VEC = LY::VEC, TPT = SM::TPT, GV = SM::GV;
-  constexpr int JB = D / 16, KS = D / 32, LDQ = LY::LDQ;
+  constexpr int JB = D / 16, KS = D / 32, LDQ = LY::LDQ, LDBF = LY::LDBF;
   constexpr int NVT = C * (D / VEC) / NTHR;   // 16-byte vectors per thread of a [C][D] tile
   constexpr int NSH = D / 64;                 // 64-row slices of the state
 
-  extern __shared__ __align__(16) unsigned char smem[];
   T* sK = reinterpret_cast<T*>(smem + LY::oK);
   T* sV = reinterpret_cast<T*>(smem + LY::oV);
   T* sX = reinterpret_cast<T*>(smem + LY::oX);
@@ -108,23 +132,19 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   float* sScan = reinterpret_cast<float*>(smem + LY::oS);
   T* sMk = reinterpret_cast<T*>(smem + LY::oMk);
   T* sMvt = reinterpret_cast<T*>(smem + LY::oMvt);
+  float* sB = reinterpret_cast<float*>(smem + LY::oB);       // STRONG only
+  float* sBT = reinterpret_cast<float*>(smem + LY::oBT);     // STRONG only
+  int* sPair = reinterpret_cast<int*>(smem + LY::oPair);     // STRONG only
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, kg = lane >> 4;
   const int L = a.L, NC = (L + C - 1) / C, M = a.M, W = a.W;
-  // workgroup -> (batch*head, chunk); consecutive chunks of one head share an XCD
-  const int BH = a.B * a.H;
-  int bh, c;
-  {
-    const int bid = blockIdx.x;
-    if ((BH & 7) == 0) {
-      const int x = bid % 8, y = bid / 8;
-      c = y % NC;
-      bh = (y / NC) * 8 + x;
-    } else {
-      bh = bid / NC;
-      c = bid % NC;
-    }
+  // fast path: the sweep's strong-column masks of this chunk (checked once the loads are out)
+  uint64_t smask = 0;
+  if constexpr (!STRONG) {
+    const uint64_t* mp = reinterpret_cast<const uint64_t*>(a.strong + ((size_t)bh * NC + c) * (D / 16));
+    smask = mp[0];
+    if constexpr (D == 128) smask |= mp[1];
   }
   const int h = bh % a.H;
   const size_t hoff = (size_t)bh * L * D;
@@ -190,6 +210,13 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   frag qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = ldg_row_frag<T>(q, D, tq, 32 * ks + 8 * kg, L);
+
+  if constexpr (!STRONG) {
+    if (smask != 0) {   // the sub-block launch takes this chunk
+      if (tid == 0) a.list[atomicAdd(a.list_count, 1)] = bh * NC + c;
+      return;
+    }
+  }
 
   // meta keys / values (absent values staged as zeros: no branch around the product)
   for (int e = tid; e < 16 * (D / VEC); e += NTHR) {
@@ -308,6 +335,7 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
 
   // ---- GLA branch
   __syncthreads();   // every wave is done with the last key tile
+  f32x4 sufl[TPT][GV];   // STRONG: block-local exclusive suffixes S of this thread's tokens
   {
     if constexpr (FEAT) {
 #pragma unroll
@@ -320,28 +348,96 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
         }
     }
     f32x4 tot[GV];
+    f32x4 pinl[TPT][GV];   // STRONG: in-thread inclusive prefixes
+    if constexpr (STRONG) {
+#pragma unroll
+      for (int e = 0; e < GV; ++e) {
+        pinl[0][e] = rg[0][e];
+#pragma unroll
+        for (int u = 1; u < TPT; ++u) pinl[u][e] = pinl[u - 1][e] + rg[u][e];
+        sufl[TPT - 1][e] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = TPT - 2; u >= 0; --u) sufl[u][e] = sufl[u + 1][e] + rg[u + 1][e];
+      }
+    }
     chunk_prefix<D, VEC, NTHR, TPT, GV>(rg, tot, sScan, cg, tg);
+    if constexpr (STRONG) {
+      // block-local prefixes P (to LDS), suffixes S (kept in registers) and the block totals T
+      // (to LDS), from the token groups' totals the prefix left in the scan scratch
+      constexpr int GPB = 16 / TPT;               // token groups per 16-token block
+      const int blk = tg / GPB, lg = tg % GPB;
+#pragma unroll
+      for (int e = 0; e < GV; ++e) {
+        f32x4 ep = f32x4{0, 0, 0, 0}, es = ep, tb = ep;
+#pragma unroll
+        for (int j = 0; j < GPB; ++j) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(sScan + (blk * GPB + j) * D + cg * VEC + 4 * e);
+          tb += o;
+          if (j < lg) ep += o;
+          if (j > lg) es += o;
+        }
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+          *reinterpret_cast<f32x4*>(sB + (tg * TPT + u) * LDBF + cg * VEC + 4 * e) = pinl[u][e] + ep;
+          sufl[u][e] += es;
+        }
+        if (lg == 0) *reinterpret_cast<f32x4*>(sBT + blk * D + cg * VEC + 4 * e) = tb;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
+      // q~ = q e^b (the inter-chunk operand), and on the fast path k^ = k e^-b
+      const bool in = t0 + tg * TPT + u < L;   // rows past the end: -inf, a zero operand as in the raw form
       float qt[VEC], kh[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float bb = rg[u][e >> 2][e & 3];
-        if constexpr (FEAT) {   // rows past the end: -inf, a zero operand as in the raw form
-          const bool in = t0 + tg * TPT + u < L;
-          qt[e] = __expf((in ? lqv[u][e >> 2][e & 3] : -INFINITY) + bb);
-          kh[e] = __expf((in ? lkv[u][e >> 2][e & 3] : -INFINITY) - bb);
+        if constexpr (FEAT) {
+          qt[e] = gate_op<true>(in ? lqv[u][e >> 2][e & 3] : -INFINITY, bb);
+          if constexpr (!STRONG) kh[e] = gate_op<true>(in ? lkv[u][e >> 2][e & 3] : -INFINITY, -bb);
         } else {
-          qt[e] = v16_get(rq[u], e, (T*)nullptr) * __expf(bb);
-          kh[e] = v16_get(rk[u], e, (T*)nullptr) * __expf(-bb);
+          qt[e] = gate_op<false>(v16_get(rq[u], e, (T*)nullptr), bb);
+          if constexpr (!STRONG) kh[e] = gate_op<false>(v16_get(rk[u], e, (T*)nullptr), -bb);
         }
       }
       const int t = tg * TPT + u;
       st_vec(sK + t * LDQ + cg * VEC, qt);
+      if constexpr (!STRONG) st_vec(sX + t * LDQ + cg * VEC, kh);
+    }
+  }
+  if constexpr (STRONG) {
+    // keys folded to the end of their own block: k e^S, at most |k|
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = tg * TPT + u;
+      const bool in = t0 + t < L;
+      float kh[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float x = sufl[u][e >> 2][e & 3];
+        if constexpr (FEAT)
+          kh[e] = gate_op<true>(in ? lkv[u][e >> 2][e & 3] : -INFINITY, x);
+        else
+          kh[e] = gate_op<false>(v16_get(rk[u], e, (T*)nullptr), x);
+      }
       st_vec(sX + t * LDQ + cg * VEC, kh);
     }
   }
   __syncthreads();   // q~, k^ visible; scan scratch free
+  if constexpr (STRONG) {
+    // diagonal blocks whose own decay exceeds the factoring's range (bf16) or its accurate range
+    // (fp32) take the pairwise form (the barrier before the intra-chunk part publishes it)
+    constexpr float kPairSpan = std::is_same<T, float>::value ? 16.f : kStrongGate;
+    if (w == 0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float span = 0.f;
+        for (int col = lane; col < D; col += WAVE) span = fmaxf(span, -sBT[kb * D + col]);
+        span = wave_max(span);
+        if (lane == 0) sPair[kb] = span > kPairSpan ? 1 : 0;
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < NVT; ++u) {
     const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
@@ -351,18 +447,97 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   {
     // intra-chunk: O^T += V^T (q~ k^T masked)^T
     f32x4 sc[4];
+    if constexpr (STRONG) {
+      // this wave's queries: block-local gate prefixes and the raw operand (log features) in the
+      // operand layout
+      f32x4 bq[KS][2];
+      float qs[KS][8];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sc[kb] = f32x4{0, 0, 0, 0};
-      if (kb <= w) {
+      for (int ks = 0; ks < KS; ++ks) {
+        bq[ks][0] = ld4f(sB + (16 * w + r) * LDBF + 32 * ks + 8 * kg);
+        bq[ks][1] = ld4f(sB + (16 * w + r) * LDBF + 32 * ks + 8 * kg + 4);
+        if constexpr (FEAT) {
+          const float* lp = a.lq + hoff + (size_t)min(tq, L - 1) * D + 32 * ks + 8 * kg;
+          const f32x4 l0 = ld4f(lp), l1 = ld4f(lp + 4);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          mma32(sc[kb], ld_frag(sX, LDQ, 16 * kb + r, 32 * ks + 8 * kg), ld_frag(sK, LDQ, 16 * w + r, 32 * ks + 8 * kg));
-        mfma_drain();
-        if (kb == w) {
+          for (int e = 0; e < 4; ++e) {
+            qs[ks][e] = qvalid ? l0[e] : -INFINITY;
+            qs[ks][4 + e] = qvalid ? l1[e] : -INFINITY;
+          }
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * kg + i > r) sc[kb][i] = 0.f;
+          for (int e = 0; e < 8; ++e) qs[ks][e] = (float)qf[ks][e];
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sc[kb] = f32x4{0, 0, 0, 0};
+        if (kb <= w) {
+          if (kb == w && sPair[w] != 0) {
+            // exact pairwise scores: query 16w + r against keys 16w + 4kg + i, every column (the
+            // same block: b_t - b_s = P_t - P_s)
+            const int tl = 16 * w + r;
+            const size_t tr = (size_t)min(t0 + tl, L - 1) * D;
+            for (int f = 0; f < D; f += 4) {
+              const f32x4 bt = ld4f(sB + tl * LDBF + f);
+              const f32x4 qv = FEAT ? ld4f(a.lq + hoff + tr + f) : ld4f(q + tr + f);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int sl = 16 * w + 4 * kg + i;
+                const size_t sr = (size_t)min(t0 + sl, L - 1) * D;
+                const f32x4 bs = ld4f(sB + sl * LDBF + f);
+                const f32x4 kv = FEAT ? ld4f(a.lk + hoff + sr + f) : ld4f(k + sr + f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float x = fminf(bt[e] - bs[e], 0.f);   // keys after the query are masked below
+                  sc[kb][i] += FEAT ? __expf(qv[e] + kv[e] + x) : qv[e] * kv[e] * __expf(x);
+                }
+              }
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              // b_t - rho_kb: P_t + T_{kb+1} + .. + T_{w-1} below the diagonal, P_t - T_w on it
+              f32x4 h[2];
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const int col = 32 * ks + 8 * kg + 4 * h2;
+                if (kb < w) {
+                  h[h2] = f32x4{0, 0, 0, 0};
+                  for (int m = kb + 1; m < w; ++m) h[h2] += ld4f(sBT + m * D + col);
+                } else {
+                  h[h2] = -ld4f(sBT + w * D + col);
+                }
+              }
+              frag qop;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                set_elem(qop, e, gate_op<FEAT>(qs[ks][e], bq[ks][e >> 2][e & 3] + h[e >> 2][e & 3]));
+              mma32(sc[kb], ld_frag(sX, LDQ, 16 * kb + r, 32 * ks + 8 * kg), qop);
+            }
+            mfma_drain();
+          }
+          if (kb == w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * kg + i > r) sc[kb][i] = 0.f;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sc[kb] = f32x4{0, 0, 0, 0};
+        if (kb <= w) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            mma32(sc[kb], ld_frag(sX, LDQ, 16 * kb + r, 32 * ks + 8 * kg), ld_frag(sK, LDQ, 16 * w + r, 32 * ks + 8 * kg));
+          mfma_drain();
+          if (kb == w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * kg + i > r) sc[kb][i] = 0.f;
+          }
         }
       }
     }
@@ -405,32 +580,84 @@ __global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __rest
   }
 }
 
+// The fast path: one workgroup per (batch, head, chunk); consecutive chunks of one head share
+// an XCD.  Chunks flagged by the sweep go to the dispatch list instead.
+template <typename T, int D, bool CONT, bool SG, bool FEAT>
+__global__ __launch_bounds__(NTHR, 2) void out_kernel(FwdArgs a, const T* __restrict__ cstates) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NC = (a.L + C - 1) / C, BH = a.B * a.H;
+  int bh, c;
+  const int bid = blockIdx.x;
+  if ((BH & 7) == 0) {
+    const int x = bid % 8, y = bid / 8;
+    c = y % NC;
+    bh = (y / NC) * 8 + x;
+  } else {
+    bh = bid / NC;
+    c = bid % NC;
+  }
+  out_chunk<T, D, CONT, SG, FEAT, false>(a, cstates, bh, c, smem, threadIdx.x);
+}
+
+// The sub-block path over the dispatch list (persistent workgroups; an empty list ends at once).
+template <typename T, int D, bool CONT, bool SG, bool FEAT>
+__global__ __launch_bounds__(NTHR, 1) void out_strong_kernel(FwdArgs a, const T* __restrict__ cstates) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NC = (a.L + C - 1) / C;
+  const int n = *a.list_count;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int id = a.list[i];
+    __syncthreads();   // the previous chunk's LDS readers are done
+    // the thread index passes through an empty asm so that nothing derived from it is hoisted out
+    // of this loop (it would stay live, and spill, across the whole chunk)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    out_chunk<T, D, CONT, SG, FEAT, true>(a, cstates, id / NC, id % NC, smem, tid);
+  }
+}
+
 __global__ void zero_state_kernel(float* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
 }
 
+template <typename K>
+hipError_t set_lds(K kern, size_t bytes) {
+  // every launch: idempotent and cheap, and no process-wide flag to race on
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+// Workgroups of the sub-block launch: persistent, one per compute unit.
+constexpr int kStrongGrid = 256;
+
 template <typename T, int D>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t st) {
   using LY = OutLayout<T, D>;
   hipError_t e;
-  if (a.L == 0) {
-    if (a.state_out != nullptr) {
-      const size_t n = (size_t)a.B * a.H * D * D;
-      hipLaunchKernelGGL(zero_state_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.state_out, n);
+  if (args.L == 0) {
+    if (args.state_out != nullptr) {
+      const size_t n = (size_t)args.B * args.H * D * D;
+      hipLaunchKernelGGL(zero_state_kernel, dim3((n + 255) / 256), dim3(256), 0, st, args.state_out, n);
     }
     return hipGetLastError();
   }
-  // workspace: segment buffers of the sweep (when it runs in segments), then the chunk states
+  // workspace: segment buffers of the sweep (when it runs in segments), the strong-gate
+  // dispatch, then the chunk states (when they are not an output)
+  FwdArgs a = args;
   const int NC = (a.L + C - 1) / C;
   const int NS = sweep_segments(a.B, a.H, a.L, D);
   const size_t segb = fwd_segment_bytes(a.B, a.H, a.L, D);
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
-  void* states = a.chunk_states != nullptr ? a.chunk_states : ws + segb;
+  const StrongDispatch sd = dispatch_layout(ws + segb, a.B, a.H, a.L, D);
+  a.strong = sd.mask;
+  a.list = sd.list;
+  a.list_count = sd.count;
+  void* states = a.chunk_states != nullptr ? a.chunk_states : ws + segb + dispatch_bytes(a.B, a.H, a.L, D);
   const bool feat = a.lk != nullptr;
   SweepArgs sw{feat ? (const void*)a.lk : a.k, a.v, a.g, nullptr, states, nullptr, a.state_out, a.state_in,
                a.B, a.H, a.L, NS, (NC + NS - 1) / NS, nullptr, nullptr, nullptr, a.gate, feat ? 1 : 0,
-               nullptr, nullptr, 0.f};
+               nullptr, nullptr, 0.f, sd.mask, sd.count};
   if (NS > 1) {
     const size_t mat = (size_t)a.B * a.H * NS * D * D * sizeof(float);
     sw.seg_in = reinterpret_cast<float*>(ws);
@@ -445,14 +672,19 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
       variant == 0 ? out_kernel<T, D, false, false, false> : variant == 1 ? out_kernel<T, D, true, false, false>
       : variant == 2 ? out_kernel<T, D, false, true, false> : variant == 3 ? out_kernel<T, D, true, true, false>
       : variant == 4 ? out_kernel<T, D, false, false, true> : out_kernel<T, D, true, false, true>;
-  static bool attr_set[6] = {false, false, false, false, false, false};   // idempotent; a race only repeats the same call
-  if (!attr_set[variant]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)LY::bytes);
-    if (e != hipSuccess) return e;
-    attr_set[variant] = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H * NC), dim3(NTHR), LY::bytes, st, a, (const T*)states);
+  decltype(&out_strong_kernel<T, D, false, false, false>) skern =
+      variant == 0 ? out_strong_kernel<T, D, false, false, false>
+      : variant == 1 ? out_strong_kernel<T, D, true, false, false>
+      : variant == 2 ? out_strong_kernel<T, D, false, true, false>
+      : variant == 3 ? out_strong_kernel<T, D, true, true, false>
+      : variant == 4 ? out_strong_kernel<T, D, false, false, true> : out_strong_kernel<T, D, true, false, true>;
+  if ((e = set_lds(kern, LY::bytes)) != hipSuccess) return e;
+  if ((e = set_lds(skern, LY::strong_bytes)) != hipSuccess) return e;
+  const int nchunks = a.B * a.H * NC;
+  hipLaunchKernelGGL(kern, dim3(nchunks), dim3(NTHR), LY::bytes, st, a, (const T*)states);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(skern, dim3(min(nchunks, kStrongGrid)), dim3(NTHR), LY::strong_bytes, st, a,
+                     (const T*)states);
   return hipGetLastError();
 }
 
@@ -513,8 +745,28 @@ size_t fwd_segment_bytes(int B, int H, int L, int D) {
   return 2 * mat + (vec + 255) / 256 * 256;
 }
 
+size_t dispatch_bytes(int B, int H, int L, int D) {
+  const size_t n = (size_t)B * H * ((L + C - 1) / C);
+  return 256 + (4 * n + 255) / 256 * 256 + (2 * n * (D / 16) + 255) / 256 * 256;
+}
+
+StrongDispatch dispatch_layout(void* base, int B, int H, int L, int D) {
+  unsigned char* p = reinterpret_cast<unsigned char*>(base);
+  const size_t n = (size_t)B * H * ((L + C - 1) / C);
+  StrongDispatch d;
+  d.count = reinterpret_cast<int32_t*>(p);
+  d.list = reinterpret_cast<int32_t*>(p + 256);
+  d.mask = reinterpret_cast<uint16_t*>(p + 256 + (4 * n + 255) / 256 * 256);
+  (void)D;
+  return d;
+}
+
+size_t fwd_aux_bytes(int B, int H, int L, int D) {
+  return L > 0 ? fwd_segment_bytes(B, H, L, D) + dispatch_bytes(B, H, L, D) : 0;
+}
+
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype) {
-  return fwd_segment_bytes(B, H, L, D) + (size_t)B * H * ((L + C - 1) / C) * D * D * (dtype == 1 ? 2 : 4);
+  return fwd_aux_bytes(B, H, L, D) + (size_t)B * H * ((L + C - 1) / C) * D * D * (dtype == 1 ? 2 : 4);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, hipStream_t st) {

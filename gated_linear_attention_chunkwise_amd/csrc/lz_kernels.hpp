@@ -22,7 +22,23 @@ struct FwdArgs {
   // optional fp32 log features [B,H,L,d] of phi(q), phi(k) for the GLA branch (both or neither;
   // per-dimension gates, no continuation); the window branch reads q and k
   const float* lq; const float* lk;
+  // set by the launcher (strong-gate dispatch, see StrongDispatch)
+  uint16_t* strong; int32_t* list; int32_t* list_count;
 };
+
+// Strong-gate dispatch.  The gate is folded into q and k relative to the chunk start only while
+// every column's chunk total Gamma stays at or above -kStrongGate; a chunk with any column below
+// takes the sub-block path instead.  The state sweep writes, per (b*h, chunk), D/16 masks of 16
+// bits (bit e of mask m: column 16m + e has Gamma < -kStrongGate) and zeroes list_count; the
+// chunk-parallel kernel of the fast path appends every chunk with a nonzero mask to `list`
+// (index b*h*NC + c) and leaves it, and a second launch of the sub-block variant works through
+// the list.  Workspace: dispatch_bytes().
+constexpr float kStrongGate = 64.f;
+size_t dispatch_bytes(int B, int H, int L, int D);
+struct StrongDispatch {
+  uint16_t* mask; int32_t* list; int32_t* count;
+};
+StrongDispatch dispatch_layout(void* base, int B, int H, int L, int D);
 
 struct BwdArgs {
   const void* q; const void* k; const void* v; const float* g;
@@ -39,6 +55,8 @@ struct BwdArgs {
   // optional log features as in FwdArgs, with their gradients dlq, dlk [B,H,L,d] fp32 written;
   // dq, dk then hold the window branch's part only
   const float* lq; const float* lk; float* dlq; float* dlk;
+  // set by the launcher (strong-gate dispatch)
+  uint16_t* strong; int32_t* list; int32_t* list_count;
 };
 
 // One sequential sweep over chunks (lz_sweep.hip).  Forward: a_src = k,
@@ -68,6 +86,11 @@ struct SweepArgs {
   // delta_t = mix * dO_t . o_swa_t [B,H,L] fp32 from the dO rows they stream (each block a
   // share of the token rows)
   const void* o_swa; float* delta; float mix;
+  // strong-gate masks [B*H][NC][D/16] written by the sweep pass (NULL: none), and the
+  // dispatch list counter it zeroes (NULL: none).  Backward: the state gradient is stored
+  // decayed (dS' = e^Gamma dS) in the columns whose mask bit is clear and undecayed (dS) in
+  // the columns whose bit is set, where e^Gamma may underflow.
+  uint16_t* strong; int32_t* list_count;
 };
 
 struct DecodeArgs {
@@ -129,9 +152,10 @@ hipError_t launch_gate_bwd(const GateArgs& a, int dtype, hipStream_t st);   // L
 
 // Segments of the forward sweep for this shape (sequence parallelism when B*H is small).
 int sweep_segments(int B, int H, int L, int D);
-// Workspace bytes of the forward: the segment buffers (first), then the chunk states
-// (used when no chunk-state output is given).
+// Workspace bytes of the forward: the segment buffers (first), the strong-gate dispatch
+// (fwd_aux_bytes covers both), then the chunk states (used when no chunk-state output is given).
 size_t fwd_segment_bytes(int B, int H, int L, int D);
+size_t fwd_aux_bytes(int B, int H, int L, int D);
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype);
 // Workspace bytes needed by launch_decode.
 size_t decode_workspace_bytes(int B, int H, int D);

@@ -12,9 +12,12 @@
 //             row-major [d_k][d_v], and the final state in fp32;
 //   backward, chunks descending:  dS_{c-1} = diag(e^Gamma) dS_c + (q e^b)^T dO
 //             where dS_c is the gradient w.r.t. the state after chunk c;
-//             stores dS'_c = diag(e^Gamma) dS_c transposed ([d_v][d_k]) and the
-//             boundary term of the gate gradient, rowsum(S_{c+1} (.) dS_c),
-//             per 64-wide d_v tile.
+//             stores dS'_c = diag(e^Gamma) dS_c transposed ([d_v][d_k]) (rows i whose
+//             Gamma_i is below -kStrongGate keep dS_c undecayed: e^Gamma may underflow
+//             there) and the boundary term of the gate gradient,
+//             rowsum(S_{c+1} (.) dS_c), per 64-wide d_v tile.
+//   Both directions also publish, per chunk, which key columns have a chunk total
+//   below -kStrongGate (the dispatch of the chunk kernels' sub-block path).
 //
 // Element (i, j) of the carried matrix evolves independently of every other,
 // so the sweep is tiled over blocks of 64 rows (d_k): one workgroup per
@@ -46,16 +49,10 @@ struct SwLayout {
   static constexpr size_t oA = 0;                                   // [C][TT]  gate-folded q or k (i tile)
   static constexpr size_t oB = oA + sizeof(T) * CHUNK * LDA;        // [C][D]   v or dO (every j)
   static constexpr size_t oS = oB + sizeof(T) * CHUNK * LDB;        // [TT][D]  state rows (backward)
-  static constexpr size_t oDec = oS + sizeof(T) * TT * LDB;
-  static constexpr size_t bytes = oDec + sizeof(float) * TT;
+  static constexpr size_t oDec = oS + sizeof(T) * TT * LDB;   // e^Gamma of the 64 rows
+  static constexpr size_t oFac = oDec + sizeof(float) * TT;    // backward: factor of the stored dS
+  static constexpr size_t bytes = oFac + sizeof(float) * TT;
 };
-
-// Four consecutive elements of T (8 or 16 bytes) as floats.
-__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 ld4f(const bf16_t* p) {
-  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
 
 // Four values of column c0 + (lane & 15), rows r0 .. r0+3, of a row-major LDS tile.
 __device__ __forceinline__ f32x4 col4(const bf16_t* tile, int ld, int r0, int c0, int lane) {
@@ -103,6 +100,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   T* sB = reinterpret_cast<T*>(smem + LY::oB);
   T* sS = reinterpret_cast<T*>(smem + LY::oS);
   float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
+  float* sFac = reinterpret_cast<float*>(smem + LY::oFac);
 
   // One workgroup carries a block of 64 rows (i) of the state over every column (j): four waves
   // per 64 x 64 tile (wave w of tile jt), so the i tile's gate-folded q or k is formed once and
@@ -221,6 +219,8 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
     for (int ib = 0; ib < 4; ++ib) asm volatile("" ::"v"(acc[ib][0]), "v"(acc[ib][1]), "v"(acc[ib][2]), "v"(acc[ib][3]));
   }
   f32x4 gsum = f32x4{0, 0, 0, 0};   // reduce: gate total of this lane's four key columns
+  if constexpr (!REDUCE)
+    if (a.list_count != nullptr && blockIdx.x == 0 && tid == 0) *a.list_count = 0;
 
   auto chunk_of = [&](int n) { return REV ? c_end - 1 - n : c_begin + n; };
   const int nlast = max(NCs - 1, 0);
@@ -268,30 +268,61 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
           s.rg[u] = f32x4{0, 0, 0, 0};
         }
       }
-      // chunk-local inclusive prefix b of the gates and the chunk total Gamma
+      // chunk-local inclusive prefix b of the gates and the chunk total Gamma; the forward also
+      // forms Gamma - b (the keys' decay to the chunk end) directly as the exclusive suffix of the
+      // gates, not as the difference of two chunk-long sums, so it is as accurate as its own size
+      f32x4 sx[4];   // forward: exclusive suffix inside the lane
+      if constexpr (!REV) {
+        sx[3] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 2; u >= 0; --u) sx[u] = sx[u + 1] + s.rg[u + 1];
+      }
 #pragma unroll
       for (int u = 1; u < 4; ++u) s.rg[u] += s.rg[u - 1];
-      f32x4 excl, tot;
+      f32x4 excl, tot, esx;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float own = s.rg[3][e];
         excl[e] = row_scan16(own) - own;
         tot[e] = row_sum16(own);
+        if constexpr (!REV) esx[e] = dpp_row<0x101>(row_suffix16(own));   // later lanes of the row
       }
+      // a column is strong when its chunk total is below -kStrongGate: there the chunk kernels
+      // take the sub-block path, and the backward stores the state gradient undecayed (e^Gamma
+      // may underflow); the one comparison below decides both, so they always agree
+      bool strongc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) strongc[e] = tot[e] < -kStrongGate;
       if (tg == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sDec[16 * w + 4 * cg + e] = __expf(tot[e]);
+        for (int e = 0; e < 4; ++e) {
+          const float dec = __expf(tot[e]);
+          sDec[16 * w + 4 * cg + e] = dec;
+          if constexpr (REV) sFac[16 * w + 4 * cg + e] = strongc[e] ? 1.f : dec;
+        }
+      if constexpr (!REDUCE) {
+        if (a.strong != nullptr) {
+          // 16 columns of this wave: bit 4*cg + e (every lane of a row holds the row's totals)
+          unsigned m16 = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned long long bal = __ballot(strongc[e]);
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) m16 |= (unsigned)((bal >> (16 * g4)) & 1ull) << (4 * g4 + e);
+          }
+          if (lane == 0) a.strong[((size_t)bh * NC + c) * (D / 16) + it * 4 + w] = (uint16_t)m16;
+        }
+      }
       if constexpr (REDUCE) gsum += tot;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float b = s.rg[u][e] + excl[e];
-          const float c = REV ? b : tot[e] - b;
+          const float ex = REV ? s.rg[u][e] + excl[e] : sx[u][e] + esx[e];
           const bool okr = c * CHUNK + 4 * tg + u < L;
           const float av = okr ? (float)s.ra[u][e] : (FEAT ? -INFINITY : 0.f);
-          x[e] = FEAT ? __expf(av + c) : av * __expf(c);
+          x[e] = FEAT ? __expf(av + ex) : av * __expf(ex);
         }
         st4(sA + (4 * tg + u) * LDA + 16 * w + 4 * cg, x[0], x[1], x[2], x[3]);
       }
@@ -312,15 +343,20 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
           stg4(a.bnd + (((size_t)bh * NC + c) * NTI + jt) * D + i0 + 16 * w + 4 * kg, rsum[0], rsum[1], rsum[2],
                rsum[3]);
       }
-      f32x4 dec;
+      f32x4 dec, fac;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dec[e] = sDec[16 * w + 4 * kg + e];
+      for (int e = 0; e < 4; ++e) {
+        dec[e] = sDec[16 * w + 4 * kg + e];
+        fac[e] = sFac[16 * w + 4 * kg + e];
+      }
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
+        if constexpr (!REDUCE) {
+          // dS' = e^Gamma dS, or dS itself in the strong columns (fac = 1)
+          const f32x4 y = acc[jb] * fac;
+          stg4(out + ((size_t)c * D + j0 + 16 * jb + r) * D + i0 + 16 * w + 4 * kg, y[0], y[1], y[2], y[3]);
+        }
         acc[jb] *= dec;
-        if constexpr (!REDUCE)
-          stg4(out + ((size_t)c * D + j0 + 16 * jb + r) * D + i0 + 16 * w + 4 * kg, acc[jb][0], acc[jb][1],
-               acc[jb][2], acc[jb][3]);
       }
       // + (q e^b)^T dO
 #pragma unroll

@@ -43,11 +43,16 @@
  *   at most three chunks); decode: 1 <= W <= 8192.  0 <= M <= 16; B, H >= 1;
  *   L >= 0 (L = 0 writes only the zero state / zero meta gradients).
  *   Anything else returns LIZARD_EUNSUPPORTED.
- * - Numerical domain: within one chunk the cumulative log-gate of every key
- *   dimension must stay above -80, so that the factor exp(-b) of the
- *   chunk-local prefix b stays finite in fp32; the library does not scan the
- *   gates (that would need a synchronisation).  Gates of the form
- *   logsigmoid(x)/16 stay above -5 per chunk.
+ * - Numerical domain: every finite log-gate g <= 0, per token and key
+ *   dimension (English page §2.C: the gate handled in log space keeps gated
+ *   attention exact in low precision).  Inside a chunk the gate is folded into
+ *   q and k relative to the chunk start while every key dimension's chunk
+ *   total stays at or above -64; a chunk with a stronger gate (the pages' own
+ *   sigmoid gate, g = log sigmoid(z), sums to about -50 .. -200 per 64 tokens)
+ *   is computed by 16-token blocks with the gate folded relative to each
+ *   block's end, and a block that itself decays by more than that range is
+ *   formed exactly pair by pair.  The state sweep decides per chunk on the
+ *   device; no host scan, no synchronisation.
  */
 #ifndef LIZARD_ATTN_H
 #define LIZARD_ATTN_H
@@ -110,14 +115,18 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op);
  *                     is NULL at least lizard_attn_workspace_bytes(s, LIZARD_OP_FWD)
  *                     bytes (the chunk states go there); when chunk_states is
  *                     given, that figure less B*H*ceil(L/chunk)*d_k*d_v*esz
- *                     bytes (esz = 2 for bf16, 4 for fp32), which is zero unless
- *                     B*H is small enough for the state sweep to run in
- *                     sequence segments; NULL when zero bytes are needed
+ *                     bytes (esz = 2 for bf16, 4 for fp32): the per-chunk
+ *                     strong-gate masks and dispatch list (about 24 bytes per
+ *                     (b, h, chunk)) and, when B*H is small enough for the state
+ *                     sweep to run in sequence segments, its segment buffers;
+ *                     may be NULL only for L = 0
  * NULL optional outputs are not written.  Launches on `stream`: the state
  * sweep over chunks (when B*H*(d/64)^2 < 512 and L spans at least 32
  * chunks, in segments of the sequence: a reduce pass per segment, a scan
  * over segments, then the sweep of every segment from its entering state),
- * then one workgroup per (batch, head, chunk). */
+ * then one workgroup per (batch, head, chunk), then a persistent launch that
+ * computes the chunks the sweep flagged as strong-gated (it ends at once when
+ * there are none). */
 lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
                                 const void* q, const void* k, const void* v, const float* g,
                                 const void* meta_k, const void* meta_v,

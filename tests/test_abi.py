@@ -119,7 +119,10 @@ def test_decode_validation(lib):
 def test_fwd_needs_workspace_without_chunk_states(lib):
     s = shape()
     need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)
-    assert need == 1 * 2 * 2 * 128 * 128 * 2          # B*H*chunks*d*d bf16 chunk states
+    n = 1 * 2 * 2                                     # B*H*chunks
+    up = lambda x: (x + 255) // 256 * 256
+    dispatch = 256 + up(4 * n) + up(2 * n * (128 // 16))   # strong-gate counter, list, column masks
+    assert need == n * 128 * 128 * 2 + dispatch       # + the bf16 chunk states
     def call(ws, ws_bytes):
         return lib.lizard_attn_fwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None,
                                    None, None, None, ws, ws_bytes, None)
