@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblizard_attn.so")
 
 LIZARD_FP32, LIZARD_BF16 = 0, 1
-OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE, OP_DISTILL, OP_FEATURE_BWD = 0, 1, 2, 3, 4, 5
+OP_FWD, OP_BWD, OP_DECODE, OP_FWD_CONTINUE, OP_DISTILL, OP_FEATURE_BWD, OP_BWD_RECOMPUTE = 0, 1, 2, 3, 4, 5, 6
 GATE_PER_DIM, GATE_SCALAR = 0, 1
 SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "lizard_attn_fwd_continue",
            "lizard_attn_workspace_bytes", "lizard_attn_status_string", "lizard_gate_proj_fwd",
@@ -198,27 +198,31 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
 BWD_STAGES = 3
 
 
-def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *, window: int,
+def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse=None, o_swa=None, chunk_states=None, *, window: int,
                     scale: float | None = None, mix: float = 1.0, chunk: int = 64,
                     stage_events=None) -> dict:
-    """Backward pass from the saved forward tensors; returns dq, dk, dv, dg, dmeta_k, dmeta_v.
+    """Backward pass; returns dq, dk, dv, dg, dmeta_k, dmeta_v.  ``lse``, ``o_swa`` and
+    ``chunk_states`` are the forward's saved tensors; when any is None the library
+    recomputes them (a forward's time, a larger workspace).
 
     ``stage_events``: optional sequence of BWD_STAGES + 1 raw hipEvent_t handles
     (ints) recorded around the backward's kernels (profiling hook)."""
     lib = load()
     dt, dev = q.dtype, q.device
-    for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO), ("o_swa", o_swa),
-                 ("chunk_states", chunk_states)):
+    for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
         _need(t, n, dt, dev)
+    _opt(o_swa, "o_swa", dt, dev)
+    _opt(chunk_states, "chunk_states", dt, dev)
     _need(g, "g", torch.float32, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _opt(lse, "lse", torch.float32, dev)
     _opt(meta_k, "meta_k", dt, dev)
     _opt(meta_v, "meta_v", dt, dev)
     B, H, L, d = q.shape
     M = 0 if meta_k is None else meta_k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, _gate_mode(g, q))
-    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD)
+    recompute = lse is None or o_swa is None or chunk_states is None
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD_RECOMPUTE if recompute else OP_BWD)
     ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dg": torch.empty_like(g)}
@@ -361,24 +365,28 @@ def lizard_attn_fwd_feat(q, k, v, lq, lk, g, meta_k, meta_v=None, *, window: int
     return out
 
 
-def lizard_attn_bwd_feat(q, k, v, lq, lk, g, meta_k, meta_v, dO, lse, o_swa, chunk_states, *, window: int,
-                         scale: float | None = None, mix: float = 1.0, chunk: int = 64,
+def lizard_attn_bwd_feat(q, k, v, lq, lk, g, meta_k, meta_v, dO, lse=None, o_swa=None, chunk_states=None, *,
+                         window: int, scale: float | None = None, mix: float = 1.0, chunk: int = 64,
                          stage_events=None) -> dict:
     """Backward of lizard_attn_fwd_feat: dq, dk (window branch), dv, dlq, dlk (GLA log features),
-    dg, dmeta_k, dmeta_v."""
+    dg, dmeta_k, dmeta_v; the saved forward tensors may be None (recomputed)."""
     lib = load()
     dt, dev = q.dtype, q.device
-    for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO), ("o_swa", o_swa), ("chunk_states", chunk_states)):
+    for n, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
         _need(t, n, dt, dev)
-    for n, t in (("lq", lq), ("lk", lk), ("g", g), ("lse", lse)):
+    _opt(o_swa, "o_swa", dt, dev)
+    _opt(chunk_states, "chunk_states", dt, dev)
+    for n, t in (("lq", lq), ("lk", lk), ("g", g)):
         _need(t, n, torch.float32, dev)
+    _opt(lse, "lse", torch.float32, dev)
     _opt(meta_k, "meta_k", dt, dev)
     _opt(meta_v, "meta_v", dt, dev)
     B, H, L, d = q.shape
     M = 0 if meta_k is None else meta_k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, GATE_PER_DIM)
-    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD)
+    recompute = lse is None or o_swa is None or chunk_states is None
+    ws_bytes = lib.lizard_attn_workspace_bytes(ctypes.byref(s), OP_BWD_RECOMPUTE if recompute else OP_BWD)
     ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dlq": torch.empty_like(lq), "dlk": torch.empty_like(lk), "dg": torch.empty_like(g)}

@@ -67,5 +67,43 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """Path of the toolchain's AddressSanitizer runtime (to preload into a host process)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found in the ROCm toolchain")
+    return path
+
+
+def build_host_sanitized() -> str:
+    """A variant of the library whose host code for the C ABI (validation and dispatch,
+    lz_api.cpp) is built with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    regular kernel objects (device code is not instrumented).  For CPU-side testing only: load it
+    into a process that preloads asan_runtime().  Returns the path of the shared library."""
+    objdir = os.path.join(ROOT, "_build")
+    objs = [os.path.join(objdir, os.path.basename(f) + ".o") for f in sources() if f.endswith(".hip")]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    sandir = os.path.join(objdir, "san")
+    os.makedirs(sandir, exist_ok=True)
+    api = os.path.join(CSRC, "lz_api.cpp")
+    obj = os.path.join(sandir, "lz_api.o")
+    host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-x", "hip",
+                        "-I", os.path.join(ROOT, "include"), *host_san, "-c", api, "-o", obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized build of lz_api.cpp failed:\n" + r.stdout + r.stderr)
+    lib = os.path.join(sandir, "liblizard_attn_san.so")
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan",
+                        "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-o", lib, obj, *objs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stdout + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

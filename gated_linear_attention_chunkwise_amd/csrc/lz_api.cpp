@@ -6,6 +6,7 @@
 // synchronisation or allocation.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/lizard_attn.h"
 #include "lz_kernels.hpp"
@@ -113,13 +114,16 @@ lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
   if ((meta_v == nullptr) != (dmeta_v == nullptr)) return LIZARD_EINVAL;
   if (s->M > 0 && (meta_k == nullptr || dmeta_k == nullptr)) return LIZARD_EINVAL;
   if (s->L > 0)
-    st = check_ptrs({q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg},
-                    {meta_k, meta_v, dmeta_k, dmeta_v, workspace, lq, lk, dlq, dlk});
+    st = check_ptrs({q, k, v, g, dO, dq, dk, dv, dg},
+                    {lse, o_swa, chunk_states, meta_k, meta_v, dmeta_k, dmeta_v, workspace, lq, lk, dlq, dlk});
   else   // L = 0: only the meta gradients (zero) are written
     st = check_ptrs({}, {q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg,
                          meta_k, meta_v, dmeta_k, dmeta_v, workspace, lq, lk, dlq, dlk});
   if (st != LIZARD_OK) return st;
-  const size_t need = lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
+  // without the saved forward tensors the workspace also holds their recomputation
+  const bool recompute = s->L > 0 && (lse == nullptr || o_swa == nullptr || chunk_states == nullptr);
+  const size_t need = recompute ? lz::bwd_recompute_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype)
+                                : lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   lz::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g;
@@ -179,7 +183,11 @@ lizard_status_t decode_impl(const lizard_attn_shape_t* s, const void* q, const v
 extern "C" {
 
 const char* lizard_attn_status_string(lizard_status_t st) {
-  switch (st) {
+  // a C caller may pass any int: read it as one (an out-of-range enum value is undefined in C++)
+  static_assert(sizeof(lizard_status_t) == sizeof(int), "status codes travel as int");
+  int code;
+  memcpy(&code, &st, sizeof(code));
+  switch (code) {
     case LIZARD_OK: return "ok";
     case LIZARD_EINVAL: return "invalid argument (null pointer, bad size or inconsistent optional pair)";
     case LIZARD_EUNSUPPORTED: return "unsupported size, dtype or parameter";
@@ -192,13 +200,15 @@ const char* lizard_attn_status_string(lizard_status_t st) {
 
 size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
   if (op != LIZARD_OP_FWD && op != LIZARD_OP_BWD && op != LIZARD_OP_DECODE && op != LIZARD_OP_FWD_CONTINUE &&
-      op != LIZARD_OP_DISTILL && op != LIZARD_OP_FEATURE_BWD)
+      op != LIZARD_OP_DISTILL && op != LIZARD_OP_FEATURE_BWD && op != LIZARD_OP_BWD_RECOMPUTE)
     return 0;
-  const bool seq_op = op == LIZARD_OP_DISTILL || op == LIZARD_OP_FEATURE_BWD;
+  const bool seq_op = op == LIZARD_OP_DISTILL || op == LIZARD_OP_FEATURE_BWD || op == LIZARD_OP_BWD_RECOMPUTE;
   if (check_shape(s, seq_op ? LIZARD_OP_FWD : op) != LIZARD_OK) return 0;
   if (op == LIZARD_OP_DISTILL) return lz::distill_workspace_bytes(s->B, s->H, s->L);
   if (op == LIZARD_OP_FEATURE_BWD) return s->L > 0 ? lz::feature_workspace_bytes(s->B, s->H, s->L, s->d_k) : 0;
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
+  if (op == LIZARD_OP_BWD_RECOMPUTE)
+    return lz::bwd_recompute_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (op == LIZARD_OP_FWD || op == LIZARD_OP_FWD_CONTINUE)
     return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
   return lz::decode_workspace_bytes(s->B, s->H, s->d_k);

@@ -50,6 +50,9 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
   size_t delta, dS, bnd, dmeta, seg, disp, total;
+  // recompute (lse, o_swa or chunk_states not given): the forward's workspace (its chunk
+  // states at its end), lse and o_swa, after `total`
+  size_t rc_fwd, rc_lse, rc_oswa, rc_total;
 };
 
 WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
@@ -70,6 +73,13 @@ WsLayout ws_layout(int B, int H, int L, int M, int D, int dtype) {
   w.disp = off;  // strong-gate dispatch: masks, list
   off += dispatch_bytes(B, H, L, D);
   w.total = off;
+  w.rc_fwd = off;
+  off += round_up(fwd_workspace_bytes(B, H, L, D, dtype), 256);
+  w.rc_lse = off;
+  off += round_up(sizeof(float) * (size_t)B * H * L, 256);
+  w.rc_oswa = off;
+  off += round_up(esz * (size_t)B * H * L * D, 256);
+  w.rc_total = off;
   return w;
 }
 
@@ -1188,6 +1198,25 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     if (a.stage_events != nullptr) (void)hipEventRecord(a.stage_events[i], st);
   };
   mark(0);
+  if (a.lse == nullptr || a.o_swa == nullptr || a.chunk_states == nullptr) {
+    // the saved forward tensors were not kept: the forward kernels recompute all three into the
+    // workspace (o itself is not written)
+    FwdArgs f{};
+    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.meta_k = a.meta_k; f.meta_v = a.meta_v;
+    f.o = nullptr;
+    f.lse = reinterpret_cast<float*>(ws + wl.rc_lse);
+    f.o_swa = ws + wl.rc_oswa;
+    f.chunk_states = nullptr;
+    f.state_out = nullptr;
+    f.workspace = ws + wl.rc_fwd;
+    f.B = a.B; f.H = a.H; f.L = a.L; f.W = a.W; f.M = a.M;
+    f.scale = a.scale; f.mix = a.mix; f.gate = a.gate;
+    f.lq = a.lq; f.lk = a.lk;
+    if ((e = launch_fwd(f, std::is_same<T, bf16_t>::value ? 1 : 0, D, st)) != hipSuccess) return e;
+    a.lse = f.lse;
+    a.o_swa = f.o_swa;
+    a.chunk_states = ws + wl.rc_fwd + fwd_aux_bytes(a.B, a.H, a.L, D);
+  }
   // the state-gradient sweep also forms the window row dots delta_t from the dO rows it streams
   {
     const bool feat = a.lq != nullptr;
@@ -1241,6 +1270,10 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
 
 size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype) {
   return ws_layout(B, H, L, M, D, dtype).total;
+}
+
+size_t bwd_recompute_workspace_bytes(int B, int H, int L, int M, int D, int dtype) {
+  return L > 0 ? ws_layout(B, H, L, M, D, dtype).rc_total : 0;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int D, hipStream_t st) {

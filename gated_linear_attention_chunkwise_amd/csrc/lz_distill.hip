@@ -330,13 +330,10 @@ hipError_t launch_distill_t(const DistillArgs& a, hipStream_t st) {
   using LY = TeLayout<T, D>;
   const int nwg = a.B * a.H * ((a.L + TQ - 1) / TQ);
   if (a.L > 0) {
-    static bool attr = false;   // idempotent; a race only repeats the same call
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(teacher_mse_kernel<T, D>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::bytes);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
+    // set on every launch: idempotent and cheap, and no process-wide flag to race on
+    hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(teacher_mse_kernel<T, D>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::bytes);
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL((teacher_mse_kernel<T, D>), dim3(nwg), dim3(NTHR_TE), LY::bytes, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

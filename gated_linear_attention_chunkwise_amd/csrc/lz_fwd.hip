@@ -573,7 +573,7 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
     }
   }
   mfma_drain();
-  if (qvalid) {
+  if (qvalid && a.o != nullptr) {   // (no o when the backward recomputes lse and o_swa)
     T* orow = reinterpret_cast<T*>(a.o) + hoff + (size_t)tq * D;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) stg4(orow + 16 * jb + 4 * kg, OW[jb][0], OW[jb][1], OW[jb][2], OW[jb][3]);

@@ -354,13 +354,10 @@ hipError_t run_gemm(const GemmArgs& a, hipStream_t st) {
   constexpr size_t lds = GemmShape<T, AKC, BKC, EPI, BM, BN, BK, WGM, WGN>::lds_bytes;
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = gemm_kernel<T, AKC, BKC, EPI, BM, BN, BK, WGM, WGN>;
-  static bool attr = false;   // idempotent; a race only repeats the same call
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // set on every launch: idempotent and cheap, and no process-wide flag to race on
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3(tiles, a.ksplit), dim3(64 * WGM * WGN), lds, st, a);
   return hipGetLastError();

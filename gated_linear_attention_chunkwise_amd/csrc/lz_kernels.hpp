@@ -166,7 +166,9 @@ size_t gate_bwd_workspace_bytes(int B, int H, int L, int dk, int sg, int d_model
 size_t feature_workspace_bytes(int B, int H, int L, int D);
 // Workspace bytes needed by launch_distill: one fp32 partial per workgroup.
 size_t distill_workspace_bytes(int B, int H, int L);
-// Workspace bytes needed by launch_bwd.
+// Workspace bytes needed by launch_bwd when lse, o_swa and chunk_states are given, and when
+// any of them is NULL (the forward kernels then recompute all three into the workspace).
 size_t bwd_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
+size_t bwd_recompute_workspace_bytes(int B, int H, int L, int M, int D, int dtype);
 
 }  // namespace lz

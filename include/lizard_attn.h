@@ -96,7 +96,8 @@ typedef struct {
 } lizard_attn_shape_t;
 
 enum { LIZARD_OP_FWD = 0, LIZARD_OP_BWD = 1, LIZARD_OP_DECODE = 2, LIZARD_OP_FWD_CONTINUE = 3,
-       LIZARD_OP_DISTILL = 4, LIZARD_OP_FEATURE_BWD = 5 };
+       LIZARD_OP_DISTILL = 4, LIZARD_OP_FEATURE_BWD = 5,
+       LIZARD_OP_BWD_RECOMPUTE = 6 /* the backward without its saved forward tensors */ };
 
 /* Bytes of device workspace that `op` needs for shape `s` (0 when none, or
  * when `s` is invalid).  Pass at least this many bytes to the call. */
@@ -136,20 +137,29 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
 
 /* Backward pass: exact gradients of sum(dO * o) (the pages give no backward;
  * the formulas are the derivative of the forward above).
- *   lse, o_swa, chunk_states   required, as written by lizard_attn_fwd on the
- *                              same inputs
+ *   lse, o_swa, chunk_states   optional: as written by lizard_attn_fwd on the
+ *                              same inputs; when any of them is NULL, the forward
+ *                              kernels recompute all three into the workspace
+ *                              first (o is not written), which trades the memory
+ *                              of keeping them between the passes (about
+ *                              B*H*L*(4 + 2*d) + B*H*ceil(L/64)*d*d*2 bytes in
+ *                              bf16) for a forward's time
  *   dq, dk, dv                 written (dtype)
  *   dg                         written, fp32 [B,H,L,d_k]
  *   dmeta_k                    written, fp32 [H,M,d_k] (summed over batch)
  *   dmeta_v                    fp32 [H,M,d_v]; must be NULL iff meta_v is NULL
  *   workspace                  lizard_attn_workspace_bytes(s, LIZARD_OP_BWD) bytes,
- *                              caller-owned device memory, clobbered by the call
+ *                              or (LIZARD_OP_BWD_RECOMPUTE) bytes when any saved
+ *                              tensor is NULL; caller-owned device memory,
+ *                              clobbered by the call
  *   stage_events          opt  profiling hook: NULL, or LIZARD_BWD_STAGES + 1
  *                              caller-created events that are recorded on
  *                              `stream` before the first, between consecutive
  *                              and after the last of the backward's kernels
  *                              (state-gradient sweep with the window row
- *                              dots, chunk gradients, meta reduction; a stage
+ *                              dots, preceded by the recomputed forward when a
+ *                              saved tensor is NULL; chunk gradients; meta
+ *                              reduction; a stage
  *                              with nothing to do still gets its event).  For
  *                              L = 0 they are not recorded. */
 #define LIZARD_BWD_STAGES 3

@@ -22,9 +22,11 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(pkg._lib.LIB_PATH):
+    # LIZARD_ATTN_LIB: another build of the same library (the host-sanitized variant)
+    path = os.environ.get("LIZARD_ATTN_LIB", pkg._lib.LIB_PATH)
+    if not os.path.exists(path):
         pytest.skip("library not built")
-    return load()
+    return load(path)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -100,6 +102,27 @@ def test_bwd_validation(lib):
         assert call(ws_bytes=need - 1) == EWORKSPACE
 
 
+def test_bwd_saved_tensors_optional(lib):
+    """lse, o_swa and chunk_states may be NULL: the backward then recomputes them, in a larger
+    workspace (the forward's workspace with its chunk states, lse and o_swa on top)."""
+    s = shape()
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 1)
+    rc = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 6)
+    up = lambda x: (x + 255) // 256 * 256
+    fwd = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)
+    B, H, L, d = 1, 2, 128, 128
+    assert rc == need + up(fwd) + up(4 * B * H * L) + up(2 * B * H * L * d)
+    def call(lse=GOOD, o_swa=GOOD, cs=GOOD, ws=GOOD, ws_bytes=need):
+        return lib.lizard_attn_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD,
+                                   lse, o_swa, cs, GOOD, GOOD, GOOD, GOOD, GOOD, None, ws,
+                                   ws_bytes, None, None)
+    for kw in (dict(lse=None), dict(o_swa=None), dict(cs=None), dict(lse=None, o_swa=None, cs=None)):
+        assert call(**kw) == EWORKSPACE, kw                  # the plain backward's workspace is too small
+        assert call(ws=BAD, ws_bytes=rc, **kw) == EALIGN, kw
+    assert call(lse=BAD) == EALIGN
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 6) == 0
+
+
 def test_decode_validation(lib):
     s = shape(L=0)
     def call(state=GOOD, pos=GOOD, s_=s, ws=GOOD, ws_bytes=1 << 40):
@@ -158,7 +181,7 @@ def test_workspace_query(lib):
     assert lib.lizard_attn_workspace_bytes(None, 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(d_k=96, d_v=96)), 1) == 0
     assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape(L=0)), 0) == 0
-    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 6) == 0       # unknown op
+    assert lib.lizard_attn_workspace_bytes(ctypes.byref(shape()), 7) == 0       # unknown op
 
 
 def test_gate_proj_validation(lib):
@@ -267,3 +290,27 @@ def test_feature_carry_entry_points_validation(lib):
     assert dec(lk=None) == EINVAL
     assert dec(lk=BAD) == EALIGN
     assert dec(s=shape(L=0, gate=1)) == EUNSUPPORTED
+
+
+def _device_visible():
+    # (counting devices through torch does not initialise the GPU on this image)
+    import torch
+    return os.path.exists("/dev/kfd") or torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_device_visible(), reason="needs a machine without a GPU: the call below passes "
+                    "validation with placeholder pointers and must fail at its launch")
+def test_launch_failure_returns_ehip(lib):
+    """A call that passes validation but whose launch fails (here: no device at all) returns
+    LIZARD_EHIP instead of succeeding or crashing, for the forward, backward and decode step."""
+    s = shape()
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)
+    assert lib.lizard_attn_fwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None, None, None,
+                               None, GOOD, need, None) == EHIP
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 1)
+    assert lib.lizard_attn_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD,
+                               GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, need, None, None) == EHIP
+    d = shape(L=0)
+    need = lib.lizard_attn_workspace_bytes(ctypes.byref(d), 2)
+    assert lib.lizard_attn_decode_step(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD,
+                                       GOOD, GOOD, GOOD, need, None) == EHIP

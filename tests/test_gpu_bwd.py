@@ -145,3 +145,33 @@ def test_forward_backward_bit_reproducible(dtname, D, with_mv):
     for n in outs[0]:
         for o in outs[1:]:
             assert torch.equal(outs[0][n], o[n]), n
+
+
+@pytest.mark.parametrize("drop", ["all", "lse", "o_swa", "chunk_states"])
+@pytest.mark.parametrize("dtname,D,L,x_mean,gate_div", [("fp32", 64, 200, 0.0, 16.0), ("bf16", 128, 256, 0.0, 16.0),
+                                                        ("bf16", 64, 4101, 0.0, 16.0),
+                                                        ("bf16", 128, 200, -1.0, 1.0)])
+def test_backward_recomputes_omitted_saved_tensors(drop, dtname, D, L, x_mean, gate_div):
+    """Without lse, o_swa or chunk_states the backward recomputes them (the forward's kernels into
+    its workspace): the gradients equal those from the saved tensors bit for bit, and the oracle's.
+    Covers the segmented sweep (B*H = 2, L = 4101) and strong gates (tau = 1, x ~ N(-1, 1))."""
+    dt = tdtype(dtname)
+    x = make_small(1, 2, L, D, 4, seed=L + D, bf16=(dtname == "bf16"), x_mean=x_mean, gate_div=gate_div)
+    scale = 1.0 / math.sqrt(D)
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v", "dO", "meta_k")}
+    g = dev(x["g"], torch.float32)
+    f = lizard_attn_fwd(T["q"], T["k"], T["v"], g, T["meta_k"], None, window=64, scale=scale, want_lse=True,
+                        want_o_swa=True, want_chunk_states=True)
+    saved = {"lse": f["lse"], "o_swa": f["o_swa"], "chunk_states": f["chunk_states"]}
+    full = lizard_attn_bwd(T["q"], T["k"], T["v"], g, T["meta_k"], None, T["dO"], window=64, scale=scale, **saved)
+    if drop == "all":
+        saved = {}
+    else:
+        saved.pop(drop)
+    part = lizard_attn_bwd(T["q"], T["k"], T["v"], g, T["meta_k"], None, T["dO"], window=64, scale=scale, **saved)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dg", "dmeta_k"):
+        assert torch.equal(part[n], full[n]), (drop, n)
+    if L <= 256:
+        ref = orc.hybrid_backward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, x["dO"], window=64, scale=scale)
+        check(part, ref, dtname)

@@ -109,3 +109,40 @@ def test_decode_caller_workspace_matches_default():
         runs.append((torch.stack(outs), state.clone(), rk.clone(), rv.clone(), pos.clone()))
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtname,D", [("fp32", 64), ("bf16", 128)])
+def test_decode_checkpoint_restore(dtname, D):
+    """The decode carry (state, ring, pos) is the whole of a sequence's memory: copied out after
+    some steps (a checkpoint, here through host memory) and copied into fresh buffers, it continues
+    bit for bit like the uninterrupted run, for sequences at different positions."""
+    B, H, W, M, pre, n1, n2 = 3, 2, 16, 4, 37, 9, 14
+    x = make_small(B, H, pre + n1 + n2, D, M, seed=91, bf16=(dtname == "bf16"), with_grad=False)
+    dt = tdtype(dtname)
+    scale = 1.0 / math.sqrt(D)
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk = dev(x["meta_k"], dt)
+    state = torch.zeros(B, H, D, D, device="cuda", dtype=torch.float32)
+    rk = torch.zeros(B, H, W, D, device="cuda", dtype=dt)
+    rv = torch.zeros_like(rk)
+    pos = torch.zeros(B, device="cuda", dtype=torch.int32)
+    step = lambda t, st, a, b, p: lizard_attn_decode_step(*(T[n][:, :, t].contiguous() for n in "qkvg"), mk, None,
+                                                          st, a, b, p, window=W, scale=scale)
+    for t in range(pre + n1):
+        step(t, state, rk, rv, pos)
+    torch.cuda.synchronize()
+    ckpt = [a.cpu() for a in (state, rk, rv, pos)]            # the checkpoint
+    ref = [step(t, state, rk, rv, pos) for t in range(pre + n1, pre + n1 + n2)]
+    torch.cuda.synchronize()
+    s2, rk2, rv2, pos2 = (a.to("cuda") for a in ckpt)          # restored into fresh buffers
+    got = [step(t, s2, rk2, rv2, pos2) for t in range(pre + n1, pre + n1 + n2)]
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    for a, b in zip((s2, rk2, rv2, pos2), (state, rk, rv, pos)):
+        assert torch.equal(a, b)
+    # and the continued run still matches the oracle's whole-sequence forward
+    o = host(torch.stack(got, 2))
+    r = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=W, scale=scale)
+    assert rel_l2(o, r["o"][:, :, pre + n1:]) <= TOL[dtname]

@@ -99,3 +99,33 @@ def test_stage1_train_shape_sampled():
     e_dO = rel_l2(host(ls["dO"][b, h])[rows], ref)
     print(f"train shape: loss vs property {e_loss:.2e}, dO rows {e_dO:.2e}", flush=True)
     assert e_loss <= TOL["bf16"] and e_dO <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtname,B,H,L,D", [("fp32", 1, 2, 200, 64), ("bf16", 2, 2, 300, 128), ("bf16", 1, 3, 129, 64)])
+@pytest.mark.parametrize("law", ["independent", "near_teacher"])
+def test_distill_mse_alone(dtname, B, H, L, D, law):
+    """lizard_distill_mse by itself, on one o_S given to both sides (rounded to the operand dtype
+    first): the loss and dO against the oracle's teacher attention and MSE, at the plain bound.
+    o_S is either independent of the teacher (same size) or the oracle's teacher output with a
+    30 % relative perturbation (the student near the teacher)."""
+    t = make_small(B, H, L, D, 0, seed=L + D, bf16=(dtname == "bf16"), with_grad=False)
+    scale = 1.0 / math.sqrt(D)
+    o_t = dst.teacher_attention(t["q"], t["k"], t["v"], scale=scale)
+    rng = np.random.default_rng(L)
+    rms = float(np.sqrt(np.mean(o_t ** 2)))
+    if law == "independent":
+        o_s = rng.standard_normal(o_t.shape) * rms
+    else:
+        o_s = o_t * (1.0 + 0.3 * rng.standard_normal(o_t.shape))
+    o_s = o_s.astype(np.float32)
+    if dtname == "bf16":
+        from gated_linear_attention_chunkwise_amd.inputs import round_to_bf16
+        o_s = round_to_bf16(o_s)
+    dt = tdtype(dtname)
+    ls = lizard_distill_mse(dev(t["q"], dt), dev(t["k"], dt), dev(t["v"], dt), dev(o_s, dt), scale=scale)
+    torch.cuda.synchronize()
+    loss, dO = dst.mse_and_grad(o_s, o_t)
+    e_loss = abs(float(ls["loss"]) - loss) / loss
+    e_do = rel_l2(host(ls["dO"]), dO)
+    print(dtname, B, H, L, D, law, f"loss {e_loss:.2e} dO {e_do:.2e}", flush=True)
+    assert e_loss <= TOL[dtname] and e_do <= TOL[dtname]

@@ -116,3 +116,39 @@ def test_scalar_gate_train_8k_full_size_sampled():
     print("train_8k scalar gate head", h, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for n, e in errs.items():
         assert e <= TOL["bf16"], (n, e)
+
+
+@pytest.mark.parametrize("dtname,D", [("fp32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gate_div,x_mean", [(16.0, 0.0), (1.0, -1.0)])
+def test_equal_per_dim_gates_equal_the_scalar_gate(dtname, D, gate_div, x_mean):
+    """Per-key-dimension gates whose entries are all equal are the scalar gate: the same outputs
+    and q/k/v/meta gradients, and per-dimension gate gradients that sum to the scalar one (slow
+    recipe gates, and tau = 1 gates that take the strong-gate path)."""
+    from gated_linear_attention_chunkwise_amd import lizard_attn_bwd as bwd, lizard_attn_fwd as fwd
+    B, H, L, W = 2, 2, 200, 64
+    x = make_small(B, H, L, D, 4, seed=5, bf16=(dtname == "bf16"))
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((B, H, L)) + x_mean
+    gs = ((np.minimum(z, 0.0) - np.log1p(np.exp(-np.abs(z)))) / gate_div).astype(np.float32)
+    gd = np.ascontiguousarray(np.repeat(gs[..., None], D, axis=-1))
+    dt = tdtype(dtname)
+    scale = 1.0 / math.sqrt(D)
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v", "dO", "meta_k")}
+    res = []
+    for g in (dev(gs, torch.float32), dev(gd, torch.float32)):
+        f = fwd(T["q"], T["k"], T["v"], g, T["meta_k"], None, window=W, scale=scale, want_lse=True,
+                want_o_swa=True, want_chunk_states=True, want_state=True)
+        b = bwd(T["q"], T["k"], T["v"], g, T["meta_k"], None, T["dO"], f["lse"], f["o_swa"], f["chunk_states"],
+                window=W, scale=scale)
+        res.append((f, b))
+    torch.cuda.synchronize()
+    (fs, bs), (fd, bd) = res
+    for n in ("o", "o_swa", "lse", "state"):
+        e = rel_l2(host(fd[n]), host(fs[n]))
+        assert e <= 1e-6, (n, e)
+    for n in ("dq", "dk", "dv", "dmeta_k"):
+        e = rel_l2(host(bd[n]), host(bs[n]))
+        assert e <= 1e-6, (n, e)
+    e = rel_l2(host(bd["dg"]).sum(-1), host(bs["dg"]))
+    print(dtname, D, gate_div, x_mean, f"dg(sum over dims) vs scalar {e:.2e}", flush=True)
+    assert e <= TOL[dtname]
