@@ -24,7 +24,7 @@ SYMBOLS = ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_decode_step", "liz
            "lizard_attn_workspace_bytes", "lizard_attn_status_string", "lizard_gate_proj_fwd",
            "lizard_gate_proj_bwd", "lizard_gate_proj_workspace_bytes", "lizard_distill_mse",
            "lizard_attn_fwd_feat", "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd",
-           "lizard_attn_fwd_continue_feat", "lizard_attn_decode_step_feat")
+           "lizard_attn_fwd_continue_feat", "lizard_attn_decode_step_feat", "lizard_attn_decode_step_noalloc")
 
 
 class Shape(ctypes.Structure):
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_continue_feat.restype = I32
     lib.lizard_attn_decode_step_feat.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.lizard_attn_decode_step_feat.restype = I32
+    lib.lizard_attn_decode_step_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.lizard_attn_decode_step_noalloc.restype = I32
     lib.lizard_hedgehog_fwd.argtypes = [SP, P, P, P, P]
     lib.lizard_hedgehog_fwd.restype = I32
     lib.lizard_hedgehog_bwd.argtypes = [SP, P, P, P, P, P, P, SZ, P]
@@ -277,6 +279,30 @@ def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, p
                                        _ptr(ring_v), _ptr(pos), _ptr(o), _ptr(workspace),
                                        ws_bytes, _stream(dev)))
     return o
+
+
+def lizard_attn_decode_step_noalloc(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
+                                    window: int, scale: float | None = None, mix: float = 1.0, out):
+    """lizard_attn_decode_step with no workspace: the library keeps the step's partials in its own
+    per-device array (B*H <= 4032 at d = 128).  ``out`` [B,H,d] must be given (this call
+    allocates nothing); returns it.  Calls that overlap on one device race."""
+    lib = load()
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v), ("out", out)):
+        _need(t, n, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    _need(pos, "pos", torch.int32, dev)
+    _opt(meta_k, "meta_k", dt, dev)
+    _opt(meta_v, "meta_v", dt, dev)
+    B, H, d = q.shape
+    M = 0 if meta_k is None else meta_k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    s = make_shape(B, H, 0, d, window, M, scale, mix, dt, gate=_gate_mode(g, q))
+    _check(lib.lizard_attn_decode_step_noalloc(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                               _ptr(meta_k), _ptr(meta_v), _ptr(state), _ptr(ring_k),
+                                               _ptr(ring_v), _ptr(pos), _ptr(out), _stream(dev)))
+    return out
 
 
 def continue_workspace(B: int, H: int, L: int, d: int, dtype, device) -> torch.Tensor:

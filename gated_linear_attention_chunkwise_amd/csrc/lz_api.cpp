@@ -298,6 +298,23 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                      workspace_bytes, stream);
 }
 
+lizard_status_t lizard_attn_decode_step_noalloc(const lizard_attn_shape_t* s,
+                                                const void* q, const void* k, const void* v,
+                                                const float* g, const void* meta_k, const void* meta_v,
+                                                float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                                void* o, hipStream_t stream) {
+  lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
+  if (st != LIZARD_OK) return st;
+  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v});
+  if (st != LIZARD_OK) return st;
+  // the partials live in the library's own per-device array, of a fixed size
+  if (lz::decode_workspace_bytes(s->B, s->H, s->d_k) > lz::kDecodeScratchBytes) return LIZARD_EWORKSPACE;
+  lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
+                   nullptr, s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate, nullptr, nullptr};
+  return lz::launch_decode_noalloc(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+}
+
 lizard_status_t lizard_attn_decode_step_feat(const lizard_attn_shape_t* s,
                                              const void* q, const void* k, const void* v,
                                              const float* lq, const float* lk, const float* g,

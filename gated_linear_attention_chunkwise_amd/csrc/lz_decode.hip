@@ -23,10 +23,20 @@
 //   o = sum_j gla_j + mix * sum_j e^{m_j - m} o_j / sum_j e^{m_j - m} l_j  (m = max_j m_j),
 // and advances pos: the kernel boundary orders the partials' writes and reads, and
 // orders every read of pos (first launch) before its update (second launch).
+#include <atomic>
+#include <mutex>
+
 #include "lz_common.hpp"
 #include "lz_kernels.hpp"
 
 namespace lz {
+
+// The decode step's partials for callers that cannot allocate (lizard_attn_decode_step_noalloc):
+// one array per device, resident until the process ends.  Host code never passes its name to a
+// kernel (on the host it is only a stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
 namespace {
 
 constexpr int NTHR = 256;
@@ -323,6 +333,43 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 
 size_t decode_workspace_bytes(int B, int H, int D) {
   return D == 128 ? DecWs<128>::bytes(B, H) : DecWs<64>::bytes(B, H);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(const DecodeArgs& args, int dtype, int D, hipStream_t st) {
+  if (decode_workspace_bytes(args.B, args.H, D) > kDecodeScratchBytes) return hipErrorInvalidValue;
+  void* p = nullptr;
+  const hipError_t e = scratch_address(&p);
+  if (e != hipSuccess) return e;
+  DecodeArgs a = args;
+  a.o_part = reinterpret_cast<float*>(p);   // every partial is written by the step before it is read
+  return launch_decode(a, dtype, D, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t st) {

@@ -301,6 +301,22 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* lizard_attn_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same step with the same
+ * arguments, minus the workspace.  The per-workgroup partials go to a static array the library
+ * holds on every device it runs on until the process ends (16 MiB), so the call allocates
+ * nothing: B*H*(d/32)*(2d+4)*4 bytes must fit, i.e. B*H <= 4032 at d = 128 and B*H <= 15887 at
+ * d = 64; larger shapes return LIZARD_EWORKSPACE before anything is launched.  The array is
+ * found on the calling thread's current device (the device of `stream`).  Nothing in it has to
+ * start at zero (the step writes every partial before reading it), but all calls on one device
+ * share it: calls that overlap on one device (concurrent streams or threads) race and must be
+ * serialised by the caller. */
+lizard_status_t lizard_attn_decode_step_noalloc(const lizard_attn_shape_t* s,
+                                                const void* q, const void* k, const void* v,
+                                                const float* g, const void* meta_k, const void* meta_v,
+                                                float* state, void* ring_k, void* ring_v, int32_t* pos,
+                                                void* o, hipStream_t stream);
+
 /* Stage-1 attention-approximation loss (English page §2, "Stage 1: Attention
  * Approximation"; French page "Étape 1"): the layer is trained to reproduce
  * the teacher's softmax attention output under a mean squared error.

@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "lizard_attn_status_string", "lizard_gate_proj_fwd", "lizard_gate_proj_bwd",
                           "lizard_gate_proj_workspace_bytes", "lizard_distill_mse", "lizard_attn_fwd_feat",
                           "lizard_attn_bwd_feat", "lizard_hedgehog_fwd", "lizard_hedgehog_bwd",
-                          "lizard_attn_fwd_continue_feat", "lizard_attn_decode_step_feat"}
+                          "lizard_attn_fwd_continue_feat", "lizard_attn_decode_step_feat",
+                          "lizard_attn_decode_step_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(pkg.SYMBOLS) == set(names)
@@ -314,3 +315,18 @@ def test_launch_failure_returns_ehip(lib):
     need = lib.lizard_attn_workspace_bytes(ctypes.byref(d), 2)
     assert lib.lizard_attn_decode_step(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD,
                                        GOOD, GOOD, GOOD, need, None) == EHIP
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode step validates like the plain one and refuses shapes whose
+    partials exceed its built-in 16 MiB (B*H*(d/32)*(2d+4)*4 bytes) before any launch."""
+    def call(s_, state=GOOD, pos=GOOD, o=GOOD):
+        return lib.lizard_attn_decode_step_noalloc(ctypes.byref(s_), GOOD, GOOD, GOOD, GOOD, GOOD, None,
+                                                   state, GOOD, GOOD, pos, o, None)
+    assert call(shape(L=0), state=None) == EINVAL
+    assert call(shape(L=0), o=None) == EINVAL
+    assert call(shape(L=0), pos=BAD) == EALIGN
+    assert call(shape(L=0, W=9000)) == EUNSUPPORTED
+    assert call(shape(L=0, B=64, H=64)) == EWORKSPACE          # 4096 heads at d = 128: 17 MB
+    assert call(shape(L=0, B=4033, H=1)) == EWORKSPACE
+    assert call(shape(L=0, B=15888, H=1, d_k=64, d_v=64)) == EWORKSPACE
