@@ -106,25 +106,68 @@ def load_traffic(kernel):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(x, w, heads):
-    """Time the fp64 oracle (as it stands) on a bounded sample: all batches of
-    `heads` heads at full length, forward + backward, one thread."""
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def _oracle_shard(args):
+    """One (batch, head) shard of the oracle's forward + backward (process-pool worker)."""
+    q, k, v, g, dO, mk, window, scale, dtype = args
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import lizard_oracle as orc
-    hs = {n: x[n][:, :heads].float().cpu().numpy() for n in ("q", "k", "v", "g", "dO")}
-    mk = x["meta_k"][:heads].float().cpu().numpy()
+    dt = np.float64 if dtype == "fp64" else np.float32
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        orc.hybrid_forward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, window=w.W, scale=w.scale)
-        orc.hybrid_backward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, hs["dO"], window=w.W,
-                            scale=w.scale)
-        dt = time.perf_counter() - t0
+        orc.hybrid_forward(q, k, v, g, mk, None, window=window, scale=scale, dtype=dt)
+        orc.hybrid_backward(q, k, v, g, mk, None, dO, window=window, scale=scale, dtype=dt)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(x, w, heads):
+    """Time the oracle as it stands on a bounded sample of the step's work: all batches of `heads`
+    heads at full length, forward + backward, on this host's cores.  Three ways: fp64 (the
+    parity reference) and fp32 in one process with BLAS threads = cores, and fp32 as a process
+    pool over (batch, head) shards with one worker per core (capped by the shards)."""
+    import multiprocessing as mp
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import lizard_oracle as orc
+    cores = len(os.sched_getaffinity(0))
+    hs = {n: x[n][:, :heads].float().cpu().numpy() for n in ("q", "k", "v", "g", "dO")}
+    mk = x["meta_k"][:heads].float().cpu().numpy()
     tokens = w.B * w.L * heads / w.H          # a token is one position through all H heads
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 numpy oracle, forward+backward of {w.B * heads} of {w.B * w.H} "
-                      f"(batch, head) pairs at full L={w.L} ({heads}/{w.H} of the step's work, "
-                      f"{dt:.1f} s), tokens scaled by {heads}/{w.H}"}
+    modes = {}
+    for dtype, dt in (("fp64", np.float64), ("fp32", np.float32)):
+        with threadpool_limits(cores):
+            t0 = time.perf_counter()
+            orc.hybrid_forward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, window=w.W, scale=w.scale, dtype=dt)
+            orc.hybrid_backward(hs["q"], hs["k"], hs["v"], hs["g"], mk, None, hs["dO"], window=w.W,
+                                scale=w.scale, dtype=dt)
+            sec = time.perf_counter() - t0
+        modes[f"{dtype}_one_process"] = {"tokens_per_s": round(tokens / sec, 1), "seconds": round(sec, 2),
+                                         "cores": cores, "blas_threads": cores}
+    shards = [(np.ascontiguousarray(hs["q"][b:b + 1, h:h + 1]), np.ascontiguousarray(hs["k"][b:b + 1, h:h + 1]),
+               np.ascontiguousarray(hs["v"][b:b + 1, h:h + 1]), np.ascontiguousarray(hs["g"][b:b + 1, h:h + 1]),
+               np.ascontiguousarray(hs["dO"][b:b + 1, h:h + 1]), mk[h:h + 1], w.W, w.scale, "fp32")
+              for b in range(w.B) for h in range(heads)]
+    workers = max(1, min(cores, len(shards)))
+    ctx = mp.get_context("spawn")            # fresh interpreters: nothing of this process's GPU state
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_shard, shards[:workers])   # start-up and imports outside the timed region
+        t0 = time.perf_counter()
+        pool.map(_oracle_shard, shards)
+        sec = time.perf_counter() - t0
+    modes["fp32_process_pool"] = {"tokens_per_s": round(tokens / sec, 1), "seconds": round(sec, 2),
+                                  "cores": workers, "workers": workers}
+    best = max(modes, key=lambda m: modes[m]["tokens_per_s"])
+    return {"value": modes[best]["tokens_per_s"], "unit": "tokens/s", "cores": modes[best]["cores"],
+            "kind": "oracle", "mode": best, "modes": modes, "host_cores": cores,
+            "sample": f"numpy oracle, forward+backward of {w.B * heads} of {w.B * w.H} (batch, head) pairs at "
+                      f"full L={w.L} ({heads}/{w.H} of the step's work), tokens scaled by {heads}/{w.H}; "
+                      f"value = the fastest of the three modes"}
 
 
 def bench_train(args, hip, torch, lib):
@@ -155,14 +198,15 @@ def bench_train(args, hip, torch, lib):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # forward = state sweep + output kernel; then the backward's three stages
+    # forward = state sweep + output kernel(s); then the backward's three stages.  Every figure is
+    # the median over the timed steps of HIP-event intervals on the kernels' stream.
     names = ["forward", "sweep_kernel_bwd", "chunk_kernel", "dmeta_kernels"]
     per = {n: [] for n in names}
     for ev in evs:
         for i, n in enumerate(names):
             per[n].append(hip.ms(ev[i], ev[i + 1]))
-    avg = {n: sum(v) / len(v) for n, v in per.items()}
-    ms_step = wall * 1e3 / args.steps
+    avg = {n: median(v) for n, v in per.items()}
+    ms_step = median([hip.ms(ev[0], ev[4]) for ev in evs])
 
     ht = w.B * w.H * w.L
     f_fwd, f_bwd = flops_per_head_token(w.L, w.D, w.chunk, w.W, w.M)
@@ -176,6 +220,7 @@ def bench_train(args, hip, torch, lib):
     traffic = load_traffic(dom)
     return w, {
         "ms_per_step": ms_step,
+        "ms_per_step_wall_mean": wall * 1e3 / args.steps,
         "value": w.B * w.L / (ms_step * 1e-3),
         "kernels_ms": {n: round(v, 4) for n, v in avg.items()},
         "dominant": dom,
@@ -192,6 +237,133 @@ def bench_train(args, hip, torch, lib):
                                          bytes_step / (PEAK_HBM_GBS * 1e9)) / (ms_step * 1e-3), 4),
         },
     }, x
+
+
+def bench_fwd_8b(args, hip, torch, lib):
+    """The 8B-shaped forward, B=1 H=32 L=4096 d=128 (fwd_4k).  Its working set (201 MB) fits the
+    256 MB last-level cache, so besides back-to-back forwards each is also timed alone after a
+    read of 1 GiB elsewhere (cold cache); both are medians of HIP-event intervals."""
+    from gated_linear_attention_chunkwise_amd.inputs import WORKLOADS, make_inputs_device
+    w = WORKLOADS["fwd_4k"]
+    x = make_inputs_device(w, "cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    o = torch.empty_like(x["q"])
+    s = lib.make_shape(w.B, w.H, w.L, w.D, w.W, w.M, w.scale, 1.0, torch.bfloat16)
+    nws = lib.workspace_bytes(s, lib.OP_FWD)
+    ws = torch.empty(nws, device="cuda", dtype=torch.uint8)
+    raw = lib.load()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args_c = (ctypes.byref(s), P(x["q"]), P(x["k"]), P(x["v"]), P(x["g"]), P(x["meta_k"]), None, P(o), None,
+              None, None, None, P(ws), nws, ctypes.c_void_p(stream))
+
+    def fwd():   # the C entry point itself: outputs and workspace allocated once, outside the loop
+        rc = raw.lizard_attn_fwd(*args_c)
+        if rc != 0:
+            raise RuntimeError(f"lizard_attn_fwd returned {rc}")
+
+    for _ in range(5):
+        fwd()
+    n = max(5, args.steps)
+    evs = [(hip.event(), hip.event()) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        hip.record(a, stream)
+        fwd()
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    warm = median([hip.ms(a, b) for a, b in evs])
+    flush = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    cold = []
+    for _ in range(n):
+        float(flush.max())
+        a, b = hip.event(), hip.event()
+        hip.record(a, stream)
+        fwd()
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        cold.append(hip.ms(a, b))
+    del flush
+    cold = median(cold)
+    ht = w.B * w.H * w.L
+    f_fwd, _ = flops_per_head_token(w.L, w.D, w.chunk, w.W, w.M)
+    flop, byt = f_fwd * ht, FWD_BYTES * ht
+
+    def fr(ms):
+        return {"ms": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+                "mfma_frac": round(flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                "hbm_frac": round(byt / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+                "attainable_frac": round(max(flop / (PEAK_BF16_TFLOPS * 1e12), byt / (PEAK_HBM_GBS * 1e9))
+                                         / (ms * 1e-3), 4)}
+    return {"workload": f"fwd_4k: B={w.B} H={w.H} L={w.L} d={w.D} W={w.W} M={w.M} chunk={w.chunk}, forward, "
+                        "bf16 activations, fp32 gates",
+            "flop": flop, "bytes": byt, "warm": fr(warm), "cold_cache": fr(cold),
+            "method": "medians of HIP-event intervals: back-to-back forwards (warm), and single forwards "
+                      "after a read of 1 GiB elsewhere (cold)"}
+
+
+def bench_bwd_recompute(args, hip, torch, lib, x, w):
+    """The training step's backward without the forward's saved tensors (lse, o_swa, chunk
+    states recomputed inside the backward) against the backward from them."""
+    stream = torch.cuda.current_stream().cuda_stream
+    f = lib.lizard_attn_fwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=w.W, scale=w.scale,
+                            want_lse=True, want_o_swa=True, want_chunk_states=True)
+    saved = {"lse": f["lse"], "o_swa": f["o_swa"], "chunk_states": f["chunk_states"]}
+    res = {}
+    for name, kw in (("saved", saved), ("recomputed", {})):
+        def bwd():
+            lib.lizard_attn_bwd(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, x["dO"], window=w.W,
+                                scale=w.scale, **kw)
+        for _ in range(2):
+            bwd()
+        n = max(3, min(args.steps, 10))
+        evs = [(hip.event(), hip.event()) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            hip.record(a, stream)
+            bwd()
+            hip.record(b, stream)
+        torch.cuda.synchronize()
+        res[name] = median([hip.ms(a, b) for a, b in evs])
+    kept = sum(t.numel() * t.element_size() for t in saved.values())
+    return {"workload": "train_8k backward", "ms_saved": round(res["saved"], 4),
+            "ms_recomputed": round(res["recomputed"], 4),
+            "saved_tensor_bytes": kept,
+            "note": "recomputing lse, o_swa and the chunk states costs the difference in time and saves "
+                    "saved_tensor_bytes of memory kept between the passes per layer"}
+
+
+def bench_strong_gates(args, hip, torch, lib, x, w):
+    """The training step with the pages' own gate at temperature 1, g = log sigmoid(z) with
+    pre-activations z ~ N(-1, 1): chunk sums near -86, so almost every chunk takes the 16-token
+    sub-block path."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    z = torch.randn(x["g"].shape, generator=gen, device="cuda", dtype=torch.float32) - 1.0
+    g = torch.nn.functional.logsigmoid(z)
+    del z
+    strong = float((g.reshape(w.B, w.H, w.L // 64, 64, w.D).sum(3).amin(-1) < -64).float().mean())
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        f = lib.lizard_attn_fwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, window=w.W, scale=w.scale,
+                                want_lse=True, want_o_swa=True, want_chunk_states=True)
+        lib.lizard_attn_bwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, x["dO"], f["lse"], f["o_swa"],
+                            f["chunk_states"], window=w.W, scale=w.scale)
+    for _ in range(2):
+        step()
+    n = max(3, min(args.steps, 10))
+    evs = [(hip.event(), hip.event()) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        hip.record(a, stream)
+        step()
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = median([hip.ms(a, b) for a, b in evs])
+    return {"workload": f"train_8k with g = log sigmoid(z), z ~ N(-1, 1) (tau = 1): B={w.B} H={w.H} L={w.L} "
+                        f"d={w.D}, forward+backward",
+            "strong_chunk_fraction": round(strong, 4), "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1)}
 
 
 # compulsory bytes per head-token with one gate per head and token (4 B of gate, 4 B of dg)
@@ -295,6 +467,29 @@ def bench_decode(args, hip, torch, lib):
     del flush
     us_cold = sorted(cold)[len(cold) // 2]
     us_iso = sorted(iso)[len(iso) // 2]
+    # the step sequence captured once in a HIP graph (kernel nodes only) and replayed: no host
+    # launch work between steps
+    ng = min(64, steps)
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        with torch.cuda.graph(graph, stream=gstream):
+            for t in range(ng):
+                lib.lizard_attn_decode_step(tok["q"][t], tok["k"][t], tok["v"][t], tok["g"][t], mk, None, state,
+                                            ring_k, ring_v, pos, window=w.W, scale=w.scale, out=out[t], workspace=ws)
+    torch.cuda.current_stream().wait_stream(gstream)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    ga, gb = hip.event(), hip.event()
+    hip.record(ga, stream)
+    for _ in range(reps):
+        graph.replay()
+    hip.record(gb, stream)
+    torch.cuda.synchronize()
+    us_graph = hip.ms(ga, gb) * 1e3 / (reps * ng)
+    del graph
     d = w.D
     bytes_step = (2 * w.B * w.H * d * d * 4 + 2 * w.B * w.H * w.W * d * 2
                   + 4 * w.B * w.H * d * 2 + w.B * w.H * d * 4 + 2 * w.B * w.H * d * 2)
@@ -302,6 +497,8 @@ def bench_decode(args, hip, torch, lib):
     return {"workload": f"decode_b64: B={w.B} H={w.H} d={d} fp32 state, W={w.W} bf16 ring, M={w.M}; "
                         f"{steps} steps after a {P}-token prefill",
             "tokens_per_s": round(w.B / (us * 1e-6), 1), "us_per_step": round(us, 2),
+            "graph": {"us_per_step": round(us_graph, 2), "steps_per_graph": ng,
+                      "hbm_frac": round(bytes_step / (us_graph * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
             "cold_cache": {"us_per_step_median": round(us_cold, 2), "isolated_us_per_step_median": round(us_iso, 2),
                            "steps": ncold,
                            "hbm_frac": round(bytes_step / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
@@ -535,6 +732,9 @@ def main():
     ap.add_argument("--no-stage1", action="store_true")
     ap.add_argument("--no-features", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fwd-8b", action="store_true")
+    ap.add_argument("--no-recompute", action="store_true")
+    ap.add_argument("--no-strong-gates", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle timing sample")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -573,12 +773,21 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads)
     if not args.no_scalar_gate:
         rec["scalar_gate"] = bench_scalar_gate(args, hip, torch, lib, x, w)
+    if not args.no_recompute:
+        rec["bwd_recompute"] = bench_bwd_recompute(args, hip, torch, lib, x, w)
+        torch.cuda.empty_cache()
+    if not args.no_strong_gates:
+        rec["strong_gates"] = bench_strong_gates(args, hip, torch, lib, x, w)
+        torch.cuda.empty_cache()
     if not args.no_stage1:
         rec["stage1"] = bench_stage1(args, hip, torch, lib, x, w)
     if not args.no_features:
         rec["features"] = bench_features(args, hip, torch, lib, x, w)
     del x
     torch.cuda.empty_cache()
+    if not args.no_fwd_8b:
+        rec["fwd_8b"] = bench_fwd_8b(args, hip, torch, lib)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         rec["decode"] = bench_decode(args, hip, torch, lib)
         torch.cuda.empty_cache()

@@ -146,3 +146,51 @@ def test_decode_checkpoint_restore(dtname, D):
     o = host(torch.stack(got, 2))
     r = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], None, window=W, scale=scale)
     assert rel_l2(o, r["o"][:, :, pre + n1:]) <= TOL[dtname]
+
+
+def test_decode_steps_captured_in_a_graph():
+    """Decode steps captured once in a HIP graph (kernel nodes only) and replayed: every replay,
+    from a restored carry and with host work and synchronisations between the replays, equals
+    the eager steps bit for bit."""
+    B, H, D, W, pre, n = 4, 4, 128, 32, 40, 6
+    x = make_small(B, H, pre + n, D, 4, seed=123, bf16=True, with_grad=False)
+    T = {k_: dev(x[k_], torch.bfloat16) for k_ in ("q", "k", "v")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk = dev(x["meta_k"], torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    carry0 = prefill_handoff(*(T[c][:, :, :pre].contiguous() for c in "qkvg"), mk, None, W, scale, 1.0)
+    tok = {c: T[c][:, :, pre:].permute(2, 0, 1, 3).contiguous() for c in "qkvg"}
+    from gated_linear_attention_chunkwise_amd import decode_workspace
+    ws = decode_workspace(B, H, D, "cuda")
+
+    def run(carry, outs):
+        st, a, b, p = carry
+        for t in range(n):
+            lizard_attn_decode_step(tok["q"][t], tok["k"][t], tok["v"][t], tok["g"][t], mk, None, st, a, b, p,
+                                    window=W, scale=scale, out=outs[t], workspace=ws)
+
+    eager = [torch.empty(B, H, D, device="cuda", dtype=torch.bfloat16) for _ in range(n)]
+    c_e = tuple(a.clone() for a in carry0)
+    run(c_e, eager)
+    torch.cuda.synchronize()
+    c_g = tuple(a.clone() for a in carry0)
+    gout = [torch.empty_like(eager[0]) for _ in range(n)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run(c_g, gout)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for a, b in zip(c_g, carry0):
+            a.copy_(b)                       # restore the carry the graph starts from
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(n):
+            assert torch.equal(gout[t], eager[t]), (rep, t)
+        for a, b in zip(c_g, c_e):
+            assert torch.equal(a, b), rep
+        _ = float(gout[0].float().sum())     # eager work between the replays
