@@ -31,11 +31,11 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
   const int d = s->d_k;
   if (d != 64 && d != 128) return LIZARD_EUNSUPPORTED;
   if (s->M > kMaxMeta) return LIZARD_EUNSUPPORTED;
-  if (op == LIZARD_OP_DECODE) {
-    if (s->W > kMaxDecodeWindow) return LIZARD_EUNSUPPORTED;
-  } else {
+  // a continued segment and a decode step keep the window's keys in a ring of W slots
+  if ((op == LIZARD_OP_DECODE || op == LIZARD_OP_FWD_CONTINUE) && s->W > kMaxDecodeWindow)
+    return LIZARD_EUNSUPPORTED;
+  if (op != LIZARD_OP_DECODE) {
     if (s->chunk != 0 && s->chunk != kChunk) return LIZARD_EUNSUPPORTED;
-    if (s->W > 2 * kChunk + 1) return LIZARD_EUNSUPPORTED;     // window spans at most 3 chunks
     if (s->dtype == LIZARD_FP32 && d != 64) return LIZARD_EUNSUPPORTED;
   }
   // every tensor of the call must be addressable with 64-bit offsets and
@@ -47,6 +47,10 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
     return LIZARD_EUNSUPPORTED;   // one workgroup per (batch, head, chunk)
   return LIZARD_OK;
 }
+
+// Window length a whole sequence uses: keys in (t - W, t] that exist, so any W >= L sees the
+// full causal prefix and is the same as W = L (this also keeps t - W + 1 far from overflow).
+int32_t window_in(const lizard_attn_shape_t* s) { return s->W < s->L ? s->W : (s->L > 0 ? s->L : 1); }
 
 lizard_status_t check_ptrs(std::initializer_list<const void*> required,
                            std::initializer_list<const void*> optional) {
@@ -96,7 +100,7 @@ lizard_status_t fwd_impl(const lizard_attn_shape_t* s,
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   if (s->L == 0 && state_out == nullptr) return LIZARD_OK;
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
-                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, s->W, s->M, s->scale, s->mix,
+                workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, window_in(s), s->M, s->scale, s->mix,
                 s->gate, s->L > 0 ? lq : nullptr, s->L > 0 ? lk : nullptr};
   return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
@@ -132,7 +136,7 @@ lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
   a.dmeta_k = s->M > 0 ? dmeta_k : nullptr;
   a.dmeta_v = s->M > 0 ? dmeta_v : nullptr;
-  a.B = s->B; a.H = s->H; a.L = s->L; a.W = s->W; a.M = s->M;
+  a.B = s->B; a.H = s->H; a.L = s->L; a.W = window_in(s); a.M = s->M;
   a.scale = s->scale; a.mix = s->mix; a.gate = s->gate;
   a.workspace = workspace;
   a.stage_events = stage_events;

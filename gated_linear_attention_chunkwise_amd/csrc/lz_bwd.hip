@@ -105,8 +105,8 @@ struct CkLayout {
   static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
   static constexpr size_t oDLm = oMkT + sizeof(T) * D * LDM;         // dl_meta^T [16][C]
   static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // mix * p_meta^T [16][C]
-  static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 chunks (log2 units)
-  static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 chunks
+  static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 query chunks (log2 units)
+  static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 query chunks
   static constexpr size_t oBnd = oDel + sizeof(float) * 3 * C;       // boundary term of dg [D]
   static constexpr size_t oTot = oBnd + sizeof(float) * D;           // per-block column totals of d b [4][D]
   static constexpr size_t fast_end = oTot + sizeof(float) * 4 * D;
@@ -907,6 +907,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   const int n_q = c - kt_lo + 1, n_k = qc_hi - c + 1;
   const int n_it = max(n_q, n_k);
   const int lo = t0 + 16 * wb;                     // first query (Q role) or key (K role) of this wave
+  // lse / delta of query chunk c + it sit in slot it % 3: the staging phase filled the first
+  // three, a window reaching further refills a slot once its previous chunk is done
+  float nls = 0.f, ndl = 0.f;
   for (int it = 0; it < n_it; ++it) {
     __syncthreads();   // the previous tiles' readers are done
     if (it < n_q) {
@@ -916,6 +919,11 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     if (it < n_k) {
       put_rows(sQw, pq, (c + it) * C);
       if (it > 0) put_rows(sDw, pd, (c + it) * C);
+      if (it >= 3 && tid < C) {
+        const bool ok = (c + it) * C + tid < L;
+        sLse[(it % 3) * C + tid] = ok ? nls * LOG2E : 0.f;
+        sDel[(it % 3) * C + tid] = ok ? ndl : 0.f;
+      }
     }
     // next iteration's tiles load while this one is processed
     if (it + 1 < n_q) {
@@ -925,6 +933,11 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     if (it + 1 < n_k) {
       fetch_rows(pq, q, (c + it + 1) * C);
       fetch_rows(pd, dO, (c + it + 1) * C);
+      if (it + 1 >= 3 && tid < C) {
+        const int row = min((c + it + 1) * C + tid, L - 1);
+        nls = a.lse[(size_t)bh * L + row];
+        ndl = a.ws_delta[(size_t)bh * L + row];
+      }
     }
     __syncthreads();
     if (qrole) {
@@ -1015,8 +1028,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
           for (int h2 = 0; h2 < 2; ++h2) {
             const int tb = 2 * p + h2, q0 = qbase + 16 * tb;
             const f32x4 x = xs[h2], dp = dps[h2];
-            const f32x4 lse4 = ld4f(sLse + it * C + 16 * tb + 4 * kg);
-            const f32x4 del4 = ld4f(sDel + it * C + 16 * tb + 4 * kg);
+            const f32x4 lse4 = ld4f(sLse + (it % 3) * C + 16 * tb + 4 * kg);
+            const f32x4 del4 = ld4f(sDel + (it % 3) * C + 16 * tb + 4 * kg);
             // every query of the block at or after every key of this wave, within the window,
             // inside the sequence: no per-element mask
             const bool full = vis[h2] && q0 >= lo + 15 && q0 + 15 - lo < W && q0 + 15 < L;

@@ -39,10 +39,10 @@
  *   for HIP, at the caller's next synchronisation.
  * - Supported: d_k = d_v; bf16: d in {64, 128}; fp32: d = 64 for the forward
  *   and backward, d in {64, 128} for decode.  chunk in {64} (0 selects 64).
- *   Forward/backward: 1 <= W <= 2*chunk + 1 = 129 (a query's window spans
- *   at most three chunks); decode: 1 <= W <= 8192.  0 <= M <= 16; B, H >= 1;
- *   L >= 0 (L = 0 writes only the zero state / zero meta gradients).
- *   Anything else returns LIZARD_EUNSUPPORTED.
+ *   Forward/backward: any W >= 1 (W >= L sees the whole causal prefix);
+ *   continued segments and decode keep the window in a ring: 1 <= W <= 8192.
+ *   0 <= M <= 16; B, H >= 1; L >= 0 (L = 0 writes only the zero state / zero
+ *   meta gradients).  Anything else returns LIZARD_EUNSUPPORTED.
  * - Numerical domain: every finite log-gate g <= 0, per token and key
  *   dimension (English page §2.C: the gate handled in log space keeps gated
  *   attention exact in low precision).  Inside a chunk the gate is folded into

@@ -69,7 +69,7 @@ def fwd(lib, s, q=GOOD, meta_k=GOOD, meta_v=None, o=GOOD, lse=None):
 @pytest.mark.parametrize("kw,code", [
     (dict(d_k=96, d_v=96), EUNSUPPORTED), (dict(d_k=64, d_v=128), EUNSUPPORTED),
     (dict(dtype=7), EUNSUPPORTED), (dict(dtype=0, d_k=128, d_v=128), EUNSUPPORTED), (dict(gate=2), EUNSUPPORTED),
-    (dict(M=17), EUNSUPPORTED), (dict(W=130), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED),
+    (dict(M=17), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED),
     (dict(B=0), EINVAL), (dict(L=-1), EINVAL), (dict(W=0), EINVAL), (dict(M=-1), EINVAL),
     (dict(scale=float("nan")), EINVAL),
 ])
@@ -140,6 +140,17 @@ def test_decode_validation(lib):
     assert call(ws=BAD, ws_bytes=need) == EALIGN
 
 
+def test_long_windows_accepted(lib):
+    """Forward and backward take any window length: W beyond three chunks, and W far beyond L
+    (the whole causal prefix), pass validation up to the workspace check."""
+    for W in (130, 1000, 2 ** 31 - 1):
+        s = shape(W=W)
+        assert lib.lizard_attn_fwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None,
+                                   None, None, None, None, 0, None) == EWORKSPACE
+        assert lib.lizard_attn_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD,
+                                   GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 0, None, None) == EWORKSPACE
+
+
 def test_fwd_needs_workspace_without_chunk_states(lib):
     s = shape()
     need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)
@@ -167,7 +178,8 @@ def test_fwd_continue_validation(lib):
     assert call(pos=None) == EINVAL
     assert call(meta_k=None) == EINVAL
     assert call(pos=BAD) == EALIGN
-    assert call(s_=shape(W=130)) == EUNSUPPORTED
+    assert call(s_=shape(W=9000)) == EUNSUPPORTED           # the ring holds at most 8192 keys
+    assert call(s_=shape(W=8192), ws=None) == EWORKSPACE    # (a valid shape: the workspace check is next)
     assert call(s_=shape(dtype=0)) == EUNSUPPORTED          # fp32 runs d = 64 only
     assert call(ws=None) == EWORKSPACE
     assert call(ws_bytes=need - 1) == EWORKSPACE

@@ -65,11 +65,22 @@ def test_bf16_d128_ragged(L):
 
 
 @pytest.mark.parametrize("W,M,with_mv,mix", [(1, 0, False, 1.0), (5, 1, False, 0.5), (64, 16, True, 1.0),
-                                             (65, 4, True, 2.0), (129, 3, False, 1.0), (100, 0, False, 1.0)])
+                                             (65, 4, True, 2.0), (129, 3, False, 1.0), (100, 0, False, 1.0),
+                                             # windows beyond three chunks, and past the sequence's end
+                                             (130, 2, False, 1.0), (190, 4, True, 1.0), (1000, 1, False, 0.5)])
 @pytest.mark.parametrize("dtname", ["fp32", "bf16"])
 def test_window_and_meta_edge_cases(W, M, with_mv, mix, dtname):
     x = make_small(2, 2, 190, 64, M, seed=11 * W + M, bf16=(dtname == "bf16"), with_meta_v=with_mv)
     b, ref = run_both(x, dtname, W, mix=mix)
+    check(b, ref, dtname)
+
+
+@pytest.mark.parametrize("dtname,D,L,W", [("fp32", 64, 700, 300), ("bf16", 128, 700, 300), ("bf16", 64, 333, 4000)])
+def test_long_window(dtname, D, L, W):
+    """Windows reaching more than three chunks back (the key side of a chunk then walks up to
+    six later query chunks), and one longer than the sequence."""
+    x = make_small(1, 2, L, D, 4, seed=L + W + D, bf16=(dtname == "bf16"), with_meta_v=True)
+    b, ref = run_both(x, dtname, W)
     check(b, ref, dtname)
 
 

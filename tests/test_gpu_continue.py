@@ -44,6 +44,8 @@ CASES = [
     ("bf16", 128, (130, 3, 64), 1, 129, 16, True, 33),
     ("bf16", 64, (17, 0, 300), 130, 1, 0, False, 100),
     ("fp32", 64, (64, 128, 2), 200, 129, 2, True, 64),
+    # a window of several chunks held in the ring
+    ("bf16", 128, (300, 20, 0), 150, 260, 4, True, 90),
     # a segment long enough for the state sweep to run in sequence segments from the carried state
     ("bf16", 64, (100, 0, 3000), 2100, 64, 4, False, 1024),
 ]

@@ -62,12 +62,22 @@ def test_bf16_d128_ragged(L):
 
 
 @pytest.mark.parametrize("W,M,with_mv,mix", [(1, 0, False, 1.0), (5, 1, False, 0.5), (64, 16, True, 1.0),
-                                             (65, 4, True, 2.0), (129, 3, False, 1.0), (100, 0, False, 1.0)])
+                                             (65, 4, True, 2.0), (129, 3, False, 1.0), (100, 0, False, 1.0),
+                                             # windows beyond three chunks, and past the sequence's end
+                                             (130, 2, False, 1.0), (190, 4, True, 1.0), (1000, 1, False, 0.5)])
 @pytest.mark.parametrize("dtname", ["fp32", "bf16"])
 def test_window_and_meta_edge_cases(W, M, with_mv, mix, dtname):
     x = make_small(1, 2, 190, 64, M, seed=7 * W + M, bf16=(dtname == "bf16"), with_grad=False,
                    with_meta_v=with_mv)
     out, ref = run_fwd(x, dtname, W, mix=mix)
+    check(out, ref, dtname)
+
+
+@pytest.mark.parametrize("dtname,D", [("fp32", 64), ("bf16", 128)])
+def test_long_window(dtname, D):
+    """A window of up to six chunks of keys (W = 300 over L = 700)."""
+    x = make_small(2, 2, 700, D, 4, seed=300 + D, bf16=(dtname == "bf16"), with_grad=False, with_meta_v=True)
+    out, ref = run_fwd(x, dtname, 300)
     check(out, ref, dtname)
 
 

@@ -125,6 +125,16 @@ def test_strong_gates_meta_values_and_mix():
     check(b, gref, GRADS, "bf16", "meta_v bwd")
 
 
+@pytest.mark.parametrize("dtname,D", [("fp32", 64), ("bf16", 128)])
+def test_strong_gates_long_window(dtname, D):
+    """A window of several chunks on the sub-block path (every chunk strong)."""
+    x = make_small(1, 2, 700, D, 4, seed=91 + D, bf16=(dtname == "bf16"), with_meta_v=True)
+    x = strong_gates(x, "tau1_mu-1", seed=92)
+    f, b, ref, gref = run_both(x, dtname, 300)
+    check(f, ref, ("o", "o_swa", "lse", "state"), dtname, "long window fwd")
+    check(b, gref, GRADS, dtname, "long window bwd")
+
+
 def test_strong_gates_repeatable():
     """The dispatch list is filled in whatever order the chunks finish; results may not depend on it."""
     x = make_small(2, 4, 512, 128, 4, seed=5, bf16=True)
