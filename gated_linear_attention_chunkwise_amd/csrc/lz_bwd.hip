@@ -420,7 +420,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         for (int x = 0; x < NB; ++x) mma32(Y[x], cur[x], fo[ks]);
         if (ks + 2 < KS) load_s(cur, ks + 2);
       }
-      mfma_drain();
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
         const int col = 16 * x + 4 * kg;
@@ -439,7 +438,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         if (sb <= wb) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) mma32(blk[sb], ld_frag(sV, LDQ, 16 * sb + r, 32 * ks + 8 * kg), fo[ks]);
-          mfma_drain();
           if (sb == wb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -480,7 +478,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
 #pragma unroll
           for (int x = 0; x < NB; ++x)
             mma32(X[x], ld_frag_tr(sKh, LDQ, 16 * sb + 4 * kg, 16 * sb + 4 * kg, 16 * x, lane), op);
-          mfma_drain();
 #pragma unroll
           for (int x = 0; x < NB; ++x) {
             const int col = 16 * x + 4 * kg;
@@ -544,7 +541,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
           } else {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], qop_row(16 * tb + r, ks), fkh[ks]);
-            mfma_drain();
           }
           if (tb == wb)
 #pragma unroll
@@ -568,7 +564,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         if (tb >= wb) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sdO, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fvu[ks]);
-          mfma_drain();
           if (tb == wb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -626,7 +621,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
             __builtin_amdgcn_sched_barrier(0);   // one operand's loads at a time (register pressure)
           }
         }
-      mfma_drain();
       // intra-chunk k side: terms of d b from k'', and dk = dk'' e^(T_wb - P_s) (at most 1)
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
@@ -673,7 +667,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
           mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fki);
         }
       }
-      mfma_drain();
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
         const int col = 16 * x + 4 * kg;
@@ -699,7 +692,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       if (sb <= wb) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mma32(blk[sb], ld_frag(sV, LDQ, 16 * sb + r, 32 * ks + 8 * kg), fo[ks]);
-        mfma_drain();
         if (sb == wb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -738,7 +730,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       if (tb >= wb) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sQt, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fkh[ks]);
-        mfma_drain();
         if (tb == wb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -761,7 +752,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       if (tb >= wb) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sdO, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fvu[ks]);
-        mfma_drain();
         if (tb == wb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -787,7 +777,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       }
     }
   }
-  mfma_drain();
   // this lane's window operands: Q role raw q and dO of its query, K role raw k and v of its key
   frag fa[KS], fb[KS];
 #pragma unroll
@@ -887,7 +876,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       mma32(x, ld_frag_tr(sMkT, LY::LDM, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 0, lane), fa[ks]);
       mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), fb[ks]);
     }
-    mfma_drain();
     f32x4 dl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -967,7 +955,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
               mma32(xs[h2], ld_frag(sKw, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fa[ks]);
               mma32(dps[h2], ld_frag(sV, LDQ, 16 * kb + r, 32 * ks + 8 * kg), fb[ks]);
             }
-          mfma_drain();
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int kb = 2 * p + h2, s0 = kbase + 16 * kb;
@@ -1023,7 +1010,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
               mma32(xs[h2], ld_frag(sQw, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fa[ks]);
               mma32(dps[h2], ld_frag(dOr, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fb[ks]);
             }
-          mfma_drain();
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int tb = 2 * p + h2, q0 = qbase + 16 * tb;
@@ -1077,7 +1063,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
             mma32(xv, ld_frag_tr(sdO, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
                   ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
           }
-          mfma_drain();
           if (r < M)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1090,7 +1075,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   }
 
   // ------------------------------------------------------------------ store
-  mfma_drain();
   if (tvalid) {
     const size_t o = hoff + (size_t)tok * D;
     if (qrole) {

@@ -209,7 +209,6 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      mfma_drain();   // the block ends in control flow
     } else if (kbase <= qw + QW - 1) {   // the diagonal: some keys are visible to some queries
       bool vis[NQ][4];
       f32x4 x[NQ][4];
@@ -229,7 +228,6 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
             for (int b = 0; b < NQ; ++b)
               if (vis[b][kb]) mma32(x[b][kb], kf, qf[b][ks]);
           }
-          mfma_drain();
         }
       }
 #pragma unroll
@@ -260,7 +258,6 @@ __global__ __launch_bounds__(NTHR_TE, 2) void teacher_mse_kernel(DistillArgs a) 
           for (int b = 0; b < NQ; ++b)
             if (vb[b]) mma32(O[b][jb], vf, bop[b]);
         }
-        mfma_drain();
       }
     }
     if (more) store_tile(stage ^ 1);   // that stage was last read before the previous barrier

@@ -266,7 +266,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
       xm[0] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) mma32(xm[0], ld_frag(sMk, LDQ, r, 32 * ks + 8 * kg), qf[ks]);
-      mfma_drain();
 #pragma unroll
       for (int i = 0; i < 4; ++i) xm[0][i] = (4 * kg + i < M) ? xm[0][i] * sl2 : -INFINITY;
       absorb<1, JB>(xm, mrun, lpart, OW);
@@ -274,7 +273,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
       pack_acc(bop, xm[0], f32x4{0, 0, 0, 0});
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) mma32(OW[jb], ld_frag_perm(sMvt, LY::LDMV, 16 * jb + r, 0, 0, kg), bop);
-      mfma_drain();
     }
 
     const int kbase = kt * C;
@@ -290,7 +288,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
       if (vis[kb]) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mma32(x[kb], ld_frag(sK, LDQ, 16 * kb + r, 32 * ks + 8 * kg), qf[ks]);
-        mfma_drain();
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -310,7 +307,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
           mma32(OW[jb], ld_frag_tr(sV, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane), bop);
       }
   }
-  mfma_drain();
   if constexpr (NSH > 1) load_state(rs1, 1);
 
   // window epilogue: o_swa and lse; OW becomes mix * O_swa, the GLA terms add onto it
@@ -515,7 +511,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
                 set_elem(qop, e, gate_op<FEAT>(qs[ks][e], bq[ks][e >> 2][e & 3] + h[e >> 2][e & 3]));
               mma32(sc[kb], ld_frag(sX, LDQ, 16 * kb + r, 32 * ks + 8 * kg), qop);
             }
-            mfma_drain();
           }
           if (kb == w) {
 #pragma unroll
@@ -532,7 +527,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
             mma32(sc[kb], ld_frag(sX, LDQ, 16 * kb + r, 32 * ks + 8 * kg), ld_frag(sK, LDQ, 16 * w + r, 32 * ks + 8 * kg));
-          mfma_drain();
           if (kb == w) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -550,7 +544,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
         for (int jb = 0; jb < JB; ++jb)
           mma32(OW[jb], ld_frag_tr(sV, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * jb, lane), bop);
       }
-    mfma_drain();
   }
   // inter-chunk: O^T += S_c^T q~^T, 64 state rows at a time
 #pragma unroll
@@ -572,7 +565,6 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
         mma32(OW[jb], ld_frag_tr(sS, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane), fq);
     }
   }
-  mfma_drain();
   if (qvalid && a.o != nullptr) {   // (no o when the backward recomputes lse and o_swa)
     T* orow = reinterpret_cast<T*>(a.o) + hoff + (size_t)tq * D;
 #pragma unroll

@@ -400,7 +400,6 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   }
   if (n0 < NCs) process(s0, n0);
   if (DEPTH > 2 && n0 + 1 < NCs) process(s1, n0 + 1);
-  mfma_drain();
   if constexpr (REDUCE) {
     const size_t sb = (size_t)bh * a.NS + seg;
     float* sf = a.seg_fin + sb * D * D;
