@@ -37,6 +37,7 @@ METRIC = "hybrid-attn fwd+bwd tokens/s (8B-shaped layer) + % MFMA/HBM roofline"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
 def flops_per_head_token(L, d, C, W, M):
@@ -104,6 +105,154 @@ def load_traffic(kernel):
     if not ent or ent.get("source_sha") != source_sha(ent.get("sources", [])):
         return None
     return ent.get("bytes_per_launch")
+
+
+def load_counters(kernel):
+    """Matrix-core and LDS counter figures of one kernel from the committed rocprofv3 summary, if
+    they were taken on the current sources of that kernel; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel)
+    if not ent or ent.get("source_sha") != source_sha(ent.get("sources", [])):
+        return None
+    return {k: ent[k] for k in ("mfma_busy_frac", "lds_bank_conflict_cycles_per_lds_inst") if k in ent}
+
+
+# ------------------------------------------------------------ rocprofv3 summaries
+# The kernels of the training step and of one decode step, as the counter runs name them:
+# (name in the summaries, kernel template, grid in threads, source file)
+PROFILED = [
+    ("sweep_kernel_fwd", "sweep_kernel<bf16_t, 128, false, false, false, false>", 131072, "lz_sweep.hip"),
+    ("out_kernel", "out_kernel<bf16_t, 128, false, false, false>", 4194304, "lz_fwd.hip"),
+    ("sweep_kernel_bwd", "sweep_kernel<bf16_t, 128, true, false, false, false>", 131072, "lz_sweep.hip"),
+    ("chunk_kernel", "chunk_kernel<bf16_t, 128, false, false>", 8388608, "lz_bwd.hip"),
+    ("decode_kernel", "decode_kernel<bf16_t, 128, false>", 2097152, "lz_decode.hip"),
+    ("decode_combine_kernel", "decode_combine_kernel<bf16_t, 128>", 262144, "lz_decode.hip"),
+]
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4
+PROFILE_ARGS = ("--steps 5 --warmup 2 --no-cpu-baseline --no-prefill --no-scalar-gate --no-gate-proj --no-stage1 "
+                "--no-features --no-fwd-8b --no-recompute --no-strong-gates --decode-steps 16 --copy-calibration")
+
+
+def _kernel_key(name):
+    import re
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("lz::", "")
+    return re.sub(r"\(.*$", "", n).strip()
+
+
+def _rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(prof_dir, out_dir):
+    """Turn four rocprofv3 runs of `bench.py PROFILE_ARGS` under prof_dir (kt: --kernel-trace
+    --stats; fetch: --pmc FETCH_SIZE; write: --pmc WRITE_SIZE; mfma: --pmc of the matrix-core,
+    LDS and busy counters) into profiles/traffic.json, profiles/counters.json and a text table."""
+    import collections
+    csrc = "gated_linear_attention_chunkwise_amd/csrc/"
+
+    def per_kernel(sub, fname, counter=None):
+        d = collections.defaultdict(list)
+        for r in _rows(os.path.join(prof_dir, sub, fname)):
+            key = (_kernel_key(r["Kernel_Name"]), int(r.get("Grid_Size") or r.get("Grid_Size_X")))
+            if counter is None:
+                d[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            elif r["Counter_Name"] == counter:
+                d[key].append(float(r["Counter_Value"]))
+        return d
+
+    dur = per_kernel("kt", "run_kernel_trace.csv")
+    fetch = per_kernel("fetch", "run_counter_collection.csv", "FETCH_SIZE")
+    write = per_kernel("write", "run_counter_collection.csv", "WRITE_SIZE")
+    pmc = {c: per_kernel("mfma", "run_counter_collection.csv", c)
+           for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE", "SQ_INSTS_LDS",
+                     "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES")}
+    mean = lambda v: sum(v) / len(v)
+    # calibration: the largest plain device copy in the runs (1 GiB read, 1 GiB written)
+    copy = max((k for k in fetch if k[0].startswith("__amd_rocclr_copyBuffer")), key=lambda k: k[1])
+    ff = (1 << 30) / (mean(fetch[copy]) * 1024)
+    wf = (1 << 30) / (mean(write[copy]) * 1024)
+    traffic = {"_calibration": {"copy_bytes": 1 << 30, "fetch_kib": mean(fetch[copy]), "write_kib": mean(write[copy]),
+                                "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                                "kernel": "__amd_rocclr_copyBuffer (torch copy_ of a 1 GiB bf16 tensor)"}}
+    counters = {"_normalisation": (
+        "mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 256 * 4): the matrix-core busy "
+        "cycles summed over all SIMDs (16 per v_mfma_f32_16x16x32_bf16, = 16 * SQ_INSTS_MFMA) over the SIMD-cycles "
+        "of the launch (GRBM_GUI_ACTIVE sums the busy cycles of the 8 XCDs; 256 CUs of 4 SIMDs)")}
+    lines = []
+    for name, tmpl, grid, src in PROFILED:
+        key = (tmpl, grid)
+        srcs = [csrc + "lz_common.hpp", csrc + "lz_kernels.hpp", csrc + src]
+        sha = source_sha(srcs)
+        launch = f"{tmpl} grid={grid // 512 if 'chunk' in tmpl or 'sweep' in tmpl else grid}"
+        row = {"kernel": name, "launches": len(dur.get(key, []))}
+        if key in dur:
+            row["us_mean"] = mean(dur[key]) / 1e3
+        if key in fetch and key in write:
+            rb, wb = mean(fetch[key]) * 1024 * ff, mean(write[key]) * 1024 * wf
+            traffic[name] = {"bytes_per_launch": round(rb + wb), "read_bytes": round(rb), "write_bytes": round(wb),
+                             "launch": launch, "sources": srcs, "source_sha": sha}
+            row.update(read_gb=rb / 1e9, write_gb=wb / 1e9)
+        if all(key in pmc[c] for c in pmc):
+            gui = mean(pmc["GRBM_GUI_ACTIVE"][key])
+            busy = mean(pmc["SQ_VALU_MFMA_BUSY_CYCLES"][key])
+            lds = mean(pmc["SQ_INSTS_LDS"][key])
+            ent = {"mfma_busy_frac": round(busy / (gui / XCDS * CUS * SIMDS_PER_CU), 4),
+                   "mfma_busy_cycles": busy, "mfma_insts": mean(pmc["SQ_INSTS_MFMA"][key]),
+                   "gui_active_cycles_per_xcd": gui / XCDS,
+                   "lds_insts": lds, "lds_bank_conflict_cycles": mean(pmc["SQ_LDS_BANK_CONFLICT"][key]),
+                   "lds_bank_conflict_cycles_per_lds_inst": (round(mean(pmc["SQ_LDS_BANK_CONFLICT"][key]) / lds, 3)
+                                                             if lds else None),
+                   "launch": launch, "sources": srcs, "source_sha": sha}
+            counters[name] = ent
+            row.update(mfma_busy=ent["mfma_busy_frac"], conflicts_per_lds=ent["lds_bank_conflict_cycles_per_lds_inst"],
+                       clock_ghz=(gui / XCDS) / (row["us_mean"] * 1e3) if "us_mean" in row else None)
+        lines.append(row)
+    if "decode_kernel" in traffic and "decode_combine_kernel" in traffic:
+        a, b = traffic["decode_kernel"], traffic["decode_combine_kernel"]
+        traffic["decode"] = {"bytes_per_launch": a["bytes_per_launch"] + b["bytes_per_launch"],
+                             "read_bytes": a["read_bytes"] + b["read_bytes"],
+                             "write_bytes": a["write_bytes"] + b["write_bytes"],
+                             "launch": a["launch"] + " + " + b["launch"] + " (one decode step)",
+                             "sources": a["sources"], "source_sha": a["source_sha"]}
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    with open(os.path.join(out_dir, "counters.json"), "w") as f:
+        json.dump(counters, f, indent=1)
+    cmd = f"python -u bench.py {PROFILE_ARGS}"
+    txt = ["# train_8k forward+backward (B=4 H=32 L=8192 d=128 W=128 M=4, bf16) and decode_b64 (B=64 H=32 d=128):",
+           "# kernel times, HBM bytes and matrix-core / LDS counters per launch",
+           "#",
+           "# made by (TMPDIR=/tmp, from the repository root), one run each:",
+           f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt -o run -- {cmd}",
+           f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- {cmd}",
+           f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- {cmd}",
+           "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+           f"SQ_BUSY_CYCLES --output-format csv -d <dir>/mfma -o run -- {cmd}",
+           "#   python bench.py --summarize-profiles <dir> --profiles-out profiles",
+           "#",
+           f"# HBM bytes: FETCH_SIZE x 1024 x {ff:.4f} (read), WRITE_SIZE x 1024 x {wf:.4f} (written); the factors make",
+           "# the counters of a plain 1 GiB device copy in the same runs read 1 GiB each way.",
+           "# " + counters["_normalisation"],
+           "# clock = GRBM_GUI_ACTIVE / 8 over the trace's mean duration (a check of the normalisation).",
+           "",
+           f"{'kernel':24s}{'launches':>9s}{'us mean':>10s}{'read GB':>9s}{'write GB':>9s}{'GB/s':>8s}"
+           f"{'MFMA busy':>11s}{'LDS confl/inst':>16s}{'clock GHz':>10s}"]
+    for r in lines:
+        gbs = ((r.get("read_gb", 0) + r.get("write_gb", 0)) / (r["us_mean"] * 1e-6)) if "us_mean" in r and "read_gb" in r else None
+        f = lambda v, fmt: (fmt % v) if v is not None else "-"
+        txt.append(f"{r['kernel']:24s}{r['launches']:>9d}{f(r.get('us_mean'), '%.1f'):>10s}{f(r.get('read_gb'), '%.3f'):>9s}"
+                   f"{f(r.get('write_gb'), '%.3f'):>9s}{f(gbs, '%.0f'):>8s}{f(r.get('mfma_busy'), '%.4f'):>11s}"
+                   f"{f(r.get('conflicts_per_lds'), '%.2f'):>16s}{f(r.get('clock_ghz'), '%.2f'):>10s}")
+    with open(os.path.join(out_dir, "train_8k_and_decode_counters.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(txt))
 
 
 def median(v):
@@ -218,6 +367,7 @@ def bench_train(args, hip, torch, lib):
     dom_bytes = BWD_BYTES * ht
     achieved = dom_bytes / (avg[dom] * 1e-3) / 1e9
     traffic = load_traffic(dom)
+    counters = {k: load_counters(k) for k in ("sweep_kernel_fwd", "out_kernel", "sweep_kernel_bwd", "chunk_kernel")}
     return w, {
         "ms_per_step": ms_step,
         "ms_per_step_wall_mean": wall * 1e3 / args.steps,
@@ -226,7 +376,9 @@ def bench_train(args, hip, torch, lib):
         "dominant": dom,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes},
+                     "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
+                     "mfma_busy_frac": (counters[dom] or {}).get("mfma_busy_frac")},
+        "counters": counters,
         "step_roofline": {
             "flop": flops_step, "bytes": bytes_step,
             "mfma_frac": round(flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
@@ -739,7 +891,13 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="summarise rocprofv3 runs under DIR (kt, fetch, write, mfma) instead of measuring")
+    ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.profiles_out)
+        return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards over batch and heads with no exchange between GPUs)",
@@ -762,6 +920,7 @@ def main():
         "roofline": tr["roofline"],
         "kernels_ms": tr["kernels_ms"],
         "step_roofline": tr["step_roofline"],
+        "kernel_counters": tr["counters"],
     }
     if args.copy_calibration:
         src = torch.empty(1 << 29, device="cuda", dtype=torch.bfloat16).fill_(1.0)

@@ -1,0 +1,51 @@
+"""The rocprofv3 summariser of bench.py (CPU only): byte calibration against the plain copy and the
+matrix-core busy normalisation, on hand-made counter files."""
+import csv
+import json
+import os
+
+import bench
+
+TRACE_COLS = ["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"]
+PMC_COLS = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+CHUNK = "void lz::(anonymous namespace)::chunk_kernel<lz::bf16_t, 128, false, false>(lz::BwdArgs, lz::bf16_t const*, float const*)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write(path, cols, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_summary_scales_bytes_and_normalises_mfma(tmp_path):
+    d = str(tmp_path / "prof")
+    # a 1 ms chunk kernel at 2.4 GHz: 2.4e6 cycles on each of the 8 XCDs
+    _write(f"{d}/kt/run_kernel_trace.csv", TRACE_COLS,
+           [{"Kernel_Name": CHUNK, "Grid_Size_X": 8388608, "Start_Timestamp": 0, "End_Timestamp": 1_000_000}])
+    # the copy reads half its bytes in FETCH_SIZE units and all of them in WRITE_SIZE units
+    _write(f"{d}/fetch/run_counter_collection.csv", PMC_COLS,
+           [{"Kernel_Name": COPY, "Grid_Size": 131072, "Counter_Name": "FETCH_SIZE", "Counter_Value": 524288.0},
+            {"Kernel_Name": CHUNK, "Grid_Size": 8388608, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1000.0}])
+    _write(f"{d}/write/run_counter_collection.csv", PMC_COLS,
+           [{"Kernel_Name": COPY, "Grid_Size": 131072, "Counter_Name": "WRITE_SIZE", "Counter_Value": 1048576.0},
+            {"Kernel_Name": CHUNK, "Grid_Size": 8388608, "Counter_Name": "WRITE_SIZE", "Counter_Value": 500.0}])
+    insts = 1.0e6
+    vals = {"SQ_VALU_MFMA_BUSY_CYCLES": 16 * insts, "SQ_INSTS_MFMA": insts, "GRBM_GUI_ACTIVE": 8 * 2.4e6,
+            "SQ_INSTS_LDS": 2.0e6, "SQ_LDS_BANK_CONFLICT": 3.0e6, "SQ_BUSY_CYCLES": 1.0}
+    _write(f"{d}/mfma/run_counter_collection.csv", PMC_COLS,
+           [{"Kernel_Name": CHUNK, "Grid_Size": 8388608, "Counter_Name": k, "Counter_Value": v} for k, v in vals.items()])
+    out = str(tmp_path / "out")
+    bench.summarize_profiles(d, out)
+    tr = json.load(open(f"{out}/traffic.json"))
+    assert tr["_calibration"]["fetch_factor"] == 2.0 and tr["_calibration"]["write_factor"] == 1.0
+    assert tr["chunk_kernel"]["read_bytes"] == 1000 * 1024 * 2 and tr["chunk_kernel"]["write_bytes"] == 500 * 1024
+    c = json.load(open(f"{out}/counters.json"))["chunk_kernel"]
+    # 16e6 busy SIMD-cycles over 2.4e6 cycles x 1024 SIMDs
+    assert abs(c["mfma_busy_frac"] - 16e6 / (2.4e6 * 1024)) < 1e-4
+    assert c["lds_bank_conflict_cycles_per_lds_inst"] == 1.5
+    txt = open(f"{out}/train_8k_and_decode_counters.txt").read()
+    assert "rocprofv3 --pmc FETCH_SIZE" in txt and "2.40" in txt   # the clock check: 2.4e6 cycles in 1 ms
