@@ -145,7 +145,9 @@ __device__ __forceinline__ float pair_term(float qv, float kv, float x) {
 // One workgroup per (b, h, chunk), eight waves in two roles over the four
 // 16-token blocks of the chunk: waves 0..3 accumulate dq (GLA and the window
 // seen from the query side), waves 4..7 accumulate dk and dv (GLA and the
-// window seen from the key side), so every score tile is formed once.
+// window seen from the key side).  Each side forms the score tiles it needs
+// once for all output columns (dA and the window scores are formed on both
+// sides; split by output columns, every wave would form every tile).
 // Accumulators are kept transposed: acc[x][e] belongs to token 16*wb + r of
 // the chunk and column 16*x + 4*kg + e.
 // SG: one log-gate per head and token (g, dg [B,H,L]).
