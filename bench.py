@@ -253,6 +253,34 @@ def summarize_profiles(prof_dir, out_dir):
     with open(os.path.join(out_dir, "train_8k_and_decode_counters.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
     print("\n".join(txt))
+    # every kernel of the traced run, grouped by template and grid
+    groups = collections.defaultdict(list)
+    for r in _rows(os.path.join(prof_dir, "kt", "run_kernel_trace.csv")):
+        if r["Kernel_Name"].lstrip().startswith(("at::", "void at::")):
+            continue   # torch's own kernels (input generation, copies)
+        wg = int(r["Workgroup_Size_X"])
+        key = (_kernel_key(r["Kernel_Name"])[:64], int(r["Grid_Size_X"]) // wg, wg, int(r["VGPR_Count"]),
+               int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]))
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    kt = ["# Kernel trace: train_8k forward+backward (B=4 H=32 L=8192 d=128 W=128 M=4, bf16) and decode_b64",
+          "# (B=64 H=32 d=128, 16 steps after a 4096-token prefill)",
+          "#",
+          "# command (TMPDIR=/tmp, from the repository root):",
+          f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt -o run -- {cmd}",
+          "#   python bench.py --summarize-profiles <dir> --profiles-out profiles",
+          "# durations in microseconds per launch (kernel trace start/end); grid in workgroups; the step's kernels",
+          "# are the state sweeps (grid 256), out_kernel and chunk_kernel (grid 16384), the dmeta reduction and the",
+          "# empty sub-block launches; grid 4096 / 131072 sweeps and outputs are the decode workload's prefill;",
+          "# torch's own kernels (input generation) are left out.",
+          "",
+          f"{'kernel':66s}{'wgs':>8s}{'thr':>5s}{'vgpr':>6s}{'agpr':>6s}{'lds':>7s}{'calls':>7s}{'avg_us':>10s}"
+          f"{'median_us':>11s}{'min_us':>10s}{'max_us':>10s}"]
+    for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        name, wgs, wg, vg, ag, lds = key
+        kt.append(f"{name:66s}{wgs:>8d}{wg:>5d}{vg:>6d}{ag:>6d}{lds:>7d}{len(v):>7d}{sum(v) / len(v):>10.1f}"
+                  f"{median(v):>11.1f}{min(v):>10.1f}{max(v):>10.1f}")
+    with open(os.path.join(out_dir, "train_8k_and_decode_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(kt) + "\n")
 
 
 def median(v):

@@ -6,7 +6,8 @@ import os
 
 import bench
 
-TRACE_COLS = ["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"]
+TRACE_COLS = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "VGPR_Count", "Accum_VGPR_Count", "LDS_Block_Size",
+              "Start_Timestamp", "End_Timestamp"]
 PMC_COLS = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
 CHUNK = "void lz::(anonymous namespace)::chunk_kernel<lz::bf16_t, 128, false, false>(lz::BwdArgs, lz::bf16_t const*, float const*)"
 COPY = "__amd_rocclr_copyBuffer"
@@ -25,7 +26,8 @@ def test_summary_scales_bytes_and_normalises_mfma(tmp_path):
     d = str(tmp_path / "prof")
     # a 1 ms chunk kernel at 2.4 GHz: 2.4e6 cycles on each of the 8 XCDs
     _write(f"{d}/kt/run_kernel_trace.csv", TRACE_COLS,
-           [{"Kernel_Name": CHUNK, "Grid_Size_X": 8388608, "Start_Timestamp": 0, "End_Timestamp": 1_000_000}])
+           [{"Kernel_Name": CHUNK, "Grid_Size_X": 8388608, "Workgroup_Size_X": 512, "VGPR_Count": 112,
+             "Accum_VGPR_Count": 0, "LDS_Block_Size": 0, "Start_Timestamp": 0, "End_Timestamp": 1_000_000}])
     # the copy reads half its bytes in FETCH_SIZE units and all of them in WRITE_SIZE units
     _write(f"{d}/fetch/run_counter_collection.csv", PMC_COLS,
            [{"Kernel_Name": COPY, "Grid_Size": 131072, "Counter_Name": "FETCH_SIZE", "Counter_Value": 524288.0},
@@ -49,3 +51,5 @@ def test_summary_scales_bytes_and_normalises_mfma(tmp_path):
     assert c["lds_bank_conflict_cycles_per_lds_inst"] == 1.5
     txt = open(f"{out}/train_8k_and_decode_counters.txt").read()
     assert "rocprofv3 --pmc FETCH_SIZE" in txt and "2.40" in txt   # the clock check: 2.4e6 cycles in 1 ms
+    kt = open(f"{out}/train_8k_and_decode_kernel_trace.txt").read()
+    assert "chunk_kernel<bf16_t, 128, false, false>" in kt and "16384" in kt and "1000.0" in kt
