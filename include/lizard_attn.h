@@ -20,7 +20,9 @@
  * - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *   library never allocates or frees device memory, never synchronises the
  *   stream and keeps no global mutable state: calls are re-entrant and
- *   thread-safe; calls that overlap on the same output buffers race.
+ *   thread-safe; calls that overlap on the same output buffers race.  The
+ *   one exception is lizard_attn_decode_step_noalloc, which keeps its
+ *   partials in a static per-device array (see there).
  * - All tensors are dense row-major ("contiguous") in the shapes given:
  *     q, k, o, dq, dk, dO : [B,H,L,d_k]      v, dv : [B,H,L,d_v]
  *     g, dg               : [B,H,L,d_k] fp32 (log-gates, g <= 0)
