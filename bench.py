@@ -129,8 +129,8 @@ PROFILED = [
     ("out_kernel", "out_kernel<bf16_t, 128, false, false, false>", 4194304, "lz_fwd.hip"),
     ("sweep_kernel_bwd", "sweep_kernel<bf16_t, 128, true, false, false, false>", 131072, "lz_sweep.hip"),
     ("chunk_kernel", "chunk_kernel<bf16_t, 128, false, false>", 8388608, "lz_bwd.hip"),
-    ("decode_kernel", "decode_kernel<bf16_t, 128, false>", 2097152, "lz_decode.hip"),
-    ("decode_combine_kernel", "decode_combine_kernel<bf16_t, 128>", 262144, "lz_decode.hip"),
+    ("decode_kernel", "decode_kernel<bf16_t, 128, false>", 1048576, "lz_decode.hip"),
+    ("decode_pos_kernel", "decode_pos_kernel", 256, "lz_decode.hip"),
 ]
 XCDS, CUS, SIMDS_PER_CU = 8, 256, 4
 PROFILE_ARGS = ("--steps 5 --warmup 2 --no-cpu-baseline --no-prefill --no-scalar-gate --no-gate-proj --no-stage1 "
@@ -189,7 +189,7 @@ def summarize_profiles(prof_dir, out_dir):
         key = (tmpl, grid)
         srcs = [csrc + "lz_common.hpp", csrc + "lz_kernels.hpp", csrc + src]
         sha = source_sha(srcs)
-        launch = f"{tmpl} grid={grid // 512 if 'chunk' in tmpl or 'sweep' in tmpl else grid}"
+        launch = f"{tmpl}, {grid} threads"
         row = {"kernel": name, "launches": len(dur.get(key, []))}
         if key in dur:
             row["us_mean"] = mean(dur[key]) / 1e3
@@ -213,8 +213,8 @@ def summarize_profiles(prof_dir, out_dir):
             row.update(mfma_busy=ent["mfma_busy_frac"], conflicts_per_lds=ent["lds_bank_conflict_cycles_per_lds_inst"],
                        clock_ghz=(gui / XCDS) / (row["us_mean"] * 1e3) if "us_mean" in row else None)
         lines.append(row)
-    if "decode_kernel" in traffic and "decode_combine_kernel" in traffic:
-        a, b = traffic["decode_kernel"], traffic["decode_combine_kernel"]
+    if "decode_kernel" in traffic and "decode_pos_kernel" in traffic:
+        a, b = traffic["decode_kernel"], traffic["decode_pos_kernel"]
         traffic["decode"] = {"bytes_per_launch": a["bytes_per_launch"] + b["bytes_per_launch"],
                              "read_bytes": a["read_bytes"] + b["read_bytes"],
                              "write_bytes": a["write_bytes"] + b["write_bytes"],
@@ -686,7 +686,7 @@ def bench_decode(args, hip, torch, lib):
                                      "a read of 1 GiB elsewhere first"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode"),
-                         "kernel": "decode_kernel + decode_combine_kernel",
+                         "kernel": "decode_kernel + decode_pos_kernel",
                          "algorithmic_bytes_per_step": bytes_step}}
 
 

@@ -242,7 +242,8 @@ def lizard_attn_bwd(q, k, v, g, meta_k, meta_v, dO, lse=None, o_swa=None, chunk_
 
 
 def decode_workspace(B: int, H: int, d: int, device) -> torch.Tensor:
-    """Workspace for lizard_attn_decode_step at this shape (reusable across steps)."""
+    """Workspace for lizard_attn_decode_step at this shape (the step needs none: a one-byte
+    placeholder, kept so that callers written for a workspace still work)."""
     s = make_shape(B, H, 0, d, 1, 0, 1.0, 1.0, torch.bfloat16)
     n = int(load().lizard_attn_workspace_bytes(ctypes.byref(s), OP_DECODE))
     return torch.empty(max(n, 1), device=device, dtype=torch.uint8)
@@ -283,9 +284,8 @@ def lizard_attn_decode_step(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, p
 
 def lizard_attn_decode_step_noalloc(q, k, v, g, meta_k, meta_v, state, ring_k, ring_v, pos, *,
                                     window: int, scale: float | None = None, mix: float = 1.0, out):
-    """lizard_attn_decode_step with no workspace: the library keeps the step's partials in its own
-    per-device array (B*H <= 4032 at d = 128).  ``out`` [B,H,d] must be given (this call
-    allocates nothing); returns it.  Calls that overlap on one device race."""
+    """lizard_attn_decode_step with no workspace argument (the step needs none).  ``out`` [B,H,d]
+    must be given (this call allocates nothing); returns it."""
     lib = load()
     dt, dev = q.dtype, q.device
     for n, t in (("q", q), ("k", k), ("v", v), ("ring_k", ring_k), ("ring_v", ring_v), ("out", out)):

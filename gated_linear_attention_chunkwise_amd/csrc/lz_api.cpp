@@ -169,16 +169,15 @@ lizard_status_t continue_impl(const lizard_attn_shape_t* s, const void* q, const
 lizard_status_t decode_impl(const lizard_attn_shape_t* s, const void* q, const void* k, const void* v,
                             const float* lq, const float* lk, const float* g, const void* meta_k, const void* meta_v,
                             float* state, void* ring_k, void* ring_v, int32_t* pos, void* o, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            size_t /*workspace_bytes*/, hipStream_t stream) {
   lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
   if (st != LIZARD_OK) return st;
   if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
+  // the step needs no workspace (lizard_attn_workspace_bytes gives 0): the argument may be NULL
   st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v, workspace, lq, lk});
   if (st != LIZARD_OK) return st;
-  if (workspace == nullptr || workspace_bytes < lz::decode_workspace_bytes(s->B, s->H, s->d_k))
-    return LIZARD_EWORKSPACE;
   lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
-                   reinterpret_cast<float*>(workspace), s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate, lq, lk};
+                   s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate, lq, lk};
   return lz::launch_decode(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
@@ -215,7 +214,7 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
     return lz::bwd_recompute_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (op == LIZARD_OP_FWD || op == LIZARD_OP_FWD_CONTINUE)
     return lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
-  return lz::decode_workspace_bytes(s->B, s->H, s->d_k);
+  return 0;   // the decode step keeps nothing between its launches but pos
 }
 
 lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
@@ -307,16 +306,9 @@ lizard_status_t lizard_attn_decode_step_noalloc(const lizard_attn_shape_t* s,
                                                 const float* g, const void* meta_k, const void* meta_v,
                                                 float* state, void* ring_k, void* ring_v, int32_t* pos,
                                                 void* o, hipStream_t stream) {
-  lizard_status_t st = check_shape(s, LIZARD_OP_DECODE);
-  if (st != LIZARD_OK) return st;
-  if (s->M > 0 && meta_k == nullptr) return LIZARD_EINVAL;
-  st = check_ptrs({q, k, v, g, state, ring_k, ring_v, pos, o}, {meta_k, meta_v});
-  if (st != LIZARD_OK) return st;
-  // the partials live in the library's own per-device array, of a fixed size
-  if (lz::decode_workspace_bytes(s->B, s->H, s->d_k) > lz::kDecodeScratchBytes) return LIZARD_EWORKSPACE;
-  lz::DecodeArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, state, ring_k, ring_v, pos, o,
-                   nullptr, s->B, s->H, s->W, s->M, s->scale, s->mix, s->gate, nullptr, nullptr};
-  return lz::launch_decode_noalloc(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  // the step keeps nothing in device memory of its own: the plain step without a workspace
+  return decode_impl(s, q, k, v, nullptr, nullptr, g, meta_k, meta_v, state, ring_k, ring_v, pos, o, nullptr, 0,
+                     stream);
 }
 
 lizard_status_t lizard_attn_decode_step_feat(const lizard_attn_shape_t* s,

@@ -97,7 +97,6 @@ struct DecodeArgs {
   const void* q; const void* k; const void* v; const float* g;
   const void* meta_k; const void* meta_v;
   float* state; void* ring_k; void* ring_v; int32_t* pos; void* o;
-  float* o_part;        // workspace: [B,H,d/32,d] fp32 partial q.S per block of 32 state rows
   int B, H, W, M;
   float scale, mix;
   int gate;             // 0: g [B,H,d]; 1: g [B,H]
@@ -157,12 +156,6 @@ int sweep_segments(int B, int H, int L, int D);
 size_t fwd_segment_bytes(int B, int H, int L, int D);
 size_t fwd_aux_bytes(int B, int H, int L, int D);
 size_t fwd_workspace_bytes(int B, int H, int L, int D, int dtype);
-// Workspace bytes needed by launch_decode.
-size_t decode_workspace_bytes(int B, int H, int D);
-// The decode step with its partials in a per-device static array of kDecodeScratchBytes instead of
-// a caller's workspace (no allocation anywhere); shapes needing more return hipErrorInvalidValue.
-constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
-hipError_t launch_decode_noalloc(const DecodeArgs& a, int dtype, int D, hipStream_t st);
 // Workspace bytes needed by launch_gate_bwd: dz [B*L][Ng rounded up to 16 bytes] in the operand
 // dtype, then the fp32 partial sums of dW when its contraction over tokens is split.
 size_t gate_bwd_workspace_bytes(int B, int H, int L, int dk, int sg, int d_model, int dtype);

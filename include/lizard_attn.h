@@ -20,9 +20,7 @@
  * - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *   library never allocates or frees device memory, never synchronises the
  *   stream and keeps no global mutable state: calls are re-entrant and
- *   thread-safe; calls that overlap on the same output buffers race.  The
- *   one exception is lizard_attn_decode_step_noalloc, which keeps its
- *   partials in a static per-device array (see there).
+ *   thread-safe; calls that overlap on the same output buffers race.
  * - All tensors are dense row-major ("contiguous") in the shapes given:
  *     q, k, o, dq, dk, dO : [B,H,L,d_k]      v, dv : [B,H,L,d_v]
  *     g, dg               : [B,H,L,d_k] fp32 (log-gates, g <= 0)
@@ -289,11 +287,11 @@ lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
  *   pos    in/out, device int32 [B]: tokens already consumed (>= 0); incremented
  *   o      [B,H,d_v] written: q S + mix * softmax over M meta keys and the
  *          min(pos+1, W) filled ring slots.
- *   workspace  lizard_attn_workspace_bytes(s, LIZARD_OP_DECODE) bytes of
- *          caller-owned device memory (clobbered): the partials of the d/32
- *          workgroups of each head (q S of 32 state rows; softmax statistics
- *          and value sum of a share of the ring slots), passed from the step's
- *          first launch to its second
+ *   workspace  none is needed: lizard_attn_workspace_bytes(s, LIZARD_OP_DECODE)
+ *          is 0 and the argument may be NULL (kept for the signature)
+ * Two launches on `stream`: the step (d/64 workgroups per head, each owning
+ * 64 value columns of the state, the output and the ring), then the advance
+ * of pos.
  * Uses s->B, H, d_k, d_v, W, M, scale, mix, dtype; s->L and s->chunk are ignored. */
 lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
                                         const void* q, const void* k, const void* v,
@@ -305,14 +303,9 @@ lizard_status_t lizard_attn_decode_step(const lizard_attn_shape_t* s,
 
 /* lizard_attn_decode_step for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same step with the same
- * arguments, minus the workspace.  The per-workgroup partials go to a static array the library
- * holds on every device it runs on until the process ends (16 MiB), so the call allocates
- * nothing: B*H*(d/32)*(2d+4)*4 bytes must fit, i.e. B*H <= 4032 at d = 128 and B*H <= 15887 at
- * d = 64; larger shapes return LIZARD_EWORKSPACE before anything is launched.  The array is
- * found on the calling thread's current device (the device of `stream`).  Nothing in it has to
- * start at zero (the step writes every partial before reading it), but all calls on one device
- * share it: calls that overlap on one device (concurrent streams or threads) race and must be
- * serialised by the caller. */
+ * arguments, minus the workspace.  The step needs no device memory beyond its arguments, so this
+ * call allocates nothing and keeps nothing between calls; it validates like
+ * lizard_attn_decode_step and launches the same kernels. */
 lizard_status_t lizard_attn_decode_step_noalloc(const lizard_attn_shape_t* s,
                                                 const void* q, const void* k, const void* v,
                                                 const float* g, const void* meta_k, const void* meta_v,

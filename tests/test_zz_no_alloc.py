@@ -1,5 +1,5 @@
-"""lizard_attn_decode_step_noalloc (no workspace argument; the partials live in the library's own
-per-device array) against lizard_attn_decode_step, through the C ABI: two runs in a row on one
+"""lizard_attn_decode_step_noalloc (no workspace argument; the step needs no device memory beyond
+its arguments) against lizard_attn_decode_step, through the C ABI: two runs in a row on one
 device, the second on a smaller batch, each bit for bit equal to the plain step and within the
 bf16 bound of the oracle's whole-sequence forward."""
 import ctypes
