@@ -65,6 +65,35 @@ def test_decode_after_prefill(dtname, D, L0, steps, W, M, with_mv):
     assert (pos.cpu().numpy() == L0 + steps).all()
 
 
+@pytest.mark.parametrize("dtname,D,B,H,L0,steps,W,M", [
+    ("bf16", 128, 5, 2, 1100, 6, 1000, 3),    # window of 1000 slots, ring wrapped; 10 heads: both head maps
+    ("bf16", 64, 3, 3, 300, 4, 8192, 16),     # the largest ring, mostly empty
+    ("fp32", 64, 1, 9, 40, 5, 33, 1),         # 9 heads: one group of 8 and a remainder
+])
+def test_decode_long_ring_and_head_maps(dtname, D, B, H, L0, steps, W, M):
+    """Windows of many key blocks (the logits walk the ring in groups of blocks, the value sum
+    beyond the rows loaded ahead), and head counts on either side of the workgroup map's groups
+    of eight heads."""
+    x = make_small(B, H, L0 + steps, D, M, seed=W + 7 * L0 + B * H, bf16=(dtname == "bf16"),
+                   with_grad=False, with_meta_v=True)
+    dt = tdtype(dtname)
+    scale, mix = 1.0 / math.sqrt(D), 1.25
+    T = {n: dev(x[n], dt) for n in ("q", "k", "v")}
+    T["g"] = dev(x["g"], torch.float32)
+    mk, mv = dev(x["meta_k"], dt), dev(x["meta_v"], dt)
+    state, rk, rv, pos = prefill_handoff(*(T[n][:, :, :L0].contiguous() for n in "qkvg"), mk, mv, W, scale, mix)
+    outs = [lizard_attn_decode_step(*(T[n][:, :, t].contiguous() for n in "qkvg"), mk, mv, state, rk, rv, pos,
+                                    window=W, scale=scale, mix=mix) for t in range(L0, L0 + steps)]
+    torch.cuda.synchronize()
+    ref = orc.hybrid_forward(x["q"], x["k"], x["v"], x["g"], x["meta_k"], x["meta_v"], window=W, scale=scale,
+                             mix=mix)
+    e_o = rel_l2(host(torch.stack(outs, 2)), ref["o"][:, :, L0:])
+    e_s = rel_l2(host(state), ref["state"])
+    print(dtname, D, B, H, W, f"o {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= TOL[dtname] and e_s <= TOL[dtname]
+    assert (pos.cpu().numpy() == L0 + steps).all()
+
+
 def test_decode_b64_full_size_sampled():
     """4096-token prefill + 1024 decode steps at B=64, H=32, d=128, W=128, M=4."""
     w = WORKLOADS["decode_b64"]
@@ -91,8 +120,8 @@ def test_decode_b64_full_size_sampled():
 
 
 def test_decode_caller_workspace_matches_default():
-    """A caller-owned workspace reused across steps gives bit-identical results to the
-    per-call one (the workspace carries only values recomputed every step)."""
+    """A caller-owned workspace passed to every step gives bit-identical results to none (the
+    step needs no workspace; one that is passed is left alone)."""
     from gated_linear_attention_chunkwise_amd import decode_workspace
     x = make_small(3, 4, 40, 128, 4, seed=77, bf16=True)
     T = {n: dev(x[n], torch.bfloat16) for n in ("q", "k", "v")}
