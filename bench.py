@@ -950,6 +950,13 @@ def main():
         "step_roofline": tr["step_roofline"],
         "kernel_counters": tr["counters"],
     }
+    props = torch.cuda.get_device_properties(0)
+    rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                     "compute_units": props.multi_processor_count, "l2_bytes": getattr(props, "L2_cache_size", None),
+                     "hbm_bytes": props.total_memory,
+                     "peaks_used": {"hbm_GBs": PEAK_HBM_GBS, "bf16_dense_TFLOPs": PEAK_BF16_TFLOPS,
+                                    "basis": "256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU; the engine clock seen by "
+                                             "the counters is in profiles/train_8k_and_decode_counters.txt"}}
     if args.copy_calibration:
         src = torch.empty(1 << 29, device="cuda", dtype=torch.bfloat16).fill_(1.0)
         dst = torch.empty_like(src)
