@@ -253,15 +253,6 @@ def summarize_profiles(prof_dir, out_dir):
     with open(os.path.join(out_dir, "train_8k_and_decode_counters.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
     print("\n".join(txt))
-    # every kernel of the traced run, grouped by template and grid
-    groups = collections.defaultdict(list)
-    for r in _rows(os.path.join(prof_dir, "kt", "run_kernel_trace.csv")):
-        if r["Kernel_Name"].lstrip().startswith(("at::", "void at::")):
-            continue   # torch's own kernels (input generation, copies)
-        wg = int(r["Workgroup_Size_X"])
-        key = (_kernel_key(r["Kernel_Name"])[:64], int(r["Grid_Size_X"]) // wg, wg, int(r["VGPR_Count"]),
-               int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]))
-        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     kt = ["# Kernel trace: train_8k forward+backward (B=4 H=32 L=8192 d=128 W=128 M=4, bf16) and decode_b64",
           "# (B=64 H=32 d=128, 16 steps after a 4096-token prefill)",
           "#",
@@ -272,15 +263,77 @@ def summarize_profiles(prof_dir, out_dir):
           "# are the state sweeps (grid 256), out_kernel and chunk_kernel (grid 16384), the dmeta reduction and the",
           "# empty sub-block launches; grid 4096 / 131072 sweeps and outputs are the decode workload's prefill;",
           "# torch's own kernels (input generation) are left out.",
-          "",
-          f"{'kernel':66s}{'wgs':>8s}{'thr':>5s}{'vgpr':>6s}{'agpr':>6s}{'lds':>7s}{'calls':>7s}{'avg_us':>10s}"
-          f"{'median_us':>11s}{'min_us':>10s}{'max_us':>10s}"]
+          ""]
+    with open(os.path.join(out_dir, "train_8k_and_decode_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(kt + trace_table(os.path.join(prof_dir, "kt", "run_kernel_trace.csv"))) + "\n")
+
+
+def trace_table(path):
+    """Every kernel of a rocprofv3 kernel trace (csv), grouped by template and grid, as text rows."""
+    import collections
+    groups = collections.defaultdict(list)
+    for r in _rows(path):
+        if "at::" in r["Kernel_Name"]:
+            continue   # torch's own kernels (input generation, copies)
+        wg = int(r["Workgroup_Size_X"])
+        key = (_kernel_key(r["Kernel_Name"])[:64], int(r["Grid_Size_X"]) // wg, wg, int(r["VGPR_Count"]),
+               int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]))
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"{'kernel':66s}{'wgs':>8s}{'thr':>5s}{'vgpr':>6s}{'agpr':>6s}{'lds':>7s}{'calls':>7s}{'avg_us':>10s}"
+           f"{'median_us':>11s}{'min_us':>10s}{'max_us':>10s}"]
     for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         name, wgs, wg, vg, ag, lds = key
-        kt.append(f"{name:66s}{wgs:>8d}{wg:>5d}{vg:>6d}{ag:>6d}{lds:>7d}{len(v):>7d}{sum(v) / len(v):>10.1f}"
-                  f"{median(v):>11.1f}{min(v):>10.1f}{max(v):>10.1f}")
-    with open(os.path.join(out_dir, "train_8k_and_decode_kernel_trace.txt"), "w") as f:
-        f.write("\n".join(kt) + "\n")
+        out.append(f"{name:66s}{wgs:>8d}{wg:>5d}{vg:>6d}{ag:>6d}{lds:>7d}{len(v):>7d}{sum(v) / len(v):>10.1f}"
+                   f"{median(v):>11.1f}{min(v):>10.1f}{max(v):>10.1f}")
+    return out
+
+
+ALL_SECTIONS_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --decode-steps 16"
+
+
+def summarize_trace(prof_dir, out_dir, bench_log=None):
+    """profiles/bench_all_sections_kernel_trace.txt from one rocprofv3 --kernel-trace run of
+    `bench.py ALL_SECTIONS_ARGS` under prof_dir; bench_log (the run's stdout) adds its JSON line's
+    per-section times."""
+    cmd = f"python -u bench.py {ALL_SECTIONS_ARGS}"
+    txt = ["# Kernel trace of every bench.py section: train_8k forward+backward (B=4 H=32 L=8192 d=128 W=128 M=4,",
+           "# bf16), the backward that recomputes the forward's states, the step with log-sigmoid gates (sub-block",
+           "# path), the scalar-gate step, the stage-1 step (layer + teacher_mse_kernel), the Hedgehog feature-map",
+           "# step, fwd_4k (B=1 H=32 L=4096), decode_b64 (16 steps after a B=64 L=4096 prefill), prefill_64k one",
+           "# shot and in 8 continued segments, and the gate projection (x [4,8192,4096], per key dimension",
+           "# Ng=4096 and scalar Ng=32).",
+           "#",
+           "# command (TMPDIR=/tmp, from the repository root):",
+           f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt -o run -- {cmd} > <dir>/bench.log",
+           "#   python bench.py --summarize-trace <dir> --profiles-out profiles",
+           "# durations in microseconds per launch (kernel trace start/end); grid in workgroups; the template",
+           "# arguments are those of the kernels' declarations; one name with several grids covers several",
+           "# sections; torch's own kernels (input generation) are left out.  vgpr is the trace's VGPR_Count,",
+           "# which on gfx950 is half the compiler's per-lane count rounded up to its granule of 8 (230 -> 116).",
+           ""]
+    txt += trace_table(os.path.join(prof_dir, "kt", "run_kernel_trace.csv"))
+    if bench_log and os.path.exists(bench_log):
+        lines = [l for l in open(bench_log) if l.startswith("{")]
+        if lines:
+            rec = json.loads(lines[-1])
+            txt += ["", "# times from the bench.py line of the same run (under the tracer, so a little slower):",
+                    f"#   train step {rec['ms_per_step']} ms, {rec['value']} tokens/s; kernels_ms {rec.get('kernels_ms')}"]
+            for sec, v in rec.items():
+                if not isinstance(v, dict) or sec in ("config", "roofline", "kernels_ms", "step_roofline", "device",
+                                                      "kernel_counters"):
+                    continue
+                nums = {k: x for k, x in v.items() if isinstance(x, (int, float)) and
+                        (k.endswith("_ms") or k in ("ms_per_step", "us_per_step", "ms_saved", "ms_recomputed"))}
+                for sub, x in v.items():
+                    if isinstance(x, dict) and sub not in ("roofline",):
+                        nums.update({f"{sub}.{k}": y for k, y in x.items() if isinstance(y, (int, float)) and
+                                     (k.endswith("_ms") or k in ("ms", "us_per_step", "us_per_step_median"))})
+                if nums:
+                    txt.append(f"#   {sec}: " + ", ".join(f"{k} {y}" for k, y in nums.items()))
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "bench_all_sections_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(txt[:40]))
 
 
 def median(v):
@@ -921,8 +974,13 @@ def main():
                     help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="summarise rocprofv3 runs under DIR (kt, fetch, write, mfma) instead of measuring")
+    ap.add_argument("--summarize-trace", metavar="DIR", default=None,
+                    help="summarise one rocprofv3 --kernel-trace run of every section under DIR/kt instead of measuring")
     ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.profiles_out, os.path.join(args.summarize_trace, "bench.log"))
+        return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.profiles_out)
         return

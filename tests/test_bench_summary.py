@@ -53,3 +53,26 @@ def test_summary_scales_bytes_and_normalises_mfma(tmp_path):
     assert "rocprofv3 --pmc FETCH_SIZE" in txt and "2.40" in txt   # the clock check: 2.4e6 cycles in 1 ms
     kt = open(f"{out}/train_8k_and_decode_kernel_trace.txt").read()
     assert "chunk_kernel<bf16_t, 128, false, false>" in kt and "16384" in kt and "1000.0" in kt
+
+
+def test_all_sections_trace_groups_by_grid_and_drops_torch_kernels(tmp_path):
+    d = str(tmp_path / "prof")
+    row = lambda name, grid, t0, t1: {"Kernel_Name": name, "Grid_Size_X": grid, "Workgroup_Size_X": 256,
+                                      "VGPR_Count": 64, "Accum_VGPR_Count": 0, "LDS_Block_Size": 0,
+                                      "Start_Timestamp": t0, "End_Timestamp": t1}
+    out_k = "void lz::(anonymous namespace)::out_kernel<lz::bf16_t, 128, false, false, false>(lz::FwdArgs)"
+    torch_k = "void at::native::(anonymous namespace)::elementwise_kernel_with_index<int, at::native::arange>(int)"
+    _write(f"{d}/kt/run_kernel_trace.csv", TRACE_COLS,
+           [row(out_k, 16384 * 256, 0, 600_000), row(out_k, 16384 * 256, 0, 700_000),
+            row(out_k, 4096 * 256, 0, 150_000), row(torch_k, 256, 0, 4_000)])
+    with open(f"{d}/bench.log", "w") as f:
+        f.write("noise\n" + json.dumps({"ms_per_step": 3.2, "value": 1.0e7, "kernels_ms": {"forward": 0.9},
+                                        "decode": {"us_per_step": 65.0, "graph": {"us_per_step": 64.0}}}) + "\n")
+    out = str(tmp_path / "out")
+    bench.summarize_trace(d, out, f"{d}/bench.log")
+    txt = open(f"{out}/bench_all_sections_kernel_trace.txt").read()
+    rows = [l for l in txt.splitlines() if l.startswith("out_kernel")]
+    # one row per grid, the two 16384-workgroup launches averaged (650 us), the torch kernel left out
+    assert len(rows) == 2 and "650.0" in rows[0] and "16384" in rows[0] and "4096" in rows[1]
+    assert "at::" not in txt.split("\n\n")[1]
+    assert "decode: us_per_step 65.0, graph.us_per_step 64.0" in txt
