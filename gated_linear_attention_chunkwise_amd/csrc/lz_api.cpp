@@ -16,6 +16,7 @@ namespace {
 constexpr int kChunk = 64;
 constexpr int kMaxMeta = 16;
 constexpr int kMaxDecodeWindow = 8192;
+constexpr int32_t kMaxL = 1 << 30;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -24,6 +25,8 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
   if (s == nullptr) return LIZARD_EINVAL;
   if (s->B < 1 || s->H < 1 || s->d_k < 1 || s->d_v < 1 || s->W < 1 || s->M < 0) return LIZARD_EINVAL;
   if (op != LIZARD_OP_DECODE && s->L < 0) return LIZARD_EINVAL;
+  // token indices (and a chunk's end, t0 + 64) stay far inside int32 in every kernel
+  if (op != LIZARD_OP_DECODE && s->L > kMaxL) return LIZARD_EUNSUPPORTED;
   if (!isfinite(s->scale) || !isfinite(s->mix)) return LIZARD_EINVAL;
   if (s->dtype != LIZARD_FP32 && s->dtype != LIZARD_BF16) return LIZARD_EUNSUPPORTED;
   if (s->gate != LIZARD_GATE_PER_DIM && s->gate != LIZARD_GATE_SCALAR) return LIZARD_EUNSUPPORTED;

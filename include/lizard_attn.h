@@ -41,8 +41,8 @@
  *   and backward, d in {64, 128} for decode.  chunk in {64} (0 selects 64).
  *   Forward/backward: any W >= 1 (W >= L sees the whole causal prefix);
  *   continued segments and decode keep the window in a ring: 1 <= W <= 8192.
- *   0 <= M <= 16; B, H >= 1; L >= 0 (L = 0 writes only the zero state / zero
- *   meta gradients).  Anything else returns LIZARD_EUNSUPPORTED.
+ *   0 <= M <= 16; B, H >= 1; 0 <= L <= 2^30 (L = 0 writes only the zero state /
+ *   zero meta gradients).  Anything else returns LIZARD_EUNSUPPORTED.
  * - Numerical domain: every finite log-gate g <= 0, per token and key
  *   dimension (English page §2.C: the gate handled in log space keeps gated
  *   attention exact in low precision).  Inside a chunk the gate is folded into
@@ -284,7 +284,8 @@ lizard_status_t lizard_attn_fwd_continue(const lizard_attn_shape_t* s,
  *   q, k [B,H,d_k], v [B,H,d_v] (dtype), g [B,H,d_k] fp32: the new token
  *   state  in/out: S <- diag(exp g) S + k^T v (fp32)
  *   ring_k, ring_v in/out: the new key/value is stored in slot pos[b] mod W
- *   pos    in/out, device int32 [B]: tokens already consumed (>= 0); incremented
+ *   pos    in/out, device int32 [B]: tokens already consumed, 0 <= pos[b] <
+ *          2^31 - 1 (not checked: it lives on the device); incremented
  *   o      [B,H,d_v] written: q S + mix * softmax over M meta keys and the
  *          min(pos+1, W) filled ring slots.
  *   workspace  none is needed: lizard_attn_workspace_bytes(s, LIZARD_OP_DECODE)

@@ -69,7 +69,7 @@ def fwd(lib, s, q=GOOD, meta_k=GOOD, meta_v=None, o=GOOD, lse=None):
 @pytest.mark.parametrize("kw,code", [
     (dict(d_k=96, d_v=96), EUNSUPPORTED), (dict(d_k=64, d_v=128), EUNSUPPORTED),
     (dict(dtype=7), EUNSUPPORTED), (dict(dtype=0, d_k=128, d_v=128), EUNSUPPORTED), (dict(gate=2), EUNSUPPORTED),
-    (dict(M=17), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED),
+    (dict(M=17), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED), (dict(L=(1 << 30) + 1), EUNSUPPORTED),
     (dict(B=0), EINVAL), (dict(L=-1), EINVAL), (dict(W=0), EINVAL), (dict(M=-1), EINVAL),
     (dict(scale=float("nan")), EINVAL),
 ])
