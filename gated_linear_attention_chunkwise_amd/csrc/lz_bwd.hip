@@ -495,12 +495,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         }
       }
     } else {
-      frag fvu[KS], fkh[KS];
+      frag fkh[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        fvu[ks] = ld_frag(sV, LDQ, u, 32 * ks + 8 * kg);
-        fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
-      }
+      for (int ks = 0; ks < KS; ++ks) fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
       // exponent of query row `row` (block tb >= wb) against this key block's end: b_t - rho_wb
       auto qexp1 = [&](int row, int col) {
         const int tb = row >> 4;
@@ -565,37 +562,12 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         blk[tb] = f32x4{0, 0, 0, 0};
         if (tb >= wb) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sdO, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fvu[ks]);
+          for (int ks = 0; ks < KS; ++ks)
+            mma32(blk[tb], ld_frag(sdO, LDQ, 16 * tb + r, 32 * ks + 8 * kg), ld_frag(sV, LDQ, u, 32 * ks + 8 * kg));
           if (tb == wb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (4 * kg + i < r) blk[tb][i] = 0.f;
-        }
-      }
-      f32x4 dkr[NB];   // raw dk (GLA)
-#pragma unroll
-      for (int x = 0; x < NB; ++x) dkr[x] = f32x4{0, 0, 0, 0};
-      if (prw) {
-        // pairwise diagonal block: dk and the k-side terms directly, e^(g_{s+1} + .. + g_t) with
-        // the sum formed going forward from the key; dA[query 16 wb + t2][this key] sits in lane
-        // r + 16 (t2 / 4), slot t2 % 4
-        const f32x4 dAq = blk[wb];
-#pragma unroll
-        for (int x = 0; x < NB; ++x) {
-          const int col = 16 * x + 4 * kg;
-          const f32x4 kv = kraw4(u, col);
-          f32x4 run = f32x4{0, 0, 0, 0};
-#pragma unroll 1
-          for (int t2 = 0; t2 < 16; ++t2) {
-            if (t2 > r) run += graw4(16 * wb + t2, col);   // queries before the key carry dA = 0
-            const float dAv = __shfl(dAq[t2 & 3], r + 16 * (t2 >> 2), WAVE);
-            const f32x4 qv = qraw4(16 * wb + t2, col);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              dbs[x][e] += dAv * pair_term<FEAT>(qv[e], kv[e], run[e]);
-              if constexpr (!FEAT) dkr[x][e] += dAv * (qv[e] * __expf(run[e]));
-            }
-          }
         }
       }
       // dk'' += dA^T q' over the other blocks (q' of queries before this key block is zero)
@@ -623,7 +595,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
             __builtin_amdgcn_sched_barrier(0);   // one operand's loads at a time (register pressure)
           }
         }
-      // intra-chunk k side: terms of d b from k'', and dk = dk'' e^(T_wb - P_s) (at most 1)
+      // intra-chunk k side: terms of d b from k'', then acc0 turns from dk'' into the raw dk,
+      // dk = dk'' e^(T_wb - P_s) (at most 1); log features keep no GLA part in dk
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
         const int col = 16 * x + 4 * kg;
@@ -632,7 +605,30 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           dbs[x][e] += kpp[e] * acc0[x][e];
-          if constexpr (!FEAT) dkr[x][e] += __expf(xs[e]) * acc0[x][e];
+          acc0[x][e] = FEAT ? 0.f : __expf(xs[e]) * acc0[x][e];
+        }
+      }
+      if (prw) {
+        // pairwise diagonal block (its dA was left out above): dk and the k-side terms directly, e^(g_{s+1} + .. + g_t) with
+        // the sum formed going forward from the key; dA[query 16 wb + t2][this key] sits in lane
+        // r + 16 (t2 / 4), slot t2 % 4
+        const f32x4 dAq = blk[wb];
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+          const int col = 16 * x + 4 * kg;
+          const f32x4 kv = kraw4(u, col);
+          f32x4 run = f32x4{0, 0, 0, 0};
+#pragma unroll 1
+          for (int t2 = 0; t2 < 16; ++t2) {
+            if (t2 > r) run += graw4(16 * wb + t2, col);   // queries before the key carry dA = 0
+            const float dAv = __shfl(dAq[t2 & 3], r + 16 * (t2 >> 2), WAVE);
+            const f32x4 qv = qraw4(16 * wb + t2, col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dbs[x][e] += dAv * pair_term<FEAT>(qv[e], kv[e], run[e]);
+              if constexpr (!FEAT) acc0[x][e] += dAv * (qv[e] * __expf(run[e]));
+            }
+          }
         }
       }
       // inter-chunk with k e^(gamma - b) against the stored state gradient (gamma = Gamma in the
@@ -650,35 +646,36 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         }
         return z;
       };
-#pragma unroll
-      for (int x = 0; x < NB; ++x) acc0[x] = f32x4{0, 0, 0, 0};
+      frag fki[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        frag fki;
         const int col = 32 * ks + 8 * kg;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const f32x4 xk = kexp4(col + 4 * h2), kv = kraw4(u, col + 4 * h2);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) set_elem(fki, 4 * h2 + e, gate_op<FEAT>(kv[e], xk[e]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int x = 0; x < NB; ++x) {
-          mma32(acc0[x], ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * x, lane), fvu[ks]);
-          mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fki);
+          for (int e = 0; e < 4; ++e) set_elem(fki[ks], 4 * h2 + e, gate_op<FEAT>(kv[e], xk[e]));
         }
       }
+      // one 16-column block at a time: its V dS^T part goes straight into d b and dk
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
+        f32x4 y = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          // (this key's values read again here: keeping them live across the sub-block products
+          // would spill)
+          mma32(y, ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * x, lane),
+                ld_frag(sV, LDQ, u, 32 * ks + 8 * kg));
+          mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fki[ks]);
+        }
         const int col = 16 * x + 4 * kg;
         const f32x4 xk = kexp4(col), kv = kraw4(u, col);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dbs[x][e] += rnd_op<T>(gate_op<FEAT>(kv[e], xk[e])) * acc0[x][e];
-          if constexpr (!FEAT) dkr[x][e] += __expf(xk[e]) * acc0[x][e];
+          dbs[x][e] += rnd_op<T>(gate_op<FEAT>(kv[e], xk[e])) * y[e];
+          if constexpr (!FEAT) acc0[x][e] += __expf(xk[e]) * y[e];
         }
-        acc0[x] = dkr[x];
       }
     }
   } else if (qrole) {
