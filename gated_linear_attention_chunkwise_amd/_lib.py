@@ -175,7 +175,8 @@ def lizard_attn_fwd(q, k, v, g, meta_k, meta_v=None, *, window: int, scale: floa
     gate = _gate_mode(g, q)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     s = make_shape(B, H, L, d, window, M, scale, mix, dt, chunk, gate)
-    NC = (L + 63) // 64
+    C = chunk if chunk else 64
+    NC = (L + C - 1) // C
     out = {"o": torch.empty_like(q)}
     out["lse"] = torch.empty(B, H, L, device=dev, dtype=torch.float32) if want_lse else None
     out["o_swa"] = torch.empty_like(q) if want_o_swa else None

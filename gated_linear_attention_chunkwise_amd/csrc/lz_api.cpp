@@ -38,17 +38,29 @@ lizard_status_t check_shape(const lizard_attn_shape_t* s, int op) {
   if ((op == LIZARD_OP_DECODE || op == LIZARD_OP_FWD_CONTINUE) && s->W > kMaxDecodeWindow)
     return LIZARD_EUNSUPPORTED;
   if (op != LIZARD_OP_DECODE) {
-    if (s->chunk != 0 && s->chunk != kChunk) return LIZARD_EUNSUPPORTED;
-    if (s->dtype == LIZARD_FP32 && d != 64) return LIZARD_EUNSUPPORTED;
+    const int C = s->chunk == 0 ? kChunk : s->chunk;
+    if (C != 16 && C != 32 && C != 64 && C != 128) return LIZARD_EUNSUPPORTED;
+    // a continued segment runs on the fast kernels only: chunk 64, fp32 at d = 64
+    if (op == LIZARD_OP_FWD_CONTINUE && (C != kChunk || (s->dtype == LIZARD_FP32 && d != 64)))
+      return LIZARD_EUNSUPPORTED;
   }
   // every tensor of the call must be addressable with 64-bit offsets and
   // the grid must fit one launch
   const double elems = (double)s->B * s->H * (op == LIZARD_OP_DECODE ? s->W : (s->L > 0 ? s->L : 1)) * d;
   if (elems > 9.0e15) return LIZARD_EUNSUPPORTED;
   if ((double)s->B * s->H * (d / 16) > 2.0e9) return LIZARD_EUNSUPPORTED;
-  if (op != LIZARD_OP_DECODE && (double)s->B * s->H * ((s->L + kChunk - 1) / kChunk) > 2.0e9)
-    return LIZARD_EUNSUPPORTED;   // one workgroup per (batch, head, chunk)
+  if (op != LIZARD_OP_DECODE && (double)s->B * s->H * ((s->L + 15) / 16) > 2.0e9)
+    return LIZARD_EUNSUPPORTED;   // one workgroup per (batch, head, chunk or 16-token block)
   return LIZARD_OK;
+}
+
+// The chunk size of a call (0 selects 64).
+int chunk_of(const lizard_attn_shape_t* s) { return s->chunk == 0 ? kChunk : s->chunk; }
+
+// Calls the fast kernels are not laid out for run on the general path: a chunk other than 64, or
+// fp32 operands at d = 128 (forward and backward of the plain layer only).
+bool general_path(const lizard_attn_shape_t* s) {
+  return chunk_of(s) != kChunk || (s->dtype == LIZARD_FP32 && s->d_k != 64);
 }
 
 // Window length a whole sequence uses: keys in (t - W, t] that exist, so any W >= L sees the
@@ -96,8 +108,13 @@ lizard_status_t fwd_impl(const lizard_attn_shape_t* s,
   else
     st = check_ptrs({}, {q, k, v, g, o, meta_k, meta_v, lse, o_swa, chunk_states, state_out, workspace, lq, lk});
   if (st != LIZARD_OK) return st;
-  // the workspace holds the sweep's segment buffers, and the chunk states unless chunk_states is given
+  const bool gen = general_path(s);
+  if (gen && lq != nullptr) return LIZARD_EUNSUPPORTED;   // log features: chunk 64, fast kernels only
+  // the workspace holds the sweep's segment buffers (general path: the gates' block sums), and the
+  // chunk states unless chunk_states is given
   const size_t need = s->L == 0 ? 0
+                      : gen ? lz::fwd_general_workspace_bytes(s->B, s->H, s->L, s->d_k, chunk_of(s), s->dtype,
+                                                              chunk_states != nullptr)
                       : chunk_states != nullptr ? lz::fwd_aux_bytes(s->B, s->H, s->L, s->d_k)
                                                 : lz::fwd_workspace_bytes(s->B, s->H, s->L, s->d_k, s->dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
@@ -105,7 +122,9 @@ lizard_status_t fwd_impl(const lizard_attn_shape_t* s,
   lz::FwdArgs a{q, k, v, g, meta_k, s->M > 0 ? meta_v : nullptr, o, lse, o_swa, chunk_states, state_out,
                 workspace, nullptr, nullptr, nullptr, nullptr, s->B, s->H, s->L, window_in(s), s->M, s->scale, s->mix,
                 s->gate, s->L > 0 ? lq : nullptr, s->L > 0 ? lk : nullptr};
-  return lz::launch_fwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  const hipError_t e = gen ? lz::launch_fwd_general(a, s->dtype, s->d_k, chunk_of(s), stream)
+                           : lz::launch_fwd(a, s->dtype, s->d_k, stream);
+  return e == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
 lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
@@ -127,10 +146,14 @@ lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
     st = check_ptrs({}, {q, k, v, g, dO, lse, o_swa, chunk_states, dq, dk, dv, dg,
                          meta_k, meta_v, dmeta_k, dmeta_v, workspace, lq, lk, dlq, dlk});
   if (st != LIZARD_OK) return st;
+  const bool gen = general_path(s);
+  if (gen && lq != nullptr) return LIZARD_EUNSUPPORTED;   // log features: chunk 64, fast kernels only
   // without the saved forward tensors the workspace also holds their recomputation
   const bool recompute = s->L > 0 && (lse == nullptr || o_swa == nullptr || chunk_states == nullptr);
-  const size_t need = recompute ? lz::bwd_recompute_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype)
-                                : lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
+  const size_t need =
+      gen ? lz::bwd_general_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, chunk_of(s), s->dtype, recompute)
+      : recompute ? lz::bwd_recompute_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype)
+                  : lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_EWORKSPACE;
   lz::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g;
@@ -144,7 +167,9 @@ lizard_status_t bwd_impl(const lizard_attn_shape_t* s,
   a.workspace = workspace;
   a.stage_events = stage_events;
   if (s->L > 0 && lq != nullptr) { a.lq = lq; a.lk = lk; a.dlq = dlq; a.dlk = dlk; }
-  return lz::launch_bwd(a, s->dtype, s->d_k, stream) == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
+  const hipError_t e = gen ? lz::launch_bwd_general(a, s->dtype, s->d_k, chunk_of(s), stream)
+                           : lz::launch_bwd(a, s->dtype, s->d_k, stream);
+  return e == hipSuccess ? LIZARD_OK : LIZARD_EHIP;
 }
 
 lizard_status_t continue_impl(const lizard_attn_shape_t* s, const void* q, const void* k, const void* v,
@@ -212,6 +237,12 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op) {
   if (check_shape(s, seq_op ? LIZARD_OP_FWD : op) != LIZARD_OK) return 0;
   if (op == LIZARD_OP_DISTILL) return lz::distill_workspace_bytes(s->B, s->H, s->L);
   if (op == LIZARD_OP_FEATURE_BWD) return s->L > 0 ? lz::feature_workspace_bytes(s->B, s->H, s->L, s->d_k) : 0;
+  if (general_path(s) && (op == LIZARD_OP_FWD || op == LIZARD_OP_BWD || op == LIZARD_OP_BWD_RECOMPUTE)) {
+    if (op == LIZARD_OP_FWD)
+      return lz::fwd_general_workspace_bytes(s->B, s->H, s->L, s->d_k, chunk_of(s), s->dtype, false);
+    return lz::bwd_general_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, chunk_of(s), s->dtype,
+                                           op == LIZARD_OP_BWD_RECOMPUTE);
+  }
   if (op == LIZARD_OP_BWD) return lz::bwd_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
   if (op == LIZARD_OP_BWD_RECOMPUTE)
     return lz::bwd_recompute_workspace_bytes(s->B, s->H, s->L, s->M, s->d_k, s->dtype);
@@ -331,6 +362,7 @@ lizard_status_t lizard_hedgehog_fwd(const lizard_attn_shape_t* s, const void* x,
                                     hipStream_t stream) {
   lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
   if (st != LIZARD_OK) return st;
+  if (s->dtype == LIZARD_FP32 && s->d_k != 64) return LIZARD_EUNSUPPORTED;   // fp32 kernels: d = 64
   st = s->L > 0 ? check_ptrs({x, w, lphi}, {}) : check_ptrs({}, {x, w, lphi});
   if (st != LIZARD_OK) return st;
   if (s->L == 0) return LIZARD_OK;
@@ -343,6 +375,7 @@ lizard_status_t lizard_hedgehog_bwd(const lizard_attn_shape_t* s, const void* x,
                                     hipStream_t stream) {
   lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
   if (st != LIZARD_OK) return st;
+  if (s->dtype == LIZARD_FP32 && s->d_k != 64) return LIZARD_EUNSUPPORTED;   // fp32 kernels: d = 64
   st = s->L > 0 ? check_ptrs({x, w, dl, dx, dw, workspace}, {}) : check_ptrs({w, dw}, {x, dl, dx, workspace});
   if (st != LIZARD_OK) return st;
   if (s->L > 0 && workspace_bytes < lz::feature_workspace_bytes(s->B, s->H, s->L, s->d_k)) return LIZARD_EWORKSPACE;
@@ -355,6 +388,7 @@ lizard_status_t lizard_distill_mse(const lizard_attn_shape_t* s, const void* q_t
                                    size_t workspace_bytes, hipStream_t stream) {
   lizard_status_t st = check_shape(s, LIZARD_OP_FWD);
   if (st != LIZARD_OK) return st;
+  if (s->dtype == LIZARD_FP32 && s->d_k != 64) return LIZARD_EUNSUPPORTED;   // fp32 kernels: d = 64
   st = s->L > 0 ? check_ptrs({q_t, k_t, v_t, o_s, dO, loss, workspace}, {})
                 : check_ptrs({loss}, {q_t, k_t, v_t, o_s, dO, workspace});
   if (st != LIZARD_OK) return st;

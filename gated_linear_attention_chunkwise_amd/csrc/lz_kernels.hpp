@@ -149,6 +149,14 @@ hipError_t launch_feature_bwd(const FeatArgs& a, int dtype, int D, hipStream_t s
 hipError_t launch_gate_fwd(const GateArgs& a, int dtype, hipStream_t st);
 hipError_t launch_gate_bwd(const GateArgs& a, int dtype, hipStream_t st);   // L = 0: dw = 0
 
+// General path (lz_general.hip): the chunkwise forward / backward at any chunk C in {16, 32, 64, 128}
+// for fp32 or bf16 operands at d in {64, 128}, fp32 arithmetic on the vector units.  Same arguments
+// as launch_fwd / launch_bwd (no continuation, no log features); chunk_states are [B,H,ceil(L/C),d,d].
+hipError_t launch_fwd_general(const FwdArgs& a, int dtype, int D, int C, hipStream_t st);
+hipError_t launch_bwd_general(const BwdArgs& a, int dtype, int D, int C, hipStream_t st);
+size_t fwd_general_workspace_bytes(int B, int H, int L, int D, int C, int dtype, bool states_given);
+size_t bwd_general_workspace_bytes(int B, int H, int L, int M, int D, int C, int dtype, bool recompute);
+
 // Segments of the forward sweep for this shape (sequence parallelism when B*H is small).
 int sweep_segments(int B, int H, int L, int D);
 // Workspace bytes of the forward: the segment buffers (first), the strong-gate dispatch

@@ -37,8 +37,15 @@
  *   launched and no output is written; the return value says why.  A launch
  *   failure returns LIZARD_EHIP.  Faults inside kernels surface, as usual
  *   for HIP, at the caller's next synchronisation.
- * - Supported: d_k = d_v; bf16: d in {64, 128}; fp32: d = 64 for the forward
- *   and backward, d in {64, 128} for decode.  chunk in {64} (0 selects 64).
+ * - Supported: d_k = d_v in {64, 128}, bf16 or fp32.  lizard_attn_fwd and
+ *   lizard_attn_bwd take chunk in {16, 32, 64, 128} (0 selects 64): chunk 64 in
+ *   bf16, or in fp32 at d = 64, runs on the fast (matrix-core) kernels; every
+ *   other chunk, and fp32 at d = 128, on the general path -- the same chunkwise
+ *   algorithm (states passed and stored at the chunk boundaries in the operand
+ *   dtype) with fp32 arithmetic on the vector units, exact for every gate and
+ *   many times slower.  The continuation, the log-feature entry points, the
+ *   Hedgehog map and the stage-1 loss take chunk 64 and, in fp32, d = 64 only;
+ *   decode has no chunk and takes either dtype at d in {64, 128}.
  *   Forward/backward: any W >= 1 (W >= L sees the whole causal prefix);
  *   continued segments and decode keep the window in a ring: 1 <= W <= 8192.
  *   0 <= M <= 16; B, H >= 1; 0 <= L <= 2^30 (L = 0 writes only the zero state /
@@ -110,7 +117,8 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op);
  *   o                 [B,H,L,d_v] output (written)
  *   lse          opt  [B,H,L] fp32, log-sum-exp of each window softmax row
  *   o_swa        opt  [B,H,L,d_v] window branch before mixing
- *   chunk_states opt  state entering every chunk (needed by lizard_attn_bwd)
+ *   chunk_states opt  [B,H,ceil(L/chunk),d_k,d_v] dtype: the state entering every
+ *                     chunk (needed by lizard_attn_bwd with the same chunk)
  *   state_out    opt  [B,H,d_k,d_v] fp32 state after the last token (decode hand-off)
  *   workspace         caller-owned device memory, clobbered: when chunk_states
  *                     is NULL at least lizard_attn_workspace_bytes(s, LIZARD_OP_FWD)
@@ -119,8 +127,9 @@ size_t lizard_attn_workspace_bytes(const lizard_attn_shape_t* s, int op);
  *                     bytes (esz = 2 for bf16, 4 for fp32): the per-chunk
  *                     strong-gate masks and dispatch list (about 24 bytes per
  *                     (b, h, chunk)) and, when B*H is small enough for the state
- *                     sweep to run in sequence segments, its segment buffers;
- *                     may be NULL only for L = 0
+ *                     sweep to run in sequence segments, its segment buffers
+ *                     (general path: the gates' 16-token block sums, B*H*L*d*4
+ *                     + B*H*ceil(L/16)*d*4 bytes); may be NULL only for L = 0
  * NULL optional outputs are not written.  Launches on `stream`: the state
  * sweep over chunks (when B*H*(d/64)^2 < 512 and L spans at least 32
  * chunks, in segments of the sequence: a reduce pass per segment, a scan
@@ -142,7 +151,7 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
  *                              kernels recompute all three into the workspace
  *                              first (o is not written), which trades the memory
  *                              of keeping them between the passes (about
- *                              B*H*L*(4 + 2*d) + B*H*ceil(L/64)*d*d*2 bytes in
+ *                              B*H*L*(4 + 2*d) + B*H*ceil(L/chunk)*d*d*2 bytes in
  *                              bf16) for a forward's time
  *   dq, dk, dv                 written (dtype)
  *   dg                         written, fp32 [B,H,L,d_k]
@@ -161,7 +170,8 @@ lizard_status_t lizard_attn_fwd(const lizard_attn_shape_t* s,
  *                              saved tensor is NULL; chunk gradients; meta
  *                              reduction; a stage
  *                              with nothing to do still gets its event).  For
- *                              L = 0 they are not recorded. */
+ *                              L = 0, and on the general path, they are not
+ *                              recorded. */
 #define LIZARD_BWD_STAGES 3
 lizard_status_t lizard_attn_bwd(const lizard_attn_shape_t* s,
                                 const void* q, const void* k, const void* v, const float* g,

@@ -68,8 +68,9 @@ def fwd(lib, s, q=GOOD, meta_k=GOOD, meta_v=None, o=GOOD, lse=None):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d_k=96, d_v=96), EUNSUPPORTED), (dict(d_k=64, d_v=128), EUNSUPPORTED),
-    (dict(dtype=7), EUNSUPPORTED), (dict(dtype=0, d_k=128, d_v=128), EUNSUPPORTED), (dict(gate=2), EUNSUPPORTED),
-    (dict(M=17), EUNSUPPORTED), (dict(chunk=32), EUNSUPPORTED), (dict(L=(1 << 30) + 1), EUNSUPPORTED),
+    (dict(dtype=7), EUNSUPPORTED), (dict(gate=2), EUNSUPPORTED),
+    (dict(M=17), EUNSUPPORTED), (dict(chunk=24), EUNSUPPORTED), (dict(chunk=256), EUNSUPPORTED),
+    (dict(chunk=-64), EUNSUPPORTED), (dict(L=(1 << 30) + 1), EUNSUPPORTED),
     (dict(B=0), EINVAL), (dict(L=-1), EINVAL), (dict(W=0), EINVAL), (dict(M=-1), EINVAL),
     (dict(scale=float("nan")), EINVAL),
 ])
@@ -338,3 +339,40 @@ def test_decode_noalloc_validation(lib):
     assert call(shape(L=0), pos=BAD) == EALIGN
     assert call(shape(L=0, W=9000)) == EUNSUPPORTED
     assert call(shape(L=0, d_k=96, d_v=96)) == EUNSUPPORTED
+
+
+def test_general_path_validation(lib):
+    """Chunks of 16, 32 and 128 tokens and fp32 at d = 128 run on the general path (forward and
+    backward of the plain layer): accepted up to the workspace check, with their own workspace
+    layout (the gates' 16-token block sums, then the chunk states); the entry points that run on
+    the fast kernels only (log features, continuation, Hedgehog map) refuse them."""
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, L, D = 1, 2, 128, 128
+    for kw in (dict(chunk=16), dict(chunk=32), dict(chunk=128), dict(dtype=0), dict(dtype=0, chunk=16)):
+        s = shape(**kw)
+        C = kw.get("chunk", 64)
+        esz = 4 if kw.get("dtype", 1) == 0 else 2
+        nc, nb = (L + C - 1) // C, (L + 15) // 16
+        need = lib.lizard_attn_workspace_bytes(ctypes.byref(s), 0)
+        assert need == up(4 * B * H * L * D) + up(4 * B * H * nb * D) + up(esz * B * H * nc * D * D), kw
+        assert lib.lizard_attn_workspace_bytes(ctypes.byref(s), 1) > 0
+        assert lib.lizard_attn_workspace_bytes(ctypes.byref(s), 6) > lib.lizard_attn_workspace_bytes(ctypes.byref(s), 1)
+        fwd_call = lambda ws, nbytes: lib.lizard_attn_fwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD,
+                                                          None, None, None, None, ws, nbytes, None)
+        assert fwd_call(None, 0) == EWORKSPACE, kw
+        assert fwd_call(GOOD, need - 1) == EWORKSPACE, kw
+        assert fwd_call(BAD, need) == EALIGN, kw
+        assert lib.lizard_attn_bwd(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                   GOOD, GOOD, GOOD, GOOD, None, None, 0, None, None) == EWORKSPACE, kw
+        # fast kernels only
+        assert lib.lizard_attn_fwd_feat(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None,
+                                        None, GOOD, None, GOOD, 1 << 40, None) == EUNSUPPORTED, kw
+        assert lib.lizard_attn_bwd_feat(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD,
+                                        GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 1 << 40,
+                                        None, None) == EUNSUPPORTED, kw
+        assert lib.lizard_attn_fwd_continue(ctypes.byref(s), GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD,
+                                            GOOD, GOOD, GOOD, 1 << 40, None) == EUNSUPPORTED, kw
+        assert lib.lizard_attn_workspace_bytes(ctypes.byref(s), 3) == 0, kw
+    f128 = shape(dtype=0)
+    assert lib.lizard_hedgehog_fwd(ctypes.byref(f128), GOOD, GOOD, GOOD, None) == EUNSUPPORTED
+    assert lib.lizard_hedgehog_bwd(ctypes.byref(f128), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 40, None) == EUNSUPPORTED
