@@ -146,3 +146,13 @@ def test_general_scalar_gate_and_recompute():
                x, "bf16", W, 32)
     _check_bwd(_bwd(x, "bf16", W, 32), x, "bf16", W)
     _check_bwd(_bwd(x, "bf16", W, 32, saved=False), x, "bf16", W)
+
+
+def test_general_long_sequence():
+    """fp32 at d = 128 over 2048 tokens in chunks of 128 (16 chunks, a 200-token window, slow gates):
+    the state sweeps cross many boundaries and the window's tiles span chunks."""
+    x = make_small(1, 2, 2048, 128, 4, seed=2048, bf16=False, with_meta_v=True, x_mean=2.0)
+    W = 200
+    _check_fwd(_fwd(x, "fp32", W, 128, want_lse=True, want_o_swa=True, want_chunk_states=True, want_state=True),
+               x, "fp32", W, 128)
+    _check_bwd(_bwd(x, "fp32", W, 128), x, "fp32", W)
