@@ -495,6 +495,36 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         }
       }
     } else {
+      // inter-chunk with k e^(gamma - b) against the stored state gradient (gamma = Gamma in the
+      // columns stored undecayed, 0 in the others): Gamma - b_s = (T_wb - P_s) + T_{wb+1} + .. + T_3,
+      // -b_s = -(T_0 + .. + T_{wb-1} + P_s); dk part V dS^T, dv += k e^(gamma - b) dS
+      auto kexp4 = [&](int col) {
+        const f32x4 ps = ld4f(sB + u * LDBF + col);
+        const f32x4 ks = ld4f(sBT + wb * D + col) - ps + bsum4(wb + 1, 3, col);
+        const f32x4 kw = -(bsum4(0, wb - 1, col) + ps);
+        f32x4 z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cc = col + e;
+          z[e] = ((cc < 64 ? sm0 >> cc : sm1 >> (cc - 64)) & 1ull) ? ks[e] : kw[e];
+        }
+        return z;
+      };
+      // inter-chunk dv first, while no other accumulator is live: dv += k e^(gamma - b) dS, the key
+      // operand formed one K step at a time
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        frag fki;
+        const int col = 32 * ks + 8 * kg;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f32x4 xk = kexp4(col + 4 * h2), kv = kraw4(u, col + 4 * h2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) set_elem(fki, 4 * h2 + e, gate_op<FEAT>(kv[e], xk[e]));
+        }
+#pragma unroll
+        for (int x = 0; x < NB; ++x) mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fki);
+      }
       frag fkh[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
@@ -631,46 +661,30 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
           }
         }
       }
-      // inter-chunk with k e^(gamma - b) against the stored state gradient (gamma = Gamma in the
-      // columns stored undecayed, 0 in the others): Gamma - b_s = (T_wb - P_s) + T_{wb+1} + .. + T_3,
-      // -b_s = -(T_0 + .. + T_{wb-1} + P_s); dk part V dS^T, dv += k e^(gamma - b) dS
-      auto kexp4 = [&](int col) {
-        const f32x4 ps = ld4f(sB + u * LDBF + col);
-        const f32x4 ks = ld4f(sBT + wb * D + col) - ps + bsum4(wb + 1, 3, col);
-        const f32x4 kw = -(bsum4(0, wb - 1, col) + ps);
-        f32x4 z;
+      // inter-chunk dk (the dv part went first): V dS^T, one 16-column block at a time, straight
+      // into d b and dk.  This key's raw values come in once, packed (their loads would otherwise
+      // be hoisted out of the loop in fp32 and spill).
+      using R4 = decltype(ld4raw(static_cast<const T*>(nullptr)));
+      R4 kr[NB];
+      const bool kin = t0 + u < L;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int cc = col + e;
-          z[e] = ((cc < 64 ? sm0 >> cc : sm1 >> (cc - 64)) & 1ull) ? ks[e] : kw[e];
-        }
-        return z;
-      };
-      frag fki[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int col = 32 * ks + 8 * kg;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const f32x4 xk = kexp4(col + 4 * h2), kv = kraw4(u, col + 4 * h2);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) set_elem(fki[ks], 4 * h2 + e, gate_op<FEAT>(kv[e], xk[e]));
-        }
-      }
-      // one 16-column block at a time: its V dS^T part goes straight into d b and dk
+      for (int x = 0; x < NB; ++x) kr[x] = ld4raw(k + (size_t)min(t0 + u, L - 1) * D + 16 * x + 4 * kg);
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
         f32x4 y = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          // (this key's values read again here: keeping them live across the sub-block products
-          // would spill)
+        for (int ks = 0; ks < KS; ++ks)
           mma32(y, ld_frag_tr(sdSt, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * x, lane),
                 ld_frag(sV, LDQ, u, 32 * ks + 8 * kg));
-          mma32(acc1[x], ld_frag(sdSt, LDQ, 16 * x + r, 32 * ks + 8 * kg), fki[ks]);
-        }
         const int col = 16 * x + 4 * kg;
-        const f32x4 xk = kexp4(col), kv = kraw4(u, col);
+        f32x4 kv;
+        if constexpr (FEAT) {
+          kv = kraw4(u, col);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = kin ? (float)kr[x][e] : 0.f;
+        }
+        const f32x4 xk = kexp4(col);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           dbs[x][e] += rnd_op<T>(gate_op<FEAT>(kv[e], xk[e])) * y[e];
