@@ -22,7 +22,8 @@ from oracle import lizard_oracle as orc
 from gated_linear_attention_chunkwise_amd import (lizard_attn_bwd, lizard_attn_bwd_feat, lizard_attn_fwd,
                                                   lizard_attn_fwd_continue, lizard_attn_fwd_feat,
                                                   lizard_gate_proj_bwd, lizard_gate_proj_fwd)
-from gated_linear_attention_chunkwise_amd.inputs import make_log_features, make_small, round_to_bf16
+from gated_linear_attention_chunkwise_amd.inputs import (WORKLOADS, make_inputs_device, make_log_features, make_small,
+                                                          round_to_bf16)
 from helpers import TOL, dev, host, rel_l2, tdtype
 
 pytestmark = pytest.mark.gpu
@@ -254,3 +255,31 @@ def test_tau1_gate_projection_into_the_layer(mu, dtname):
     refs = {"g": ref_g, "o": ref["o"], "dq": gr["dq"], "dk": gr["dk"], "dv": gr["dv"], "dg": gr["dg"],
             "dx": ref_dx, "dw": ref_dw}
     check(out, refs, tuple(out), dtname, f"tau=1 chain mu={mu}")
+
+
+def test_tau1_train_shape_sampled_heads():
+    """The training shape (B=4, H=32, L=8192, d=128, W=128, M=4, bf16) with the pages' gate at
+    temperature 1, g = log sigmoid(z), z ~ N(-1, 1) (the benchmark's strong-gate step, same seed):
+    nearly every chunk takes the sub-block kernels, in the persistent launch over one dispatch
+    list of all 16384 chunks.  Forward and backward of two sampled heads against the oracle."""
+    w = WORKLOADS["train_8k"]
+    x = make_inputs_device(w, "cuda", with_grad=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    g = torch.nn.functional.logsigmoid(torch.randn(x["g"].shape, generator=gen, device="cuda") - 1.0)
+    strong = float((g.reshape(w.B, w.H, w.L // 64, 64, w.D).sum(3).amin(-1) < -64).float().mean())
+    assert strong > 0.9, strong
+    f = lizard_attn_fwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, window=w.W, scale=w.scale,
+                        want_lse=True, want_o_swa=True, want_chunk_states=True)
+    b = lizard_attn_bwd(x["q"], x["k"], x["v"], g, x["meta_k"], None, x["dO"], f["lse"], f["o_swa"],
+                        f["chunk_states"], window=w.W, scale=w.scale)
+    torch.cuda.synchronize()
+    for h in (0, 31):
+        hs = {n: x[n][:, h:h + 1].float().cpu().numpy() for n in ("q", "k", "v", "dO")}
+        gh = g[:, h:h + 1].cpu().numpy()
+        mk = x["meta_k"][h:h + 1].float().cpu().numpy()
+        ref = orc.hybrid_forward(hs["q"], hs["k"], hs["v"], gh, mk, None, window=w.W, scale=w.scale)
+        gref = orc.hybrid_backward(hs["q"], hs["k"], hs["v"], gh, mk, None, hs["dO"], window=w.W, scale=w.scale)
+        out = {"o": f["o"][:, h:h + 1], "lse": f["lse"][:, h:h + 1], "dmeta_k": b["dmeta_k"][h:h + 1],
+               **{n: b[n][:, h:h + 1] for n in ("dq", "dk", "dv", "dg")}}
+        check(out, {**ref, **gref}, ("o", "lse", "dq", "dk", "dv", "dg", "dmeta_k"), "bf16", f"tau1 train head {h}")
