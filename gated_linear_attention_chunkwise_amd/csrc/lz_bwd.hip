@@ -102,14 +102,20 @@ struct CkLayout {
   static constexpr size_t oBig = NT * tile;   // dS'^T [D][D] | d b [C][LDB] fp32
   static constexpr size_t bigBytes = sizeof(T) * D * LDQ > sizeof(float) * C * LDB ? sizeof(T) * D * LDQ
                                                                                    : sizeof(float) * C * LDB;
-  static constexpr size_t oMkT = oBig + bigBytes;                    // meta keys^T [D][16]
+  static constexpr size_t oBnd = oBig + bigBytes;                    // boundary term of dg [D]
+  static constexpr size_t oTot = oBnd + sizeof(float) * D;           // per-block column totals of d b [4][D]
+  // window-phase tiles; on the fast path they share their region with S_prev [D][D] (row-major),
+  // staged once for the dq waves' inter-chunk product and dead after the GLA part
+  static constexpr size_t oWin = oTot + sizeof(float) * 4 * D;
+  static constexpr size_t oSp = oWin;                                // fast path: S_prev
+  static constexpr size_t oMkT = oWin;                               // meta keys^T [D][16]
   static constexpr size_t oDLm = oMkT + sizeof(T) * D * LDM;         // dl_meta^T [16][C]
   static constexpr size_t oPm = oDLm + sizeof(T) * 16 * LDC;         // mix * p_meta^T [16][C]
   static constexpr size_t oLse = oPm + sizeof(T) * 16 * LDC;         // lse of 3 query chunks (log2 units)
   static constexpr size_t oDel = oLse + sizeof(float) * 3 * C;       // delta of 3 query chunks
-  static constexpr size_t oBnd = oDel + sizeof(float) * 3 * C;       // boundary term of dg [D]
-  static constexpr size_t oTot = oBnd + sizeof(float) * D;           // per-block column totals of d b [4][D]
-  static constexpr size_t fast_end = oTot + sizeof(float) * 4 * D;
+  static constexpr size_t win_end = oDel + sizeof(float) * 3 * C;
+  static constexpr size_t sp_end = oSp + sizeof(T) * D * LDQ;
+  static constexpr size_t fast_end = STRONG || win_end > sp_end ? win_end : sp_end;
   // sub-block path: fp32 block-local gate prefixes [C][LDBF] (the window's dO tile of a later
   // chunk afterwards), the 16-token block totals [4][D], the strips' largest in-block decays [D/16][4]
   static constexpr int LDBF = D + 4;
@@ -192,6 +198,7 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   float* sDel = reinterpret_cast<float*>(smem + LY::oDel);
   float* sBnd = reinterpret_cast<float*>(smem + LY::oBnd);
   float* sTot = reinterpret_cast<float*>(smem + LY::oTot);
+  T* sSp = reinterpret_cast<T*>(smem + LY::oSp);                 // fast path only
   float* sB = reinterpret_cast<float*>(smem + LY::oB);         // STRONG only
   float* sBT = reinterpret_cast<float*>(smem + LY::oBT);       // STRONG only
   float* sSpan = reinterpret_cast<float*>(smem + LY::oSpan);   // STRONG only
@@ -243,43 +250,76 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     }
   };
 
-  // S_prev rows of the dq waves' inter-chunk product, two K steps ahead: the first two go out
-  // last among the staging loads (so nothing in the staging phase waits for them) and arrive
-  // during it; each step of the product then issues the rows of the step two ahead.
+  // Sub-block path: S_prev rows of the dq waves' inter-chunk product, two K steps ahead: the first
+  // two go out last among the staging loads (so nothing in the staging phase waits for them) and
+  // arrive during it; each step of the product then issues the rows of the step two ahead.  (The
+  // fast path stages S_prev in LDS once for all four dq waves.)
   auto load_s = [&](frag (&dst)[NB], int ks) {
 #pragma unroll
     for (int x = 0; x < NB; ++x) dst[x] = ldg_frag<T>(Sprev + (size_t)(16 * x + r) * D + 32 * ks + 8 * kg);
   };
   frag fs0[NB], fs1[NB];
 
+  // fast path: the window phase's lse / delta rows and raw meta keys (one 16-byte vector of
+  // meta_k [16][D] per dq lane, rows clamped; any valid address when there are none) come with
+  // the staging loads and wait in the dq waves' registers until the hand-over, when S_prev's LDS
+  // region is free
+  constexpr int NMV = 16 * (D / VEC);
+  static_assert(NMV <= 4 * 64, "one meta-key vector per dq lane");
+  float wls = 0.f, wdl = 0.f;
+  V16 wmk = zero16();
+
   // ---------------------------------------------------------------- staging
   // Every load of the staging phase is issued before anything waits on one: no load sits
   // in a branch with its use, so the compiler places no wait between them (each such wait
   // would cost a full memory round trip before the next loads go out).
   {
-    // lse / delta of this chunk and the next two (rows clamped into the sequence)
-    const int lrow = min(t0 + min(tid, 3 * C - 1), L - 1);
-    const float rls = a.lse[(size_t)bh * L + lrow], rdl = a.ws_delta[(size_t)bh * L + lrow];
+    // lse / delta of this chunk and the next two (rows clamped into the sequence) and the raw
+    // meta keys (rows clamped; any valid address when there are none); the fast path reads these
+    // after its GLA part, when their LDS region (S_prev until then) is free
+    constexpr int NMK = D * 16 / NTHR_CK;          // meta-key elements per thread
+    float rls = 0.f, rdl = 0.f;
+    T rmk[NMK];
+    if constexpr (STRONG) {
+      const int lrow = min(t0 + min(tid, 3 * C - 1), L - 1);
+      rls = a.lse[(size_t)bh * L + lrow];
+      rdl = a.ws_delta[(size_t)bh * L + lrow];
+      const T* mkp = M > 0 ? mk : q;
+#pragma unroll
+      for (int e = 0; e < NMK; ++e) {
+        const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
+        rmk[e] = mkp[(size_t)min(m, max(M - 1, 0)) * D + d];
+      }
+    }
     // boundary term of dg for this thread's column, per d_v tile (the sweep writes zero for
     // the last chunk); summed when stored
     float bndp[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bndp[j] = wsbnd[(((size_t)bh * NC + c) * NJ + j) * D + tid % D];
-    // meta keys, raw, rows clamped (any valid address when there are none)
-    constexpr int NMK = D * 16 / NTHR_CK;          // meta-key elements per thread
-    const T* mkp = M > 0 ? mk : q;
-    T rmk[NMK];
-#pragma unroll
-    for (int e = 0; e < NMK; ++e) {
-      const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
-      rmk[e] = mkp[(size_t)min(m, max(M - 1, 0)) * D + d];
-    }
-    constexpr int NVS = D * (D / VEC) / NTHR_CK;   // dS' vectors per thread
+    constexpr int NVS = D * (D / VEC) / NTHR_CK;   // [D][D] vectors per thread
     V16 rds[NVS];
 #pragma unroll
     for (int e = 0; e < NVS; ++e) {
       const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
       rds[e] = ldg16(dSpT + (size_t)j * D + cv * VEC);
+    }
+    if constexpr (!STRONG) {
+      if (qrole) {
+        const int lrow = min(t0 + min(tid, 3 * C - 1), L - 1);
+        wls = a.lse[(size_t)bh * L + lrow];
+        wdl = a.ws_delta[(size_t)bh * L + lrow];
+        const int mi = min(tid, NMV - 1), m = mi % 16, cv = mi / 16;
+        wmk = ldg16((M > 0 ? mk : q) + (size_t)min(m, max(M - 1, 0)) * D + cv * VEC);
+      }
+    }
+    // fast path: S_prev once for all four dq waves (the sub-block path loads fragments per wave)
+    V16 rsp[STRONG ? 1 : NVS];
+    if constexpr (!STRONG) {
+#pragma unroll
+      for (int e = 0; e < NVS; ++e) {
+        const int idx = tid + e * NTHR_CK, i = idx / (D / VEC), cv = idx % (D / VEC);
+        rsp[e] = ldg16(Sprev + (size_t)i * D + cv * VEC);
+      }
     }
     V16 rdo[NVT], rv[NVT];
     fetch_rows(rdo, dO, t0);
@@ -291,9 +331,11 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     } else {
       if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
     }
-    if (qrole) {
-      load_s(fs0, 0);
-      if (KS > 1) load_s(fs1, 1);
+    if constexpr (STRONG) {
+      if (qrole) {
+        load_s(fs0, 0);
+        if (KS > 1) load_s(fs1, 1);
+      }
     }
     if constexpr (!STRONG) {
       if ((sm0 | sm1) != 0) {   // the sub-block launch takes this chunk
@@ -303,15 +345,17 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     }
     put_rows(sdO, rdo, t0);
     put_rows(sV, rv, t0);
+    if constexpr (STRONG) {
 #pragma unroll
-    for (int e = 0; e < NMK; ++e) {
-      const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
-      put_elem(sMkT + d * LY::LDM + m, m < M ? Tr<T>::to_f(rmk[e]) : 0.f);
-    }
-    if (tid < 3 * C) {
-      const bool ok = t0 + tid < L;
-      sLse[tid] = ok ? rls * LOG2E : 0.f;
-      sDel[tid] = ok ? rdl : 0.f;
+      for (int e = 0; e < NMK; ++e) {
+        const int idx = tid + e * NTHR_CK, d = idx / 16, m = idx % 16;
+        put_elem(sMkT + d * LY::LDM + m, m < M ? Tr<T>::to_f(rmk[e]) : 0.f);
+      }
+      if (tid < 3 * C) {
+        const bool ok = t0 + tid < L;
+        sLse[tid] = ok ? rls * LOG2E : 0.f;
+        sDel[tid] = ok ? rdl : 0.f;
+      }
     }
     if (tid < D) {
       float bnd = 0.f;
@@ -331,6 +375,7 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     for (int e = 0; e < NVS; ++e) {
       const int idx = tid + e * NTHR_CK, j = idx / (D / VEC), cv = idx % (D / VEC);
       *reinterpret_cast<V16*>(sdSt + j * LDQ + cv * VEC) = rds[e];
+      if constexpr (!STRONG) *reinterpret_cast<V16*>(sSp + j * LDQ + cv * VEC) = rsp[e];
     }
     __syncthreads();
   }
@@ -722,12 +767,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       }
     // dq~ += dO S_prev^T
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      frag (&cur)[NB] = (ks & 1) ? fs1 : fs0;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int x = 0; x < NB; ++x) mma32(acc0[x], cur[x], fo[ks]);
-      if (ks + 2 < KS) load_s(cur, ks + 2);
-    }
+      for (int x = 0; x < NB; ++x) mma32(acc0[x], ld_frag(sSp, LDQ, 16 * x + r, 32 * ks + 8 * kg), fo[ks]);
   } else {
     frag fvu[KS], fkh[KS];
 #pragma unroll
@@ -826,6 +868,21 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
     }
   }
   __syncthreads();
+  if constexpr (!STRONG) {
+    if (qrole) {   // the window phase's tiles (S_prev is dead; the next barrier publishes them)
+      if (tid < NMV) {   // consecutive lanes, consecutive meta rows: adjacent LDS halfwords
+        const int m = tid % 16, cv = tid / 16;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          put_elem(sMkT + (cv * VEC + e) * LY::LDM + m, m < M ? v16_get(wmk, e, (T*)nullptr) : 0.f);
+      }
+      if (tid < 3 * C) {
+        const bool ok = t0 + tid < L;
+        sLse[tid] = ok ? wls * LOG2E : 0.f;
+        sDel[tid] = ok ? wdl : 0.f;
+      }
+    }
+  }
   f32x4 db[NB];
   if (!qrole) {
 #pragma unroll
@@ -858,16 +915,41 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   __syncthreads();
   if (!qrole) {
     float dsum = 0.f;   // scalar gate: the token's gradient is the sum over the key dimensions
+    if constexpr (STRONG) {
 #pragma unroll
-    for (int x = 0; x < NB; ++x) {
-      const int i = 16 * x + 4 * kg;
-      f32x4 carry = *reinterpret_cast<const f32x4*>(sBnd + i);
-      for (int b2 = wb + 1; b2 < 4; ++b2) carry += *reinterpret_cast<const f32x4*>(sTot + b2 * D + i);
-      const f32x4 dgv = db[x] + carry;
-      if constexpr (SG)
-        dsum += (dgv[0] + dgv[1]) + (dgv[2] + dgv[3]);
-      else if (tok < L)
-        *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = dgv;
+      for (int x = 0; x < NB; ++x) {
+        const int i = 16 * x + 4 * kg;
+        f32x4 carry = *reinterpret_cast<const f32x4*>(sBnd + i);
+        for (int b2 = wb + 1; b2 < 4; ++b2) carry += *reinterpret_cast<const f32x4*>(sTot + b2 * D + i);
+        const f32x4 dgv = db[x] + carry;
+        if constexpr (SG)
+          dsum += (dgv[0] + dgv[1]) + (dgv[2] + dgv[3]);
+        else if (tok < L)
+          *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = dgv;
+      }
+    } else {
+      // the boundary term plus the totals of the later blocks: every total is read and weighted
+      // by an exact 0 or 1 (a loop over wb + 1 .. 3, or a branch per block, would wait on each
+      // read), and all column blocks are summed before any store (the sub-block kernel, at its
+      // register limit, keeps the loop above)
+      const float w1 = wb < 1 ? 1.f : 0.f, w2 = wb < 2 ? 1.f : 0.f, w3 = wb < 3 ? 1.f : 0.f;
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int i = 16 * x + 4 * kg;
+        f32x4 carry = *reinterpret_cast<const f32x4*>(sBnd + i);
+        carry += w1 * *reinterpret_cast<const f32x4*>(sTot + D + i);
+        carry += w2 * *reinterpret_cast<const f32x4*>(sTot + 2 * D + i);
+        carry += w3 * *reinterpret_cast<const f32x4*>(sTot + 3 * D + i);
+        db[x] += carry;
+      }
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int i = 16 * x + 4 * kg;
+        if constexpr (SG)
+          dsum += (db[x][0] + db[x][1]) + (db[x][2] + db[x][3]);
+        else if (tok < L)
+          *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = db[x];
+      }
     }
     if constexpr (SG) {
       dsum = xor_sum(xor_sum(dsum, 16), 32);   // the four column groups of the token
@@ -880,14 +962,33 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   const bool tvalid = tok < L;
   const float lse2 = sLse[u], delq = sDel[u];
   if (qrole && M > 0) {
-    // meta keys (always visible); absent meta values read as zero rows (no branch around the product)
-    const T* mvp = mv ? mv : mk;
-    const int mvrows = mv ? M : 0;
+    // meta keys (always visible) and, when given, meta values
     f32x4 x = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+    if constexpr (STRONG) {
+      // absent meta values read as zero rows (no branch around the product)
+      const T* mvp = mv ? mv : mk;
+      const int mvrows = mv ? M : 0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      mma32(x, ld_frag_tr(sMkT, LY::LDM, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 0, lane), fa[ks]);
-      mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), fb[ks]);
+      for (int ks = 0; ks < KS; ++ks) {
+        mma32(x, ld_frag_tr(sMkT, LY::LDM, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 0, lane), fa[ks]);
+        mma32(dp, ldg_row_frag<T>(mvp, D, r, 32 * ks + 8 * kg, mvrows), fb[ks]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        mma32(x, ld_frag_tr(sMkT, LY::LDM, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 0, lane), fa[ks]);
+      if (mv != nullptr) {
+        // meta values (absent ones add nothing to dp); rows clamped and zeroed past M, with no
+        // branch around the loads (each such branch ends in a wait for every load in flight)
+        frag fmv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          fmv[ks] = ldg_frag<T>(mv + (size_t)min(r, M - 1) * D + 32 * ks + 8 * kg);
+          if (r >= M) fmv[ks] = zero_frag<T>();
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma32(dp, fmv[ks], fb[ks]);
+      }
     }
     f32x4 dl;
 #pragma unroll
