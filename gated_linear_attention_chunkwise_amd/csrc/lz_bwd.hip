@@ -274,10 +274,21 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   // in a branch with its use, so the compiler places no wait between them (each such wait
   // would cost a full memory round trip before the next loads go out).
   {
-    // lse / delta of this chunk and the next two (rows clamped into the sequence) and the raw
-    // meta keys (rows clamped; any valid address when there are none); the fast path reads these
-    // after its GLA part, when their LDS region (S_prev until then) is free
     constexpr int NMK = D * 16 / NTHR_CK;          // meta-key elements per thread
+    // issued in the order of their use: the gate strips' q, k, g (the fold goes first), dO and v,
+    // then the rest, so that the fold runs while the later loads are still in flight
+    const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
+    std::conditional_t<FEAT, GateStripLog<T>, GateStrip<T>> gs;
+    if constexpr (FEAT) {
+      if (has_strip) gs.template load<SG>(a.lq + hoff, a.lk + hoff, g, D, t0, L, 16 * w + 4 * kg, r);
+    } else {
+      if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
+    }
+    V16 rdo[NVT], rv[NVT];
+    fetch_rows(rdo, dO, t0);
+    fetch_rows(rv, v, t0);
+    // sub-block path: lse / delta of this chunk and the next two (rows clamped into the sequence)
+    // and the raw meta keys (rows clamped; any valid address when there are none)
     float rls = 0.f, rdl = 0.f;
     T rmk[NMK];
     if constexpr (STRONG) {
@@ -321,16 +332,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         rsp[e] = ldg16(Sprev + (size_t)i * D + cv * VEC);
       }
     }
-    V16 rdo[NVT], rv[NVT];
-    fetch_rows(rdo, dO, t0);
-    fetch_rows(rv, v, t0);
-    const bool has_strip = w < D / 16;             // wave w folds the gates of columns 16w .. 16w+15
-    std::conditional_t<FEAT, GateStripLog<T>, GateStrip<T>> gs;
-    if constexpr (FEAT) {
-      if (has_strip) gs.template load<SG>(a.lq + hoff, a.lk + hoff, g, D, t0, L, 16 * w + 4 * kg, r);
-    } else {
-      if (has_strip) gs.template load<SG>(q, k, g, D, t0, L, 16 * w + 4 * kg, r);
-    }
     if constexpr (STRONG) {
       if (qrole) {
         load_s(fs0, 0);
@@ -342,6 +343,14 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         if (tid == 0) a.list[atomicAdd(a.list_count, 1)] = bh * NC + c;
         return;
       }
+    }
+    // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b (sub-block path: b, rho, raw q and
+    // keys folded to the end of their block)
+    if (has_strip) {
+      if constexpr (STRONG)
+        gs.fold_strong(sQt, sKh, LDQ, sB, LDBF, sBT, D, sSpan + 4 * w, 16 * w + 4 * kg, r, lane);
+      else
+        gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
     }
     put_rows(sdO, rdo, t0);
     put_rows(sV, rv, t0);
@@ -362,14 +371,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bnd += bndp[j];
       sBnd[tid] = bnd;
-    }
-    // chunk-local gate prefix b: q~ = q e^b, k^ = k e^-b, e^b (sub-block path: b, rho, raw q and
-    // keys folded to the end of their block)
-    if (has_strip) {
-      if constexpr (STRONG)
-        gs.fold_strong(sQt, sKh, LDQ, sB, LDBF, sBT, D, sSpan + 4 * w, 16 * w + 4 * kg, r, lane);
-      else
-        gs.fold(sQt, sKh, sEb, LDQ, 16 * w + 4 * kg, r);
     }
 #pragma unroll
     for (int e = 0; e < NVS; ++e) {
