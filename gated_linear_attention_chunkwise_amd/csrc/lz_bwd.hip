@@ -1190,17 +1190,48 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   }
 
   // ------------------------------------------------------------------ store
-  if (tvalid) {
-    const size_t o = hoff + (size_t)tok * D;
+  // Fast path: through LDS (every tile is free after the window phase), so that each lane writes
+  // 16-byte runs of whole rows (dq to the first tile, dk to the second, dv to the third).  The
+  // sub-block path, at its register limit, stores its accumulators directly.
+  if constexpr (STRONG) {
+    if (tvalid) {
+      const size_t o = hoff + (size_t)tok * D;
+      if (qrole) {
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+          stg4(reinterpret_cast<T*>(a.dq) + o + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
+      } else {
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+          stg4(reinterpret_cast<T*>(a.dk) + o + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
+          stg4(reinterpret_cast<T*>(a.dv) + o + 16 * x + 4 * kg, acc1[x][0], acc1[x][1], acc1[x][2], acc1[x][3]);
+        }
+      }
+    }
+  } else {
+    T* sOq = reinterpret_cast<T*>(smem);
+    T* sOk = reinterpret_cast<T*>(smem + LY::tile);
+    T* sOv = reinterpret_cast<T*>(smem + 2 * LY::tile);
+    __syncthreads();   // the window phase's last readers of the tiles are done
     if (qrole) {
 #pragma unroll
-      for (int x = 0; x < NB; ++x)
-        stg4(reinterpret_cast<T*>(a.dq) + o + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
+      for (int x = 0; x < NB; ++x) st4(sOq + u * LDQ + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
     } else {
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
-        stg4(reinterpret_cast<T*>(a.dk) + o + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
-        stg4(reinterpret_cast<T*>(a.dv) + o + 16 * x + 4 * kg, acc1[x][0], acc1[x][1], acc1[x][2], acc1[x][3]);
+        st4(sOk + u * LDQ + 16 * x + 4 * kg, acc0[x][0], acc0[x][1], acc0[x][2], acc0[x][3]);
+        st4(sOv + u * LDQ + 16 * x + 4 * kg, acc1[x][0], acc1[x][1], acc1[x][2], acc1[x][3]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NVT; ++e) {
+      const int idx = tid + e * NTHR_CK, row = idx / (D / VEC), cv = idx % (D / VEC);
+      if (t0 + row < L) {
+        const size_t o = hoff + (size_t)(t0 + row) * D + cv * VEC;
+        *reinterpret_cast<V16*>(reinterpret_cast<T*>(a.dq) + o) = *reinterpret_cast<const V16*>(sOq + row * LDQ + cv * VEC);
+        *reinterpret_cast<V16*>(reinterpret_cast<T*>(a.dk) + o) = *reinterpret_cast<const V16*>(sOk + row * LDQ + cv * VEC);
+        *reinterpret_cast<V16*>(reinterpret_cast<T*>(a.dv) + o) = *reinterpret_cast<const V16*>(sOv + row * LDQ + cv * VEC);
       }
     }
   }
