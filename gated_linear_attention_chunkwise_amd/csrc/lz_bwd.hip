@@ -943,11 +943,15 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         carry += w3 * *reinterpret_cast<const f32x4*>(sTot + 3 * D + i);
         db[x] += carry;
       }
+      // (raw per-dimension gates: dg goes to its own rows of the gate-gradient area, which every
+      // other wave has read by now, and leaves as whole rows in the window's first iteration)
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
         const int i = 16 * x + 4 * kg;
         if constexpr (SG)
           dsum += (db[x][0] + db[x][1]) + (db[x][2] + db[x][3]);
+        else if constexpr (!FEAT)
+          *reinterpret_cast<f32x4*>(sDb + u * LDB + i) = db[x];
         else if (tok < L)
           *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)tok * D + i) = db[x];
       }
@@ -1015,6 +1019,19 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
   float nls = 0.f, ndl = 0.f;
   for (int it = 0; it < n_it; ++it) {
     __syncthreads();   // the previous tiles' readers are done
+    if constexpr (!STRONG && !SG && !FEAT) {
+      if (it == 0) {
+        // dg of this chunk from the gate-gradient area: 16 bytes a lane, whole rows
+        constexpr int NDG = C * D / 4 / NTHR_CK;
+#pragma unroll
+        for (int e = 0; e < NDG; ++e) {
+          const int idx = tid + e * NTHR_CK, row = idx / (D / 4), c4 = idx % (D / 4);
+          if (t0 + row < L)
+            *reinterpret_cast<f32x4*>(a.dg + hoff + (size_t)(t0 + row) * D + 4 * c4) =
+                *reinterpret_cast<const f32x4*>(sDb + row * LDB + 4 * c4);
+        }
+      }
+    }
     if (it < n_q) {
       put_rows(sKw, pk, (c - it) * C);
       if (it > 0) put_rows(sV, pv, (c - it) * C);

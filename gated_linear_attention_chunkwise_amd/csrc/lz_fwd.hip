@@ -565,10 +565,28 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
         mma32(OW[jb], ld_frag_tr(sS, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, 16 * jb, lane), fq);
     }
   }
-  if (qvalid && a.o != nullptr) {   // (no o when the backward recomputes lse and o_swa)
-    T* orow = reinterpret_cast<T*>(a.o) + hoff + (size_t)tq * D;
+  // o (none when the backward recomputes lse and o_swa).  Fast path: through LDS (the value tile is
+  // free once every wave's products are done), so that each lane writes 16-byte runs of whole rows;
+  // the sub-block path, at its register limit, stores its accumulators directly.
+  if constexpr (STRONG) {
+    if (qvalid && a.o != nullptr) {
+      T* orow = reinterpret_cast<T*>(a.o) + hoff + (size_t)tq * D;
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) stg4(orow + 16 * jb + 4 * kg, OW[jb][0], OW[jb][1], OW[jb][2], OW[jb][3]);
+      for (int jb = 0; jb < JB; ++jb) stg4(orow + 16 * jb + 4 * kg, OW[jb][0], OW[jb][1], OW[jb][2], OW[jb][3]);
+    }
+  } else if (a.o != nullptr) {
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+      st4(sV + (16 * w + r) * LDQ + 16 * jb + 4 * kg, OW[jb][0], OW[jb][1], OW[jb][2], OW[jb][3]);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NVT; ++u) {
+      const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+      if (t0 + row < L)
+        *reinterpret_cast<V16*>(reinterpret_cast<T*>(a.o) + hoff + (size_t)(t0 + row) * D + cv * VEC) =
+            *reinterpret_cast<const V16*>(sV + row * LDQ + cv * VEC);
+    }
   }
 }
 
