@@ -313,8 +313,8 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
   {
     const float l = xor_sum(xor_sum(lpart, 16), 32);
     const float inv = 1.f / l;
-    if (qvalid) {
-      if (a.o_swa != nullptr) {
+    if constexpr (STRONG || CONT) {
+      if (qvalid && a.o_swa != nullptr) {
         T* srow = reinterpret_cast<T*>(a.o_swa) + hoff + (size_t)tq * D;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
@@ -322,8 +322,17 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
           stg4(srow + 16 * jb + 4 * kg, y[0], y[1], y[2], y[3]);
         }
       }
-      if (a.lse != nullptr && kg == 0) a.lse[(size_t)bh * L + tq] = (mrun + __log2f(l)) * 0.6931471805599453f;
+    } else if (a.o_swa != nullptr) {
+      // fast path (a continuation writes it directly): o_swa goes to the k^ tile (unused by the
+      // window) and leaves from there as whole rows, 16 bytes a lane, once the next barrier has
+      // published it
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const f32x4 y = inv * OW[jb];
+        st4(sX + (16 * w + r) * LDQ + 16 * jb + 4 * kg, y[0], y[1], y[2], y[3]);
+      }
     }
+    if (qvalid && a.lse != nullptr && kg == 0) a.lse[(size_t)bh * L + tq] = (mrun + __log2f(l)) * 0.6931471805599453f;
     const float f = a.mix * inv;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) OW[jb] *= f;
@@ -331,6 +340,18 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
 
   // ---- GLA branch
   __syncthreads();   // every wave is done with the last key tile
+  if constexpr (!STRONG && !CONT) {
+    // o_swa from the k^ tile (the fold writes k^ there only after the gate scan's barrier)
+    if (a.o_swa != nullptr) {
+#pragma unroll
+      for (int u = 0; u < NVT; ++u) {
+        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        if (t0 + row < L)
+          *reinterpret_cast<V16*>(reinterpret_cast<T*>(a.o_swa) + hoff + (size_t)(t0 + row) * D + cv * VEC) =
+              *reinterpret_cast<const V16*>(sX + row * LDQ + cv * VEC);
+      }
+    }
+  }
   f32x4 sufl[TPT][GV];   // STRONG: block-local exclusive suffixes S of this thread's tokens
   {
     if constexpr (FEAT) {
