@@ -48,10 +48,14 @@ struct SwLayout {
   static constexpr int LDB = D + Tr<T>::PAD;
   static constexpr size_t oA = 0;                                   // [C][TT]  gate-folded q or k (i tile)
   static constexpr size_t oB = oA + sizeof(T) * CHUNK * LDA;        // [C][D]   v or dO (every j)
-  static constexpr size_t oS = oB + sizeof(T) * CHUNK * LDB;        // [TT][D]  state rows (backward)
-  static constexpr size_t oDec = oS + sizeof(T) * TT * LDB;   // e^Gamma of the 64 rows
+  static constexpr size_t oS = oB + sizeof(T) * CHUNK * LDB;        // [TT][D]  state rows (backward);
+                                                                    // forward: the chunk state on its way out
+  static constexpr int LDT = TT + Tr<T>::PAD;
+  static constexpr size_t oT = oS + sizeof(T) * TT * LDB;     // backward: dS' on its way out [D][TT]
+  static constexpr size_t oDec = oT + sizeof(T) * D * LDT;    // e^Gamma of the 64 rows
   static constexpr size_t oFac = oDec + sizeof(float) * TT;    // backward: factor of the stored dS
   static constexpr size_t bytes = oFac + sizeof(float) * TT;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
 // Four values of column c0 + (lane & 15), rows r0 .. r0+3, of a row-major LDS tile.
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   T* sA = reinterpret_cast<T*>(smem + LY::oA);
   T* sB = reinterpret_cast<T*>(smem + LY::oB);
   T* sS = reinterpret_cast<T*>(smem + LY::oS);
+  T* sT = reinterpret_cast<T*>(smem + LY::oT);
   float* sDec = reinterpret_cast<float*>(smem + LY::oDec);
   float* sFac = reinterpret_cast<float*>(smem + LY::oFac);
 
@@ -223,17 +228,38 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
     if (a.list_count != nullptr && blockIdx.x == 0 && tid == 0) *a.list_count = 0;
 
   auto chunk_of = [&](int n) { return REV ? c_end - 1 - n : c_begin + n; };
+  // backward: dS' of chunk cs from its LDS tile to HBM as whole row runs, 16 bytes a lane (the
+  // tile is written after one barrier and read after the next)
+  auto flush_dS = [&](int cs) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + u * NTHR, row = idx / (TT / VEC), cv = idx % (TT / VEC);
+      *reinterpret_cast<V16*>(out + ((size_t)cs * D + row) * D + i0 + cv * VEC) =
+          *reinterpret_cast<const V16*>(sT + row * LY::LDT + cv * VEC);
+    }
+  };
   const int nlast = max(NCs - 1, 0);
   auto process = [&](SwStage<NV, RA>& s, int n) {
     const int c = chunk_of(n);
     if constexpr (!REV && !REDUCE) {
-      // state entering chunk c
+      // state entering chunk c, to LDS (its readers of the previous chunk passed the last barrier)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
-        stg4(out + ((size_t)c * D + i0 + 16 * ib + r) * D + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1],
-             acc[ib][2], acc[ib][3]);
+        st4(sS + (16 * ib + r) * LDB + j0 + 16 * w + 4 * kg, acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
     }
     __syncthreads();   // the previous chunk's operand reads are done
+    if constexpr (REV && !REDUCE) {
+      if (n > 0) flush_dS(c + 1);   // the chunk processed last (descending order)
+    }
+    if constexpr (!REV && !REDUCE) {
+      // ... and out as whole rows, 16 bytes a lane
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
+        *reinterpret_cast<V16*>(out + ((size_t)c * D + i0 + row) * D + cv * VEC) =
+            *reinterpret_cast<const V16*>(sS + row * LDB + cv * VEC);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int idx = tid + u * NTHR, row = idx / (D / VEC), cv = idx % (D / VEC);
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
         if constexpr (!REDUCE) {
           // dS' = e^Gamma dS, or dS itself in the strong columns (fac = 1)
           const f32x4 y = acc[jb] * fac;
-          stg4(out + ((size_t)c * D + j0 + 16 * jb + r) * D + i0 + 16 * w + 4 * kg, y[0], y[1], y[2], y[3]);
+          st4(sT + (j0 + 16 * jb + r) * LY::LDT + 16 * w + 4 * kg, y[0], y[1], y[2], y[3]);
         }
         acc[jb] *= dec;
       }
@@ -400,6 +426,12 @@ __global__ __launch_bounds__(NTHR_SW * (D / TT)) void sweep_kernel(SweepArgs a) 
   }
   if (n0 < NCs) process(s0, n0);
   if (DEPTH > 2 && n0 + 1 < NCs) process(s1, n0 + 1);
+  if constexpr (REV && !REDUCE) {
+    if (NCs > 0) {
+      __syncthreads();
+      flush_dS(chunk_of(NCs - 1));
+    }
+  }
   if constexpr (REDUCE) {
     const size_t sb = (size_t)bh * a.NS + seg;
     float* sf = a.seg_fin + sb * D * D;
@@ -458,6 +490,15 @@ hipError_t launch_sweep_g(const SweepArgs& a, hipStream_t st) {
   using LY = SwLayout<T, D>;
   const int blocks = D / TT;                    // 64-row blocks of the state
   const int nthr = NTHR_SW * (D / TT);
+  // (the fp32 layout exceeds the default 64 KB of dynamic LDS; set on every launch, which is cheap
+  // and keeps no state on the host)
+  hipError_t e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(sweep_kernel<T, D, REV, true, SG, FEAT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::bytes)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(sweep_kernel<T, D, REV, false, SG, FEAT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::bytes)) != hipSuccess)
+    return e;
   if (a.NS > 1) {   // segments: reduce (all but the first to be swept), scan, then the sweep
     hipLaunchKernelGGL((sweep_kernel<T, D, REV, true, SG, FEAT>), dim3(a.B * a.H * blocks * (a.NS - 1)),
                        dim3(nthr), LY::bytes, st, a);
