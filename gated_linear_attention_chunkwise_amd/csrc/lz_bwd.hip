@@ -1182,25 +1182,28 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
         }
       }
       // meta partial sums over this chunk's queries: dmk^T = q^T dl_meta, dmv^T = (mix dO)^T p_meta
+      // (the latter only with meta values: each partial holds M rows of MW columns)
       if (it == 0 && M > 0) {
-        float* dst = a.ws_dmeta + (((size_t)b * NC + c) * a.H + h) * M * 2 * D;
+        const int MW = mv != nullptr ? 2 * D : D;
+        float* dst = a.ws_dmeta + (((size_t)b * NC + c) * a.H + h) * M * MW;
 #pragma unroll
         for (int xb = 0; xb < NB / 4; ++xb) {
           const int d0 = 16 * (wb * (NB / 4) + xb);
           f32x4 xk = f32x4{0, 0, 0, 0}, xv = f32x4{0, 0, 0, 0};
 #pragma unroll
-          for (int ks = 0; ks < C / 32; ++ks) {
+          for (int ks = 0; ks < C / 32; ++ks)
             mma32(xk, ld_frag_tr(sQw, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
                   ld_frag(sDLm, LY::LDC, r, 32 * ks + 8 * kg));
-            mma32(xv, ld_frag_tr(sdO, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
-                  ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
-          }
-          if (r < M)
+          if (mv != nullptr) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              dst[(size_t)r * 2 * D + d0 + 4 * kg + i] = xk[i];
-              dst[(size_t)r * 2 * D + D + d0 + 4 * kg + i] = xv[i];
-            }
+            for (int ks = 0; ks < C / 32; ++ks)
+              mma32(xv, ld_frag_tr(sdO, LDQ, 32 * ks + 8 * kg, 32 * ks + 8 * kg + 4, d0, lane),
+                    ld_frag(sPm, LY::LDC, r, 32 * ks + 8 * kg));
+          }
+          if (r < M) {
+            *reinterpret_cast<f32x4*>(dst + (size_t)r * MW + d0 + 4 * kg) = xk;
+            if (mv != nullptr) *reinterpret_cast<f32x4*>(dst + (size_t)r * MW + D + d0 + 4 * kg) = xv;
+          }
         }
       }
     }
@@ -1293,8 +1296,9 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_strong_kernel(BwdArgs a, con
 
 // ------------------------------------------------------------ meta reduce
 // Two-level deterministic sum of the per-(batch, chunk) meta partials
-// part[slot][H*M*2D]: level 1 folds each run of `per` slots into its first
-// slot (in place), level 2 sums the run heads in order.
+// part[slot][H*M*MW] (MW = 2D with meta values, D without): level 1 folds each
+// run of `per` slots into its first slot (in place), level 2 sums the run
+// heads in order.
 __global__ __launch_bounds__(NTHR) void dmeta_fold_kernel(float* __restrict__ part, int slots, int n, int per) {
   const int e = blockIdx.x * NTHR + threadIdx.x;
   if (e >= n) return;
@@ -1305,12 +1309,13 @@ __global__ __launch_bounds__(NTHR) void dmeta_fold_kernel(float* __restrict__ pa
 }
 
 __global__ __launch_bounds__(NTHR) void dmeta_kernel(const float* __restrict__ part, float* __restrict__ dmk,
-                                                      float* __restrict__ dmv, int slots, int per, int n, int D) {
-  const int e = blockIdx.x * NTHR + threadIdx.x;   // over H*M*2D
+                                                      float* __restrict__ dmv, int slots, int per, int n, int D,
+                                                      int MW) {
+  const int e = blockIdx.x * NTHR + threadIdx.x;   // over H*M*MW
   if (e >= n) return;
   float acc = 0.f;
   for (int s = 0; s < slots; s += per) acc += part[(size_t)s * n + e];
-  const int hm = e / (2 * D), col = e % (2 * D);
+  const int hm = e / MW, col = e % MW;
   if (col < D) dmk[(size_t)hm * D + col] = acc;
   else if (dmv != nullptr) dmv[(size_t)hm * D + col - D] = acc;
 }
@@ -1411,7 +1416,8 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
   }
   mark(2);
   if (a.M > 0) {
-    const int n = a.H * a.M * 2 * D;
+    const int MW = a.meta_v != nullptr ? 2 * D : D;
+    const int n = a.H * a.M * MW;
     const int slots = a.B * NC;
     const int runs = slots < 32 ? slots : 32;
     const int per = (slots + runs - 1) / runs;
@@ -1419,7 +1425,7 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
                        a.ws_dmeta, slots, n, per);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(dmeta_kernel, dim3((n + NTHR - 1) / NTHR), dim3(NTHR), 0, st,
-                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, slots, per, n, D);
+                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, slots, per, n, D, MW);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(3);
