@@ -218,19 +218,19 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
     }
   }
 
-  // meta keys / values (absent values staged as zeros: no branch around the product)
+  // meta keys / values (values only when given; absent ones add nothing to the sum)
   for (int e = tid; e < 16 * (D / VEC); e += NTHR) {
     const int m = e / (D / VEC), cv = e % (D / VEC);
     V16 x = zero16();
     if (m < M) x = ldg16(reinterpret_cast<const T*>(a.meta_k) + ((size_t)h * M + m) * D + cv * VEC);
     *reinterpret_cast<V16*>(sMk + m * LDQ + cv * VEC) = x;
   }
-  for (int e = tid; e < D * 16; e += NTHR) {
-    const int j = e / 16, m = e % 16;
-    float x = 0.f;
-    if (a.meta_v != nullptr && m < M)
-      x = Tr<T>::to_f(reinterpret_cast<const T*>(a.meta_v)[((size_t)h * M + m) * D + j]);
-    put_elem(sMvt + j * LY::LDMV + m, x);
+  if (a.meta_v != nullptr) {
+    for (int e = tid; e < D * 16; e += NTHR) {
+      const int j = e / 16, m = e % 16;
+      const float x = m < M ? Tr<T>::to_f(reinterpret_cast<const T*>(a.meta_v)[((size_t)h * M + m) * D + j]) : 0.f;
+      put_elem(sMvt + j * LY::LDMV + m, x);
+    }
   }
 
   // ---- anchor window: online softmax over the meta keys and keys in (t-W, t]
@@ -269,10 +269,12 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i) xm[0][i] = (4 * kg + i < M) ? xm[0][i] * sl2 : -INFINITY;
       absorb<1, JB>(xm, mrun, lpart, OW);
-      frag bop;
-      pack_acc(bop, xm[0], f32x4{0, 0, 0, 0});
+      if (a.meta_v != nullptr) {   // (without meta values the sinks add nothing to the sum)
+        frag bop;
+        pack_acc(bop, xm[0], f32x4{0, 0, 0, 0});
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) mma32(OW[jb], ld_frag_perm(sMvt, LY::LDMV, 16 * jb + r, 0, 0, kg), bop);
+        for (int jb = 0; jb < JB; ++jb) mma32(OW[jb], ld_frag_perm(sMvt, LY::LDMV, 16 * jb + r, 0, 0, kg), bop);
+      }
     }
 
     const int kbase = kt * C;
