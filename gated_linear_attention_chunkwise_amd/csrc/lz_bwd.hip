@@ -28,7 +28,7 @@
 //   chunk_kernel   one workgroup per (b, h, chunk): every GLA gradient plus
 //                  the anchor-window gradients (query side for dq, key side
 //                  for dk and dv) and per-chunk meta-key partial sums
-//   dmeta_fold_kernel, dmeta_kernel
+//   dmeta_sum_kernel
 //                  deterministic sum of the meta partials over batch and chunks
 // With log features (lizard_attn_bwd_feat) the GLA operands are exp(lq + b) and
 // exp(lk - b), and the GLA gradients of q and k leave as dlq = q~ dq~ and
@@ -1295,29 +1295,32 @@ __global__ __launch_bounds__(NTHR_CK, 1) void chunk_strong_kernel(BwdArgs a, con
 }
 
 // ------------------------------------------------------------ meta reduce
-// Two-level deterministic sum of the per-(batch, chunk) meta partials
-// part[slot][H*M*MW] (MW = 2D with meta values, D without): level 1 folds each
-// run of `per` slots into its first slot (in place), level 2 sums the run
-// heads in order.
-__global__ __launch_bounds__(NTHR) void dmeta_fold_kernel(float* __restrict__ part, int slots, int n, int per) {
-  const int e = blockIdx.x * NTHR + threadIdx.x;
-  if (e >= n) return;
-  const int s0 = blockIdx.y * per, s1 = min(slots, s0 + per);
+// Deterministic sum of the per-(batch, chunk) meta partials part[slot][H*M*MW] (MW = 2D with meta
+// values, D without) in one launch: a workgroup takes 64 partial columns; its 16 groups of 64
+// threads sum every 16th slot, and the 16 group sums are added in a fixed order.
+constexpr int DM_COLS = 64, DM_GROUPS = 16;
+__global__ __launch_bounds__(DM_COLS * DM_GROUPS) void dmeta_sum_kernel(const float* __restrict__ part,
+                                                                         float* __restrict__ dmk,
+                                                                         float* __restrict__ dmv, int slots, int n,
+                                                                         int D, int MW) {
+  __shared__ float red[DM_GROUPS][DM_COLS];
+  const int col = threadIdx.x % DM_COLS, grp = threadIdx.x / DM_COLS;
+  const int e = blockIdx.x * DM_COLS + col;
   float acc = 0.f;
-  for (int s = s0; s < s1; ++s) acc += part[(size_t)s * n + e];
-  if (s0 < slots) part[(size_t)s0 * n + e] = acc;
-}
-
-__global__ __launch_bounds__(NTHR) void dmeta_kernel(const float* __restrict__ part, float* __restrict__ dmk,
-                                                      float* __restrict__ dmv, int slots, int per, int n, int D,
-                                                      int MW) {
-  const int e = blockIdx.x * NTHR + threadIdx.x;   // over H*M*MW
-  if (e >= n) return;
-  float acc = 0.f;
-  for (int s = 0; s < slots; s += per) acc += part[(size_t)s * n + e];
-  const int hm = e / MW, col = e % MW;
-  if (col < D) dmk[(size_t)hm * D + col] = acc;
-  else if (dmv != nullptr) dmv[(size_t)hm * D + col - D] = acc;
+  if (e < n) {
+#pragma unroll 8
+    for (int s = grp; s < slots; s += DM_GROUPS) acc += part[(size_t)s * n + e];
+  }
+  red[grp][col] = acc;
+  __syncthreads();
+  if (grp == 0 && e < n) {
+    float t = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < DM_GROUPS; ++g2) t += red[g2][col];
+    const int hm = e / MW, c2 = e % MW;
+    if (c2 < D) dmk[(size_t)hm * D + c2] = t;
+    else if (dmv != nullptr) dmv[(size_t)hm * D + c2 - D] = t;
+  }
 }
 
 __global__ void fill_zero_kernel(float* p, size_t n) {
@@ -1419,13 +1422,8 @@ hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t st) {
     const int MW = a.meta_v != nullptr ? 2 * D : D;
     const int n = a.H * a.M * MW;
     const int slots = a.B * NC;
-    const int runs = slots < 32 ? slots : 32;
-    const int per = (slots + runs - 1) / runs;
-    hipLaunchKernelGGL(dmeta_fold_kernel, dim3((n + NTHR - 1) / NTHR, runs), dim3(NTHR), 0, st,
-                       a.ws_dmeta, slots, n, per);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(dmeta_kernel, dim3((n + NTHR - 1) / NTHR), dim3(NTHR), 0, st,
-                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, slots, per, n, D, MW);
+    hipLaunchKernelGGL(dmeta_sum_kernel, dim3((n + DM_COLS - 1) / DM_COLS), dim3(DM_COLS * DM_GROUPS), 0, st,
+                       (const float*)a.ws_dmeta, a.dmeta_k, a.dmeta_v, slots, n, D, MW);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(3);
