@@ -218,7 +218,7 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
     }
   }
 
-  // meta keys / values (values only when given; absent ones add nothing to the sum)
+  // meta keys / values (values only when given: absent ones add nothing to the weighted value sum)
   for (int e = tid; e < 16 * (D / VEC); e += NTHR) {
     const int m = e / (D / VEC), cv = e % (D / VEC);
     V16 x = zero16();
@@ -269,7 +269,7 @@ __device__ __forceinline__ void out_chunk(const FwdArgs& a, const T* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i) xm[0][i] = (4 * kg + i < M) ? xm[0][i] * sl2 : -INFINITY;
       absorb<1, JB>(xm, mrun, lpart, OW);
-      if (a.meta_v != nullptr) {   // (without meta values the sinks add nothing to the sum)
+      if (a.meta_v != nullptr) {   // (without meta values the sinks only enter the denominator)
         frag bop;
         pack_acc(bop, xm[0], f32x4{0, 0, 0, 0});
 #pragma unroll
