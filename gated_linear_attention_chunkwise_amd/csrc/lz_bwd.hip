@@ -778,29 +778,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       fvu[ks] = ld_frag(sV, LDQ, u, 32 * ks + 8 * kg);
       fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
     }
-    // A blocks (queries of block tb >= wb, keys of block wb): dv += A^T dO
+    // (the intra-chunk dv product, A^T dO, waits for the hand-over below)
     f32x4 blk[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      blk[tb] = f32x4{0, 0, 0, 0};
-      if (tb >= wb) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sQt, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fkh[ks]);
-        if (tb == wb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * kg + i < r) blk[tb][i] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      if (2 * p + 1 >= wb) {
-        frag op;
-        pack_acc(op, blk[2 * p], blk[2 * p + 1]);
-#pragma unroll
-        for (int x = 0; x < NB; ++x)
-          mma32(acc1[x], ld_frag_tr(sdO, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
-      }
     // dA blocks (queries tb >= wb, keys of block wb): dk^ += dA^T q~
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -866,6 +845,37 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, const T* __restrict
       } else if constexpr (!STRONG) {
         acc0[x] *= ld4f(sEb + u * LDQ + i);
       }
+    }
+  }
+  if constexpr (!STRONG) {
+    if (!qrole) {
+      // intra-chunk dv += A^T dO (A blocks: queries of block tb >= wb, keys of block wb), while the
+      // dq waves hand their terms over (q~, k^ and dO stay in LDS until the window phase)
+      frag fkh[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) fkh[ks] = ld_frag(sKh, LDQ, u, 32 * ks + 8 * kg);
+      f32x4 blk[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        blk[tb] = f32x4{0, 0, 0, 0};
+        if (tb >= wb) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma32(blk[tb], ld_frag(sQt, LDQ, 16 * tb + r, 32 * ks + 8 * kg), fkh[ks]);
+          if (tb == wb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * kg + i < r) blk[tb][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        if (2 * p + 1 >= wb) {
+          frag op;
+          pack_acc(op, blk[2 * p], blk[2 * p + 1]);
+#pragma unroll
+          for (int x = 0; x < NB; ++x)
+            mma32(acc1[x], ld_frag_tr(sdO, LDQ, 32 * p + 4 * kg, 32 * p + 16 + 4 * kg, 16 * x, lane), op);
+        }
     }
   }
   __syncthreads();
